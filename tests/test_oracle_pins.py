@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each checks the oracle against a
+hand-derived fixture (tests/golden), a library routine (torch FP8 casts,
+scipy's Hadamard), an independent formulation, a closed form, an invariant,
+or a float64 brute force.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from oracle import hadamard as H
+from oracle import quant as Q
+from oracle import study
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append(line)
+    return rows
+
+
+def _hexf32(s):
+    return np.float32(float.fromhex(s))
+
+
+# ------------------------------------------------------------- E2M1 ----
+def test_e2m1_golden_table():
+    for row in _read_golden("e2m1_rne.txt"):
+        y, idx = row.split()[:2]
+        assert int(F.e2m1_rne_index(_hexf32(y))) == int(idx), row
+
+
+def _e2m1_by_rint(y):
+    """Independent formulation: round to the spacing of the binade (0.5 below
+    2, 1 in [2,4), 2 from 4 up) with numpy's half-to-even rint, cap at 6."""
+    y = y.astype(np.float64)
+    q = np.where(y < 2, np.rint(y * 2) / 2, np.where(y < 4, np.rint(y), 2 * np.rint(y / 2)))
+    return np.minimum(q, 6.0)
+
+
+def test_e2m1_dense_sweep_three_formulations():
+    # every float32 in [0, 8) with the low 8 mantissa bits cleared, plus all
+    # float32 neighbours of the seven midpoints
+    bits = np.arange(0, np.float32(8.0).view(np.uint32), 256, dtype=np.uint32)
+    y = bits.view(np.float32)
+    mids = F.E2M1_MIDPOINTS
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(9))])
+    y = np.concatenate([y, near.astype(np.float32), np.float32([6, 6.5, 7, 8, 100, 3e38])])
+    got = F.e2m1_value(F.e2m1_rne_index(y)).astype(np.float64)
+    np.testing.assert_array_equal(got, _e2m1_by_rint(y))
+    np.testing.assert_array_equal(got, study.e2m1_nearest64(y))
+
+
+# ------------------------------------------------------------- E4M3 ----
+def test_e4m3_table_matches_torch():
+    pats = torch.arange(127, dtype=torch.uint8)
+    ref = pats.view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(F.E4M3_VALUES64, ref)
+    assert np.count_nonzero(F.E4M3_VALUES64 > 0) == 126       # 126 positive finite
+    assert F.E4M3_VALUES64[0x7E] == 448.0 and F.E4M3_VALUES64[0x78] == 256.0
+
+
+def test_e4m3_golden():
+    for row in _read_golden("e4m3_rne.txt"):
+        t, p = row.split()[:2]
+        assert int(F.e4m3_rne_pattern(_hexf32(t))) == int(p, 16), row
+
+
+def test_e4m3_rne_matches_torch_cast():
+    # torch's cast is round-to-nearest-even and does not saturate (>= 480 is
+    # NaN), so compare on (0, 464)
+    rng = np.random.default_rng(5)
+    t = np.concatenate([
+        np.exp(rng.uniform(np.log(1e-5), np.log(463.0), 200_000)),
+        (F.E4M3_VALUES64[:-1] + F.E4M3_VALUES64[1:]) / 2,           # every tie
+        F.E4M3_VALUES64[1:],
+    ]).astype(np.float32)
+    t = t[(t > 0) & (t < 464)]
+    mids32 = ((F.E4M3_VALUES64[:-1] + F.E4M3_VALUES64[1:]) / 2).astype(np.float32)
+    t = np.concatenate([t, np.nextafter(mids32, np.float32(0)), np.nextafter(mids32, np.float32(500))])
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    np.testing.assert_array_equal(F.e4m3_rne_pattern(t), ref)
+
+
+# ------------------------------------------------------------- E8M0 ----
+def test_e8m0_decode_matches_torch():
+    b = torch.arange(255, dtype=torch.uint8)
+    ref = b.view(torch.float8_e8m0fnu).double().numpy()
+    np.testing.assert_array_equal(F.e8m0_decode(np.arange(255)), ref)
+
+
+def test_mx_base_exponent_golden():
+    for row in _read_golden("mx_base_exponent.txt"):
+        a, e = row.split()[:2]
+        assert int(Q.mx_base_exponent(np.float32(_hexf32(a)))) == int(e), row
+
+
+def test_mx_base_exponent_frexp_rule():
+    # independent closed form: a = m * 2**e, m in [1/2, 1): E = e-3 if m <= 3/4 else e-2
+    rng = np.random.default_rng(6)
+    a = np.exp(rng.normal(0, 8, 200_000)).astype(np.float32)
+    a = a[(a > 1e-37) & np.isfinite(a)]
+    m, e = np.frexp(a.astype(np.float64))
+    ref = np.where(m <= 0.75, e - 3, e - 2)
+    np.testing.assert_array_equal(Q.mx_base_exponent(a), np.clip(ref, -127, 127))
+
+
+# ------------------------------------------------------ tree and pack ----
+def test_tree_sum_golden_order():
+    for row in _read_golden("tree_sum.txt"):
+        vals, expect = row.split("|")
+        v = np.array([float(s) for s in vals.split()], dtype=np.float32)
+        assert float(Q.tree_sum_f32(v)) == float(expect), row
+
+
+def test_nibble_order():
+    codes = np.array([[0x1, 0x2, 0xF, 0x8]], dtype=np.uint8)
+    packed = Q.pack_nibbles(codes)
+    assert packed.tolist() == [[0x21, 0x8F]]
+    np.testing.assert_array_equal(Q.unpack_nibbles(packed), codes)
+
+
+# ------------------------------------------------------------ bounds ----
+def test_window_envelopes_reproduce_page_offsets():
+    """Offsets +7, -3, -8 are the bit-pattern envelopes of 12/7, 4/5 and 1/2
+    of the base ("Resumo Técnico: ScaleSweep", 2. Limites Teóricos)."""
+    assert study.pattern_window_envelope(0.8, 12 / 7) == (-3, 7)
+    assert study.pattern_window_envelope(0.5, 12 / 7) == (-8, 7)
+
+
+def _blocks(kind, n, rng):
+    if kind == "normal":
+        u = rng.standard_normal((n, 16))
+    elif kind == "t4":
+        u = rng.standard_t(4, (n, 16))
+    elif kind == "laplace":
+        u = rng.laplace(0, 1, (n, 16))
+    elif kind == "outlier":
+        u = rng.standard_normal((n, 16))
+        u[:, 3] *= 20
+    return np.abs(u)
+
+
+def _block_base_t(u):
+    return u.max(axis=-1) / 6.0
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "laplace", "outlier"])
+def test_lemma41_scale_above_12_7_never_beats_half(kind):
+    """Lemma 4.1: for s > 12/7 * (block max / 6), loss(s) >= loss(s / 2),
+    for any non-negative weights; checked in float64 on every E4M3 pattern p
+    whose half is the pattern p - 8."""
+    rng = np.random.default_rng(11)
+    u = _blocks(kind, 400, rng) * rng.uniform(0.05, 40, (400, 1))
+    w = np.exp(rng.standard_normal(u.shape) * 2)
+    t = _block_base_t(u)
+    V = F.E4M3_VALUES64
+    pats = np.arange(16, 127)                      # V[p - 8] == V[p] / 2 exactly
+    assert np.all(V[pats - 8] * 2 == V[pats])
+    L_hi = study.block_loss64(u, np.broadcast_to(V[pats], (400, pats.size)), w)
+    L_half = study.block_loss64(u, np.broadcast_to(V[pats - 8], (400, pats.size)), w)
+    above = V[pats][None, :] > (12.0 / 7.0) * t[:, None]
+    assert np.all(L_hi[above] >= L_half[above])
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "laplace", "outlier"])
+def test_exhaustive_float64_optimum_in_window(kind):
+    """Exhaustive sweep over all 126 E4M3 scales (float64): the MSE optimum
+    lies in [-3, +7] around the AbsMax base (Lemmas 4.1 and 4.3); with any
+    non-negative weights it is never above +7."""
+    rng = np.random.default_rng(12)
+    n = 1500
+    u = _blocks(kind, n, rng) * np.exp(rng.uniform(np.log(0.01), np.log(50), (n, 1)))
+    base = np.maximum(F.e4m3_rne_pattern((u.max(-1) / 6.0).astype(np.float32)), 1)
+    # the lemmas are stated for scales whose halves and 4/5 are on the E4M3
+    # grid's geometric part: keep normal bases (pattern >= 8)
+    normal = base >= 8
+    u, base = u[normal], base[normal]
+    assert u.shape[0] > 1000
+    best, _ = study.exhaustive_best_pattern64(u)
+    off = best - base
+    assert off.min() >= -3 and off.max() <= 7
+    w = np.exp(2 * rng.standard_normal(u.shape))
+    best_w, _ = study.exhaustive_best_pattern64(u, w)
+    assert (best_w - base).max() <= 7
+
+
+def test_subnormal_base_can_leave_the_window():
+    """Below 2**-6 the E4M3 patterns are evenly spaced, so +7 patterns no
+    longer reach 12/7 of the base and s/2 may be off the grid: the bounded
+    window is still what the method evaluates, and the exhaustive optimum can
+    lie above it.  Pinned on one hand-checked block."""
+    u = np.zeros((1, 16))
+    u[0, 0] = 0.0625          # t = u_max / 6 = 0.0104 -> base pattern 5 (5 * 2**-9)
+    u[0, 1:] = 0.0439453125    # 1.5 * V[15]: exact at pattern 15, off-grid below it
+    base = int(F.e4m3_rne_pattern(np.float32(0.0625 / 6)))
+    assert base == 5
+    best, L = study.exhaustive_best_pattern64(u)
+    assert best[0] == 15 and best[0] - base > 7
+
+
+def test_exhaustive_canonical_fp32_matches_window():
+    """The oracle's own float32 sweep, run over every E4M3 pattern, picks an
+    MSE optimum inside [-3, +7] and the same pattern as the bounded window;
+    for WMSE the optimum is never above +7 (the -8 lower end is empirical and
+    only reported)."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_t(4, (64, 256)).astype(np.float32) * 0.02
+    x[rng.random(x.shape) < 0.003] *= 25
+    full = Q.quantize_nvfp4(x, window=(-126, 126))
+    win = Q.quantize_nvfp4(x, window=(-3, 7))
+    assert full.offsets.min() >= -3 and full.offsets.max() <= 7
+    np.testing.assert_array_equal(full.scales, win.scales)
+    np.testing.assert_array_equal(full.codes, win.codes)
+    w = np.exp(2 * rng.standard_normal(256)).astype(np.float32)
+    full_w = Q.quantize_nvfp4(x, importance=w, window=(-126, 126))
+    assert full_w.offsets.max() <= 7
+    below = np.mean(full_w.offsets < -8)
+    assert below < 0.05   # reported: the WMSE lower end is an empirical bound
+
+
+def test_sweep_never_worse_than_absmax():
+    rng = np.random.default_rng(14)
+    x = rng.laplace(0, 0.02, (32, 512)).astype(np.float32)
+    w = np.exp(rng.standard_normal(512)).astype(np.float32)
+    for imp in (None, w):
+        s = Q.quantize_nvfp4(x, importance=imp)
+        a = Q.quantize_nvfp4(x, importance=imp, window=(0, 0))
+        assert np.all(s.block_loss <= a.block_loss)
+        assert np.all(a.offsets == 0)
+    m = Q.quantize_mxfp4(x)
+    ma = Q.quantize_mxfp4(x, window=(0, 0))
+    assert np.all(m.block_loss <= ma.block_loss)
+
+
+# ------------------------------------------------------- global scale ----
+def test_global_scale_closed_form_and_max_block_base():
+    rng = np.random.default_rng(15)
+    x = (rng.standard_normal((16, 64)) * 0.02).astype(np.float32)
+    x[3, 17] = -0.9
+    r = Q.quantize_nvfp4(x)
+    assert r.global_scale == np.float32(np.float32(0.9) / np.float32(1536))
+    assert abs(float(r.global_scale) - 0.9 / (256 * 6)) <= 1e-7 * 0.9 / 1536
+    assert r.base[3, 1] == 0x78        # the tensor maximum lands on 256 = 0x78
+    assert r.scales[3, 1] <= 0x7E      # window clipped at the largest finite E4M3
+
+
+# ---------------------------------------------------- consistency pins ----
+def _dequant_independent_nvfp4(codes, scales, S):
+    c = Q.unpack_nibbles(codes)
+    sign = np.where(c >> 3, -1.0, 1.0)
+    mag = F.E2M1_VALUES.astype(np.float64)[c & 7]
+    pats = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).double().numpy()
+    return sign * mag * np.repeat(pats, 16, axis=-1) * float(S)
+
+
+@pytest.mark.parametrize("wmse", [False, True])
+def test_loss_matches_float64_reconstruction(wmse):
+    """sum_i w_i (x_i - x_hat_i)**2 recomputed in float64 from the codes and
+    scales (decoded with torch's FP8 table) matches the reported block loss
+    normwise; catches sign, nibble, importance-column and scale mix-ups."""
+    rng = np.random.default_rng(16)
+    x = (rng.standard_t(4, (48, 320)) * 0.02).astype(np.float32)
+    imp = np.exp(rng.standard_normal(320)).astype(np.float32) if wmse else None
+    r = Q.quantize_nvfp4(x, importance=imp)
+    xh = _dequant_independent_nvfp4(r.codes, r.scales, r.global_scale)
+    err = (x.astype(np.float64) - xh) ** 2
+    if wmse:
+        err = err * imp.astype(np.float64)[None, :]
+    ref = err.reshape(48, 20, 16).sum(-1)
+    rel = np.linalg.norm(ref - r.block_loss) / np.linalg.norm(ref)
+    assert rel <= 1e-5
+    np.testing.assert_allclose(Q.dequantize_nvfp4(r.codes, r.scales, r.global_scale), xh, rtol=1e-6, atol=0)
+
+
+def test_choice_is_float64_argmin_up_to_rounding():
+    """The chosen pattern's float64 loss is within float32 rounding of the
+    float64 minimum over the window."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    imp = np.exp(rng.standard_normal(256)).astype(np.float32)
+    r = Q.quantize_nvfp4(x, importance=imp)
+    S = float(r.global_scale)
+    u = np.abs(x.astype(np.float64)) / S
+    ub = u.reshape(40, 16, 16)
+    w = imp.astype(np.float64).reshape(16, 16)
+    for o in range(-8, 8):
+        p = np.clip(r.base + o, 1, 126)
+        L = study.block_loss64(ub, F.E4M3_VALUES64[p][..., None], np.broadcast_to(w, ub.shape))[..., 0]
+        Lbest = study.block_loss64(ub, F.E4M3_VALUES64[r.scales.astype(np.int64)][..., None],
+                                   np.broadcast_to(w, ub.shape))[..., 0]
+        assert np.all(Lbest <= L * (1 + 1e-5) + 1e-30)
+
+
+def test_codes_are_nearest_grid_points():
+    rng = np.random.default_rng(18)
+    x = (rng.laplace(0, 0.02, (20, 160))).astype(np.float32)
+    r = Q.quantize_nvfp4(x)
+    S = float(r.global_scale)
+    c = Q.unpack_nibbles(r.codes).astype(np.int64)
+    V = np.repeat(F.E4M3_VALUES64[r.scales.astype(np.int64)], 16, axis=-1)
+    y = np.abs(x.astype(np.float64)) / S / V
+    q = F.E2M1_VALUES.astype(np.float64)[c & 7]
+    dist = np.abs(y[..., None] - F.E2M1_VALUES.astype(np.float64))
+    assert np.all(np.abs(y - q) <= dist.min(-1) + 1e-5)
+    assert np.all((c >> 3) == np.signbit(x))
+
+
+# ------------------------------------------------------ special cases ----
+def test_exact_grid_block_has_zero_loss():
+    S = np.float32(1.0)
+    V = F.E4M3_VALUES[0x40]                      # 2.0
+    x = np.zeros((1, 16), dtype=np.float32)
+    x[0, :8] = np.float32([6, 4, 3, 2, 1.5, 1, 0.5, 0]) * V * S
+    x[0, 8:] = -x[0, :8]
+    r = Q.quantize_nvfp4(x, global_scale=S)
+    assert r.base[0, 0] == 0x40 and r.block_loss[0, 0] == 0 and r.offsets[0, 0] == 0
+    np.testing.assert_array_equal(Q.dequantize_nvfp4(r.codes, r.scales, S), x)
+
+
+def test_zero_tensor_and_zero_importance():
+    z = np.zeros((3, 32), dtype=np.float32)
+    r = Q.quantize_nvfp4(z)
+    assert r.global_scale == 0
+    assert np.all(r.scales == 1) and np.all(r.block_loss == 0) and np.all(r.offsets == 0)
+    z[0, 0] = -0.0
+    assert Q.unpack_nibbles(Q.quantize_nvfp4(z).codes)[0, 0] == 0x8   # sign of -0.0 kept
+    rng = np.random.default_rng(19)
+    x = (rng.standard_normal((4, 32)) * 0.02).astype(np.float32)
+    imp = np.ones(32, dtype=np.float32)
+    imp[16:] = 0
+    r = Q.quantize_nvfp4(x, importance=imp)
+    # a block whose weights are all zero ties at 0: the lowest window pattern wins
+    np.testing.assert_array_equal(r.scales[:, 1], np.maximum(r.base[:, 1] - 8, 1))
+
+
+def test_mxfp4_absmax_never_clips():
+    rng = np.random.default_rng(20)
+    x = rng.laplace(0, 1, (64, 256)).astype(np.float32)
+    m = Q.quantize_mxfp4(x, window=(0, 0))
+    E = m.scales.astype(np.int64) - 127
+    y = np.abs(x.astype(np.float64)).reshape(64, 8, 32) / np.ldexp(1.0, E)[..., None]
+    assert y.max() <= 6.0
+    xh = Q.dequantize_mxfp4(m.codes, m.scales)
+    ref = np.abs(x.astype(np.float64) - xh) ** 2
+    np.testing.assert_allclose(ref.reshape(64, 8, 32).sum(-1), m.block_loss, rtol=2e-5)
+
+
+# ----------------------------------------------------------- Hadamard ----
+@pytest.mark.parametrize("n", [2, 16, 32, 128])
+def test_sylvester_matrix(n):
+    import scipy.linalg
+    h = H.sylvester(n)
+    np.testing.assert_array_equal(h, scipy.linalg.hadamard(n))
+    np.testing.assert_array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("n", [16, 32, 128])
+def test_fwht_matches_dense_and_is_orthonormal(n):
+    rng = np.random.default_rng(21)
+    x = rng.laplace(0, 1, (8, 512)).astype(np.float32)
+    z = H.block_hadamard(x, n)
+    ref = H.block_hadamard_dense64(x, n)
+    assert np.max(np.abs(z - ref)) <= 1e-6 * np.max(np.abs(ref))
+    g = lambda a: a.reshape(8, 512 // n, n)
+    np.testing.assert_allclose(np.linalg.norm(g(z.astype(np.float64)), axis=-1),
+                               np.linalg.norm(g(x.astype(np.float64)), axis=-1), rtol=1e-5)
+    np.testing.assert_allclose(H.block_hadamard(z, n), x, atol=1e-5 * np.abs(x).max())
+    # one-hot rows give a row of the normalized Hadamard matrix
+    e = np.zeros((n, n), dtype=np.float32)
+    np.fill_diagonal(e, 1)
+    np.testing.assert_allclose(H.block_hadamard(e, n), H.sylvester(n) / math.sqrt(n), rtol=1e-7)
+
+
+def test_scale_constants():
+    assert H.hadamard_scale_f32(16) == np.float32(0.25)
+    assert abs(float(H.hadamard_scale_f32(32)) * math.sqrt(32) - 1) < 1e-7
