@@ -1,0 +1,245 @@
+"""Throughput of the FP4 block quantizer on one MI355X.
+
+One step = one pass of the hot path over one batch: the global max pass and
+the NVFP4 ScaleSweep (WMSE, window [-8, +7]) over a bf16 4096 x 4096 weight
+with per-column importance, i.e. everything fp4q_quantize_nvfp4 does.
+
+Prints ONE JSON line.  ``value`` is quantized elements per second (G/s) with
+the inputs already resident in HBM; ten distinct input buffers (320 MiB, more
+than the 256 MB Infinity Cache) are rotated so every step reads HBM.
+
+The ``roofline`` object is for the dominant kernel (the sweep), timed alone
+with HIP events on the stream it runs on (a call with a given global scale
+launches exactly that kernel).  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload on this host.
+
+Other workloads (for the design notes, not the headline line) are selected
+with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
+c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
+c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# one fp32 VALU operation per lane per clock: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+METRIC = "G elements/s quantized (NVFP4 WMSE sweep) + % of MI355X HBM roofline"
+
+
+def _alg_ops_per_element(n_cand, wmse, had=0):
+    """Algorithmic fp32 operations per element: per candidate a scale
+    multiply, E2M1 rounding, dequant multiply, subtract, square, [weight
+    multiply] and one tree add; a Hadamard adds log2(n) butterflies + 1."""
+    per_cand = 7 if wmse else 6
+    return n_cand * per_cand + (int(math.log2(had)) + 1 if had else 0)
+
+
+def _alg_bytes_per_element(in_bytes, block):
+    # read x, write 4-bit codes, per block 1 B scale + 4 B loss + 1 B offset
+    return in_bytes + 0.5 + 6.0 / block
+
+
+def _events_time(fn, iters):
+    import torch
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def _rotating_copies(x, min_bytes=300 * 2**20, min_count=10):
+    import torch
+    nbytes = x.numel() * x.element_size()
+    n = max(min_count, math.ceil(min_bytes / nbytes))
+    if n * nbytes > 40 * 2**30:
+        n = max(2, (40 * 2**30) // nbytes)
+    bufs = [x]
+    for _ in range(n - 1):
+        bufs.append(torch.empty_like(x).copy_(x))
+    return bufs
+
+
+def cpu_baseline(x_cpu, imp, sample_rows, window=None, had=0, fmt="nvfp4"):
+    """The CPU oracle (numpy, one core) on the first ``sample_rows`` rows."""
+    from oracle import quant as Q
+    xs = x_cpu[:sample_rows].float().numpy()
+    t0 = time.perf_counter()
+    if fmt == "nvfp4":
+        Q.quantize_nvfp4(xs, None if imp is None else imp.numpy(), window=window, hadamard_n=had)
+    else:
+        Q.quantize_mxfp4(xs, window=window, hadamard_n=had)
+    dt = time.perf_counter() - t0
+    return {"value": xs.size / dt / 1e9, "unit": "G elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {sample_rows} rows ({xs.size} elements) of the same workload, "
+                      f"{dt:.1f} s single-threaded numpy"}
+
+
+def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
+    """Time the full call (max pass + sweep) and the sweep kernel alone."""
+    import torch
+    import fp4_post_quantization_amd as fq
+    bufs = _rotating_copies(x)
+    out = fq.quantize_nvfp4(bufs[0], imp, window=window, hadamard_n=had)
+    ws = fq.workspace(x.device)
+    fq.clear_status(ws)
+    step = lambda i: fq.quantize_nvfp4(bufs[i % len(bufs)], imp, window=window, hadamard_n=had, out=out, ws=ws)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = _events_time(step, steps)
+    # out.global_scale now holds S; passing it back launches the sweep kernel only
+    sweep = lambda i: fq.quantize_nvfp4(bufs[i % len(bufs)], imp, window=window, hadamard_n=had,
+                                        global_scale=out.global_scale, out=out, ws=ws)
+    for i in range(warmup):
+        sweep(i)
+    ms_sweep = _events_time(sweep, steps)
+    torch.cuda.synchronize()
+    status = fq.read_status(ws)
+    if status:
+        raise RuntimeError(f"device reported data error 0x{status:x}")
+    return ms_step, ms_sweep
+
+
+def run_c2(args):
+    import torch
+    import workloads as W
+    x_cpu, imp_cpu = W.c2_weight_and_importance()
+    x = x_cpu.to("cuda:0")
+    imp = imp_cpu.to("cuda:0")
+    rows, cols = x.shape
+    n = rows * cols
+    window = (-8, 7)
+    ms_step, ms_sweep = bench_nvfp4_matrix(x, imp, window, 0, args.steps, args.warmup)
+    value = n / (ms_step * 1e-3) / 1e9
+    ops = _alg_ops_per_element(16, True)
+    byts = _alg_bytes_per_element(2, 16)
+    achieved_tops = ops * n / (ms_sweep * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "G elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "NVFP4 WMSE ScaleSweep, bf16 weight 4096x4096 (Student-t nu=4, std 0.02), "
+                               "importance = Gram diagonal of 512x4096 lognormal-scaled activations, "
+                               "block 16, E4M3 offsets [-8,+7]",
+                   "rows": rows, "cols": cols, "input_dtype": "bf16", "block": 16, "window": list(window)},
+        "hbm": {"alg_bytes_per_element": byts, "achieved_GBs": round(byts * n / (ms_step * 1e-3) / 1e9, 1),
+                "peak_GBs": HBM_PEAK_GBS,
+                "frac": round(byts * n / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "nvfp4_sweep_kernel<bf16, WMSE, no rotation>", "bound": "alu",
+                     "achieved": round(achieved_tops, 3), "peak": round(VALU_PEAK_TOPS, 2), "unit": "TFLOP/s",
+                     "frac": round(achieved_tops / VALU_PEAK_TOPS, 4), "traffic": None,
+                     "alg_ops_per_element": ops, "elements_per_launch": n,
+                     "kernel_ms": round(ms_sweep, 5)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x_cpu, imp_cpu, args.cpu_rows, window=window)
+    return line
+
+
+def run_other(args):
+    """Side measurements for the design notes (not the headline)."""
+    import torch
+    import fp4_post_quantization_amd as fq
+    import workloads as W
+    res = {"config": args.config}
+    if args.config == "c1":
+        x = W.c1_weight().to("cuda:0")
+        ms, msw = bench_nvfp4_matrix(x, None, (-3, 7), 0, args.steps, args.warmup)
+        res.update(elements=x.numel(), ms_step=ms, ms_sweep=msw, gel_s=x.numel() / ms / 1e6)
+    elif args.config.startswith("c3"):
+        x = W.c3_activation().to("cuda:0")
+        window = (0, 0) if args.config == "c3a" else (-1, 0)
+        had = 32 if args.config == "c3c" else 0
+        bufs = _rotating_copies(x)
+        out = fq.quantize_mxfp4(bufs[0], window=window, hadamard_n=had)
+        step = lambda i: fq.quantize_mxfp4(bufs[i % len(bufs)], window=window, hadamard_n=had, out=out)
+        for i in range(args.warmup):
+            step(i)
+        ms = _events_time(step, args.steps)
+        byts = _alg_bytes_per_element(2, 32)
+        res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6,
+                   hbm_GBs=byts * x.numel() / ms / 1e6, hbm_frac=byts * x.numel() / ms / 1e6 / HBM_PEAK_GBS)
+    elif args.config == "c4":
+        total_ms = {"mse": 0.0, "wmse": 0.0}
+        n = 0
+        for name in W.LAYER_8B:
+            x = W.c4_matrix(name).to("cuda:0")
+            imp = W.c4_importance(name).to("cuda:0")
+            n += x.numel()
+            for loss, im, win in (("mse", None, (-3, 7)), ("wmse", imp, (-8, 7))):
+                ms, _ = bench_nvfp4_matrix(x, im, win, 0, max(3, args.steps // 5), 2)
+                total_ms[loss] += ms
+            del x
+            torch.cuda.empty_cache()
+        res.update(elements=n, ms_layer=total_ms, gel_s={k: n / v / 1e6 for k, v in total_ms.items()})
+    elif args.config == "c5":
+        imps = {name: W.c5_importance(name).to("cuda:0") for name in W.LAYER_70B}
+        out_ms = 0.0
+        n = 0
+        for layer in range(args.layers):
+            for name in W.LAYER_70B:
+                x = W.c5_matrix(layer, name, "cuda:0")
+                torch.cuda.synchronize()
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                fq.quantize_nvfp4(x, imps[name], hadamard_n=16)
+                e.record()
+                e.synchronize()
+                out_ms += s.elapsed_time(e)
+                n += x.numel()
+                del x
+            print(f"layer {layer} done, {n / out_ms / 1e6:.1f} G el/s so far", file=sys.stderr, flush=True)
+        res.update(layers=args.layers, elements=n, ms_total=out_ms, gel_s=n / out_ms / 1e6)
+    else:
+        raise SystemExit(f"unknown config {args.config}")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this quantizer runs on a single MI355X "
+              "(no sharding or collectives are built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    line = run_c2(args) if args.config == "c2" else run_other(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

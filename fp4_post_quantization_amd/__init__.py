@@ -1,0 +1,219 @@
+"""fp4_post_quantization_amd -- FP4 microscaling block quantization with
+block-scale search on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/fp4q.h (libfp4q.so, built in
+place).  It only marshals arguments: torch supplies device memory and the
+current HIP stream, and every step of the computation runs in the library's
+HIP kernels.  There is no CPU fallback; a missing library raises.
+
+    quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, ...)
+    quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, ...)
+    dequantize(fmt, codes, scales, global_scale=None)
+    block_hadamard(x, n)
+"""
+
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib as L
+from ._lib import FP4QError  # noqa: F401
+
+__all__ = [
+    "quantize_nvfp4", "quantize_mxfp4", "dequantize", "block_hadamard",
+    "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
+]
+
+
+class NVFP4Result(NamedTuple):
+    codes: torch.Tensor         # uint8 [R, C/2] packed E2M1 codes
+    scales: torch.Tensor        # uint8 [R, C/16] E4M3 block-scale patterns
+    global_scale: torch.Tensor  # float32 [1]
+    block_loss: Optional[torch.Tensor]  # float32 [R, C/16]
+    offsets: Optional[torch.Tensor]     # int8 [R, C/16]
+
+
+class MXFP4Result(NamedTuple):
+    codes: torch.Tensor         # uint8 [R, C/2]
+    scales: torch.Tensor        # uint8 [R, C/32] E8M0 bytes
+    block_loss: Optional[torch.Tensor]  # float32 [R, C/32]
+    offsets: Optional[torch.Tensor]     # int8 [R, C/32]
+
+
+_WORKSPACES = {}
+
+
+def workspace(device=None):
+    """The per-device workspace used when none is passed (calls that overlap
+    on one device through this shared workspace race; pass your own)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    ws = _WORKSPACES.get(device.index)
+    if ws is None:
+        ws = torch.zeros(L.load().fp4q_workspace_bytes(), dtype=torch.uint8, device=device)
+        _WORKSPACES[device.index] = ws
+    return ws
+
+
+def read_status(ws):
+    """Device status word (FP4Q_DATA_* bits, sticky until cleared) after the
+    stream has finished."""
+    return int(ws[:4].view(torch.int32).item())
+
+
+def clear_status(ws):
+    ws[:4].zero_()
+
+
+def _check_data(ws):
+    torch.cuda.current_stream(ws.device).synchronize()
+    st = read_status(ws)
+    if st:
+        clear_status(ws)
+        names = []
+        if st & L.DATA_NONFINITE_INPUT:
+            names.append("non-finite input")
+        if st & L.DATA_BAD_IMPORTANCE:
+            names.append("negative or non-finite importance")
+        if st & L.DATA_BAD_GLOBAL_SCALE:
+            names.append("invalid global scale")
+        raise FP4QError("data error: " + ", ".join(names))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return L.F32
+    if t.dtype == torch.bfloat16:
+        return L.BF16
+    raise TypeError(f"x must be float32 or bfloat16, got {t.dtype}")
+
+
+def _matrix(x):
+    if x.dim() != 2:
+        raise ValueError("x must be a 2-D row-major matrix")
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    if x.stride(1) != 1 and x.size(1) > 1:
+        x = x.contiguous()
+    ld = x.stride(0) if x.size(0) > 1 else x.size(1)
+    return x, max(ld, x.size(1))
+
+
+def _stream(device):
+    return ctypes_ptr(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ctypes_ptr(v):
+    return None if v is None else int(v)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _importance(importance, cols, device):
+    if importance is None:
+        return None
+    imp = torch.as_tensor(importance, dtype=torch.float32, device=device).contiguous()
+    if imp.numel() != cols:
+        raise ValueError("importance must have one entry per column")
+    return imp
+
+
+def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=None, *,
+                   out=None, with_loss=True, with_offsets=True, ws=None, check=False):
+    """NVFP4 ScaleSweep quantization of a 2-D float32/bfloat16 device tensor.
+
+    importance: per-column weights -> WMSE (default window (-8, 7)); None ->
+    MSE (default window (-3, 7)).  global_scale: a given S (float or [1]
+    tensor; passing ``out.global_scale`` itself copies nothing) instead of
+    max|x|/1536.  out: a preallocated NVFP4Result to write into.  check: synchronize and raise on data errors.
+    """
+    lib = L.load()
+    x, ld = _matrix(x)
+    rows, cols = x.shape
+    dev = x.device
+    imp = _importance(importance, cols, dev)
+    loss = L.WMSE if imp is not None else L.MSE
+    if window is None:
+        window = (-8, 7) if imp is not None else (-3, 7)
+    if out is None:
+        out = NVFP4Result(
+            codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+            global_scale=torch.empty(1, dtype=torch.float32, device=dev),
+            block_loss=torch.empty((rows, cols // 16), dtype=torch.float32, device=dev) if with_loss else None,
+            offsets=torch.empty((rows, cols // 16), dtype=torch.int8, device=dev) if with_offsets else None,
+        )
+    flags = 0
+    if global_scale is not None:
+        same = isinstance(global_scale, torch.Tensor) and global_scale.data_ptr() == out.global_scale.data_ptr()
+        if not same:
+            out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
+        flags |= L.GIVEN_SCALE
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_quantize_nvfp4(
+        x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 16, loss, int(window[0]), int(window[1]),
+        int(hadamard_n), flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
+        _ptr(out.block_loss), _ptr(out.offsets), ws.data_ptr(), ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
+
+
+def quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, *, out=None, with_loss=True,
+                   with_offsets=True, ws=None, check=False):
+    """MXFP4 quantization (E8M0 scales, blocks of 32) with an exponent-window
+    search; window (0, 0) is the AbsMax rule."""
+    lib = L.load()
+    x, ld = _matrix(x)
+    rows, cols = x.shape
+    dev = x.device
+    imp = _importance(importance, cols, dev)
+    loss = L.WMSE if imp is not None else L.MSE
+    if out is None:
+        out = MXFP4Result(
+            codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+            block_loss=torch.empty((rows, cols // 32), dtype=torch.float32, device=dev) if with_loss else None,
+            offsets=torch.empty((rows, cols // 32), dtype=torch.int8, device=dev) if with_offsets else None,
+        )
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_quantize_mxfp4(
+        x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 32, loss, int(window[0]), int(window[1]),
+        int(hadamard_n), out.codes.data_ptr(), out.scales.data_ptr(), _ptr(out.block_loss),
+        _ptr(out.offsets), ws.data_ptr(), ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
+
+
+def dequantize(fmt, codes, scales, global_scale=None, out=None):
+    """Decode packed codes and block scales to float32 ([R, C])."""
+    lib = L.load()
+    fmt_code = {"nvfp4": L.NVFP4, "mxfp4": L.MXFP4}[fmt]
+    block = 16 if fmt_code == L.NVFP4 else 32
+    rows, half = codes.shape
+    cols = half * 2
+    dev = codes.device
+    codes = codes.contiguous()
+    scales = scales.contiguous()
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    gs = None
+    if fmt_code == L.NVFP4:
+        gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1)
+    L.check(lib.fp4q_dequantize(fmt_code, codes.data_ptr(), scales.data_ptr(), _ptr(gs), rows, cols, block,
+                                out.data_ptr(), _stream(dev)))
+    return out
+
+
+def block_hadamard(x, n, out=None):
+    """Rotate each row's n-column groups by H_n / sqrt(n) (float32 output)."""
+    lib = L.load()
+    x, ld = _matrix(x)
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    L.check(lib.fp4q_block_hadamard(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(n), out.data_ptr(),
+                                    _stream(x.device)))
+    return out

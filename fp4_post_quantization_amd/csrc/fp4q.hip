@@ -1,0 +1,632 @@
+// fp4q: FP4 microscaling block quantization with block-scale search for
+// gfx950 (MI355X).  Kernels and the C ABI declared in include/fp4q.h.
+//
+// Work decomposition (all kernels): a lane owns 16 contiguous elements of a
+// row ("chunk"); an NVFP4 block is one lane, an MXFP4 block two adjacent
+// lanes, an n-point Hadamard group n/16 adjacent lanes.  Block losses are
+// reduced inside the lane (plus one DPP exchange for MXFP4), so the
+// candidate sweep needs no LDS and no barriers.
+//
+// The quantize kernels map a wave to a tile of 64 consecutive chunks of a
+// column band times a few rows; the per-column importance of WMSE is loaded
+// into registers once per tile and reused for every row.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "../../include/fp4q.h"
+#include "fp4q_device.h"
+
+namespace fp4q {
+
+// ============================================================ kernels ====
+
+// Global scale of an empty NVFP4 tensor (max over nothing = 0).
+__global__ void zero_scale_kernel(float *global_scale) { *global_scale = 0.0f; }
+
+// Per-workgroup maximum of |x| (after the optional rotation) as a float32
+// bit pattern.  Integer order of |bits| is float order for finite values,
+// and any Inf/NaN yields a pattern >= 0x7F800000.
+template <typename T, int HAD>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const T *__restrict__ x, int64_t ld, int cpr,
+                                                         int total, uint32_t *__restrict__ partials) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t m = 0;
+  const int stride = gridDim.x * kThreads;
+  for (int g = blockIdx.x * kThreads + threadIdx.x; g < total; g += stride) {
+    const int r = g / cpr, c = g - r * cpr;
+    float z[16];
+    load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
+    if constexpr (HAD != 0) fwht<HAD>(z, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b = as_u(z[i]) & 0x7FFFFFFFu;
+      m = b > m ? b : m;
+    }
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[kWaves];
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
+    partials[blockIdx.x] = r;
+  }
+}
+
+struct SweepArgs {
+  const void *x;
+  int64_t ld;
+  int rows, cols, cpr;          // cpr = chunks (16 columns) per row
+  const float *imp;             // [cols] or null
+  int off_lo, off_hi;
+  int rows_per_tile, nbands, ntiles;
+  const uint32_t *partials;     // amax partials (NVFP4, computed scale)
+  int n_partials;
+  const float *given_scale;     // NVFP4 with FP4Q_GIVEN_SCALE, else null
+  uint8_t *codes, *scales;
+  float *gscale_out;            // NVFP4 global scale output (computed scale)
+  float *loss;
+  int8_t *offs;
+  uint32_t *status;
+};
+
+__device__ __forceinline__ void load_importance(const float *p, float w[16]) {
+  const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 v = q[k];
+    w[4 * k] = v.x;
+    w[4 * k + 1] = v.y;
+    w[4 * k + 2] = v.z;
+    w[4 * k + 3] = v.w;
+  }
+}
+
+__device__ __forceinline__ bool importance_ok(const float w[16]) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ok &= (w[i] >= 0.0f) & (w[i] <= 3.402823466e38f);
+  return ok;
+}
+
+// Loss of one candidate scale over this lane's 16 elements:
+// tree of fp32(e*e) [* w] with e = fp32(u - q*V), q = E2M1(fp32(u*R)).
+// q*V is exact, so fmaf(-q, V, u) is exactly fp32(u - q*V).
+template <bool WMSE>
+__device__ __forceinline__ float lane_loss(const float u[16], const float w[16], float V, float R) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = e2m1_round(u[i] * R);
+    const float e = fmaf(-q, V, u[i]);
+    const float s = e * e;
+    t[i] = WMSE ? w[i] * s : s;
+  }
+  return tree16(t);
+}
+
+// Packed codes of this lane's 16 elements for the chosen candidate.
+__device__ __forceinline__ uint2 lane_codes(const float u[16], uint32_t sgn, float R) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c0 = e2m1_index(e2m1_round(u[i] * R)) | (((sgn >> i) & 1u) << 3);
+    const uint32_t c1 = e2m1_index(e2m1_round(u[i + 8] * R)) | (((sgn >> (i + 8)) & 1u) << 3);
+    lo |= c0 << (4 * i);
+    hi |= c1 << (4 * i);
+  }
+  return make_uint2(lo, hi);
+}
+
+// NVFP4 ScaleSweep: one lane per 16-element block.
+template <typename T, bool WMSE, int HAD>
+__global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
+  __shared__ float Vtab[128], Rtab[128];
+  __shared__ uint32_t red[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (tid < 128) {
+    const float v = (tid >= 1 && tid <= 126) ? e4m3_value(tid) : 1.0f;
+    Vtab[tid] = v;
+    Rtab[tid] = 1.0f / v;  // correctly rounded division
+  }
+  uint32_t amax_bits = 0;
+  if (!a.given_scale) {
+    for (int i = tid; i < a.n_partials; i += kThreads) {
+      const uint32_t p = a.partials[i];
+      amax_bits = p > amax_bits ? p : amax_bits;
+    }
+    amax_bits = wave_max_u32(amax_bits);
+    if (lane == 0) red[wave] = amax_bits;
+  }
+  __syncthreads();
+  float S;
+  if (a.given_scale) {
+    S = *a.given_scale;
+    if (blockIdx.x == 0 && tid == 0 && (!(S >= 0.0f) || isinf(S)))
+      atomicOr(a.status, FP4Q_DATA_BAD_GLOBAL_SCALE);
+  } else {
+    amax_bits = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) amax_bits = red[i] > amax_bits ? red[i] : amax_bits;
+    S = as_f(amax_bits) / 1536.0f;  // max|x| / (256 * 6), correctly rounded
+    if (blockIdx.x == 0 && tid == 0) {
+      *a.gscale_out = S;
+      if (amax_bits >= 0x7F800000u) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    }
+  }
+  const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
+  const float SS = S * S;
+
+  const int tile = blockIdx.x * kWaves + wave;
+  if (tile >= a.ntiles) return;
+  const int band = tile % a.nbands, rg = tile / a.nbands;
+  const int c = band * 64 + lane;
+  const bool active = c < a.cpr;
+  const int r0 = rg * a.rows_per_tile;
+  const int r1 = min(a.rows, r0 + a.rows_per_tile);
+
+  float w[16];
+  if constexpr (WMSE) {
+    if (active) {
+      load_importance(a.imp + (int64_t)c * 16, w);
+      if (!importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+    }
+  }
+  if (!active) return;  // whole Hadamard groups are active or not together
+
+  const T *x = static_cast<const T *>(a.x);
+  const int bpr = a.cpr;  // blocks per row
+  for (int r = r0; r < r1; ++r) {
+    float z[16];
+    load16(x + (int64_t)r * a.ld + (int64_t)c * 16, z);
+    if constexpr (HAD != 0) fwht<HAD>(z, lane);
+
+    float u[16];
+    uint32_t sgn = 0;
+    float amax = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sgn |= (as_u(z[i]) >> 31) << i;
+      finite &= fabsf(z[i]) <= 3.402823466e38f;
+      u[i] = fabsf(z[i]) * S_inv;
+      amax = fmaxf(amax, u[i]);
+    }
+    // with a computed scale the global-max pass already reported non-finite x
+    if (a.given_scale && !finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    const float t = amax / 6.0f;  // correctly rounded
+    int base = e4m3_rne_sat(t);
+    base = base < 1 ? 1 : base;
+    const int plo = max(1, base + a.off_lo);
+
+    float Lbest = 0.0f;
+    int pbest = plo;
+    for (int o = a.off_lo; o <= a.off_hi; ++o) {
+      const int p = base + o;
+      const bool ok = (p >= 1) & (p <= 126);
+      const int pc = min(max(p, 1), 126);
+      const float L = lane_loss<WMSE>(u, w, Vtab[pc], Rtab[pc]);
+      const bool take = ok & ((p == plo) | (L < Lbest));
+      Lbest = take ? L : Lbest;
+      pbest = take ? p : pbest;
+    }
+
+    const uint2 pk = lane_codes(u, sgn, Rtab[pbest]);
+    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = pk;
+    const int64_t bi = (int64_t)r * bpr + c;
+    a.scales[bi] = (uint8_t)pbest;
+    if (a.loss) a.loss[bi] = Lbest * SS;
+    if (a.offs) a.offs[bi] = (int8_t)(pbest - base);
+  }
+}
+
+// MXFP4 exponent sweep: two adjacent lanes per 32-element block.
+template <bool WMSE>
+__device__ __forceinline__ float lane_loss_pow2(const float u[16], const float w[16], float down, float up) {
+  float t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = e2m1_round(u[i] * down);
+    const float e = fmaf(-q, up, u[i]);  // q * 2^E is exact
+    const float s = e * e;
+    t[i] = WMSE ? w[i] * s : s;
+  }
+  return tree16(t);
+}
+
+template <typename T, bool WMSE, int HAD>
+__global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x * kWaves + wave;
+  if (tile >= a.ntiles) return;
+  const int band = tile % a.nbands, rg = tile / a.nbands;
+  const int c = band * 64 + lane;
+  const bool active = c < a.cpr;  // cpr is even: both lanes of a block agree
+  const int r0 = rg * a.rows_per_tile;
+  const int r1 = min(a.rows, r0 + a.rows_per_tile);
+
+  float w[16];
+  if constexpr (WMSE) {
+    if (active) {
+      load_importance(a.imp + (int64_t)c * 16, w);
+      if (!importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+    }
+  }
+  if (!active) return;
+
+  const T *x = static_cast<const T *>(a.x);
+  const int bpr = a.cpr / 2;
+  const bool even = (lane & 1) == 0;
+  for (int r = r0; r < r1; ++r) {
+    float z[16];
+    load16(x + (int64_t)r * a.ld + (int64_t)c * 16, z);
+    if constexpr (HAD != 0) fwht<HAD>(z, lane);
+
+    float u[16];
+    uint32_t sgn = 0;
+    float amax = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sgn |= (as_u(z[i]) >> 31) << i;
+      u[i] = fabsf(z[i]);
+      finite &= u[i] <= 3.402823466e38f;
+      amax = fmaxf(amax, u[i]);
+    }
+    if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    amax = fmaxf(amax, xor_lane<1>(amax));
+    const int eb = mx_base_exponent(amax);
+    const int elo = max(-127, eb + a.off_lo);
+
+    float Lbest = 0.0f;
+    int ebest = elo;
+    for (int o = a.off_lo; o <= a.off_hi; ++o) {
+      const int E = eb + o;
+      const bool ok = (E >= -127) & (E <= 127);
+      const int Ec = min(max(E, -127), 127);
+      const float half = lane_loss_pow2<WMSE>(u, w, pow2f(-Ec), pow2f(Ec));
+      const float L = half + xor_lane<1>(half);
+      const bool take = ok & ((E == elo) | (L < Lbest));
+      Lbest = take ? L : Lbest;
+      ebest = take ? E : ebest;
+    }
+
+    const uint2 pk = lane_codes(u, sgn, pow2f(-ebest));
+    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = pk;
+    if (even) {
+      const int64_t bi = (int64_t)r * bpr + (c >> 1);
+      a.scales[bi] = (uint8_t)(ebest + 127);
+      if (a.loss) a.loss[bi] = Lbest;
+      if (a.offs) a.offs[bi] = (int8_t)(ebest - eb);
+    }
+  }
+}
+
+// Decode of an arbitrary E4M3 byte (sign, 0x7F / 0xFF = NaN).
+__device__ __forceinline__ float e4m3_decode_any(uint32_t b) {
+  const uint32_t m = b & 0x7Fu;
+  float v = (m == 0x7Fu) ? __builtin_nanf("") : (m == 0 ? 0.0f : e4m3_value((int)m));
+  return (b & 0x80u) ? -v : v;
+}
+
+// Magnitude of an E2M1 code index 0..7.
+__device__ __forceinline__ float e2m1_magnitude(uint32_t idx) {
+  return idx < 2 ? 0.5f * (float)idx : as_f((((idx >> 1) + 126u) << 23) | ((idx & 1u) << 22));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            const float *__restrict__ gscale, int cpr,
+                                                            int cols, int total, float *__restrict__ out) {
+  const int g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const int r = g / cpr, c = g - r * cpr;
+  const uint2 pk = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)c * 8);
+  float scale, S = 1.0f;
+  if constexpr (FMT == FP4Q_NVFP4) {
+    scale = e4m3_decode_any(scales[(int64_t)r * cpr + c]);
+    S = *gscale;
+  } else {
+    const uint32_t b = scales[(int64_t)r * (cpr / 2) + (c >> 1)];
+    scale = (b == 255u) ? __builtin_nanf("") : pow2f((int)b - 127);
+  }
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = ((i < 8 ? pk.x : pk.y) >> (4 * (i & 7))) & 0xFu;
+    float mag = e2m1_magnitude(code & 7u) * scale;  // exact
+    if constexpr (FMT == FP4Q_NVFP4) mag = mag * S;
+    v[i] = (code & 8u) ? -mag : mag;
+  }
+  float4 *o = reinterpret_cast<float4 *>(out + (int64_t)r * cols + (int64_t)c * 16);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+}
+
+template <typename T, int HAD>
+__global__ __launch_bounds__(kThreads) void hadamard_kernel(const T *__restrict__ x, int64_t ld, int cpr,
+                                                             int cols, int total, float *__restrict__ out) {
+  const int g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;  // whole groups end together: total is a multiple of HAD/16
+  const int r = g / cpr, c = g - r * cpr;
+  float z[16];
+  load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
+  fwht<HAD>(z, threadIdx.x & 63);
+  float4 *o = reinterpret_cast<float4 *>(out + (int64_t)r * cols + (int64_t)c * 16);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+}
+
+// ============================================================ dispatch ===
+
+template <typename F>
+static void with_had(int n, F &&f) {
+  switch (n) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 16: f(std::integral_constant<int, 16>{}); break;
+    case 32: f(std::integral_constant<int, 32>{}); break;
+    case 64: f(std::integral_constant<int, 64>{}); break;
+    default: f(std::integral_constant<int, 128>{}); break;
+  }
+}
+
+template <typename F>
+static void with_dtype(fp4q_dtype_t dt, F &&f) {
+  if (dt == FP4Q_BF16) f((const uint16_t *)nullptr);
+  else f((const float *)nullptr);
+}
+
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Rows per wave tile: enough tiles to give every SIMD several waves.
+static int pick_rows_per_tile(int rows, int nbands) {
+  const int64_t target_tiles = 8192;
+  const int64_t units = (int64_t)rows * nbands;
+  int rpt = (int)((units + target_tiles - 1) / target_tiles);
+  return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);
+}
+
+}  // namespace fp4q
+
+// ============================================================ C ABI ======
+using namespace fp4q;
+
+extern "C" {
+
+int fp4q_version(void) { return 100; }
+
+const char *fp4q_status_string(fp4q_status_t s) {
+  switch (s) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_ERR_NULL: return "a required pointer is NULL";
+    case FP4Q_ERR_SHAPE: return "inconsistent shape (rows, cols, ld, block or Hadamard size)";
+    case FP4Q_ERR_ARG: return "invalid argument (dtype, loss, window, Hadamard size or flags)";
+    case FP4Q_ERR_ALIGN: return "misaligned pointer or row stride (16 bytes required)";
+    case FP4Q_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP4Q_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t fp4q_workspace_bytes(void) { return kWorkspaceBytes; }
+
+}  // extern "C"
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static fp4q_status_t check_matrix(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                  int block, int hadamard_n) {
+  if (dtype != FP4Q_F32 && dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32 && hadamard_n != 64 && hadamard_n != 128)
+    return FP4Q_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld < cols) return FP4Q_ERR_SHAPE;
+  if (cols % block) return FP4Q_ERR_SHAPE;
+  if (hadamard_n && cols % hadamard_n) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
+    return FP4Q_ERR_SHAPE;
+  const size_t esz = dtype == FP4Q_BF16 ? 2 : 4;
+  if (rows > 0 && cols > 0 && (!aligned(x, 16) || (ld * (int64_t)esz) % 16)) return FP4Q_ERR_ALIGN;
+  return FP4Q_OK;
+}
+
+static fp4q_status_t last_hip_status() {
+  return hipGetLastError() == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
+}
+
+extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                             int64_t ld, const float *importance, int block,
+                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
+                                             uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                             float *global_scale, float *block_loss, int8_t *offsets,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!global_scale || (!empty && (!x || !codes || !scales))) return FP4Q_ERR_NULL;
+  if (loss != FP4Q_MSE && loss != FP4Q_WMSE) return FP4Q_ERR_ARG;
+  if (loss == FP4Q_WMSE && !importance && !empty) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (block != 16) return FP4Q_ERR_SHAPE;
+  if (off_lo > 0 || off_hi < 0 || off_lo < -126 || off_hi > 126) return FP4Q_ERR_ARG;
+  if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
+  fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, hadamard_n);
+  if (st != FP4Q_OK) return st;
+  const bool wmse = loss == FP4Q_WMSE;
+  if (!empty && wmse && !aligned(importance, 16)) return FP4Q_ERR_ALIGN;
+  if (!empty && (!aligned(codes, 8) || (block_loss && !aligned(block_loss, 4)))) return FP4Q_ERR_ALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
+  const bool given = flags & FP4Q_GIVEN_SCALE;
+
+  if (rows == 0 || cols == 0) {
+    if (!given) hipLaunchKernelGGL(zero_scale_kernel, dim3(1), dim3(1), 0, s, global_scale);
+    return last_hip_status();
+  }
+
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  int n_partials = 0;
+  if (!given) {
+    n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
+    with_dtype(dtype, [&](auto tp) {
+      using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+      with_had(hadamard_n, [&](auto hc) {
+        constexpr int H = decltype(hc)::value;
+        hipLaunchKernelGGL((amax_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x, ld, cpr,
+                           total, partials);
+      });
+    });
+  }
+
+  SweepArgs a;
+  a.x = x;
+  a.ld = ld;
+  a.rows = (int)rows;
+  a.cols = (int)cols;
+  a.cpr = cpr;
+  a.imp = wmse ? importance : nullptr;
+  a.off_lo = off_lo;
+  a.off_hi = off_hi;
+  a.nbands = ceil_div(cpr, 64);
+  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands);
+  a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
+  a.partials = partials;
+  a.n_partials = n_partials;
+  a.given_scale = given ? global_scale : nullptr;
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale_out = global_scale;
+  a.loss = block_loss;
+  a.offs = offsets;
+  a.status = status;
+  const int grid = ceil_div(a.ntiles, kWaves);
+  with_dtype(dtype, [&](auto tp) {
+    using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+    with_had(hadamard_n, [&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      if (wmse)
+        hipLaunchKernelGGL((nvfp4_sweep_kernel<T, true, H>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((nvfp4_sweep_kernel<T, false, H>), dim3(grid), dim3(kThreads), 0, s, a);
+    });
+  });
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                             int64_t ld, const float *importance, int block,
+                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
+                                             uint8_t *codes, uint8_t *scales, float *block_loss,
+                                             int8_t *offsets, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!x || !codes || !scales)) return FP4Q_ERR_NULL;
+  if (loss != FP4Q_MSE && loss != FP4Q_WMSE) return FP4Q_ERR_ARG;
+  if (loss == FP4Q_WMSE && !importance && !empty) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (block != 32) return FP4Q_ERR_SHAPE;
+  if (off_lo > 0 || off_hi < 0 || off_lo < -16 || off_hi > 16) return FP4Q_ERR_ARG;
+  fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, hadamard_n);
+  if (st != FP4Q_OK) return st;
+  const bool wmse = loss == FP4Q_WMSE;
+  if (!empty && wmse && !aligned(importance, 16)) return FP4Q_ERR_ALIGN;
+  if (!empty && (!aligned(codes, 8) || (block_loss && !aligned(block_loss, 4)))) return FP4Q_ERR_ALIGN;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  if (rows == 0 || cols == 0) return FP4Q_OK;
+
+  const int cpr = (int)(cols / 16);
+  SweepArgs a;
+  a.x = x;
+  a.ld = ld;
+  a.rows = (int)rows;
+  a.cols = (int)cols;
+  a.cpr = cpr;
+  a.imp = wmse ? importance : nullptr;
+  a.off_lo = off_lo;
+  a.off_hi = off_hi;
+  a.nbands = ceil_div(cpr, 64);
+  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands);
+  a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
+  a.partials = nullptr;
+  a.n_partials = 0;
+  a.given_scale = nullptr;
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale_out = nullptr;
+  a.loss = block_loss;
+  a.offs = offsets;
+  a.status = status;
+  const int grid = ceil_div(a.ntiles, kWaves);
+  with_dtype(dtype, [&](auto tp) {
+    using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+    with_had(hadamard_n, [&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      if (wmse)
+        hipLaunchKernelGGL((mxfp4_sweep_kernel<T, true, H>), dim3(grid), dim3(kThreads), 0, s, a);
+      else
+        hipLaunchKernelGGL((mxfp4_sweep_kernel<T, false, H>), dim3(grid), dim3(kThreads), 0, s, a);
+    });
+  });
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_dequantize(fp4q_format_t format, const uint8_t *codes, const uint8_t *scales,
+                                         const float *global_scale, int64_t rows, int64_t cols, int block,
+                                         float *out, void *stream) {
+  if (format != FP4Q_NVFP4 && format != FP4Q_MXFP4) return FP4Q_ERR_ARG;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!codes || !scales || !out)) return FP4Q_ERR_NULL;
+  if (!empty && format == FP4Q_NVFP4 && !global_scale) return FP4Q_ERR_NULL;
+  if (block != (format == FP4Q_NVFP4 ? 16 : 32)) return FP4Q_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || cols % block) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
+    return FP4Q_ERR_SHAPE;
+  if (empty) return FP4Q_OK;
+  if (!aligned(codes, 8) || !aligned(out, 16)) return FP4Q_ERR_ALIGN;
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = ceil_div(total, kThreads);
+  if (format == FP4Q_NVFP4)
+    hipLaunchKernelGGL((dequant_kernel<FP4Q_NVFP4>), dim3(grid), dim3(kThreads), 0, s, codes, scales,
+                       global_scale, cpr, (int)cols, total, out);
+  else
+    hipLaunchKernelGGL((dequant_kernel<FP4Q_MXFP4>), dim3(grid), dim3(kThreads), 0, s, codes, scales,
+                       global_scale, cpr, (int)cols, total, out);
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_block_hadamard(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                             int64_t ld, int n, float *out, void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!x || !out)) return FP4Q_ERR_NULL;
+  if (n == 0) return FP4Q_ERR_ARG;
+  fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, 16, n);
+  if (st != FP4Q_OK) return st;
+  if (empty) return FP4Q_OK;
+  if (!aligned(out, 16)) return FP4Q_ERR_ALIGN;
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  hipStream_t s = (hipStream_t)stream;
+  const int grid = ceil_div(total, kThreads);
+  with_dtype(dtype, [&](auto tp) {
+    using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+    with_had(n, [&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      if constexpr (H != 0)
+        hipLaunchKernelGGL((hadamard_kernel<T, H>), dim3(grid), dim3(kThreads), 0, s, (const T *)x, ld, cpr,
+                           (int)cols, total, out);
+    });
+  });
+  return last_hip_status();
+}

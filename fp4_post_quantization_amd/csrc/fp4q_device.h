@@ -1,0 +1,214 @@
+// Device helpers for the fp4q kernels (gfx950, wave64).
+//
+// Number formats (see include/fp4q.h for the page citations):
+//   E2M1  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (code index 0..7)
+//   E4M3  FP8 block scale, bias 7, 3 mantissa bits, 0x7E = 448 largest
+//   E8M0  power-of-two block scale 2^(b - 127)
+// Every helper here is exact or a single correctly rounded float32 step;
+// the file is compiled with -ffp-contract=off so nothing is fused unless it
+// is written as an explicit fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+constexpr int kLaneElems = 16;  // every lane owns 16 contiguous elements of a row
+constexpr int kWaveLanes = 64;
+constexpr int kWaves = 4;       // waves per workgroup
+constexpr int kThreads = kWaveLanes * kWaves;
+constexpr int kAmaxGroups = 1024;  // max workgroups of the global-max pass
+
+// Workspace layout (bytes): [0,4) status word, [256, 256 + 4*kAmaxGroups)
+// per-workgroup maxima of |x| as float32 bit patterns.
+constexpr size_t kWsStatus = 0;
+constexpr size_t kWsPartials = 256;
+constexpr size_t kWorkspaceBytes = 8192;
+static_assert(kWsPartials + 4 * kAmaxGroups <= kWorkspaceBytes, "workspace layout");
+
+__device__ __forceinline__ float as_f(uint32_t b) { return __uint_as_float(b); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// ------------------------------------------------------------ loads ----
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16 consecutive elements starting at p (16-byte aligned) widened to fp32.
+// The input is streamed once, so the loads are marked non-temporal.
+__device__ __forceinline__ void load16(const uint16_t *p, float z[16]) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+  const u32x4 a = __builtin_nontemporal_load(q);
+  const u32x4 b = __builtin_nontemporal_load(q + 1);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    z[2 * k] = as_f(w[k] << 16);
+    z[2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void load16(const float *p, float z[16]) {
+  const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4 v = __builtin_nontemporal_load(q + k);
+    z[4 * k] = v.x;
+    z[4 * k + 1] = v.y;
+    z[4 * k + 2] = v.z;
+    z[4 * k + 3] = v.w;
+  }
+}
+
+// ------------------------------------------------- cross-lane moves ----
+// Value held by lane (lane ^ M) of the wave, M in {1, 2, 4}.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  int i = __float_as_int(v);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else {
+    static_assert(M == 4, "xor distance");
+    r = __builtin_amdgcn_ds_swizzle(i, 0x101F);  // bitmask mode: and 0x1F, xor 4
+  }
+  return __int_as_float(r);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint32_t o = __shfl_xor(v, m, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// ------------------------------------------------- block Hadamard ----
+// fp32(1/sqrt(N)): 1/sqrt(2) rounds to 0x3F3504F3; the odd powers of two
+// below are that value scaled by exact powers of two.
+template <int N>
+__device__ __forceinline__ float hadamard_scale() {
+  if constexpr (N == 16) return 0.25f;
+  else if constexpr (N == 32) return as_f(0x3E3504F3u);
+  else if constexpr (N == 64) return 0.125f;
+  else {
+    static_assert(N == 128, "Hadamard size");
+    return as_f(0x3DB504F3u);
+  }
+}
+
+// Sylvester block Hadamard of the N-group this lane's 16 elements belong to
+// (N/16 consecutive lanes hold one group).  Stages h = 1 .. N/2 in order;
+// h < 16 stay inside the lane, h >= 16 pair lane l with lane l ^ (h/16).
+template <int N>
+__device__ __forceinline__ void fwht(float z[16], int lane) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = z[i], b = z[i + h];
+        z[i] = a + b;
+        z[i + h] = a - b;
+      }
+    }
+  }
+  if constexpr (N >= 32) {
+    const bool hi = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float o = xor_lane<1>(z[i]);
+      z[i] = hi ? (o - z[i]) : (z[i] + o);
+    }
+  }
+  if constexpr (N >= 64) {
+    const bool hi = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float o = xor_lane<2>(z[i]);
+      z[i] = hi ? (o - z[i]) : (z[i] + o);
+    }
+  }
+  if constexpr (N >= 128) {
+    const bool hi = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float o = xor_lane<4>(z[i]);
+      z[i] = hi ? (o - z[i]) : (z[i] + o);
+    }
+  }
+  const float c = hadamard_scale<N>();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = z[i] * c;
+}
+
+// ------------------------------------------------------------ E2M1 ----
+// Nearest E2M1 magnitude to y >= 0, ties to the even code index, saturating
+// at 6.  Adding M = 2^(e+22), e = floor(log2(max(y, 1))), makes the float32
+// spacing around M equal to the E2M1 step of y's binade (0.5 below 2, 1 in
+// [2, 4), 2 from 4), so the addition itself rounds y to that step with
+// ties-to-even; subtracting M is exact.  y is capped at 8 first (every
+// y >= 6 saturates anyway).
+__device__ __forceinline__ float e2m1_round(float y) {
+  const float yc = fminf(y, 8.0f);
+  const float M = as_f((as_u(fmaxf(yc, 1.0f)) & 0x7F800000u) + (22u << 23));
+  const float q = (yc + M) - M;
+  return fminf(q, 6.0f);
+}
+
+// Code index 0..7 of an E2M1 magnitude q (one of the eight values).
+__device__ __forceinline__ uint32_t e2m1_index(float q) {
+  // 0, .5, 1, 1.5 -> 2q; 2, 3 -> q + 2; 4 -> 6; 6 -> 7
+  return q < 2.0f ? (uint32_t)(q * 2.0f) : (q < 4.0f ? (uint32_t)q + 2u : (q < 5.0f ? 6u : 7u));
+}
+
+// ------------------------------------------------------------ E4M3 ----
+// Value of a non-negative E4M3 pattern p in 1..126 (exact).
+__device__ __forceinline__ float e4m3_value(int p) {
+  if (p < 8) return (float)p * 0.001953125f;  // subnormal p * 2^-9
+  return as_f(((uint32_t)((p >> 3) + 120) << 23) | ((uint32_t)(p & 7) << 20));
+}
+
+// Nearest non-negative E4M3 pattern to t >= 0, ties to the even pattern,
+// saturating at 0x7E (448).
+__device__ __forceinline__ int e4m3_rne_sat(float t) {
+  if (!(t < 448.0f)) return 126;
+  if (t < 0.015625f) return (int)rintf(t * 512.0f);  // subnormal grid m * 2^-9
+  uint32_t b = as_u(t);
+  b += 0x7FFFFu + ((b >> 20) & 1u);  // round the mantissa to 3 bits, ties to even
+  const int e = (int)(b >> 23) - 127;
+  const int m = (int)((b >> 20) & 7u);
+  const int p = ((e + 7) << 3) | m;
+  return p < 126 ? p : 126;
+}
+
+// ------------------------------------------------------------ E8M0 ----
+// 2^e for e in [-127, 127] (2^-127 is subnormal).
+__device__ __forceinline__ float pow2f(int e) {
+  return e >= -126 ? as_f((uint32_t)(e + 127) << 23) : as_f(0x00400000u);
+}
+
+// Least E with 6 * 2^E >= a (a >= 0), clamped to [-127, 127].  With
+// a = 1.f * 2^k (normal), 6 * 2^E >= a iff E >= k - 1 - [1.f <= 1.5].
+__device__ __forceinline__ int mx_base_exponent(float a) {
+  const uint32_t b = as_u(a);
+  const int ef = (int)(b >> 23);
+  if (ef == 0) return -127;  // zero or subnormal: 6 * 2^-127 covers it
+  const int E = (ef - 127) - ((b & 0x7FFFFFu) <= 0x400000u ? 3 : 2) + 1;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// ------------------------------------------------------------ trees ----
+// Contiguous pairwise float32 tree sum of 16 values.
+__device__ __forceinline__ float tree16(const float t[16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = t[2 * i] + t[2 * i + 1];
+  float b0 = a[0] + a[1], b1 = a[2] + a[3], b2 = a[4] + a[5], b3 = a[6] + a[7];
+  return (b0 + b1) + (b2 + b3);
+}
+
+}  // namespace fp4q

@@ -1,0 +1,194 @@
+/*
+ * fp4q -- FP4 microscaling block quantization with block-scale search,
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the library computes is defined on these web pages (cited by title
+ * and section):
+ *   [SS]  "Resumo Técnico: ScaleSweep" -- NVFP4 two-level scaling
+ *         (Declaração do Problema), the MSE / WMSE objectives (1. Objetivos
+ *         de Otimização), the global scale S = max|x| / (256 * 6) and the
+ *         bit-pattern window around the AbsMax block scale bounded by
+ *         Lemma 4.1 (+7) and Lemma 4.3 (-3, MSE) or the empirical -8 (WMSE)
+ *         (2. Limites Teóricos para Varredura Eficiente, 3. Implementação).
+ *   [MR]  "Bridging the Gap Between Promise and Performance for Microscaling
+ *         FP4 Quantization" -- MXFP4 with power-of-two E8M0 scales
+ *         (1. O Problema), MSE-optimised scale grid and fused block Hadamard
+ *         micro-rotation (2. Metodologia e Análise, 3. Implementação de
+ *         Hardware).
+ *   [TQ]  "Resumo Técnico: TORQ" -- MXFP4 activations; the S-step maps the
+ *         block maximum onto the largest E2M1 code (B. Rotação de
+ *         Alinhamento Micro).
+ *   [FC]  "FOCUS: FP4 Optimization via Coupled-Relaxation and
+ *         Dual-Granularity Scaling" -- block sizes 16 (NVFP4) and 32
+ *         (MXFP4); only the FP4 codes and the dequantization scales are
+ *         stored (Declaração do Problema, 4. Implantação e Compatibilidade).
+ *
+ * Conventions shared by every call
+ *   - x is a row-major R x C matrix with leading dimension ld >= C (elements).
+ *     Blocks and Hadamard groups run along C.  C must be a multiple of the
+ *     block size (and of the Hadamard size).  R * C / 16 must be below 2^31.
+ *   - x must be 16-byte aligned and ld * sizeof(element) a multiple of 16.
+ *   - Outputs are dense row-major: packed codes have C/2 bytes per row
+ *     (element 2k in the low nibble of byte k, element 2k+1 in the high
+ *     nibble; a code is (sign << 3) | e2m1_index, index 0..7 for magnitudes
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6); per-block arrays (scales, losses,
+ *     offsets) have C/block entries per row.
+ *   - Every pointer except the stream is a DEVICE pointer.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no state
+ *     between calls.
+ *   - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; nothing waits on the host.
+ *   - Errors in the arguments are returned synchronously, before anything is
+ *     enqueued.  Errors in the data (non-finite x, negative or non-finite
+ *     importance, an invalid given global scale) are found on the device:
+ *     they set bits of the status word at byte 0 of the workspace
+ *     (FP4Q_DATA_* below) and leave that call's outputs unspecified.  The
+ *     word is sticky: kernels only ever set bits, never clear them, so the
+ *     caller zero-fills the workspace once before first use, reads the word
+ *     after the stream has finished, and writes 0 to it to clear an error.
+ *     Calls that overlap on one workspace race on its scratch part.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp4q_status {
+  FP4Q_OK = 0,
+  FP4Q_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP4Q_ERR_SHAPE = 2,     /* rows/cols/ld/block/Hadamard size inconsistent */
+  FP4Q_ERR_ARG = 3,       /* bad enum, window or flag */
+  FP4Q_ERR_ALIGN = 4,     /* x or its row stride not 16-byte aligned */
+  FP4Q_ERR_WORKSPACE = 5, /* workspace NULL or smaller than fp4q_workspace_bytes() */
+  FP4Q_ERR_HIP = 6        /* a kernel launch failed (hipGetLastError) */
+} fp4q_status_t;
+
+typedef enum fp4q_dtype { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype_t;
+typedef enum fp4q_loss { FP4Q_MSE = 0, FP4Q_WMSE = 1 } fp4q_loss_t;
+typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
+
+/* flags of fp4q_quantize_nvfp4 */
+#define FP4Q_GIVEN_SCALE 0x1u /* read S from *global_scale instead of computing it */
+
+/* bits of the device status word (uint32 at byte 0 of the workspace) */
+#define FP4Q_DATA_NONFINITE_INPUT 0x1u  /* x (after rotation) holds Inf or NaN */
+#define FP4Q_DATA_BAD_IMPORTANCE 0x2u   /* an importance entry is < 0, Inf or NaN */
+#define FP4Q_DATA_BAD_GLOBAL_SCALE 0x4u /* given S is < 0, Inf or NaN */
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int fp4q_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *fp4q_status_string(fp4q_status_t status);
+
+/* Bytes of device workspace every quantize call needs (a constant).  Bytes
+ * 0..3 hold the sticky status word (zero it before first use); the rest is
+ * scratch the library overwrites. */
+size_t fp4q_workspace_bytes(void);
+
+/*
+ * NVFP4 quantization with the ScaleSweep block-scale search [SS], optionally
+ * after a block Hadamard rotation [MR].
+ *
+ *   x, dtype, rows, cols, ld  input matrix (FP4Q_F32 or FP4Q_BF16).
+ *   importance  [cols] float32 per-column weights (WMSE; NULL for MSE)
+ *               ([SS] 1.: importance from input-activation norms or the
+ *               Gram diagonal).  With a rotation it must already be in the
+ *               rotated basis.
+ *   block       16.
+ *   loss        FP4Q_MSE or FP4Q_WMSE (WMSE requires importance).
+ *   off_lo, off_hi  E4M3 bit-pattern window around the AbsMax base pattern,
+ *               -126 <= off_lo <= 0 <= off_hi <= 126 ([SS] 3.: -3, 7 for
+ *               MSE; -8, 7 for WMSE; 0, 0 is plain AbsMax round-to-nearest).
+ *   hadamard_n  0 (none) or 16, 32, 64, 128: rotate each row's n-column
+ *               groups by the orthonormal Sylvester Hadamard matrix first.
+ *   flags       0 or FP4Q_GIVEN_SCALE.
+ *   codes       [rows * cols / 2] packed E2M1 codes (out).
+ *   scales      [rows * cols / 16] E4M3 block-scale bit patterns (out).
+ *   global_scale [1] float32 S (out; in with FP4Q_GIVEN_SCALE).
+ *   block_loss  [rows * cols / 16] float32 loss of the chosen scale in the
+ *               units of x (sum over the block of w * (x - x_hat)^2 in
+ *               S-units, times S*S) (out; may be NULL).
+ *   offsets     [rows * cols / 16] int8 chosen pattern minus base pattern
+ *               (out; may be NULL).
+ *   workspace   fp4q_workspace_bytes() bytes of device memory.
+ *
+ * Computation (every float32 step rounds to nearest even, no fused
+ * multiply-add except where the product is exact):
+ *   S = fp32(max|x| / 1536), S_inv = fp32(1/S) (0 if S = 0);
+ *   u = fp32(|x| * S_inv); per block t = fp32(max u / 6);
+ *   base = max(1, nearest E4M3 pattern to t, ties to even, saturating 0x7E);
+ *   for p = max(1, base+off_lo) .. min(126, base+off_hi): V = E4M3(p),
+ *   R = fp32(1/V), q = E2M1 nearest to fp32(u*R) (ties to even index,
+ *   saturating at 6), e = fp32(u - q*V), tau = fp32(e*e) [WMSE: fp32(w*tau)],
+ *   L_p = contiguous pairwise float32 tree sum of tau over the block;
+ *   the chosen p is the smallest p with the least L_p.
+ */
+fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                  int64_t ld, const float *importance, int block, fp4q_loss_t loss,
+                                  int off_lo, int off_hi, int hadamard_n, uint32_t flags,
+                                  uint8_t *codes, uint8_t *scales, float *global_scale,
+                                  float *block_loss, int8_t *offsets, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * MXFP4 quantization with an exponent-window search over E8M0 block scales
+ * ([MR] 1., 2.: power-of-two scales, MSE-optimised grid; [TQ] S-step for the
+ * base), optionally after a block Hadamard rotation.
+ *
+ *   block       32.
+ *   off_lo, off_hi  window in powers of two around the base exponent,
+ *               -16 <= off_lo <= 0 <= off_hi <= 16 (default -1, 0; 0, 0 is
+ *               the AbsMax rule).
+ *   scales      [rows * cols / 32] E8M0 bytes (E + 127) (out).
+ *   block_loss  [rows * cols / 32] float32 loss in the units of x (may be NULL).
+ *   offsets     [rows * cols / 32] int8 chosen exponent minus base (may be NULL).
+ *   Other arguments as for fp4q_quantize_nvfp4; there is no global scale.
+ *
+ * Computation: u = |x|; per block E_base = least E with 6 * 2^E >= max u,
+ * clamped to [-127, 127]; for E = max(-127, E_base+off_lo) ..
+ * min(127, E_base+off_hi): q = E2M1 nearest to fp32(u * 2^-E),
+ * e = fp32(u - q*2^E), tau and the pairwise tree over 32 as above; the
+ * smallest E with the least loss is chosen.
+ */
+fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                  int64_t ld, const float *importance, int block, fp4q_loss_t loss,
+                                  int off_lo, int off_hi, int hadamard_n, uint8_t *codes,
+                                  uint8_t *scales, float *block_loss, int8_t *offsets,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dequantization (the consumer side: only codes and dequantization scales
+ * are stored, [FC] 4.).
+ *   NVFP4 (block 16): x_hat = sign * fp32(fp32(q * E4M3(scale)) * S), S read
+ *   from global_scale (device).  MXFP4 (block 32): x_hat = sign * q *
+ *   2^(scale - 127); global_scale is ignored and may be NULL.
+ *   out [rows * cols] float32, dense row-major.
+ *   Scale bytes are not checked: 0x7F (E4M3) and 0xFF (E8M0) decode as NaN.
+ */
+fp4q_status_t fp4q_dequantize(fp4q_format_t format, const uint8_t *codes, const uint8_t *scales,
+                              const float *global_scale, int64_t rows, int64_t cols, int block,
+                              float *out, void *stream);
+
+/*
+ * Block Hadamard rotation ([MR] 2., component 3): each row's groups of n
+ * contiguous columns times H_n / sqrt(n), H_n the Sylvester Hadamard matrix
+ * in natural order, n in {16, 32, 64, 128}.  Evaluated as a fast transform:
+ * stages h = 1, 2, ..., n/2 map (z_i, z_{i+h}) to (z_i + z_{i+h},
+ * z_i - z_{i+h}) for i with (i & h) == 0, then every value is multiplied by
+ * fp32(1/sqrt(n)).  The transform is its own inverse (up to rounding).
+ *   out [rows * cols] float32, dense row-major.  Inf/NaN propagate.
+ */
+fp4q_status_t fp4q_block_hadamard(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                  int64_t ld, int n, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_H */

@@ -1,0 +1,142 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments synchronously, before anything is
+enqueued on a device (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+
+def _lib():
+    from fp4_post_quantization_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libfp4q.so not built (run __graft_entry__.build())")
+    return L, L.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_dequantize", "fp4q_block_hadamard"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L, lib = _lib()
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_helpers_without_gpu():
+    L, lib = _lib()
+    assert lib.fp4q_version() >= 100
+    assert lib.fp4q_workspace_bytes() >= 256
+    for code in range(7):
+        assert lib.fp4q_status_string(code)
+    assert lib.fp4q_status_string(0) == b"ok"
+
+
+# fake, aligned device addresses: validation must reject before any use
+X = 0x10000
+OUT = 0x20000
+WS = 0x40000
+
+
+def _nv(lib, L, **kw):
+    a = dict(x=X, dtype=L.BF16, rows=4, cols=64, ld=64, imp=None, block=16, loss=L.MSE, lo=-3, hi=7,
+             had=0, flags=0, codes=OUT, scales=OUT, gs=OUT, bl=None, offs=None, ws=WS,
+             wsb=lib.fp4q_workspace_bytes(), stream=None)
+    a.update(kw)
+    return lib.fp4q_quantize_nvfp4(a["x"], a["dtype"], a["rows"], a["cols"], a["ld"], a["imp"], a["block"],
+                                   a["loss"], a["lo"], a["hi"], a["had"], a["flags"], a["codes"], a["scales"],
+                                   a["gs"], a["bl"], a["offs"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_nvfp4_argument_validation():
+    L, lib = _lib()
+    assert _nv(lib, L, x=None) == L.ERR_NULL
+    assert _nv(lib, L, codes=None) == L.ERR_NULL
+    assert _nv(lib, L, gs=None) == L.ERR_NULL
+    assert _nv(lib, L, loss=L.WMSE, imp=None) == L.ERR_NULL
+    assert _nv(lib, L, ws=None) == L.ERR_WORKSPACE
+    assert _nv(lib, L, wsb=16) == L.ERR_WORKSPACE
+    assert _nv(lib, L, dtype=7) == L.ERR_ARG
+    assert _nv(lib, L, loss=5) == L.ERR_ARG
+    assert _nv(lib, L, lo=1) == L.ERR_ARG
+    assert _nv(lib, L, hi=-1) == L.ERR_ARG
+    assert _nv(lib, L, lo=-127) == L.ERR_ARG
+    assert _nv(lib, L, hi=127) == L.ERR_ARG
+    assert _nv(lib, L, had=8) == L.ERR_ARG
+    assert _nv(lib, L, flags=0x8) == L.ERR_ARG
+    assert _nv(lib, L, block=32) == L.ERR_SHAPE
+    assert _nv(lib, L, cols=40, ld=40) == L.ERR_SHAPE
+    assert _nv(lib, L, ld=32) == L.ERR_SHAPE
+    assert _nv(lib, L, rows=-1) == L.ERR_SHAPE
+    assert _nv(lib, L, cols=48, ld=48, had=32) == L.ERR_SHAPE
+    assert _nv(lib, L, rows=1 << 31, cols=16, ld=16) == L.ERR_SHAPE
+    assert _nv(lib, L, x=X + 2) == L.ERR_ALIGN
+    assert _nv(lib, L, ld=68) == L.ERR_ALIGN            # 136-byte bf16 rows
+    assert _nv(lib, L, codes=OUT + 4) == L.ERR_ALIGN
+    assert _nv(lib, L, loss=L.WMSE, imp=OUT + 4) == L.ERR_ALIGN
+
+
+def test_mxfp4_dequant_hadamard_validation():
+    L, lib = _lib()
+    wsb = lib.fp4q_workspace_bytes()
+    mx = lambda **kw: lib.fp4q_quantize_mxfp4(
+        kw.get("x", X), kw.get("dtype", L.F32), kw.get("rows", 2), kw.get("cols", 64), kw.get("ld", 64),
+        kw.get("imp", None), kw.get("block", 32), kw.get("loss", L.MSE), kw.get("lo", -1), kw.get("hi", 0),
+        kw.get("had", 0), OUT, OUT, None, None, kw.get("ws", WS), wsb, None)
+    assert mx(x=None) == L.ERR_NULL
+    assert mx(block=16) == L.ERR_SHAPE
+    assert mx(cols=48, ld=48) == L.ERR_SHAPE
+    assert mx(lo=-17) == L.ERR_ARG
+    assert mx(hi=17) == L.ERR_ARG
+    assert mx(ws=None) == L.ERR_WORKSPACE
+    assert mx(loss=L.WMSE) == L.ERR_NULL
+    dq = lambda **kw: lib.fp4q_dequantize(kw.get("fmt", L.NVFP4), kw.get("codes", OUT), OUT,
+                                          kw.get("gs", OUT), 2, kw.get("cols", 64), kw.get("block", 16),
+                                          kw.get("out", OUT), None)
+    assert dq(fmt=9) == L.ERR_ARG
+    assert dq(codes=None) == L.ERR_NULL
+    assert dq(gs=None) == L.ERR_NULL
+    assert dq(block=32) == L.ERR_SHAPE
+    assert dq(cols=40) == L.ERR_SHAPE
+    assert dq(out=OUT + 4) == L.ERR_ALIGN
+    hd = lambda **kw: lib.fp4q_block_hadamard(kw.get("x", X), L.F32, 2, kw.get("cols", 64), 64,
+                                              kw.get("n", 16), kw.get("out", OUT), None)
+    assert hd(x=None) == L.ERR_NULL
+    assert hd(n=0) == L.ERR_ARG
+    assert hd(n=24) == L.ERR_ARG
+    assert hd(n=128) == L.ERR_SHAPE
+    assert hd(cols=40) == L.ERR_SHAPE
+
+
+def test_empty_shapes_need_no_device_for_dequant_and_hadamard():
+    L, lib = _lib()
+    assert lib.fp4q_dequantize(L.NVFP4, OUT, OUT, OUT, 0, 64, 16, OUT, None) == L.OK
+    assert lib.fp4q_block_hadamard(X, L.F32, 0, 64, 64, 16, OUT, None) == L.OK
+
+
+def test_binding_raises_without_library(tmp_path):
+    from fp4_post_quantization_amd import _lib as L
+    saved = L._lib
+    L._lib = None
+    try:
+        with pytest.raises(L.FP4QError):
+            L.load(str(tmp_path / "missing.so"))
+    finally:
+        L._lib = saved

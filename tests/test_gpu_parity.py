@@ -1,0 +1,363 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bar: codes, scales, offsets, the global scale and per-block losses are
+bit-exact on unrotated inputs.  With a block Hadamard rotation the rotated
+values must be within 1e-5 of the float64 dense product (per block,
+relative to the block's largest magnitude), at most 1e-4 of the codes may
+differ and per-block losses must agree within 1e-5 relative; the GPU rotation
+is additionally checked to reproduce the oracle's float32 fast transform bit
+for bit, in which case everything downstream is bit-exact too.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import quant as Q
+from oracle import hadamard as OH
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _fp4():
+    import fp4_post_quantization_amd as fq
+    return fq
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _host_f32(x):
+    return x.detach().float().cpu().numpy()
+
+
+def _assert_equal(name, got, ref):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if got.dtype.kind == "f":
+        same = (got.view(np.uint32) == ref.astype(np.float32).view(np.uint32))
+    else:
+        same = got == ref
+    if not np.all(same):
+        idx = np.argwhere(~same)
+        i = tuple(idx[0])
+        raise AssertionError(f"{name}: {idx.shape[0]} of {same.size} differ; first at {i}: "
+                             f"gpu={got[i]!r} oracle={ref[i]!r}")
+
+
+def _check_nvfp4(res, ref, rows=None):
+    sl = slice(None) if rows is None else rows
+    _assert_equal("global_scale", np.float32(_np(res.global_scale)[0]), np.float32(ref.global_scale))
+    _assert_equal("codes", _np(res.codes)[sl], ref.codes)
+    _assert_equal("scales", _np(res.scales)[sl], ref.scales)
+    _assert_equal("offsets", _np(res.offsets)[sl], ref.offsets)
+    _assert_equal("block_loss", _np(res.block_loss)[sl], ref.block_loss)
+
+
+def _check_mxfp4(res, ref, rows=None):
+    sl = slice(None) if rows is None else rows
+    _assert_equal("codes", _np(res.codes)[sl], ref.codes)
+    _assert_equal("scales", _np(res.scales)[sl], ref.scales)
+    _assert_equal("offsets", _np(res.offsets)[sl], ref.offsets)
+    _assert_equal("block_loss", _np(res.block_loss)[sl], ref.block_loss)
+
+
+def _run_nvfp4(x, imp=None, window=None, had=0, gs=None):
+    fq = _fp4()
+    xd = x.to(DEV)
+    impd = None if imp is None else imp.to(DEV)
+    res = fq.quantize_nvfp4(xd, impd, window=window, hadamard_n=had, global_scale=gs, check=True)
+    torch.cuda.synchronize()
+    return res
+
+
+def _oracle_nvfp4(x, imp=None, window=None, had=0, gs=None):
+    return Q.quantize_nvfp4(_host_f32(x), None if imp is None else imp.numpy(), window=window,
+                            hadamard_n=had, global_scale=gs)
+
+
+# ------------------------------------------------------- small shapes ----
+SHAPES = [(1, 16), (3, 32), (3, 48), (257, 4112), (64, 1024), (5, 2048)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("wmse", [False, True])
+def test_nvfp4_small_shapes(rows, cols, dtype, wmse):
+    x = W.random_matrix(rows, cols, seed=rows * 7919 + cols, dist="t4", dtype=dtype)
+    imp = W.random_importance(cols, seed=cols, zero_frac=0.05) if wmse else None
+    _check_nvfp4(_run_nvfp4(x, imp), _oracle_nvfp4(x, imp))
+
+
+@pytest.mark.parametrize("window", [(0, 0), (-3, 7), (-8, 7), (-1, 2), (-126, 126)])
+def test_nvfp4_windows(window):
+    x = W.random_matrix(96, 512, seed=31, dist="laplace")
+    x[5, 17] = 3.0  # a tensor-maximum block whose window clips at 0x7E
+    imp = W.random_importance(512, seed=32)
+    for im in (None, imp):
+        _check_nvfp4(_run_nvfp4(x, im, window=window), _oracle_nvfp4(x, im, window=window))
+
+
+def test_nvfp4_leading_dimension_larger_than_cols():
+    big = W.random_matrix(33, 1056, seed=41, dtype=torch.bfloat16)
+    fq = _fp4()
+    xd = big.to(DEV)[:, :1024]                  # ld = 1056 > cols = 1024
+    res = fq.quantize_nvfp4(xd, check=True)
+    ref = _oracle_nvfp4(big[:, :1024].contiguous())
+    _check_nvfp4(res, ref)
+
+
+def test_nvfp4_given_scale():
+    x = W.random_matrix(40, 256, seed=42)
+    S = np.float32(0.37 / 1536)
+    _check_nvfp4(_run_nvfp4(x, gs=float(S)), _oracle_nvfp4(x, gs=S))
+
+
+# -------------------------------------------------------- edge tensors ----
+def test_edge_zero_tensor_and_negative_zero():
+    x = torch.zeros(4, 64)
+    x[1, 3] = -0.0
+    res = _run_nvfp4(x)
+    _check_nvfp4(res, _oracle_nvfp4(x))
+    assert float(_np(res.global_scale)[0]) == 0.0
+
+
+def test_edge_single_nonzero():
+    x = torch.zeros(3, 48)
+    x[2, 40] = -1e-3
+    _check_nvfp4(_run_nvfp4(x), _oracle_nvfp4(x))
+    m = torch.zeros(3, 64)
+    m[0, 5] = 7.0
+    fq = _fp4()
+    r = fq.quantize_mxfp4(m.to(DEV), check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(m.numpy()))
+
+
+def test_edge_exact_ties():
+    """With S = 1 and a power-of-two base scale, u * R hits every E2M1
+    midpoint exactly: ties must go to the even code on both sides."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows = []
+    for scale in (1.0, 0.5, 2.0 ** -7, 4.0):
+        r = np.zeros(16, dtype=np.float32)
+        r[0] = 6 * scale
+        r[1:8] = np.float32(mids) * scale
+        r[8:15] = -np.float32(mids) * scale
+        r[15] = np.float32(2.9) * scale
+        rows.append(r)
+    x = torch.from_numpy(np.stack(rows))
+    _check_nvfp4(_run_nvfp4(x, gs=1.0), _oracle_nvfp4(x, gs=np.float32(1.0)))
+    _check_nvfp4(_run_nvfp4(x, window=(0, 0), gs=1.0), _oracle_nvfp4(x, window=(0, 0), gs=np.float32(1.0)))
+    xm = torch.from_numpy(np.concatenate([np.stack(rows), np.stack(rows)], axis=1))
+    fq = _fp4()
+    r = fq.quantize_mxfp4(xm.to(DEV), window=(0, 0), check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(xm.numpy(), window=(0, 0)))
+
+
+def test_edge_subnormal_bases_and_bf16_extremes():
+    rng = np.random.default_rng(51)
+    x = (rng.standard_normal((16, 256)) * 1e-7).astype(np.float32)
+    x[0, 0] = 1.0                                  # most blocks get subnormal E4M3 bases
+    x[1, :16] = np.float32(3.0e38)                 # near the bf16 / fp32 maximum
+    x[2, :32] = np.float32(1e-39)                  # float32 subnormals
+    xt = torch.from_numpy(x)
+    _check_nvfp4(_run_nvfp4(xt), _oracle_nvfp4(xt))
+    xb = xt.to(torch.bfloat16)
+    _check_nvfp4(_run_nvfp4(xb), _oracle_nvfp4(xb))
+    fq = _fp4()
+    r = fq.quantize_mxfp4(xb.to(DEV), check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(_host_f32(xb)))
+
+
+def test_edge_zero_importance_columns():
+    x = W.random_matrix(20, 256, seed=52)
+    imp = W.random_importance(256, seed=53)
+    imp[:64] = 0.0
+    _check_nvfp4(_run_nvfp4(x, imp), _oracle_nvfp4(x, imp))
+
+
+def test_empty_rows():
+    fq = _fp4()
+    x = torch.empty(0, 64, device=DEV)
+    r = fq.quantize_nvfp4(x, check=True)
+    torch.cuda.synchronize()
+    assert r.codes.shape == (0, 32)
+    assert float(r.global_scale.item()) == 0.0
+
+
+# ------------------------------------------------------- data errors ----
+def test_data_errors_set_status():
+    fq = _fp4()
+    x = W.random_matrix(8, 64, seed=54).to(DEV)
+    x[3, 7] = float("nan")
+    with pytest.raises(fq.FP4QError, match="non-finite"):
+        fq.quantize_nvfp4(x, check=True)
+    with pytest.raises(fq.FP4QError, match="non-finite"):
+        fq.quantize_mxfp4(x, check=True)
+    y = W.random_matrix(8, 64, seed=55).to(DEV)
+    imp = torch.ones(64, device=DEV)
+    imp[9] = -1.0
+    with pytest.raises(fq.FP4QError, match="importance"):
+        fq.quantize_nvfp4(y, imp, check=True)
+    with pytest.raises(fq.FP4QError, match="global scale"):
+        fq.quantize_nvfp4(y, global_scale=float("inf"), check=True)
+    # a clean call afterwards resets the status word
+    fq.quantize_nvfp4(y, check=True)
+
+
+def test_deterministic():
+    fq = _fp4()
+    x = W.random_matrix(512, 2048, seed=56, dtype=torch.bfloat16).to(DEV)
+    imp = W.random_importance(2048, seed=57).to(DEV)
+    a = fq.quantize_nvfp4(x, imp)
+    b = fq.quantize_nvfp4(x, imp)
+    torch.cuda.synchronize()
+    for f in ("codes", "scales", "offsets", "block_loss", "global_scale"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+# ------------------------------------------------------------- MXFP4 ----
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (257, 4128), (64, 1024)])
+@pytest.mark.parametrize("window", [(-1, 0), (0, 0), (-3, 2)])
+def test_mxfp4_small(rows, cols, window):
+    x = W.random_matrix(rows, cols, seed=rows + cols, dist="laplace", scale=1.0, dtype=torch.bfloat16)
+    fq = _fp4()
+    r = fq.quantize_mxfp4(x.to(DEV), window=window, check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(_host_f32(x), window=window))
+    imp = W.random_importance(cols, seed=cols + 1)
+    r = fq.quantize_mxfp4(x.to(DEV), imp.to(DEV), window=window, check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(_host_f32(x), imp.numpy(), window=window))
+
+
+# ---------------------------------------------------------- dequant ----
+def test_dequantize_matches_oracle():
+    fq = _fp4()
+    x = W.random_matrix(77, 512, seed=61, dist="t4")
+    r = fq.quantize_nvfp4(x.to(DEV))
+    out = fq.dequantize("nvfp4", r.codes, r.scales, r.global_scale)
+    ref = Q.dequantize_nvfp4(_np(r.codes), _np(r.scales), _np(r.global_scale)[0])
+    _assert_equal("nvfp4 dequant", _np(out), ref)
+    m = fq.quantize_mxfp4(x.to(DEV))
+    out = fq.dequantize("mxfp4", m.codes, m.scales)
+    _assert_equal("mxfp4 dequant", _np(out), Q.dequantize_mxfp4(_np(m.codes), _np(m.scales)))
+
+
+# ---------------------------------------------------------- Hadamard ----
+@pytest.mark.parametrize("n", [16, 32, 64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_block_hadamard(n, dtype):
+    fq = _fp4()
+    x = W.random_matrix(131, 1024, seed=n, dist="laplace", scale=1.0, dtype=dtype)
+    z = _np(fq.block_hadamard(x.to(DEV), n))
+    xf = _host_f32(x)
+    _assert_equal("fwht", z, OH.block_hadamard(xf, n))
+    ref = OH.block_hadamard_dense64(xf, n)
+    blk = np.abs(ref).reshape(131, -1, n).max(-1, keepdims=True)
+    err = np.abs(z - ref).reshape(131, -1, n)
+    assert np.all(err <= 1e-5 * blk)
+
+
+def _rotated_checks(res, ref_fn, x_host, n, imp=None):
+    """Spec tolerances for rotated inputs, then bit-exactness."""
+    ref = ref_fn()
+    codes_g = Q.unpack_nibbles(_np(res.codes))
+    codes_o = Q.unpack_nibbles(ref.codes)
+    mismatch = np.mean(codes_g != codes_o)
+    assert mismatch <= 1e-4, mismatch
+    lg, lo = _np(res.block_loss), ref.block_loss
+    assert np.all(np.abs(lg - lo) <= 1e-5 * np.maximum(lo, 1e-6 * lo.mean() + 1e-45))
+    return ref
+
+
+@pytest.mark.parametrize("n", [16, 32, 128])
+def test_nvfp4_rotated(n):
+    fq = _fp4()
+    x = W.random_matrix(129, 2048, seed=70 + n, dist="laplace", dtype=torch.bfloat16)
+    imp = W.random_importance(2048, seed=71)
+    res = fq.quantize_nvfp4(x.to(DEV), imp.to(DEV), hadamard_n=n, check=True)
+    torch.cuda.synchronize()
+    ref = _rotated_checks(res, lambda: _oracle_nvfp4(x, imp, had=n), None, n)
+    _check_nvfp4(res, ref)
+
+
+@pytest.mark.parametrize("n", [32, 128])
+def test_mxfp4_rotated(n):
+    fq = _fp4()
+    x = W.random_matrix(65, 4096, seed=80 + n, dist="laplace", scale=1.0, dtype=torch.bfloat16)
+    res = fq.quantize_mxfp4(x.to(DEV), hadamard_n=n, check=True)
+    torch.cuda.synchronize()
+    ref = _rotated_checks(res, lambda: Q.quantize_mxfp4(_host_f32(x), hadamard_n=n), None, n)
+    _check_mxfp4(res, ref)
+
+
+# ------------------------------------------------- workload sizes ----
+def _sample_rows(rows, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(rows, size=min(k, rows), replace=False))
+
+
+def test_c1_nvfp4_mse_fp32_full():
+    x = W.c1_weight()
+    _check_nvfp4(_run_nvfp4(x), _oracle_nvfp4(x))
+
+
+def test_c2_nvfp4_wmse_bf16_4096_sampled_rows():
+    x, imp = W.c2_weight_and_importance()
+    res = _run_nvfp4(x, imp)
+    xf = _host_f32(x)
+    S = Q.global_scale_nvfp4(xf)
+    rows = _sample_rows(4096, 384, 202)
+    ref = Q.quantize_nvfp4(xf[rows], imp.numpy(), global_scale=S)
+    ref.global_scale = S
+    _check_nvfp4(res, ref, rows=rows)
+
+
+@pytest.mark.parametrize("variant", ["absmax", "sweep", "rot32"])
+def test_c3_mxfp4_activations_sampled_rows(variant):
+    fq = _fp4()
+    x = W.c3_activation()
+    window = (0, 0) if variant == "absmax" else (-1, 0)
+    had = 32 if variant == "rot32" else 0
+    res = fq.quantize_mxfp4(x.to(DEV), window=window, hadamard_n=had, check=True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(8192, 256, 303)
+    ref = Q.quantize_mxfp4(_host_f32(x[rows]), window=window, hadamard_n=had)
+    _check_mxfp4(res, ref, rows=rows)
+
+
+@pytest.mark.parametrize("name", list(W.LAYER_8B))
+def test_c4_8b_layer_sampled_rows(name):
+    x = W.c4_matrix(name)
+    imp = W.c4_importance(name)
+    xf = _host_f32(x)
+    S = Q.global_scale_nvfp4(xf)
+    rows = _sample_rows(x.shape[0], 96, 404)
+    for im in (None, imp):
+        res = _run_nvfp4(x, im)
+        ref = Q.quantize_nvfp4(xf[rows], None if im is None else im.numpy(), global_scale=S)
+        _check_nvfp4(res, ref, rows=rows)
+
+
+@pytest.mark.parametrize("name", list(W.LAYER_70B))
+def test_c5_70b_layer0_rotated_sampled_rows(name):
+    fq = _fp4()
+    x = W.c5_matrix(0, name, DEV)
+    imp = W.c5_importance(name)
+    res = fq.quantize_nvfp4(x, imp.to(DEV), hadamard_n=16, check=True)
+    torch.cuda.synchronize()
+    xf = _host_f32(x)
+    del x
+    # S from the oracle's own rotation of the whole matrix, row chunk by row chunk
+    amax = np.float32(0)
+    for r0 in range(0, xf.shape[0], 1024):
+        amax = max(amax, np.abs(OH.block_hadamard(xf[r0:r0 + 1024], 16)).max())
+    S = np.float32(np.float32(amax) / np.float32(1536))
+    rows = _sample_rows(xf.shape[0], 64, 505)
+    ref = Q.quantize_nvfp4(xf[rows], imp.numpy(), global_scale=S, hadamard_n=16)
+    ref.global_scale = S
+    _check_nvfp4(res, ref, rows=rows)
