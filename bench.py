@@ -218,6 +218,17 @@ def run_other(args):
     return res
 
 
+def copy_calibration(nbytes=256 * 2**20, reps=3):
+    """A kernel of known traffic (reads and writes nbytes once each) whose HBM
+    counters calibrate FETCH_SIZE / WRITE_SIZE of the quantizer's kernels."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +238,8 @@ def main():
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB read + 256 MiB write elementwise kernel (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -238,6 +251,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     line = run_c2(args) if args.config == "c2" else run_other(args)
+    if args.copy_calib:
+        copy_calibration()
     print(json.dumps(line), flush=True)
 
 

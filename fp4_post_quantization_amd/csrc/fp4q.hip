@@ -59,6 +59,52 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const T *__restrict__ x,
   }
 }
 
+// Same maximum for a contiguous, unrotated matrix viewed as n_vec 16-byte
+// vectors; eight independent loads per thread are in flight per iteration.
+template <typename T>
+__device__ __forceinline__ uint32_t fold_abs_bits(uint32_t m, u32x4 v) {
+  if constexpr (sizeof(T) == 2) {  // two bf16 per dword
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = v[k] & 0x7FFFu, hi = (v[k] >> 16) & 0x7FFFu;
+      m = max(m, max(lo, hi));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m = max(m, v[k] & 0x7FFFFFFFu);
+  }
+  return m;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const u32x4 *__restrict__ v, int64_t n_vec,
+                                                              uint32_t *__restrict__ partials) {
+  constexpr int U = 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t m = 0;
+  for (; i + (U - 1) * stride < n_vec; i += U * stride) {
+    u32x4 a[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) a[k] = v[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < U; ++k) m = fold_abs_bits<T>(m, a[k]);
+  }
+  for (; i < n_vec; i += stride) m = fold_abs_bits<T>(m, v[i]);
+  if constexpr (sizeof(T) == 2) m <<= 16;  // bf16 pattern -> float32 pattern
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
+    partials[blockIdx.x] = r;
+  }
+}
+
 struct SweepArgs {
   const void *x;
   int64_t ld;
@@ -97,31 +143,31 @@ __device__ __forceinline__ bool importance_ok(const float w[16]) {
 
 // Loss of one candidate scale over this lane's 16 elements:
 // tree of fp32(e*e) [* w] with e = fp32(u - q*V), q = E2M1(fp32(u*R)).
-// q*V is exact, so fmaf(-q, V, u) is exactly fp32(u - q*V).
+// q*V is exact, so fmaf(-q, V, u) is exactly fp32(u - q*V).  The E2M1
+// rounding and the decode back to float are the hardware conversions.
 template <bool WMSE>
 __device__ __forceinline__ float lane_loss(const float u[16], const float w[16], float V, float R) {
-  float t[16];
+  float y[16], q[16], t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = u[i] * R;
+  fp4x8_to_f32(cvt_fp4x8(y), q);
+  fp4x8_to_f32(cvt_fp4x8(y + 8), q + 8);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float q = e2m1_round(u[i] * R);
-    const float e = fmaf(-q, V, u[i]);
+    const float e = fmaf(-q[i], V, u[i]);
     const float s = e * e;
     t[i] = WMSE ? w[i] * s : s;
   }
   return tree16(t);
 }
 
-// Packed codes of this lane's 16 elements for the chosen candidate.
+// Packed codes of this lane's 16 elements for the chosen candidate: the
+// sign of x is attached to the scaled magnitude before conversion.
 __device__ __forceinline__ uint2 lane_codes(const float u[16], uint32_t sgn, float R) {
-  uint32_t lo = 0, hi = 0;
+  float y[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c0 = e2m1_index(e2m1_round(u[i] * R)) | (((sgn >> i) & 1u) << 3);
-    const uint32_t c1 = e2m1_index(e2m1_round(u[i + 8] * R)) | (((sgn >> (i + 8)) & 1u) << 3);
-    lo |= c0 << (4 * i);
-    hi |= c1 << (4 * i);
-  }
-  return make_uint2(lo, hi);
+  for (int i = 0; i < 16; ++i) y[i] = as_f(as_u(u[i] * R) | (((sgn >> i) & 1u) << 31));
+  return make_uint2(cvt_fp4x8(y), cvt_fp4x8(y + 8));
 }
 
 // NVFP4 ScaleSweep: one lane per 16-element block.
@@ -230,11 +276,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
 // MXFP4 exponent sweep: two adjacent lanes per 32-element block.
 template <bool WMSE>
 __device__ __forceinline__ float lane_loss_pow2(const float u[16], const float w[16], float down, float up) {
-  float t[16];
+  float y[16], q[16], t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = u[i] * down;
+  fp4x8_to_f32(cvt_fp4x8(y), q);
+  fp4x8_to_f32(cvt_fp4x8(y + 8), q + 8);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float q = e2m1_round(u[i] * down);
-    const float e = fmaf(-q, up, u[i]);  // q * 2^E is exact
+    const float e = fmaf(-q[i], up, u[i]);  // q * 2^E is exact
     const float s = e * e;
     t[i] = WMSE ? w[i] * s : s;
   }
@@ -475,15 +524,27 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   const int total = (int)(rows * cpr);
   int n_partials = 0;
   if (!given) {
-    n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
-    with_dtype(dtype, [&](auto tp) {
-      using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
-      with_had(hadamard_n, [&](auto hc) {
-        constexpr int H = decltype(hc)::value;
-        hipLaunchKernelGGL((amax_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x, ld, cpr,
-                           total, partials);
+    const int64_t esz = dtype == FP4Q_BF16 ? 2 : 4;
+    if (hadamard_n == 0 && ld == cols) {
+      const int64_t n_vec = rows * cols * esz / 16;
+      n_partials = std::min<int64_t>(kAmaxGroups, (n_vec + kThreads * 8 - 1) / (kThreads * 8));
+      if (dtype == FP4Q_BF16)
+        hipLaunchKernelGGL((amax_flat_kernel<uint16_t>), dim3(n_partials), dim3(kThreads), 0, s,
+                           (const u32x4 *)x, n_vec, partials);
+      else
+        hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n_partials), dim3(kThreads), 0, s,
+                           (const u32x4 *)x, n_vec, partials);
+    } else {
+      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
+      with_dtype(dtype, [&](auto tp) {
+        using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+        with_had(hadamard_n, [&](auto hc) {
+          constexpr int H = decltype(hc)::value;
+          hipLaunchKernelGGL((amax_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x, ld,
+                             cpr, total, partials);
+        });
       });
-    });
+    }
   }
 
   SweepArgs a;

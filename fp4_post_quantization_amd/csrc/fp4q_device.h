@@ -18,7 +18,7 @@ constexpr int kLaneElems = 16;  // every lane owns 16 contiguous elements of a r
 constexpr int kWaveLanes = 64;
 constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kThreads = kWaveLanes * kWaves;
-constexpr int kAmaxGroups = 1024;  // max workgroups of the global-max pass
+constexpr int kAmaxGroups = 512;  // max workgroups of the global-max pass
 
 // Workspace layout (bytes): [0,4) status word, [256, 256 + 4*kAmaxGroups)
 // per-workgroup maxima of |x| as float32 bit patterns.
@@ -146,23 +146,42 @@ __device__ __forceinline__ void fwht(float z[16], int lane) {
 }
 
 // ------------------------------------------------------------ E2M1 ----
-// Nearest E2M1 magnitude to y >= 0, ties to the even code index, saturating
-// at 6.  Adding M = 2^(e+22), e = floor(log2(max(y, 1))), makes the float32
-// spacing around M equal to the E2M1 step of y's binade (0.5 below 2, 1 in
-// [2, 4), 2 from 4), so the addition itself rounds y to that step with
-// ties-to-even; subtracting M is exact.  y is capped at 8 first (every
-// y >= 6 saturates anyway).
-__device__ __forceinline__ float e2m1_round(float y) {
-  const float yc = fminf(y, 8.0f);
-  const float M = as_f((as_u(fmaxf(yc, 1.0f)) & 0x7F800000u) + (22u << 23));
-  const float q = (yc + M) - M;
-  return fminf(q, 6.0f);
+// gfx950 packed FP4 conversions with a unit scale: nearest E2M1 value,
+// ties to the even code, saturation at 6 (Inf included), the sign of -0.0
+// kept, the first operand in the low nibble of the selected byte.  This
+// matches the E2M1 definition on every float32 in [0, 16) (checked against
+// an independent software rounding on the GPU).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Writes the codes of (y0, y1) into byte BYTE of old (other bytes kept).
+template <int BYTE>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, BYTE);
 }
 
-// Code index 0..7 of an E2M1 magnitude q (one of the eight values).
-__device__ __forceinline__ uint32_t e2m1_index(float q) {
-  // 0, .5, 1, 1.5 -> 2q; 2, 3 -> q + 2; 4 -> 6; 6 -> 7
-  return q < 2.0f ? (uint32_t)(q * 2.0f) : (q < 4.0f ? (uint32_t)q + 2u : (q < 5.0f ? 6u : 7u));
+// The two E2M1 values (signed) held by byte BYTE of pk.
+template <int BYTE>
+__device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t pk) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pk, 1.0f, BYTE);
+}
+
+// Codes of 8 values y[0..8) packed into one dword (element 2k in the low
+// nibble of byte k).
+__device__ __forceinline__ uint32_t cvt_fp4x8(const float y[8]) {
+  uint32_t pk = 0;
+  pk = cvt_fp4x2<0>(pk, y[0], y[1]);
+  pk = cvt_fp4x2<1>(pk, y[2], y[3]);
+  pk = cvt_fp4x2<2>(pk, y[4], y[5]);
+  pk = cvt_fp4x2<3>(pk, y[6], y[7]);
+  return pk;
+}
+
+// E2M1 values of the 8 codes in pk.
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t pk, float q[8]) {
+  const f32x2 a = fp4x2_to_f32<0>(pk), b = fp4x2_to_f32<1>(pk);
+  const f32x2 c = fp4x2_to_f32<2>(pk), d = fp4x2_to_f32<3>(pk);
+  q[0] = a.x; q[1] = a.y; q[2] = b.x; q[3] = b.y;
+  q[4] = c.x; q[5] = c.y; q[6] = d.x; q[7] = d.y;
 }
 
 // ------------------------------------------------------------ E4M3 ----

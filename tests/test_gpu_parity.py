@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import formats as F
 from oracle import quant as Q
 from oracle import hadamard as OH
 
@@ -233,6 +234,31 @@ def test_mxfp4_small(rows, cols, window):
     imp = W.random_importance(cols, seed=cols + 1)
     r = fq.quantize_mxfp4(x.to(DEV), imp.to(DEV), window=window, check=True)
     _check_mxfp4(r, Q.quantize_mxfp4(_host_f32(x), imp.numpy(), window=window))
+
+
+def test_e2m1_rounding_dense_through_mxfp4():
+    """The E2M1 rounding of the library on every float32 within 2**14 steps
+    of each midpoint and on every 256th float32 in [0, 6]: MXFP4 blocks led
+    by 6.0 get the scale 2**0 under the AbsMax window, so each code is the
+    E2M1 rounding of |x| itself.  Signs alternate to cover the sign bit."""
+    mids = F.E2M1_MIDPOINTS.view(np.uint32).astype(np.int64)
+    near = (mids[:, None] + np.arange(-2**14, 2**14)[None, :]).ravel()
+    sweep = np.arange(0, int(np.float32(6.0).view(np.uint32)) + 1, 256, dtype=np.int64)
+    vals = np.concatenate([near, sweep]).astype(np.uint32).view(np.float32)
+    vals = vals[(vals >= 0) & (vals <= 6)]
+    n = -(-vals.size // 31)
+    body = np.zeros(n * 31, dtype=np.float32)
+    body[:vals.size] = vals
+    body[1::2] *= -1
+    x = np.empty((n, 32), dtype=np.float32)
+    x[:, 0] = 6.0
+    x[:, 1:] = body.reshape(n, 31)
+    fq = _fp4()
+    r = fq.quantize_mxfp4(torch.from_numpy(x).to(DEV), window=(0, 0), check=True)
+    torch.cuda.synchronize()
+    ref = Q.quantize_mxfp4(x, window=(0, 0))
+    assert np.all(ref.scales == 127)
+    _check_mxfp4(r, ref)
 
 
 # ---------------------------------------------------------- dequant ----
