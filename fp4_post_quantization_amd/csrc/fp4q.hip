@@ -4,8 +4,8 @@
 // Work decomposition (all kernels): a lane owns 16 contiguous elements of a
 // row ("chunk"); an NVFP4 block is one lane, an MXFP4 block two adjacent
 // lanes, an n-point Hadamard group n/16 adjacent lanes.  Block losses are
-// reduced inside the lane (plus one DPP exchange for MXFP4), so the
-// candidate sweep needs no LDS and no barriers.
+// accumulated inside the lane (plus one DPP exchange for MXFP4), so the
+// candidate sweep needs no LDS traffic for data and no barriers.
 //
 // The quantize kernels map a wave to a tile of 64 consecutive chunks of a
 // column band times a few rows; the per-column importance of WMSE is loaded
@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <stdlib.h>
 
 #include <algorithm>
 #include <type_traits>
@@ -141,36 +143,88 @@ __device__ __forceinline__ bool importance_ok(const float w[16]) {
   return ok;
 }
 
-// Loss of one candidate scale over this lane's 16 elements:
-// tree of fp32(e*e) [* w] with e = fp32(u - q*V), q = E2M1(fp32(u*R)).
-// q*V is exact, so fmaf(-q, V, u) is exactly fp32(u - q*V).  The E2M1
-// rounding and the decode back to float are the hardware conversions.
-template <bool WMSE>
-__device__ __forceinline__ float lane_loss(const float u[16], const float w[16], float V, float R) {
-  float y[16], q[16], t[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = u[i] * R;
-  fp4x8_to_f32(cvt_fp4x8(y), q);
-  fp4x8_to_f32(cvt_fp4x8(y + 8), q + 8);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float e = fmaf(-q[i], V, u[i]);
-    const float s = e * e;
-    t[i] = WMSE ? w[i] * s : s;
-  }
-  return tree16(t);
+// Codes of 8 values, optionally halved first: the scale operand 2.0 makes
+// the hardware convert y / 2 (exactly, checked on every float32 below 2^21).
+// All four bytes of the result are written, so `old` only carries a register.
+template <bool HALF>
+__device__ __forceinline__ uint32_t cvt8(const float y[8], uint32_t old) {
+  const float sc = HALF ? 2.0f : 1.0f;
+  old = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[0], y[1], sc, 0);
+  old = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[2], y[3], sc, 1);
+  old = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[4], y[5], sc, 2);
+  old = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y[6], y[7], sc, 3);
+  return old;
 }
 
-// Packed codes of this lane's 16 elements for the chosen candidate: the
-// sign of x is attached to the scaled magnitude before conversion.
-__device__ __forceinline__ uint2 lane_codes(const float u[16], uint32_t sgn, float R) {
-  float y[16];
+// Loss of one candidate over this lane's 16 elements from their codes:
+// e_i = fp32(us_i - q_i*V), summed in element order with one rounding per
+// term, acc <- fma(t_i, e_i, acc), t_i = e_i (MSE) or fp32(w_i * e_i) (WMSE).
+// us and q carry the sign of x (the conversions are sign-symmetric), so e_i
+// is the error up to its sign and t_i * e_i is unchanged; q*V is exact, so
+// fmaf(-q, V, us) is exactly fp32(us - q*V).
+template <bool WMSE>
+__device__ __forceinline__ float loss_of_codes(const float us[16], const float w[16], uint32_t pk0,
+                                               uint32_t pk1, float V) {
+  float q[16];
+  fp4x8_to_f32(pk0, q);
+  fp4x8_to_f32(pk1, q + 8);
+  float acc = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = as_f(as_u(u[i] * R) | (((sgn >> i) & 1u) << 31));
-  return make_uint2(cvt_fp4x8(y), cvt_fp4x8(y + 8));
+  for (int i = 0; i < 16; ++i) {
+    const float e = fmaf(-q[i], V, us[i]);
+    acc = fmaf(WMSE ? w[i] * e : e, e, acc);
+  }
+  return acc;
+}
+
+// Keep the candidate with the least loss; among equal losses the smallest
+// pattern / exponent, whatever order the candidates are visited in.
+__device__ __forceinline__ void consider(float L, int p, bool ok, float &Lbest, int &pbest) {
+  const bool take = ok & ((L < Lbest) | ((L == Lbest) & (p < pbest)));
+  Lbest = take ? L : Lbest;
+  pbest = take ? p : pbest;
+}
+
+// Raw 16-element chunk as loaded (for next-row prefetch).
+template <typename T>
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  u32x4 v[2];
+};
+template <>
+struct Raw<float> {
+  f32x4 v[4];
+};
+
+__device__ __forceinline__ void load_raw(const uint16_t *p, Raw<uint16_t> &r) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+  r.v[0] = __builtin_nontemporal_load(q);
+  r.v[1] = __builtin_nontemporal_load(q + 1);
+}
+__device__ __forceinline__ void load_raw(const float *p, Raw<float> &r) {
+  const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.v[k] = __builtin_nontemporal_load(q + k);
+}
+__device__ __forceinline__ void widen(const Raw<uint16_t> &r, float z[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t w = r.v[k >> 2][k & 3];
+    z[2 * k] = as_f(w << 16);
+    z[2 * k + 1] = as_f(w & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen(const Raw<float> &r, float z[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) z[k] = r.v[k >> 2][k & 3];
 }
 
 // NVFP4 ScaleSweep: one lane per 16-element block.
+//
+// Candidates p and p + 8 (both >= 8) have E4M3 values V and 2V, so
+// fp32(u * R[p+8]) = fp32(u * R[p]) / 2 exactly and the pair shares one set
+// of products u * R; the upper member is converted with the halving scale.
 template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   __shared__ float Vtab[128], Rtab[128];
@@ -227,69 +281,86 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   }
   if (!active) return;  // whole Hadamard groups are active or not together
 
-  const T *x = static_cast<const T *>(a.x);
+  const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
   const int bpr = a.cpr;  // blocks per row
+  const int lo = a.off_lo, hi = a.off_hi;
+  Raw<T> cur, nxt;
+  load_raw(xc + (int64_t)r0 * a.ld, cur);
+  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
   for (int r = r0; r < r1; ++r) {
+    if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
     float z[16];
-    load16(x + (int64_t)r * a.ld + (int64_t)c * 16, z);
+    widen(cur, z);
     if constexpr (HAD != 0) fwht<HAD>(z, lane);
 
-    float u[16];
-    uint32_t sgn = 0;
+    // signed magnitudes in units of S: |us| = fp32(|x| * S_inv) exactly
+    float us[16];
     float amax = 0.0f;
     bool finite = true;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sgn |= (as_u(z[i]) >> 31) << i;
       finite &= fabsf(z[i]) <= 3.402823466e38f;
-      u[i] = fabsf(z[i]) * S_inv;
-      amax = fmaxf(amax, u[i]);
+      us[i] = z[i] * S_inv;
+      amax = fmaxf(amax, fabsf(us[i]));
     }
     // with a computed scale the global-max pass already reported non-finite x
     if (a.given_scale && !finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
     const float t = amax / 6.0f;  // correctly rounded
     int base = e4m3_rne_sat(t);
     base = base < 1 ? 1 : base;
-    const int plo = max(1, base + a.off_lo);
+    const int plo = max(1, base + lo);
 
-    float Lbest = 0.0f;
+    float Lbest = __builtin_inff();
     int pbest = plo;
-    for (int o = a.off_lo; o <= a.off_hi; ++o) {
+    for (int o = lo; o <= hi; ++o) {
+      // offsets pair up octet by octet: [lo, lo+8) with [lo+8, lo+16), ...
+      if (((o - lo) >> 3) & 1) continue;  // visited as the upper member of a pair
       const int p = base + o;
       const bool ok = (p >= 1) & (p <= 126);
       const int pc = min(max(p, 1), 126);
-      const float L = lane_loss<WMSE>(u, w, Vtab[pc], Rtab[pc]);
-      const bool take = ok & ((p == plo) | (L < Lbest));
-      Lbest = take ? L : Lbest;
-      pbest = take ? p : pbest;
+      const float R = Rtab[pc], V = Vtab[pc];
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = us[i] * R;
+      k0 = cvt8<false>(y, k0);
+      k1 = cvt8<false>(y + 8, k1);
+      if (o + 8 <= hi) {
+        const int ph = p + 8;
+        const bool okh = (ph >= 1) & (ph <= 126);
+        const int phc = min(max(ph, 1), 126);
+        if (p >= 8) {
+          h0 = cvt8<true>(y, h0);
+          h1 = cvt8<true>(y + 8, h1);
+        } else {  // E4M3 subnormal lower member: no exact factor 2
+          const float Rh = Rtab[phc];
+          float y2[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y2[i] = us[i] * Rh;
+          h0 = cvt8<false>(y2, h0);
+          h1 = cvt8<false>(y2 + 8, h1);
+        }
+        consider(loss_of_codes<WMSE>(us, w, h0, h1, Vtab[phc]), ph, okh, Lbest, pbest);
+      }
+      consider(loss_of_codes<WMSE>(us, w, k0, k1, V), p, ok, Lbest, pbest);
     }
 
-    const uint2 pk = lane_codes(u, sgn, Rtab[pbest]);
-    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = pk;
+    const float Rb = Rtab[pbest];
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = us[i] * Rb;
+    k0 = cvt8<false>(y, k0);
+    k1 = cvt8<false>(y + 8, k1);
+    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
     const int64_t bi = (int64_t)r * bpr + c;
     a.scales[bi] = (uint8_t)pbest;
     if (a.loss) a.loss[bi] = Lbest * SS;
     if (a.offs) a.offs[bi] = (int8_t)(pbest - base);
+    cur = nxt;
   }
 }
 
-// MXFP4 exponent sweep: two adjacent lanes per 32-element block.
-template <bool WMSE>
-__device__ __forceinline__ float lane_loss_pow2(const float u[16], const float w[16], float down, float up) {
-  float y[16], q[16], t[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = u[i] * down;
-  fp4x8_to_f32(cvt_fp4x8(y), q);
-  fp4x8_to_f32(cvt_fp4x8(y + 8), q + 8);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float e = fmaf(-q[i], up, u[i]);  // q * 2^E is exact
-    const float s = e * e;
-    t[i] = WMSE ? w[i] * s : s;
-  }
-  return tree16(t);
-}
-
+// MXFP4 exponent sweep: two adjacent lanes per 32-element block.  Exponents
+// E and E + 1 form pairs: fp32(x * 2^-(E+1)) = fp32(x * 2^-E) / 2.
 template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -310,51 +381,79 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   }
   if (!active) return;
 
-  const T *x = static_cast<const T *>(a.x);
+  const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
   const int bpr = a.cpr / 2;
   const bool even = (lane & 1) == 0;
+  const int lo = a.off_lo, hi = a.off_hi;
+  Raw<T> cur, nxt;
+  load_raw(xc + (int64_t)r0 * a.ld, cur);
+  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
   for (int r = r0; r < r1; ++r) {
+    if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
     float z[16];
-    load16(x + (int64_t)r * a.ld + (int64_t)c * 16, z);
+    widen(cur, z);
     if constexpr (HAD != 0) fwht<HAD>(z, lane);
 
-    float u[16];
-    uint32_t sgn = 0;
     float amax = 0.0f;
     bool finite = true;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sgn |= (as_u(z[i]) >> 31) << i;
-      u[i] = fabsf(z[i]);
-      finite &= u[i] <= 3.402823466e38f;
-      amax = fmaxf(amax, u[i]);
+      finite &= fabsf(z[i]) <= 3.402823466e38f;
+      amax = fmaxf(amax, fabsf(z[i]));
     }
     if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
     amax = fmaxf(amax, xor_lane<1>(amax));
     const int eb = mx_base_exponent(amax);
-    const int elo = max(-127, eb + a.off_lo);
+    const int elo = max(-127, eb + lo);
 
-    float Lbest = 0.0f;
+    float Lbest = __builtin_inff();
     int ebest = elo;
-    for (int o = a.off_lo; o <= a.off_hi; ++o) {
+    for (int o = lo; o <= hi; o += 2) {
       const int E = eb + o;
       const bool ok = (E >= -127) & (E <= 127);
       const int Ec = min(max(E, -127), 127);
-      const float half = lane_loss_pow2<WMSE>(u, w, pow2f(-Ec), pow2f(Ec));
-      const float L = half + xor_lane<1>(half);
-      const bool take = ok & ((E == elo) | (L < Lbest));
-      Lbest = take ? L : Lbest;
-      ebest = take ? E : ebest;
+      const float down = pow2f(-Ec);
+      float y[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = z[i] * down;
+      k0 = cvt8<false>(y, k0);
+      k1 = cvt8<false>(y + 8, k1);
+      if (o + 1 <= hi) {
+        const int E1 = E + 1;
+        const bool ok1 = (E1 >= -127) & (E1 <= 127);
+        const int E1c = min(max(E1, -127), 127);
+        if (E >= -127) {
+          h0 = cvt8<true>(y, h0);
+          h1 = cvt8<true>(y + 8, h1);
+        } else {  // lower member clamped: convert the upper one directly
+          const float d1 = pow2f(-E1c);
+          float y2[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y2[i] = z[i] * d1;
+          h0 = cvt8<false>(y2, h0);
+          h1 = cvt8<false>(y2 + 8, h1);
+        }
+        const float half1 = loss_of_codes<WMSE>(z, w, h0, h1, pow2f(E1c));
+        consider(half1 + xor_lane<1>(half1), E1, ok1, Lbest, ebest);
+      }
+      const float half0 = loss_of_codes<WMSE>(z, w, k0, k1, pow2f(Ec));
+      consider(half0 + xor_lane<1>(half0), E, ok, Lbest, ebest);
     }
 
-    const uint2 pk = lane_codes(u, sgn, pow2f(-ebest));
-    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = pk;
+    const float db = pow2f(-ebest);
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = z[i] * db;
+    k0 = cvt8<false>(y, k0);
+    k1 = cvt8<false>(y + 8, k1);
+    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
     if (even) {
       const int64_t bi = (int64_t)r * bpr + (c >> 1);
       a.scales[bi] = (uint8_t)(ebest + 127);
       if (a.loss) a.loss[bi] = Lbest;
       if (a.offs) a.offs[bi] = (int8_t)(ebest - eb);
     }
+    cur = nxt;
   }
 }
 
@@ -435,9 +534,11 @@ static void with_dtype(fp4q_dtype_t dt, F &&f) {
 
 static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Rows per wave tile: enough tiles to give every SIMD several waves.
+// Rows per wave tile: enough tiles to give every SIMD several waves.  The
+// target tile count can be overridden with FP4Q_TILE_TARGET (tuning only).
 static int pick_rows_per_tile(int rows, int nbands) {
-  const int64_t target_tiles = 8192;
+  const char *now = getenv("FP4Q_TILE_TARGET");
+  const int64_t target_tiles = (now && atoi(now) > 0) ? atoi(now) : 8192;
   const int64_t units = (int64_t)rows * nbands;
   int rpt = (int)((units + target_tiles - 1) / target_tiles);
   return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);

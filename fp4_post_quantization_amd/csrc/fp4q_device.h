@@ -220,14 +220,4 @@ __device__ __forceinline__ int mx_base_exponent(float a) {
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
-// ------------------------------------------------------------ trees ----
-// Contiguous pairwise float32 tree sum of 16 values.
-__device__ __forceinline__ float tree16(const float t[16]) {
-  float a[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = t[2 * i] + t[2 * i + 1];
-  float b0 = a[0] + a[1], b1 = a[2] + a[3], b2 = a[4] + a[5], b3 = a[6] + a[7];
-  return (b0 + b1) + (b2 + b3);
-}
-
 }  // namespace fp4q

@@ -118,16 +118,17 @@ size_t fp4q_workspace_bytes(void);
  *               (out; may be NULL).
  *   workspace   fp4q_workspace_bytes() bytes of device memory.
  *
- * Computation (every float32 step rounds to nearest even, no fused
- * multiply-add except where the product is exact):
+ * Computation (every float32 step rounds to nearest even; fused
+ * multiply-adds only where written):
  *   S = fp32(max|x| / 1536), S_inv = fp32(1/S) (0 if S = 0);
  *   u = fp32(|x| * S_inv); per block t = fp32(max u / 6);
  *   base = max(1, nearest E4M3 pattern to t, ties to even, saturating 0x7E);
  *   for p = max(1, base+off_lo) .. min(126, base+off_hi): V = E4M3(p),
  *   R = fp32(1/V), q = E2M1 nearest to fp32(u*R) (ties to even index,
- *   saturating at 6), e = fp32(u - q*V), tau = fp32(e*e) [WMSE: fp32(w*tau)],
- *   L_p = contiguous pairwise float32 tree sum of tau over the block;
- *   the chosen p is the smallest p with the least L_p.
+ *   saturating at 6), e = fp32(u - q*V); L_p sums the block's terms in
+ *   element order with one rounding each: acc = fma(t, e, acc) from 0,
+ *   t = e (MSE) or fp32(w*e) (WMSE); the chosen p is the smallest p with
+ *   the least L_p.
  */
 fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
                                   int64_t ld, const float *importance, int block, fp4q_loss_t loss,
@@ -153,8 +154,9 @@ fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t row
  * Computation: u = |x|; per block E_base = least E with 6 * 2^E >= max u,
  * clamped to [-127, 127]; for E = max(-127, E_base+off_lo) ..
  * min(127, E_base+off_hi): q = E2M1 nearest to fp32(u * 2^-E),
- * e = fp32(u - q*2^E), tau and the pairwise tree over 32 as above; the
- * smallest E with the least loss is chosen.
+ * e = fp32(u - q*2^E); the loss is fp32(L_a + L_b), L_a and L_b the fused
+ * in-order sums above over the block's two 16-element halves; the smallest
+ * E with the least loss is chosen.
  */
 fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
                                   int64_t ld, const float *importance, int block, fp4q_loss_t loss,

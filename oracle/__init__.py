@@ -31,9 +31,11 @@ Modules
   study     float64 exhaustive-sweep tools used to pin the lemmas
 
 Parity-unpinned items (no value printed on the pages fixes them): the FP32
-evaluation order of the per-candidate loss (a contiguous pairwise tree) and
-the reciprocal-multiply form y = u * fp32(1/V).  They are this oracle's
-canonical reading; the tests pin everything around them.
+evaluation order of the per-candidate loss (terms summed in element order
+with one rounding each, a fused multiply-add) and the reciprocal-multiply
+form y = u * fp32(1/V).  They are this oracle's canonical reading; the tests
+pin everything around them (the float32 FMA emulation against exact
+rational arithmetic).
 """
 
 from . import formats, quant, hadamard, study  # noqa: F401

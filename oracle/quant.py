@@ -23,11 +23,12 @@ NVFP4 ("Resumo Técnico: ScaleSweep")
      p = base + o for o in [lo, hi] (default [-3, 7] for MSE, [-8, 7] for
      WMSE), clipped to 1..126.
   5. Per candidate, with V = E4M3 value of p and R = fp32(1/V):
-       y = fp32(u * R); q = RNE_E2M1(y); d = q * V (exact);
-       e = fp32(u - d); tau = fp32(e * e)            (MSE)
-                        tau = fp32(w_col * fp32(e * e))  (WMSE; importance of
-                              the element's column, 1. Objetivos de Otimização)
-       L_p = contiguous pairwise tree sum of tau over the block in float32.
+       y = fp32(u * R); q = RNE_E2M1(y); d = q * V (exact); e = fp32(u - d);
+       L_p = the block's squared errors summed in element order, each term
+       added with a single rounding: acc <- fp32(t_i * e_i + acc) (a fused
+       multiply-add), acc starting at 0, with t_i = e_i for MSE and
+       t_i = fp32(w_col * e_i) for WMSE (importance of the element's column,
+       1. Objetivos de Otimização).
   6. p* = smallest p whose L_p is the minimum over the candidates.
   7. Outputs: scale byte p*; code = (signbit(x) << 3) | index(q at p*);
      offset = p* - base; block loss = fp32(L_{p*} * fp32(S * S)); S.
@@ -38,7 +39,9 @@ grid; "Resumo Técnico: TORQ", B. Rotação de Alinhamento Micro, S-step)
   to [-127, 127] (a_b = 0 gives -127): the block maximum maps onto the largest
   code without clipping.  Candidates E in [E_base + lo, E_base + hi] clipped to
   [-127, 127] (default lo, hi = -1, 0); per E: y = fp32(u * 2**-E);
-  q = RNE_E2M1(y); d = q * 2**E (exact); e, tau, L as above (blocks of 32).
+  q = RNE_E2M1(y); d = q * 2**E (exact); e as above; L = fp32(L_a + L_b)
+  where L_a, L_b are the fused in-order sums above over the block's two
+  16-element halves.
   E* = smallest E with the minimum loss.  Scale byte E* + 127, offset
   E* - E_base, loss L_{E*} (no global scale).
 """
@@ -51,16 +54,43 @@ from . import formats as F
 from .hadamard import block_hadamard
 
 
-def tree_sum_f32(v):
-    """Contiguous pairwise tree sum over the last axis (length a power of
-    two): T(v[0:n]) = fp32(T(v[0:n/2]) + T(v[n/2:n])), one float32 add each."""
-    v = np.asarray(v, dtype=np.float32)
-    n = v.shape[-1]
-    if n & (n - 1):
-        raise ValueError("block length must be a power of two")
-    while v.shape[-1] > 1:
-        v = v[..., 0::2] + v[..., 1::2]
-    return v[..., 0]
+def fma_f32(a, b, c):
+    """fp32(a * b + c) rounded once (to nearest, ties to even), for float32
+    inputs, computed exactly in float64: a * b is exact there (two 24-bit
+    significands); s = fp64(a*b + c) carries an exact error err (Knuth's
+    two-sum), and rounding s to float32 is only wrong when s lies exactly
+    half-way between two float32 values while err is not zero; then the
+    sign of err picks the side."""
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a64 * b64
+    s = p + c64
+    bv = s - p
+    err = (p - (s - bv)) + (c64 - bv)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    up = np.nextafter(r, np.float32(np.inf)).astype(np.float64)
+    dn = np.nextafter(r, np.float32(-np.inf)).astype(np.float64)
+    lo = np.where(r64 <= s, r64, dn)
+    hi = np.where(r64 >= s, r64, up)
+    with np.errstate(invalid="ignore"):
+        tie = (lo != hi) & (s - lo == hi - s)
+    fix = tie & (err != 0)
+    return np.where(fix, np.where(err > 0, hi, lo), r64).astype(np.float32)
+
+
+def fused_sum_sq(e, w=None):
+    """Squared errors of the last axis summed in order with one rounding per
+    term: acc <- fma(t_i, e_i, acc), acc = 0 first, t_i = e_i (MSE) or
+    fp32(w_i * e_i) (WMSE)."""
+    e = np.asarray(e, dtype=np.float32)
+    acc = np.zeros(e.shape[:-1], dtype=np.float32)
+    for i in range(e.shape[-1]):
+        ei = e[..., i]
+        t = ei if w is None else (np.asarray(w, dtype=np.float32)[..., i] * ei).astype(np.float32)
+        acc = fma_f32(t, ei, acc)
+    return acc
 
 
 def pack_nibbles(codes):
@@ -172,10 +202,7 @@ def quantize_nvfp4(x, importance=None, window=None, block=16,
         q = F.e2m1_value(F.e2m1_rne_index(y))
         d = (q * V).astype(np.float32)
         e = (ub - d).astype(np.float32)
-        tau = (e * e).astype(np.float32)
-        if wmse:
-            tau = (w * tau).astype(np.float32)
-        losses[..., k] = tree_sum_f32(tau)
+        losses[..., k] = fused_sum_sq(e, np.broadcast_to(w, e.shape) if wmse else None)
         valid[..., k] = ok
 
     k_best = _first_argmin(losses, valid)
@@ -277,10 +304,10 @@ def quantize_mxfp4(x, importance=None, window=(-1, 0), block=32, hadamard_n=0):
         q = F.e2m1_value(F.e2m1_rne_index(y))
         d = (q * up).astype(np.float32)
         e = (ub - d).astype(np.float32)
-        tau = (e * e).astype(np.float32)
-        if wmse:
-            tau = (w * tau).astype(np.float32)
-        losses[..., k] = tree_sum_f32(tau)
+        halves = e.reshape(e.shape[:-1] + (2, 16))
+        wh = np.broadcast_to(w, e.shape).reshape(halves.shape) if wmse else None
+        part = fused_sum_sq(halves, wh)
+        losses[..., k] = (part[..., 0] + part[..., 1]).astype(np.float32)
         valid[..., k] = ok
 
     k_best = _first_argmin(losses, valid)

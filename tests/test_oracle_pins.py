@@ -118,11 +118,73 @@ def test_mx_base_exponent_frexp_rule():
 
 
 # ------------------------------------------------------ tree and pack ----
-def test_tree_sum_golden_order():
-    for row in _read_golden("tree_sum.txt"):
-        vals, expect = row.split("|")
-        v = np.array([float(s) for s in vals.split()], dtype=np.float32)
-        assert float(Q.tree_sum_f32(v)) == float(expect), row
+def test_fused_loss_golden():
+    for row in _read_golden("fused_loss.txt"):
+        parts = [p.strip() for p in row.split("|")]
+        e = np.zeros(16, dtype=np.float32)
+        vals = [float.fromhex(v) for v in parts[0].split()]
+        e[:len(vals)] = vals
+        w = None
+        if parts[1].startswith("w:"):
+            w = np.ones(16, dtype=np.float32)
+            wv = [float.fromhex(v) for v in parts[1][2:].split()]
+            w[:len(wv)] = wv
+        expect = np.float32(float.fromhex(parts[-1]))
+        got = Q.fused_sum_sq(e[None, :], None if w is None else w[None, :])[0]
+        assert got.view(np.uint32) == expect.view(np.uint32), (row, got, expect)
+
+
+def _rn32_exact(v):
+    """Nearest float32 to the rational v (ties to an even significand),
+    found by exact comparisons; independent of the float64 emulation."""
+    from fractions import Fraction
+    if v == 0:
+        return np.float32(0.0)
+    lo = np.float32(float(v))
+    inf32 = np.float32(np.inf)
+    while Fraction(float(lo)) > v:
+        lo = np.nextafter(lo, -inf32)
+    while Fraction(float(np.nextafter(lo, inf32))) <= v:
+        lo = np.nextafter(lo, inf32)
+    if Fraction(float(lo)) == v:
+        return lo
+    hi = np.nextafter(lo, inf32)
+    dl, dh = v - Fraction(float(lo)), Fraction(float(hi)) - v
+    if dl != dh:
+        return lo if dl < dh else hi
+    return lo if (lo.view(np.uint32) & 1) == 0 else hi
+
+
+def test_fma_emulation_against_exact_rationals():
+    """fma_f32 equals the exactly rounded a*b + c on random triples and on
+    triples built so that float64 rounding lands exactly on a float32
+    midpoint (where a plain double rounding would go wrong)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(22)
+    n = 3000
+    a = (rng.standard_normal(n) * np.exp(rng.uniform(-20, 20, n))).astype(np.float32)
+    b = (rng.standard_normal(n) * np.exp(rng.uniform(-20, 20, n))).astype(np.float32)
+    c = (rng.standard_normal(n) * np.exp(rng.uniform(-30, 30, n))).astype(np.float32)
+    # adversarial: a*b = half an ulp of c, nudged by 2^-46 relative either way
+    cs = np.abs((rng.standard_normal(400) * np.exp(rng.uniform(-10, 10, 400)))).astype(np.float32)
+    half = (np.spacing(cs) / 2).astype(np.float64)
+    k = np.round(np.log2(half) / 2).astype(np.int64)
+    a2 = np.ldexp(np.float64(1 + 2.0 ** -23), k).astype(np.float32)
+    sign = np.where(rng.random(400) < 0.5, 1.0, -1.0)
+    b2 = np.ldexp(1 + sign * 2.0 ** -23, np.log2(half).astype(np.int64) - k).astype(np.float32)
+    A = np.concatenate([a, a2, -a2])
+    B = np.concatenate([b, b2, b2])
+    C = np.concatenate([c, cs, cs])
+    got = Q.fma_f32(A, B, C)
+    for i in range(A.size):
+        v = Fraction(float(A[i])) * Fraction(float(B[i])) + Fraction(float(C[i]))
+        ref = _rn32_exact(v)
+        assert got[i].view(np.uint32) == np.float32(ref).view(np.uint32) or (v == 0 and got[i] == 0), \
+            (A[i], B[i], C[i], got[i], ref)
+    # the adversarial set really contains float64 midpoint landings
+    s = A.astype(np.float64) * B.astype(np.float64) + C.astype(np.float64)
+    naive = s.astype(np.float32)
+    assert np.count_nonzero(naive != got) > 50
 
 
 def test_nibble_order():
