@@ -19,10 +19,40 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "../../include/fp4q.h"
+#include "fp4q.h"
 #include "fp4q_device.h"
 
 namespace fp4q {
+
+// ============================================================ tables =====
+
+// Values and correctly rounded reciprocals of the non-negative E4M3 patterns
+// (index = pattern; entries 0 and 127 are 1.0), evaluated at compile time.
+struct E4M3Tables {
+  float v[128];
+  float r[128];
+};
+
+constexpr float e4m3_value_const(int p) {
+  float scale = 1.0f;  // 2^(exponent - 7)
+  const int ef = p >> 3;
+  if (ef == 0) return (float)p * 0.001953125f;  // subnormal p * 2^-9
+  for (int k = 7; k > ef; --k) scale *= 0.5f;
+  for (int k = 7; k < ef; ++k) scale *= 2.0f;
+  return (1.0f + (float)(p & 7) * 0.125f) * scale;
+}
+
+constexpr E4M3Tables make_e4m3_tables() {
+  E4M3Tables t{};
+  for (int p = 0; p < 128; ++p) {
+    const float v = (p >= 1 && p <= 126) ? e4m3_value_const(p) : 1.0f;
+    t.v[p] = v;
+    t.r[p] = 1.0f / v;  // IEEE division, correctly rounded
+  }
+  return t;
+}
+
+__constant__ E4M3Tables kE4M3 = make_e4m3_tables();
 
 // ============================================================ kernels ====
 
@@ -185,6 +215,71 @@ __device__ __forceinline__ void consider(float L, int p, bool ok, float &Lbest, 
   pbest = take ? p : pbest;
 }
 
+// ScaleSweep candidate search for one block (this lane's 16 elements).
+// Offsets pair up octet by octet, [lo, lo+8) with [lo+8, lo+16), ...; the
+// lower and the upper members are tracked as two running minima, each
+// visited in ascending pattern order with a strict "<", and merged with the
+// smallest-pattern tie rule.  CHECKED handles windows that leave the normal
+// E4M3 range (clamping, validity, subnormal lower members).  Returns p*.
+template <bool WMSE, bool CHECKED>
+__device__ __forceinline__ int nv_sweep(const float us[16], const float w[16], int base, int lo, int hi,
+                                        const float *Vtab, const float *Rtab, float &Lout) {
+  const int plo = max(1, base + lo);
+  float La = __builtin_inff(), Lb = __builtin_inff();
+  int pa = plo, pb = 0x7FFFFFFF;
+  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
+  for (int o = lo; o <= hi; ++o) {
+    if (((o - lo) >> 3) & 1) continue;  // visited as the upper member of a pair
+    const int p = base + o;
+    bool ok = true;
+    int pc = p;
+    if constexpr (CHECKED) {
+      ok = (p >= 1) & (p <= 126);
+      pc = min(max(p, 1), 126);
+    }
+    float y[16];
+    const float R = Rtab[pc];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = us[i] * R;
+    k0 = cvt8<false>(y, k0);
+    k1 = cvt8<false>(y + 8, k1);
+    if (o + 8 <= hi) {
+      const int ph = p + 8;
+      bool okh = true;
+      int phc = ph;
+      if constexpr (CHECKED) {
+        okh = (ph >= 1) & (ph <= 126);
+        phc = min(max(ph, 1), 126);
+        if (p >= 8) {
+          h0 = cvt8<true>(y, h0);
+          h1 = cvt8<true>(y + 8, h1);
+        } else {  // E4M3 subnormal lower member: no exact factor 2
+          const float Rh = Rtab[phc];
+          float y2[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y2[i] = us[i] * Rh;
+          h0 = cvt8<false>(y2, h0);
+          h1 = cvt8<false>(y2 + 8, h1);
+        }
+      } else {
+        h0 = cvt8<true>(y, h0);  // y / 2 == fp32(us * R[p + 8]) exactly
+        h1 = cvt8<true>(y + 8, h1);
+      }
+      const float L = loss_of_codes<WMSE>(us, w, h0, h1, Vtab[phc]);
+      const bool take = okh & (L < Lb);
+      Lb = take ? L : Lb;
+      pb = take ? ph : pb;
+    }
+    const float L = loss_of_codes<WMSE>(us, w, k0, k1, Vtab[pc]);
+    const bool take = ok & (L < La);
+    La = take ? L : La;
+    pa = take ? p : pa;
+  }
+  const bool upper = (Lb < La) | ((Lb == La) & (pb < pa));
+  Lout = upper ? Lb : La;
+  return upper ? pb : pa;
+}
+
 // Raw 16-element chunk as loaded (for next-row prefetch).
 template <typename T>
 struct Raw;
@@ -232,9 +327,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (tid < 128) {
-    const float v = (tid >= 1 && tid <= 126) ? e4m3_value(tid) : 1.0f;
-    Vtab[tid] = v;
-    Rtab[tid] = 1.0f / v;  // correctly rounded division
+    Vtab[tid] = kE4M3.v[tid];
+    Rtab[tid] = kE4M3.r[tid];
   }
   uint32_t amax_bits = 0;
   if (!a.given_scale) {
@@ -286,7 +380,6 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   const int lo = a.off_lo, hi = a.off_hi;
   Raw<T> cur, nxt;
   load_raw(xc + (int64_t)r0 * a.ld, cur);
-  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
   for (int r = r0; r < r1; ++r) {
     if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
     float z[16];
@@ -296,61 +389,37 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
     // signed magnitudes in units of S: |us| = fp32(|x| * S_inv) exactly
     float us[16];
     float amax = 0.0f;
-    bool finite = true;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      finite &= fabsf(z[i]) <= 3.402823466e38f;
       us[i] = z[i] * S_inv;
       amax = fmaxf(amax, fabsf(us[i]));
     }
     // with a computed scale the global-max pass already reported non-finite x
-    if (a.given_scale && !finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    if (a.given_scale) {
+      bool finite = true;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
+      if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    }
     const float t = amax / 6.0f;  // correctly rounded
     int base = e4m3_rne_sat(t);
     base = base < 1 ? 1 : base;
-    const int plo = max(1, base + lo);
-
-    float Lbest = __builtin_inff();
-    int pbest = plo;
-    for (int o = lo; o <= hi; ++o) {
-      // offsets pair up octet by octet: [lo, lo+8) with [lo+8, lo+16), ...
-      if (((o - lo) >> 3) & 1) continue;  // visited as the upper member of a pair
-      const int p = base + o;
-      const bool ok = (p >= 1) & (p <= 126);
-      const int pc = min(max(p, 1), 126);
-      const float R = Rtab[pc], V = Vtab[pc];
-      float y[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = us[i] * R;
-      k0 = cvt8<false>(y, k0);
-      k1 = cvt8<false>(y + 8, k1);
-      if (o + 8 <= hi) {
-        const int ph = p + 8;
-        const bool okh = (ph >= 1) & (ph <= 126);
-        const int phc = min(max(ph, 1), 126);
-        if (p >= 8) {
-          h0 = cvt8<true>(y, h0);
-          h1 = cvt8<true>(y + 8, h1);
-        } else {  // E4M3 subnormal lower member: no exact factor 2
-          const float Rh = Rtab[phc];
-          float y2[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) y2[i] = us[i] * Rh;
-          h0 = cvt8<false>(y2, h0);
-          h1 = cvt8<false>(y2 + 8, h1);
-        }
-        consider(loss_of_codes<WMSE>(us, w, h0, h1, Vtab[phc]), ph, okh, Lbest, pbest);
-      }
-      consider(loss_of_codes<WMSE>(us, w, k0, k1, V), p, ok, Lbest, pbest);
-    }
+    float Lbest;
+    int pbest;
+    // all candidates of every lane normal E4M3 patterns: no clamping, no
+    // validity tests, every pair related by an exact factor 2
+    const bool interior = (base + lo >= 8) & (base + hi <= 126);
+    if (__all(interior))
+      pbest = nv_sweep<WMSE, false>(us, w, base, lo, hi, Vtab, Rtab, Lbest);
+    else
+      pbest = nv_sweep<WMSE, true>(us, w, base, lo, hi, Vtab, Rtab, Lbest);
 
     const float Rb = Rtab[pbest];
     float y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = us[i] * Rb;
-    k0 = cvt8<false>(y, k0);
-    k1 = cvt8<false>(y + 8, k1);
-    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
+    const uint32_t c0 = cvt8<false>(y, 0u), c1 = cvt8<false>(y + 8, 0u);
+    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(c0, c1);
     const int64_t bi = (int64_t)r * bpr + c;
     a.scales[bi] = (uint8_t)pbest;
     if (a.loss) a.loss[bi] = Lbest * SS;

@@ -18,7 +18,7 @@ constexpr int kLaneElems = 16;  // every lane owns 16 contiguous elements of a r
 constexpr int kWaveLanes = 64;
 constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kThreads = kWaveLanes * kWaves;
-constexpr int kAmaxGroups = 512;  // max workgroups of the global-max pass
+constexpr int kAmaxGroups = 256;  // max workgroups of the global-max pass
 
 // Workspace layout (bytes): [0,4) status word, [256, 256 + 4*kAmaxGroups)
 // per-workgroup maxima of |x| as float32 bit patterns.
