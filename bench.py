@@ -214,6 +214,9 @@ def run_other(args):
         res.update(elements=n, ms_layer=total_ms, gel_s={k: n / v / 1e6 for k, v in total_ms.items()})
     elif args.config == "c5":
         imps = {name: W.c5_importance(name).to("cuda:0") for name in W.LAYER_70B}
+        warm = W.c5_matrix(0, "k", "cuda:0")
+        prewarm(lambda i: fq.quantize_nvfp4(warm, imps["k"], hadamard_n=16))
+        del warm
         out_ms = 0.0
         n = 0
         for layer in range(args.layers):

@@ -137,6 +137,54 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const u32x4 *__rest
   }
 }
 
+// Maximum of |rotated x| for a contiguous matrix viewed as total chunks of
+// 16 elements: Hadamard groups never straddle rows (cols is a multiple of
+// n), so consecutive chunks form the groups whatever the row length.  Four
+// chunks per thread are loaded before any is used.  stride is a multiple of
+// 64 and total of HAD/16, so the lanes of a group enter and leave every
+// branch together.
+template <typename T, int HAD>
+__global__ __launch_bounds__(kThreads) void amax_chunks_kernel(const T *__restrict__ x, int64_t total,
+                                                                uint32_t *__restrict__ partials) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t m = 0;
+  for (; g + (U - 1) * stride < total; g += U * stride) {
+    Raw<T> r[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) load_raw(x + (g + k * stride) * 16, r[k]);
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      float z[16];
+      widen(r[k], z);
+      fwht<HAD>(z, lane);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = max(m, as_u(z[i]) & 0x7FFFFFFFu);
+    }
+  }
+  for (; g < total; g += stride) {
+    Raw<T> r;
+    load_raw(x + g * 16, r);
+    float z[16];
+    widen(r, z);
+    fwht<HAD>(z, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = max(m, as_u(z[i]) & 0x7FFFFFFFu);
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t red[kWaves];
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
+    partials[blockIdx.x] = r;
+  }
+}
+
 struct SweepArgs {
   const void *x;
   int64_t ld;
@@ -278,41 +326,6 @@ __device__ __forceinline__ int nv_sweep(const float us[16], const float w[16], i
   const bool upper = (Lb < La) | ((Lb == La) & (pb < pa));
   Lout = upper ? Lb : La;
   return upper ? pb : pa;
-}
-
-// Raw 16-element chunk as loaded (for next-row prefetch).
-template <typename T>
-struct Raw;
-template <>
-struct Raw<uint16_t> {
-  u32x4 v[2];
-};
-template <>
-struct Raw<float> {
-  f32x4 v[4];
-};
-
-__device__ __forceinline__ void load_raw(const uint16_t *p, Raw<uint16_t> &r) {
-  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-  r.v[0] = __builtin_nontemporal_load(q);
-  r.v[1] = __builtin_nontemporal_load(q + 1);
-}
-__device__ __forceinline__ void load_raw(const float *p, Raw<float> &r) {
-  const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) r.v[k] = __builtin_nontemporal_load(q + k);
-}
-__device__ __forceinline__ void widen(const Raw<uint16_t> &r, float z[16]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t w = r.v[k >> 2][k & 3];
-    z[2 * k] = as_f(w << 16);
-    z[2 * k + 1] = as_f(w & 0xFFFF0000u);
-  }
-}
-__device__ __forceinline__ void widen(const Raw<float> &r, float z[16]) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) z[k] = r.v[k >> 2][k & 3];
 }
 
 // NVFP4 ScaleSweep: one lane per 16-element block.
@@ -604,10 +617,14 @@ static void with_dtype(fp4q_dtype_t dt, F &&f) {
 static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Rows per wave tile: enough tiles to give every SIMD several waves.  The
-// target tile count can be overridden with FP4Q_TILE_TARGET (tuning only).
-static int pick_rows_per_tile(int rows, int nbands) {
+// VALU-bound NVFP4 sweep is best near 16 waves of one row per SIMD, the
+// memory-bound MXFP4 sweep with as many one-row waves as there are rows.
+// The target tile count can be overridden with FP4Q_TILE_TARGET (tuning).
+constexpr int64_t kNvTileTarget = 16384;
+constexpr int64_t kMxTileTarget = 65536;
+static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
   const char *now = getenv("FP4Q_TILE_TARGET");
-  const int64_t target_tiles = (now && atoi(now) > 0) ? atoi(now) : 8192;
+  const int64_t target_tiles = (now && atoi(now) > 0) ? atoi(now) : default_target;
   const int64_t units = (int64_t)rows * nbands;
   int rpt = (int)((units + target_tiles - 1) / target_tiles);
   return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);
@@ -704,6 +721,17 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
       else
         hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n_partials), dim3(kThreads), 0, s,
                            (const u32x4 *)x, n_vec, partials);
+    } else if (ld == cols) {
+      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
+      with_dtype(dtype, [&](auto tp) {
+        using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+        with_had(hadamard_n, [&](auto hc) {
+          constexpr int H = decltype(hc)::value;
+          if constexpr (H != 0)
+            hipLaunchKernelGGL((amax_chunks_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x,
+                               (int64_t)total, partials);
+        });
+      });
     } else {
       n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
       with_dtype(dtype, [&](auto tp) {
@@ -727,7 +755,7 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   a.off_lo = off_lo;
   a.off_hi = off_hi;
   a.nbands = ceil_div(cpr, 64);
-  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands);
+  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands, kNvTileTarget);
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
   a.partials = partials;
   a.n_partials = n_partials;
@@ -786,7 +814,7 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   a.off_lo = off_lo;
   a.off_hi = off_hi;
   a.nbands = ceil_div(cpr, 64);
-  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands);
+  a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands, kMxTileTarget);
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
   a.partials = nullptr;
   a.n_partials = 0;

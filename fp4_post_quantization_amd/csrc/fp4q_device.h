@@ -34,30 +34,48 @@ __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 16 consecutive elements starting at p (16-byte aligned) widened to fp32.
-// The input is streamed once, so the loads are marked non-temporal.
-__device__ __forceinline__ void load16(const uint16_t *p, float z[16]) {
-  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-  const u32x4 a = __builtin_nontemporal_load(q);
-  const u32x4 b = __builtin_nontemporal_load(q + 1);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    z[2 * k] = as_f(w[k] << 16);
-    z[2 * k + 1] = as_f(w[k] & 0xFFFF0000u);
-  }
-}
+// Raw 16-element chunk as loaded (16-byte aligned); the input is streamed
+// once, so the loads are marked non-temporal.
+template <typename T>
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  u32x4 v[2];
+};
+template <>
+struct Raw<float> {
+  f32x4 v[4];
+};
 
-__device__ __forceinline__ void load16(const float *p, float z[16]) {
+__device__ __forceinline__ void load_raw(const uint16_t *p, Raw<uint16_t> &r) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+  r.v[0] = __builtin_nontemporal_load(q);
+  r.v[1] = __builtin_nontemporal_load(q + 1);
+}
+__device__ __forceinline__ void load_raw(const float *p, Raw<float> &r) {
   const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x4 v = __builtin_nontemporal_load(q + k);
-    z[4 * k] = v.x;
-    z[4 * k + 1] = v.y;
-    z[4 * k + 2] = v.z;
-    z[4 * k + 3] = v.w;
+  for (int k = 0; k < 4; ++k) r.v[k] = __builtin_nontemporal_load(q + k);
+}
+__device__ __forceinline__ void widen(const Raw<uint16_t> &r, float z[16]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t w = r.v[k >> 2][k & 3];
+    z[2 * k] = as_f(w << 16);
+    z[2 * k + 1] = as_f(w & 0xFFFF0000u);
   }
+}
+__device__ __forceinline__ void widen(const Raw<float> &r, float z[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) z[k] = r.v[k >> 2][k & 3];
+}
+
+// 16 consecutive elements starting at p widened to fp32.
+template <typename T>
+__device__ __forceinline__ void load16(const T *p, float z[16]) {
+  Raw<T> r;
+  load_raw(p, r);
+  widen(r, z);
 }
 
 // ------------------------------------------------- cross-lane moves ----

@@ -114,6 +114,16 @@ def test_nvfp4_leading_dimension_larger_than_cols():
     _check_nvfp4(res, ref)
 
 
+@pytest.mark.parametrize("had", [16, 128])
+def test_nvfp4_rotated_leading_dimension_larger_than_cols(had):
+    big = W.random_matrix(37, 1280, seed=43, dist="laplace", dtype=torch.bfloat16)
+    imp = W.random_importance(1024, seed=44)
+    fq = _fp4()
+    res = fq.quantize_nvfp4(big.to(DEV)[:, :1024], imp.to(DEV), hadamard_n=had, check=True)
+    torch.cuda.synchronize()
+    _check_nvfp4(res, _oracle_nvfp4(big[:, :1024].contiguous(), imp, had=had))
+
+
 def test_nvfp4_given_scale():
     x = W.random_matrix(40, 256, seed=42)
     S = np.float32(0.37 / 1536)
