@@ -10,7 +10,10 @@ than the 256 MB Infinity Cache) are rotated so every step reads HBM.
 
 The ``roofline`` object is for the dominant kernel (the sweep), timed alone
 with HIP events on the stream it runs on (a call with a given global scale
-launches exactly that kernel).  ``cpu_baseline`` times the CPU oracle on a
+launches exactly that kernel).  Its ``traffic`` is the calibrated
+FETCH_SIZE + WRITE_SIZE bytes per launch recorded under profiles/ by
+``python -m fp4_post_quantization_amd.evidence`` for the current kernel
+sources, or null when the kernels changed since.  ``cpu_baseline`` times the CPU oracle on a
 bounded sample of the same workload on this host.  Before the warmup steps,
 untimed steps run for 0.3 s so the GPU has left its idle clocks.
 
@@ -170,6 +173,10 @@ def run_c2(args):
                      "alg_ops_per_element": ops, "elements_per_launch": n,
                      "kernel_ms": round(ms_sweep, 5)},
     }
+    from fp4_post_quantization_amd import evidence
+    rec = evidence.committed_traffic("c2")
+    if rec:  # calibrated FETCH_SIZE + WRITE_SIZE of this kernel source, from profiles/
+        line["roofline"]["traffic"] = round(rec["traffic_bytes"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(x_cpu, imp_cpu, args.cpu_rows, window=window)
     return line

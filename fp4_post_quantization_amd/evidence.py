@@ -1,0 +1,239 @@
+"""rocprofv3 evidence for the fp4q kernels.
+
+    python -m fp4_post_quantization_amd.evidence run --config c2 --out DIR
+    python -m fp4_post_quantization_amd.evidence summarize --config c2 --in DIR --profiles profiles
+
+``run`` profiles ``bench.py --config <config>`` four times, each in a pass of
+its own: a kernel trace with statistics, one counter pass for the VALU
+(SQ_WAVES, SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, SQ_BUSY_CYCLES,
+GRBM_GUI_ACTIVE), one for FETCH_SIZE and one for WRITE_SIZE.  The bench
+also runs a plain elementwise kernel that reads and writes 256 MiB once
+(``--copy-calib``); its counter readings give the factors that turn
+FETCH_SIZE / WRITE_SIZE into bytes.
+
+``summarize`` writes ``<profiles>/<stem>.md`` (durations, VALU issue
+utilisation, calibrated HBM traffic per dispatch) and ``<stem>.traffic.json``
+(the dominant kernel's calibrated traffic, tagged with a hash of the kernel
+sources so that it is only reported while the kernels are unchanged).
+
+This module starts rocprofv3 as a child process and never touches the GPU
+itself.
+"""
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", "fp4q.hip"), os.path.join(PKG, "csrc", "fp4q_device.h"),
+                  os.path.join(ROOT, "include", "fp4q.h")]
+
+VALU_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+PASSES = {
+    "trace": ["--kernel-trace", "--stats"],
+    "valu": ["--pmc", *VALU_COUNTERS],
+    "fetch": ["--pmc", "FETCH_SIZE"],
+    "write": ["--pmc", "WRITE_SIZE"],
+}
+COPY_BYTES = 256 * 2**20  # bench.py --copy-calib: one read and one write of 256 MiB
+
+# dominant kernel and algorithmic bytes per dispatch of each workload
+WORKLOADS = {
+    "c2": {"stem": "nvfp4_wmse_bf16_4096x4096", "kernel": "nvfp4_sweep_kernel",
+           "title": "NVFP4 WMSE ScaleSweep, bf16 4096x4096, offsets [-8,+7]",
+           "alg_bytes": {"nvfp4_sweep_kernel": 4096 * 4096 * (2 + 0.5 + 6 / 16),
+                         "amax_flat_kernel": 4096 * 4096 * 2}},
+    "c3b": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
+            "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
+            "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
+    "c3a": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
+            "title": "MXFP4 AbsMax window [0,0], bf16 8192x4096 activations",
+            "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
+}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def bench_cmd(config, steps):
+    return [sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--steps", str(steps),
+            "--warmup", "1", "--no-cpu-baseline", "--copy-calib"]
+
+
+def rocprof_cmd(name, out_dir, config, steps):
+    return ["rocprofv3", *PASSES[name], "-d", os.path.join(out_dir, name), "-o", config,
+            "--output-format", "csv", "--", *bench_cmd(config, steps)]
+
+
+def run(config, out_dir, steps):
+    os.makedirs(out_dir, exist_ok=True)
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    for name in PASSES:
+        cmd = rocprof_cmd(name, out_dir, config, steps)
+        print("==", " ".join(cmd), flush=True)
+        # each pass is bounded; a counter request the hardware cannot serve hangs
+        subprocess.run(["timeout", "-s", "KILL", "240", *cmd], check=True, env=env)
+
+
+def _short(name):
+    base = name.split("(")[0]
+    return base.replace("void fp4q::", "").replace("void ", "")
+
+
+def _counter_means(path):
+    rows = list(csv.DictReader(open(path)))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        key = (r["Kernel_Name"], r["Grid_Size"], r["Counter_Name"])
+        agg[key].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in agg.items()}
+
+
+def _agent(path):
+    for r in csv.DictReader(open(path)):
+        if r.get("Agent_Type", "").upper().endswith("GPU") or r.get("Name", "").startswith("gfx"):
+            return r
+    return {}
+
+
+def summarize(config, in_dir, profiles):
+    w = WORKLOADS[config]
+    trace_dir = os.path.join(in_dir, "trace")
+    stats = list(csv.DictReader(open(os.path.join(trace_dir, f"{config}_kernel_stats.csv"))))
+    agent = _agent(os.path.join(trace_dir, f"{config}_agent_info.csv"))
+    simds = int(agent.get("Simd_Count", 1024))
+    clk_mhz = float(agent.get("Max_Engine_Clk_Fcompute", 2400))
+    xcc = int(agent.get("Num_Xcc", 8))
+    cus = int(agent.get("Cu_Count", 256))
+    valu = _counter_means(os.path.join(in_dir, "valu", f"{config}_counter_collection.csv"))
+    fetch = _counter_means(os.path.join(in_dir, "fetch", f"{config}_counter_collection.csv"))
+    write = _counter_means(os.path.join(in_dir, "write", f"{config}_counter_collection.csv"))
+
+    def pick(table, kname, counter):
+        best = None
+        for (k, grid, c), (v, n) in table.items():
+            if c == counter and kname in k:
+                if best is None or n > best[1]:
+                    best = (v, n)
+        return best
+
+    # copy calibration: the elementwise neg kernel of bench.py --copy-calib
+    cf = pick(fetch, "neg_kernel", "FETCH_SIZE")
+    cw = pick(write, "neg_kernel", "WRITE_SIZE")
+    f_factor = COPY_BYTES / (cf[0] * 1024) if cf else None
+    w_factor = COPY_BYTES / (cw[0] * 1024) if cw else None
+
+    lines = [f"# {w['title']}", "",
+             f"Device: {agent.get('Name', '?')}, {cus} CUs, {simds} SIMDs, {xcc} XCDs, "
+             f"max engine clock {clk_mhz:.0f} MHz.", "", "Commands (each a pass of its own):", ""]
+    for name in PASSES:
+        cmd = rocprof_cmd(name, in_dir, config, 20)
+        cmd = ["python" if c == sys.executable else ("bench.py" if c.endswith("bench.py") else c) for c in cmd]
+        lines.append("    " + " ".join(cmd))
+    lines += ["", "run together by", "",
+              f"    python -m fp4_post_quantization_amd.evidence run --config {config} --out {in_dir} --steps 20",
+              "", "and summarized by", "",
+              f"    python -m fp4_post_quantization_amd.evidence summarize --config {config} --in {in_dir}"
+              f" --profiles profiles", "",
+              "## Kernel durations (kernel trace)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    durations = {}
+    for r in stats:
+        name = r["Name"]
+        if "fp4q::" not in name and "neg_kernel" not in name:
+            continue
+        avg = float(r["AverageNs"]) / 1000
+        durations[name] = avg
+        lines.append(f"| `{_short(name)}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1000:.2f} "
+                     f"| {float(r['MaxNs'])/1000:.2f} |")
+    lines += ["", "## Counters per dispatch (averages)", "",
+              "VALU issue = SQ_INSTS_VALU x 4 cycles / (SIMDs x trace duration x clock); VALUBusy = "
+              "100 x SQ_ACTIVE_INST_VALU / CUs / (GRBM_GUI_ACTIVE / XCDs), the counter runs being "
+              "slower than the trace.", "",
+              "| kernel | waves | VALU insts | VALU issue | VALUBusy | FETCH KiB | WRITE KiB | HBM bytes "
+              "(calibrated) | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
+    record = None
+    for name, avg_us in durations.items():
+        if "fp4q::" not in name:
+            continue
+        key = _short(name).split("<")[0]
+        insts = pick(valu, name, "SQ_INSTS_VALU")
+        waves = pick(valu, name, "SQ_WAVES")
+        active = pick(valu, name, "SQ_ACTIVE_INST_VALU")
+        grbm = pick(valu, name, "GRBM_GUI_ACTIVE")
+        fk = pick(fetch, name, "FETCH_SIZE")
+        wk = pick(write, name, "WRITE_SIZE")
+        issue = insts[0] * 4 / (simds * avg_us * 1e-6 * clk_mhz * 1e6) if insts else None
+        busy = 100 * active[0] / cus / (grbm[0] / xcc) if active and grbm else None
+        hbm = (fk[0] * 1024 * f_factor + wk[0] * 1024 * w_factor) if (fk and wk and f_factor) else None
+        alg = w["alg_bytes"].get(key)
+        lines.append(
+            f"| `{_short(name)}` | {waves[0]:.0f} | {insts[0]:.4g} | "
+            f"{'' if issue is None else f'{100 * issue:.1f}%'} | {'' if busy is None else f'{busy:.1f}%'} | "
+            f"{fk[0] if fk else float('nan'):.1f} | {wk[0] if wk else float('nan'):.1f} | "
+            f"{'' if hbm is None else f'{hbm / 1e6:.2f} MB'} | {'' if alg is None else f'{alg / 1e6:.2f} MB'} | "
+            f"{'' if (hbm is None or alg is None) else f'{hbm / alg:.3f}'} |")
+        if w["kernel"] in name and hbm is not None:
+            record = {"workload": config, "kernel": _short(name), "avg_us": avg_us, "fetch_kib": fk[0],
+                      "write_kib": wk[0], "fetch_factor": f_factor, "write_factor": w_factor,
+                      "traffic_bytes": hbm, "alg_bytes": alg, "valu_issue": issue, "valu_busy_pct": busy,
+                      "source_sha256": source_hash()}
+    lines += ["", "## Copy calibration", "",
+              f"Plain elementwise kernel reading and writing {COPY_BYTES // 2**20} MiB once: FETCH_SIZE "
+              f"{cf[0] if cf else float('nan'):.1f} KiB (factor {f_factor if f_factor else float('nan'):.4f}), "
+              f"WRITE_SIZE {cw[0] if cw else float('nan'):.1f} KiB (factor "
+              f"{w_factor if w_factor else float('nan'):.4f}).", ""]
+    os.makedirs(profiles, exist_ok=True)
+    md = os.path.join(profiles, w["stem"] + ".md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    if record:
+        with open(os.path.join(profiles, w["stem"] + ".traffic.json"), "w") as f:
+            json.dump(record, f, indent=1)
+    print(md)
+
+
+def committed_traffic(config):
+    """The calibrated traffic record for a workload if it was measured on the
+    current kernel sources, else None."""
+    w = WORKLOADS.get(config)
+    if not w:
+        return None
+    path = os.path.join(ROOT, "profiles", w["stem"] + ".traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    return rec if rec.get("source_sha256") == source_hash() else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--config", default="c2")
+    r.add_argument("--out", required=True)
+    r.add_argument("--steps", type=int, default=20)
+    s = sub.add_parser("summarize")
+    s.add_argument("--config", default="c2")
+    s.add_argument("--in", dest="in_dir", required=True)
+    s.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args()
+    if a.cmd == "run":
+        run(a.config, a.out, a.steps)
+    else:
+        summarize(a.config, a.in_dir, a.profiles)
+
+
+if __name__ == "__main__":
+    main()
