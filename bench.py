@@ -20,7 +20,8 @@ untimed steps run for 0.3 s so the GPU has left its idle clocks.
 Other workloads (for the design notes, not the headline line) are selected
 with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
-c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N).
+c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
+focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8).
 """
 
 import argparse
@@ -204,6 +205,24 @@ def run_other(args):
             step(i)
         ms = _events_time(step, args.steps)
         byts = _alg_bytes_per_element(2, 32)
+        res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6,
+                   hbm_GBs=byts * x.numel() / ms / 1e6, hbm_frac=byts * x.numel() / ms / 1e6 / HBM_PEAK_GBS)
+    elif args.config == "focus":
+        # FOCUS forward quantizer on the c2 weight: stored scales from the
+        # sweep, FP16 coefficients per 8-element sub-block, dequantized output
+        x, imp = W.c2_weight_and_importance()
+        x = x.to("cuda:0")
+        base = fq.quantize_nvfp4(x, imp.to("cuda:0"))
+        c = torch.exp(0.1 * torch.randn(x.shape[0], x.shape[1] // 8, device="cuda:0")).to(torch.float16)
+        bufs = _rotating_copies(x)
+        codes, dq = fq.quantize_relaxed(bufs[0], base.scales, c, global_scale=base.global_scale, sub=8)
+        step = lambda i: fq.quantize_relaxed(bufs[i % len(bufs)], base.scales, c, global_scale=base.global_scale,
+                                             sub=8, out_codes=codes, out_dequant=dq)
+        prewarm(step)
+        for i in range(args.warmup):
+            step(i)
+        ms = _events_time(step, args.steps)
+        byts = 2 + 2 / 8 + 1 / 16 + 0.5 + 4  # x, coefficients, scales in; codes, dequantized out
         res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6,
                    hbm_GBs=byts * x.numel() / ms / 1e6, hbm_frac=byts * x.numel() / ms / 1e6 / HBM_PEAK_GBS)
     elif args.config == "c4":

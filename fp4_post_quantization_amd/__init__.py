@@ -8,6 +8,7 @@ HIP kernels.  There is no CPU fallback; a missing library raises.
 
     quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, ...)
     quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, ...)
+    quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub=8, ...)
     dequantize(fmt, codes, scales, global_scale=None)
     block_hadamard(x, n)
 """
@@ -20,7 +21,7 @@ from . import _lib as L
 from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
-    "quantize_nvfp4", "quantize_mxfp4", "dequantize", "block_hadamard",
+    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "dequantize", "block_hadamard",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
 ]
 
@@ -76,6 +77,8 @@ def _check_data(ws):
             names.append("negative or non-finite importance")
         if st & L.DATA_BAD_GLOBAL_SCALE:
             names.append("invalid global scale")
+        if st & L.DATA_BAD_SCALE:
+            names.append("invalid scale or coefficient")
         raise FP4QError("data error: " + ", ".join(names))
 
 
@@ -185,6 +188,39 @@ def quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, *, out=None
     if check:
         _check_data(ws)
     return out
+
+
+def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub=8, *, dequant=True,
+                     out_codes=None, out_dequant=None, ws=None, check=False):
+    """FOCUS forward quantizer: codes under the quantization scale
+    S_dq * c_k of each sub-block (coeffs: float16 [R, C/sub] or None for all
+    ones), plus the dequantized values q * S_dq when ``dequant``.
+    Returns (codes, dequantized or None)."""
+    lib = L.load()
+    x, ld = _matrix(x)
+    rows, cols = x.shape
+    dev = x.device
+    fmt_code = {"nvfp4": L.NVFP4, "mxfp4": L.MXFP4}[fmt]
+    scales = scales.contiguous()
+    c = None
+    if coeffs is not None:
+        c = torch.as_tensor(coeffs, device=dev).to(torch.float16).contiguous()
+        if c.numel() != rows * (cols // sub):
+            raise ValueError("coeffs must hold one entry per sub-block")
+    gs = None
+    if fmt_code == L.NVFP4:
+        gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1)
+    codes = out_codes if out_codes is not None else torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    dq = None
+    if dequant:
+        dq = out_dequant if out_dequant is not None else torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_quantize_relaxed(
+        fmt_code, x.data_ptr(), _dtype_code(x), rows, cols, ld, scales.data_ptr(), _ptr(gs), _ptr(c), int(sub),
+        codes.data_ptr(), _ptr(dq), ws.data_ptr(), ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return codes, dq
 
 
 def dequantize(fmt, codes, scales, global_scale=None, out=None):

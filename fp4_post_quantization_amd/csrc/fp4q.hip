@@ -539,6 +539,80 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   }
 }
 
+// FOCUS forward quantizer: one lane per 16-element chunk (flat over
+// rows x chunks); the codes use the quantization scale Vc = V * c_k of each
+// sub-block, the optional dequantized output the stored scale V alone.
+template <typename T, int FMT, int SUB>
+__global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__restrict__ x, int64_t ld, int cpr,
+                                                                  int cols, int total,
+                                                                  const uint8_t *__restrict__ scales,
+                                                                  const float *__restrict__ gscale,
+                                                                  const uint16_t *__restrict__ coeffs,
+                                                                  uint8_t *__restrict__ codes,
+                                                                  float *__restrict__ dq,
+                                                                  uint32_t *__restrict__ status) {
+  const int g = blockIdx.x * kThreads + threadIdx.x;
+  if (g >= total) return;
+  const int r = g / cpr, c = g - r * cpr;
+  float z[16];
+  load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
+
+  bool bad = false;
+  float V, S_inv = 1.0f, S = 1.0f;
+  if constexpr (FMT == FP4Q_NVFP4) {
+    const int p = scales[(int64_t)r * cpr + c];
+    bad |= (p < 1) | (p > 126);
+    V = kE4M3.v[p & 127];
+    S = *gscale;
+    S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
+  } else {
+    const int b = scales[(int64_t)r * (cpr / 2) + (c >> 1)];
+    bad |= b == 255;
+    V = pow2f(min(b, 254) - 127);
+  }
+  bool finite = true;
+  float us[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    finite &= fabsf(z[i]) <= 3.402823466e38f;
+    us[i] = FMT == FP4Q_NVFP4 ? z[i] * S_inv : z[i];
+  }
+  // coefficients of this lane's sub-blocks: 16/SUB of them, or one shared
+  // by the two lanes of a 32-element sub-block
+  constexpr int NS = SUB >= 16 ? 1 : 16 / SUB;
+  const int64_t crow = (int64_t)r * (cols / SUB);
+  float y[16];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int64_t ci = SUB == 32 ? crow + (c >> 1) : crow + (int64_t)c * (16 / min(SUB, 16)) + j;
+    const float cf = coeffs ? (float)__builtin_bit_cast(_Float16, coeffs[ci]) : 1.0f;
+    bad |= !((cf > 0.0f) & (cf <= 65504.0f));
+    const float R = 1.0f / (V * cf);
+    bad |= !(R <= 3.402823466e38f);
+    constexpr int E = SUB >= 16 ? 16 : SUB;
+#pragma unroll
+    for (int i = 0; i < E; ++i) y[j * E + i] = us[j * E + i] * R;
+  }
+  if (bad) atomicOr(status, FP4Q_DATA_BAD_SCALE);
+  if (!finite) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+  const uint32_t k0 = cvt8<false>(y, 0u), k1 = cvt8<false>(y + 8, 0u);
+  *reinterpret_cast<uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
+  if (dq) {
+    float q[16];
+    fp4x8_to_f32(k0, q);
+    fp4x8_to_f32(k1, q + 8);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float m = q[i] * V;  // exact
+      v[i] = FMT == FP4Q_NVFP4 ? m * S : m;
+    }
+    f32x4 *o = reinterpret_cast<f32x4 *>(dq + (int64_t)r * cols + (int64_t)c * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+  }
+}
+
 // Decode of an arbitrary E4M3 byte (sign, 0x7F / 0xFF = NaN).
 __device__ __forceinline__ float e4m3_decode_any(uint32_t b) {
   const uint32_t m = b & 0x7Fu;
@@ -835,6 +909,54 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
       else
         hipLaunchKernelGGL((mxfp4_sweep_kernel<T, false, H>), dim3(grid), dim3(kThreads), 0, s, a);
     });
+  });
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dtype_t dtype,
+                                               int64_t rows, int64_t cols, int64_t ld, const uint8_t *scales,
+                                               const float *global_scale, const uint16_t *coeffs,
+                                               int sub_block, uint8_t *codes, float *dequant_out,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (format != FP4Q_NVFP4 && format != FP4Q_MXFP4) return FP4Q_ERR_ARG;
+  const int block = format == FP4Q_NVFP4 ? 16 : 32;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!x || !scales || !codes)) return FP4Q_ERR_NULL;
+  if (!empty && format == FP4Q_NVFP4 && !global_scale) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (sub_block != 4 && sub_block != 8 && sub_block != 16 && !(sub_block == 32 && block == 32))
+    return FP4Q_ERR_ARG;
+  fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, 0);
+  if (st != FP4Q_OK) return st;
+  if (empty) return FP4Q_OK;
+  if (!aligned(codes, 8) || (dequant_out && !aligned(dequant_out, 16)) || (coeffs && !aligned(coeffs, 2)))
+    return FP4Q_ERR_ALIGN;
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  const int grid = ceil_div(total, kThreads);
+  with_dtype(dtype, [&](auto tp) {
+    using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+    auto go = [&](auto fmt_c, auto sub_c) {
+      constexpr int FM = decltype(fmt_c)::value, SB = decltype(sub_c)::value;
+      hipLaunchKernelGGL((relaxed_quant_kernel<T, FM, SB>), dim3(grid), dim3(kThreads), 0, s, (const T *)x, ld,
+                         cpr, (int)cols, total, scales, global_scale, coeffs, codes, dequant_out, status);
+    };
+    auto with_sub = [&](auto fmt_c) {
+      switch (sub_block) {
+        case 4: go(fmt_c, std::integral_constant<int, 4>{}); break;
+        case 8: go(fmt_c, std::integral_constant<int, 8>{}); break;
+        case 16: go(fmt_c, std::integral_constant<int, 16>{}); break;
+        default:
+          if constexpr (decltype(fmt_c)::value == FP4Q_MXFP4) go(fmt_c, std::integral_constant<int, 32>{});
+          break;
+      }
+    };
+    if (format == FP4Q_NVFP4)
+      with_sub(std::integral_constant<int, FP4Q_NVFP4>{});
+    else
+      with_sub(std::integral_constant<int, FP4Q_MXFP4>{});
   });
   return last_hip_status();
 }

@@ -79,6 +79,7 @@ typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
 #define FP4Q_DATA_NONFINITE_INPUT 0x1u  /* x (after rotation) holds Inf or NaN */
 #define FP4Q_DATA_BAD_IMPORTANCE 0x2u   /* an importance entry is < 0, Inf or NaN */
 #define FP4Q_DATA_BAD_GLOBAL_SCALE 0x4u /* given S is < 0, Inf or NaN */
+#define FP4Q_DATA_BAD_SCALE 0x8u        /* fp4q_quantize_relaxed: invalid scale byte or coefficient */
 
 /* Library version as 10000 * major + 100 * minor + patch. */
 int fp4q_version(void);
@@ -163,6 +164,40 @@ fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t row
                                   int off_lo, int off_hi, int hadamard_n, uint8_t *codes,
                                   uint8_t *scales, float *block_loss, int8_t *offsets,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * FOCUS forward quantizer with coupled-relaxation coefficients ([FC]
+ * Metodologia 2. CRS and 3. DGS): the codes of sub-block k of a hardware
+ * block are Q(x / (S_dq * c_k)), where S_dq is the block's stored
+ * dequantization scale and c_k a full-precision FP16 coefficient per
+ * sub-block; dequantization keeps using S_dq alone ([FC] 4.).
+ *
+ *   format      FP4Q_NVFP4 (blocks of 16, E4M3 scale patterns, FP32 global
+ *               scale) or FP4Q_MXFP4 (blocks of 32, E8M0 scale bytes).
+ *   x, dtype, rows, cols, ld   input matrix as for the quantize calls.
+ *   scales      [rows * cols / block] stored scales (e.g. from a quantize call).
+ *   global_scale [1] float32 S (NVFP4; ignored for MXFP4, may be NULL).
+ *   coeffs      [rows * cols / sub_block] FP16 coefficients, row-major, or
+ *               NULL for all ones (then the codes equal the
+ *               round-to-nearest codes at the given scales).
+ *   sub_block   4, 8 or 16 (NVFP4); 4, 8, 16 or 32 (MXFP4).
+ *   codes       [rows * cols / 2] packed codes (out).
+ *   dequant_out [rows * cols] float32 x_hat = q * S_dq, dense row-major
+ *               (out; may be NULL).
+ *   workspace   as for the quantize calls (status word at byte 0).
+ *
+ * Computation (each float32 step rounded to nearest even): NVFP4 u =
+ * fp32(|x| * fp32(1/S)), Vc = fp32(E4M3(p) * c_k); MXFP4 u = |x|,
+ * Vc = fp32(2^E * c_k); R = fp32(1/Vc), q = E2M1 nearest to fp32(u * R).
+ * A scale pattern outside 1..126 (NVFP4) or 255 (MXFP4), a coefficient
+ * that is not finite and positive, or an infinite R sets
+ * FP4Q_DATA_BAD_SCALE; non-finite x sets FP4Q_DATA_NONFINITE_INPUT.
+ */
+fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dtype_t dtype, int64_t rows,
+                                    int64_t cols, int64_t ld, const uint8_t *scales,
+                                    const float *global_scale, const uint16_t *coeffs, int sub_block,
+                                    uint8_t *codes, float *dequant_out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
 
 /*
  * Dequantization (the consumer side: only codes and dequantization scales

@@ -125,6 +125,26 @@ def test_mxfp4_dequant_hadamard_validation():
     assert hd(cols=40) == L.ERR_SHAPE
 
 
+def test_relaxed_validation():
+    L, lib = _lib()
+    wsb = lib.fp4q_workspace_bytes()
+    rq = lambda **kw: lib.fp4q_quantize_relaxed(
+        kw.get("fmt", L.NVFP4), kw.get("x", X), L.BF16, 2, kw.get("cols", 64), kw.get("ld", 64),
+        kw.get("scales", OUT), kw.get("gs", OUT), None, kw.get("sub", 8), kw.get("codes", OUT),
+        kw.get("dq", None), kw.get("ws", WS), wsb, None)
+    assert rq(fmt=7) == L.ERR_ARG
+    assert rq(x=None) == L.ERR_NULL
+    assert rq(scales=None) == L.ERR_NULL
+    assert rq(gs=None) == L.ERR_NULL
+    assert rq(ws=None) == L.ERR_WORKSPACE
+    assert rq(sub=32) == L.ERR_ARG          # NVFP4 blocks hold 16
+    assert rq(sub=3) == L.ERR_ARG
+    assert rq(fmt=L.MXFP4, cols=48, ld=48) == L.ERR_SHAPE
+    assert rq(ld=60) == L.ERR_SHAPE
+    assert rq(codes=OUT + 4) == L.ERR_ALIGN
+    assert rq(dq=OUT + 4) == L.ERR_ALIGN
+
+
 def test_empty_shapes_need_no_device_for_dequant_and_hadamard():
     L, lib = _lib()
     assert lib.fp4q_dequantize(L.NVFP4, OUT, OUT, OUT, 0, 64, 16, OUT, None) == L.OK

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import focus as FO
 from oracle import formats as F
 from oracle import quant as Q
 from oracle import hadamard as OH
@@ -397,3 +398,47 @@ def test_c5_70b_layer0_rotated_sampled_rows(name):
     ref = Q.quantize_nvfp4(xf[rows], imp.numpy(), global_scale=S, hadamard_n=16)
     ref.global_scale = S
     _check_nvfp4(res, ref, rows=rows)
+
+
+# --------------------------------------------------- FOCUS quantizer ----
+@pytest.mark.parametrize("fmt,sub", [("nvfp4", 4), ("nvfp4", 8), ("nvfp4", 16),
+                                     ("mxfp4", 4), ("mxfp4", 8), ("mxfp4", 16), ("mxfp4", 32)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_relaxed_quantizer(fmt, sub, dtype):
+    fq = _fp4()
+    rows, cols = 67, 2080
+    x = W.random_matrix(rows, cols, seed=90 + sub, dist="t4", dtype=dtype)
+    xd = x.to(DEV)
+    if fmt == "nvfp4":
+        base = fq.quantize_nvfp4(xd)
+        gs = base.global_scale
+    else:
+        base = fq.quantize_mxfp4(xd)
+        gs = None
+    c = torch.from_numpy(np.exp(np.random.default_rng(sub).normal(0, 0.2, (rows, cols // sub)))).to(torch.float16)
+    codes, dq = fq.quantize_relaxed(xd, base.scales, c.to(DEV), fmt=fmt, global_scale=gs, sub=sub, check=True)
+    torch.cuda.synchronize()
+    ref_codes, ref_dq = FO.quantize_given_scales(_host_f32(x), fmt, _np(base.scales),
+                                                 None if gs is None else _np(gs)[0], c.numpy(), sub=sub)
+    _assert_equal("relaxed codes", _np(codes), ref_codes)
+    _assert_equal("relaxed dequant", _np(dq), ref_dq)
+    # unit coefficients reproduce the scale search's own codes
+    codes1, _ = fq.quantize_relaxed(xd, base.scales, None, fmt=fmt, global_scale=gs, sub=sub, dequant=False,
+                                    check=True)
+    torch.cuda.synchronize()
+    _assert_equal("relaxed c=1 vs sweep codes", _np(codes1), _np(base.codes))
+
+
+def test_relaxed_quantizer_data_errors():
+    fq = _fp4()
+    x = W.random_matrix(4, 64, seed=98).to(DEV)
+    base = fq.quantize_nvfp4(x)
+    bad = base.scales.clone()
+    bad[1, 2] = 0
+    with pytest.raises(fq.FP4QError, match="scale or coefficient"):
+        fq.quantize_relaxed(x, bad, None, global_scale=base.global_scale, check=True)
+    c = torch.ones(4, 8, dtype=torch.float16, device=DEV)
+    c[0, 3] = -1.0
+    with pytest.raises(fq.FP4QError, match="scale or coefficient"):
+        fq.quantize_relaxed(x, base.scales, c, global_scale=base.global_scale, check=True)
+    fq.quantize_relaxed(x, base.scales, None, global_scale=base.global_scale, check=True)

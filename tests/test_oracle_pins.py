@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import focus as FO
 from oracle import formats as F
 from oracle import hadamard as H
 from oracle import quant as Q
@@ -449,3 +450,57 @@ def test_fwht_matches_dense_and_is_orthonormal(n):
 def test_scale_constants():
     assert H.hadamard_scale_f32(16) == np.float32(0.25)
     assert abs(float(H.hadamard_scale_f32(32)) * math.sqrt(32) - 1) < 1e-7
+
+
+# ------------------------------------------------------ FOCUS quantizer ----
+def test_relaxed_with_unit_coefficients_is_rtn_at_given_scales():
+    """With every c_k = 1 the relaxed quantizer reproduces the codes the
+    scale search chose for its own scales (NVFP4 and MXFP4)."""
+    rng = np.random.default_rng(23)
+    x = (rng.standard_t(4, (24, 256)) * 0.02).astype(np.float32)
+    r = Q.quantize_nvfp4(x, importance=np.exp(rng.standard_normal(256)).astype(np.float32))
+    codes, xhat = FO.quantize_given_scales(x, "nvfp4", r.scales, r.global_scale, None, sub=8)
+    np.testing.assert_array_equal(codes, r.codes)
+    np.testing.assert_array_equal(xhat, Q.dequantize_nvfp4(r.codes, r.scales, r.global_scale))
+    m = Q.quantize_mxfp4(x)
+    codes, _ = FO.quantize_given_scales(x, "mxfp4", m.scales, None, np.ones((24, 8), np.float16), sub=32)
+    np.testing.assert_array_equal(codes, m.codes)
+
+
+@pytest.mark.parametrize("fmt,sub", [("nvfp4", 4), ("nvfp4", 8), ("nvfp4", 16), ("mxfp4", 8), ("mxfp4", 32)])
+def test_relaxed_codes_are_nearest_at_sub_block_scale(fmt, sub):
+    """Each code is the E2M1 value nearest to |x| / (S_dq * c_k) in float64
+    (up to float32 rounding of the scaled value), the sign is x's, and the
+    dequantized output uses S_dq alone (decoded independently with torch)."""
+    rng = np.random.default_rng(24)
+    x = (rng.laplace(0, 0.02, (16, 128))).astype(np.float32)
+    if fmt == "nvfp4":
+        r = Q.quantize_nvfp4(x)
+        scales, S = r.scales, r.global_scale
+        sdq = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e4m3fn).double().numpy() * float(S)
+        block = 16
+    else:
+        r = Q.quantize_mxfp4(x)
+        scales, S = r.scales, None
+        sdq = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu).double().numpy()
+        block = 32
+    c = np.exp(rng.normal(0, 0.15, (16, 128 // sub))).astype(np.float16)
+    codes, xhat = FO.quantize_given_scales(x, fmt, scales, S, c, sub=sub)
+    cu = Q.unpack_nibbles(codes).astype(np.int64)
+    sq = np.repeat(sdq, block, axis=1) * np.repeat(c.astype(np.float64), sub, axis=1)
+    y = np.abs(x.astype(np.float64)) / sq
+    q = F.E2M1_VALUES.astype(np.float64)[cu & 7]
+    dist = np.abs(y[..., None] - F.E2M1_VALUES.astype(np.float64))
+    assert np.all(np.abs(y - q) <= dist.min(-1) + 1e-5 * np.maximum(y, 1))
+    assert np.all((cu >> 3) == np.signbit(x))
+    ref = np.where(cu >> 3, -1.0, 1.0) * q * np.repeat(sdq, block, axis=1)
+    np.testing.assert_allclose(xhat, ref, rtol=1e-6, atol=0)
+
+
+def test_relaxed_rejects_invalid_data():
+    x = np.ones((1, 16), np.float32)
+    with pytest.raises(ValueError):
+        FO.quantize_given_scales(x, "nvfp4", np.zeros((1, 1), np.uint8), np.float32(1), None)
+    with pytest.raises(ValueError):
+        FO.quantize_given_scales(x, "nvfp4", np.full((1, 1), 0x38, np.uint8), np.float32(1),
+                                 np.zeros((1, 2), np.float16))
