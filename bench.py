@@ -21,7 +21,8 @@ Other workloads (for the design notes, not the headline line) are selected
 with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
 c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
-focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8).
+focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8),
+study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage).
 """
 
 import argparse
@@ -225,6 +226,16 @@ def run_other(args):
         byts = 2 + 2 / 8 + 1 / 16 + 0.5 + 4  # x, coefficients, scales in; codes, dequantized out
         res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6,
                    hbm_GBs=byts * x.numel() / ms / 1e6, hbm_frac=byts * x.numel() / ms / 1e6 / HBM_PEAK_GBS)
+    elif args.config == "study":
+        # AbsMax vs ScaleSweep vs exhaustive windows; MXFP4 code usage
+        from fp4_post_quantization_amd import study
+        x2, imp2 = W.c2_weight_and_importance()
+        res["c2_wmse"] = study.nvfp4_scale_rules(x2.to("cuda:0"), imp2.to("cuda:0"))
+        res["c4_q_mse"] = study.nvfp4_scale_rules(W.c4_matrix("q").to("cuda:0"))
+        res["c1_mse"] = study.nvfp4_scale_rules(W.c1_weight().to("cuda:0"))
+        x3 = W.c3_activation().to("cuda:0")
+        res["c3_mxfp4"] = [study.mxfp4_code_usage(x3, window=w, hadamard_n=h)
+                           for h in (0, 32) for w in ((0, 0), (-1, 0))]
     elif args.config == "c4":
         total_ms = {"mse": 0.0, "wmse": 0.0}
         n = 0

@@ -442,3 +442,28 @@ def test_relaxed_quantizer_data_errors():
     with pytest.raises(fq.FP4QError, match="scale or coefficient"):
         fq.quantize_relaxed(x, base.scales, c, global_scale=base.global_scale, check=True)
     fq.quantize_relaxed(x, base.scales, None, global_scale=base.global_scale, check=True)
+
+
+# ------------------------------------------------------ scale study ----
+def test_study_histogram_and_rule_ordering():
+    from fp4_post_quantization_amd import study
+    fq = _fp4()
+    x = W.random_matrix(96, 1024, seed=99, dist="laplace", dtype=torch.bfloat16)
+    xd = x.to(DEV)
+    r = fq.quantize_mxfp4(xd, hadamard_n=32)
+    ref = Q.quantize_mxfp4(_host_f32(x), hadamard_n=32)
+    h = study.code_histogram(r.codes).cpu().numpy()
+    np.testing.assert_array_equal(h, np.bincount(Q.unpack_nibbles(ref.codes).ravel(), minlength=16))
+    imp = W.random_importance(1024, seed=100).to(DEV)
+    res = study.nvfp4_scale_rules(xd, imp, iters=2)
+    a = fq.quantize_nvfp4(xd, imp, window=(0, 0)).block_loss
+    s_ = fq.quantize_nvfp4(xd, imp, window=(-8, 7)).block_loss
+    e = fq.quantize_nvfp4(xd, imp, window=(-126, 126)).block_loss
+    torch.cuda.synchronize()
+    # wider windows contain the narrower ones and use identical arithmetic
+    assert bool((s_ <= a).all()) and bool((e <= s_).all())
+    assert res["sweep_vs_absmax"]["loss_reduction"] >= 0
+    assert res["exhaustive_vs_sweep"]["loss_reduction"] >= 0
+    assert sum(res["sweep_offset_histogram"].values()) == res["blocks"]
+    u = study.mxfp4_code_usage(xd, window=(0, 0))
+    assert abs(sum(u["magnitude_histogram"]) - x.numel()) == 0
