@@ -22,11 +22,14 @@ with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
 c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
 focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8),
-study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage).
+study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage),
+gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight).
 """
 
 import argparse
 import json
+
+import numpy as np
 import math
 import os
 import sys
@@ -236,6 +239,33 @@ def run_other(args):
         x3 = W.c3_activation().to("cuda:0")
         res["c3_mxfp4"] = [study.mxfp4_code_usage(x3, window=w, hadamard_n=h)
                            for h in (0, 32) for w in ((0, 0), (-1, 0))]
+    elif args.config == "gptq":
+        # GPTQ with ScaleSweep group scales on the 4096 x 4096 c2 weight,
+        # Hessian from 2048 correlated synthetic calibration tokens
+        x, imp = W.c2_weight_and_importance()
+        X = W.calibration_activations(2048, 4096, seed=204)
+        H, U = W.hessian_and_factor(X)
+        xd = x.to("cuda:0").float()
+        Ud = torch.from_numpy(U).to("cuda:0")
+        Hd = torch.from_numpy(H).to("cuda:0")
+        impd = torch.from_numpy(np.diag(H).astype(np.float32)).to("cuda:0")
+
+        def proxy(codes, scales, S):
+            xh = fq.dequantize("nvfp4", codes, scales, S).double()
+            d = xd.double() - xh
+            return float(((d @ Hd) * d).sum())
+
+        for name, im in (("mse", None), ("wmse", impd)):
+            r = fq.gptq_nvfp4(xd, Ud, im, check=True)
+            step = lambda i: fq.gptq_nvfp4(xd, Ud, im)
+            prewarm(step, seconds=0.5)
+            ms = _events_time(step, max(3, args.steps // 10))
+            rtn = fq.quantize_nvfp4(xd, im)
+            ab = fq.quantize_nvfp4(xd, im, window=(0, 0))
+            res[name] = {"ms": ms, "gel_s": xd.numel() / ms / 1e6,
+                         "proxy_gptq": proxy(r.codes, r.scales, r.global_scale),
+                         "proxy_rtn_sweep": proxy(rtn.codes, rtn.scales, rtn.global_scale),
+                         "proxy_rtn_absmax": proxy(ab.codes, ab.scales, ab.global_scale)}
     elif args.config == "c4":
         total_ms = {"mse": 0.0, "wmse": 0.0}
         n = 0

@@ -9,6 +9,7 @@ HIP kernels.  There is no CPU fallback; a missing library raises.
     quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, ...)
     quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, ...)
     quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub=8, ...)
+    gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, ...)
     dequantize(fmt, codes, scales, global_scale=None)
     block_hadamard(x, n)
 """
@@ -21,7 +22,7 @@ from . import _lib as L
 from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
-    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "dequantize", "block_hadamard",
+    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "gptq_nvfp4", "dequantize", "block_hadamard",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
 ]
 
@@ -79,6 +80,8 @@ def _check_data(ws):
             names.append("invalid global scale")
         if st & L.DATA_BAD_SCALE:
             names.append("invalid scale or coefficient")
+        if st & L.DATA_BAD_HESSIAN:
+            names.append("invalid inverse-Hessian factor")
         raise FP4QError("data error: " + ", ".join(names))
 
 
@@ -221,6 +224,43 @@ def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub
     if check:
         _check_data(ws)
     return codes, dq
+
+
+def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *, ws=None, check=False):
+    """GPTQ with ScaleSweep group scales (NVFP4).  w: [R, C] weight (any
+    float dtype; a float32 working copy is made, C a multiple of 128);
+    hinv_chol: [C, C] upper Cholesky factor U of the damped inverse Hessian
+    (H^-1 = U^T U); importance: per-column WMSE weights or None (MSE).
+    Returns an NVFP4Result without losses and offsets."""
+    lib = L.load()
+    if w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D device tensor")
+    rows, cols = w.shape
+    dev = w.device
+    work = w.to(torch.float32).contiguous().clone()
+    U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
+    if U.shape != (cols, cols):
+        raise ValueError("hinv_chol must be [cols, cols]")
+    imp = _importance(importance, cols, dev)
+    if window is None:
+        window = (-8, 7) if imp is not None else (-3, 7)
+    out = NVFP4Result(
+        codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+        global_scale=torch.empty(1, dtype=torch.float32, device=dev),
+        block_loss=None, offsets=None)
+    flags = 0
+    if global_scale is not None:
+        out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
+        flags |= L.GIVEN_SCALE
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_gptq_nvfp4(
+        work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
+        flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
 
 
 def dequantize(fmt, codes, scales, global_scale=None, out=None):

@@ -17,6 +17,7 @@ DATA_NONFINITE_INPUT = 0x1
 DATA_BAD_IMPORTANCE = 0x2
 DATA_BAD_GLOBAL_SCALE = 0x4
 DATA_BAD_SCALE = 0x8
+DATA_BAD_HESSIAN = 0x10
 
 EXPORTS = (
     "fp4q_version",
@@ -25,6 +26,7 @@ EXPORTS = (
     "fp4q_quantize_nvfp4",
     "fp4q_quantize_mxfp4",
     "fp4q_quantize_relaxed",
+    "fp4q_gptq_nvfp4",
     "fp4q_dequantize",
     "fp4q_block_hadamard",
 )
@@ -44,6 +46,7 @@ _SIGNATURES = {
     "fp4q_quantize_mxfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I,
                                  _P, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_quantize_relaxed": (_I, [_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
+    "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_dequantize": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "fp4q_block_hadamard": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P]),
 }

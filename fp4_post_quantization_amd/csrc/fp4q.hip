@@ -613,6 +613,203 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
   }
 }
 
+// ================================================================ GPTQ ====
+// Column-by-column NVFP4 quantization with error feedback through the
+// inverse-Hessian factor U (upper Cholesky factor of H^-1), in lazy
+// batches of 128 columns; each 16-column group's scale comes from the
+// ScaleSweep candidate search on the group's current values.
+
+constexpr int kGptqBatch = 128;
+constexpr int kGptqRowsPerBlock = 16;  // one wave per row
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Global scale from the max-pass partials (a single workgroup).
+__global__ __launch_bounds__(kThreads) void scale_from_partials_kernel(const uint32_t *__restrict__ partials,
+                                                                        int n, float *__restrict__ gscale,
+                                                                        uint32_t *__restrict__ status) {
+  __shared__ uint32_t red[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partials[i]);
+  m = wave_max_u32(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kWaves; ++i) m = max(m, red[i]);
+    m = max(m, red[0]);
+    *gscale = as_f(m) / 1536.0f;
+    if (m >= 0x7F800000u) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+  }
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// One batch of 128 columns [i1, i1 + 128) for kGptqRowsPerBlock rows.  Lane
+// j of a row's wave holds columns j and 64 + j; at step i every lane sees
+// the current value of column i (readlane), quantizes it identically, and
+// updates its own columns with fma(-err, U[i][col], w).  The batch's scaled
+// errors replace its columns of W for the trailing update.
+template <bool WMSE>
+__global__ __launch_bounds__(1024) void gptq_batch_kernel(float *__restrict__ W, int64_t ld, int rows,
+                                                           int cols, int i1, const float *__restrict__ U,
+                                                           const float *__restrict__ imp,
+                                                           const float *__restrict__ gscale, int lo, int hi,
+                                                           uint8_t *__restrict__ codes,
+                                                           uint8_t *__restrict__ scales,
+                                                           uint32_t *__restrict__ status) {
+  __shared__ float Ub[kGptqBatch][kGptqBatch];
+  __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < kGptqBatch * kGptqBatch / 4; e += 1024) {
+    const int rr = e >> 5, c4 = e & 31;
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + rr) * cols + i1 + c4 * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Ub[rr][c4 * 4 + k] = v[k];
+  }
+  if (tid < 128) {
+    Vtab[tid] = kE4M3.v[tid];
+    Rtab[tid] = kE4M3.r[tid];
+    const float d = U[(int64_t)(i1 + tid) * cols + i1 + tid];
+    if (!((d > 0.0f) & (d <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
+    rdiag[tid] = 1.0f / d;  // correctly rounded
+  }
+  __syncthreads();
+  const int r = blockIdx.x * kGptqRowsPerBlock + wave;
+  if (r >= rows) return;
+  const float S = *gscale;
+  const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
+  float *wr = W + (int64_t)r * ld + i1;
+  float w0 = wr[lane], w1 = wr[64 + lane];
+  float m0 = 1.0f, m1 = 1.0f;
+  if constexpr (WMSE) {
+    m0 = imp[i1 + lane];
+    m1 = imp[i1 + 64 + lane];
+  }
+  uint32_t c0 = 0, c1 = 0;
+  float e0 = 0.0f, e1 = 0.0f;
+  float V = 1.0f, R = 1.0f;
+  for (int i = 0; i < kGptqBatch; ++i) {
+    const int src = i & 63;
+    const bool upper = i >= 64;
+    if ((i & 15) == 0) {
+      // the group's 16 current values (and weights), the same in every lane
+      float us[16], wg[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        us[e] = readlane_f(upper ? w1 : w0, src + e) * S_inv;
+        wg[e] = WMSE ? readlane_f(upper ? m1 : m0, src + e) : 1.0f;
+      }
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(us[e]));
+      const int base = max(e4m3_rne_sat(a / 6.0f), 1);
+      // lane k evaluates the candidate at offset lo + k
+      const int p = base + lo + lane;
+      const bool ok = (lane <= hi - lo) & (p >= 1) & (p <= 126);
+      const int pc = min(max(p, 1), 126);
+      const float Rk = Rtab[pc];
+      float y[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[e] = us[e] * Rk;
+      const float L = loss_of_codes<WMSE>(us, wg, cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), Vtab[pc]);
+      // least loss, then smallest pattern, over the wave
+      float Lm = ok ? L : __builtin_inff();
+      int pm = ok ? p : 0x7FFFFFFF;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float L2 = __shfl_xor(Lm, m, 64);
+        const int p2 = __shfl_xor(pm, m, 64);
+        const bool take = (L2 < Lm) | ((L2 == Lm) & (p2 < pm));
+        Lm = take ? L2 : Lm;
+        pm = take ? p2 : pm;
+      }
+      int ps = __builtin_amdgcn_readfirstlane(pm);
+      if (ps == 0x7FFFFFFF) ps = max(1, base + lo);
+      V = Vtab[ps];
+      R = Rtab[ps];
+      if (lane == 0) scales[(int64_t)r * (cols / 16) + ((i1 + i) >> 4)] = (uint8_t)ps;
+    }
+    const float wi = readlane_f(upper ? w1 : w0, src);
+    const float us_i = wi * S_inv;
+    const float y_i = us_i * R;
+    const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
+    const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
+    const float what = (q * V) * S;           // q * V exact, one rounding by S
+    const float err = (wi - what) * rdiag[i];
+    if (lane == src) {
+      if (upper) {
+        c1 = code;
+        e1 = err;
+      } else {
+        c0 = code;
+        e0 = err;
+      }
+    }
+    // U is upper triangular: columns already done get fma(-err, 0, w)
+    w0 = fmaf(-err, Ub[i][lane], w0);
+    w1 = fmaf(-err, Ub[i][64 + lane], w1);
+  }
+  wr[lane] = e0;
+  wr[64 + lane] = e1;
+  const uint32_t n0 = (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)c0)));
+  const uint32_t n1 = (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)c1)));
+  if ((lane & 1) == 0) {
+    uint8_t *cr = codes + (int64_t)r * (cols / 2) + i1 / 2;
+    cr[lane >> 1] = (uint8_t)(c0 | (n0 << 4));
+    cr[32 + (lane >> 1)] = (uint8_t)(c1 | (n1 << 4));
+  }
+}
+
+// Trailing update W[:, i2:] -= E * U[i1:i2, i2:] with E = W[:, i1:i2] (the
+// batch's scaled errors), i2 = i1 + 128: a dense contraction with K = 128
+// on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile; E and U
+// tiles are staged in LDS (k-major), each wave owns a 32 x 32 sub-tile.
+__global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict__ W, int64_t ld, int rows,
+                                                               int cols, int i1,
+                                                               const float *__restrict__ U) {
+  __shared__ float As[kGptqBatch][64];
+  __shared__ float Bs[kGptqBatch][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i2 = i1 + kGptqBatch;
+  const int r0 = blockIdx.x * 64, c0 = i2 + blockIdx.y * 64;
+  for (int e = tid; e < 64 * 32; e += kThreads) {
+    const int rr = e >> 5, k4 = e & 31;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r0 + rr < rows) v = *reinterpret_cast<const f32x4 *>(W + (int64_t)(r0 + rr) * ld + i1 + k4 * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) As[k4 * 4 + k][rr] = v[k];
+  }
+  for (int e = tid; e < kGptqBatch * 16; e += kThreads) {
+    const int kk = e >> 4, j4 = e & 15;
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + kk) * cols + c0 + j4 * 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Bs[kk][j4 * 4 + k] = v[k];
+  }
+  __syncthreads();
+  const int wr = wave & 1, wc = wave >> 1;
+  const int lr = lane & 31, lk = lane >> 5;
+  f32x16 acc = {0};
+#pragma unroll 8
+  for (int k = 0; k < kGptqBatch; k += 2) {
+    const float av = As[k + lk][wr * 32 + lr];
+    const float bv = Bs[k + lk][wc * 32 + lr];
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+  // accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+    const int col = c0 + wc * 32 + lr;
+    if (row < rows) {
+      float *p = W + (int64_t)row * ld + col;
+      *p = *p - acc[v];
+    }
+  }
+}
+
 // Decode of an arbitrary E4M3 byte (sign, 0x7F / 0xFF = NaN).
 __device__ __forceinline__ float e4m3_decode_any(uint32_t b) {
   const uint32_t m = b & 0x7Fu;
@@ -958,6 +1155,60 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
     else
       with_sub(std::integral_constant<int, FP4Q_MXFP4>{});
   });
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
+                                         const float *hinv_chol, const float *importance, int off_lo,
+                                         int off_hi, uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                         float *global_scale, void *workspace, size_t workspace_bytes,
+                                         void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!global_scale || (!empty && (!w || !hinv_chol || !codes || !scales))) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 63) return FP4Q_ERR_ARG;
+  if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
+    return FP4Q_ERR_SHAPE;
+  if (empty) return FP4Q_OK;
+  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || (importance && !aligned(importance, 4)))
+    return FP4Q_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
+  const bool given = flags & FP4Q_GIVEN_SCALE;
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  if (!given) {
+    int n_partials;
+    if (ld == cols) {
+      const int64_t n_vec = rows * cols * 4 / 16;
+      n_partials = (int)std::min<int64_t>(kAmaxGroups, (n_vec + kThreads * 8 - 1) / (kThreads * 8));
+      hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n_partials), dim3(kThreads), 0, s, (const u32x4 *)w,
+                         n_vec, partials);
+    } else {
+      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
+      hipLaunchKernelGGL((amax_kernel<float, 0>), dim3(n_partials), dim3(kThreads), 0, s, (const float *)w, ld,
+                         cpr, total, partials);
+    }
+    hipLaunchKernelGGL(scale_from_partials_kernel, dim3(1), dim3(kThreads), 0, s, partials, n_partials,
+                       global_scale, status);
+  }
+  const bool wmse = importance != nullptr;
+  const int gb = ceil_div(rows, kGptqRowsPerBlock);
+  for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
+    if (wmse)
+      hipLaunchKernelGGL((gptq_batch_kernel<true>), dim3(gb), dim3(1024), 0, s, w, ld, (int)rows, (int)cols, i1,
+                         hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
+    else
+      hipLaunchKernelGGL((gptq_batch_kernel<false>), dim3(gb), dim3(1024), 0, s, w, ld, (int)rows, (int)cols, i1,
+                         hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
+    const int rest = (int)cols - i1 - kGptqBatch;
+    if (rest > 0)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), rest / 64), dim3(kThreads), 0, s, w, ld,
+                         (int)rows, (int)cols, i1, hinv_chol);
+  }
   return last_hip_status();
 }
 

@@ -80,6 +80,7 @@ typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
 #define FP4Q_DATA_BAD_IMPORTANCE 0x2u   /* an importance entry is < 0, Inf or NaN */
 #define FP4Q_DATA_BAD_GLOBAL_SCALE 0x4u /* given S is < 0, Inf or NaN */
 #define FP4Q_DATA_BAD_SCALE 0x8u        /* fp4q_quantize_relaxed: invalid scale byte or coefficient */
+#define FP4Q_DATA_BAD_HESSIAN 0x10u     /* fp4q_gptq_nvfp4: a diagonal entry of U is not finite and > 0 */
 
 /* Library version as 10000 * major + 100 * minor + patch. */
 int fp4q_version(void);
@@ -198,6 +199,41 @@ fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dt
                                     const float *global_scale, const uint16_t *coeffs, int sub_block,
                                     uint8_t *codes, float *dequant_out, void *workspace,
                                     size_t workspace_bytes, void *stream);
+
+/*
+ * GPTQ with ScaleSweep group scales for NVFP4 ([SS] Principais
+ * Contribuições 2: the bounded sweep chooses block scales in GPTQ
+ * pipelines too; [MR] 2., MR-GPTQ component 1: the grid is chosen per
+ * format).  GPTQ (only named on the pages) is the published column-by-column
+ * quantization with error feedback through the inverse Hessian.
+ *
+ *   w          [rows x cols] float32, leading dimension ld (multiple of 4),
+ *              the weight; OVERWRITTEN (working storage: on return it holds
+ *              the scaled quantization errors).
+ *   cols       a multiple of 128 (the lazy-batch width).
+ *   hinv_chol  [cols x cols] float32 row-major U, the upper Cholesky factor
+ *              of H^-1 (H = X^T X of calibration activations, damped by the
+ *              caller), so that H^-1 = U^T U.
+ *   importance [cols] float32 per-column WMSE weights, or NULL for MSE.
+ *   off_lo, off_hi  E4M3 bit-pattern window of the group-scale search
+ *              (off_hi - off_lo <= 63), e.g. -3, 7 (MSE) or -8, 7 (WMSE).
+ *   flags      0 or FP4Q_GIVEN_SCALE (read S from *global_scale).
+ *   codes, scales, global_scale  as for fp4q_quantize_nvfp4 (no losses).
+ *
+ * Computation: S = fp32(max|w| / 1536) from w before any update.  Columns
+ * are processed in order; when column c opens a 16-column group, each row's
+ * scale pattern is the sweep's choice on the group's current values;
+ * column c is rounded to nearest at that scale, its scaled error
+ * err = fp32(fp32(w_c - x_hat_c) * fp32(1 / U[c][c])) is kept, and every
+ * later column j of the same 128-column batch becomes fma(-err, U[c][j],
+ * w_j); after a batch the remaining columns receive w -= Err * U[batch, rest]
+ * (an fp32 MFMA contraction).  A non-positive or non-finite diagonal entry of
+ * U sets FP4Q_DATA_BAD_HESSIAN.
+ */
+fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
+                              const float *importance, int off_lo, int off_hi, uint32_t flags,
+                              uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * Dequantization (the consumer side: only codes and dequantization scales

@@ -1,0 +1,81 @@
+"""GPTQ with ScaleSweep group scales (oracle; test infrastructure).
+
+"Resumo Técnico: ScaleSweep" (Principais Contribuições 2; Resultados,
+Dados de Calibração): the bounded sweep chooses the NVFP4 block scales
+inside GPTQ pipelines as well as RTN ones.  "Bridging the Gap ... Microscaling
+FP4" (2. Metodologia, MR-GPTQ component 1): GPTQ's grid (group and global
+scales) is chosen per format.  GPTQ itself is only named on the pages; it is
+the published column-by-column quantization with error feedback through the
+inverse Hessian, restated here:
+
+  Given W (R x C), H = X^T X of calibration activations and U, the upper
+  Cholesky factor of H^-1 (H^-1 = U^T U), columns are quantized in order.
+  When column c opens a 16-column group, each row's E4M3 group scale is
+  chosen by the sweep (oracle.quant.sweep_blocks) on the group's current,
+  already error-corrected values; the global scale S is fixed from W before
+  any update.  Column c is quantized at its group's scale, its scaled error
+  err = fp32(fp32(W[:, c] - x_hat) * fp32(1 / U[c, c])) is recorded and
+  every later column j of the same 128-column batch is updated with one
+  fused multiply-add, W[:, j] <- fma(-err, U[c, j], W[:, j]); at the end of
+  a batch the columns after it receive W <- fp32(W - Err @ U[batch, after])
+  (the product taken in float64 here).
+  Readings: S from the matrix before GPTQ; err uses the reciprocal of the
+  diagonal; importance (WMSE) per column as given.
+"""
+
+import numpy as np
+
+from . import formats as F
+from .quant import fma_f32, global_scale_nvfp4, pack_nibbles, sweep_blocks, dequantize_nvfp4
+
+BATCH = 128
+
+
+def gptq_nvfp4(W, U, importance=None, window=None, global_scale=None):
+    """Returns (packed codes, scale patterns, S)."""
+    W = np.array(W, dtype=np.float32, copy=True)
+    U = np.asarray(U, dtype=np.float32)
+    rows, cols = W.shape
+    if cols % BATCH:
+        raise ValueError("columns must be a multiple of 128")
+    wmse = importance is not None
+    lo, hi = window if window is not None else ((-8, 7) if wmse else (-3, 7))
+    S = global_scale_nvfp4(W) if global_scale is None else np.float32(global_scale)
+    S_inv = np.float32(np.float32(1.0) / S) if S != 0 else np.float32(0.0)
+    recip = F.e4m3_reciprocal_table()
+    rdiag = (np.float32(1.0) / np.diag(U)).astype(np.float32)
+    imp = None if not wmse else np.asarray(importance, dtype=np.float32).reshape(cols // 16, 16)
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    for i1 in range(0, cols, BATCH):
+        i2 = i1 + BATCH
+        E = np.zeros((rows, BATCH), dtype=np.float32)
+        for c in range(i1, i2):
+            if c % 16 == 0:
+                g = c // 16
+                ub = (np.abs(W[:, c:c + 16]) * S_inv).astype(np.float32)[:, None, :]
+                p, _, _ = sweep_blocks(ub, None if imp is None else imp[g][None, None, :], lo, hi)
+                p = p[:, 0]
+                scales[:, g] = p
+                V = F.E4M3_VALUES[p]
+                R = recip[p]
+            w = W[:, c]
+            u = (np.abs(w) * S_inv).astype(np.float32)
+            idx = F.e2m1_rne_index((u * R).astype(np.float32))
+            mag = ((F.e2m1_value(idx) * V).astype(np.float32) * S).astype(np.float32)
+            what = np.where(np.signbit(w), -mag, mag).astype(np.float32)
+            codes[:, c] = (np.signbit(w).astype(np.uint8) << 3) | idx
+            err = ((w - what).astype(np.float32) * rdiag[c]).astype(np.float32)
+            E[:, c - i1] = err
+            if c + 1 < i2:
+                W[:, c + 1:i2] = fma_f32(-err[:, None], U[c, c + 1:i2][None, :], W[:, c + 1:i2])
+        if i2 < cols:
+            acc = (E.astype(np.float64) @ U[i1:i2, i2:].astype(np.float64)).astype(np.float32)
+            W[:, i2:] = (W[:, i2:] - acc).astype(np.float32)
+    return pack_nibbles(codes), scales, S
+
+
+def proxy_loss(W0, codes, scales, S, H):
+    """GPTQ's objective tr((W0 - W_hat) H (W0 - W_hat)^T) in float64."""
+    D = np.asarray(W0, dtype=np.float64) - dequantize_nvfp4(codes, scales, S).astype(np.float64)
+    return float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))

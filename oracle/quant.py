@@ -137,6 +137,35 @@ class NVFP4Result:
     rotated: np.ndarray      # float32 [R, C], the values quantized
 
 
+def sweep_blocks(ub, w, lo, hi):
+    """Steps 3-6 of the NVFP4 sweep on blocks of magnitudes ub [..., 16] in
+    units of S with per-element weights w (broadcastable, or None for MSE):
+    returns the chosen pattern, its loss and the AbsMax base pattern."""
+    a = ub.max(axis=-1)
+    t = (a / np.float32(6.0)).astype(np.float32)
+    base = np.maximum(F.e4m3_rne_pattern(t), 1)
+    recip = F.e4m3_reciprocal_table()
+    offsets = np.arange(lo, hi + 1)
+    losses = np.empty(base.shape + (offsets.size,), dtype=np.float32)
+    valid = np.empty(base.shape + (offsets.size,), dtype=bool)
+    for k, o in enumerate(offsets):
+        p = base + o
+        ok = (p >= 1) & (p <= F.E4M3_MAX_PATTERN)
+        pc = np.clip(p, 1, F.E4M3_MAX_PATTERN)
+        V = F.E4M3_VALUES[pc][..., None]
+        R = recip[pc][..., None]
+        y = (ub * R).astype(np.float32)
+        q = F.e2m1_value(F.e2m1_rne_index(y))
+        d = (q * V).astype(np.float32)
+        e = (ub - d).astype(np.float32)
+        losses[..., k] = fused_sum_sq(e, None if w is None else np.broadcast_to(w, e.shape))
+        valid[..., k] = ok
+    k_best = _first_argmin(losses, valid)
+    p_best = base + offsets[k_best]
+    L_best = np.take_along_axis(losses, k_best[..., None], axis=-1)[..., 0]
+    return p_best, L_best, base
+
+
 def global_scale_nvfp4(x):
     """S = fp32(max|x| / 1536) for a float32 matrix ("Resumo Técnico:
     ScaleSweep", 2. Limites Teóricos, Escala Global)."""
@@ -180,35 +209,9 @@ def quantize_nvfp4(x, importance=None, window=None, block=16,
 
     u = (np.abs(x) * S_inv).astype(np.float32)
     ub = u.reshape(rows, cols // block, block)
-    a = ub.max(axis=-1)
-    t = (a / np.float32(6.0)).astype(np.float32)
-    base = np.maximum(F.e4m3_rne_pattern(t), 1)
-
-    if wmse:
-        w = np.asarray(importance, dtype=np.float32).reshape(cols // block, block)
-
+    w = np.asarray(importance, dtype=np.float32).reshape(cols // block, block) if wmse else None
+    p_best, L_best, base = sweep_blocks(ub, w, lo, hi)
     recip = F.e4m3_reciprocal_table()
-    offsets = np.arange(lo, hi + 1)
-    n_cand = offsets.size
-    losses = np.empty(base.shape + (n_cand,), dtype=np.float32)
-    valid = np.empty(base.shape + (n_cand,), dtype=bool)
-    for k, o in enumerate(offsets):
-        p = base + o
-        ok = (p >= 1) & (p <= F.E4M3_MAX_PATTERN)
-        pc = np.clip(p, 1, F.E4M3_MAX_PATTERN)
-        V = F.E4M3_VALUES[pc][..., None]
-        R = recip[pc][..., None]
-        y = (ub * R).astype(np.float32)
-        q = F.e2m1_value(F.e2m1_rne_index(y))
-        d = (q * V).astype(np.float32)
-        e = (ub - d).astype(np.float32)
-        losses[..., k] = fused_sum_sq(e, np.broadcast_to(w, e.shape) if wmse else None)
-        valid[..., k] = ok
-
-    k_best = _first_argmin(losses, valid)
-    p_best = base + offsets[k_best]
-    L_best = np.take_along_axis(losses, k_best[..., None], axis=-1)[..., 0]
-
     R_best = recip[p_best][..., None]
     idx = F.e2m1_rne_index((ub * R_best).astype(np.float32))
     sign = np.signbit(x).reshape(rows, cols // block, block).astype(np.uint8)

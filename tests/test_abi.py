@@ -145,6 +145,24 @@ def test_relaxed_validation():
     assert rq(dq=OUT + 4) == L.ERR_ALIGN
 
 
+def test_gptq_validation():
+    L, lib = _lib()
+    wsb = lib.fp4q_workspace_bytes()
+    gq = lambda **kw: lib.fp4q_gptq_nvfp4(
+        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("u", OUT), None, kw.get("lo", -3),
+        kw.get("hi", 7), kw.get("flags", 0), OUT, OUT, kw.get("gs", OUT), kw.get("ws", WS), wsb, None)
+    assert gq(w=None) == L.ERR_NULL
+    assert gq(u=None) == L.ERR_NULL
+    assert gq(gs=None) == L.ERR_NULL
+    assert gq(ws=None) == L.ERR_WORKSPACE
+    assert gq(lo=-60, hi=7) == L.ERR_ARG
+    assert gq(flags=4) == L.ERR_ARG
+    assert gq(cols=144, ld=144) == L.ERR_SHAPE
+    assert gq(ld=100) == L.ERR_SHAPE
+    assert gq(ld=130) == L.ERR_ALIGN
+    assert gq(u=OUT + 4) == L.ERR_ALIGN
+
+
 def test_empty_shapes_need_no_device_for_dequant_and_hadamard():
     L, lib = _lib()
     assert lib.fp4q_dequantize(L.NVFP4, OUT, OUT, OUT, 0, 64, 16, OUT, None) == L.OK

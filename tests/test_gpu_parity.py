@@ -16,6 +16,7 @@ import torch
 
 import workloads as W
 from oracle import focus as FO
+from oracle import gptq as GQ
 from oracle import formats as F
 from oracle import quant as Q
 from oracle import hadamard as OH
@@ -467,3 +468,73 @@ def test_study_histogram_and_rule_ordering():
     assert sum(res["sweep_offset_histogram"].values()) == res["blocks"]
     u = study.mxfp4_code_usage(xd, window=(0, 0))
     assert abs(sum(u["magnitude_histogram"]) - x.numel()) == 0
+
+
+# ------------------------------------------------------------- GPTQ ----
+def _gptq_inputs(rows, cols, seed):
+    w = W.random_matrix(rows, cols, seed=seed, dist="t4")
+    X = W.calibration_activations(4 * cols, cols, seed=seed + 1)
+    H, U = W.hessian_and_factor(X)
+    imp = torch.from_numpy(np.diag(H).astype(np.float32))
+    return w, H, U, imp
+
+
+@pytest.mark.parametrize("wmse", [False, True])
+def test_gptq_single_batch_bitexact(wmse):
+    """One 128-column batch involves no contraction, so GPU and oracle
+    follow the same float32 steps: codes, scales and S are bit-exact."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(37, 128, seed=110)
+    im = imp if wmse else None
+    res = fq.gptq_nvfp4(w.to(DEV), U, None if im is None else im.to(DEV), check=True)
+    torch.cuda.synchronize()
+    codes, scales, S = GQ.gptq_nvfp4(w.numpy(), U, None if im is None else im.numpy())
+    _assert_equal("gptq S", np.float32(_np(res.global_scale)[0]), S)
+    _assert_equal("gptq scales", _np(res.scales), scales)
+    _assert_equal("gptq codes", _np(res.codes), codes)
+
+
+def test_gptq_without_feedback_equals_sweep():
+    fq = _fp4()
+    w = W.random_matrix(64, 512, seed=111, dist="t4").to(DEV)
+    U = np.diag(np.exp(np.random.default_rng(112).normal(0, 0.3, 512))).astype(np.float32)
+    imp = W.random_importance(512, seed=113).to(DEV)
+    for im in (None, imp):
+        g = fq.gptq_nvfp4(w, U, im, check=True)
+        s_ = fq.quantize_nvfp4(w, im, check=True)
+        torch.cuda.synchronize()
+        _assert_equal("codes", _np(g.codes), _np(s_.codes))
+        _assert_equal("scales", _np(g.scales), _np(s_.scales))
+
+
+@pytest.mark.parametrize("wmse", [False, True])
+def test_gptq_multi_batch_against_oracle(wmse):
+    """Across batches the trailing update is an MFMA contraction whose
+    summation order differs from the oracle's float64 product, so values
+    agree to float32 rounding: code and scale mismatch rates <= 1e-3, GPTQ
+    proxy losses within 1e-3 relative, and both below round-to-nearest."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(192, 512, seed=114)
+    im = imp if wmse else None
+    res = fq.gptq_nvfp4(w.to(DEV), U, None if im is None else im.to(DEV), check=True)
+    torch.cuda.synchronize()
+    codes, scales, S = GQ.gptq_nvfp4(w.numpy(), U, None if im is None else im.numpy())
+    gc, gs = _np(res.codes), _np(res.scales)
+    assert np.float32(_np(res.global_scale)[0]) == S
+    assert np.mean(Q.unpack_nibbles(gc) != Q.unpack_nibbles(codes)) <= 1e-3
+    assert np.mean(gs != scales) <= 1e-3
+    lg = GQ.proxy_loss(w.numpy(), gc, gs, S, H)
+    lo = GQ.proxy_loss(w.numpy(), codes, scales, S, H)
+    rtn = Q.quantize_nvfp4(w.numpy(), None if im is None else im.numpy())
+    lr = GQ.proxy_loss(w.numpy(), rtn.codes, rtn.scales, rtn.global_scale, H)
+    assert abs(lg - lo) <= 1e-3 * lo
+    assert lg < lr and lo < lr
+
+
+def test_gptq_bad_hessian_sets_status():
+    fq = _fp4()
+    w = W.random_matrix(8, 128, seed=115).to(DEV)
+    U = np.eye(128, dtype=np.float32)
+    U[5, 5] = 0.0
+    with pytest.raises(fq.FP4QError, match="inverse-Hessian"):
+        fq.gptq_nvfp4(w, U, check=True)

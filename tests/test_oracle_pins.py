@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from oracle import focus as FO
+from oracle import gptq as GQ
 from oracle import formats as F
 from oracle import hadamard as H
 from oracle import quant as Q
@@ -504,3 +505,43 @@ def test_relaxed_rejects_invalid_data():
     with pytest.raises(ValueError):
         FO.quantize_given_scales(x, "nvfp4", np.full((1, 1), 0x38, np.uint8), np.float32(1),
                                  np.zeros((1, 2), np.float16))
+
+
+# ------------------------------------------------------------------ GPTQ ----
+def test_gptq_without_feedback_is_the_sweep():
+    """With a diagonal inverse-Hessian factor no error propagates, so GPTQ
+    reduces to round-to-nearest at the sweep's scales (MSE and WMSE)."""
+    rng = np.random.default_rng(25)
+    W = (rng.standard_t(4, (24, 256)) * 0.02).astype(np.float32)
+    U = np.diag(np.exp(rng.normal(0, 0.3, 256))).astype(np.float32)
+    imp = np.exp(rng.standard_normal(256)).astype(np.float32)
+    for im in (None, imp):
+        codes, scales, S = GQ.gptq_nvfp4(W, U, im)
+        ref = Q.quantize_nvfp4(W, im)
+        np.testing.assert_array_equal(codes, ref.codes)
+        np.testing.assert_array_equal(scales, ref.scales)
+        assert S == ref.global_scale
+
+
+def test_gptq_lowers_the_proxy_loss():
+    """GPTQ's error feedback lowers tr(dW H dW^T) against round-to-nearest
+    at the sweep's scales on correlated calibration data."""
+    import workloads as W_
+    rng = np.random.default_rng(26)
+    W = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    X = W_.calibration_activations(512, 256, seed=27)
+    H, U = W_.hessian_and_factor(X)
+    codes, scales, S = GQ.gptq_nvfp4(W, U)
+    rtn = Q.quantize_nvfp4(W)
+    g = GQ.proxy_loss(W, codes, scales, S, H)
+    r = GQ.proxy_loss(W, rtn.codes, rtn.scales, rtn.global_scale, H)
+    assert g < 0.9 * r
+
+
+def test_hessian_factor_inverts():
+    import workloads as W_
+    X = W_.calibration_activations(300, 128, seed=28)
+    H, U = W_.hessian_and_factor(X, damp=0.01)
+    Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(128)
+    np.testing.assert_allclose(U.astype(np.float64).T @ U.astype(np.float64) @ Hd, np.eye(128), atol=2e-4)
+    assert np.allclose(U, np.triu(U))

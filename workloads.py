@@ -166,3 +166,29 @@ def random_importance(cols, seed, zero_frac=0.0):
     if zero_frac:
         w[rng.random(cols) < zero_frac] = 0.0
     return torch.from_numpy(w)
+
+
+# ------------------------------------------------------------ GPTQ ----
+def calibration_activations(n_tokens, n_channels, seed, corr=0.5):
+    """Correlated synthetic calibration activations: lognormal channel
+    scales times Gaussian tokens mixed by a random low-rank factor."""
+    rng = np.random.default_rng(seed)
+    lam = np.exp(rng.standard_normal(n_channels))
+    rank = max(1, n_channels // 16)
+    z = rng.standard_normal((n_tokens, n_channels)) * (1 - corr) \
+        + rng.standard_normal((n_tokens, rank)) @ rng.standard_normal((rank, n_channels)) * (corr / np.sqrt(rank))
+    return z * lam
+
+
+def hessian_and_factor(x, damp=0.01):
+    """H = X^T X (float64) and U, the upper Cholesky factor of (H + damp *
+    mean(diag H) * I)^-1, as float32: the inputs GPTQ consumes.  Computed
+    with numpy's dense linear algebra (input preparation, not the path)."""
+    x = np.asarray(x, dtype=np.float64)
+    H = x.T @ x
+    Hd = H + damp * np.mean(np.diag(H)) * np.eye(H.shape[0])
+    L = np.linalg.cholesky(Hd)
+    Linv = np.linalg.inv(L)
+    Hinv = Linv.T @ Linv
+    U = np.linalg.cholesky(Hinv).T
+    return H, np.ascontiguousarray(U, dtype=np.float32)
