@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "fp4q.h"
 #include "fp4q_device.h"
@@ -620,7 +621,6 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
 // ScaleSweep candidate search on the group's current values.
 
 constexpr int kGptqBatch = 128;
-constexpr int kGptqRowsPerBlock = 16;  // one wave per row
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -647,27 +647,40 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// One batch of 128 columns [i1, i1 + 128) for kGptqRowsPerBlock rows.  Lane
-// j of a row's wave holds columns j and 64 + j; at step i every lane sees
-// the current value of column i (readlane), quantizes it identically, and
-// updates its own columns with fma(-err, U[i][col], w).  The batch's scaled
-// errors replace its columns of W for the trailing update.
+// One batch of 128 columns [i1, i1 + 128).  A row is handled by 16 lanes
+// (one DPP row; four rows per wave), lane t holding columns 8t .. 8t+7 of
+// the batch.  At step i the owner's current value of column i is broadcast
+// to the row's 16 lanes (DPP row broadcast, a VALU modifier, so the serial
+// chain from one column's error to the next column's value has no LDS
+// round trip), which all quantize it identically; the owner keeps code and
+// error, and every lane updates its own columns with fma(-err, U[i][col], w)
+// (U is zero below the diagonal, so finished columns are left as they are).
+// At the start of each 16-column group lane t evaluates the window candidate
+// at offset lo + t on the group's current values (the sweep's loss), and a
+// (loss, pattern) minimum over the row's lanes picks the scale.  The batch's
+// scaled errors replace its columns of W for the trailing update.  The
+// column loop is unrolled at compile time because the broadcast's source
+// lane is an immediate.
+constexpr int kGptqBatchThreads = 256;
+constexpr int kGptqRowsPerWg = kGptqBatchThreads / 16;
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &&f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
 template <bool WMSE>
-__global__ __launch_bounds__(1024) void gptq_batch_kernel(float *__restrict__ W, int64_t ld, int rows,
-                                                           int cols, int i1, const float *__restrict__ U,
-                                                           const float *__restrict__ imp,
-                                                           const float *__restrict__ gscale, int lo, int hi,
-                                                           uint8_t *__restrict__ codes,
-                                                           uint8_t *__restrict__ scales,
-                                                           uint32_t *__restrict__ status) {
+__global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
+    float *__restrict__ W, int64_t ld, int rows, int cols, int i1, const float *__restrict__ U,
+    const float *__restrict__ imp, const float *__restrict__ gscale, int lo, int hi, uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ scales, uint32_t *__restrict__ status) {
   __shared__ float Ub[kGptqBatch][kGptqBatch];
-  __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < kGptqBatch * kGptqBatch / 4; e += 1024) {
+  __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch], impb[kGptqBatch];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kGptqBatch * kGptqBatch / 4; e += kGptqBatchThreads) {
     const int rr = e >> 5, c4 = e & 31;
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + rr) * cols + i1 + c4 * 4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) Ub[rr][c4 * 4 + k] = v[k];
+    *reinterpret_cast<f32x4 *>(&Ub[rr][c4 * 4]) =
+        *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + rr) * cols + i1 + c4 * 4);
   }
   if (tid < 128) {
     Vtab[tid] = kE4M3.v[tid];
@@ -675,138 +688,162 @@ __global__ __launch_bounds__(1024) void gptq_batch_kernel(float *__restrict__ W,
     const float d = U[(int64_t)(i1 + tid) * cols + i1 + tid];
     if (!((d > 0.0f) & (d <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
     rdiag[tid] = 1.0f / d;  // correctly rounded
+    impb[tid] = WMSE ? imp[i1 + tid] : 1.0f;
   }
   __syncthreads();
-  const int r = blockIdx.x * kGptqRowsPerBlock + wave;
-  if (r >= rows) return;
+  const int lane = tid & 63;
+  const int t = lane & 15;
+  const int r = blockIdx.x * kGptqRowsPerWg + (tid >> 4);
+  const bool live = r < rows;  // dead rows still take part in the broadcasts
   const float S = *gscale;
   const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
-  float *wr = W + (int64_t)r * ld + i1;
-  float w0 = wr[lane], w1 = wr[64 + lane];
-  float m0 = 1.0f, m1 = 1.0f;
-  if constexpr (WMSE) {
-    m0 = imp[i1 + lane];
-    m1 = imp[i1 + 64 + lane];
+  float *wr = W + (int64_t)(live ? r : 0) * ld + i1 + 8 * t;
+  float w[8];
+  {
+    const f32x4 a = live ? *reinterpret_cast<const f32x4 *>(wr) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 b = live ? *reinterpret_cast<const f32x4 *>(wr + 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[k] = a[k];
+      w[4 + k] = b[k];
+    }
   }
-  uint32_t c0 = 0, c1 = 0;
-  float e0 = 0.0f, e1 = 0.0f;
+  uint32_t code8 = 0;
+  float err8[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) err8[k] = 0.0f;
   float V = 1.0f, R = 1.0f;
-  for (int i = 0; i < kGptqBatch; ++i) {
-    const int src = i & 63;
-    const bool upper = i >= 64;
-    if ((i & 15) == 0) {
-      // the group's 16 current values (and weights), the same in every lane
+  static_for(std::make_integer_sequence<int, 16>{}, [&](auto tt_c) {
+    constexpr int tt = decltype(tt_c)::value;
+    if constexpr ((tt & 1) == 0) {
+      // group [8 tt, 8 tt + 16): its values sit in lanes tt and tt + 1 of the row
       float us[16], wg[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        us[e] = readlane_f(upper ? w1 : w0, src + e) * S_inv;
-        wg[e] = WMSE ? readlane_f(upper ? m1 : m0, src + e) : 1.0f;
+      for (int e = 0; e < 8; ++e) {
+        us[e] = row_bcast<tt>(w[e]) * S_inv;
+        us[8 + e] = row_bcast<tt + 1>(w[e]) * S_inv;
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wg[e] = impb[8 * tt + e];
       float a = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(us[e]));
       const int base = max(e4m3_rne_sat(a / 6.0f), 1);
-      // lane k evaluates the candidate at offset lo + k
-      const int p = base + lo + lane;
-      const bool ok = (lane <= hi - lo) & (p >= 1) & (p <= 126);
+      const int p = base + lo + t;
+      const bool ok = (t <= hi - lo) & (p >= 1) & (p <= 126);
       const int pc = min(max(p, 1), 126);
       const float Rk = Rtab[pc];
       float y[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) y[e] = us[e] * Rk;
       const float L = loss_of_codes<WMSE>(us, wg, cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), Vtab[pc]);
-      // least loss, then smallest pattern, over the wave
       float Lm = ok ? L : __builtin_inff();
       int pm = ok ? p : 0x7FFFFFFF;
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float L2 = __shfl_xor(Lm, m, 64);
-        const int p2 = __shfl_xor(pm, m, 64);
+      for (int m = 8; m >= 1; m >>= 1) {
+        const float L2 = __shfl_xor(Lm, m, 16);
+        const int p2 = __shfl_xor(pm, m, 16);
         const bool take = (L2 < Lm) | ((L2 == Lm) & (p2 < pm));
         Lm = take ? L2 : Lm;
         pm = take ? p2 : pm;
       }
-      int ps = __builtin_amdgcn_readfirstlane(pm);
-      if (ps == 0x7FFFFFFF) ps = max(1, base + lo);
+      const int ps = pm == 0x7FFFFFFF ? max(1, base + lo) : pm;
       V = Vtab[ps];
       R = Rtab[ps];
-      if (lane == 0) scales[(int64_t)r * (cols / 16) + ((i1 + i) >> 4)] = (uint8_t)ps;
+      if (live && t == 0) scales[(int64_t)r * (cols / 16) + ((i1 + 8 * tt) >> 4)] = (uint8_t)ps;
     }
-    const float wi = readlane_f(upper ? w1 : w0, src);
-    const float us_i = wi * S_inv;
-    const float y_i = us_i * R;
-    const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
-    const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
-    const float what = (q * V) * S;           // q * V exact, one rounding by S
-    const float err = (wi - what) * rdiag[i];
-    if (lane == src) {
-      if (upper) {
-        c1 = code;
-        e1 = err;
-      } else {
-        c0 = code;
-        e0 = err;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = 8 * tt + k;
+      const float wi = row_bcast<tt>(w[k]);
+      const float us_i = wi * S_inv;
+      const float y_i = us_i * R;
+      const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
+      const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
+      const float what = (q * V) * S;           // q * V exact, one rounding by S
+      const float err = (wi - what) * rdiag[i];
+      if (t == tt) {
+        code8 |= code << (4 * k);
+        err8[k] = err;
+      }
+      const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&Ub[i][8 * t]);
+      const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&Ub[i][8 * t + 4]);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        w[kk] = fmaf(-err, u0[kk], w[kk]);
+        w[4 + kk] = fmaf(-err, u1[kk], w[4 + kk]);
       }
     }
-    // U is upper triangular: columns already done get fma(-err, 0, w)
-    w0 = fmaf(-err, Ub[i][lane], w0);
-    w1 = fmaf(-err, Ub[i][64 + lane], w1);
-  }
-  wr[lane] = e0;
-  wr[64 + lane] = e1;
-  const uint32_t n0 = (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)c0)));
-  const uint32_t n1 = (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)c1)));
-  if ((lane & 1) == 0) {
-    uint8_t *cr = codes + (int64_t)r * (cols / 2) + i1 / 2;
-    cr[lane >> 1] = (uint8_t)(c0 | (n0 << 4));
-    cr[32 + (lane >> 1)] = (uint8_t)(c1 | (n1 << 4));
+  });
+  if (live) {
+    *reinterpret_cast<f32x4 *>(wr) = f32x4{err8[0], err8[1], err8[2], err8[3]};
+    *reinterpret_cast<f32x4 *>(wr + 4) = f32x4{err8[4], err8[5], err8[6], err8[7]};
+    *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (i1 + 8 * t) / 2) = code8;
   }
 }
 
 // Trailing update W[:, i2:] -= E * U[i1:i2, i2:] with E = W[:, i1:i2] (the
 // batch's scaled errors), i2 = i1 + 128: a dense contraction with K = 128
-// on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile; E and U
-// tiles are staged in LDS (k-major), each wave owns a 32 x 32 sub-tile.
+// on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile, each wave a
+// 32 x 32 sub-tile whose 16 accumulator rows per lane are read from W at the
+// start (their HBM latency then hides behind the contraction instead of
+// stalling the epilogue).  E and U are staged through LDS in K chunks of 32:
+// E row-major with a padded stride of 33 floats, U k-major, so the stores and
+// the operand reads of each k step hit distinct banks.  The k steps run in
+// ascending order, so every output element accumulates in the same order.
+constexpr int kUpdKc = 32;
+
 __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict__ W, int64_t ld, int rows,
                                                                int cols, int i1,
                                                                const float *__restrict__ U) {
-  __shared__ float As[kGptqBatch][64];
-  __shared__ float Bs[kGptqBatch][64];
+  __shared__ float As[64][kUpdKc + 1];
+  __shared__ float Bs[kUpdKc][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i2 = i1 + kGptqBatch;
   const int r0 = blockIdx.x * 64, c0 = i2 + blockIdx.y * 64;
-  for (int e = tid; e < 64 * 32; e += kThreads) {
-    const int rr = e >> 5, k4 = e & 31;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (r0 + rr < rows) v = *reinterpret_cast<const f32x4 *>(W + (int64_t)(r0 + rr) * ld + i1 + k4 * 4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) As[k4 * 4 + k][rr] = v[k];
-  }
-  for (int e = tid; e < kGptqBatch * 16; e += kThreads) {
-    const int kk = e >> 4, j4 = e & 15;
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + kk) * cols + c0 + j4 * 4);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) Bs[kk][j4 * 4 + k] = v[k];
-  }
-  __syncthreads();
   const int wr = wave & 1, wc = wave >> 1;
   const int lr = lane & 31, lk = lane >> 5;
-  f32x16 acc = {0};
-#pragma unroll 8
-  for (int k = 0; k < kGptqBatch; k += 2) {
-    const float av = As[k + lk][wr * 32 + lr];
-    const float bv = Bs[k + lk][wc * 32 + lr];
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-  }
   // accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32
+  float cur[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-    const int col = c0 + wc * 32 + lr;
-    if (row < rows) {
-      float *p = W + (int64_t)row * ld + col;
-      *p = *p - acc[v];
+    cur[v] = row < rows ? W[(int64_t)row * ld + c0 + wc * 32 + lr] : 0.0f;
+  }
+  f32x16 acc = {0};
+  for (int kc = 0; kc < kGptqBatch; kc += kUpdKc) {
+    f32x4 a[2], b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + kThreads * j;
+      const int rr = e >> 3, k4 = e & 7;  // A chunk: 64 rows x 8 float4
+      a[j] = (r0 + rr < rows) ? *reinterpret_cast<const f32x4 *>(W + (int64_t)(r0 + rr) * ld + i1 + kc + k4 * 4)
+                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int kk = e >> 4, j4 = e & 15;  // B chunk: 32 rows x 16 float4
+      b[j] = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + kc + kk) * cols + c0 + j4 * 4);
     }
+    if (kc) __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = tid + kThreads * j;
+      const int rr = e >> 3, k4 = e & 7;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) As[rr][k4 * 4 + k] = a[j][k];
+      const int kk = e >> 4, j4 = e & 15;
+      *reinterpret_cast<f32x4 *>(&Bs[kk][j4 * 4]) = b[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kUpdKc; k += 2) {
+      const float av = As[wr * 32 + lr][k + lk];
+      const float bv = Bs[k + lk][wc * 32 + lr];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+    if (row < rows) W[(int64_t)row * ld + c0 + wc * 32 + lr] = cur[v] - acc[v];
   }
 }
 
@@ -1166,13 +1203,14 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
   const bool empty = rows == 0 || cols == 0;
   if (!global_scale || (!empty && (!w || !hinv_chol || !codes || !scales))) return FP4Q_ERR_NULL;
   if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
-  if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 63) return FP4Q_ERR_ARG;
+  if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
   if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
   if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
   if (empty) return FP4Q_OK;
-  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || (importance && !aligned(importance, 4)))
+  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
+      (importance && !aligned(importance, 4)))
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
@@ -1196,13 +1234,15 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
                        global_scale, status);
   }
   const bool wmse = importance != nullptr;
-  const int gb = ceil_div(rows, kGptqRowsPerBlock);
+  const int gb = ceil_div(rows, kGptqRowsPerWg);
   for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
     if (wmse)
-      hipLaunchKernelGGL((gptq_batch_kernel<true>), dim3(gb), dim3(1024), 0, s, w, ld, (int)rows, (int)cols, i1,
+      hipLaunchKernelGGL((gptq_batch_kernel<true>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
+                         (int)cols, i1,
                          hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
     else
-      hipLaunchKernelGGL((gptq_batch_kernel<false>), dim3(gb), dim3(1024), 0, s, w, ld, (int)rows, (int)cols, i1,
+      hipLaunchKernelGGL((gptq_batch_kernel<false>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
+                         (int)cols, i1,
                          hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
     const int rest = (int)cols - i1 - kGptqBatch;
     if (rest > 0)

@@ -80,6 +80,14 @@ __device__ __forceinline__ void load16(const T *p, float z[16]) {
 
 // ------------------------------------------------- cross-lane moves ----
 // Value held by lane (lane ^ M) of the wave, M in {1, 2, 4}.
+// Value of lane (l & ~15) + N, i.e. lane N of the caller's 16-lane DPP row
+// (row_newbcast, CDNA3 and later).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(N >= 0 && N < 16, "row lane");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
   int i = __float_as_int(v);

@@ -216,9 +216,12 @@ fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dt
  *              caller), so that H^-1 = U^T U.
  *   importance [cols] float32 per-column WMSE weights, or NULL for MSE.
  *   off_lo, off_hi  E4M3 bit-pattern window of the group-scale search
- *              (off_hi - off_lo <= 63), e.g. -3, 7 (MSE) or -8, 7 (WMSE).
+ *              (at most 16 candidates, off_hi - off_lo <= 15), e.g. -3, 7
+ *              (MSE) or -8, 7 (WMSE).
  *   flags      0 or FP4Q_GIVEN_SCALE (read S from *global_scale).
- *   codes, scales, global_scale  as for fp4q_quantize_nvfp4 (no losses).
+ *   codes, scales, global_scale  as for fp4q_quantize_nvfp4 (no losses);
+ *              codes must be 4-byte aligned.
+ * Alignment: w and hinv_chol 16-byte aligned, otherwise FP4Q_ERR_ALIGN.
  *
  * Computation: S = fp32(max|w| / 1536) from w before any update.  Columns
  * are processed in order; when column c opens a 16-column group, each row's

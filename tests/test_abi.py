@@ -155,7 +155,7 @@ def test_gptq_validation():
     assert gq(u=None) == L.ERR_NULL
     assert gq(gs=None) == L.ERR_NULL
     assert gq(ws=None) == L.ERR_WORKSPACE
-    assert gq(lo=-60, hi=7) == L.ERR_ARG
+    assert gq(lo=-9, hi=7) == L.ERR_ARG
     assert gq(flags=4) == L.ERR_ARG
     assert gq(cols=144, ld=144) == L.ERR_SHAPE
     assert gq(ld=100) == L.ERR_SHAPE
