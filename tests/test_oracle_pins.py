@@ -538,6 +538,63 @@ def test_gptq_lowers_the_proxy_loss():
     assert g < 0.9 * r
 
 
+def _gptq_explicit_inverse64(W, Hd, window):
+    """Textbook GPTQ in float64 with the explicit inverse Hessian: after
+    column c is rounded, the later columns move by -(w_c - q_c) / Hinv[c, c]
+    * Hinv[c, :] and column c is eliminated from Hinv (Hinv -= Hinv[:, c]
+    Hinv[c, :] / Hinv[c, c]).  No Cholesky factor, no lazy batches.  Group
+    scales come from the sweep on the group's current values rounded to
+    float32; the E2M1 rounding is the pinned nearest search."""
+    W = np.array(W, dtype=np.float64)
+    rows, cols = W.shape
+    Hinv = np.linalg.inv(np.asarray(Hd, dtype=np.float64))
+    S = Q.global_scale_nvfp4(W.astype(np.float32))
+    S_inv = np.float32(1.0) / S
+    recip = F.e4m3_reciprocal_table()
+    codes = np.zeros((rows, cols), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    for c in range(cols):
+        if c % 16 == 0:
+            ub = (np.abs(W[:, c:c + 16].astype(np.float32)) * S_inv).astype(np.float32)[:, None, :]
+            p = Q.sweep_blocks(ub, None, *window)[0][:, 0]
+            scales[:, c // 16] = p
+            V, R = F.E4M3_VALUES[p], recip[p]
+        w = W[:, c].astype(np.float32)
+        idx = F.e2m1_rne_index(((np.abs(w) * S_inv).astype(np.float32) * R).astype(np.float32))
+        codes[:, c] = (np.signbit(w).astype(np.uint8) << 3) | idx
+        xhat = np.where(np.signbit(w), -1.0, 1.0) * (F.e2m1_value(idx) * V).astype(np.float64) * float(S)
+        d = (W[:, c] - xhat) / Hinv[c, c]
+        W[:, c + 1:] -= d[:, None] * Hinv[c, c + 1:][None, :]
+        Hinv = Hinv - np.outer(Hinv[:, c], Hinv[c, :]) / Hinv[c, c]
+    return Q.pack_nibbles(codes), scales, S
+
+
+def test_gptq_matches_explicit_inverse_formulation():
+    """The oracle's Cholesky, lazy-batch float32 GPTQ against the textbook
+    explicit-inverse float64 elimination on two batches: the two differ only
+    by rounding, so almost every code and scale agrees and the proxy losses
+    match.  Catches a transposed factor, a wrong diagonal, a missed in-batch
+    or trailing update and a batch-boundary slip."""
+    import workloads as W_
+    rng = np.random.default_rng(29)
+    W = (rng.standard_t(4, (16, 256)) * 0.02).astype(np.float32)
+    X = W_.calibration_activations(512, 256, seed=30)
+    H, U = W_.hessian_and_factor(X, damp=0.01)
+    Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(256)
+    codes, scales, S = GQ.gptq_nvfp4(W, U)
+    c64, s64, S64 = _gptq_explicit_inverse64(W, Hd, (-3, 7))
+    assert S == S64
+    code_agree = np.mean(Q.unpack_nibbles(codes) == Q.unpack_nibbles(c64))
+    scale_agree = np.mean(scales == s64)
+    assert code_agree >= 0.995 and scale_agree >= 0.995, (code_agree, scale_agree)
+    g = GQ.proxy_loss(W, codes, scales, S, H)
+    t = GQ.proxy_loss(W, c64, s64, S64, H)
+    assert abs(g - t) <= 0.02 * t, (g, t)
+    # a plain round-to-nearest is far away, so the agreement above is not trivial
+    rtn = Q.quantize_nvfp4(W)
+    assert np.mean(Q.unpack_nibbles(rtn.codes) == Q.unpack_nibbles(c64)) < 0.9
+
+
 def test_hessian_factor_inverts():
     import workloads as W_
     X = W_.calibration_activations(300, 128, seed=28)
