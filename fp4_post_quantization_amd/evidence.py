@@ -52,6 +52,13 @@ WORKLOADS = {
     "c3b": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
+    # GPTQ: per-dispatch bytes averaged over the 31 trailing updates (rest = 3968 ... 128 columns,
+    # mean 2048: read and write W[:, rest], read the batch's errors and U[batch, rest]) and the
+    # 32 batch kernels (read and write 128 columns, write codes and scales, read U's 128 x 128 block)
+    "gptq": {"stem": "gptq_nvfp4_f32_4096x4096", "kernel": "gptq_update_kernel",
+             "title": "GPTQ with ScaleSweep group scales, fp32 4096x4096, MSE and WMSE",
+             "alg_bytes": {"gptq_update_kernel": 4096 * 2048 * 8 + 4096 * 128 * 4 + 128 * 2048 * 4,
+                           "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4}},
     "c3a": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 AbsMax window [0,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
@@ -88,7 +95,8 @@ def run(config, out_dir, steps):
 
 def _short(name):
     base = name.split("(")[0]
-    return base.replace("void fp4q::", "").replace("void ", "")
+    base = base.replace("void fp4q::", "").replace("void ", "")
+    return base[len("fp4q::"):] if base.startswith("fp4q::") else base
 
 
 def _counter_means(path):
@@ -121,12 +129,14 @@ def summarize(config, in_dir, profiles):
     write = _counter_means(os.path.join(in_dir, "write", f"{config}_counter_collection.csv"))
 
     def pick(table, kname, counter):
-        best = None
+        # dispatch-weighted mean over every grid size of the kernel, matching
+        # the trace's average duration (GPTQ's update grid shrinks per batch)
+        tot, cnt = 0.0, 0
         for (k, grid, c), (v, n) in table.items():
             if c == counter and kname in k:
-                if best is None or n > best[1]:
-                    best = (v, n)
-        return best
+                tot += v * n
+                cnt += n
+        return (tot / cnt, cnt) if cnt else None
 
     # copy calibration: the elementwise neg kernel of bench.py --copy-calib
     cf = pick(fetch, "neg_kernel", "FETCH_SIZE")
