@@ -29,6 +29,9 @@ Modules
   quant     NVFP4 ScaleSweep and MXFP4 exponent sweep, dequantization
   hadamard  block Hadamard rotation (fast transform and dense reference)
   study     float64 exhaustive-sweep tools used to pin the lemmas
+  focus     FOCUS forward quantizer with coupled-relaxation coefficients
+  gptq      GPTQ with sweep-chosen NVFP4 group scales
+  gemm      W4A4 matrix product of MXFP4 / NVFP4 operands (float64)
 
 Parity-unpinned items (no value printed on the pages fixes them): the FP32
 evaluation order of the per-candidate loss (terms summed in element order
@@ -38,7 +41,7 @@ pin everything around them (the float32 FMA emulation against exact
 rational arithmetic).
 """
 
-from . import formats, quant, hadamard, study  # noqa: F401
+from . import formats, quant, hadamard, study, focus, gptq, gemm  # noqa: F401
 from .quant import (  # noqa: F401
     quantize_nvfp4,
     quantize_mxfp4,

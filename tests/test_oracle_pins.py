@@ -602,3 +602,113 @@ def test_hessian_factor_inverts():
     Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(128)
     np.testing.assert_allclose(U.astype(np.float64).T @ U.astype(np.float64) @ Hd, np.eye(128), atol=2e-4)
     assert np.allclose(U, np.triu(U))
+
+
+# ------------------------------------------------------------------ GEMM ----
+from fractions import Fraction
+
+from oracle import gemm as GM
+
+# E2M1 magnitudes as exact rationals, typed from the format definition
+_E2M1_Q = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4), Fraction(6)]
+
+
+def _decode_mx_fraction(codes, scales):
+    """Independent exact decode: byte i of a row holds elements 2i (low
+    nibble) and 2i+1 (high nibble); bit 3 of a nibble is the sign; element k
+    is scaled by 2**(scales[k // 32] - 127)."""
+    rows = []
+    for r in range(codes.shape[0]):
+        row = []
+        for i, byte in enumerate(codes[r]):
+            for k, nib in ((2 * i, int(byte) & 0xF), (2 * i + 1, int(byte) >> 4)):
+                v = _E2M1_Q[nib & 7] * Fraction(2) ** (int(scales[r][k // 32]) - 127)
+                row.append(-v if nib & 8 else v)
+        rows.append(row)
+    return rows
+
+
+def _random_mx(rng, rows, k, lo=120, hi=134):
+    codes = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(lo, hi + 1, (rows, k // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def test_gemm_mxfp4_exact_rationals():
+    """C = A_hat B_hat^T against exact rational arithmetic with an
+    independent decode (nibble order, sign, per-32 scale, transposition)."""
+    rng = np.random.default_rng(41)
+    ac, as_ = _random_mx(rng, 3, 96)
+    bc, bs = _random_mx(rng, 4, 96)
+    A = _decode_mx_fraction(ac, as_)
+    B = _decode_mx_fraction(bc, bs)
+    C = GM.gemm_mxfp4(ac, as_, bc, bs)
+    for i in range(3):
+        for j in range(4):
+            exact = sum(a * b for a, b in zip(A[i], B[j]))
+            assert Fraction(C[i, j]) == exact
+
+
+def test_gemm_nvfp4_exact_rationals():
+    """NVFP4 operands: element = sign * q * E4M3(p) * S, E4M3 decoded from
+    torch's float8_e4m3fn cast of the pattern."""
+    rng = np.random.default_rng(42)
+    ac = rng.integers(0, 256, (2, 16)).astype(np.uint8)
+    bc = rng.integers(0, 256, (3, 16)).astype(np.uint8)
+    asc = rng.integers(1, 127, (2, 2)).astype(np.uint8)
+    bsc = rng.integers(1, 127, (3, 2)).astype(np.uint8)
+    Sa, Sb = np.float32(0.375), np.float32(2.0 ** -7)
+    e4m3 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+
+    def dec(codes, sc, S):
+        out = []
+        for r in range(codes.shape[0]):
+            row = []
+            for i, byte in enumerate(codes[r]):
+                for k, nib in ((2 * i, int(byte) & 0xF), (2 * i + 1, int(byte) >> 4)):
+                    v = _E2M1_Q[nib & 7] * Fraction(float(e4m3[sc[r][k // 16]])) * Fraction(float(S))
+                    row.append(-v if nib & 8 else v)
+            out.append(row)
+        return out
+
+    A, B = dec(ac, asc, Sa), dec(bc, bsc, Sb)
+    C = GM.gemm_nvfp4(ac, asc, Sa, bc, bsc, Sb)
+    for i in range(2):
+        for j in range(3):
+            assert Fraction(C[i, j]) == sum(a * b for a, b in zip(A[i], B[j]))
+
+
+def test_gemm_scale_and_transpose_laws():
+    """Raising every E8M0 byte of A by one doubles C exactly; swapping the
+    operands transposes C; a single non-zero per row gives the product of
+    the two decoded values."""
+    rng = np.random.default_rng(43)
+    ac, as_ = _random_mx(rng, 5, 128)
+    bc, bs = _random_mx(rng, 7, 128)
+    C = GM.gemm_mxfp4(ac, as_, bc, bs)
+    np.testing.assert_array_equal(GM.gemm_mxfp4(ac, as_ + 1, bc, bs), 2 * C)
+    np.testing.assert_array_equal(GM.gemm_mxfp4(bc, bs, ac, as_), C.T)
+    a1 = np.zeros((1, 64), np.uint8)
+    b1 = np.zeros((1, 64), np.uint8)
+    a1[0, 37] = 0x0B << 4        # element 75: code 0xB = -1.5
+    b1[0, 37] = 0x07 << 4        # element 75: code 0x7 = 6
+    C1 = GM.gemm_mxfp4(a1, np.array([[127, 127, 130, 127]], np.uint8), b1, np.array([[127, 127, 125, 127]], np.uint8))
+    assert C1[0, 0] == -1.5 * 8 * 6 * 0.25
+
+
+def test_gemm_e8m0_nan_and_quantized_product():
+    """E8M0 byte 255 is NaN; and the product of quantized operands tracks the
+    product of the originals to within the quantization error."""
+    rng = np.random.default_rng(44)
+    ac, as_ = _random_mx(rng, 2, 64)
+    bc, bs = _random_mx(rng, 2, 64)
+    as_[1, 0] = 255
+    C = GM.gemm_mxfp4(ac, as_, bc, bs)
+    assert np.all(np.isnan(C[1])) and np.all(np.isfinite(C[0]))
+    X = rng.laplace(0, 1, (16, 256)).astype(np.float32)
+    W = (rng.standard_normal((24, 256)) * 0.02).astype(np.float32)
+    qa, qb = Q.quantize_mxfp4(X, window=(0, 0)), Q.quantize_mxfp4(W, window=(0, 0))
+    Cq = GM.gemm_mxfp4(qa.codes, qa.scales, qb.codes, qb.scales)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    rel = np.linalg.norm(Cq - ref) / np.linalg.norm(ref)
+    assert 0.01 < rel < 0.25, rel
