@@ -293,3 +293,31 @@ def block_hadamard(x, n, out=None):
     L.check(lib.fp4q_block_hadamard(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(n), out.data_ptr(),
                                     _stream(x.device)))
     return out
+
+
+def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None):
+    """C = alpha * A_hat @ B_hat^T for MXFP4 operands (W4A4).
+
+    ``a`` and ``b`` are MXFP4Result (or (codes, scales) pairs) as written by
+    ``quantize_mxfp4``: A is M x K (activations), B is N x K (weights).
+    Returns C [M, N] in float32 or bfloat16."""
+    lib = L.load()
+    ac, as_ = (a.codes, a.scales) if isinstance(a, MXFP4Result) else a
+    bc, bs = (b.codes, b.scales) if isinstance(b, MXFP4Result) else b
+    m, kh = ac.shape
+    n, kh2 = bc.shape
+    if kh != kh2:
+        raise ValueError(f"K mismatch: A has {2 * kh}, B has {2 * kh2}")
+    k = 2 * kh
+    dev = ac.device
+    ac, as_, bc, bs = (t.contiguous() for t in (ac, as_, bc, bs))
+    if as_.shape != (m, k // 32) or bs.shape != (n, k // 32):
+        raise ValueError("scales must be rows x K/32")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
+    code = L.F32 if out.dtype == torch.float32 else L.BF16
+    L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,
+                                float(alpha), code, out.data_ptr(), out.stride(0), _stream(dev)))
+    return out

@@ -1,4 +1,4 @@
-"""ctypes declarations of the fp4q C ABI (include/fp4q.h)."""
+"""ctypes declarations of the fp4q C ABI (include/fp4q.h, include/fp4q_gemm.h)."""
 
 import ctypes
 import os
@@ -29,6 +29,7 @@ EXPORTS = (
     "fp4q_gptq_nvfp4",
     "fp4q_dequantize",
     "fp4q_block_hadamard",
+    "fp4q_gemm_mxfp4",
 )
 
 _P = ctypes.c_void_p
@@ -49,6 +50,7 @@ _SIGNATURES = {
     "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_dequantize": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "fp4q_block_hadamard": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P]),
+    "fp4q_gemm_mxfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _I, _P, _I64, _P]),
 }
 
 _lib = None

@@ -7,8 +7,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfp4q.so")
-SOURCES = [os.path.join(PKG, "csrc", "fp4q.hip")]
-HEADERS = [os.path.join(PKG, "csrc", "fp4q_device.h"), os.path.join(ROOT, "include", "fp4q.h")]
+SOURCES = [os.path.join(PKG, "csrc", "fp4q.hip"), os.path.join(PKG, "csrc", "fp4q_gemm.hip")]
+HEADERS = [os.path.join(PKG, "csrc", "fp4q_device.h"), os.path.join(ROOT, "include", "fp4q.h"),
+           os.path.join(ROOT, "include", "fp4q_gemm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

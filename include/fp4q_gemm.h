@@ -1,0 +1,66 @@
+/* fp4q_gemm.h -- W4A4 matrix product of microscaled FP4 operands on gfx950.
+ *
+ * Consumer of the quantizers in fp4q.h.  "Bridging the Gap Between Promise
+ * and Performance for Microscaling FP4 Quantization" (2. Metodologia;
+ * 3. QuTLASS): weights and activations are both quantized to FP4 (W4A4),
+ * and their product runs on FP4 matrix hardware.  With a block rotation,
+ * both operands carry the same block Hadamard along K, and it cancels in the
+ * product (H H^T = I; the same page, 2., micro-rotation).  Quantizing A and
+ * B with fp4q_quantize_mxfp4(..., hadamard_n = n, ...) therefore gives the
+ * product of the unrotated matrices, up to quantization error.
+ *
+ * All pointers are device pointers; stream is a hipStream_t (NULL = the
+ * default stream).  The call enqueues one kernel and returns.  It allocates
+ * nothing and keeps no state.  Argument errors are returned synchronously,
+ * before anything is enqueued.
+ */
+#ifndef FP4Q_GEMM_H
+#define FP4Q_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fp4q.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C = alpha * A_hat * B_hat^T for MXFP4 operands.
+ *
+ *   a_codes   [m x k/2] bytes, row-major, row stride k/2: the E2M1 codes of
+ *             A (activations, one row per token).  Element 2i of a row is in
+ *             the low nibble of byte i, and bit 3 of a nibble is the sign.
+ *             This is the layout fp4q_quantize_mxfp4 writes.
+ *   a_scales  [m x k/32] E8M0 bytes, row-major: element k of row r is
+ *             q * 2^(a_scales[r][k/32] - 127).  Byte 255 encodes NaN.
+ *   b_codes, b_scales  the same for B [n x k] (weights, one row per output
+ *             channel).
+ *   m, n, k   m, n >= 0; k > 0 and a multiple of 32.
+ *   alpha     float32 factor applied to the float32 accumulator.
+ *   out_dtype FP4Q_F32 or FP4Q_BF16 (round to nearest even).
+ *   c         [m x n] row-major with leading dimension ldc >= n (elements),
+ *             written in full.  It must not overlap the inputs.
+ *
+ * Arithmetic: the products of two decoded elements are exact.  They are
+ * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), one
+ * 64-element step of K at a time, each step added to a float32 accumulator
+ * in ascending K order.  The result differs from the exact product by a few
+ * float32 roundings per step.
+ *
+ * Alignment: a_codes and b_codes 16-byte aligned.  c aligned to its element
+ * size.
+ *
+ * Returns FP4Q_ERR_NULL for a missing pointer (none is needed when m or n
+ * is 0), FP4Q_ERR_SHAPE for a bad m, n, k or ldc, FP4Q_ERR_ARG for an
+ * unknown out_dtype, FP4Q_ERR_ALIGN, or FP4Q_ERR_HIP if the launch fails.
+ */
+fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                              const uint8_t *b_scales, int64_t m, int64_t n, int64_t k, float alpha,
+                              fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4Q_GEMM_H */

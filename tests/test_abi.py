@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp4q.h")
+HEADERS = [os.path.join(ROOT, "include", "fp4q.h"), os.path.join(ROOT, "include", "fp4q_gemm.h")]
 
 
 def _lib():
@@ -20,14 +20,17 @@ def _lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(fp4q_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_dequantize", "fp4q_block_hadamard"):
+    for n in ("fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_dequantize", "fp4q_block_hadamard",
+              "fp4q_gemm_mxfp4"):
         assert n in names
 
 
@@ -161,6 +164,28 @@ def test_gptq_validation():
     assert gq(ld=100) == L.ERR_SHAPE
     assert gq(ld=130) == L.ERR_ALIGN
     assert gq(u=OUT + 4) == L.ERR_ALIGN
+
+
+def test_gemm_validation():
+    L, lib = _lib()
+
+    def gm(**kw):
+        return lib.fp4q_gemm_mxfp4(kw.get("a", X), kw.get("as_", OUT), kw.get("b", X), kw.get("bs", OUT),
+                                   kw.get("m", 64), kw.get("n", 64), kw.get("k", 128), 1.0,
+                                   kw.get("dt", L.F32), kw.get("c", WS), kw.get("ldc", 64), None)
+    assert gm(a=None) == L.ERR_NULL
+    assert gm(bs=None) == L.ERR_NULL
+    assert gm(c=None) == L.ERR_NULL
+    assert gm(dt=7) == L.ERR_ARG
+    assert gm(k=48) == L.ERR_SHAPE
+    assert gm(k=0) == L.ERR_SHAPE
+    assert gm(m=-1) == L.ERR_SHAPE
+    assert gm(ldc=63) == L.ERR_SHAPE
+    assert gm(a=X + 8) == L.ERR_ALIGN
+    assert gm(c=WS + 2) == L.ERR_ALIGN
+    # empty products need no pointers and enqueue nothing
+    assert gm(m=0, a=None, as_=None, c=None) == L.OK
+    assert gm(n=0, b=None, bs=None, c=None) == L.OK
 
 
 def test_empty_shapes_need_no_device_for_dequant_and_hadamard():

@@ -1,0 +1,172 @@
+"""GPU parity of the W4A4 MXFP4 matrix product (fp4q_gemm_mxfp4) against the
+float64 oracle (oracle/gemm.py) on the same seeded operands.
+
+Bar:
+  * bit-exact whenever every partial sum is exactly representable in float32.
+    With all scales 2^0, every product is a multiple of 1/4 of magnitude
+    <= 36, so any sum of up to 4096 of them is exact in float32, whatever
+    the order.  This case checks the operand, scale and accumulator layouts
+    element by element.
+  * otherwise |C - C_exact| <= (2 ceil(K/64) + 2) * 2^-24 * sum_k |a_ik b_jk|.
+    That is one float32 rounding for each 64-element step's sum, one for
+    adding it to the accumulator, and one each for alpha and the store.
+  * bfloat16 output: additionally the bfloat16 unit roundoff of |C| (8-bit
+    significand: 2^-8 relative).
+Operands are random E2M1 bytes with scales around 2^0, the oracle's MXFP4
+quantization of Laplace activations with outlier channels and Gaussian
+weights (block Hadamard 32 on both), and, at full size in the bench's launch
+configuration, random operands compared on sampled rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm as GM
+from oracle import quant as Q
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _fq():
+    import fp4_post_quantization_amd as fq
+    return fq
+
+
+def _rand_mx(rng, rows, k, lo=120, hi=134):
+    codes = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(lo, hi + 1, (rows, k // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def _dev(*arrs):
+    return tuple(torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrs)
+
+
+def _bound(a_hat, b_hat, k):
+    return (2 * math.ceil(k / 64) + 2) * 2.0 ** -24 * GM.abs_product(a_hat, b_hat)
+
+
+def _run(ac, as_, bc, bs, out_dtype=torch.float32, alpha=1.0):
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c = _fq().gemm_mxfp4((a, asd), (b, bsd), alpha=alpha, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy().astype(np.float64)
+
+
+def _check(c, ac, as_, bc, bs, k, bf16=False, rows=None):
+    A = GM.decode_mxfp4_64(ac, as_)
+    B = GM.decode_mxfp4_64(bc, bs)
+    if rows is not None:
+        A = A[rows]
+    ref = GM.gemm(A, B)
+    tol = _bound(A, B, k)
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(c - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outside the bound; worst ratio "
+                           f"{np.max(err / np.maximum(tol, 1e-300)):.3g}")
+    return float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 32), (5, 7, 64), (33, 65, 128), (64, 64, 256), (130, 257, 160),
+                                   (257, 129, 4096), (300, 260, 1056), (96, 640, 2048)])
+def test_gemm_exact_when_partial_sums_are_representable(m, n, k):
+    rng = np.random.default_rng(1000 + m + n + k)
+    ac, _ = _rand_mx(rng, m, k)
+    bc, _ = _rand_mx(rng, n, k)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    c = _run(ac, as_, bc, bs)
+    ref = GM.gemm_mxfp4(ac, as_, bc, bs)
+    np.testing.assert_array_equal(c, ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(5, 7, 64), (33, 65, 128), (130, 257, 160), (257, 129, 4096),
+                                   (300, 260, 1056), (512, 1024, 512)])
+def test_gemm_random_scales_within_bound(m, n, k):
+    rng = np.random.default_rng(2000 + m + n + k)
+    ac, as_ = _rand_mx(rng, m, k, 100, 150)
+    bc, bs = _rand_mx(rng, n, k, 100, 150)
+    _check(_run(ac, as_, bc, bs), ac, as_, bc, bs, k)
+
+
+def test_gemm_bf16_output_and_alpha():
+    rng = np.random.default_rng(3001)
+    m, n, k = 200, 300, 512
+    ac, as_ = _rand_mx(rng, m, k)
+    bc, bs = _rand_mx(rng, n, k)
+    c = _run(ac, as_, bc, bs, out_dtype=torch.bfloat16)
+    _check(c, ac, as_, bc, bs, k, bf16=True)
+    # alpha = 0.5 only halves, exactly
+    c1 = _run(ac, as_, bc, bs)
+    c2 = _run(ac, as_, bc, bs, alpha=0.5)
+    np.testing.assert_array_equal(c2, 0.5 * c1)
+
+
+def test_gemm_leading_dimension_and_untouched_padding():
+    fq = _fq()
+    rng = np.random.default_rng(3002)
+    m, n, k = 70, 90, 256
+    ac, as_ = _rand_mx(rng, m, k)
+    bc, bs = _rand_mx(rng, n, k)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    big = torch.full((m, 128), 7.0, device=DEV)
+    fq.gemm_mxfp4((a, asd), (b, bsd), out=big[:, :n])
+    torch.cuda.synchronize()
+    out = big.cpu().numpy()
+    assert np.all(out[:, n:] == 7.0)
+    _check(out[:, :n].astype(np.float64), ac, as_, bc, bs, k)
+
+
+def test_gemm_nan_scale_byte():
+    """E8M0 byte 255 encodes NaN; every output that reads it is NaN."""
+    rng = np.random.default_rng(3003)
+    m, n, k = 40, 50, 128
+    ac, as_ = _rand_mx(rng, m, k)
+    bc, bs = _rand_mx(rng, n, k)
+    as_[3, 2] = 255
+    c = _run(ac, as_, bc, bs)
+    ref = GM.gemm_mxfp4(ac, as_, bc, bs)
+    assert np.all(np.isnan(c[3])) and np.all(np.isnan(ref[3]))
+    mask = np.ones(m, bool)
+    mask[3] = False
+    assert np.all(np.isfinite(c[mask]))
+
+
+def test_gemm_of_quantized_rotated_operands():
+    """W4A4 on the oracle's MXFP4 quantization of rotated activations and
+    weights: the GPU product matches the oracle's product of the same codes,
+    and both approximate X W^T (the rotation cancels)."""
+    x = np.random.default_rng(3004).laplace(0, 1, (192, 1024)).astype(np.float32)
+    x[:, [5, 300, 777]] *= 50
+    w = (np.random.default_rng(3005).standard_normal((320, 1024)) * 0.02).astype(np.float32)
+    qa = Q.quantize_mxfp4(x, window=(0, 0), hadamard_n=32)
+    qb = Q.quantize_mxfp4(w, window=(-1, 0), hadamard_n=32)
+    c = _run(qa.codes, qa.scales, qb.codes, qb.scales)
+    _check(c, qa.codes, qa.scales, qb.codes, qb.scales, 1024)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.linalg.norm(c - ref) / np.linalg.norm(ref) < 0.2
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_full_size_sampled_rows(out_dtype):
+    """8192 tokens x 14336 outputs x 4096 inputs (an 8B-shaped up/gate
+    projection) in the bench's launch configuration; 48 sampled rows are
+    checked against the oracle."""
+    rng = np.random.default_rng(3006)
+    m, n, k = 8192, 14336, 4096
+    ac, as_ = _rand_mx(rng, m, k)
+    bc, bs = _rand_mx(rng, n, k)
+    c_all = torch.empty((m, n), dtype=out_dtype, device=DEV)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    _fq().gemm_mxfp4((a, asd), (b, bsd), out=c_all)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(m, 42, replace=False)]))
+    c = c_all[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    _check(c, ac, as_, bc, bs, k, bf16=out_dtype == torch.bfloat16, rows=rows)
