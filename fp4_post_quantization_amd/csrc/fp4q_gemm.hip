@@ -12,13 +12,17 @@
 // (register v of lane l holds row 8 (v / 4) + 4 (l / 32) + v % 4, column
 // l % 32) and the operand layout were checked on the device.
 //
-// A workgroup of four waves (2 x 2) computes a BM x BN tile of C.  Each
-// wave computes TM x TN blocks of 32 x 32, with the accumulators in
-// registers.  K advances in stages of 128 elements: 64 bytes of codes and 4
-// scale bytes per row of A and B.  A stage is loaded from global memory
-// into registers while the matrix cores consume the previous stage from
-// LDS (double buffer, one barrier per stage).  LDS rows are padded from 64
-// to 80 bytes, so a wave's 16-byte operand reads hit distinct banks.
+// Two kernels:
+//  * mx_gemm_ring_kernel (K a multiple of 128, the main path): 8 waves
+//    compute a 256 x 256 tile, each wave 128 x 64 (4 x 2 accumulator
+//    blocks, two waves per SIMD).  K advances in stages of 128 elements.
+//    Stages travel from global memory straight into a 3-deep LDS ring
+//    (direct global-to-LDS loads), so two stages are in flight while one is
+//    consumed.  Each wave reads a k step's operands while the previous k
+//    step's MFMAs run.  The output tile leaves through LDS as 16-byte row
+//    stores.
+//  * mx_gemm_kernel (any K that is a multiple of 32): register-staged
+//    double buffer, padded LDS rows, K tail zero-filled.
 // Workgroups are renumbered so that each XCD (dispatched round-robin) gets
 // a contiguous range of tiles, taken in groups of tile rows, and tiles that
 // share A or B panels share an L2.
@@ -192,6 +196,232 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Main path (K a multiple of 128): operands move from global memory straight
+// into LDS (global_load_lds_dwordx4; lane l of a wave writes bytes
+// [16 l, 16 l + 16) after the wave's LDS base), through a ring of NS stages,
+// so NS - 1 stages of loads are in flight while the matrix cores consume
+// one.  Per stage a row contributes 64 code bytes (four 16-byte chunks) and
+// one scale dword.  Rows are stored unpadded, with chunk c of row r at
+// position c ^ sw(r), sw(r) = ((r >> 1) ^ (r >> 3)) & 3.  The 32 rows a
+// wave reads for one operand then fall on distinct banks, whether the LDS
+// serves 16 lanes from 64 banks or 8 lanes from 32 banks per cycle.  Rows
+// past M or N are loaded from row M - 1 or N - 1 (no branches); they only
+// feed outputs that are never stored.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt with only the vector-memory counter (expcnt, lgkmcnt at their maxima)
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+__device__ __forceinline__ void load_lds16(const void *g, void *l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void *g, void *l) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                   (__attribute__((address_space(3))) void *)l, 4, 0, 0);
+}
+
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(const uint8_t *__restrict__ A,
+                                                                      const uint8_t *__restrict__ As,
+                                                                      const uint8_t *__restrict__ B,
+                                                                      const uint8_t *__restrict__ Bs, int M, int N,
+                                                                      int K, float alpha, OutT *__restrict__ C,
+                                                                      int64_t ldc) {
+  constexpr int WAVES = WGM * WGN;
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+  constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * 4;
+  constexpr int STAGE = SB_OFF + BN * 4;
+  // 1 KB code loads (16 rows each) and 256 B scale loads (64 rows each) per stage, spread over the waves
+  constexpr int A_INSTR = BM / 16 / WAVES, B_INSTR = BN / 16 / WAVES;
+  constexpr int SA_INSTR = BM / 64, SB_INSTR = BN / 64;
+  // every wave issues the same number of scale loads (a wave without one loads into a spare slot),
+  // so that the per-wave count of loads per stage is a constant
+  constexpr int SQ = (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES;
+  static_assert(A_INSTR * WAVES * 16 == BM && B_INSTR * WAVES * 16 == BN, "code loads must divide evenly");
+  constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
+  constexpr int SPARE = NS * STAGE;               // 256 B target of the filler scale loads
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 256];
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t kb = K / 2;
+  const int ksc = K / 32;
+  const int nst = K / 128;
+
+  // per-lane source addresses of the loads (advanced by 64 code bytes / 4 scale bytes per stage)
+  const uint8_t *srcA[A_INSTR];
+  const uint8_t *srcB[B_INSTR];
+#pragma unroll
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = (wave * A_INSTR + i) * 16 + (lane >> 2);
+    srcA[i] = A + (int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane & 3) ^ swz(row));
+  }
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int row = (wave * B_INSTR + i) * 16 + (lane >> 2);
+    srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane & 3) ^ swz(row));
+  }
+  const uint8_t *srcS[SQ];
+  int dstS[SQ];
+#pragma unroll
+  for (int j = 0; j < SQ; ++j) {
+    const int q = wave + WAVES * j;
+    if (q < SA_INSTR) {
+      srcS[j] = As + (int64_t)min(m0 + 64 * q + lane, M - 1) * ksc;
+      dstS[j] = SA_OFF + 256 * q;
+    } else if (q < SA_INSTR + SB_INSTR) {
+      const int qb = q - SA_INSTR;
+      srcS[j] = Bs + (int64_t)min(n0 + 64 * qb + lane, N - 1) * ksc;
+      dstS[j] = SB_OFF + 256 * qb;
+    } else {
+      srcS[j] = As + (int64_t)min(m0 + lane, M - 1) * ksc;
+      dstS[j] = -1;
+    }
+  }
+
+  auto issue = [&](int st, int slot) {
+    uint8_t *base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) load_lds16(srcA[i] + st * 64, base + (wave * A_INSTR + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) load_lds16(srcB[i] + st * 64, base + A_BYTES + (wave * B_INSTR + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < SQ; ++j) load_lds4(srcS[j] + st * 4, dstS[j] >= 0 ? base + dstS[j] : smem + SPARE);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
+
+  // operands of one 64-element k step: code registers and scale bytes for TM blocks of A, TN of B
+  struct Ops {
+    i32x8 a[TM], b[TN];
+    int sa[TM], sb[TN];
+  };
+  auto read_ops = [&](int slot_, int ks, Ops &o) {
+    const uint8_t *base = smem + slot_ * STAGE;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * TM * 32 + i * 32 + l32;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
+      o.a[i] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+      o.sa[i] = base[SA_OFF + 4 * r + 2 * ks + h];  // the byte itself: no ALU work between read and MFMA
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * TN * 32 + j * 32 + l32;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
+      o.b[j] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
+      o.sb[j] = base[SB_OFF + 4 * r + 2 * ks + h];
+    }
+  };
+  auto mfmas = [&](const Ops &o) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 4, 4, 0, o.sa[i], 0,
+                                                                    o.sb[j]);
+  };
+  // A barrier between stages: the compiler-only fences keep LDS reads on their side of it;
+  // no workgroup fence, which would also drain the loads still in flight.
+  auto stage_barrier = [&]() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // Stage st sits in slot st % NS.  Stages 0 .. NS-1 are issued up front; in iteration st, once
+  // every wave has read all of stage st, stage st + NS is issued into its slot.  Every iteration
+  // issues exactly one stage of loads (past the last stage it reloads the last stage into the slot
+  // just freed, which is never read again), so the loop body has no branches and each wait is one
+  // constant: after stage st + 1, NS - 2 stages of this wave's loads may still be in flight.
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue(min(s, nst - 1), s);
+  wait_vmcnt<(NS - 1) * LOADS>();
+  stage_barrier();
+
+  Ops o0, o1;
+  read_ops(0, 0, o0);
+  int slot = 0;
+  for (int st = 0; st < nst; ++st) {
+    read_ops(slot, 1, o1);  // second k step of this stage, read while the first one's MFMAs run
+    mfmas(o0);
+    __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the barrier below
+    const int next = slot == NS - 1 ? 0 : slot + 1;
+    wait_lgkmcnt0();                    // this wave's reads of stage st are complete
+    wait_vmcnt<(NS - 2) * LOADS>();     // stage st + 1 has landed
+    stage_barrier();                    // ... for every wave, and nobody reads stage st any more
+    issue(min(st + NS, nst - 1), slot);
+    read_ops(next, 0, o0);  // first k step of the next stage, read while this stage's last MFMAs run
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(o1);
+    slot = next;
+  }
+
+  // Epilogue through LDS: each wave writes one 32-row block of its tile at a time into its own
+  // LDS area (row-major, padded), then stores it with 16-byte writes along the rows of C.
+  __syncthreads();  // every wave is done reading the ring
+  constexpr int WCOLS = TN * 32;                    // columns of a wave's tile
+  constexpr int EPAD = 16 / (int)sizeof(OutT);      // 16 bytes of padding per row
+  constexpr int EROW = WCOLS + EPAD;                // elements per staged row
+  constexpr int VEC = 16 / (int)sizeof(OutT);       // elements per 16-byte store
+  constexpr int LPR = WCOLS / VEC;                  // lanes per row
+  constexpr int RPI = 64 / LPR;                     // rows per store instruction
+  static_assert(WAVES * 32 * EROW * (int)sizeof(OutT) <= NS * STAGE, "epilogue staging must fit in the ring");
+  OutT *stage_out = reinterpret_cast<OutT *>(smem) + wave * 32 * EROW;
+  const int col0 = n0 + wn * WCOLS;
+  const bool vec_ok = ((uintptr_t)C % 16 == 0) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+        OutT o;
+        if constexpr (sizeof(OutT) == 4) o = alpha * acc[i][j][v];
+        else o = f32_to_bf16_rne(alpha * acc[i][j][v]);
+        stage_out[r * EROW + j * 32 + l32] = o;
+      }
+    const int row0 = m0 + wm * TM * 32 + i * 32;
+#pragma unroll
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int r = q * RPI + lane / LPR, c = (lane % LPR) * VEC;
+      const int row = row0 + r, col = col0 + c;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(stage_out + r * EROW + c);
+      if (row < M) {
+        OutT *dst = C + (int64_t)row * ldc + col;
+        if (vec_ok && col + VEC <= N) {
+          *reinterpret_cast<i32x4 *>(dst) = v;
+        } else {
+          const OutT *e = reinterpret_cast<const OutT *>(&v);
+#pragma unroll
+          for (int t = 0; t < VEC; ++t)
+            if (col + t < N) dst[t] = e[t];
+        }
+      }
+    }
+  }
+}
+
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 template <int TM, int TN, typename OutT>
@@ -209,11 +439,26 @@ hipError_t launch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const u
   return hipGetLastError();
 }
 
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
+                       float alpha, OutT *c, int64_t ldc, hipStream_t s) {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT>), dim3((unsigned)tiles),
+                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+  return hipGetLastError();
+}
+
 template <typename OutT>
 hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
                     float alpha, OutT *c, int64_t ldc, hipStream_t s) {
-  // 256 x 256 tiles when they fill the chip at least once, else 128 x 128
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+  if (k % 128 == 0 && aligned(as, 4) && aligned(bs, 4)) {
+    // direct-to-LDS ring: 256 x 256 tiles on 8 waves when they fill the chip, else 128 x 128 on 4
+    if (big >= 256) return launch_ring<2, 4, 4, 2, 3>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    return launch_ring<2, 2, 2, 2, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+  }
+  // any K that is a multiple of 32: register-staged double buffer
   if (big >= 256) return launch<4, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
   return launch<2, 2>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
 }
