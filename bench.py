@@ -23,7 +23,10 @@ c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
 c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
 focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8),
 study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage),
-gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight).
+gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight),
+w4a4 (an 8B-shaped decoder layer at 8192 tokens in W4A4 MXFP4: on-the-fly
+activation quantization with a 32-point Hadamard, then the seven projections
+on the scaled FP4 matrix cores against weights quantized in the same basis).
 """
 
 import argparse
@@ -301,19 +304,79 @@ def run_other(args):
                 del x
             print(f"layer {layer} done, {n / out_ms / 1e6:.1f} G el/s so far", file=sys.stderr, flush=True)
         res.update(layers=args.layers, elements=n, ms_total=out_ms, gel_s=n / out_ms / 1e6)
+    elif args.config == "w4a4":
+        res.update(run_w4a4(args))
     else:
         raise SystemExit(f"unknown config {args.config}")
     return res
 
 
+def run_w4a4(args):
+    """8B-shaped layer in W4A4 MXFP4 at 8192 tokens: per layer step, the four
+    activation inputs are quantized (AbsMax, fused 32-point Hadamard) and the
+    seven projections run as MXFP4 GEMMs (bf16 out) against weights quantized
+    offline in the same rotated basis (window [-1, 0])."""
+    import torch
+    import fp4_post_quantization_amd as fq
+    import workloads as W
+    dev = "cuda:0"
+    acts = {n: W.w4a4_activation(n, dev) for n in W.W4A4_INPUTS}
+    wq, flops, err = {}, {}, {}
+    for name in W.LAYER_8B:
+        w = W.c4_matrix(name).to(dev)
+        wq[name] = fq.quantize_mxfp4(w, window=(-1, 0), hadamard_n=32, with_loss=False, check=True)
+        flops[name] = 2 * W.W4A4_TOKENS * w.shape[0] * w.shape[1]
+        # accuracy of the W4A4 product on 256 sampled tokens against the unquantized product
+        xs = acts[W.W4A4_READS[name]][:256]
+        xq = fq.quantize_mxfp4(xs, window=(0, 0), hadamard_n=32, with_loss=False)
+        c = fq.gemm_mxfp4(xq, wq[name], out_dtype=torch.float32)
+        ref = xs.float() @ w.float().t()
+        err[name] = float((c - ref).norm() / ref.norm())
+        del w
+    aq = {n: fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, with_loss=False, check=True)
+          for n, x in acts.items()}
+    outs = {n: torch.empty((W.W4A4_TOKENS, wq[n].codes.shape[0]), dtype=torch.bfloat16, device=dev)
+            for n in W.LAYER_8B}
+
+    def quant_step():
+        for n, x in acts.items():
+            fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, out=aq[n], with_loss=False)
+
+    def gemm_step():
+        for n in W.LAYER_8B:
+            fq.gemm_mxfp4(aq[W.W4A4_READS[n]], wq[n], out=outs[n])
+
+    def layer(i):
+        quant_step()
+        gemm_step()
+
+    prewarm(layer, seconds=0.5)
+    for i in range(args.warmup):
+        layer(i)
+    ms_layer = _events_time(layer, args.steps)
+    ms_quant = _events_time(lambda i: quant_step(), args.steps)
+    ms_gemm = _events_time(lambda i: gemm_step(), args.steps)
+    per = {}
+    for n in W.LAYER_8B:
+        ms_n = _events_time(lambda i, n=n: fq.gemm_mxfp4(aq[W.W4A4_READS[n]], wq[n], out=outs[n]), args.steps)
+        per[n] = {"shape_mnk": [W.W4A4_TOKENS, *W.LAYER_8B[n]], "ms": ms_n,
+                  "tflops": flops[n] / ms_n / 1e9, "rel_err_vs_unquantized": err[n]}
+    total_flops = sum(flops.values())
+    return {"tokens": W.W4A4_TOKENS, "ms_layer": ms_layer, "ms_activation_quant": ms_quant, "ms_gemms": ms_gemm,
+            "gemm_tflops": total_flops / ms_gemm / 1e9, "layer_tflops": total_flops / ms_layer / 1e9,
+            "fp4_dense_peak_tflops": 10100.0, "per_matrix": per}
+
+
 def copy_calibration(nbytes=256 * 2**20, reps=3):
     """A kernel of known traffic (reads and writes nbytes once each) whose HBM
-    counters calibrate FETCH_SIZE / WRITE_SIZE of the quantizer's kernels."""
+    counters calibrate FETCH_SIZE / WRITE_SIZE of the quantizer's kernels.  An
+    int32 bitwise NOT: an elementwise kernel no workload runs itself, so its
+    counters are found by name."""
     import torch
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(reps):
-        torch.neg(src, out=dst)
+        torch.bitwise_not(src, out=dst)
     torch.cuda.synchronize()
 
 

@@ -33,6 +33,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "fp4q.hip"), os.path.join(PKG, "csrc", "fp4q_device.h"),
                   os.path.join(ROOT, "include", "fp4q.h")]
+GEMM_SOURCES = [os.path.join(PKG, "csrc", "fp4q_gemm.hip"), os.path.join(ROOT, "include", "fp4q_gemm.h")]
 
 VALU_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
 PASSES = {
@@ -42,6 +43,20 @@ PASSES = {
     "write": ["--pmc", "WRITE_SIZE"],
 }
 COPY_BYTES = 256 * 2**20  # bench.py --copy-calib: one read and one write of 256 MiB
+
+# (N, K) of the projections of an 8B-shaped layer by GEMM kernel instantiation, and the widths of
+# its four activation inputs
+_W4A4_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 3, unsigned short>"
+_W4A4_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 4, unsigned short>"
+_W4A4_NK_BIG = [(4096, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
+_W4A4_NK_SMALL = [(1024, 4096), (1024, 4096)]
+_W4A4_IN = [4096, 4096, 4096, 14336]
+
+
+def _gemm_mean(nks, what, m=8192):
+    vals = [2 * m * n * k if what == "flops" else m * k * (0.5 + 1 / 32) + n * k * (0.5 + 1 / 32) + m * n * 2
+            for n, k in nks]
+    return sum(vals) / len(vals)
 
 # dominant kernel and algorithmic bytes per dispatch of each workload
 WORKLOADS = {
@@ -59,15 +74,29 @@ WORKLOADS = {
              "title": "GPTQ with ScaleSweep group scales, fp32 4096x4096, MSE and WMSE",
              "alg_bytes": {"gptq_update_kernel": 4096 * 2048 * 8 + 4096 * 128 * 4 + 128 * 2048 * 4,
                            "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4}},
+    # W4A4 8B layer at 8192 tokens.  Per GEMM dispatch: A (codes + scales) + B (codes + scales)
+    # + C (bf16), flops 2 M N K, averaged over the projections each kernel instantiation serves
+    # (256 x 256 tiles: q, o, gate, up, down; 128 x 128 tiles: k, v).  The activation quantizer
+    # reads bf16 and writes codes, scales and offsets (mean over the four inputs).
+    "w4a4": {"stem": "mxfp4_w4a4_gemm_8b_layer_8192tok", "kernel": _W4A4_BIG,
+             "title": "W4A4 MXFP4 layer (8B shapes, 8192 tokens): scaled-FP4 MFMA GEMMs + activation quantization",
+             "alg_bytes": {_W4A4_BIG: _gemm_mean(_W4A4_NK_BIG, "bytes"), _W4A4_SMALL: _gemm_mean(_W4A4_NK_SMALL, "bytes"),
+                           "mxfp4_sweep_kernel": sum(8192 * k * (2 + 0.5 + 2 / 32) for k in _W4A4_IN)
+                           / len(_W4A4_IN)},
+             "alg_flops": {_W4A4_BIG: _gemm_mean(_W4A4_NK_BIG, "flops"),
+                           _W4A4_SMALL: _gemm_mean(_W4A4_NK_SMALL, "flops")},
+             "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
+             "peak_tflops": 10100.0, "sources": GEMM_SOURCES},
     "c3a": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 AbsMax window [0,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
 }
 
 
-def source_hash():
+def source_hash(config=None):
+    """sha256 over the sources of the workload's dominant kernel."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in WORKLOADS.get(config, {}).get("sources", KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -78,25 +107,38 @@ def bench_cmd(config, steps):
             "--warmup", "1", "--no-cpu-baseline", "--copy-calib"]
 
 
+def passes(config):
+    w = WORKLOADS.get(config, {})
+    p = dict(PASSES)
+    p["valu"] = ["--pmc", *VALU_COUNTERS, *w.get("extra_counters", [])]
+    return p
+
+
 def rocprof_cmd(name, out_dir, config, steps):
-    return ["rocprofv3", *PASSES[name], "-d", os.path.join(out_dir, name), "-o", config,
+    return ["rocprofv3", *passes(config)[name], "-d", os.path.join(out_dir, name), "-o", config,
             "--output-format", "csv", "--", *bench_cmd(config, steps)]
 
 
 def run(config, out_dir, steps):
     os.makedirs(out_dir, exist_ok=True)
     env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
-    for name in PASSES:
+    for name in passes(config):
         cmd = rocprof_cmd(name, out_dir, config, steps)
         print("==", " ".join(cmd), flush=True)
         # each pass is bounded; a counter request the hardware cannot serve hangs
         subprocess.run(["timeout", "-s", "KILL", "240", *cmd], check=True, env=env)
 
 
+def _ours(name):
+    return "fp4q::" in name or "fp4q_gemm::" in name
+
+
 def _short(name):
-    base = name.split("(")[0]
-    base = base.replace("void fp4q::", "").replace("void ", "")
-    return base[len("fp4q::"):] if base.startswith("fp4q::") else base
+    base = name.split("(")[0].replace("void ", "")
+    for ns in ("fp4q::", "fp4q_gemm::"):
+        if base.startswith(ns):
+            base = base[len(ns):]
+    return base
 
 
 def _counter_means(path):
@@ -138,16 +180,26 @@ def summarize(config, in_dir, profiles):
                 cnt += n
         return (tot / cnt, cnt) if cnt else None
 
-    # copy calibration: the elementwise neg kernel of bench.py --copy-calib
-    cf = pick(fetch, "neg_kernel", "FETCH_SIZE")
-    cw = pick(write, "neg_kernel", "WRITE_SIZE")
+    # copy calibration: the int32 bitwise-NOT kernel of bench.py --copy-calib (runs recorded
+    # before it existed used a float32 negation: the neg dispatch size seen most often)
+    def pick_calib(table, counter):
+        best = None
+        for (k, grid, c), (v, n) in table.items():
+            if c == counter and "bitwise_not" in k:
+                return (v, n)
+            if c == counter and "neg_kernel" in k and (best is None or n > best[1]):
+                best = (v, n)
+        return best
+
+    cf = pick_calib(fetch, "FETCH_SIZE")
+    cw = pick_calib(write, "WRITE_SIZE")
     f_factor = COPY_BYTES / (cf[0] * 1024) if cf else None
     w_factor = COPY_BYTES / (cw[0] * 1024) if cw else None
 
     lines = [f"# {w['title']}", "",
              f"Device: {agent.get('Name', '?')}, {cus} CUs, {simds} SIMDs, {xcc} XCDs, "
              f"max engine clock {clk_mhz:.0f} MHz.", "", "Commands (each a pass of its own):", ""]
-    for name in PASSES:
+    for name in passes(config):
         cmd = rocprof_cmd(name, in_dir, config, 20)
         cmd = ["python" if c == sys.executable else ("bench.py" if c.endswith("bench.py") else c) for c in cmd]
         lines.append("    " + " ".join(cmd))
@@ -161,7 +213,7 @@ def summarize(config, in_dir, profiles):
     durations = {}
     for r in stats:
         name = r["Name"]
-        if "fp4q::" not in name and "neg_kernel" not in name:
+        if not _ours(name) and "neg_kernel" not in name and "bitwise_not" not in name:
             continue
         avg = float(r["AverageNs"]) / 1000
         durations[name] = avg
@@ -175,9 +227,9 @@ def summarize(config, in_dir, profiles):
               "(calibrated) | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
     record = None
     for name, avg_us in durations.items():
-        if "fp4q::" not in name:
+        if not _ours(name):
             continue
-        key = _short(name).split("<")[0]
+        key = _short(name) if _short(name) in w["alg_bytes"] else _short(name).split("<")[0]
         insts = pick(valu, name, "SQ_INSTS_VALU")
         waves = pick(valu, name, "SQ_WAVES")
         active = pick(valu, name, "SQ_ACTIVE_INST_VALU")
@@ -198,7 +250,31 @@ def summarize(config, in_dir, profiles):
             record = {"workload": config, "kernel": _short(name), "avg_us": avg_us, "fetch_kib": fk[0],
                       "write_kib": wk[0], "fetch_factor": f_factor, "write_factor": w_factor,
                       "traffic_bytes": hbm, "alg_bytes": alg, "valu_issue": issue, "valu_busy_pct": busy,
-                      "source_sha256": source_hash()}
+                      "source_sha256": source_hash(config)}
+    if w.get("alg_flops"):
+        lines += ["", "## Matrix cores", "",
+                  f"Achieved = mean algorithmic flops per dispatch / average duration; peak = the published dense "
+                  f"FP4 figure ({w['peak_tflops']:.0f} TFLOP/s at 2.4 GHz).  MFMA busy share = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCDs); cycles per MFMA = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA.", "",
+                  "| kernel | flops per dispatch | achieved TFLOP/s | of peak | MFMA insts | cycles per MFMA | "
+                  "MFMA busy share | GPU clock (GRBM) |", "|---|---|---|---|---|---|---|---|"]
+        for name, avg_us in durations.items():
+            fl = w["alg_flops"].get(_short(name))
+            if fl is None:
+                continue
+            mi = pick(valu, name, "SQ_INSTS_MFMA")
+            mb = pick(valu, name, "SQ_VALU_MFMA_BUSY_CYCLES")
+            grbm = pick(valu, name, "GRBM_GUI_ACTIVE")
+            tf = fl / (avg_us * 1e-6) / 1e12
+            share = mb[0] / (simds * grbm[0] / xcc) if (mb and grbm) else None
+            cpm = mb[0] / mi[0] if (mb and mi and mi[0]) else None
+            lines.append(f"| `{_short(name)}` | {fl:.4g} | {tf:.0f} | {100 * tf / w['peak_tflops']:.1f}% | "
+                         f"{'' if mi is None else f'{mi[0]:.4g}'} | {'' if cpm is None else f'{cpm:.1f}'} | "
+                         f"{'' if share is None else f'{100 * share:.1f}%'} | counter-run cycles "
+                         f"{'' if grbm is None else f'{grbm[0] / xcc:.4g}'} per XCD |")
+            if record is not None and w["kernel"] in name:
+                record.update(alg_flops=fl, achieved_tflops=tf, peak_tflops=w["peak_tflops"])
     lines += ["", "## Copy calibration", "",
               f"Plain elementwise kernel reading and writing {COPY_BYTES // 2**20} MiB once: FETCH_SIZE "
               f"{cf[0] if cf else float('nan'):.1f} KiB (factor {f_factor if f_factor else float('nan'):.4f}), "

@@ -142,6 +142,30 @@ def c5_matrix(layer, name, device):
     return w.to(torch.bfloat16)
 
 
+# ----------------------------------------------------- W4A4 layer ----
+W4A4_TOKENS = 8192
+# activation inputs of an 8B-shaped decoder layer and the matrices that read them
+W4A4_INPUTS = {"attn_in": 4096, "attn_out": 4096, "mlp_in": 4096, "mlp_mid": 14336}
+W4A4_READS = {"q": "attn_in", "k": "attn_in", "v": "attn_in", "o": "attn_out",
+              "gate": "mlp_in", "up": "mlp_in", "down": "mlp_mid"}
+
+
+def w4a4_activation(name, device, tokens=W4A4_TOKENS):
+    """Activations of one layer input, drawn on ``device``: Laplace(0, 1) as
+    the difference of two Exp(1) draws, -log(1 - r) with r a seeded uniform
+    in [0, 1) (always finite), 8 seeded outlier channels times 50 (the c3
+    recipe at the input's width), bf16."""
+    cols = W4A4_INPUTS[name]
+    g = torch.Generator(device=device)
+    g.manual_seed(700 + list(W4A4_INPUTS).index(name))
+    r1 = torch.rand((tokens, cols), generator=g, device=device, dtype=torch.float32)
+    r2 = torch.rand((tokens, cols), generator=g, device=device, dtype=torch.float32)
+    x = torch.log1p(-r2) - torch.log1p(-r1)
+    ch = torch.randperm(cols, generator=g, device=device)[:8]
+    x[:, ch] *= 50.0
+    return x.to(torch.bfloat16)
+
+
 # ------------------------------------------------------- small cases ----
 def random_matrix(rows, cols, seed, dist="normal", scale=0.02, dtype=torch.float32):
     """Generic seeded test matrix (normal, t4, laplace)."""
