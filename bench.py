@@ -26,7 +26,8 @@ study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage),
 gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight),
 w4a4 (an 8B-shaped decoder layer at 8192 tokens in W4A4 MXFP4: on-the-fly
 activation quantization with a 32-point Hadamard, then the seven projections
-on the scaled FP4 matrix cores against weights quantized in the same basis).
+on the scaled FP4 matrix cores against weights quantized in the same basis),
+w4a4nv (the same layer with NVFP4 operands on the bf16 matrix cores).
 """
 
 import argparse
@@ -306,45 +307,69 @@ def run_other(args):
         res.update(layers=args.layers, elements=n, ms_total=out_ms, gel_s=n / out_ms / 1e6)
     elif args.config == "w4a4":
         res.update(run_w4a4(args))
+    elif args.config == "w4a4nv":
+        res.update(run_w4a4(args, fmt="nvfp4"))
     else:
         raise SystemExit(f"unknown config {args.config}")
     return res
 
 
-def run_w4a4(args):
-    """8B-shaped layer in W4A4 MXFP4 at 8192 tokens: per layer step, the four
-    activation inputs are quantized (AbsMax, fused 32-point Hadamard) and the
-    seven projections run as MXFP4 GEMMs (bf16 out) against weights quantized
-    offline in the same rotated basis (window [-1, 0])."""
+def run_w4a4(args, fmt="mxfp4"):
+    """8B-shaped layer in W4A4 at 8192 tokens: per layer step, the four
+    activation inputs are quantized and the seven projections run as FP4
+    GEMMs (bf16 out) against weights quantized offline.  MXFP4: AbsMax
+    activations with a fused 32-point Hadamard, weights in the same rotated
+    basis with window [-1, 0], scaled-FP4 matrix cores.  NVFP4: AbsMax
+    activations, weights by the MSE sweep [-3, +7], operands decoded to bf16
+    for the bf16 matrix cores."""
     import torch
     import fp4_post_quantization_amd as fq
     import workloads as W
     dev = "cuda:0"
+    mx = fmt == "mxfp4"
     acts = {n: W.w4a4_activation(n, dev) for n in W.W4A4_INPUTS}
+
+    def quant_act(x, out=None, check=False):
+        if mx:
+            return fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, out=out, with_loss=False, check=check)
+        return fq.quantize_nvfp4(x, window=(0, 0), out=out, with_loss=False, check=check)
+
+    ws_nv = None
+    if not mx:
+        need = max(fq._lib.load().fp4q_gemm_nvfp4_workspace_bytes(W.W4A4_TOKENS, n, k)
+                   for n, k in W.LAYER_8B.values())
+        ws_nv = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def gemm(a, b, out=None, out_dtype=torch.bfloat16):
+        if mx:
+            return fq.gemm_mxfp4(a, b, out=out, out_dtype=out_dtype)
+        return fq.gemm_nvfp4(a, b, out=out, out_dtype=out_dtype, workspace_buf=ws_nv)
+
     wq, flops, err = {}, {}, {}
     for name in W.LAYER_8B:
         w = W.c4_matrix(name).to(dev)
-        wq[name] = fq.quantize_mxfp4(w, window=(-1, 0), hadamard_n=32, with_loss=False, check=True)
+        if mx:
+            wq[name] = fq.quantize_mxfp4(w, window=(-1, 0), hadamard_n=32, with_loss=False, check=True)
+        else:
+            wq[name] = fq.quantize_nvfp4(w, window=(-3, 7), with_loss=False, check=True)
         flops[name] = 2 * W.W4A4_TOKENS * w.shape[0] * w.shape[1]
         # accuracy of the W4A4 product on 256 sampled tokens against the unquantized product
         xs = acts[W.W4A4_READS[name]][:256]
-        xq = fq.quantize_mxfp4(xs, window=(0, 0), hadamard_n=32, with_loss=False)
-        c = fq.gemm_mxfp4(xq, wq[name], out_dtype=torch.float32)
+        c = gemm(quant_act(xs), wq[name], out_dtype=torch.float32)
         ref = xs.float() @ w.float().t()
         err[name] = float((c - ref).norm() / ref.norm())
         del w
-    aq = {n: fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, with_loss=False, check=True)
-          for n, x in acts.items()}
+    aq = {n: quant_act(x, check=True) for n, x in acts.items()}
     outs = {n: torch.empty((W.W4A4_TOKENS, wq[n].codes.shape[0]), dtype=torch.bfloat16, device=dev)
             for n in W.LAYER_8B}
 
     def quant_step():
         for n, x in acts.items():
-            fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, out=aq[n], with_loss=False)
+            quant_act(x, out=aq[n])
 
     def gemm_step():
         for n in W.LAYER_8B:
-            fq.gemm_mxfp4(aq[W.W4A4_READS[n]], wq[n], out=outs[n])
+            gemm(aq[W.W4A4_READS[n]], wq[n], out=outs[n])
 
     def layer(i):
         quant_step()
@@ -358,13 +383,13 @@ def run_w4a4(args):
     ms_gemm = _events_time(lambda i: gemm_step(), args.steps)
     per = {}
     for n in W.LAYER_8B:
-        ms_n = _events_time(lambda i, n=n: fq.gemm_mxfp4(aq[W.W4A4_READS[n]], wq[n], out=outs[n]), args.steps)
+        ms_n = _events_time(lambda i, n=n: gemm(aq[W.W4A4_READS[n]], wq[n], out=outs[n]), args.steps)
         per[n] = {"shape_mnk": [W.W4A4_TOKENS, *W.LAYER_8B[n]], "ms": ms_n,
                   "tflops": flops[n] / ms_n / 1e9, "rel_err_vs_unquantized": err[n]}
     total_flops = sum(flops.values())
-    return {"tokens": W.W4A4_TOKENS, "ms_layer": ms_layer, "ms_activation_quant": ms_quant, "ms_gemms": ms_gemm,
+    return {"format": fmt, "tokens": W.W4A4_TOKENS, "ms_layer": ms_layer, "ms_activation_quant": ms_quant, "ms_gemms": ms_gemm,
             "gemm_tflops": total_flops / ms_gemm / 1e9, "layer_tflops": total_flops / ms_layer / 1e9,
-            "fp4_dense_peak_tflops": 10100.0, "per_matrix": per}
+            "matrix_core_dense_peak_tflops": 10100.0 if mx else 2500.0, "per_matrix": per}
 
 
 def copy_calibration(nbytes=256 * 2**20, reps=3):

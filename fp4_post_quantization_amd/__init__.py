@@ -321,3 +321,36 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None):
     L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,
                                 float(alpha), code, out.data_ptr(), out.stride(0), _stream(dev)))
     return out
+
+
+def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
+    """C = fp32(S_a S_b) * A_hat @ B_hat^T for NVFP4 operands (NVFP4Result
+    or (codes, scales, global_scale) triples as written by quantize_nvfp4):
+    A is M x K, B is N x K.  The operands are decoded to bfloat16 (exact) in
+    a workspace, allocated here unless ``workspace_buf`` is given."""
+    lib = L.load()
+    ac, as_, ag = (a.codes, a.scales, a.global_scale) if isinstance(a, NVFP4Result) else a
+    bc, bs, bg = (b.codes, b.scales, b.global_scale) if isinstance(b, NVFP4Result) else b
+    m, kh = ac.shape
+    n, kh2 = bc.shape
+    if kh != kh2:
+        raise ValueError(f"K mismatch: A has {2 * kh}, B has {2 * kh2}")
+    k = 2 * kh
+    dev = ac.device
+    ac, as_, bc, bs = (t.contiguous() for t in (ac, as_, bc, bs))
+    ag = torch.as_tensor(ag, dtype=torch.float32, device=dev).reshape(1)
+    bg = torch.as_tensor(bg, dtype=torch.float32, device=dev).reshape(1)
+    if as_.shape != (m, k // 16) or bs.shape != (n, k // 16):
+        raise ValueError("scales must be rows x K/16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
+        raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
+    need = lib.fp4q_gemm_nvfp4_workspace_bytes(m, n, k)
+    if workspace_buf is None or workspace_buf.numel() < need:
+        workspace_buf = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    code = L.F32 if out.dtype == torch.float32 else L.BF16
+    L.check(lib.fp4q_gemm_nvfp4(ac.data_ptr(), as_.data_ptr(), ag.data_ptr(), bc.data_ptr(), bs.data_ptr(),
+                                bg.data_ptr(), m, n, k, code, out.data_ptr(), out.stride(0),
+                                workspace_buf.data_ptr(), workspace_buf.numel(), _stream(dev)))
+    return out

@@ -37,6 +37,8 @@ namespace fp4q_gemm {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kKc = 128;     // K elements per stage
@@ -229,28 +231,31 @@ __device__ __forceinline__ void load_lds4(const void *g, void *l) {
                                    (__attribute__((address_space(3))) void *)l, 4, 0, 0);
 }
 
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
-__global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(const uint8_t *__restrict__ A,
-                                                                      const uint8_t *__restrict__ As,
-                                                                      const uint8_t *__restrict__ B,
-                                                                      const uint8_t *__restrict__ Bs, int M, int N,
-                                                                      int K, float alpha, OutT *__restrict__ C,
-                                                                      int64_t ldc) {
+// MX = true: MXFP4 operands (a stage is 128 K elements = 64 code bytes + 4 E8M0 bytes per row;
+// v_mfma_scale_f32_32x32x64_f8f6f4).  MX = false: bf16 operands (a stage is 32 K elements = 64 bytes
+// per row; v_mfma_f32_32x32x16_bf16, lane l holding row l % 32 and K elements 8 (l / 32) .. +8, checked
+// on the device), scaled at the end by fp32(*ga * *gb).  Rows are kb bytes apart; nst stages.
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true>
+__global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, int ksc, const float *__restrict__ ga,
+    const float *__restrict__ gb, float alpha, OutT *__restrict__ C, int64_t ldc) {
   constexpr int WAVES = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
   constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * 4;
-  constexpr int STAGE = SB_OFF + BN * 4;
+  constexpr int STAGE = MX ? SB_OFF + BN * 4 : A_BYTES + B_BYTES;
   // 1 KB code loads (16 rows each) and 256 B scale loads (64 rows each) per stage, spread over the waves
   constexpr int A_INSTR = BM / 16 / WAVES, B_INSTR = BN / 16 / WAVES;
   constexpr int SA_INSTR = BM / 64, SB_INSTR = BN / 64;
   // every wave issues the same number of scale loads (a wave without one loads into a spare slot),
   // so that the per-wave count of loads per stage is a constant
-  constexpr int SQ = (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES;
+  constexpr int SQ = MX ? (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES : 0;
   static_assert(A_INSTR * WAVES * 16 == BM && B_INSTR * WAVES * 16 == BN, "code loads must divide evenly");
   constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
   constexpr int SPARE = NS * STAGE;               // 256 B target of the filler scale loads
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 256];
+  if constexpr (!MX) alpha = (*ga) * (*gb);
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -259,9 +264,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(const uint
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
   const int l32 = lane & 31, h = lane >> 5;
-  const int64_t kb = K / 2;
-  const int ksc = K / 32;
-  const int nst = K / 128;
 
   // per-lane source addresses of the loads (advanced by 64 code bytes / 4 scale bytes per stage)
   const uint8_t *srcA[A_INSTR];
@@ -276,8 +278,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(const uint
     const int row = (wave * B_INSTR + i) * 16 + (lane >> 2);
     srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane & 3) ^ swz(row));
   }
-  const uint8_t *srcS[SQ];
-  int dstS[SQ];
+  const uint8_t *srcS[SQ > 0 ? SQ : 1];
+  int dstS[SQ > 0 ? SQ : 1];
 #pragma unroll
   for (int j = 0; j < SQ; ++j) {
     const int q = wave + WAVES * j;
@@ -322,23 +324,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(const uint
       const int r = wm * TM * 32 + i * 32 + l32;
       const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
       o.a[i] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      o.sa[i] = base[SA_OFF + 4 * r + 2 * ks + h];  // the byte itself: no ALU work between read and MFMA
+      if constexpr (MX) o.sa[i] = base[SA_OFF + 4 * r + 2 * ks + h];  // the byte itself: no ALU work
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * TN * 32 + j * 32 + l32;
       const i32x4 v = *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
       o.b[j] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      o.sb[j] = base[SB_OFF + 4 * r + 2 * ks + h];
+      if constexpr (MX) o.sb[j] = base[SB_OFF + 4 * r + 2 * ks + h];
     }
   };
   auto mfmas = [&](const Ops &o) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 4, 4, 0, o.sa[i], 0,
-                                                                    o.sb[j]);
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (MX) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 4, 4, 0, o.sa[i],
+                                                                      0, o.sb[j]);
+        } else {
+          const i32x4 av = {o.a[i][0], o.a[i][1], o.a[i][2], o.a[i][3]};
+          const i32x4 bv = {o.b[j][0], o.b[j][1], o.b[j][2], o.b[j][3]};
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
+                                                              __builtin_bit_cast(bf16x8, bv), acc[i][j], 0, 0, 0);
+        }
+      }
   };
   // A barrier between stages: the compiler-only fences keep LDS reads on their side of it;
   // no workgroup fence, which would also drain the loads still in flight.
@@ -444,8 +454,21 @@ hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, co
                        float alpha, OutT *c, int64_t ldc, hipStream_t s) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT>), dim3((unsigned)tiles),
-                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true>), dim3((unsigned)tiles),
+                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / 128, (int64_t)(k / 2), k / 32,
+                     (const float *)nullptr, (const float *)nullptr, alpha, c, ldc);
+  return hipGetLastError();
+}
+
+// bf16 operands (rows of kp elements, kp a multiple of 32) scaled by fp32(*ga * *gb)
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, int kp, const float *ga,
+                            const float *gb, OutT *c, int64_t ldc, hipStream_t s) {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false>), dim3((unsigned)tiles),
+                     dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr, (const uint8_t *)b,
+                     (const uint8_t *)nullptr, m, n, kp / 32, (int64_t)kp * 2, 0, ga, gb, 1.0f, c, ldc);
   return hipGetLastError();
 }
 
@@ -462,6 +485,69 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
   if (big >= 256) return launch<4, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
   return launch<2, 2>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
 }
+
+// ---------------------------------------------------------------------------
+// NVFP4 operands.  The scaled matrix core takes E8M0 scales per 32 elements only, and folding an
+// E4M3 block scale into the elements would need q * V at up to 6 significant bits, more than any
+// 8-bit float holds.  The exact route: decode each element to q * V (the block scale, without the
+// tensor's global scale), which bfloat16 represents exactly (E2M1 has 2 significant bits, E4M3 4,
+// and |q * V| lies in [2^-10, 2688]); multiply on the bf16 matrix cores (bf16 products are exact
+// in the float32 accumulator); scale the result by fp32(S_a * S_b).
+
+// E4M3 byte -> float (sign bit 7; exponent 15 with mantissa 7 is NaN; exponent 0 is subnormal)
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = (e == 0) ? (float)m * 0x1p-9f : (float)(8u + m) * __builtin_ldexpf(1.0f, (int)e - 10);
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return (b & 0x80u) ? -v : v;
+}
+
+// One lane per 16-element block: 8 code bytes + 1 scale byte -> 16 bfloat16 values (two 16-byte
+// stores).  Blocks past K (up to kp, a multiple of 32) are written as zeros.
+__global__ __launch_bounds__(256) void nvfp4_to_bf16_kernel(const uint8_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales, int rows, int k,
+                                                            int kp, uint16_t *__restrict__ out) {
+  const int bpr = kp / 16;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * bpr) return;
+  const int r = (int)(t / bpr), blk = (int)(t % bpr);
+  uint32_t w[8];
+  if (blk * 16 < k) {
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (k / 2) + blk * 8);
+    const float V = e4m3_decode(scales[(int64_t)r * (k / 16) + blk]);
+    // decode the 16 codes in element order: element 2i is the low nibble of byte i
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = i < 4 ? c.x : c.y;
+      float2v q;
+      switch (i & 3) {
+        case 0: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+        case 1: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+        case 2: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+        default: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+      }
+      // q * V is exact in float32 and in bfloat16, so dropping the low 16 bits is exact
+      const uint32_t lo = __float_as_uint(q[0] * V) >> 16, hi = __float_as_uint(q[1] * V) >> 16;
+      w[i] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0;
+  }
+  uint4 *dst = reinterpret_cast<uint4 *>(out + (int64_t)r * kp + blk * 16);
+  dst[0] = uint4{w[0], w[1], w[2], w[3]};
+  dst[1] = uint4{w[4], w[5], w[6], w[7]};
+}
+
+template <typename OutT>
+hipError_t dispatch_nv(const uint16_t *a, const uint16_t *b, int m, int n, int kp, const float *ga, const float *gb,
+                       OutT *c, int64_t ldc, hipStream_t s) {
+  const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+  if (big >= 256) return launch_ring_bf16<2, 4, 4, 2, 3>(a, b, m, n, kp, ga, gb, c, ldc, s);
+  return launch_ring_bf16<2, 2, 2, 2, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
+}
+
+int64_t padded_k(int64_t k) { return (k + 31) / 32 * 32; }
 
 }  // namespace fp4q_gemm
 
@@ -485,5 +571,45 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
   else
     e = dispatch<uint16_t>(a_codes, a_scales, b_codes, b_scales, (int)m, (int)n, (int)k, alpha, (uint16_t *)c, ldc,
                            s);
+  return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
+}
+
+extern "C" size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k <= 0) return 0;
+  return (size_t)((m + n) * fp4q_gemm::padded_k(k) * 2);
+}
+
+extern "C" fp4q_status_t fp4q_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_global,
+                                         const uint8_t *b_codes, const uint8_t *b_scales, const float *b_global,
+                                         int64_t m, int64_t n, int64_t k, fp4q_dtype_t out_dtype, void *c,
+                                         int64_t ldc, void *workspace, size_t workspace_bytes, void *stream) {
+  using namespace fp4q_gemm;
+  if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
+  if (m < 0 || n < 0 || k <= 0 || k % 16 || ldc < n) return FP4Q_ERR_SHAPE;
+  if (m >= ((int64_t)1 << 31) || n >= ((int64_t)1 << 31) || k >= ((int64_t)1 << 30)) return FP4Q_ERR_SHAPE;
+  if (m == 0 || n == 0) return FP4Q_OK;
+  if (!a_codes || !a_scales || !a_global || !b_codes || !b_scales || !b_global || !c) return FP4Q_ERR_NULL;
+  const int64_t kp = padded_k(k);
+  if (((m + 127) / 128) * ((n + 127) / 128) >= ((int64_t)1 << 31) || (m + n) * (kp / 16) >= ((int64_t)1 << 40))
+    return FP4Q_ERR_SHAPE;
+  if (!workspace || workspace_bytes < fp4q_gemm_nvfp4_workspace_bytes(m, n, k)) return FP4Q_ERR_WORKSPACE;
+  if (!aligned(a_codes, 8) || !aligned(b_codes, 8) || !aligned(a_global, 4) || !aligned(b_global, 4) ||
+      !aligned(workspace, 16) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
+    return FP4Q_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t *wa = (uint16_t *)workspace;
+  uint16_t *wb = wa + m * kp;
+  const int64_t ta = m * (kp / 16), tb = n * (kp / 16);
+  hipLaunchKernelGGL(nvfp4_to_bf16_kernel, dim3((unsigned)((ta + 255) / 256)), dim3(256), 0, s, a_codes, a_scales,
+                     (int)m, (int)k, (int)kp, wa);
+  hipLaunchKernelGGL(nvfp4_to_bf16_kernel, dim3((unsigned)((tb + 255) / 256)), dim3(256), 0, s, b_codes, b_scales,
+                     (int)n, (int)k, (int)kp, wb);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) {
+    if (out_dtype == FP4Q_F32)
+      e = dispatch_nv<float>(wa, wb, (int)m, (int)n, (int)kp, a_global, b_global, (float *)c, ldc, s);
+    else
+      e = dispatch_nv<uint16_t>(wa, wb, (int)m, (int)n, (int)kp, a_global, b_global, (uint16_t *)c, ldc, s);
+  }
   return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
 }

@@ -1,4 +1,4 @@
-/* fp4q_gemm.h -- W4A4 matrix product of microscaled FP4 operands on gfx950.
+/* fp4q_gemm.h -- W4A4 matrix products of microscaled FP4 operands on gfx950.
  *
  * Consumer of the quantizers in fp4q.h.  "Bridging the Gap Between Promise
  * and Performance for Microscaling FP4 Quantization" (2. Metodologia;
@@ -58,6 +58,47 @@ extern "C" {
 fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
                               const uint8_t *b_scales, int64_t m, int64_t n, int64_t k, float alpha,
                               fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *stream);
+
+/* Workspace the NVFP4 product needs: (m + n) * roundup(k, 32) * 2 bytes (the
+ * operands decoded to bfloat16).  0 for invalid sizes. */
+size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* C = fp32(S_a * S_b) * (A_hat * B_hat^T) for NVFP4 operands, where A_hat and
+ * B_hat hold q * E4M3(p) without the global scales.
+ *
+ * The NVFP4 tensors are the ones "Resumo Tecnico: ScaleSweep" describes:
+ * E2M1 codes, one E4M3 scale per 16 elements of K, and one FP32 global scale
+ * per tensor.  This is the layout fp4q_quantize_nvfp4 writes.
+ *   a_codes   [m x k/2] bytes, row-major (element 2i in the low nibble of
+ *             byte i; bit 3 of a nibble is the sign).
+ *   a_scales  [m x k/16] E4M3 bytes (bit 7 sign; 0x7F / 0xFF NaN).
+ *   a_global  device pointer to A's float32 global scale S_a.
+ *   b_codes, b_scales, b_global  the same for B [n x k].
+ *   m, n, k   m, n >= 0; k > 0 and a multiple of 16.
+ *   out_dtype, c, ldc  as for fp4q_gemm_mxfp4.
+ *   workspace device memory of at least fp4q_gemm_nvfp4_workspace_bytes(m,
+ *             n, k) bytes, 16-byte aligned; its contents are overwritten.
+ *
+ * The scaled FP4 matrix core takes only power-of-two (E8M0) scales per 32
+ * elements.  Folding an E4M3 block scale into the elements would need
+ * up to 6 significant bits per element, more than an 8-bit float holds.
+ * So each element is decoded to q * E4M3(p), which bfloat16 holds exactly.
+ * That costs one pass over both operands into the workspace.  The products
+ * run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16), where each
+ * product is exact, summed in float32 one 16-element step of K at a time in
+ * ascending K order.  The result is multiplied by fp32(S_a * S_b).
+ *
+ * Alignment: a_codes and b_codes 8-byte aligned; the global-scale pointers
+ * 4-byte aligned; c aligned to its element size.
+ *
+ * Returns FP4Q_ERR_NULL, FP4Q_ERR_SHAPE, FP4Q_ERR_ARG, FP4Q_ERR_WORKSPACE,
+ * FP4Q_ERR_ALIGN or FP4Q_ERR_HIP, as for fp4q_gemm_mxfp4 (nothing is needed
+ * when m or n is 0).
+ */
+fp4q_status_t fp4q_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_global,
+                              const uint8_t *b_codes, const uint8_t *b_scales, const float *b_global, int64_t m,
+                              int64_t n, int64_t k, fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("fp4q_quantize_nvfp4", "fp4q_quantize_mxfp4", "fp4q_dequantize", "fp4q_block_hadamard",
-              "fp4q_gemm_mxfp4"):
+              "fp4q_gemm_mxfp4", "fp4q_gemm_nvfp4"):
         assert n in names
 
 
@@ -186,6 +186,28 @@ def test_gemm_validation():
     # empty products need no pointers and enqueue nothing
     assert gm(m=0, a=None, as_=None, c=None) == L.OK
     assert gm(n=0, b=None, bs=None, c=None) == L.OK
+
+
+def test_gemm_nvfp4_validation():
+    L, lib = _lib()
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(64, 32, 48) == (64 + 32) * 64 * 2
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(64, 32, 0) == 0
+
+    def gn(**kw):
+        m, n, k = kw.get("m", 64), kw.get("n", 64), kw.get("k", 128)
+        return lib.fp4q_gemm_nvfp4(kw.get("a", X), OUT, kw.get("ag", OUT), X, OUT, OUT, m, n, k,
+                                   kw.get("dt", L.F32), kw.get("c", WS), kw.get("ldc", 64), kw.get("ws", WS),
+                                   kw.get("wsb", 1 << 30), None)
+    assert gn(a=None) == L.ERR_NULL
+    assert gn(ag=None) == L.ERR_NULL
+    assert gn(dt=5) == L.ERR_ARG
+    assert gn(k=40) == L.ERR_SHAPE
+    assert gn(ldc=10) == L.ERR_SHAPE
+    assert gn(ws=None) == L.ERR_WORKSPACE
+    assert gn(wsb=100) == L.ERR_WORKSPACE
+    assert gn(ws=WS + 8) == L.ERR_ALIGN
+    assert gn(ag=OUT + 2) == L.ERR_ALIGN
+    assert gn(m=0, a=None, ag=None, c=None, ws=None) == L.OK
 
 
 def test_empty_shapes_need_no_device_for_dequant_and_hadamard():

@@ -170,3 +170,97 @@ def test_gemm_full_size_sampled_rows(out_dtype):
     rows = np.sort(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(m, 42, replace=False)]))
     c = c_all[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     _check(c, ac, as_, bc, bs, k, bf16=out_dtype == torch.bfloat16, rows=rows)
+
+
+# ----------------------------------------------------------- NVFP4 operands ----
+# Bar: the operands are decoded exactly (q * E4M3 in bfloat16) and each product is exact in the
+# float32 accumulator, so |C - C_exact| <= (2 ceil(K/16) + 3) * 2^-24 * sum_k |a_ik b_jk|, with
+# one rounding for each 16-element step's sum and one for adding it, plus fp32(S_a S_b), the final
+# multiply and the store; bit-exact when every partial sum is representable (unit block and global
+# scales).
+
+
+def _rand_nv(rng, rows, k, lo=40, hi=80):
+    codes = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(lo, hi + 1, (rows, k // 16)).astype(np.uint8)
+    return codes, scales
+
+
+def _run_nv(ac, as_, ag, bc, bs, bg, out_dtype=torch.float32):
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c = _fq().gemm_nvfp4((a, asd, float(ag)), (b, bsd, float(bg)), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy().astype(np.float64)
+
+
+def _check_nv(c, ac, as_, ag, bc, bs, bg, k, bf16=False, rows=None):
+    A = GM.decode_nvfp4_64(ac, as_, ag)
+    B = GM.decode_nvfp4_64(bc, bs, bg)
+    if rows is not None:
+        A = A[rows]
+    ref = GM.gemm(A, B)
+    tol = (2 * math.ceil(k / 16) + 3) * 2.0 ** -24 * GM.abs_product(A, B)
+    if bf16:
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(c - ref)
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} outside the bound; worst ratio "
+                           f"{np.max(err / np.maximum(tol, 1e-300)):.3g}")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (5, 7, 48), (33, 65, 128), (130, 257, 176), (257, 129, 2048),
+                                   (300, 260, 1040)])
+def test_gemm_nvfp4_exact_with_unit_scales(m, n, k):
+    rng = np.random.default_rng(4000 + m + n + k)
+    ac, _ = _rand_nv(rng, m, k)
+    bc, _ = _rand_nv(rng, n, k)
+    as_ = np.full((m, k // 16), 0x38, np.uint8)  # E4M3 1.0
+    bs = np.full((n, k // 16), 0x38, np.uint8)
+    c = _run_nv(ac, as_, 1.0, bc, bs, 1.0)
+    np.testing.assert_array_equal(c, GM.gemm_nvfp4(ac, as_, np.float32(1), bc, bs, np.float32(1)))
+
+
+@pytest.mark.parametrize("m,n,k", [(5, 7, 48), (130, 257, 176), (257, 129, 2048), (512, 1024, 512)])
+def test_gemm_nvfp4_random_scales_within_bound(m, n, k):
+    rng = np.random.default_rng(5000 + m + n + k)
+    ac, as_ = _rand_nv(rng, m, k, 1, 126)
+    bc, bs = _rand_nv(rng, n, k, 1, 126)
+    ag, bg = np.float32(0.0137), np.float32(0.71)
+    _check_nv(_run_nv(ac, as_, ag, bc, bs, bg), ac, as_, ag, bc, bs, bg, k)
+
+
+def test_gemm_nvfp4_of_quantized_operands_and_nan_scale():
+    """The oracle's NVFP4 sweep of t4 weights and Laplace activations: the GPU
+    product matches the oracle's product of the same codes and tracks X W^T;
+    an E4M3 NaN scale byte gives a NaN row."""
+    rng = np.random.default_rng(5100)
+    x = rng.laplace(0, 1, (96, 512)).astype(np.float32)
+    w = (rng.standard_t(4, (160, 512)) * 0.02).astype(np.float32)
+    qa, qb = Q.quantize_nvfp4(x), Q.quantize_nvfp4(w)
+    c = _run_nv(qa.codes, qa.scales, qa.global_scale, qb.codes, qb.scales, qb.global_scale)
+    _check_nv(c, qa.codes, qa.scales, qa.global_scale, qb.codes, qb.scales, qb.global_scale, 512)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.linalg.norm(c - ref) / np.linalg.norm(ref) < 0.2
+    sc = qa.scales.copy()
+    sc[7, 3] = 0x7F
+    c2 = _run_nv(qa.codes, sc, qa.global_scale, qb.codes, qb.scales, qb.global_scale)
+    assert np.all(np.isnan(c2[7]))
+    mask = np.ones(96, bool)
+    mask[7] = False
+    assert np.all(np.isfinite(c2[mask]))
+
+
+def test_gemm_nvfp4_full_size_sampled_rows():
+    """8192 x 14336 x 4096 with bf16 output in the launch configuration of
+    the large-tile path; 40 sampled rows against the oracle."""
+    rng = np.random.default_rng(5200)
+    m, n, k = 8192, 14336, 4096
+    ac, as_ = _rand_nv(rng, m, k)
+    bc, bs = _rand_nv(rng, n, k)
+    ag, bg = np.float32(0.003), np.float32(0.02)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c_all = _fq().gemm_nvfp4((a, asd, float(ag)), (b, bsd, float(bg)), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, 255, 256, 8191], rng.choice(m, 36, replace=False)]))
+    c = c_all[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
+    _check_nv(c, ac, as_, ag, bc, bs, bg, k, bf16=True, rows=rows)
