@@ -476,10 +476,13 @@ template <typename OutT>
 hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
                     float alpha, OutT *c, int64_t ldc, hipStream_t s) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
   if (k % 128 == 0 && aligned(as, 4) && aligned(bs, 4)) {
-    // direct-to-LDS ring: 256 x 256 tiles on 8 waves when they fill the chip, else 128 x 128 on 4
+    // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to
+    // half the CUs, 64 x 64 for few-token products
     if (big >= 256) return launch_ring<2, 4, 4, 2, 3>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
-    return launch_ring<2, 2, 2, 2, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    if (mid >= 128) return launch_ring<2, 2, 2, 2, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    return launch_ring<2, 2, 1, 1, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
   }
   // any K that is a multiple of 32: register-staged double buffer
   if (big >= 256) return launch<4, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
@@ -543,8 +546,10 @@ template <typename OutT>
 hipError_t dispatch_nv(const uint16_t *a, const uint16_t *b, int m, int n, int kp, const float *ga, const float *gb,
                        OutT *c, int64_t ldc, hipStream_t s) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
   if (big >= 256) return launch_ring_bf16<2, 4, 4, 2, 3>(a, b, m, n, kp, ga, gb, c, ldc, s);
-  return launch_ring_bf16<2, 2, 2, 2, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
+  if (mid >= 128) return launch_ring_bf16<2, 2, 2, 2, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
+  return launch_ring_bf16<2, 2, 1, 1, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
 }
 
 int64_t padded_k(int64_t k) { return (k + 31) / 32 * 32; }
