@@ -201,13 +201,14 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t *__rest
 // ---------------------------------------------------------------------------
 // Main path (K a multiple of 128): operands move from global memory straight
 // into LDS (global_load_lds_dwordx4; lane l of a wave writes bytes
-// [16 l, 16 l + 16) after the wave's LDS base), through a ring of NS stages,
-// so NS - 1 stages of loads are in flight while the matrix cores consume
-// one.  Per stage a row contributes 64 code bytes (four 16-byte chunks) and
-// one scale dword.  Rows are stored unpadded, with chunk c of row r at
-// position c ^ sw(r), sw(r) = ((r >> 1) ^ (r >> 3)) & 3.  The 32 rows a
-// wave reads for one operand then fall on distinct banks, whether the LDS
-// serves 16 lanes from 64 banks or 8 lanes from 32 banks per cycle.  Rows
+// [16 l, 16 l + 16) after the wave's LDS base) through a ring of NS stages,
+// so that up to NS - 1 stages of loads are in flight while the matrix cores
+// consume one.  Per stage a row contributes 64 bytes (four 16-byte chunks:
+// 128 FP4 codes or 32 bf16 values) and, for MXFP4, one dword of E8M0 scales.
+// Rows are stored unpadded, with chunk c of row r at position c ^ sw(r),
+// sw(r) = (r >> 2) & 3.  This LDS serves a 16-byte read for 16 lanes per
+// cycle from 64 banks; with this swizzle the 16 rows of each group fall on
+// distinct banks, and the bank-conflict counter reads close to zero.  Rows
 // past M or N are loaded from row M - 1 or N - 1 (no branches); they only
 // feed outputs that are never stored.
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
