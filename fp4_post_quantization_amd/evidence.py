@@ -26,6 +26,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import subprocess
 import sys
 
@@ -93,12 +94,21 @@ WORKLOADS = {
 }
 
 
+def _code_only(text):
+    """C/C++ source with comments and whitespace removed (string literals in
+    these sources contain no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def source_hash(config=None):
-    """sha256 over the sources of the workload's dominant kernel."""
+    """sha256 over the code (comments and whitespace removed) of the sources
+    of the workload's dominant kernel."""
     h = hashlib.sha256()
     for p in WORKLOADS.get(config, {}).get("sources", KERNEL_SOURCES):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -300,7 +310,7 @@ def committed_traffic(config):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    return rec if rec.get("source_sha256") == source_hash() else None
+    return rec if rec.get("source_sha256") == source_hash(config) else None
 
 
 def main():
