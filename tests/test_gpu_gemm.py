@@ -154,6 +154,25 @@ def test_gemm_of_quantized_rotated_operands():
     assert np.linalg.norm(c - ref) / np.linalg.norm(ref) < 0.2
 
 
+def test_gemm_large_tiles_with_k_tail():
+    """K not a multiple of 128 with enough rows and columns for 256 x 256
+    tiles: the register-staged path with its zero-filled K tail; sampled rows
+    against the oracle, bit-exact with unit scales."""
+    rng = np.random.default_rng(3007)
+    m, n, k = 4096, 4096, 1056
+    ac, _ = _rand_mx(rng, m, k)
+    bc, _ = _rand_mx(rng, n, k)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c_all = _fq().gemm_mxfp4((a, asd), (b, bsd))
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([[0, 255, 256, 4095], rng.choice(m, 28, replace=False)]))
+    c = c_all[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+    ref = GM.gemm(GM.decode_mxfp4_64(ac, as_)[rows], GM.decode_mxfp4_64(bc, bs))
+    np.testing.assert_array_equal(c, ref)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_gemm_full_size_sampled_rows(out_dtype):
     """8192 tokens x 14336 outputs x 4096 inputs (an 8B-shaped up/gate
