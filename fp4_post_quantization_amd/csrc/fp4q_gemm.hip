@@ -15,10 +15,12 @@
 // Two kernels:
 //  * mx_gemm_ring_kernel (K a multiple of 128, the main path): 8 waves
 //    compute a 256 x 256 tile, each wave 128 x 64 (4 x 2 accumulator
-//    blocks, two waves per SIMD).  K advances in stages of 128 elements.
-//    Stages travel from global memory straight into a 3-deep LDS ring
-//    (direct global-to-LDS loads), so two stages are in flight while one is
-//    consumed.  Each wave reads a k step's operands while the previous k
+//    blocks, two waves per SIMD); smaller problems use 128 x 128 or 64 x 64
+//    tiles.  K advances in stages of 128 or 64 bytes per row (256 or 128
+//    MXFP4 elements; 64 or 32 bf16 values).  Stages travel from global
+//    memory straight into an LDS ring (direct global-to-LDS loads), so the
+//    next stages are in flight while one is consumed; 128-byte stages make
+//    every load cover whole 128-byte lines.  Each wave reads a k step's operands while the previous k
 //    step's MFMAs run.  The output tile leaves through LDS as 16-byte row
 //    stores.
 //  * mx_gemm_kernel (any K that is a multiple of 32): register-staged
@@ -211,7 +213,11 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(const uint8_t *__rest
 // distinct banks, and the bank-conflict counter reads close to zero.  Rows
 // past M or N are loaded from row M - 1 or N - 1 (no branches); they only
 // feed outputs that are never stored.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+template <int ROWB>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (ROWB == 64) return (r >> 2) & 3;  // 16 rows of 64 B cover all 64 banks 4 times
+  else return (r >> 1) & 7;                       // 128-byte rows: 8 chunks, rows pair up per bank half
+}
 
 // s_waitcnt with only the vector-memory counter (expcnt, lgkmcnt at their maxima)
 template <int VM>
@@ -236,23 +242,29 @@ __device__ __forceinline__ void load_lds4(const void *g, void *l) {
 // v_mfma_scale_f32_32x32x64_f8f6f4).  MX = false: bf16 operands (a stage is 32 K elements = 64 bytes
 // per row; v_mfma_f32_32x32x16_bf16, lane l holding row l % 32 and K elements 8 (l / 32) .. +8, checked
 // on the device), scaled at the end by fp32(*ga * *gb).  Rows are kb bytes apart; nst stages.
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true>
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true, int ROWB = 64>
 __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, int ksc, const float *__restrict__ ga,
     const float *__restrict__ gb, float alpha, OutT *__restrict__ C, int64_t ldc) {
   constexpr int WAVES = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
-  constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
-  constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * 4;
-  constexpr int STAGE = MX ? SB_OFF + BN * 4 : A_BYTES + B_BYTES;
-  // 1 KB code loads (16 rows each) and 256 B scale loads (64 rows each) per stage, spread over the waves
-  constexpr int A_INSTR = BM / 16 / WAVES, B_INSTR = BN / 16 / WAVES;
-  constexpr int SA_INSTR = BM / 64, SB_INSTR = BN / 64;
+  static_assert(ROWB == 64 || ROWB == 128, "a stage holds 64 or 128 bytes of each row");
+  constexpr int CPR = ROWB / 16;  // 16-byte chunks per row per stage
+  constexpr int KS = ROWB / 32;   // k steps per stage (32 bytes of a row each)
+  constexpr int SPR = ROWB / 16;  // MXFP4 scale bytes per row per stage
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * SPR;
+  constexpr int STAGE = MX ? SB_OFF + BN * SPR : A_BYTES + B_BYTES;
+  // 1 KB code loads (1024 / ROWB rows each) and 256 B scale loads per stage, spread over the waves
+  constexpr int RPL = 1024 / ROWB;
+  constexpr int A_INSTR = BM / RPL / WAVES, B_INSTR = BN / RPL / WAVES;
+  constexpr int SA_INSTR = BM * SPR / 256, SB_INSTR = BN * SPR / 256;
   // every wave issues the same number of scale loads (a wave without one loads into a spare slot),
   // so that the per-wave count of loads per stage is a constant
   constexpr int SQ = MX ? (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES : 0;
-  static_assert(A_INSTR * WAVES * 16 == BM && B_INSTR * WAVES * 16 == BN, "code loads must divide evenly");
+  static_assert(A_INSTR * WAVES * RPL == BM && B_INSTR * WAVES * RPL == BN, "code loads must divide evenly");
+  static_assert(!MX || (SA_INSTR * 256 == BM * SPR && SB_INSTR * 256 == BN * SPR), "scale loads cover whole rows");
   constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
   constexpr int SPARE = NS * STAGE;               // 256 B target of the filler scale loads
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 256];
@@ -266,33 +278,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   const int wm = wave % WGM, wn = wave / WGM;
   const int l32 = lane & 31, h = lane >> 5;
 
-  // per-lane source addresses of the loads (advanced by 64 code bytes / 4 scale bytes per stage)
+  // per-lane source addresses of the loads (advanced by ROWB code bytes / SPR scale bytes per stage)
   const uint8_t *srcA[A_INSTR];
   const uint8_t *srcB[B_INSTR];
 #pragma unroll
   for (int i = 0; i < A_INSTR; ++i) {
-    const int row = (wave * A_INSTR + i) * 16 + (lane >> 2);
-    srcA[i] = A + (int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane & 3) ^ swz(row));
+    const int row = (wave * A_INSTR + i) * RPL + lane / CPR;
+    srcA[i] = A + (int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row));
   }
 #pragma unroll
   for (int i = 0; i < B_INSTR; ++i) {
-    const int row = (wave * B_INSTR + i) * 16 + (lane >> 2);
-    srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane & 3) ^ swz(row));
+    const int row = (wave * B_INSTR + i) * RPL + lane / CPR;
+    srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row));
   }
+  // scale load q covers 256 bytes: 256 / SPR rows, lane l loading dword l % (SPR / 4) of row l / (SPR / 4)
+  constexpr int DPR = SPR / 4;  // scale dwords per row per stage
   const uint8_t *srcS[SQ > 0 ? SQ : 1];
   int dstS[SQ > 0 ? SQ : 1];
 #pragma unroll
   for (int j = 0; j < SQ; ++j) {
     const int q = wave + WAVES * j;
+    const int rl = lane / DPR, dw = lane % DPR;
     if (q < SA_INSTR) {
-      srcS[j] = As + (int64_t)min(m0 + 64 * q + lane, M - 1) * ksc;
+      srcS[j] = As + (int64_t)min(m0 + (256 / SPR) * q + rl, M - 1) * ksc + 4 * dw;
       dstS[j] = SA_OFF + 256 * q;
     } else if (q < SA_INSTR + SB_INSTR) {
       const int qb = q - SA_INSTR;
-      srcS[j] = Bs + (int64_t)min(n0 + 64 * qb + lane, N - 1) * ksc;
+      srcS[j] = Bs + (int64_t)min(n0 + (256 / SPR) * qb + rl, N - 1) * ksc + 4 * dw;
       dstS[j] = SB_OFF + 256 * qb;
     } else {
-      srcS[j] = As + (int64_t)min(m0 + lane, M - 1) * ksc;
+      srcS[j] = As + (int64_t)min(m0 + rl, M - 1) * ksc + 4 * dw;
       dstS[j] = -1;
     }
   }
@@ -300,11 +315,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   auto issue = [&](int st, int slot) {
     uint8_t *base = smem + slot * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) load_lds16(srcA[i] + st * 64, base + (wave * A_INSTR + i) * 1024);
+    for (int i = 0; i < A_INSTR; ++i) load_lds16(srcA[i] + st * ROWB, base + (wave * A_INSTR + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i) load_lds16(srcB[i] + st * 64, base + A_BYTES + (wave * B_INSTR + i) * 1024);
+    for (int i = 0; i < B_INSTR; ++i)
+      load_lds16(srcB[i] + st * ROWB, base + A_BYTES + (wave * B_INSTR + i) * 1024);
 #pragma unroll
-    for (int j = 0; j < SQ; ++j) load_lds4(srcS[j] + st * 4, dstS[j] >= 0 ? base + dstS[j] : smem + SPARE);
+    for (int j = 0; j < SQ; ++j) load_lds4(srcS[j] + st * SPR, dstS[j] >= 0 ? base + dstS[j] : smem + SPARE);
   };
 
   f32x16 acc[TM][TN];
@@ -323,16 +339,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * TM * 32 + i * 32 + l32;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * ROWB + 16 * ((2 * ks + h) ^ swz<ROWB>(r)));
       o.a[i] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sa[i] = base[SA_OFF + 4 * r + 2 * ks + h];  // the byte itself: no ALU work
+      if constexpr (MX) o.sa[i] = base[SA_OFF + SPR * r + 2 * ks + h];  // the byte itself: no ALU work
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * TN * 32 + j * 32 + l32;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * 64 + 16 * ((2 * ks + h) ^ swz(r)));
+      const i32x4 v =
+          *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * ROWB + 16 * ((2 * ks + h) ^ swz<ROWB>(r)));
       o.b[j] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sb[j] = base[SB_OFF + 4 * r + 2 * ks + h];
+      if constexpr (MX) o.sb[j] = base[SB_OFF + SPR * r + 2 * ks + h];
     }
   };
   auto mfmas = [&](const Ops &o) {
@@ -373,8 +390,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   read_ops(0, 0, o0);
   int slot = 0;
   for (int st = 0; st < nst; ++st) {
-    read_ops(slot, 1, o1);  // second k step of this stage, read while the first one's MFMAs run
-    mfmas(o0);
+    // k steps 0 .. KS-2: read step ks + 1 while step ks's MFMAs run (KS is even: o0 holds the even steps)
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      if (ks % 2 == 0) {
+        read_ops(slot, ks + 1, o1);
+        mfmas(o0);
+      } else {
+        read_ops(slot, ks + 1, o0);
+        mfmas(o1);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the barrier below
     const int next = slot == NS - 1 ? 0 : slot + 1;
     wait_lgkmcnt0();                    // this wave's reads of stage st are complete
@@ -450,26 +476,27 @@ hipError_t launch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const u
   return hipGetLastError();
 }
 
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+// MXFP4 operands; k a multiple of 2 * ROWB (a stage holds ROWB code bytes = 2 * ROWB elements per row)
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, int ROWB = 64>
 hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
                        float alpha, OutT *c, int64_t ldc, hipStream_t s) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true>), dim3((unsigned)tiles),
-                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / 128, (int64_t)(k / 2), k / 32,
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB>), dim3((unsigned)tiles),
+                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), k / 32,
                      (const float *)nullptr, (const float *)nullptr, alpha, c, ldc);
   return hipGetLastError();
 }
 
-// bf16 operands (rows of kp elements, kp a multiple of 32) scaled by fp32(*ga * *gb)
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+// bf16 operands (rows of kp elements, kp a multiple of ROWB / 2) scaled by fp32(*ga * *gb)
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, int ROWB = 64>
 hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, int kp, const float *ga,
                             const float *gb, OutT *c, int64_t ldc, hipStream_t s) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false, ROWB>), dim3((unsigned)tiles),
                      dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr, (const uint8_t *)b,
-                     (const uint8_t *)nullptr, m, n, kp / 32, (int64_t)kp * 2, 0, ga, gb, 1.0f, c, ldc);
+                     (const uint8_t *)nullptr, m, n, kp * 2 / ROWB, (int64_t)kp * 2, 0, ga, gb, 1.0f, c, ldc);
   return hipGetLastError();
 }
 
@@ -478,9 +505,15 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
                     float alpha, OutT *c, int64_t ldc, hipStream_t s) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+  // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to half
+  // the CUs, 64 x 64 for few-token products; stages of 128 code bytes per row (full 128-byte lines per
+  // load) when K allows, else 64
+  if (k % 256 == 0 && aligned(as, 4) && aligned(bs, 4)) {
+    if (big >= 256) return launch_ring<2, 4, 4, 2, 2, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    if (mid >= 128) return launch_ring<2, 2, 2, 2, 3, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    return launch_ring<2, 2, 1, 1, 4, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+  }
   if (k % 128 == 0 && aligned(as, 4) && aligned(bs, 4)) {
-    // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to
-    // half the CUs, 64 x 64 for few-token products
     if (big >= 256) return launch_ring<2, 4, 4, 2, 3>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
     if (mid >= 128) return launch_ring<2, 2, 2, 2, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
     return launch_ring<2, 2, 1, 1, 4>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
@@ -548,6 +581,9 @@ hipError_t dispatch_nv(const uint16_t *a, const uint16_t *b, int m, int n, int k
                        OutT *c, int64_t ldc, hipStream_t s) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+  // 128-byte stages pay off with the large tiles only (measured)
+  if (big >= 256 && kp % 64 == 0)
+    return launch_ring_bf16<2, 4, 4, 2, 2, OutT, 128>(a, b, m, n, kp, ga, gb, c, ldc, s);
   if (big >= 256) return launch_ring_bf16<2, 4, 4, 2, 3>(a, b, m, n, kp, ga, gb, c, ldc, s);
   if (mid >= 128) return launch_ring_bf16<2, 2, 2, 2, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
   return launch_ring_bf16<2, 2, 1, 1, 4>(a, b, m, n, kp, ga, gb, c, ldc, s);
