@@ -334,16 +334,15 @@ def run_w4a4(args, fmt="mxfp4"):
             return fq.quantize_mxfp4(x, window=(0, 0), hadamard_n=32, out=out, with_loss=False, check=check)
         return fq.quantize_nvfp4(x, window=(0, 0), out=out, with_loss=False, check=check)
 
-    ws_nv = None
-    if not mx:
-        need = max(fq._lib.load().fp4q_gemm_nvfp4_workspace_bytes(W.W4A4_TOKENS, n, k)
-                   for n, k in W.LAYER_8B.values())
-        ws_nv = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = fq._lib.load()
+    ws_bytes = lib.fp4q_gemm_mxfp4_workspace_bytes if mx else lib.fp4q_gemm_nvfp4_workspace_bytes
+    ws = torch.empty(max(max(ws_bytes(W.W4A4_TOKENS, n, k) for n, k in W.LAYER_8B.values()), 16),
+                     dtype=torch.uint8, device=dev)
 
     def gemm(a, b, out=None, out_dtype=torch.bfloat16):
         if mx:
-            return fq.gemm_mxfp4(a, b, out=out, out_dtype=out_dtype)
-        return fq.gemm_nvfp4(a, b, out=out, out_dtype=out_dtype, workspace_buf=ws_nv)
+            return fq.gemm_mxfp4(a, b, out=out, out_dtype=out_dtype, workspace_buf=ws)
+        return fq.gemm_nvfp4(a, b, out=out, out_dtype=out_dtype, workspace_buf=ws)
 
     wq, flops, err = {}, {}, {}
     for name in W.LAYER_8B:

@@ -295,12 +295,14 @@ def block_hadamard(x, n, out=None):
     return out
 
 
-def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None):
+def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_buf=None, reorganise=True):
     """C = alpha * A_hat @ B_hat^T for MXFP4 operands (W4A4).
 
     ``a`` and ``b`` are MXFP4Result (or (codes, scales) pairs) as written by
     ``quantize_mxfp4``: A is M x K (activations), B is N x K (weights).
-    Returns C [M, N] in float32 or bfloat16."""
+    Returns C [M, N] in float32 or bfloat16.  With ``reorganise`` (and K a
+    multiple of 256) the scales are first copied stage-major into a
+    workspace (``workspace_buf`` or a fresh one); the result is the same."""
     lib = L.load()
     ac, as_ = (a.codes, a.scales) if isinstance(a, MXFP4Result) else a
     bc, bs = (b.codes, b.scales) if isinstance(b, MXFP4Result) else b
@@ -318,8 +320,13 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None):
     if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     code = L.F32 if out.dtype == torch.float32 else L.BF16
+    need = lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) if reorganise else 0
+    if need and (workspace_buf is None or workspace_buf.numel() < need):
+        workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,
-                                float(alpha), code, out.data_ptr(), out.stride(0), _stream(dev)))
+                                float(alpha), code, out.data_ptr(), out.stride(0),
+                                _ptr(workspace_buf) if need else None, workspace_buf.numel() if need else 0,
+                                _stream(dev)))
     return out
 
 

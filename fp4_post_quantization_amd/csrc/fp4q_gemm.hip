@@ -238,14 +238,23 @@ __device__ __forceinline__ void load_lds4(const void *g, void *l) {
                                    (__attribute__((address_space(3))) void *)l, 4, 0, 0);
 }
 
+// Where the E8M0 bytes of row r for stage st are: S + r * row + st * stage.  Row-major scales (the
+// quantizer's layout): row = K / 32, stage = scale bytes per stage.  Stage-major scales
+// ([K / (2 ROWB)][rows][ROWB / 16], written by the scale reorganisation pass): row = ROWB / 16,
+// stage = rows * ROWB / 16, so one stage of a tile's scales is one contiguous run.
+struct ScaleLayout {
+  int64_t a_row, a_stage, b_row, b_stage;
+};
+
 // MX = true: MXFP4 operands (a stage is 128 K elements = 64 code bytes + 4 E8M0 bytes per row;
 // v_mfma_scale_f32_32x32x64_f8f6f4).  MX = false: bf16 operands (a stage is 32 K elements = 64 bytes
 // per row; v_mfma_f32_32x32x16_bf16, lane l holding row l % 32 and K elements 8 (l / 32) .. +8, checked
 // on the device), scaled at the end by fp32(*ga * *gb).  Rows are kb bytes apart; nst stages.
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true, int ROWB = 64>
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true, int ROWB = 64,
+          bool SCALE16 = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
-    const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, int ksc, const float *__restrict__ ga,
+    const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, ScaleLayout sl, const float *__restrict__ ga,
     const float *__restrict__ gb, float alpha, OutT *__restrict__ C, int64_t ldc) {
   constexpr int WAVES = WGM * WGN;
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
@@ -259,15 +268,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   // 1 KB code loads (1024 / ROWB rows each) and 256 B scale loads per stage, spread over the waves
   constexpr int RPL = 1024 / ROWB;
   constexpr int A_INSTR = BM / RPL / WAVES, B_INSTR = BN / RPL / WAVES;
-  constexpr int SA_INSTR = BM * SPR / 256, SB_INSTR = BN * SPR / 256;
+  // scale loads: 256 B (4 bytes per lane, row-major scales) or, SCALE16, 1 KB (16 bytes per lane,
+  // two rows of stage-major scales each)
+  constexpr int SBYTES = SCALE16 ? 1024 : 256;
+  constexpr int SA_INSTR = BM * SPR / SBYTES, SB_INSTR = BN * SPR / SBYTES;
   // every wave issues the same number of scale loads (a wave without one loads into a spare slot),
   // so that the per-wave count of loads per stage is a constant
   constexpr int SQ = MX ? (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES : 0;
   static_assert(A_INSTR * WAVES * RPL == BM && B_INSTR * WAVES * RPL == BN, "code loads must divide evenly");
-  static_assert(!MX || (SA_INSTR * 256 == BM * SPR && SB_INSTR * 256 == BN * SPR), "scale loads cover whole rows");
+  static_assert(!MX || (SA_INSTR * SBYTES == BM * SPR && SB_INSTR * SBYTES == BN * SPR),
+                "scale loads cover whole rows");
+  static_assert(!SCALE16 || SPR == 8, "16-byte scale loads take two rows of 8 scale bytes");
   constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
-  constexpr int SPARE = NS * STAGE;               // 256 B target of the filler scale loads
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 256];
+  constexpr int SPARE = NS * STAGE;               // target of the filler scale loads
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + SBYTES];
   if constexpr (!MX) alpha = (*ga) * (*gb);
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -294,20 +308,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   // scale load q covers 256 bytes: 256 / SPR rows, lane l loading dword l % (SPR / 4) of row l / (SPR / 4)
   constexpr int DPR = SPR / 4;  // scale dwords per row per stage
   const uint8_t *srcS[SQ > 0 ? SQ : 1];
+  int64_t stepS[SQ > 0 ? SQ : 1];
   int dstS[SQ > 0 ? SQ : 1];
 #pragma unroll
   for (int j = 0; j < SQ; ++j) {
     const int q = wave + WAVES * j;
-    const int rl = lane / DPR, dw = lane % DPR;
+    // SCALE16: lane l loads rows 2l, 2l + 1 (16 contiguous bytes of stage-major scales); the row is
+    // clamped to the last one, and a pair starting there reads 8 bytes past the rows' end (the
+    // reorganised copy is padded for it)
+    const int rl = SCALE16 ? 2 * lane : lane / DPR, dw = SCALE16 ? 0 : lane % DPR;
+    constexpr int RPS = SBYTES / SPR;  // rows per scale load
     if (q < SA_INSTR) {
-      srcS[j] = As + (int64_t)min(m0 + (256 / SPR) * q + rl, M - 1) * ksc + 4 * dw;
-      dstS[j] = SA_OFF + 256 * q;
+      srcS[j] = As + (int64_t)min(m0 + RPS * q + rl, M - 1) * sl.a_row + 4 * dw;
+      stepS[j] = sl.a_stage;
+      dstS[j] = SA_OFF + SBYTES * q;
     } else if (q < SA_INSTR + SB_INSTR) {
       const int qb = q - SA_INSTR;
-      srcS[j] = Bs + (int64_t)min(n0 + (256 / SPR) * qb + rl, N - 1) * ksc + 4 * dw;
-      dstS[j] = SB_OFF + 256 * qb;
+      srcS[j] = Bs + (int64_t)min(n0 + RPS * qb + rl, N - 1) * sl.b_row + 4 * dw;
+      stepS[j] = sl.b_stage;
+      dstS[j] = SB_OFF + SBYTES * qb;
     } else {
-      srcS[j] = As + (int64_t)min(m0 + rl, M - 1) * ksc + 4 * dw;
+      srcS[j] = As + (int64_t)min(m0 + rl, M - 1) * sl.a_row + 4 * dw;
+      stepS[j] = sl.a_stage;
       dstS[j] = -1;
     }
   }
@@ -320,7 +342,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     for (int i = 0; i < B_INSTR; ++i)
       load_lds16(srcB[i] + st * ROWB, base + A_BYTES + (wave * B_INSTR + i) * 1024);
 #pragma unroll
-    for (int j = 0; j < SQ; ++j) load_lds4(srcS[j] + st * SPR, dstS[j] >= 0 ? base + dstS[j] : smem + SPARE);
+    for (int j = 0; j < SQ; ++j) {
+      uint8_t *d = dstS[j] >= 0 ? base + dstS[j] : smem + SPARE;
+      if constexpr (SCALE16) load_lds16(srcS[j] + st * stepS[j], d);
+      else load_lds4(srcS[j] + st * stepS[j], d);
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -476,14 +502,18 @@ hipError_t launch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const u
   return hipGetLastError();
 }
 
-// MXFP4 operands; k a multiple of 2 * ROWB (a stage holds ROWB code bytes = 2 * ROWB elements per row)
-template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, int ROWB = 64>
+// MXFP4 operands; k a multiple of 2 * ROWB (a stage holds ROWB code bytes = 2 * ROWB elements per
+// row).  staged: the scales were reorganised stage-major (as / bs point into that copy).
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, int ROWB = 64, bool SCALE16 = false>
 hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
-                       float alpha, OutT *c, int64_t ldc, hipStream_t s) {
+                       float alpha, OutT *c, int64_t ldc, hipStream_t s, bool staged = false) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  constexpr int SPR = ROWB / 16;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB>), dim3((unsigned)tiles),
-                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), k / 32,
+  const ScaleLayout sl = staged ? ScaleLayout{SPR, (int64_t)m * SPR, SPR, (int64_t)n * SPR}
+                                : ScaleLayout{k / 32, SPR, k / 32, SPR};
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16>), dim3((unsigned)tiles),
+                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), sl,
                      (const float *)nullptr, (const float *)nullptr, alpha, c, ldc);
   return hipGetLastError();
 }
@@ -496,15 +526,45 @@ hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, 
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false, ROWB>), dim3((unsigned)tiles),
                      dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr, (const uint8_t *)b,
-                     (const uint8_t *)nullptr, m, n, kp * 2 / ROWB, (int64_t)kp * 2, 0, ga, gb, 1.0f, c, ldc);
+                     (const uint8_t *)nullptr, m, n, kp * 2 / ROWB, (int64_t)kp * 2, ScaleLayout{0, 0, 0, 0}, ga, gb,
+                     1.0f, c, ldc);
   return hipGetLastError();
+}
+
+// Scale reorganisation ("3. QuTLASS" of the MR-GPTQ page reorganises scales for its FP4 product):
+// row-major E8M0 bytes [rows][k / 32] -> stage-major [k / 256][rows][8], one thread per (row, stage),
+// so that the product's per-stage scale loads read contiguous runs instead of 8 bytes per row.
+__global__ __launch_bounds__(256) void scales_to_stage_major_kernel(const uint8_t *__restrict__ src, int rows, int k,
+                                                                    uint8_t *__restrict__ dst) {
+  const int stages = k / 256;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)rows * stages) return;
+  const int r = (int)(t % rows), st = (int)(t / rows);
+  const uint2 v = *reinterpret_cast<const uint2 *>(src + (int64_t)r * (k / 32) + 8 * st);
+  *reinterpret_cast<uint2 *>(dst + ((int64_t)st * rows + r) * 8) = v;
+}
+
+// (m + n) rows of k / 32 scale bytes, plus 16 bytes read past the end by a clamped 16-byte scale load
+int64_t gemm_mxfp4_workspace(int64_t m, int64_t n, int64_t k) {
+  return k % 256 == 0 ? (m + n) * (k / 32) + 32 : 0;
 }
 
 template <typename OutT>
 hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
-                    float alpha, OutT *c, int64_t ldc, hipStream_t s) {
+                    float alpha, OutT *c, int64_t ldc, hipStream_t s, uint8_t *ws = nullptr) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+  if (ws && k % 256 == 0 && big >= 256) {
+    // 256 x 256 tiles: reorganise both operands' scales stage-major first, so that each stage's scales
+    // arrive in 1 KB loads (for smaller tiles the extra pass costs more than it saves: measured)
+    uint8_t *was = ws, *wbs = ws + (int64_t)m * (k / 32) + 16;
+    const int64_t ta = (int64_t)m * (k / 256), tb = (int64_t)n * (k / 256);
+    hipLaunchKernelGGL(scales_to_stage_major_kernel, dim3((unsigned)((ta + 255) / 256)), dim3(256), 0, s, as, m, k,
+                       was);
+    hipLaunchKernelGGL(scales_to_stage_major_kernel, dim3((unsigned)((tb + 255) / 256)), dim3(256), 0, s, bs, n, k,
+                       wbs);
+    return launch_ring<2, 4, 4, 2, 2, OutT, 128, true>(a, was, b, wbs, m, n, k, alpha, c, ldc, s, true);
+  }
   // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to half
   // the CUs, 64 x 64 for few-token products; stages of 128 code bytes per row (full 128-byte lines per
   // load) when K allows, else 64
@@ -593,9 +653,15 @@ int64_t padded_k(int64_t k) { return (k + 31) / 32 * 32; }
 
 }  // namespace fp4q_gemm
 
+extern "C" size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k <= 0 || k % 32) return 0;
+  return (size_t)fp4q_gemm::gemm_mxfp4_workspace(m, n, k);
+}
+
 extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
                                          const uint8_t *b_scales, int64_t m, int64_t n, int64_t k, float alpha,
-                                         fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *stream) {
+                                         fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
   using namespace fp4q_gemm;
   if (out_dtype != FP4Q_F32 && out_dtype != FP4Q_BF16) return FP4Q_ERR_ARG;
   if (m < 0 || n < 0 || k <= 0 || k % 32 || ldc < n) return FP4Q_ERR_SHAPE;
@@ -606,13 +672,22 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
   if (tiles >= ((int64_t)1 << 31)) return FP4Q_ERR_SHAPE;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
     return FP4Q_ERR_ALIGN;
+  // the workspace is optional: with it (and K a multiple of 256) the scales are reorganised
+  uint8_t *ws = nullptr;
+  const int64_t need = gemm_mxfp4_workspace(m, n, k);
+  if (workspace && need > 0) {
+    if (workspace_bytes < (size_t)need) return FP4Q_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FP4Q_ERR_ALIGN;
+    if (aligned(a_scales, 8) && aligned(b_scales, 8) && (m + n) * (k / 256) < ((int64_t)1 << 39))
+      ws = (uint8_t *)workspace;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (out_dtype == FP4Q_F32)
-    e = dispatch<float>(a_codes, a_scales, b_codes, b_scales, (int)m, (int)n, (int)k, alpha, (float *)c, ldc, s);
+    e = dispatch<float>(a_codes, a_scales, b_codes, b_scales, (int)m, (int)n, (int)k, alpha, (float *)c, ldc, s, ws);
   else
     e = dispatch<uint16_t>(a_codes, a_scales, b_codes, b_scales, (int)m, (int)n, (int)k, alpha, (uint16_t *)c, ldc,
-                           s);
+                           s, ws);
   return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
 }
 

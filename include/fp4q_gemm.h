@@ -41,6 +41,15 @@ extern "C" {
  *   out_dtype FP4Q_F32 or FP4Q_BF16 (round to nearest even).
  *   c         [m x n] row-major with leading dimension ldc >= n (elements),
  *             written in full.  It must not overlap the inputs.
+ *   workspace optional device memory (NULL for none) of at least
+ *             fp4q_gemm_mxfp4_workspace_bytes(m, n, k) bytes, 16-byte
+ *             aligned; its contents are overwritten.  When K is a multiple
+ *             of 256 and the product is large enough for 256 x 256 tiles on
+ *             every CU, both operands' scales are first copied there in a
+ *             stage-major order ([k/256][rows][8 bytes]).  The product then
+ *             loads each stage's scales in 1 KB pieces (the MR-GPTQ page,
+ *             3.: QuTLASS reorganises scales for its FP4 product).  Results
+ *             are identical with and without it; only the speed differs.
  *
  * Arithmetic: the products of two decoded elements are exact.  They are
  * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), one
@@ -53,11 +62,18 @@ extern "C" {
  *
  * Returns FP4Q_ERR_NULL for a missing pointer (none is needed when m or n
  * is 0), FP4Q_ERR_SHAPE for a bad m, n, k or ldc, FP4Q_ERR_ARG for an
- * unknown out_dtype, FP4Q_ERR_ALIGN, or FP4Q_ERR_HIP if the launch fails.
+ * unknown out_dtype, FP4Q_ERR_WORKSPACE for a workspace smaller than
+ * fp4q_gemm_mxfp4_workspace_bytes, FP4Q_ERR_ALIGN, or FP4Q_ERR_HIP if the
+ * launch fails.
  */
 fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
                               const uint8_t *b_scales, int64_t m, int64_t n, int64_t k, float alpha,
-                              fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *stream);
+                              fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Workspace that speeds up fp4q_gemm_mxfp4: (m + n) * k / 32 + 32 bytes when K
+ * is a multiple of 256, else 0 (no workspace is used).  0 for invalid sizes. */
+size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* Workspace the NVFP4 product needs: (m + n) * roundup(k, 32) * 2 bytes (the
  * operands decoded to bfloat16).  0 for invalid sizes. */

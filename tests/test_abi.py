@@ -172,7 +172,12 @@ def test_gemm_validation():
     def gm(**kw):
         return lib.fp4q_gemm_mxfp4(kw.get("a", X), kw.get("as_", OUT), kw.get("b", X), kw.get("bs", OUT),
                                    kw.get("m", 64), kw.get("n", 64), kw.get("k", 128), 1.0,
-                                   kw.get("dt", L.F32), kw.get("c", WS), kw.get("ldc", 64), None)
+                                   kw.get("dt", L.F32), kw.get("c", WS), kw.get("ldc", 64), kw.get("ws", None),
+                                   kw.get("wsb", 0), None)
+    assert lib.fp4q_gemm_mxfp4_workspace_bytes(64, 32, 512) == 96 * 16 + 32
+    assert lib.fp4q_gemm_mxfp4_workspace_bytes(64, 32, 384) == 0
+    assert gm(k=512, ws=WS, wsb=100) == L.ERR_WORKSPACE
+    assert gm(k=512, ws=WS + 4, wsb=1 << 20) == L.ERR_ALIGN
     assert gm(a=None) == L.ERR_NULL
     assert gm(bs=None) == L.ERR_NULL
     assert gm(c=None) == L.ERR_NULL

@@ -154,6 +154,23 @@ def test_gemm_of_quantized_rotated_operands():
     assert np.linalg.norm(c - ref) / np.linalg.norm(ref) < 0.2
 
 
+@pytest.mark.parametrize("m,n,k", [(64, 96, 256), (300, 260, 1024), (1024, 640, 512), (4096, 4096, 768)])
+def test_gemm_scale_reorganisation_is_transparent(m, n, k):
+    """Stage-major scales (workspace given) and row-major scales (none) give
+    identical products for every tile configuration."""
+    rng = np.random.default_rng(3008 + m + k)
+    ac, as_ = _rand_mx(rng, m, k, 90, 160)
+    bc, bs = _rand_mx(rng, n, k, 90, 160)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    fq = _fq()
+    c1 = fq.gemm_mxfp4((a, asd), (b, bsd), reorganise=True)
+    c2 = fq.gemm_mxfp4((a, asd), (b, bsd), reorganise=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    rows = np.arange(0, m, max(1, m // 40))
+    _check(c1[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), ac, as_, bc, bs, k, rows=rows)
+
+
 def test_gemm_large_tiles_with_k_tail():
     """K not a multiple of 128 with enough rows and columns for 256 x 256
     tiles: the register-staged path with its zero-filled K tail; sampled rows
