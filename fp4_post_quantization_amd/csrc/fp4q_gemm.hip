@@ -532,16 +532,35 @@ hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, 
 }
 
 // Scale reorganisation ("3. QuTLASS" of the MR-GPTQ page reorganises scales for its FP4 product):
-// row-major E8M0 bytes [rows][k / 32] -> stage-major [k / 256][rows][8], one thread per (row, stage),
-// so that the product's per-stage scale loads read contiguous runs instead of 8 bytes per row.
-__global__ __launch_bounds__(256) void scales_to_stage_major_kernel(const uint8_t *__restrict__ src, int rows, int k,
-                                                                    uint8_t *__restrict__ dst) {
+// row-major E8M0 bytes [rows][k / 32] -> stage-major [k / 256][rows][8], so that the product's
+// per-stage scale loads read contiguous runs instead of 8 bytes per row.  One launch covers both
+// operands; a workgroup moves 64 rows x up to 64 stages through LDS, reading 8-byte pieces along
+// rows and writing them along stages, both coalesced.
+constexpr int kReoRows = 64, kReoStages = 64;
+
+__global__ __launch_bounds__(256) void scales_to_stage_major_kernel(const uint8_t *__restrict__ sa, int ra,
+                                                                    const uint8_t *__restrict__ sb, int rb, int k,
+                                                                    int blocks_a, uint8_t *__restrict__ da,
+                                                                    uint8_t *__restrict__ db) {
+  __shared__ uint2 tile[kReoStages][kReoRows];
   const int stages = k / 256;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)rows * stages) return;
-  const int r = (int)(t % rows), st = (int)(t / rows);
-  const uint2 v = *reinterpret_cast<const uint2 *>(src + (int64_t)r * (k / 32) + 8 * st);
-  *reinterpret_cast<uint2 *>(dst + ((int64_t)st * rows + r) * 8) = v;
+  const int chunks = (stages + kReoStages - 1) / kReoStages;
+  const bool is_a = (int)blockIdx.x < blocks_a;
+  const int b = is_a ? blockIdx.x : blockIdx.x - blocks_a;
+  const uint8_t *src = is_a ? sa : sb;
+  uint8_t *dst = is_a ? da : db;
+  const int rows = is_a ? ra : rb;
+  const int r0 = (b / chunks) * kReoRows, s0 = (b % chunks) * kReoStages;
+  const int nr = min(kReoRows, rows - r0), ns = min(kReoStages, stages - s0);
+  for (int e = threadIdx.x; e < nr * ns; e += 256) {
+    const int r = e / ns, st = e % ns;
+    tile[st][r] = *reinterpret_cast<const uint2 *>(src + (int64_t)(r0 + r) * (k / 32) + 8 * (s0 + st));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nr * ns; e += 256) {
+    const int st = e / nr, r = e % nr;
+    *reinterpret_cast<uint2 *>(dst + ((int64_t)(s0 + st) * rows + r0 + r) * 8) = tile[st][r];
+  }
 }
 
 // (m + n) rows of k / 32 scale bytes, plus 16 bytes read past the end by a clamped 16-byte scale load
@@ -558,11 +577,10 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
     // 256 x 256 tiles: reorganise both operands' scales stage-major first, so that each stage's scales
     // arrive in 1 KB loads (for smaller tiles the extra pass costs more than it saves: measured)
     uint8_t *was = ws, *wbs = ws + (int64_t)m * (k / 32) + 16;
-    const int64_t ta = (int64_t)m * (k / 256), tb = (int64_t)n * (k / 256);
-    hipLaunchKernelGGL(scales_to_stage_major_kernel, dim3((unsigned)((ta + 255) / 256)), dim3(256), 0, s, as, m, k,
-                       was);
-    hipLaunchKernelGGL(scales_to_stage_major_kernel, dim3((unsigned)((tb + 255) / 256)), dim3(256), 0, s, bs, n, k,
-                       wbs);
+    const int chunks = (k / 256 + kReoStages - 1) / kReoStages;
+    const int blocks_a = (m + kReoRows - 1) / kReoRows * chunks, blocks_b = (n + kReoRows - 1) / kReoRows * chunks;
+    hipLaunchKernelGGL(scales_to_stage_major_kernel, dim3(blocks_a + blocks_b), dim3(256), 0, s, as, m, bs, n, k,
+                       blocks_a, was, wbs);
     return launch_ring<2, 4, 4, 2, 2, OutT, 128, true>(a, was, b, wbs, m, n, k, alpha, c, ldc, s, true);
   }
   // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to half
@@ -678,8 +696,9 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
   if (workspace && need > 0) {
     if (workspace_bytes < (size_t)need) return FP4Q_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP4Q_ERR_ALIGN;
-    if (aligned(a_scales, 8) && aligned(b_scales, 8) && (m + n) * (k / 256) < ((int64_t)1 << 39))
-      ws = (uint8_t *)workspace;
+    const int64_t chunks = (k / 256 + kReoStages - 1) / kReoStages;
+    const int64_t blocks = ((m + kReoRows - 1) / kReoRows + (n + kReoRows - 1) / kReoRows) * chunks;
+    if (aligned(a_scales, 8) && aligned(b_scales, 8) && blocks < ((int64_t)1 << 31)) ws = (uint8_t *)workspace;
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;

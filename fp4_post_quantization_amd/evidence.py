@@ -47,8 +47,8 @@ COPY_BYTES = 256 * 2**20  # bench.py --copy-calib: one read and one write of 256
 
 # (N, K) of the projections of an 8B-shaped layer by GEMM kernel instantiation, and the widths of
 # its four activation inputs
-_W4A4_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 3, unsigned short, true>"
-_W4A4_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 4, unsigned short, true>"
+_W4A4_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, true, 128, true>"
+_W4A4_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 3, unsigned short, true, 128, false>"
 _W4A4_NK_BIG = [(4096, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
 _W4A4_NK_SMALL = [(1024, 4096), (1024, 4096)]
 _W4A4_IN = [4096, 4096, 4096, 14336]
