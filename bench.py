@@ -14,7 +14,9 @@ launches exactly that kernel).  Its ``traffic`` is the calibrated
 FETCH_SIZE + WRITE_SIZE bytes per launch recorded under profiles/ by
 ``python -m fp4_post_quantization_amd.evidence`` for the current kernel
 sources, or null when the kernels changed since.  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload on this host.  Before the warmup steps,
+bounded sample of the same workload on this host (one core on 2048 rows, and a
+pool of forked processes over the whole matrix), before the GPU is
+initialised.  Before the warmup steps,
 untimed steps run for 0.3 s so the GPU has left its idle clocks.
 
 Other workloads (for the design notes, not the headline line) are selected
@@ -87,19 +89,58 @@ def _rotating_copies(x, min_bytes=300 * 2**20, min_count=10):
     return bufs
 
 
-def cpu_baseline(x_cpu, imp, sample_rows, window=None, had=0, fmt="nvfp4"):
-    """The CPU oracle (numpy, one core) on the first ``sample_rows`` rows."""
+_POOL = {}
+
+
+def _oracle_rows(bounds):
+    """One worker of the all-cores CPU baseline: the oracle on rows [r0, r1)
+    of the shared matrix with the whole matrix's global scale."""
     from oracle import quant as Q
-    xs = x_cpu[:sample_rows].float().numpy()
+    r0, r1 = bounds
+    Q.quantize_nvfp4(_POOL["x"][r0:r1], _POOL["imp"], window=_POOL["window"], global_scale=_POOL["S"])
+    return r1 - r0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x_cpu, imp, sample_rows, window=None):
+    """The CPU oracle (numpy), unchanged, timed twice on this host: in one
+    process (one core) on the first ``sample_rows`` rows, and as a pool of
+    forked worker processes over row shards of the whole matrix (the
+    workload's global scale computed once).  Runs before the GPU is touched
+    (the pool forks)."""
+    import multiprocessing as mp
+    from oracle import quant as Q
+    x = x_cpu.float().numpy()
+    imp_np = None if imp is None else imp.numpy()
+    xs = x[:sample_rows]
     t0 = time.perf_counter()
-    if fmt == "nvfp4":
-        Q.quantize_nvfp4(xs, None if imp is None else imp.numpy(), window=window, hadamard_n=had)
-    else:
-        Q.quantize_mxfp4(xs, window=window, hadamard_n=had)
-    dt = time.perf_counter() - t0
-    return {"value": xs.size / dt / 1e9, "unit": "G elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample_rows} rows ({xs.size} elements) of the same workload, "
-                      f"{dt:.1f} s single-threaded numpy"}
+    Q.quantize_nvfp4(xs, imp_np, window=window)
+    dt1 = time.perf_counter() - t0
+    cores = min(16, len(os.sched_getaffinity(0)))
+    _POOL.update(x=x, imp=imp_np, window=window)
+    t0 = time.perf_counter()
+    _POOL["S"] = Q.global_scale_nvfp4(x)
+    rows = x.shape[0]
+    bounds = [(rows * i // cores, rows * (i + 1) // cores) for i in range(cores)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        done = sum(pool.map(_oracle_rows, bounds))
+    dtp = time.perf_counter() - t0
+    assert done == rows
+    return {"value": x.size / dtp / 1e9, "unit": "G elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {rows} x {x.shape[1]} workload in {cores} forked numpy processes (row shards, "
+                      f"global scale computed once): {dtp:.1f} s",
+            "single_core": {"value": xs.size / dt1 / 1e9, "cores": 1,
+                            "sample": f"first {sample_rows} rows ({xs.size} elements), {dt1:.1f} s in one process"},
+            "cpu_model": _cpu_model()}
 
 
 def prewarm(step, seconds=0.3):
@@ -142,10 +183,7 @@ def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
     return ms_step, ms_sweep
 
 
-def run_c2(args):
-    import torch
-    import workloads as W
-    x_cpu, imp_cpu = W.c2_weight_and_importance()
+def run_c2(args, x_cpu, imp_cpu, cpu_line):
     x = x_cpu.to("cuda:0")
     imp = imp_cpu.to("cuda:0")
     rows, cols = x.shape
@@ -186,8 +224,8 @@ def run_c2(args):
     rec = evidence.committed_traffic("c2")
     if rec:  # calibrated FETCH_SIZE + WRITE_SIZE of this kernel source, from profiles/
         line["roofline"]["traffic"] = round(rec["traffic_bytes"])
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x_cpu, imp_cpu, args.cpu_rows, window=window)
+    if cpu_line is not None:
+        line["cpu_baseline"] = cpu_line
     return line
 
 
@@ -422,10 +460,16 @@ def main():
               "(no sharding or collectives are built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
+    cpu_line = None
+    if args.config == "c2":
+        import workloads as W
+        x_cpu, imp_cpu = W.c2_weight_and_importance()
+        if not args.no_cpu_baseline:  # before the GPU is initialised: the CPU baseline forks
+            cpu_line = cpu_baseline(x_cpu, imp_cpu, args.cpu_rows, window=(-8, 7))
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    line = run_c2(args) if args.config == "c2" else run_other(args)
+    line = run_c2(args, x_cpu, imp_cpu, cpu_line) if args.config == "c2" else run_other(args)
     if args.copy_calib:
         copy_calibration()
     print(json.dumps(line), flush=True)
