@@ -23,6 +23,7 @@ Other workloads (for the design notes, not the headline line) are selected
 with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
 c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
+c5gate (one 70B-shaped gate projection, 16-point Hadamard + WMSE, repeated),
 focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8),
 study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage),
 gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight),
@@ -321,6 +322,18 @@ def run_other(args):
             del x
             torch.cuda.empty_cache()
         res.update(elements=n, ms_layer=total_ms, gel_s={k: n / v / 1e6 for k, v in total_ms.items()})
+    elif args.config == "c5gate":
+        # one 70B-shaped gate projection (28672 x 8192, 470 MB bf16) with H16 + WMSE, repeated: the c5
+        # kernel on a single shape (the c5 stream mixes seven)
+        x = W.c5_matrix(0, "gate", "cuda:0")
+        imp = W.c5_importance("gate").to("cuda:0")
+        out = fq.quantize_nvfp4(x, imp, hadamard_n=16, check=True)
+        step = lambda i: fq.quantize_nvfp4(x, imp, hadamard_n=16, out=out)
+        prewarm(step)
+        for i in range(args.warmup):
+            step(i)
+        ms = _events_time(step, args.steps)
+        res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6)
     elif args.config == "c5":
         imps = {name: W.c5_importance(name).to("cuda:0") for name in W.LAYER_70B}
         warm = W.c5_matrix(0, "k", "cuda:0")

@@ -54,6 +54,19 @@ _W4A4_NK_SMALL = [(1024, 4096), (1024, 4096)]
 _W4A4_IN = [4096, 4096, 4096, 14336]
 
 
+# NVFP4 W4A4 layer: bf16 ring instantiations (256 x 256 tiles: q, o, gate, up, down; 128 x 128: k, v)
+_W4A4NV_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, false, 128, false>"
+_W4A4NV_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 4, unsigned short, false, 64, false>"
+# decode passes: per product one of A (8192 x K) and one of B (N x K): codes + scales in, bf16 out
+_W4A4NV_DECODE = [8192 * k for n, k in _W4A4_NK_BIG + _W4A4_NK_SMALL] + [n * k for n, k in
+                                                                         _W4A4_NK_BIG + _W4A4_NK_SMALL]
+
+
+def _bf16_gemm_mean(nks, what, m=8192):
+    vals = [2 * m * n * k if what == "flops" else (m + n) * k * 2 + m * n * 2 for n, k in nks]
+    return sum(vals) / len(vals)
+
+
 def _gemm_mean(nks, what, m=8192):
     vals = [2 * m * n * k if what == "flops" else m * k * (0.5 + 1 / 32) + n * k * (0.5 + 1 / 32) + m * n * 2
             for n, k in nks]
@@ -88,6 +101,26 @@ WORKLOADS = {
                            _W4A4_SMALL: _gemm_mean(_W4A4_NK_SMALL, "flops")},
              "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
              "peak_tflops": 10100.0, "sources": GEMM_SOURCES},
+    "w4a4nv": {"stem": "nvfp4_w4a4_gemm_8b_layer_8192tok", "kernel": _W4A4NV_BIG,
+               "title": "W4A4 NVFP4 layer (8B shapes, 8192 tokens): bf16-decoded operands on the bf16 matrix cores",
+               "alg_bytes": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "bytes"),
+                             _W4A4NV_SMALL: _bf16_gemm_mean(_W4A4_NK_SMALL, "bytes"),
+                             "nvfp4_to_bf16_kernel": sum(e * (0.5 + 1 / 16 + 2) for e in _W4A4NV_DECODE)
+                             / len(_W4A4NV_DECODE)},
+               "alg_flops": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "flops"),
+                             _W4A4NV_SMALL: _bf16_gemm_mean(_W4A4_NK_SMALL, "flops")},
+               "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
+               "peak_tflops": 2500.0, "sources": GEMM_SOURCES},
+    # FOCUS forward quantizer on the c2 weight: x (bf16), FP16 coefficients per 8, E4M3 scales in;
+    # codes and the float32 dequantized output out
+    "focus": {"stem": "focus_relaxed_bf16_4096x4096", "kernel": "relaxed_quant_kernel",
+              "title": "FOCUS forward quantizer, NVFP4, bf16 4096x4096, sub-blocks of 8, dequantized output",
+              "alg_bytes": {"relaxed_quant_kernel": 4096 * 4096 * (2 + 2 / 8 + 1 / 16 + 0.5 + 4)}},
+    # one 70B-shaped gate projection with a fused 16-point Hadamard and the WMSE sweep
+    "c5gate": {"stem": "nvfp4_wmse_h16_bf16_28672x8192", "kernel": "nvfp4_sweep_kernel",
+               "title": "NVFP4 WMSE ScaleSweep after a 16-point block Hadamard, bf16 28672x8192 (70B gate)",
+               "alg_bytes": {"nvfp4_sweep_kernel": 28672 * 8192 * (2 + 0.5 + 6 / 16),
+                             "amax_chunks_kernel": 28672 * 8192 * 2}},
     "c3a": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 AbsMax window [0,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
