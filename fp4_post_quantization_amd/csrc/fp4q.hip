@@ -258,10 +258,11 @@ __device__ __forceinline__ float loss_of_codes(const float us[16], const float w
 
 // Keep the candidate with the least loss; among equal losses the smallest
 // pattern / exponent, whatever order the candidates are visited in.
-__device__ __forceinline__ void consider(float L, int p, bool ok, float &Lbest, int &pbest) {
+__device__ __forceinline__ bool consider(float L, int p, bool ok, float &Lbest, int &pbest) {
   const bool take = ok & ((L < Lbest) | ((L == Lbest) & (p < pbest)));
   Lbest = take ? L : Lbest;
   pbest = take ? p : pbest;
+  return take;
 }
 
 // ScaleSweep candidate search for one block (this lane's 16 elements).
@@ -338,7 +339,7 @@ template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   __shared__ float Vtab[128], Rtab[128];
   __shared__ uint32_t red[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
 
   if (tid < 128) {
     Vtab[tid] = kE4M3.v[tid];
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
   const float SS = S * S;
 
-  const int tile = blockIdx.x * kWaves + wave;
+  const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
   if (tile >= a.ntiles) return;
   const int band = tile % a.nbands, rg = tile / a.nbands;
   const int c = band * 64 + lane;
@@ -442,12 +443,64 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   }
 }
 
+// MXFP4 exponent sweep for one block (this lane's 16 elements and its
+// partner lane's): exponents E and E + 1 pair up, E + 1 converted from the
+// products of E with the halving scale.  Returns E*; Lbest gets its loss
+// and, KEEP, b0 / b1 its codes.
+template <bool WMSE, bool KEEP>
+__device__ __forceinline__ int mx_sweep(const float z[16], const float w[16], int eb, int lo, int hi, float &Lbest,
+                                        uint32_t &b0, uint32_t &b1) {
+  Lbest = __builtin_inff();
+  int ebest = max(-127, eb + lo);
+  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
+  for (int o = lo; o <= hi; o += 2) {
+    const int E = eb + o;
+    const bool ok = (E >= -127) & (E <= 127);
+    const int Ec = min(max(E, -127), 127);
+    const float down = pow2f(-Ec);
+    float y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = z[i] * down;
+    k0 = cvt8<false>(y, k0);
+    k1 = cvt8<false>(y + 8, k1);
+    if (o + 1 <= hi) {
+      const int E1 = E + 1;
+      const bool ok1 = (E1 >= -127) & (E1 <= 127);
+      const int E1c = min(max(E1, -127), 127);
+      if (E >= -127) {
+        h0 = cvt8<true>(y, h0);
+        h1 = cvt8<true>(y + 8, h1);
+      } else {  // lower member clamped: convert the upper one directly
+        const float d1 = pow2f(-E1c);
+        float y2[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y2[i] = z[i] * d1;
+        h0 = cvt8<false>(y2, h0);
+        h1 = cvt8<false>(y2 + 8, h1);
+      }
+      const float half1 = loss_of_codes<WMSE>(z, w, h0, h1, pow2f(E1c));
+      const bool t1 = consider(half1 + xor_lane<1>(half1), E1, ok1, Lbest, ebest);
+      if constexpr (KEEP) {
+        b0 = t1 ? h0 : b0;
+        b1 = t1 ? h1 : b1;
+      }
+    }
+    const float half0 = loss_of_codes<WMSE>(z, w, k0, k1, pow2f(Ec));
+    const bool t0 = consider(half0 + xor_lane<1>(half0), E, ok, Lbest, ebest);
+    if constexpr (KEEP) {
+      b0 = t0 ? k0 : b0;
+      b1 = t0 ? k1 : b1;
+    }
+  }
+  return ebest;
+}
+
 // MXFP4 exponent sweep: two adjacent lanes per 32-element block.  Exponents
 // E and E + 1 form pairs: fp32(x * 2^-(E+1)) = fp32(x * 2^-E) / 2.
 template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x * kWaves + wave;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
   if (tile >= a.ntiles) return;
   const int band = tile % a.nbands, rg = tile / a.nbands;
   const int c = band * 64 + lane;
@@ -468,9 +521,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   const int bpr = a.cpr / 2;
   const bool even = (lane & 1) == 0;
   const int lo = a.off_lo, hi = a.off_hi;
+  // short windows keep the winner's codes (two selects per candidate) instead of converting again
+  const bool keep = hi - lo < 8;
   Raw<T> cur, nxt;
   load_raw(xc + (int64_t)r0 * a.ld, cur);
-  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
   for (int r = r0; r < r1; ++r) {
     if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
     float z[16];
@@ -478,57 +532,35 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
     if constexpr (HAD != 0) fwht<HAD>(z, lane);
 
     float amax = 0.0f;
-    bool finite = true;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      finite &= fabsf(z[i]) <= 3.402823466e38f;
-      amax = fmaxf(amax, fabsf(z[i]));
-    }
-    if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(z[i]));
     amax = fmaxf(amax, xor_lane<1>(amax));
     const int eb = mx_base_exponent(amax);
-    const int elo = max(-127, eb + lo);
 
-    float Lbest = __builtin_inff();
-    int ebest = elo;
-    for (int o = lo; o <= hi; o += 2) {
-      const int E = eb + o;
-      const bool ok = (E >= -127) & (E <= 127);
-      const int Ec = min(max(E, -127), 127);
-      const float down = pow2f(-Ec);
+    float Lbest;
+    uint32_t b0 = 0, b1 = 0;  // codes of the best candidate (short windows)
+    const int ebest = keep ? mx_sweep<WMSE, true>(z, w, eb, lo, hi, Lbest, b0, b1)
+                           : mx_sweep<WMSE, false>(z, w, eb, lo, hi, Lbest, b0, b1);
+
+    // A non-finite element makes its e, and so every candidate's loss, NaN or infinite (the terms
+    // t * e are never negative), so a finite best loss proves the block finite; the elementwise
+    // test runs only when it is not (an overflowing loss of finite data also lands there).
+    const bool lfin = Lbest <= 3.402823466e38f;
+    if (!lfin) {
+      bool finite = true;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
+      if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+    }
+    uint32_t k0 = b0, k1 = b1;  // a finite best loss was taken, and its codes with it
+    if (!(keep & lfin)) {
+      const float db = pow2f(-ebest);
       float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = z[i] * down;
-      k0 = cvt8<false>(y, k0);
-      k1 = cvt8<false>(y + 8, k1);
-      if (o + 1 <= hi) {
-        const int E1 = E + 1;
-        const bool ok1 = (E1 >= -127) & (E1 <= 127);
-        const int E1c = min(max(E1, -127), 127);
-        if (E >= -127) {
-          h0 = cvt8<true>(y, h0);
-          h1 = cvt8<true>(y + 8, h1);
-        } else {  // lower member clamped: convert the upper one directly
-          const float d1 = pow2f(-E1c);
-          float y2[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) y2[i] = z[i] * d1;
-          h0 = cvt8<false>(y2, h0);
-          h1 = cvt8<false>(y2 + 8, h1);
-        }
-        const float half1 = loss_of_codes<WMSE>(z, w, h0, h1, pow2f(E1c));
-        consider(half1 + xor_lane<1>(half1), E1, ok1, Lbest, ebest);
-      }
-      const float half0 = loss_of_codes<WMSE>(z, w, k0, k1, pow2f(Ec));
-      consider(half0 + xor_lane<1>(half0), E, ok, Lbest, ebest);
+      for (int i = 0; i < 16; ++i) y[i] = z[i] * db;
+      k0 = cvt8<false>(y, 0u);
+      k1 = cvt8<false>(y + 8, 0u);
     }
-
-    const float db = pow2f(-ebest);
-    float y[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = z[i] * db;
-    k0 = cvt8<false>(y, k0);
-    k1 = cvt8<false>(y + 8, k1);
     *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
     if (even) {
       const int64_t bi = (int64_t)r * bpr + (c >> 1);
@@ -537,6 +569,23 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
       if (a.offs) a.offs[bi] = (int8_t)(ebest - eb);
     }
     cur = nxt;
+  }
+}
+
+// 16 floats of chunk c of an output row (row stride 16 cpr floats).  When
+// the row length is a multiple of 64 chunks, a wave's 64 chunks are one
+// contiguous 4 KB run and go out as four 1 KB stores through LDS.
+__device__ __forceinline__ void store_chunk_f32(float *row, int c, int cpr, int lane, const float v[16]) {
+  u32x4 q[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) q[k] = u32x4{as_u(v[4 * k]), as_u(v[4 * k + 1]), as_u(v[4 * k + 2]), as_u(v[4 * k + 3])};
+  if ((cpr & 63) == 0) {
+    __shared__ WaveStage<4> stage[kWaves];
+    wave_store<4>(reinterpret_cast<u32x4 *>(row) + 4 * (c - lane), q, lane, stage[threadIdx.x >> 6]);
+  } else {
+    u32x4 *o = reinterpret_cast<u32x4 *>(row) + 4 * c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = q[k];
   }
 }
 
@@ -552,9 +601,10 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
                                                                   uint8_t *__restrict__ codes,
                                                                   float *__restrict__ dq,
                                                                   uint32_t *__restrict__ status) {
-  const int g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= total) return;
-  const int r = g / cpr, c = g - r * cpr;
+  const int lane = threadIdx.x & 63;
+  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  int r, c;
+  if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
   float z[16];
   load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
 
@@ -608,9 +658,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
       const float m = q[i] * V;  // exact
       v[i] = FMT == FP4Q_NVFP4 ? m * S : m;
     }
-    f32x4 *o = reinterpret_cast<f32x4 *>(dq + (int64_t)r * cols + (int64_t)c * 16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = f32x4{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
+    store_chunk_f32(dq + (int64_t)r * cols, c, cpr, lane, v);
   }
 }
 
@@ -864,9 +912,10 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
                                                             const uint8_t *__restrict__ scales,
                                                             const float *__restrict__ gscale, int cpr,
                                                             int cols, int total, float *__restrict__ out) {
-  const int g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= total) return;
-  const int r = g / cpr, c = g - r * cpr;
+  const int lane = threadIdx.x & 63;
+  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  int r, c;
+  if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
   const uint2 pk = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)c * 8);
   float scale, S = 1.0f;
   if constexpr (FMT == FP4Q_NVFP4) {
@@ -884,23 +933,21 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
     if constexpr (FMT == FP4Q_NVFP4) mag = mag * S;
     v[i] = (code & 8u) ? -mag : mag;
   }
-  float4 *o = reinterpret_cast<float4 *>(out + (int64_t)r * cols + (int64_t)c * 16);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  store_chunk_f32(out + (int64_t)r * cols, c, cpr, lane, v);
 }
 
 template <typename T, int HAD>
 __global__ __launch_bounds__(kThreads) void hadamard_kernel(const T *__restrict__ x, int64_t ld, int cpr,
                                                              int cols, int total, float *__restrict__ out) {
-  const int g = blockIdx.x * kThreads + threadIdx.x;
-  if (g >= total) return;  // whole groups end together: total is a multiple of HAD/16
-  const int r = g / cpr, c = g - r * cpr;
+  const int lane = threadIdx.x & 63;
+  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  int r, c;
+  // whole groups end together: total is a multiple of HAD/16
+  if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
   float z[16];
   load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
-  fwht<HAD>(z, threadIdx.x & 63);
-  float4 *o = reinterpret_cast<float4 *>(out + (int64_t)r * cols + (int64_t)c * 16);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+  fwht<HAD>(z, lane);
+  store_chunk_f32(out + (int64_t)r * cols, c, cpr, lane, z);
 }
 
 // ============================================================ dispatch ===

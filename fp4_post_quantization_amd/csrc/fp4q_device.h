@@ -78,6 +78,58 @@ __device__ __forceinline__ void load16(const T *p, float z[16]) {
   widen(r, z);
 }
 
+// ------------------------------------------------ wide row stores ----
+// Flat chunk g0 + lane of a matrix with cpr chunks per row: row r and
+// chunk c, from a wave-uniform g0 (a multiple of 64) with one scalar
+// division per wave.  Returns false for lanes past total.
+__device__ __forceinline__ bool lane_chunk(int64_t g0, int lane, int cpr, int64_t total, int &r, int &c) {
+  const int64_t r0 = g0 / cpr;
+  int cc = (int)(g0 - r0 * cpr) + lane;
+  int rr = (int)r0;
+  if (cpr >= 64) {
+    const bool wrap = cc >= cpr;
+    rr += wrap;
+    cc -= wrap ? cpr : 0;
+  } else {
+    const int q = cc / cpr;
+    rr += q;
+    cc -= q * cpr;
+  }
+  r = rr;
+  c = cc;
+  return g0 + lane < total;
+}
+
+// Per-wave LDS staging for wave_store: NQ 16-byte quads per lane plus one
+// quad of padding per 16 (bank spread).
+template <int NQ>
+struct WaveStage {
+  u32x4 q[64 * NQ + 4 * NQ];
+};
+
+// Stores lane l's NQ quads to dst[NQ l .. NQ l + NQ) for all 64 lanes of a
+// wave, whose outputs form one contiguous run of 64 NQ quads.  One lane per
+// chunk would write 16 bytes every 16 NQ bytes per instruction; going
+// through LDS, each store instruction writes 1 KB contiguously, and the
+// stores are marked non-temporal (the output is not read again here).
+// Every lane of the wave must take part.
+template <int NQ>
+__device__ __forceinline__ void wave_store(u32x4 *dst, const u32x4 (&v)[NQ], int lane, WaveStage<NQ> &st) {
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int j = NQ * lane + k;
+    st.q[j + (j >> 4)] = v[k];
+  }
+  // lanes read what other lanes of the same wave wrote: LDS operations of a wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int j = 64 * k + lane;
+    __builtin_nontemporal_store(st.q[j + (j >> 4)], dst + j);
+  }
+}
+
 // ------------------------------------------------- cross-lane moves ----
 // Value held by lane (lane ^ M) of the wave, M in {1, 2, 4}.
 // Value of lane (l & ~15) + N, i.e. lane N of the caller's 16-lane DPP row
@@ -102,6 +154,10 @@ __device__ __forceinline__ float xor_lane(float v) {
   }
   return __int_as_float(r);
 }
+
+// Index of the caller's wave in its workgroup, as a wave-uniform (scalar)
+// value: tile arithmetic and row loops derived from it run on the scalar unit.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

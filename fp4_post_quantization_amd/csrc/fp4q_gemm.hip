@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp4q_device.h"
 #include "fp4q_gemm.h"
 
 namespace fp4q_gemm {
@@ -617,15 +618,19 @@ __device__ __forceinline__ float e4m3_decode(uint32_t b) {
   return (b & 0x80u) ? -v : v;
 }
 
-// One lane per 16-element block: 8 code bytes + 1 scale byte -> 16 bfloat16 values (two 16-byte
-// stores).  Blocks past K (up to kp, a multiple of 32) are written as zeros.
+// One lane per 16-element block: 8 code bytes + 1 scale byte -> 16 bfloat16 values (32 bytes).
+// Blocks past K (up to kp, a multiple of 32) are written as zeros.  When a row holds a multiple of
+// 64 blocks, a wave's output is one contiguous 2 KB run, stored in 1 KB pieces through LDS.
 __global__ __launch_bounds__(256) void nvfp4_to_bf16_kernel(const uint8_t *__restrict__ codes,
                                                             const uint8_t *__restrict__ scales, int rows, int k,
                                                             int kp, uint16_t *__restrict__ out) {
   const int bpr = kp / 16;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (int64_t)rows * bpr) return;
-  const int r = (int)(t / bpr), blk = (int)(t % bpr);
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = (int64_t)blockIdx.x * 256 + 64 * fp4q::wave_index();
+  int r, blk;
+  const bool valid = fp4q::lane_chunk(t0, lane, bpr, (int64_t)rows * bpr, r, blk);
+  const bool whole = (bpr & 63) == 0;  // then every lane of a wave is valid or none is
+  if (!valid) return;
   uint32_t w[8];
   if (blk * 16 < k) {
     const uint2 c = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (k / 2) + blk * 8);
@@ -649,9 +654,15 @@ __global__ __launch_bounds__(256) void nvfp4_to_bf16_kernel(const uint8_t *__res
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = 0;
   }
-  uint4 *dst = reinterpret_cast<uint4 *>(out + (int64_t)r * kp + blk * 16);
-  dst[0] = uint4{w[0], w[1], w[2], w[3]};
-  dst[1] = uint4{w[4], w[5], w[6], w[7]};
+  const fp4q::u32x4 q[2] = {fp4q::u32x4{w[0], w[1], w[2], w[3]}, fp4q::u32x4{w[4], w[5], w[6], w[7]}};
+  fp4q::u32x4 *row = reinterpret_cast<fp4q::u32x4 *>(out + (int64_t)r * kp);
+  if (whole) {
+    __shared__ fp4q::WaveStage<2> stage[4];
+    fp4q::wave_store<2>(row + 2 * (blk - lane), q, lane, stage[threadIdx.x >> 6]);
+  } else {
+    row[2 * blk] = q[0];
+    row[2 * blk + 1] = q[1];
+  }
 }
 
 template <typename OutT>
