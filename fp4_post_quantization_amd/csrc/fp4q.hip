@@ -60,13 +60,45 @@ __constant__ E4M3Tables kE4M3 = make_e4m3_tables();
 // Global scale of an empty NVFP4 tensor (max over nothing = 0).
 __global__ void zero_scale_kernel(float *global_scale) { *global_scale = 0.0f; }
 
+// Where the global-max pass puts its results.
+struct AmaxOut {
+  uint32_t *partials;  // [gridDim.x] per-workgroup maxima
+  uint32_t *status;
+  const float *imp;    // importance [imp_n] to validate, or null
+  int imp_n;
+};
+
+// End of a global-max pass: m is this thread's maximum |bits|; the
+// workgroup's maximum goes to partials[blockIdx.x].  The workgroups also
+// validate the importance vector between them (a strided slice each), so
+// the quantizer that follows need not.
+__device__ void finish_amax(uint32_t m, const AmaxOut &o) {
+  __shared__ uint32_t red[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (o.imp) {
+    bool ok = true;
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < o.imp_n; i += gridDim.x * kThreads)
+      ok &= (o.imp[i] >= 0.0f) & (o.imp[i] <= 3.402823466e38f);
+    if (!ok) atomicOr(o.status, FP4Q_DATA_BAD_IMPORTANCE);
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
+    o.partials[blockIdx.x] = r;
+  }
+}
+
 // Per-workgroup maximum of |x| (after the optional rotation) as a float32
 // bit pattern.  Integer order of |bits| is float order for finite values,
 // and any Inf/NaN yields a pattern >= 0x7F800000.
 template <typename T, int HAD>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const T *__restrict__ x, int64_t ld, int cpr,
-                                                         int total, uint32_t *__restrict__ partials) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                         int total, AmaxOut o) {
+  const int lane = threadIdx.x & 63;
   uint32_t m = 0;
   const int stride = gridDim.x * kThreads;
   for (int g = blockIdx.x * kThreads + threadIdx.x; g < total; g += stride) {
@@ -80,16 +112,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const T *__restrict__ x,
       m = b > m ? b : m;
     }
   }
-  m = wave_max_u32(m);
-  __shared__ uint32_t red[kWaves];
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = red[i] > r ? red[i] : r;
-    partials[blockIdx.x] = r;
-  }
+  finish_amax(m, o);
 }
 
 // Same maximum for a contiguous, unrotated matrix viewed as n_vec 16-byte
@@ -111,7 +134,7 @@ __device__ __forceinline__ uint32_t fold_abs_bits(uint32_t m, u32x4 v) {
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const u32x4 *__restrict__ v, int64_t n_vec,
-                                                              uint32_t *__restrict__ partials) {
+                                                              AmaxOut o) {
   constexpr int U = 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -125,17 +148,7 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const u32x4 *__rest
   }
   for (; i < n_vec; i += stride) m = fold_abs_bits<T>(m, v[i]);
   if constexpr (sizeof(T) == 2) m <<= 16;  // bf16 pattern -> float32 pattern
-  m = wave_max_u32(m);
-  __shared__ uint32_t red[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
-    partials[blockIdx.x] = r;
-  }
+  finish_amax(m, o);
 }
 
 // Maximum of |rotated x| for a contiguous matrix viewed as total chunks of
@@ -146,9 +159,9 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const u32x4 *__rest
 // branch together.
 template <typename T, int HAD>
 __global__ __launch_bounds__(kThreads) void amax_chunks_kernel(const T *__restrict__ x, int64_t total,
-                                                                uint32_t *__restrict__ partials) {
+                                                                AmaxOut o) {
   constexpr int U = 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t m = 0;
@@ -174,16 +187,7 @@ __global__ __launch_bounds__(kThreads) void amax_chunks_kernel(const T *__restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = max(m, as_u(z[i]) & 0x7FFFFFFFu);
   }
-  m = wave_max_u32(m);
-  __shared__ uint32_t red[kWaves];
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
-    partials[blockIdx.x] = r;
-  }
+  finish_amax(m, o);
 }
 
 struct SweepArgs {
@@ -195,6 +199,7 @@ struct SweepArgs {
   int rows_per_tile, nbands, ntiles;
   const uint32_t *partials;     // amax partials (NVFP4, computed scale)
   int n_partials;
+  bool check_imp;               // validate the importance (no global-max pass did)
   const float *given_scale;     // NVFP4 with FP4Q_GIVEN_SCALE, else null
   uint8_t *codes, *scales;
   float *gscale_out;            // NVFP4 global scale output (computed scale)
@@ -338,39 +343,38 @@ __device__ __forceinline__ int nv_sweep(const float us[16], const float w[16], i
 template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   __shared__ float Vtab[128], Rtab[128];
-  __shared__ uint32_t red[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
 
   if (tid < 128) {
     Vtab[tid] = kE4M3.v[tid];
     Rtab[tid] = kE4M3.r[tid];
   }
-  uint32_t amax_bits = 0;
-  if (!a.given_scale) {
-    for (int i = tid; i < a.n_partials; i += kThreads) {
-      const uint32_t p = a.partials[i];
-      amax_bits = p > amax_bits ? p : amax_bits;
+  // wave 0 finds S and S_inv (the maximum of the global-max partials, or the given scale) for the
+  // workgroup
+  __shared__ float sc[2];
+  if (wave == 0) {
+    float S;
+    if (a.given_scale) {
+      S = *a.given_scale;
+      if (blockIdx.x == 0 && lane == 0 && (!(S >= 0.0f) || isinf(S)))
+        atomicOr(a.status, FP4Q_DATA_BAD_GLOBAL_SCALE);
+    } else {
+      uint32_t m = 0;
+      for (int i = lane; i < a.n_partials; i += 64) m = max(m, a.partials[i]);
+      m = wave_max_u32(m);
+      S = as_f(m) / 1536.0f;  // max|x| / (256 * 6), correctly rounded
+      if (blockIdx.x == 0 && lane == 0) {
+        *a.gscale_out = S;
+        if (m >= 0x7F800000u) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+      }
     }
-    amax_bits = wave_max_u32(amax_bits);
-    if (lane == 0) red[wave] = amax_bits;
+    if (lane == 0) {
+      sc[0] = S;
+      sc[1] = (S == 0.0f) ? 0.0f : 1.0f / S;
+    }
   }
   __syncthreads();
-  float S;
-  if (a.given_scale) {
-    S = *a.given_scale;
-    if (blockIdx.x == 0 && tid == 0 && (!(S >= 0.0f) || isinf(S)))
-      atomicOr(a.status, FP4Q_DATA_BAD_GLOBAL_SCALE);
-  } else {
-    amax_bits = red[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) amax_bits = red[i] > amax_bits ? red[i] : amax_bits;
-    S = as_f(amax_bits) / 1536.0f;  // max|x| / (256 * 6), correctly rounded
-    if (blockIdx.x == 0 && tid == 0) {
-      *a.gscale_out = S;
-      if (amax_bits >= 0x7F800000u) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
-    }
-  }
-  const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
+  const float S = sc[0], S_inv = sc[1];
   const float SS = S * S;
 
   const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   if constexpr (WMSE) {
     if (active) {
       load_importance(a.imp + (int64_t)c * 16, w);
-      if (!importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+      if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
     }
   }
   if (!active) return;  // whole Hadamard groups are active or not together
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   if constexpr (WMSE) {
     if (active) {
       load_importance(a.imp + (int64_t)c * 16, w);
-      if (!importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+      if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
     }
   }
   if (!active) return;
@@ -690,6 +694,7 @@ __global__ __launch_bounds__(kThreads) void scale_from_partials_kernel(const uin
     if (m >= 0x7F800000u) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
   }
 }
+
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -985,6 +990,43 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
   return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);
 }
 
+static AmaxOut amax_out(void *workspace, const float *imp, int imp_n) {
+  char *b = (char *)workspace;
+  return AmaxOut{(uint32_t *)(b + kWsPartials), (uint32_t *)(b + kWsStatus), imp, imp_n};
+}
+
+// Global-max pass over x (after the optional rotation): per-workgroup
+// maxima into the workspace.  Returns their number.
+static int launch_amax(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols, int64_t ld, int hadamard_n,
+                       const AmaxOut &ao, hipStream_t s) {
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
+  if (hadamard_n == 0 && ld == cols) {
+    const int64_t n_vec = rows * cols * (dtype == FP4Q_BF16 ? 2 : 4) / 16;
+    const int n = (int)std::min<int64_t>(kAmaxGroups, (n_vec + kThreads * 8 - 1) / (kThreads * 8));
+    if (dtype == FP4Q_BF16)
+      hipLaunchKernelGGL((amax_flat_kernel<uint16_t>), dim3(n), dim3(kThreads), 0, s, (const u32x4 *)x, n_vec, ao);
+    else
+      hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n), dim3(kThreads), 0, s, (const u32x4 *)x, n_vec, ao);
+    return n;
+  }
+  const int n = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
+  with_dtype(dtype, [&](auto tp) {
+    using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
+    with_had(hadamard_n, [&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      if (ld == cols) {
+        if constexpr (H != 0)
+          hipLaunchKernelGGL((amax_chunks_kernel<T, H>), dim3(n), dim3(kThreads), 0, s, (const T *)x, (int64_t)total,
+                             ao);
+      } else {
+        hipLaunchKernelGGL((amax_kernel<T, H>), dim3(n), dim3(kThreads), 0, s, (const T *)x, ld, cpr, total, ao);
+      }
+    });
+  });
+  return n;
+}
+
 }  // namespace fp4q
 
 // ============================================================ C ABI ======
@@ -1054,7 +1096,6 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
   const bool given = flags & FP4Q_GIVEN_SCALE;
 
   if (rows == 0 || cols == 0) {
@@ -1064,41 +1105,9 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
 
   const int cpr = (int)(cols / 16);
   const int total = (int)(rows * cpr);
-  int n_partials = 0;
-  if (!given) {
-    const int64_t esz = dtype == FP4Q_BF16 ? 2 : 4;
-    if (hadamard_n == 0 && ld == cols) {
-      const int64_t n_vec = rows * cols * esz / 16;
-      n_partials = std::min<int64_t>(kAmaxGroups, (n_vec + kThreads * 8 - 1) / (kThreads * 8));
-      if (dtype == FP4Q_BF16)
-        hipLaunchKernelGGL((amax_flat_kernel<uint16_t>), dim3(n_partials), dim3(kThreads), 0, s,
-                           (const u32x4 *)x, n_vec, partials);
-      else
-        hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n_partials), dim3(kThreads), 0, s,
-                           (const u32x4 *)x, n_vec, partials);
-    } else if (ld == cols) {
-      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
-      with_dtype(dtype, [&](auto tp) {
-        using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
-        with_had(hadamard_n, [&](auto hc) {
-          constexpr int H = decltype(hc)::value;
-          if constexpr (H != 0)
-            hipLaunchKernelGGL((amax_chunks_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x,
-                               (int64_t)total, partials);
-        });
-      });
-    } else {
-      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
-      with_dtype(dtype, [&](auto tp) {
-        using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
-        with_had(hadamard_n, [&](auto hc) {
-          constexpr int H = decltype(hc)::value;
-          hipLaunchKernelGGL((amax_kernel<T, H>), dim3(n_partials), dim3(kThreads), 0, s, (const T *)x, ld,
-                             cpr, total, partials);
-        });
-      });
-    }
-  }
+  const int n_partials =
+      given ? 0 : launch_amax(x, dtype, rows, cols, ld, hadamard_n, amax_out(workspace, wmse ? importance : nullptr,
+                                                                                      (int)cols), s);
 
   SweepArgs a;
   a.x = x;
@@ -1112,8 +1121,9 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   a.nbands = ceil_div(cpr, 64);
   a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands, kNvTileTarget);
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
-  a.partials = partials;
+  a.partials = (const uint32_t *)((const char *)workspace + kWsPartials);
   a.n_partials = n_partials;
+  a.check_imp = given;  // else the global-max pass validates the importance
   a.given_scale = given ? global_scale : nullptr;
   a.codes = codes;
   a.scales = scales;
@@ -1173,6 +1183,7 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
   a.partials = nullptr;
   a.n_partials = 0;
+  a.check_imp = true;
   a.given_scale = nullptr;
   a.codes = codes;
   a.scales = scales;
@@ -1261,22 +1272,10 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
   const bool given = flags & FP4Q_GIVEN_SCALE;
-  const int cpr = (int)(cols / 16);
-  const int total = (int)(rows * cpr);
   if (!given) {
-    int n_partials;
-    if (ld == cols) {
-      const int64_t n_vec = rows * cols * 4 / 16;
-      n_partials = (int)std::min<int64_t>(kAmaxGroups, (n_vec + kThreads * 8 - 1) / (kThreads * 8));
-      hipLaunchKernelGGL((amax_flat_kernel<float>), dim3(n_partials), dim3(kThreads), 0, s, (const u32x4 *)w,
-                         n_vec, partials);
-    } else {
-      n_partials = std::min(kAmaxGroups, ceil_div(total, kThreads * 4));
-      hipLaunchKernelGGL((amax_kernel<float, 0>), dim3(n_partials), dim3(kThreads), 0, s, (const float *)w, ld,
-                         cpr, total, partials);
-    }
+    uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
+    const int n_partials = launch_amax(w, FP4Q_F32, rows, cols, ld, 0, amax_out(workspace, nullptr, 0), s);
     hipLaunchKernelGGL(scale_from_partials_kernel, dim3(1), dim3(kThreads), 0, s, partials, n_partials,
                        global_scale, status);
   }
