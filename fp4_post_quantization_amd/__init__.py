@@ -295,14 +295,16 @@ def block_hadamard(x, n, out=None):
     return out
 
 
-def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_buf=None, reorganise=True):
+def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_buf=None, use_workspace=True):
     """C = alpha * A_hat @ B_hat^T for MXFP4 operands (W4A4).
 
     ``a`` and ``b`` are MXFP4Result (or (codes, scales) pairs) as written by
     ``quantize_mxfp4``: A is M x K (activations), B is N x K (weights).
-    Returns C [M, N] in float32 or bfloat16.  With ``reorganise`` (and K a
-    multiple of 256) the scales are first copied stage-major into a
-    workspace (``workspace_buf`` or a fresh one); the result is the same."""
+    Returns C [M, N] in float32 or bfloat16.  With ``use_workspace`` (and K
+    a multiple of 256) the library gets a workspace (``workspace_buf`` or a
+    fresh one): large products copy the scales stage-major into it (same
+    result), few-token products (M <= 64) split K and keep their partial
+    sums there (added in K order: the result can differ in rounding)."""
     lib = L.load()
     ac, as_ = (a.codes, a.scales) if isinstance(a, MXFP4Result) else a
     bc, bs = (b.codes, b.scales) if isinstance(b, MXFP4Result) else b
@@ -320,7 +322,7 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
     if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     code = L.F32 if out.dtype == torch.float32 else L.BF16
-    need = lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) if reorganise else 0
+    need = lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) if use_workspace else 0
     if need and (workspace_buf is None or workspace_buf.numel() < need):
         workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,

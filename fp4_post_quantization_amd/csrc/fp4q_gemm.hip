@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fp4q_device.h"
 #include "fp4q_gemm.h"
 
@@ -292,6 +294,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
   const int l32 = lane & 31, h = lane >> 5;
+  // split K (blockIdx.y): this workgroup sums stages [sp nst, (sp + 1) nst) into its own M x ldc
+  // partial (row-major scales only)
+  if (gridDim.y > 1) {
+    const int64_t sp = blockIdx.y;
+    A += sp * nst * ROWB;
+    B += sp * nst * ROWB;
+    As += sp * nst * sl.a_stage;
+    Bs += sp * nst * sl.b_stage;
+    C += sp * M * ldc;
+  }
 
   // per-lane source addresses of the loads (advanced by ROWB code bytes / SPR scale bytes per stage)
   const uint8_t *srcA[A_INSTR];
@@ -504,19 +516,42 @@ hipError_t launch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const u
 }
 
 // MXFP4 operands; k a multiple of 2 * ROWB (a stage holds ROWB code bytes = 2 * ROWB elements per
-// row).  staged: the scales were reorganised stage-major (as / bs point into that copy).
+// row).  staged: the scales were reorganised stage-major (as / bs point into that copy).  splits > 1
+// (row-major scales, k a multiple of 2 ROWB splits): split j writes its partial sum over the j-th
+// K range to c + j m ldc.
 template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, int ROWB = 64, bool SCALE16 = false>
 hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, const uint8_t *bs, int m, int n, int k,
-                       float alpha, OutT *c, int64_t ldc, hipStream_t s, bool staged = false) {
+                       float alpha, OutT *c, int64_t ldc, hipStream_t s, bool staged = false, int splits = 1) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   constexpr int SPR = ROWB / 16;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const ScaleLayout sl = staged ? ScaleLayout{SPR, (int64_t)m * SPR, SPR, (int64_t)n * SPR}
                                 : ScaleLayout{k / 32, SPR, k / 32, SPR};
-  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16>), dim3((unsigned)tiles),
-                     dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), sl,
-                     (const float *)nullptr, (const float *)nullptr, alpha, c, ldc);
+  hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16>),
+                     dim3((unsigned)tiles, (unsigned)splits), dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n,
+                     k / (2 * ROWB) / splits, (int64_t)(k / 2), sl, (const float *)nullptr, (const float *)nullptr,
+                     alpha, c, ldc);
   return hipGetLastError();
+}
+
+// C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the split partial sums added in ascending K order
+// (splits <= kMaxSplits).  Row blockIdx.y, columns from blockIdx.x; every partial is loaded before
+// the first addition, so the loads overlap.
+constexpr int kMaxSplits = 16;
+template <typename OutT>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ P, int splits, int m, int n,
+                                                         float alpha, OutT *__restrict__ C, int64_t ldc) {
+  const int col = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y;
+  if (col >= n) return;
+  const int64_t plane = (int64_t)m * n, t = (int64_t)r * n + col;
+  float v[kMaxSplits];
+#pragma unroll
+  for (int j = 0; j < kMaxSplits; ++j) v[j] = j < splits ? P[j * plane + t] : 0.0f;
+  float acc = v[0];
+#pragma unroll
+  for (int j = 1; j < kMaxSplits; ++j)
+    if (j < splits) acc = acc + v[j];
+  store_out(C + (int64_t)r * ldc + col, alpha * acc);
 }
 
 // bf16 operands (rows of kp elements, kp a multiple of ROWB / 2) scaled by fp32(*ga * *gb)
@@ -565,8 +600,26 @@ __global__ __launch_bounds__(256) void scales_to_stage_major_kernel(const uint8_
 }
 
 // (m + n) rows of k / 32 scale bytes, plus 16 bytes read past the end by a clamped 16-byte scale load
+// K splits for a few-token product (M <= 64, whose 64 x 64 tiles alone would leave CUs idle): about
+// one workgroup per CU (a narrower product already fills the chip and is not split: measured), the
+// split partials (written and read once, 8 M N bytes per split) at most a quarter of B's code bytes
+// (N K / 2), and a whole number of 128-byte stages per split, at least four (the depth of the load
+// ring).
+int gemm_mxfp4_splits(int64_t m, int64_t n, int64_t k) {
+  if (m > 64 || m <= 0 || n <= 0 || k % 256) return 1;
+  const int64_t tiles = (n + 63) / 64, nst = k / 256;
+  const int64_t want = std::min<int64_t>(std::min<int64_t>(256 / tiles, nst / 4), std::max<int64_t>(1, k / (64 * m)));
+  int best = 1;
+  for (int64_t d = 2; d <= want && d <= nst && d <= kMaxSplits; ++d)
+    if (nst % d == 0) best = (int)d;
+  return best;
+}
+
 int64_t gemm_mxfp4_workspace(int64_t m, int64_t n, int64_t k) {
-  return k % 256 == 0 ? (m + n) * (k / 32) + 32 : 0;
+  if (k % 256) return 0;
+  const int splits = gemm_mxfp4_splits(m, n, k);
+  const int64_t reorg = (m + n) * (k / 32) + 32;
+  return splits > 1 ? std::max<int64_t>(reorg, (int64_t)splits * m * n * 4) : reorg;
 }
 
 template <typename OutT>
@@ -574,7 +627,19 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
                     float alpha, OutT *c, int64_t ldc, hipStream_t s, uint8_t *ws = nullptr) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
-  if (ws && k % 256 == 0 && big >= 256) {
+  const int splits = gemm_mxfp4_splits(m, n, k);
+  if (ws && splits > 1 && aligned(as, 4) && aligned(bs, 4)) {
+    // few tokens: K split over workgroups, partial sums in the workspace, then added in K order
+    float *parts = reinterpret_cast<float *>(ws);
+    hipError_t e = launch_ring<2, 2, 1, 1, 4, float, 128>(a, as, b, bs, m, n, k, 1.0f, parts, n, s, false, splits);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((splitk_sum_kernel<OutT>), dim3((unsigned)((n + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                       parts, splits, m, n, alpha, c, ldc);
+    return hipGetLastError();
+  }
+  const int64_t reo_blocks = ((m + kReoRows - 1) / kReoRows + (n + kReoRows - 1) / kReoRows) *
+                             ((k / 256 + kReoStages - 1) / kReoStages);
+  if (ws && k % 256 == 0 && big >= 256 && aligned(as, 8) && aligned(bs, 8) && reo_blocks < ((int64_t)1 << 31)) {
     // 256 x 256 tiles: reorganise both operands' scales stage-major first, so that each stage's scales
     // arrive in 1 KB loads (for smaller tiles the extra pass costs more than it saves: measured)
     uint8_t *was = ws, *wbs = ws + (int64_t)m * (k / 32) + 16;
@@ -701,15 +766,14 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
   if (tiles >= ((int64_t)1 << 31)) return FP4Q_ERR_SHAPE;
   if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
     return FP4Q_ERR_ALIGN;
-  // the workspace is optional: with it (and K a multiple of 256) the scales are reorganised
+  // the workspace is optional: with it (and K a multiple of 256) large products reorganise the scales
+  // and few-token products split K
   uint8_t *ws = nullptr;
   const int64_t need = gemm_mxfp4_workspace(m, n, k);
   if (workspace && need > 0) {
     if (workspace_bytes < (size_t)need) return FP4Q_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP4Q_ERR_ALIGN;
-    const int64_t chunks = (k / 256 + kReoStages - 1) / kReoStages;
-    const int64_t blocks = ((m + kReoRows - 1) / kReoRows + (n + kReoRows - 1) / kReoRows) * chunks;
-    if (aligned(a_scales, 8) && aligned(b_scales, 8) && blocks < ((int64_t)1 << 31)) ws = (uint8_t *)workspace;
+    ws = (uint8_t *)workspace;
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;

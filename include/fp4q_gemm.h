@@ -10,8 +10,8 @@
  * product of the unrotated matrices, up to quantization error.
  *
  * All pointers are device pointers; stream is a hipStream_t (NULL = the
- * default stream).  The call enqueues one kernel and returns.  It allocates
- * nothing and keeps no state.  Argument errors are returned synchronously,
+ * default stream).  The call enqueues its kernels (one to three) and
+ * returns.  It allocates nothing and keeps no state.  Argument errors are returned synchronously,
  * before anything is enqueued.
  */
 #ifndef FP4Q_GEMM_H
@@ -43,19 +43,25 @@ extern "C" {
  *             written in full.  It must not overlap the inputs.
  *   workspace optional device memory (NULL for none) of at least
  *             fp4q_gemm_mxfp4_workspace_bytes(m, n, k) bytes, 16-byte
- *             aligned; its contents are overwritten.  When K is a multiple
- *             of 256 and the product is large enough for 256 x 256 tiles on
- *             every CU, both operands' scales are first copied there in a
- *             stage-major order ([k/256][rows][8 bytes]).  The product then
- *             loads each stage's scales in 1 KB pieces (the MR-GPTQ page,
- *             3.: QuTLASS reorganises scales for its FP4 product).  Results
- *             are identical with and without it; only the speed differs.
+ *             aligned; its contents are overwritten.  It is used when K is
+ *             a multiple of 256:
+ *             - products large enough for 256 x 256 tiles on every CU first
+ *               copy both operands' scales there in a stage-major order
+ *               ([k/256][rows][8 bytes]), and then load each stage's scales
+ *               in 1 KB pieces (the MR-GPTQ page, 3.: QuTLASS reorganises
+ *               scales for its FP4 product).  The result is identical to
+ *               the one without a workspace;
+ *             - few-token products (m <= 64) whose column tiles alone would
+ *               leave CUs idle split K into S contiguous ranges (S chosen
+ *               from m, n and k) and keep the S float32 partial sums there.
  *
  * Arithmetic: the products of two decoded elements are exact.  They are
  * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), one
  * 64-element step of K at a time, each step added to a float32 accumulator
- * in ascending K order.  The result differs from the exact product by a few
- * float32 roundings per step.
+ * in ascending K order.  With a K split, each range is summed that way and
+ * the S partial sums are then added in ascending K order, which can round
+ * differently from a single accumulation.  Either way the result differs
+ * from the exact product by a few float32 roundings per step.
  *
  * Alignment: a_codes and b_codes 16-byte aligned.  c aligned to its element
  * size.
@@ -71,8 +77,10 @@ fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, c
                               fp4q_dtype_t out_dtype, void *c, int64_t ldc, void *workspace, size_t workspace_bytes,
                               void *stream);
 
-/* Workspace that speeds up fp4q_gemm_mxfp4: (m + n) * k / 32 + 32 bytes when K
- * is a multiple of 256, else 0 (no workspace is used).  0 for invalid sizes. */
+/* Workspace that speeds up fp4q_gemm_mxfp4 when K is a multiple of 256: the
+ * larger of (m + n) * k / 32 + 32 bytes (scale copies) and, for a split few-
+ * token product, S * m * n * 4 bytes (partial sums).  0 when K is not a
+ * multiple of 256 (no workspace is used) and for invalid sizes. */
 size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* Workspace the NVFP4 product needs: (m + n) * roundup(k, 32) * 2 bytes (the

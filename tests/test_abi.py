@@ -176,6 +176,8 @@ def test_gemm_validation():
                                    kw.get("wsb", 0), None)
     assert lib.fp4q_gemm_mxfp4_workspace_bytes(64, 32, 512) == 96 * 16 + 32
     assert lib.fp4q_gemm_mxfp4_workspace_bytes(64, 32, 384) == 0
+    # few tokens: K split in 4 (16 stages of 256, at least 4 per split), partial sums 4 x 16 x 4096 floats
+    assert lib.fp4q_gemm_mxfp4_workspace_bytes(16, 4096, 4096) == 4 * 16 * 4096 * 4
     assert gm(k=512, ws=WS, wsb=100) == L.ERR_WORKSPACE
     assert gm(k=512, ws=WS + 4, wsb=1 << 20) == L.ERR_ALIGN
     assert gm(a=None) == L.ERR_NULL

@@ -163,12 +163,47 @@ def test_gemm_scale_reorganisation_is_transparent(m, n, k):
     bc, bs = _rand_mx(rng, n, k, 90, 160)
     a, asd, b, bsd = _dev(ac, as_, bc, bs)
     fq = _fq()
-    c1 = fq.gemm_mxfp4((a, asd), (b, bsd), reorganise=True)
-    c2 = fq.gemm_mxfp4((a, asd), (b, bsd), reorganise=False)
+    c1 = fq.gemm_mxfp4((a, asd), (b, bsd), use_workspace=True)
+    c2 = fq.gemm_mxfp4((a, asd), (b, bsd), use_workspace=False)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
     rows = np.arange(0, m, max(1, m // 40))
     _check(c1[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), ac, as_, bc, bs, k, rows=rows)
+
+
+# few-token products: K split over workgroups (the workspace holds the partial sums)
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 4096), (16, 4096, 4096), (40, 700, 14336)])
+def test_gemm_few_tokens_split_k_exact(m, n, k):
+    rng = np.random.default_rng(3100 + m + n + k)
+    ac, _ = _rand_mx(rng, m, k)
+    bc, _ = _rand_mx(rng, n, k)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    np.testing.assert_array_equal(_run(ac, as_, bc, bs), GM.gemm_mxfp4(ac, as_, bc, bs))
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (8, 2000, 4096, torch.bfloat16),
+                                             (33, 1024, 8192, torch.float32), (64, 512, 14336, torch.float32)])
+def test_gemm_few_tokens_split_k_within_bound(m, n, k, out_dtype):
+    fq = _fq()
+    rng = np.random.default_rng(3200 + m + n + k)
+    ac, as_ = _rand_mx(rng, m, k, 100, 150)
+    bc, bs = _rand_mx(rng, n, k, 100, 150)
+    lib = __import__("fp4_post_quantization_amd._lib", fromlist=["load"]).load()
+    # the workspace for these shapes holds split partial sums
+    assert lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) >= 2 * m * n * 4
+    c = _run(ac, as_, bc, bs, out_dtype=out_dtype, alpha=0.75)
+    A = GM.decode_mxfp4_64(ac, as_)
+    B = GM.decode_mxfp4_64(bc, bs)
+    ref = 0.75 * GM.gemm(A, B)
+    tol = 0.75 * _bound(A, B, k)
+    if out_dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    assert (np.abs(c - ref) <= tol).all()
+    # without a workspace: one accumulation over all of K, also within the bound
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c2 = fq.gemm_mxfp4((a, asd), (b, bsd), alpha=0.75, out_dtype=out_dtype, use_workspace=False)
+    assert (np.abs(c2.float().cpu().numpy().astype(np.float64) - ref) <= tol).all()
 
 
 def test_gemm_large_tiles_with_k_tail():
