@@ -673,6 +673,9 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
 // ScaleSweep candidate search on the group's current values.
 
 constexpr int kGptqBatch = 128;
+// Columns past the current block of kGptqBlock receive the block's updates in one contraction.
+constexpr int kGptqBlock = 1024;
+static_assert(kGptqBlock % kGptqBatch == 0, "blocks hold whole batches");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -835,9 +838,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
   }
 }
 
-// Trailing update W[:, i2:] -= E * U[i1:i2, i2:] with E = W[:, i1:i2] (the
-// batch's scaled errors), i2 = i1 + 128: a dense contraction with K = 128
-// on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile, each wave a
+// Trailing update W[:, c] -= E * U[i1:i1+kn, c] for the columns c from cbeg
+// on (blockIdx.y selects 64 of them), with E = W[:, i1:i1+kn] the scaled
+// errors of kn already quantized columns (one batch of 128, or a block of
+// 1024): a dense contraction on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile, each wave a
 // 32 x 32 sub-tile whose 16 accumulator rows per lane are read from W at the
 // start (their HBM latency then hides behind the contraction instead of
 // stalling the epilogue).  E and U are staged through LDS in K chunks of 32:
@@ -847,13 +851,12 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 constexpr int kUpdKc = 32;
 
 __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict__ W, int64_t ld, int rows,
-                                                               int cols, int i1,
+                                                               int cols, int i1, int kn, int cbeg,
                                                                const float *__restrict__ U) {
   __shared__ float As[64][kUpdKc + 1];
   __shared__ float Bs[kUpdKc][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i2 = i1 + kGptqBatch;
-  const int r0 = blockIdx.x * 64, c0 = i2 + blockIdx.y * 64;
+  const int r0 = blockIdx.x * 64, c0 = cbeg + blockIdx.y * 64;
   const int wr = wave & 1, wc = wave >> 1;
   const int lr = lane & 31, lk = lane >> 5;
   // accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column l%32
@@ -864,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict
     cur[v] = row < rows ? W[(int64_t)row * ld + c0 + wc * 32 + lr] : 0.0f;
   }
   f32x16 acc = {0};
-  for (int kc = 0; kc < kGptqBatch; kc += kUpdKc) {
+  for (int kc = 0; kc < kn; kc += kUpdKc) {
     f32x4 a[2], b[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1290,10 +1293,16 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
       hipLaunchKernelGGL((gptq_batch_kernel<false>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
                          (int)cols, i1,
                          hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
-    const int rest = (int)cols - i1 - kGptqBatch;
-    if (rest > 0)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), rest / 64), dim3(kThreads), 0, s, w, ld,
-                         (int)rows, (int)cols, i1, hinv_chol);
+    // two-level lazy update: the rest of this block of kGptqBlock columns now (the batch's 128 error
+    // columns), all later columns once per block (the block's error columns as one contraction)
+    const int i2 = i1 + kGptqBatch;
+    const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
+    if (i2 < b1)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w, ld,
+                         (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
+    else if (b1 < cols)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), ((int)cols - b1) / 64), dim3(kThreads), 0, s,
+                         w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
   }
   return last_hip_status();
 }

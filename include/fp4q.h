@@ -229,9 +229,12 @@ fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dt
  * column c is rounded to nearest at that scale, its scaled error
  * err = fp32(fp32(w_c - x_hat_c) * fp32(1 / U[c][c])) is kept, and every
  * later column j of the same 128-column batch becomes fma(-err, U[c][j],
- * w_j); after a batch the remaining columns receive w -= Err * U[batch, rest]
- * (an fp32 MFMA contraction).  A non-positive or non-finite diagonal entry of
- * U sets FP4Q_DATA_BAD_HESSIAN.
+ * w_j).  Later columns receive the batch's errors as fp32 MFMA contractions
+ * w -= Err * U[batch, cols]: after each batch the rest of its block of 1024
+ * columns, and after each block all later columns, with the whole block's
+ * errors in one contraction (two-level lazy batches; the float32 grouping of
+ * the updates is therefore not that of 128-column batches alone).  A
+ * non-positive or non-finite diagonal entry of U sets FP4Q_DATA_BAD_HESSIAN.
  */
 fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
                               const float *importance, int off_lo, int off_hi, uint32_t flags,

@@ -531,6 +531,26 @@ def test_gptq_multi_batch_against_oracle(wmse):
     assert lg < lr and lo < lr
 
 
+def test_gptq_block_updates_against_oracle():
+    """2304 columns: two full 1024-column blocks, whose errors reach the later
+    columns as one contraction each, and a 256-column tail.  Same bar as the
+    multi-batch case."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(64, 2304, seed=116)
+    res = fq.gptq_nvfp4(w.to(DEV), U, None, check=True)
+    torch.cuda.synchronize()
+    codes, scales, S = GQ.gptq_nvfp4(w.numpy(), U, None)
+    gc, gs = _np(res.codes), _np(res.scales)
+    assert np.float32(_np(res.global_scale)[0]) == S
+    code_mis = np.mean(Q.unpack_nibbles(gc) != Q.unpack_nibbles(codes))
+    scale_mis = np.mean(gs != scales)
+    lg = GQ.proxy_loss(w.numpy(), gc, gs, S, H)
+    lo = GQ.proxy_loss(w.numpy(), codes, scales, S, H)
+    print(f"code mismatch {code_mis:.2e}, scale mismatch {scale_mis:.2e}, loss rel {abs(lg - lo) / lo:.2e}")
+    assert code_mis <= 1e-3 and scale_mis <= 1e-3
+    assert abs(lg - lo) <= 1e-3 * lo
+
+
 def test_gptq_bad_hessian_sets_status():
     fq = _fp4()
     w = W.random_matrix(8, 128, seed=115).to(DEV)
