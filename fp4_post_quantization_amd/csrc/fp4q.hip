@@ -853,8 +853,8 @@ constexpr int kUpdKc = 32;
 __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict__ W, int64_t ld, int rows,
                                                                int cols, int i1, int kn, int cbeg,
                                                                const float *__restrict__ U) {
-  __shared__ float As[64][kUpdKc + 1];
-  __shared__ float Bs[kUpdKc][64];
+  __shared__ float As[2][64][kUpdKc + 1];
+  __shared__ float Bs[2][kUpdKc][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * 64, c0 = cbeg + blockIdx.y * 64;
   const int wr = wave & 1, wc = wave >> 1;
@@ -866,35 +866,49 @@ __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict
     const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
     cur[v] = row < rows ? W[(int64_t)row * ld + c0 + wc * 32 + lr] : 0.0f;
   }
-  f32x16 acc = {0};
-  for (int kc = 0; kc < kn; kc += kUpdKc) {
-    f32x4 a[2], b[2];
+  // chunk kc of the operands: E rows r0.. (64 x 32, 8 float4 per row), U rows i1 + kc.. (32 x 64)
+  f32x4 a[2], b[2];
+  auto fetch = [&](int kc) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int e = tid + kThreads * j;
-      const int rr = e >> 3, k4 = e & 7;  // A chunk: 64 rows x 8 float4
+      const int rr = e >> 3, k4 = e & 7;
       a[j] = (r0 + rr < rows) ? *reinterpret_cast<const f32x4 *>(W + (int64_t)(r0 + rr) * ld + i1 + kc + k4 * 4)
                               : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int kk = e >> 4, j4 = e & 15;  // B chunk: 32 rows x 16 float4
+      const int kk = e >> 4, j4 = e & 15;
       b[j] = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + kc + kk) * cols + c0 + j4 * 4);
     }
-    if (kc) __syncthreads();  // the previous chunk's operand reads are done
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int e = tid + kThreads * j;
       const int rr = e >> 3, k4 = e & 7;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) As[rr][k4 * 4 + k] = a[j][k];
+      for (int k = 0; k < 4; ++k) As[buf][rr][k4 * 4 + k] = a[j][k];
       const int kk = e >> 4, j4 = e & 15;
-      *reinterpret_cast<f32x4 *>(&Bs[kk][j4 * 4]) = b[j];
+      *reinterpret_cast<f32x4 *>(&Bs[buf][kk][j4 * 4]) = b[j];
     }
-    __syncthreads();
+  };
+  // double-buffered: chunk kc + 1's global loads are in flight while chunk kc's MFMAs run, and one
+  // barrier per chunk separates filling one LDS buffer from reading the other
+  f32x16 acc = {0};
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int buf = 0;
+  for (int kc = 0; kc < kn; kc += kUpdKc) {
+    const bool more = kc + kUpdKc < kn;
+    if (more) fetch(kc + kUpdKc);
 #pragma unroll
     for (int k = 0; k < kUpdKc; k += 2) {
-      const float av = As[wr * 32 + lr][k + lk];
-      const float bv = Bs[k + lk][wc * 32 + lr];
+      const float av = As[buf][wr * 32 + lr][k + lk];
+      const float bv = Bs[buf][k + lk][wc * 32 + lr];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
