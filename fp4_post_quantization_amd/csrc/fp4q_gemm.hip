@@ -33,6 +33,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "fp4q_device.h"
 #include "fp4q_gemm.h"
@@ -50,6 +52,12 @@ constexpr int kKc = 128;     // K elements per stage
 constexpr int kLdsRow = 80;  // bytes per staged row (64 + 16 padding)
 constexpr int kXcds = 8;
 constexpr int kGroupRows = 8;  // tile rows per group in the tile order
+
+// f(std::integral_constant<int, I>) for I = 0, 1, ..., N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll(std::integer_sequence<int, I...>, F &&f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -249,8 +257,11 @@ struct ScaleLayout {
   int64_t a_row, a_stage, b_row, b_stage;
 };
 
-// MX = true: MXFP4 operands (a stage is 128 K elements = 64 code bytes + 4 E8M0 bytes per row;
-// v_mfma_scale_f32_32x32x64_f8f6f4).  MX = false: bf16 operands (a stage is 32 K elements = 64 bytes
+// MX = true: MXFP4 operands (a stage is 2 ROWB K elements = ROWB code bytes + ROWB / 16 E8M0 bytes
+// per row; v_mfma_scale_f32_32x32x64_f8f6f4).  K step ks of a stage (KS = ROWB / 32 steps) takes, in
+// lane half h, the 32-element block h KS + ks of the stage, so that a lane's KS scale bytes of a
+// stage are contiguous: they are read as one word per row per stage, and the MFMA's byte select
+// (op_sel, checked on the device) picks byte ks.  MX = false: bf16 operands (a stage is 32 K elements = 64 bytes
 // per row; v_mfma_f32_32x32x16_bf16, lane l holding row l % 32 and K elements 8 (l / 32) .. +8, checked
 // on the device), scaled at the end by fp32(*ga * *gb).  Rows are kb bytes apart; nst stages.
 template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true, int ROWB = 64,
@@ -368,37 +379,46 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
 
-  // operands of one 64-element k step: code registers and scale bytes for TM blocks of A, TN of B
+  // operands of one k step: code registers for TM blocks of A and TN of B, and (MX) the stage's
+  // scale words
   struct Ops {
     i32x8 a[TM], b[TN];
     int sa[TM], sb[TN];
   };
-  auto read_ops = [&](int slot_, int ks, Ops &o) {
+  // LDS chunk (16 bytes) of k step ks in lane half h
+  auto chunk = [&](int ks) { return MX ? h * KS + ks : 2 * ks + h; };
+  auto scale_word = [&](const uint8_t *p) {
+    if constexpr (SPR == 8) return (int)*reinterpret_cast<const uint32_t *>(p + 4 * h);
+    else return (int)*reinterpret_cast<const uint16_t *>(p + 2 * h);
+  };
+  auto read_ops = [&](int slot_, auto ks_c, Ops &o, const Ops &prev) {
+    constexpr int ks = decltype(ks_c)::value;
     const uint8_t *base = smem + slot_ * STAGE;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wm * TM * 32 + i * 32 + l32;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * ROWB + 16 * ((2 * ks + h) ^ swz<ROWB>(r)));
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * ROWB + 16 * (chunk(ks) ^ swz<ROWB>(r)));
       o.a[i] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sa[i] = base[SA_OFF + SPR * r + 2 * ks + h];  // the byte itself: no ALU work
+      if constexpr (MX) o.sa[i] = ks == 0 ? scale_word(base + SA_OFF + SPR * r) : prev.sa[i];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wn * TN * 32 + j * 32 + l32;
       const i32x4 v =
-          *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * ROWB + 16 * ((2 * ks + h) ^ swz<ROWB>(r)));
+          *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * ROWB + 16 * (chunk(ks) ^ swz<ROWB>(r)));
       o.b[j] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sb[j] = base[SB_OFF + SPR * r + 2 * ks + h];
+      if constexpr (MX) o.sb[j] = ks == 0 ? scale_word(base + SB_OFF + SPR * r) : prev.sb[j];
     }
   };
-  auto mfmas = [&](const Ops &o) {
+  auto mfmas = [&](const Ops &o, auto ks_c) {
+    constexpr int ks = decltype(ks_c)::value;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr (MX) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 4, 4, 0, o.sa[i],
-                                                                      0, o.sb[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[i], o.b[j], acc[i][j], 4, 4, ks, o.sa[i],
+                                                                      ks, o.sb[j]);
         } else {
           const i32x4 av = {o.a[i][0], o.a[i][1], o.a[i][2], o.a[i][3]};
           const i32x4 bv = {o.b[j][0], o.b[j][1], o.b[j][2], o.b[j][3]};
@@ -426,29 +446,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   stage_barrier();
 
   Ops o0, o1;
-  read_ops(0, 0, o0);
+  read_ops(0, std::integral_constant<int, 0>{}, o0, o1);
   int slot = 0;
   for (int st = 0; st < nst; ++st) {
     // k steps 0 .. KS-2: read step ks + 1 while step ks's MFMAs run (KS is even: o0 holds the even steps)
-#pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) {
-      if (ks % 2 == 0) {
-        read_ops(slot, ks + 1, o1);
-        mfmas(o0);
+    unroll(std::make_integer_sequence<int, KS - 1>{}, [&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      if constexpr (ks % 2 == 0) {
+        read_ops(slot, std::integral_constant<int, ks + 1>{}, o1, o0);
+        mfmas(o0, ks_c);
       } else {
-        read_ops(slot, ks + 1, o0);
-        mfmas(o1);
+        read_ops(slot, std::integral_constant<int, ks + 1>{}, o0, o1);
+        mfmas(o1, ks_c);
       }
-    }
+    });
     __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the barrier below
     const int next = slot == NS - 1 ? 0 : slot + 1;
     wait_lgkmcnt0();                    // this wave's reads of stage st are complete
     wait_vmcnt<(NS - 2) * LOADS>();     // stage st + 1 has landed
     stage_barrier();                    // ... for every wave, and nobody reads stage st any more
     issue(min(st + NS, nst - 1), slot);
-    read_ops(next, 0, o0);  // first k step of the next stage, read while this stage's last MFMAs run
+    read_ops(next, std::integral_constant<int, 0>{}, o0, o1);  // the next stage's first k step
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(o1);
+    mfmas(o1, std::integral_constant<int, KS - 1>{});
     slot = next;
   }
 

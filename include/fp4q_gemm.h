@@ -56,9 +56,13 @@ extern "C" {
  *               from m, n and k) and keep the S float32 partial sums there.
  *
  * Arithmetic: the products of two decoded elements are exact.  They are
- * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), one
- * 64-element step of K at a time, each step added to a float32 accumulator
- * in ascending K order.  With a K split, each range is summed that way and
+ * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), 64
+ * elements of K per step, each step added to a float32 accumulator.  When K
+ * is a multiple of 128, K is walked in stages of 256 elements (128 when K is
+ * not a multiple of 256), stages in ascending order, and step j of a stage
+ * holds its 32-element blocks j and j + 4 (j and j + 2 for 128-element
+ * stages); otherwise step j holds elements 64 j .. 64 j + 63.  With a K
+ * split, each range is summed that way and
  * the S partial sums are then added in ascending K order, which can round
  * differently from a single accumulation.  Either way the result differs
  * from the exact product by a few float32 roundings per step.
