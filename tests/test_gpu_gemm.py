@@ -206,6 +206,26 @@ def test_gemm_few_tokens_split_k_within_bound(m, n, k, out_dtype):
     assert (np.abs(c2.float().cpu().numpy().astype(np.float64) - ref) <= tol).all()
 
 
+def test_gemm_output_beyond_2gib_sampled_rows():
+    """C of 32800 x 16384 float32 (2.15 GB): rows past the 2^31-byte offset are
+    written where they belong.  Unit scales make every sum exact, so the
+    sampled rows are compared bit for bit with the oracle."""
+    fq = _fq()
+    m, n, k = 32800, 16384, 256
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3300)
+    a = torch.randint(0, 256, (m, k // 2), dtype=torch.uint8, device=DEV, generator=g)
+    b = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=DEV, generator=g)
+    sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=DEV)
+    sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=DEV)
+    c = fq.gemm_mxfp4((a, sa), (b, sb))
+    torch.cuda.synchronize()
+    pick = np.array([0, 32767, 32768, 32769, 32799])
+    ref = GM.gemm_mxfp4(a.cpu().numpy()[pick], sa.cpu().numpy()[pick], b.cpu().numpy(), sb.cpu().numpy())
+    got = c[torch.from_numpy(pick).to(DEV)].cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(got, ref)
+
+
 def test_gemm_large_tiles_with_k_tail():
     """K not a multiple of 128 with enough rows and columns for 256 x 256
     tiles: the register-staged path with its zero-filled K tail; sampled rows

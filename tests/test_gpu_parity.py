@@ -355,6 +355,43 @@ def test_c2_nvfp4_wmse_bf16_4096_sampled_rows():
     _check_nvfp4(res, ref, rows=rows)
 
 
+def test_tensor_beyond_2gib_sampled_rows():
+    """65600 x 16384 bf16 (2.15 GB, past 2^31 bytes; 67 M blocks): NVFP4 WMSE
+    (global-max pass + sweep) and MXFP4 checked bit-exact on rows on both
+    sides of the 2^31-byte boundary.  The values are N(0, 0.02) clipped to
+    +-0.5 with 0.75 planted in the last element, so the global maximum, and
+    with it S, is known without reading the tensor back."""
+    fq = _fp4()
+    rows, cols = 65600, 16384
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1201)
+    x = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    for r0 in range(0, rows, 8192):
+        r1 = min(rows, r0 + 8192)
+        x[r0:r1] = (torch.randn((r1 - r0, cols), device=DEV, generator=g) * 0.02).clamp_(-0.5, 0.5).to(torch.bfloat16)
+    x[-1, -1] = 0.75
+    imp = W.random_importance(cols, seed=1202)
+    pick = torch.tensor([0, 1, 32768, 65535, 65536, 65537, 65598, 65599], device=DEV)
+    host = x[pick].float().cpu().numpy()
+    S = Q.global_scale_nvfp4(np.array([[0.75]], np.float32))
+
+    res = fq.quantize_nvfp4(x, imp.to(DEV), check=True)
+    torch.cuda.synchronize()
+    ref = Q.quantize_nvfp4(host, imp.numpy(), global_scale=S)
+    _assert_equal("global_scale", np.float32(_np(res.global_scale)[0]), np.float32(S))
+    for name, got, want in (("codes", res.codes, ref.codes), ("scales", res.scales, ref.scales),
+                            ("offsets", res.offsets, ref.offsets), ("block_loss", res.block_loss, ref.block_loss)):
+        _assert_equal(name, _np(got[pick]), want)
+    del res
+
+    mx = fq.quantize_mxfp4(x, window=(-1, 0), check=True)
+    torch.cuda.synchronize()
+    mref = Q.quantize_mxfp4(host, window=(-1, 0))
+    for name, got, want in (("codes", mx.codes, mref.codes), ("scales", mx.scales, mref.scales),
+                            ("offsets", mx.offsets, mref.offsets), ("block_loss", mx.block_loss, mref.block_loss)):
+        _assert_equal("mxfp4 " + name, _np(got[pick]), want)
+
+
 @pytest.mark.parametrize("variant", ["absmax", "sweep", "rot32"])
 def test_c3_mxfp4_activations_sampled_rows(variant):
     fq = _fp4()
