@@ -26,7 +26,8 @@ inverse Hessian, restated here:
 import numpy as np
 
 from . import formats as F
-from .quant import fma_f32, global_scale_nvfp4, pack_nibbles, sweep_blocks, dequantize_nvfp4
+from .quant import (fma_f32, global_scale_nvfp4, pack_nibbles, sweep_blocks, sweep_blocks_mx, dequantize_nvfp4,
+                    dequantize_mxfp4)
 
 BATCH = 128
 
@@ -75,7 +76,59 @@ def gptq_nvfp4(W, U, importance=None, window=None, global_scale=None):
     return pack_nibbles(codes), scales, S
 
 
+def gptq_mxfp4(W, U, importance=None, window=(-1, 0)):
+    """GPTQ with MXFP4 group scales ("Bridging the Gap ... Microscaling FP4",
+    2. Metodologia, MR-GPTQ component 1: the grid is optimised per format,
+    MXFP4 included).  The same column-by-column procedure as gptq_nvfp4 with
+    MXFP4 groups: when column c opens a 32-column group, each row's E8M0
+    exponent is the exponent sweep's choice (oracle.quant.sweep_blocks_mx) on
+    the group's current values, from the base exponent over the window;
+    x_hat = q * 2^E exactly (no global scale).  Returns (packed codes, E8M0
+    scale bytes)."""
+    W = np.array(W, dtype=np.float32, copy=True)
+    U = np.asarray(U, dtype=np.float32)
+    rows, cols = W.shape
+    if cols % BATCH:
+        raise ValueError("columns must be a multiple of 128")
+    lo, hi = int(window[0]), int(window[1])
+    wmse = importance is not None
+    imp = None if not wmse else np.asarray(importance, dtype=np.float32).reshape(cols // 32, 32)
+    rdiag = (np.float32(1.0) / np.diag(U)).astype(np.float32)
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 32), dtype=np.uint8)
+    for i1 in range(0, cols, BATCH):
+        i2 = i1 + BATCH
+        E = np.zeros((rows, BATCH), dtype=np.float32)
+        for c in range(i1, i2):
+            if c % 32 == 0:
+                g = c // 32
+                ub = np.abs(W[:, c:c + 32]).astype(np.float32)[:, None, :]
+                e_best = sweep_blocks_mx(ub, None if imp is None else imp[g][None, None, :], lo, hi)[0][:, 0]
+                scales[:, g] = (e_best + 127).astype(np.uint8)
+                down = F.pow2_f32(-e_best)
+                up = F.pow2_f32(e_best)
+            w = W[:, c]
+            idx = F.e2m1_rne_index((np.abs(w) * down).astype(np.float32))
+            mag = (F.e2m1_value(idx) * up).astype(np.float32)
+            what = np.where(np.signbit(w), -mag, mag).astype(np.float32)
+            codes[:, c] = (np.signbit(w).astype(np.uint8) << 3) | idx
+            err = ((w - what).astype(np.float32) * rdiag[c]).astype(np.float32)
+            E[:, c - i1] = err
+            if c + 1 < i2:
+                W[:, c + 1:i2] = fma_f32(-err[:, None], U[c, c + 1:i2][None, :], W[:, c + 1:i2])
+        if i2 < cols:
+            acc = (E.astype(np.float64) @ U[i1:i2, i2:].astype(np.float64)).astype(np.float32)
+            W[:, i2:] = (W[:, i2:] - acc).astype(np.float32)
+    return pack_nibbles(codes), scales
+
+
 def proxy_loss(W0, codes, scales, S, H):
-    """GPTQ's objective tr((W0 - W_hat) H (W0 - W_hat)^T) in float64."""
+    """GPTQ's objective tr((W0 - W_hat) H (W0 - W_hat)^T) in float64 (NVFP4)."""
     D = np.asarray(W0, dtype=np.float64) - dequantize_nvfp4(codes, scales, S).astype(np.float64)
+    return float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))
+
+
+def proxy_loss_mx(W0, codes, scales, H):
+    """The same objective for MXFP4 codes and E8M0 scales."""
+    D = np.asarray(W0, dtype=np.float64) - dequantize_mxfp4(codes, scales).astype(np.float64)
     return float(np.sum((D @ np.asarray(H, dtype=np.float64)) * D))

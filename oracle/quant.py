@@ -272,6 +272,37 @@ def mx_base_exponent(a):
     return np.clip(E, -127, 127)
 
 
+def sweep_blocks_mx(ub, w, lo, hi):
+    """The MXFP4 exponent sweep on blocks of magnitudes ub [..., 32] with
+    per-element weights w (broadcastable, or None for MSE): the base
+    exponent, then for E = base + lo .. base + hi in ascending order the
+    loss of the block's two 16-element halves, each a fused in-order sum,
+    added in float32; returns (E*, its loss, the base exponent)."""
+    E_base = mx_base_exponent(ub.max(axis=-1))
+    offsets = np.arange(lo, hi + 1)
+    losses = np.empty(E_base.shape + (offsets.size,), dtype=np.float32)
+    valid = np.empty(E_base.shape + (offsets.size,), dtype=bool)
+    for k, o in enumerate(offsets):
+        E = E_base + o
+        ok = (E >= -127) & (E <= 127)
+        Ec = np.clip(E, -127, 127)
+        down = F.pow2_f32(-Ec)[..., None]
+        up = F.pow2_f32(Ec)[..., None]
+        y = (ub * down).astype(np.float32)
+        q = F.e2m1_value(F.e2m1_rne_index(y))
+        d = (q * up).astype(np.float32)
+        e = (ub - d).astype(np.float32)
+        halves = e.reshape(e.shape[:-1] + (2, 16))
+        wh = np.broadcast_to(w, e.shape).reshape(halves.shape) if w is not None else None
+        part = fused_sum_sq(halves, wh)
+        losses[..., k] = (part[..., 0] + part[..., 1]).astype(np.float32)
+        valid[..., k] = ok
+    k_best = _first_argmin(losses, valid)
+    E_best = E_base + offsets[k_best]
+    L_best = np.take_along_axis(losses, k_best[..., None], axis=-1)[..., 0]
+    return E_best, L_best, E_base
+
+
 def quantize_mxfp4(x, importance=None, window=(-1, 0), block=32, hadamard_n=0):
     """MXFP4 exponent sweep of a float32 matrix (steps in the module doc)."""
     if block != 32:
@@ -293,29 +324,7 @@ def quantize_mxfp4(x, importance=None, window=(-1, 0), block=32, hadamard_n=0):
 
     u = np.abs(x).astype(np.float32)
     ub = u.reshape(rows, cols // block, block)
-    E_base = mx_base_exponent(ub.max(axis=-1))
-    offsets = np.arange(lo, hi + 1)
-    losses = np.empty(E_base.shape + (offsets.size,), dtype=np.float32)
-    valid = np.empty(E_base.shape + (offsets.size,), dtype=bool)
-    for k, o in enumerate(offsets):
-        E = E_base + o
-        ok = (E >= -127) & (E <= 127)
-        Ec = np.clip(E, -127, 127)
-        down = F.pow2_f32(-Ec)[..., None]
-        up = F.pow2_f32(Ec)[..., None]
-        y = (ub * down).astype(np.float32)
-        q = F.e2m1_value(F.e2m1_rne_index(y))
-        d = (q * up).astype(np.float32)
-        e = (ub - d).astype(np.float32)
-        halves = e.reshape(e.shape[:-1] + (2, 16))
-        wh = np.broadcast_to(w, e.shape).reshape(halves.shape) if wmse else None
-        part = fused_sum_sq(halves, wh)
-        losses[..., k] = (part[..., 0] + part[..., 1]).astype(np.float32)
-        valid[..., k] = ok
-
-    k_best = _first_argmin(losses, valid)
-    E_best = E_base + offsets[k_best]
-    L_best = np.take_along_axis(losses, k_best[..., None], axis=-1)[..., 0]
+    E_best, L_best, E_base = sweep_blocks_mx(ub, w if wmse else None, lo, hi)
     y = (ub * F.pow2_f32(-E_best)[..., None]).astype(np.float32)
     idx = F.e2m1_rne_index(y)
     sign = np.signbit(x).reshape(rows, cols // block, block).astype(np.uint8)

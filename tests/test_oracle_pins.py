@@ -595,6 +595,68 @@ def test_gptq_matches_explicit_inverse_formulation():
     assert np.mean(Q.unpack_nibbles(rtn.codes) == Q.unpack_nibbles(c64)) < 0.9
 
 
+def _gptq_mx_explicit_inverse64(W, Hd, window):
+    """Textbook GPTQ (as above) with MXFP4 groups of 32: a group's exponent is
+    the MXFP4 quantizer's choice on the group's current values rounded to
+    float32, x_hat = q * 2^E."""
+    W = np.array(W, dtype=np.float64)
+    rows, cols = W.shape
+    Hinv = np.linalg.inv(np.asarray(Hd, dtype=np.float64))
+    codes = np.zeros((rows, cols), np.uint8)
+    scales = np.zeros((rows, cols // 32), np.uint8)
+    for c in range(cols):
+        if c % 32 == 0:
+            grp = Q.quantize_mxfp4(W[:, c:c + 32].astype(np.float32), window=window)
+            scales[:, c // 32] = grp.scales[:, 0]
+            e = grp.scales[:, 0].astype(np.int64) - 127
+        w = W[:, c].astype(np.float32)
+        idx = F.e2m1_rne_index((np.abs(w) * F.pow2_f32(-e)).astype(np.float32))
+        codes[:, c] = (np.signbit(w).astype(np.uint8) << 3) | idx
+        xhat = np.where(np.signbit(w), -1.0, 1.0) * F.e2m1_value(idx).astype(np.float64) * np.ldexp(1.0, e)
+        d = (W[:, c] - xhat) / Hinv[c, c]
+        W[:, c + 1:] -= d[:, None] * Hinv[c, c + 1:][None, :]
+        Hinv = Hinv - np.outer(Hinv[:, c], Hinv[c, :]) / Hinv[c, c]
+    return Q.pack_nibbles(codes), scales
+
+
+def test_gptq_mxfp4_without_feedback_is_the_sweep():
+    """With a diagonal U no error reaches another column: MXFP4 GPTQ is then
+    the plain MXFP4 exponent sweep, for MSE and WMSE and any window."""
+    rng = np.random.default_rng(41)
+    W = (rng.standard_t(4, (12, 256)) * 0.02).astype(np.float32)
+    U = np.diag(np.exp(rng.normal(0.0, 0.3, 256))).astype(np.float32)
+    imp = np.exp(rng.normal(0.0, 1.0, 256)).astype(np.float32)
+    for im in (None, imp):
+        for win in ((-1, 0), (-2, 1), (0, 0)):
+            codes, scales = GQ.gptq_mxfp4(W, U, im, window=win)
+            ref = Q.quantize_mxfp4(W, im, window=win)
+            np.testing.assert_array_equal(codes, ref.codes)
+            np.testing.assert_array_equal(scales, ref.scales)
+
+
+def test_gptq_mxfp4_matches_explicit_inverse_formulation():
+    """The oracle's MXFP4 GPTQ (Cholesky factor, lazy batches, float32)
+    against the float64 explicit-inverse elimination over two batches:
+    agreement up to rounding, and far from plain round-to-nearest."""
+    import workloads as W_
+    rng = np.random.default_rng(42)
+    W = (rng.standard_t(4, (16, 256)) * 0.02).astype(np.float32)
+    X = W_.calibration_activations(512, 256, seed=43)
+    H, U = W_.hessian_and_factor(X, damp=0.01)
+    Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(256)
+    codes, scales = GQ.gptq_mxfp4(W, U)
+    c64, s64 = _gptq_mx_explicit_inverse64(W, Hd, (-1, 0))
+    code_agree = np.mean(Q.unpack_nibbles(codes) == Q.unpack_nibbles(c64))
+    scale_agree = np.mean(scales == s64)
+    assert code_agree >= 0.995 and scale_agree >= 0.995, (code_agree, scale_agree)
+    g = GQ.proxy_loss_mx(W, codes, scales, H)
+    t = GQ.proxy_loss_mx(W, c64, s64, H)
+    assert abs(g - t) <= 0.02 * t, (g, t)
+    rtn = Q.quantize_mxfp4(W)
+    assert np.mean(Q.unpack_nibbles(rtn.codes) == Q.unpack_nibbles(c64)) < 0.9
+    assert g < GQ.proxy_loss_mx(W, rtn.codes, rtn.scales, H)
+
+
 def test_hessian_factor_inverts():
     import workloads as W_
     X = W_.calibration_activations(300, 128, seed=28)
