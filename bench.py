@@ -309,6 +309,24 @@ def run_other(args):
                          "proxy_gptq": proxy(r.codes, r.scales, r.global_scale),
                          "proxy_rtn_sweep": proxy(rtn.codes, rtn.scales, rtn.global_scale),
                          "proxy_rtn_absmax": proxy(ab.codes, ab.scales, ab.global_scale)}
+
+        def proxy_mx(codes, scales):
+            xh = fq.dequantize("mxfp4", codes, scales).double()
+            d = xd.double() - xh
+            return float(((d @ Hd) * d).sum())
+
+        # MXFP4 group scales (E8M0, window [-1, 0]); the same weight and Hessian
+        for name, im in (("mxfp4_mse", None), ("mxfp4_wmse", impd)):
+            r = fq.gptq_mxfp4(xd, Ud, im, check=True)
+            step = lambda i: fq.gptq_mxfp4(xd, Ud, im)
+            prewarm(step, seconds=0.5)
+            ms = _events_time(step, max(3, args.steps // 10))
+            rtn = fq.quantize_mxfp4(xd, im)
+            ab = fq.quantize_mxfp4(xd, im, window=(0, 0))
+            res[name] = {"ms": ms, "gel_s": xd.numel() / ms / 1e6,
+                         "proxy_gptq": proxy_mx(r.codes, r.scales),
+                         "proxy_rtn_sweep": proxy_mx(rtn.codes, rtn.scales),
+                         "proxy_rtn_absmax": proxy_mx(ab.codes, ab.scales)}
     elif args.config == "c4":
         total_ms = {"mse": 0.0, "wmse": 0.0}
         n = 0

@@ -22,7 +22,8 @@ from . import _lib as L
 from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
-    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "gptq_nvfp4", "dequantize", "block_hadamard",
+    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "gptq_nvfp4", "gptq_mxfp4", "dequantize",
+    "block_hadamard", "gemm_mxfp4", "gemm_nvfp4",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
 ]
 
@@ -258,6 +259,35 @@ def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *,
         work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
         flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(),
         ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
+
+
+def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=False):
+    """GPTQ with MXFP4 group scales.  w: [R, C] weight (a float32 working
+    copy is made, C a multiple of 128); hinv_chol: [C, C] upper Cholesky
+    factor U of the damped inverse Hessian; importance: per-column WMSE
+    weights or None (MSE); window: E8M0 exponent offsets around each group's
+    base exponent.  Returns an MXFP4Result without losses and offsets."""
+    lib = L.load()
+    if w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D device tensor")
+    rows, cols = w.shape
+    dev = w.device
+    work = w.to(torch.float32).contiguous().clone()
+    U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
+    if U.shape != (cols, cols):
+        raise ValueError("hinv_chol must be [cols, cols]")
+    imp = _importance(importance, cols, dev)
+    out = MXFP4Result(
+        codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+        block_loss=None, offsets=None)
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_gptq_mxfp4(
+        work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
+        out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
     if check:
         _check_data(ws)
     return out

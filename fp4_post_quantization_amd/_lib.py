@@ -27,6 +27,7 @@ EXPORTS = (
     "fp4q_quantize_mxfp4",
     "fp4q_quantize_relaxed",
     "fp4q_gptq_nvfp4",
+    "fp4q_gptq_mxfp4",
     "fp4q_dequantize",
     "fp4q_block_hadamard",
     "fp4q_gemm_mxfp4",
@@ -51,6 +52,7 @@ _SIGNATURES = {
                                  _P, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_quantize_relaxed": (_I, [_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
+    "fp4q_gptq_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "fp4q_dequantize": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "fp4q_block_hadamard": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P]),
     "fp4q_gemm_mxfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _I, _P, _I64, _P, _SZ, _P]),

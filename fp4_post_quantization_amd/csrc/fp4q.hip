@@ -711,9 +711,11 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 // round trip), which all quantize it identically; the owner keeps code and
 // error, and every lane updates its own columns with fma(-err, U[i][col], w)
 // (U is zero below the diagonal, so finished columns are left as they are).
-// At the start of each 16-column group lane t evaluates the window candidate
-// at offset lo + t on the group's current values (the sweep's loss), and a
-// (loss, pattern) minimum over the row's lanes picks the scale.  The batch's
+// At the start of each group (NVFP4: 16 columns, E4M3 patterns; MXFP4: 32
+// columns, E8M0 exponents, no global scale) lane t evaluates the window
+// candidate at offset lo + t on the group's current values (the sweep's
+// loss), and a (loss, candidate) minimum over the row's lanes picks the
+// scale.  The batch's
 // scaled errors replace its columns of W for the trailing update.  The
 // column loop is unrolled at compile time because the broadcast's source
 // lane is an immediate.
@@ -725,7 +727,7 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-template <bool WMSE>
+template <bool WMSE, int FMT>
 __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     float *__restrict__ W, int64_t ld, int rows, int cols, int i1, const float *__restrict__ U,
     const float *__restrict__ imp, const float *__restrict__ gscale, int lo, int hi, uint8_t *__restrict__ codes,
@@ -745,13 +747,15 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     if (!((d > 0.0f) & (d <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
     rdiag[tid] = 1.0f / d;  // correctly rounded
     impb[tid] = WMSE ? imp[i1 + tid] : 1.0f;
+    if (WMSE && !((impb[tid] >= 0.0f) & (impb[tid] <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_IMPORTANCE);
   }
   __syncthreads();
   const int lane = tid & 63;
   const int t = lane & 15;
   const int r = blockIdx.x * kGptqRowsPerWg + (tid >> 4);
   const bool live = r < rows;  // dead rows still take part in the broadcasts
-  const float S = *gscale;
+  constexpr bool MX = FMT == FP4Q_MXFP4;
+  const float S = MX ? 1.0f : *gscale;
   const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
   float *wr = W + (int64_t)(live ? r : 0) * ld + i1 + 8 * t;
   float w[8];
@@ -764,6 +768,12 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       w[4 + k] = b[k];
     }
   }
+  if constexpr (MX) {  // no global-max pass checked the weights
+    bool finite = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) finite &= fabsf(w[k]) <= 3.402823466e38f;
+    if (!finite) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+  }
   uint32_t code8 = 0;
   float err8[8];
 #pragma unroll
@@ -771,7 +781,48 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
   float V = 1.0f, R = 1.0f;
   static_for(std::make_integer_sequence<int, 16>{}, [&](auto tt_c) {
     constexpr int tt = decltype(tt_c)::value;
-    if constexpr ((tt & 1) == 0) {
+    if constexpr (MX && (tt & 3) == 0) {
+      // group [8 tt, 8 tt + 32): its values sit in lanes tt .. tt + 3 of the row
+      float z[32], wg[32];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        z[e] = row_bcast<tt>(w[e]);
+        z[8 + e] = row_bcast<tt + 1>(w[e]);
+        z[16 + e] = row_bcast<tt + 2>(w[e]);
+        z[24 + e] = row_bcast<tt + 3>(w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) wg[e] = impb[8 * tt + e];
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) a = fmaxf(a, fabsf(z[e]));
+      const int eb = mx_base_exponent(a);
+      const int E = eb + lo + t;
+      const bool ok = (t <= hi - lo) & (E >= -127) & (E <= 127);
+      const int Ec = min(max(E, -127), 127);
+      const float down = pow2f(-Ec), up = pow2f(Ec);
+      float y[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) y[e] = z[e] * down;
+      // the block's loss: its two 16-element halves, each summed in order, then added
+      const float L0 = loss_of_codes<WMSE>(z, wg, cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), up);
+      const float L1 = loss_of_codes<WMSE>(z + 16, wg + 16, cvt8<false>(y + 16, 0u), cvt8<false>(y + 24, 0u), up);
+      float Lm = ok ? L0 + L1 : __builtin_inff();
+      int em = ok ? E : 0x7FFFFFFF;
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) {
+        const float L2 = __shfl_xor(Lm, m, 16);
+        const int e2 = __shfl_xor(em, m, 16);
+        const bool take = (L2 < Lm) | ((L2 == Lm) & (e2 < em));
+        Lm = take ? L2 : Lm;
+        em = take ? e2 : em;
+      }
+      const int es = em == 0x7FFFFFFF ? max(-127, eb + lo) : em;
+      V = pow2f(es);
+      R = pow2f(-es);
+      if (live && t == 0) scales[(int64_t)r * (cols / 32) + ((i1 + 8 * tt) >> 5)] = (uint8_t)(es + 127);
+    }
+    if constexpr (!MX && (tt & 1) == 0) {
       // group [8 tt, 8 tt + 16): its values sit in lanes tt and tt + 1 of the row
       float us[16], wg[16];
 #pragma unroll
@@ -816,7 +867,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       const float y_i = us_i * R;
       const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
       const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
-      const float what = (q * V) * S;           // q * V exact, one rounding by S
+      const float what = MX ? q * V : (q * V) * S;  // q * V exact; NVFP4: one rounding by S
       const float err = (wi - what) * rdiag[i];
       if (t == tt) {
         code8 |= code << (4 * k);
@@ -1005,6 +1056,34 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
   const int64_t units = (int64_t)rows * nbands;
   int rpt = (int)((units + target_tiles - 1) / target_tiles);
   return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);
+}
+
+// The GPTQ batches of either format: per 128-column batch the batch kernel,
+// then the two-level lazy update (the rest of this block of kGptqBlock
+// columns with the batch's 128 error columns; after the block's last batch,
+// all later columns with the block's error columns as one contraction).
+template <int FMT>
+static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
+                         const float *importance, const float *global_scale, int off_lo, int off_hi, uint8_t *codes,
+                         uint8_t *scales, uint32_t *status, hipStream_t s) {
+  const int gb = ceil_div(rows, kGptqRowsPerWg);
+  for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
+    if (importance)
+      hipLaunchKernelGGL((gptq_batch_kernel<true, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
+                         (int)cols, i1, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
+    else
+      hipLaunchKernelGGL((gptq_batch_kernel<false, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld,
+                         (int)rows, (int)cols, i1, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales,
+                         status);
+    const int i2 = i1 + kGptqBatch;
+    const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
+    if (i2 < b1)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w, ld,
+                         (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
+    else if (b1 < cols)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), ((int)cols - b1) / 64), dim3(kThreads), 0, s,
+                         w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
+  }
 }
 
 static AmaxOut amax_out(void *workspace, const float *imp, int imp_n) {
@@ -1296,28 +1375,30 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
     hipLaunchKernelGGL(scale_from_partials_kernel, dim3(1), dim3(kThreads), 0, s, partials, n_partials,
                        global_scale, status);
   }
-  const bool wmse = importance != nullptr;
-  const int gb = ceil_div(rows, kGptqRowsPerWg);
-  for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
-    if (wmse)
-      hipLaunchKernelGGL((gptq_batch_kernel<true>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
-                         (int)cols, i1,
-                         hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
-    else
-      hipLaunchKernelGGL((gptq_batch_kernel<false>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
-                         (int)cols, i1,
-                         hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
-    // two-level lazy update: the rest of this block of kGptqBlock columns now (the batch's 128 error
-    // columns), all later columns once per block (the block's error columns as one contraction)
-    const int i2 = i1 + kGptqBatch;
-    const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
-    if (i2 < b1)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w, ld,
-                         (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
-    else if (b1 < cols)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), ((int)cols - b1) / 64), dim3(kThreads), 0, s,
-                         w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
-  }
+  gptq_batches<FP4Q_NVFP4>(w, rows, cols, ld, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales,
+                           status, s);
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
+                                         const float *hinv_chol, const float *importance, int off_lo,
+                                         int off_hi, uint8_t *codes, uint8_t *scales, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!w || !hinv_chol || !codes || !scales)) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
+  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
+    return FP4Q_ERR_SHAPE;
+  if (empty) return FP4Q_OK;
+  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
+      (importance && !aligned(importance, 4)))
+    return FP4Q_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, hinv_chol, importance, nullptr, off_lo, off_hi, codes, scales,
+                           status, s);
   return last_hip_status();
 }
 

@@ -242,6 +242,29 @@ fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
                               size_t workspace_bytes, void *stream);
 
 /*
+ * GPTQ with MXFP4 group scales ([MR] 2., MR-GPTQ component 1: the grid is
+ * optimised per format, MXFP4 as well as NVFP4).  The same procedure as
+ * fp4q_gptq_nvfp4 with 32-column groups: when column c opens a group, each
+ * row's E8M0 exponent is the exponent sweep's choice (fp4q_quantize_mxfp4's
+ * search: base exponent, window of exponent offsets, the block loss as two
+ * 16-element halves) on the group's current values; column c is rounded at
+ * 2^E, x_hat = q * 2^E exactly, and the scaled errors and updates are those
+ * of fp4q_gptq_nvfp4.  There is no global scale.
+ *
+ *   w, rows, cols, ld, hinv_chol, importance  as for fp4q_gptq_nvfp4.
+ *   off_lo, off_hi  exponent window (at most 16 candidates), e.g. -1, 0.
+ *   codes      [rows x cols/2] packed E2M1 codes (4-byte aligned).
+ *   scales     [rows x cols/32] E8M0 bytes (E + 127).
+ *   workspace  fp4q_workspace_bytes() bytes (status word).
+ * A non-finite weight sets FP4Q_DATA_NONFINITE_INPUT, a negative or
+ * non-finite importance FP4Q_DATA_BAD_IMPORTANCE, a bad diagonal of U
+ * FP4Q_DATA_BAD_HESSIAN.  Argument errors as for fp4q_gptq_nvfp4.
+ */
+fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
+                              const float *importance, int off_lo, int off_hi, uint8_t *codes,
+                              uint8_t *scales, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Dequantization (the consumer side: only codes and dequantization scales
  * are stored, [FC] 4.).
  *   NVFP4 (block 16): x_hat = sign * fp32(fp32(q * E4M3(scale)) * S), S read

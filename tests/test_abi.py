@@ -164,6 +164,18 @@ def test_gptq_validation():
     assert gq(ld=100) == L.ERR_SHAPE
     assert gq(ld=130) == L.ERR_ALIGN
     assert gq(u=OUT + 4) == L.ERR_ALIGN
+    gm = lambda **kw: lib.fp4q_gptq_mxfp4(
+        kw.get("w", X), kw.get("rows", 4), kw.get("cols", 128), kw.get("ld", 128), kw.get("u", OUT), None,
+        kw.get("lo", -1), kw.get("hi", 0), OUT, OUT, kw.get("ws", WS), wsb, None)
+    assert gm(w=None) == L.ERR_NULL
+    assert gm(u=None) == L.ERR_NULL
+    assert gm(ws=None) == L.ERR_WORKSPACE
+    assert gm(lo=1, hi=2) == L.ERR_ARG
+    assert gm(lo=-16, hi=0) == L.ERR_ARG
+    assert gm(cols=160, ld=160) == L.ERR_SHAPE
+    assert gm(ld=100) == L.ERR_SHAPE
+    assert gm(ld=130) == L.ERR_ALIGN
+    assert gm(rows=0) == L.OK  # empty: nothing to do
 
 
 def test_gemm_validation():

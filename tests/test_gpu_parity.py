@@ -588,6 +588,71 @@ def test_gptq_block_updates_against_oracle():
     assert abs(lg - lo) <= 1e-3 * lo
 
 
+@pytest.mark.parametrize("wmse", [False, True])
+def test_gptq_mxfp4_single_batch_bitexact(wmse):
+    """MXFP4 GPTQ, one batch (no contraction): bit-exact codes and exponents."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(37, 128, seed=120)
+    im = imp if wmse else None
+    for window in ((-1, 0), (-2, 1)):
+        res = fq.gptq_mxfp4(w.to(DEV), U, None if im is None else im.to(DEV), window=window, check=True)
+        torch.cuda.synchronize()
+        codes, scales = GQ.gptq_mxfp4(w.numpy(), U, None if im is None else im.numpy(), window=window)
+        _assert_equal("gptq_mx scales", _np(res.scales), scales)
+        _assert_equal("gptq_mx codes", _np(res.codes), codes)
+
+
+def test_gptq_mxfp4_without_feedback_equals_sweep():
+    fq = _fp4()
+    w = W.random_matrix(64, 512, seed=121, dist="t4").to(DEV)
+    U = np.diag(np.exp(np.random.default_rng(122).normal(0, 0.3, 512))).astype(np.float32)
+    imp = W.random_importance(512, seed=123).to(DEV)
+    for im in (None, imp):
+        g = fq.gptq_mxfp4(w, U, im, check=True)
+        s_ = fq.quantize_mxfp4(w, im, check=True)
+        torch.cuda.synchronize()
+        _assert_equal("codes", _np(g.codes), _np(s_.codes))
+        _assert_equal("scales", _np(g.scales), _np(s_.scales))
+
+
+@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (192, 512, True), (64, 2304, False)])
+def test_gptq_mxfp4_multi_batch_against_oracle(rows, cols, wmse):
+    """MXFP4 GPTQ across batches (and, at 2304 columns, across 1024-column
+    blocks): the same bar as NVFP4 GPTQ."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(rows, cols, seed=124 + cols)
+    im = imp if wmse else None
+    res = fq.gptq_mxfp4(w.to(DEV), U, None if im is None else im.to(DEV), check=True)
+    torch.cuda.synchronize()
+    codes, scales = GQ.gptq_mxfp4(w.numpy(), U, None if im is None else im.numpy())
+    gc, gs = _np(res.codes), _np(res.scales)
+    assert np.mean(Q.unpack_nibbles(gc) != Q.unpack_nibbles(codes)) <= 1e-3
+    assert np.mean(gs != scales) <= 1e-3
+    lg = GQ.proxy_loss_mx(w.numpy(), gc, gs, H)
+    lo = GQ.proxy_loss_mx(w.numpy(), codes, scales, H)
+    rtn = Q.quantize_mxfp4(w.numpy(), None if im is None else im.numpy())
+    lr = GQ.proxy_loss_mx(w.numpy(), rtn.codes, rtn.scales, H)
+    assert abs(lg - lo) <= 1e-3 * lo
+    assert lg < lr and lo < lr
+
+
+def test_gptq_data_errors_set_status():
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(8, 128, seed=130)
+    bad_w = w.clone()
+    bad_w[3, 17] = float("nan")
+    with pytest.raises(fq.FP4QError, match="non-finite"):
+        fq.gptq_mxfp4(bad_w.to(DEV), U, check=True)
+    with pytest.raises(fq.FP4QError, match="non-finite"):
+        fq.gptq_nvfp4(bad_w.to(DEV), U, check=True)
+    bad_imp = imp.clone()
+    bad_imp[5] = -1.0
+    with pytest.raises(fq.FP4QError, match="importance"):
+        fq.gptq_mxfp4(w.to(DEV), U, bad_imp.to(DEV), check=True)
+    with pytest.raises(fq.FP4QError, match="importance"):
+        fq.gptq_nvfp4(w.to(DEV), U, bad_imp.to(DEV), check=True)
+
+
 def test_gptq_bad_hessian_sets_status():
     fq = _fp4()
     w = W.random_matrix(8, 128, seed=115).to(DEV)
