@@ -779,6 +779,9 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) err8[k] = 0.0f;
   float V = 1.0f, R = 1.0f;
+  f32x4 un0 = *reinterpret_cast<const f32x4 *>(&Ub[0][8 * t]);
+  f32x4 un1 = *reinterpret_cast<const f32x4 *>(&Ub[0][8 * t + 4]);
+  float rdn = rdiag[0];
   static_for(std::make_integer_sequence<int, 16>{}, [&](auto tt_c) {
     constexpr int tt = decltype(tt_c)::value;
     if constexpr (MX && (tt & 3) == 0) {
@@ -862,19 +865,28 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int i = 8 * tt + k;
+      // this column's U row was read one column ahead; read the next one now, and keep the reads
+      // here (the scheduler would sink them to their use), so their LDS latency stays off the
+      // column-to-column chain
+      const f32x4 u0 = un0, u1 = un1;
+      const float rd = rdn;
+      if (i + 1 < kGptqBatch) {
+        un0 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t]);
+        un1 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t + 4]);
+        rdn = rdiag[i + 1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const float wi = row_bcast<tt>(w[k]);
       const float us_i = wi * S_inv;
       const float y_i = us_i * R;
       const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
       const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
       const float what = MX ? q * V : (q * V) * S;  // q * V exact; NVFP4: one rounding by S
-      const float err = (wi - what) * rdiag[i];
+      const float err = (wi - what) * rd;
       if (t == tt) {
         code8 |= code << (4 * k);
         err8[k] = err;
       }
-      const f32x4 u0 = *reinterpret_cast<const f32x4 *>(&Ub[i][8 * t]);
-      const f32x4 u1 = *reinterpret_cast<const f32x4 *>(&Ub[i][8 * t + 4]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         w[kk] = fmaf(-err, u0[kk], w[kk]);
