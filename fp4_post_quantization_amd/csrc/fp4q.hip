@@ -732,24 +732,9 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     float *__restrict__ W, int64_t ld, int rows, int cols, int i1, const float *__restrict__ U,
     const float *__restrict__ imp, const float *__restrict__ gscale, int lo, int hi, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ scales, uint32_t *__restrict__ status) {
-  __shared__ float Ub[kGptqBatch][kGptqBatch];
+  __shared__ __attribute__((aligned(1024))) float Ub[kGptqBatch][kGptqBatch];
   __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch], impb[kGptqBatch];
   const int tid = threadIdx.x;
-  for (int e = tid; e < kGptqBatch * kGptqBatch / 4; e += kGptqBatchThreads) {
-    const int rr = e >> 5, c4 = e & 31;
-    *reinterpret_cast<f32x4 *>(&Ub[rr][c4 * 4]) =
-        *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + rr) * cols + i1 + c4 * 4);
-  }
-  if (tid < 128) {
-    Vtab[tid] = kE4M3.v[tid];
-    Rtab[tid] = kE4M3.r[tid];
-    const float d = U[(int64_t)(i1 + tid) * cols + i1 + tid];
-    if (!((d > 0.0f) & (d <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
-    rdiag[tid] = 1.0f / d;  // correctly rounded
-    impb[tid] = WMSE ? imp[i1 + tid] : 1.0f;
-    if (WMSE && !((impb[tid] >= 0.0f) & (impb[tid] <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_IMPORTANCE);
-  }
-  __syncthreads();
   const int lane = tid & 63;
   const int t = lane & 15;
   const int r = blockIdx.x * kGptqRowsPerWg + (tid >> 4);
@@ -757,16 +742,47 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
   constexpr bool MX = FMT == FP4Q_MXFP4;
   const float S = MX ? 1.0f : *gscale;
   const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
+  // Every global load is issued before any of them is waited for: the tables, the diagonal and the
+  // importance (threads < 128), the row's weights (dead rows read row 0), and the U block into
+  // registers, part j holding rows 8j .. 8j+7.  Part j is stored to LDS only when the columns reach
+  // row 8j, so the block arrives while the first columns are quantized (the compiler waits for
+  // each register's load precisely).
+  float tv = 0.0f, trc = 0.0f, dg = 1.0f, im = 1.0f;
+  if (tid < 128) {
+    tv = kE4M3.v[tid];
+    trc = kE4M3.r[tid];
+    dg = U[(int64_t)(i1 + tid) * cols + i1 + tid];
+    if (WMSE) im = imp[i1 + tid];
+  }
   float *wr = W + (int64_t)(live ? r : 0) * ld + i1 + 8 * t;
-  float w[8];
-  {
-    const f32x4 a = live ? *reinterpret_cast<const f32x4 *>(wr) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 b = live ? *reinterpret_cast<const f32x4 *>(wr + 4) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const f32x4 wa = *reinterpret_cast<const f32x4 *>(wr);
+  const f32x4 wb = *reinterpret_cast<const f32x4 *>(wr + 4);
+  f32x4 up[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w[k] = a[k];
-      w[4 + k] = b[k];
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int e = tid + kGptqBatchThreads * j;
+    up[j] = *reinterpret_cast<const f32x4 *>(U + (int64_t)(i1 + (e >> 5)) * cols + i1 + (e & 31) * 4);
+  }
+  // part j of the U block to LDS (rows 8j .. 8j+7; element e = tid + 256 j is Ub[e / 32][4 (e % 32)])
+  auto stash_u = [&](auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    const int e = tid + kGptqBatchThreads * j;
+    *reinterpret_cast<f32x4 *>(&Ub[e >> 5][(e & 31) * 4]) = up[j];
+  };
+  if (tid < 128) {
+    Vtab[tid] = tv;
+    Rtab[tid] = trc;
+    if (!((dg > 0.0f) & (dg <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
+    rdiag[tid] = 1.0f / dg;  // correctly rounded
+    impb[tid] = im;
+    if (WMSE && !((im >= 0.0f) & (im <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_IMPORTANCE);
+  }
+  stash_u(std::integral_constant<int, 0>{});
+  float w[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w[k] = live ? wa[k] : 0.0f;
+    w[4 + k] = live ? wb[k] : 0.0f;
   }
   if constexpr (MX) {  // no global-max pass checked the weights
     bool finite = true;
@@ -774,6 +790,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     for (int k = 0; k < 8; ++k) finite &= fabsf(w[k]) <= 3.402823466e38f;
     if (!finite) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
   }
+  __syncthreads();  // the tables and rows 0 .. 7 of the U block
   uint32_t code8 = 0;
   float err8[8];
 #pragma unroll
@@ -812,14 +829,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       const float L1 = loss_of_codes<WMSE>(z + 16, wg + 16, cvt8<false>(y + 16, 0u), cvt8<false>(y + 24, 0u), up);
       float Lm = ok ? L0 + L1 : __builtin_inff();
       int em = ok ? E : 0x7FFFFFFF;
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) {
-        const float L2 = __shfl_xor(Lm, m, 16);
-        const int e2 = __shfl_xor(em, m, 16);
-        const bool take = (L2 < Lm) | ((L2 == Lm) & (e2 < em));
-        Lm = take ? L2 : Lm;
-        em = take ? e2 : em;
-      }
+      row_argmin16(Lm, em);
       const int es = em == 0x7FFFFFFF ? max(-127, eb + lo) : em;
       V = pow2f(es);
       R = pow2f(-es);
@@ -849,14 +859,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       const float L = loss_of_codes<WMSE>(us, wg, cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), Vtab[pc]);
       float Lm = ok ? L : __builtin_inff();
       int pm = ok ? p : 0x7FFFFFFF;
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) {
-        const float L2 = __shfl_xor(Lm, m, 16);
-        const int p2 = __shfl_xor(pm, m, 16);
-        const bool take = (L2 < Lm) | ((L2 == Lm) & (p2 < pm));
-        Lm = take ? L2 : Lm;
-        pm = take ? p2 : pm;
-      }
+      row_argmin16(Lm, pm);
       const int ps = pm == 0x7FFFFFFF ? max(1, base + lo) : pm;
       V = Vtab[ps];
       R = Rtab[ps];
@@ -871,6 +874,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       const f32x4 u0 = un0, u1 = un1;
       const float rd = rdn;
       if (i + 1 < kGptqBatch) {
+        if (k == 7) {  // the next column opens rows 8 (tt + 1) ..: store them, for every thread
+          stash_u(std::integral_constant<int, (tt < 15 ? tt + 1 : 15)>{});
+          __syncthreads();
+        }
         un0 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t]);
         un1 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t + 4]);
         rdn = rdiag[i + 1];

@@ -140,6 +140,27 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
 }
 
+// One step of row_argmin16: combine with the lane that DPP control CTRL selects.
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(float &L, int &p) {
+  const float L2 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(L), CTRL, 0xF, 0xF, false));
+  const int p2 = __builtin_amdgcn_mov_dpp(p, CTRL, 0xF, 0xF, false);
+  const bool take = (L2 < L) | ((L2 == L) & (p2 < p));
+  L = take ? L2 : L;
+  p = take ? p2 : p;
+}
+
+// (loss, candidate) minimum over the 16 lanes of the caller's DPP row, ties
+// to the smaller candidate, in every lane of the row: pairs (quad_perm
+// [1,0,3,2]), quads ([2,3,0,1]), halves (row_half_mirror), the row
+// (row_mirror).
+__device__ __forceinline__ void row_argmin16(float &L, int &p) {
+  argmin_step<0xB1>(L, p);
+  argmin_step<0x4E>(L, p);
+  argmin_step<0x141>(L, p);
+  argmin_step<0x140>(L, p);
+}
+
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
   int i = __float_as_int(v);
