@@ -554,6 +554,93 @@ hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, co
   return hipGetLastError();
 }
 
+// Few-token product, M <= 16: one workgroup per 16 NT output columns, its W waves splitting K into
+// contiguous ranges of S steps of 128 elements (W S 128 = K).  v_mfma_scale_f32_16x16x128_f8f6f4
+// takes from lane l row l % 16 and the 32 elements at 32 (l / 16) of a step, and its accumulator
+// register v of lane l holds row 4 (l / 16) + v, column l % 16 (both checked on the device).  Step s
+// of a wave covers 128 contiguous elements of each row, so the four lanes of a row read 64
+// contiguous code bytes per load; a row's scale bytes for four steps arrive in one 16-byte load, and
+// lane l takes byte l / 16 of the step's word by a shift.  Every load is issued before the first
+// MFMA (the whole product's bytes are in flight at once); the NT column tiles of a workgroup share
+// one read of A.  The waves' sums meet in LDS and are added in ascending K order.
+template <int S, int NT, typename OutT>
+__global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__restrict__ A,
+                                                              const uint8_t *__restrict__ As,
+                                                              const uint8_t *__restrict__ B,
+                                                              const uint8_t *__restrict__ Bs, int M, int N, int K,
+                                                              float alpha, OutT *__restrict__ C, int64_t ldc) {
+  static_assert(S % 4 == 0 && S <= 8 && NT >= 1 && NT <= 2, "steps per wave, tiles per workgroup");
+  __shared__ float part[NT][16][64][4];  // [tile][wave][lane][register]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 16 * NT;
+  const int r16 = lane & 15, h = lane >> 4;
+  const int kw0 = wave * S * 128;  // this wave's first K element
+  const int64_t kb = K / 2, sb = K / 32;
+  const bool a_ok = r16 < M;
+  const int arow = min(r16, M - 1);
+  const uint8_t *ap = A + (int64_t)arow * kb + kw0 / 2 + 16 * h;
+  i32x4 bc[NT][S], ac[S], bsw[NT][S / 4], asw[S / 4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int brow = min(n0 + 16 * t + r16, N - 1);
+    const uint8_t *bp = B + (int64_t)brow * kb + kw0 / 2 + 16 * h;
+#pragma unroll
+    for (int st = 0; st < S; ++st) bc[t][st] = *reinterpret_cast<const i32x4 *>(bp + 64 * st);
+#pragma unroll
+    for (int q = 0; q < S / 4; ++q)  // scale bytes of steps 4q .. 4q+3 (blocks 4 step + h)
+      bsw[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow * sb + kw0 / 32 + 16 * q);
+  }
+#pragma unroll
+  for (int st = 0; st < S; ++st) ac[st] = a_ok ? *reinterpret_cast<const i32x4 *>(ap + 64 * st) : i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < S / 4; ++q)  // rows past M multiply zero codes: any finite scale (2^0) keeps them zero
+    asw[q] = a_ok ? *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 32 + 16 * q)
+                  : i32x4{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  f32x4v acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  unroll(std::make_integer_sequence<int, S>{}, [&](auto st_c) {
+    constexpr int st = decltype(st_c)::value;
+    const i32x8 a = {ac[st][0], ac[st][1], ac[st][2], ac[st][3], 0, 0, 0, 0};
+    const int sa = (int)((uint32_t)asw[st / 4][st % 4] >> (8 * h));  // byte 0: block 4 st + h
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const i32x8 b = {bc[t][st][0], bc[t][st][1], bc[t][st][2], bc[t][st][3], 0, 0, 0, 0};
+      const int sbv = (int)((uint32_t)bsw[t][st / 4][st % 4] >> (8 * h));
+      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[t], 4, 4, 0, sa, 0, sbv);
+    }
+  });
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[t][wave][lane][v] = acc[t][v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256 * NT; i += blockDim.x) {
+    const int t = i >> 8, m = (i >> 4) & 15, j = i & 15;
+    const int l = 16 * (m >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
+    float sum = part[t][0][l][v];
+    for (int w = 1; w < waves; ++w) sum = sum + part[t][w][l][v];
+    const int col = n0 + 16 * t + j;
+    if (m < M && col < N) store_out(C + (int64_t)m * ldc + col, alpha * sum);
+  }
+}
+
+// Steps per wave of the few-token kernel for this shape, or 0 when it does not apply (M > 16, K not a
+// multiple of 512, or no S in {4, 8} with W = K / (128 S) <= 16 waves).
+// Column tiles per workgroup of the few-token kernel: two (one read of A serves 32 columns) for more
+// than one token once the output is wide enough to keep the chip busy with half as many
+// workgroups; past 16384 columns one tile measured faster up to eight tokens.
+int skinny_tiles(int64_t m, int64_t n) { return (m > 1 && n >= 8192 && (n <= 16384 || m > 8)) ? 2 : 1; }
+
+int skinny_steps(int64_t m, int64_t k) {
+  if (m > 16 || m <= 0 || k % 512) return 0;
+  const int64_t nst = k / 128;
+  for (int S : {4, 8})
+    if (nst % S == 0 && nst / S <= 16) return S;
+  return 0;
+}
+
 // C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the split partial sums added in ascending K order
 // (splits <= kMaxSplits).  Row blockIdx.y, columns from blockIdx.x; every partial is loaded before
 // the first addition, so the loads overlap.
@@ -647,6 +734,22 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
                     float alpha, OutT *c, int64_t ldc, hipStream_t s, uint8_t *ws = nullptr) {
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+  // at most 16 tokens: the few-token kernel (whole K in flight, no workspace)
+  const int S = skinny_steps(m, k);
+  if (S && aligned(as, 16) && aligned(bs, 16)) {
+    const int waves = k / (128 * S);
+    const int nt = skinny_tiles(m, n);
+    const dim3 grid((unsigned)((n + 16 * nt - 1) / (16 * nt))), block(64 * waves);
+    if (S == 4 && nt == 1)
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<4, 1, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+    else if (S == 4)
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<4, 2, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+    else if (nt == 1)
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<8, 1, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+    else
+      hipLaunchKernelGGL((mx_gemm_skinny_kernel<8, 2, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+    return hipGetLastError();
+  }
   const int splits = gemm_mxfp4_splits(m, n, k);
   if (ws && splits > 1 && aligned(as, 4) && aligned(bs, 4)) {
     // few tokens: K split over workgroups, partial sums in the workspace, then added in K order

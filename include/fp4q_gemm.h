@@ -52,8 +52,9 @@ extern "C" {
  *               scales for its FP4 product).  The result is identical to
  *               the one without a workspace;
  *             - few-token products (m <= 64) whose column tiles alone would
- *               leave CUs idle split K into S contiguous ranges (S chosen
- *               from m, n and k) and keep the S float32 partial sums there.
+ *               leave CUs idle, and that the few-token kernel below does not
+ *               take, split K into S contiguous ranges (S chosen from m, n
+ *               and k) and keep the S float32 partial sums there.
  *
  * Arithmetic: the products of two decoded elements are exact.  They are
  * summed on the matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), 64
@@ -64,8 +65,14 @@ extern "C" {
  * stages); otherwise step j holds elements 64 j .. 64 j + 63.  With a K
  * split, each range is summed that way and
  * the S partial sums are then added in ascending K order, which can round
- * differently from a single accumulation.  Either way the result differs
- * from the exact product by a few float32 roundings per step.
+ * differently from a single accumulation.  Products of at most 16 tokens
+ * with K a multiple of 512 and at most 16384, and both scale arrays 16-byte
+ * aligned, go to a few-token kernel (no workspace) that sums on
+ * v_mfma_scale_f32_16x16x128_f8f6f4: K is cut into W contiguous ranges of S
+ * steps of 128 contiguous elements (S = 4 or 8, W = k / (128 S) <= 16),
+ * each range is accumulated step by step in float32, and the W range sums
+ * are added in ascending K order.  Either way the result differs from the
+ * exact product by a few float32 roundings per step.
  *
  * Alignment: a_codes and b_codes 16-byte aligned.  c aligned to its element
  * size.
@@ -83,7 +90,8 @@ fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, c
 
 /* Workspace that speeds up fp4q_gemm_mxfp4 when K is a multiple of 256: the
  * larger of (m + n) * k / 32 + 32 bytes (scale copies) and, for a split few-
- * token product, S * m * n * 4 bytes (partial sums).  0 when K is not a
+ * token product, S * m * n * 4 bytes (partial sums; sized also where the
+ * few-token kernel, which needs none, takes the product).  0 when K is not a
  * multiple of 256 (no workspace is used) and for invalid sizes. */
 size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 

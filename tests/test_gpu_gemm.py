@@ -171,8 +171,44 @@ def test_gemm_scale_reorganisation_is_transparent(m, n, k):
     _check(c1[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), ac, as_, bc, bs, k, rows=rows)
 
 
-# few-token products: K split over workgroups (the workspace holds the partial sums)
-@pytest.mark.parametrize("m,n,k", [(1, 1000, 4096), (16, 4096, 4096), (40, 700, 14336)])
+# at most 16 tokens: the few-token kernel (16 or 32 columns per workgroup, K split over its waves)
+@pytest.mark.parametrize("m,n,k", [(1, 16, 512), (3, 100, 4096), (16, 4096, 4096), (7, 1000, 14336),
+                                   (16, 33, 8192), (1, 4096, 1536), (5, 8200, 1024), (16, 14336, 4096),
+                                   (2, 8192, 14336)])
+def test_gemm_few_tokens_exact(m, n, k):
+    rng = np.random.default_rng(3400 + m + n + k)
+    ac, _ = _rand_mx(rng, m, k)
+    bc, _ = _rand_mx(rng, n, k)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    np.testing.assert_array_equal(_run(ac, as_, bc, bs), GM.gemm_mxfp4(ac, as_, bc, bs))
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (5, 300, 4096, torch.bfloat16),
+                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16)])
+def test_gemm_few_tokens_within_bound(m, n, k, out_dtype):
+    fq = _fq()
+    rng = np.random.default_rng(3500 + m + n + k)
+    ac, as_ = _rand_mx(rng, m, k, 100, 150)
+    bc, bs = _rand_mx(rng, n, k, 100, 150)
+    A = GM.decode_mxfp4_64(ac, as_)
+    B = GM.decode_mxfp4_64(bc, bs)
+    ref = -1.5 * GM.gemm(A, B)
+    tol = 1.5 * _bound(A, B, k)
+    if out_dtype == torch.bfloat16:
+        tol = tol + 2.0 ** -8 * np.abs(ref)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    big = torch.full((m, n + 8), 7.0, device=DEV, dtype=out_dtype)
+    fq.gemm_mxfp4((a, asd), (b, bsd), alpha=-1.5, out_dtype=out_dtype, out=big[:, :n])
+    torch.cuda.synchronize()
+    got = big.float().cpu().numpy().astype(np.float64)
+    assert (np.abs(got[:, :n] - ref) <= tol).all()
+    assert (got[:, n:] == 7.0).all()  # the padding past n is untouched
+
+
+# few-token products beyond the few-token kernel (more than 16 tokens, or K not a multiple of 512): K
+# split over workgroups (the workspace holds the partial sums)
+@pytest.mark.parametrize("m,n,k", [(17, 1000, 4096), (32, 4096, 4096), (40, 700, 14336), (5, 1000, 4352)])
 def test_gemm_few_tokens_split_k_exact(m, n, k):
     rng = np.random.default_rng(3100 + m + n + k)
     ac, _ = _rand_mx(rng, m, k)
@@ -182,8 +218,9 @@ def test_gemm_few_tokens_split_k_exact(m, n, k):
     np.testing.assert_array_equal(_run(ac, as_, bc, bs), GM.gemm_mxfp4(ac, as_, bc, bs))
 
 
-@pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (8, 2000, 4096, torch.bfloat16),
-                                             (33, 1024, 8192, torch.float32), (64, 512, 14336, torch.float32)])
+@pytest.mark.parametrize("m,n,k,out_dtype", [(20, 4096, 14336, torch.float32), (24, 2000, 4096, torch.bfloat16),
+                                             (33, 1024, 8192, torch.float32), (64, 512, 14336, torch.float32),
+                                             (1, 4096, 14592, torch.float32)])
 def test_gemm_few_tokens_split_k_within_bound(m, n, k, out_dtype):
     fq = _fq()
     rng = np.random.default_rng(3200 + m + n + k)
