@@ -81,12 +81,17 @@ WORKLOADS = {
     "c3b": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
-    # GPTQ: per-dispatch bytes averaged over the 31 trailing updates (rest = 3968 ... 128 columns,
-    # mean 2048: read and write W[:, rest], read the batch's errors and U[batch, rest]) and the
+    # GPTQ: per-dispatch bytes averaged over the 31 updates of a call (1024-column blocks of eight
+    # 128-column batches): 28 in-block updates (the rest of the block, r = 896 ... 128 columns: read
+    # and write W[:, rest], read the batch's errors and U[batch, rest]) and 3 block updates (all later
+    # columns, L = 3072, 2048, 1024, with the block's 1024 error columns and U[block, later]); and the
     # 32 batch kernels (read and write 128 columns, write codes and scales, read U's 128 x 128 block)
     "gptq": {"stem": "gptq_nvfp4_f32_4096x4096", "kernel": "gptq_update_kernel",
              "title": "GPTQ with ScaleSweep group scales, fp32 4096x4096, MSE and WMSE",
-             "alg_bytes": {"gptq_update_kernel": 4096 * 2048 * 8 + 4096 * 128 * 4 + 128 * 2048 * 4,
+             "alg_bytes": {"gptq_update_kernel": (sum(4 * (4096 * r * 8 + 4096 * 128 * 4 + 128 * r * 4)
+                                                      for r in range(128, 1024, 128))
+                                                  + sum(4096 * L * 8 + 4096 * 1024 * 4 + 1024 * L * 4
+                                                        for L in (1024, 2048, 3072))) / 31,
                            "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4}},
     # W4A4 8B layer at 8192 tokens.  Per GEMM dispatch: A (codes + scales) + B (codes + scales)
     # + C (bf16), flops 2 M N K, averaged over the projections each kernel instantiation serves
