@@ -366,7 +366,9 @@ def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
     """C = fp32(S_a S_b) * A_hat @ B_hat^T for NVFP4 operands (NVFP4Result
     or (codes, scales, global_scale) triples as written by quantize_nvfp4):
     A is M x K, B is N x K.  The operands are decoded to bfloat16 (exact) in
-    a workspace, allocated here unless ``workspace_buf`` is given."""
+    a workspace, allocated here unless ``workspace_buf`` is given; products of
+    at most 16 tokens (K a multiple of 256 up to 16384) decode in registers
+    and need none."""
     lib = L.load()
     ac, as_, ag = (a.codes, a.scales, a.global_scale) if isinstance(a, NVFP4Result) else a
     bc, bs, bg = (b.codes, b.scales, b.global_scale) if isinstance(b, NVFP4Result) else b
@@ -386,10 +388,11 @@ def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
     if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     need = lib.fp4q_gemm_nvfp4_workspace_bytes(m, n, k)
-    if workspace_buf is None or workspace_buf.numel() < need:
-        workspace_buf = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if need and (workspace_buf is None or workspace_buf.numel() < need):
+        workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     code = L.F32 if out.dtype == torch.float32 else L.BF16
     L.check(lib.fp4q_gemm_nvfp4(ac.data_ptr(), as_.data_ptr(), ag.data_ptr(), bc.data_ptr(), bs.data_ptr(),
                                 bg.data_ptr(), m, n, k, code, out.data_ptr(), out.stride(0),
-                                workspace_buf.data_ptr(), workspace_buf.numel(), _stream(dev)))
+                                _ptr(workspace_buf) if need else None, workspace_buf.numel() if need else 0,
+                                _stream(dev)))
     return out

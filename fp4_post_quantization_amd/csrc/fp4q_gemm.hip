@@ -576,26 +576,31 @@ __global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__r
   const int r16 = lane & 15, h = lane >> 4;
   const int kw0 = wave * S * 128;  // this wave's first K element
   const int64_t kb = K / 2, sb = K / 32;
-  const bool a_ok = r16 < M;
-  const int arow = min(r16, M - 1);
+  const int arow = min(r16, M - 1);  // rows past M repeat row M - 1: computed, never stored
   const uint8_t *ap = A + (int64_t)arow * kb + kw0 / 2 + 16 * h;
+  // every load is issued before the first MFMA, in the order of use: the scale words (16 bytes per
+  // four steps), then step by step the codes of A and B, so that the first steps can start while
+  // the later loads are in flight
   i32x4 bc[NT][S], ac[S], bsw[NT][S / 4], asw[S / 4];
+  int brow[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int brow = min(n0 + 16 * t + r16, N - 1);
-    const uint8_t *bp = B + (int64_t)brow * kb + kw0 / 2 + 16 * h;
+  for (int t = 0; t < NT; ++t) brow[t] = min(n0 + 16 * t + r16, N - 1);
 #pragma unroll
-    for (int st = 0; st < S; ++st) bc[t][st] = *reinterpret_cast<const i32x4 *>(bp + 64 * st);
+  for (int q = 0; q < S / 4; ++q) {  // scale bytes of steps 4q .. 4q+3 (blocks 4 step + h)
+    asw[q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 32 + 16 * q);
 #pragma unroll
-    for (int q = 0; q < S / 4; ++q)  // scale bytes of steps 4q .. 4q+3 (blocks 4 step + h)
-      bsw[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow * sb + kw0 / 32 + 16 * q);
+    for (int t = 0; t < NT; ++t)
+      bsw[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow[t] * sb + kw0 / 32 + 16 * q);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  unroll(std::make_integer_sequence<int, S>{}, [&](auto st_c) {
+    constexpr int st = decltype(st_c)::value;
+    ac[st] = *reinterpret_cast<const i32x4 *>(ap + 64 * st);
 #pragma unroll
-  for (int st = 0; st < S; ++st) ac[st] = a_ok ? *reinterpret_cast<const i32x4 *>(ap + 64 * st) : i32x4{0, 0, 0, 0};
-#pragma unroll
-  for (int q = 0; q < S / 4; ++q)  // rows past M multiply zero codes: any finite scale (2^0) keeps them zero
-    asw[q] = a_ok ? *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 32 + 16 * q)
-                  : i32x4{0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F, 0x7F7F7F7F};
+    for (int t = 0; t < NT; ++t)
+      bc[t][st] = *reinterpret_cast<const i32x4 *>(B + (int64_t)brow[t] * kb + kw0 / 2 + 16 * h + 64 * st);
+    __builtin_amdgcn_sched_barrier(0);
+  });
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   f32x4v acc[NT];
 #pragma unroll
@@ -626,19 +631,180 @@ __global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__r
   }
 }
 
-// Steps per wave of the few-token kernel for this shape, or 0 when it does not apply (M > 16, K not a
-// multiple of 512, or no S in {4, 8} with W = K / (128 S) <= 16 waves).
 // Column tiles per workgroup of the few-token kernel: two (one read of A serves 32 columns) for more
 // than one token once the output is wide enough to keep the chip busy with half as many
 // workgroups; past 16384 columns one tile measured faster up to eight tokens.
 int skinny_tiles(int64_t m, int64_t n) { return (m > 1 && n >= 8192 && (n <= 16384 || m > 8)) ? 2 : 1; }
 
+// Steps per wave of the few-token kernel for this shape, or 0 when it does not apply (M > 16, K not a
+// multiple of 512, or no S in {4, 8} with W = K / (128 S) <= 16 waves).
 int skinny_steps(int64_t m, int64_t k) {
   if (m > 16 || m <= 0 || k % 512) return 0;
   const int64_t nst = k / 128;
   for (int S : {4, 8})
     if (nst % S == 0 && nst / S <= 16) return S;
   return 0;
+}
+
+// ---------------------------------------------------------------- few-token NVFP4 product ------
+// An E4M3 block scale V splits into a power of two 2^e and a significand m (V = 2^e m): normal
+// patterns 2^(E-7) and 1 + F/8, subnormal ones 2^-9 and F, with the sign on m; NaN patterns give
+// m = NaN, and zero m = 0.  The scaled FP4 convert applies only the exponent of its scale operand
+// (checked on the device), so it yields q 2^e exactly in float16, and one packed float16 multiply
+// by m makes q V, exact as well: q has two significant bits and m four, and |q V| lies in
+// [2^-10, 2688], inside float16's normal range.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 nv_scale_parts(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, f = b & 7u;
+  uint32_t p2, m;
+  if (e == 15u && f == 7u) {
+    p2 = 0x3F800000u;  // 1.0
+    m = 0x7E00u;       // NaN
+  } else if (e == 0u) {
+    p2 = 118u << 23;  // 2^-9
+    m = __builtin_bit_cast(uint16_t, (_Float16)(float)f);
+  } else {
+    p2 = (e + 120u) << 23;  // 2^(E-7)
+    m = 0x3C00u | (f << 7);  // 1 + F/8
+  }
+  m |= (b & 0x80u) << 8;
+  return make_uint2(p2, m | (m << 16));
+}
+
+// Eight consecutive FP4 codes (one dword) times the block scale held in parts (p2, m2).
+__device__ __forceinline__ f16x8 nv_decode8(uint32_t dw, uint2 parts) {
+  const float p2 = __uint_as_float(parts.x);
+  const f16x2 m = __builtin_bit_cast(f16x2, parts.y);
+  const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, p2, 0) * m;
+  const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, p2, 1) * m;
+  const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, p2, 2) * m;
+  const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(dw, p2, 3) * m;
+  return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// Scale byte of lane quarter h for group g, half i of its 32 elements, out of the 16-byte loads
+// v[] holding a row's scale bytes of the wave's range (8 per 128-element group).
+template <int G, int I>
+__device__ __forceinline__ uint32_t nv_scale_byte(const i32x4 *v, int h) {
+  constexpr int q = G / 2, d = 2 * (G % 2);
+  const uint32_t w = (uint32_t)((h & 2) ? v[q][d + 1] : v[q][d]);
+  return (w >> (8 * (2 * (h & 1) + I))) & 0xFFu;
+}
+
+// Few-token NVFP4 product, M <= 16: one workgroup per 16 NT output columns, its W waves splitting K
+// into contiguous ranges of S groups of 128 elements (W S 128 = K).  In group g, lane l (row l % 16,
+// quarter h = l / 16) holds the 32 elements at 128 g + 32 h of its row (one 16-byte load; the four
+// lanes of a row read 64 contiguous bytes) and feeds them to four v_mfma_f32_16x16x32_f16 steps,
+// eight at a time (step s: elements 8 s .. 8 s + 7 of every lane, in both operands alike).  Every
+// code and scale load is issued before the first decode, in the order of use.  The accumulator's
+// register v of lane l holds row 4 (l / 16) + v, column l % 16; the waves' sums meet in LDS, are
+// added in ascending K order and scaled by fp32(S_a S_b).  The small variants are held to 64 VGPRs,
+// so that two 16-wave workgroups fit on a CU.
+template <int S, int NT, typename OutT>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(S * NT <= 4 ? 8 : 4))) void
+nv_gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+                      const uint8_t *__restrict__ Bs, int M, int N, int K, const float *__restrict__ ga,
+                      const float *__restrict__ gb, OutT *__restrict__ C, int64_t ldc) {
+  static_assert(S % 2 == 0 && S <= 8 && NT >= 1 && NT <= 2, "groups per wave, tiles per workgroup");
+  __shared__ float part[NT][16][64][4];  // [tile][wave][lane][register]
+  __shared__ uint2 scale_parts[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int n0 = blockIdx.x * 16 * NT;
+  const int r16 = lane & 15, h = lane >> 4;
+  const int kw0 = wave * S * 128;  // this wave's first K element
+  const int64_t kb = K / 2, sb = K / 16;
+  const int arow = min(r16, M - 1);
+  // every load first, in the order of use: scale bytes (16 bytes per two groups), then group by group
+  // the codes of A and B (one 16-byte load each), so the first groups' decode overlaps the rest
+  i32x4 bc[NT][S], ac[S], bsv[NT][S / 2], asv[S / 2];
+  int brow[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) brow[t] = min(n0 + 16 * t + r16, N - 1);
+  // rows past M repeat row M - 1 (and columns past N column N - 1): computed, never stored
+#pragma unroll
+  for (int q = 0; q < S / 2; ++q) {
+    asv[q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 16 + 16 * q);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      bsv[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow[t] * sb + kw0 / 16 + 16 * q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const uint8_t *ap = A + (int64_t)arow * kb + kw0 / 2 + 16 * h;
+  unroll(std::make_integer_sequence<int, S>{}, [&](auto g_c) {
+    constexpr int g = decltype(g_c)::value;
+    ac[g] = *reinterpret_cast<const i32x4 *>(ap + 64 * g);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      bc[t][g] = *reinterpret_cast<const i32x4 *>(B + (int64_t)brow[t] * kb + kw0 / 2 + 16 * h + 64 * g);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) scale_parts[i] = nv_scale_parts((uint32_t)i);
+  __syncthreads();
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  unroll(std::make_integer_sequence<int, S>{}, [&](auto g_c) {
+    constexpr int g = decltype(g_c)::value;
+    const uint2 sa0 = scale_parts[nv_scale_byte<g, 0>(asv, h)], sa1 = scale_parts[nv_scale_byte<g, 1>(asv, h)];
+    uint2 sbp[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sbp[t][0] = scale_parts[nv_scale_byte<g, 0>(bsv[t], h)];
+      sbp[t][1] = scale_parts[nv_scale_byte<g, 1>(bsv[t], h)];
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const f16x8 a = nv_decode8((uint32_t)ac[g][st], st < 2 ? sa0 : sa1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f16x8 b = nv_decode8((uint32_t)bc[t][g][st], st < 2 ? sbp[t][0] : sbp[t][1]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+      }
+    }
+  });
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[t][wave][lane][v] = acc[t][v];
+  __syncthreads();
+  const float alpha = (*ga) * (*gb);
+  for (int i = threadIdx.x; i < 256 * NT; i += blockDim.x) {
+    const int t = i >> 8, m = (i >> 4) & 15, j = i & 15;
+    const int l = 16 * (m >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
+    float sum = part[t][0][l][v];
+    for (int w = 1; w < waves; ++w) sum = sum + part[t][w][l][v];
+    const int col = n0 + 16 * t + j;
+    if (m < M && col < N) store_out(C + (int64_t)m * ldc + col, alpha * sum);
+  }
+}
+
+// Groups per wave of the few-token NVFP4 kernel, or 0 when it does not apply (M > 16, K not a
+// multiple of 256, or no S in {2, 4, 8} with W = K / (128 S) <= 16 waves).
+int nv_skinny_groups(int64_t m, int64_t k) {
+  if (m > 16 || m <= 0 || k % 256) return 0;
+  const int64_t ng = k / 128;
+  for (int S : {2, 4, 8})
+    if (ng % S == 0 && ng / S <= 16) return S;
+  return 0;
+}
+
+template <typename OutT>
+hipError_t launch_nv_skinny(const uint8_t *a, const uint8_t *as, const float *ga, const uint8_t *b,
+                            const uint8_t *bs, const float *gb, int m, int n, int k, int S, OutT *c, int64_t ldc,
+                            hipStream_t s) {
+  const int nt = skinny_tiles(m, n) == 2 && S <= 4 ? 2 : 1;
+  const dim3 grid((unsigned)((n + 16 * nt - 1) / (16 * nt))), block(64 * (k / (128 * S)));
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a, as, b, bs, m, n, k, ga, gb, c, ldc); };
+  if (S == 2)
+    nt == 1 ? go(nv_gemm_skinny_kernel<2, 1, OutT>) : go(nv_gemm_skinny_kernel<2, 2, OutT>);
+  else if (S == 4)
+    nt == 1 ? go(nv_gemm_skinny_kernel<4, 1, OutT>) : go(nv_gemm_skinny_kernel<4, 2, OutT>);
+  else
+    go(nv_gemm_skinny_kernel<8, 1, OutT>);
+  return hipGetLastError();
 }
 
 // C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the split partial sums added in ascending K order
@@ -910,6 +1076,7 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
 
 extern "C" size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || n < 0 || k <= 0) return 0;
+  if (fp4q_gemm::nv_skinny_groups(m, k)) return 0;  // the few-token kernel decodes in registers
   return (size_t)((m + n) * fp4q_gemm::padded_k(k) * 2);
 }
 
@@ -926,11 +1093,25 @@ extern "C" fp4q_status_t fp4q_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *
   const int64_t kp = padded_k(k);
   if (((m + 127) / 128) * ((n + 127) / 128) >= ((int64_t)1 << 31) || (m + n) * (kp / 16) >= ((int64_t)1 << 40))
     return FP4Q_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  // at most 16 tokens: the few-token kernel decodes both operands in registers (no workspace)
+  const int S = nv_skinny_groups(m, k);
+  if (S) {
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 16) || !aligned(b_scales, 16) ||
+        !aligned(a_global, 4) || !aligned(b_global, 4) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
+      return FP4Q_ERR_ALIGN;
+    const hipError_t e =
+        out_dtype == FP4Q_F32
+            ? launch_nv_skinny<float>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
+                                      (int)k, S, (float *)c, ldc, s)
+            : launch_nv_skinny<uint16_t>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
+                                         (int)k, S, (uint16_t *)c, ldc, s);
+    return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
+  }
   if (!workspace || workspace_bytes < fp4q_gemm_nvfp4_workspace_bytes(m, n, k)) return FP4Q_ERR_WORKSPACE;
   if (!aligned(a_codes, 8) || !aligned(b_codes, 8) || !aligned(a_global, 4) || !aligned(b_global, 4) ||
       !aligned(workspace, 16) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
     return FP4Q_ERR_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
   uint16_t *wa = (uint16_t *)workspace;
   uint16_t *wb = wa + m * kp;
   const int64_t ta = m * (kp / 16), tb = n * (kp / 16);

@@ -96,7 +96,9 @@ fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, c
 size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* Workspace the NVFP4 product needs: (m + n) * roundup(k, 32) * 2 bytes (the
- * operands decoded to bfloat16).  0 for invalid sizes. */
+ * operands decoded to bfloat16); 0 for the few-token products (m <= 16, k a
+ * multiple of 256 up to 16384), which decode in registers, and for invalid
+ * sizes. */
 size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* C = fp32(S_a * S_b) * (A_hat * B_hat^T) for NVFP4 operands, where A_hat and
@@ -114,6 +116,8 @@ size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   out_dtype, c, ldc  as for fp4q_gemm_mxfp4.
  *   workspace device memory of at least fp4q_gemm_nvfp4_workspace_bytes(m,
  *             n, k) bytes, 16-byte aligned; its contents are overwritten.
+ *             None is needed (NULL is accepted) where that size is 0: the
+ *             few-token products below.
  *
  * The scaled FP4 matrix core takes only power-of-two (E8M0) scales per 32
  * elements.  Folding an E4M3 block scale into the elements would need
@@ -124,8 +128,18 @@ size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * product is exact, summed in float32 one 16-element step of K at a time in
  * ascending K order.  The result is multiplied by fp32(S_a * S_b).
  *
- * Alignment: a_codes and b_codes 8-byte aligned; the global-scale pointers
- * 4-byte aligned; c aligned to its element size.
+ * Products of at most 16 tokens with K a multiple of 256 and at most 16384
+ * skip that pass: a few-token kernel decodes the codes in registers (float16
+ * holds q * E4M3(p) exactly as well) and sums on the float16 matrix cores
+ * (v_mfma_f32_16x16x32_f16).  K is cut into W contiguous ranges of S groups
+ * of 128 elements (S = 2, 4 or 8, W = k / (128 S) <= 16); each range is
+ * accumulated in float32 one 32-element step at a time, and the W range sums
+ * are added in ascending K order before the multiplication by
+ * fp32(S_a * S_b).
+ *
+ * Alignment: a_codes and b_codes 8-byte aligned (16-byte, and the scale
+ * arrays too, for the few-token products); the global-scale pointers 4-byte
+ * aligned; c aligned to its element size.
  *
  * Returns FP4Q_ERR_NULL, FP4Q_ERR_SHAPE, FP4Q_ERR_ARG, FP4Q_ERR_WORKSPACE,
  * FP4Q_ERR_ALIGN or FP4Q_ERR_HIP, as for fp4q_gemm_mxfp4 (nothing is needed

@@ -211,10 +211,16 @@ def test_gemm_nvfp4_validation():
     L, lib = _lib()
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(64, 32, 48) == (64 + 32) * 64 * 2
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(64, 32, 0) == 0
+    # products of at most 16 tokens with K a multiple of 256 (up to 16384) decode in registers
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 4096, 4096) == 0
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(1, 4096, 16384) == 0
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(17, 4096, 4096) == (17 + 4096) * 4096 * 2
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 4096, 4224) == (16 + 4096) * 4224 * 2
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 64, 32768) == (16 + 64) * 32768 * 2
 
     def gn(**kw):
         m, n, k = kw.get("m", 64), kw.get("n", 64), kw.get("k", 128)
-        return lib.fp4q_gemm_nvfp4(kw.get("a", X), OUT, kw.get("ag", OUT), X, OUT, OUT, m, n, k,
+        return lib.fp4q_gemm_nvfp4(kw.get("a", X), kw.get("as_", OUT), kw.get("ag", OUT), X, OUT, OUT, m, n, k,
                                    kw.get("dt", L.F32), kw.get("c", WS), kw.get("ldc", 64), kw.get("ws", WS),
                                    kw.get("wsb", 1 << 30), None)
     assert gn(a=None) == L.ERR_NULL
@@ -227,6 +233,9 @@ def test_gemm_nvfp4_validation():
     assert gn(ws=WS + 8) == L.ERR_ALIGN
     assert gn(ag=OUT + 2) == L.ERR_ALIGN
     assert gn(m=0, a=None, ag=None, c=None, ws=None) == L.OK
+    # the few-token path needs 16-byte aligned codes and scales, and no workspace
+    assert gn(m=4, k=512, as_=OUT + 4, ws=None) == L.ERR_ALIGN
+    assert gn(m=4, k=512, a=X + 8, ws=None) == L.ERR_ALIGN
 
 
 def test_empty_shapes_need_no_device_for_dequant_and_hadamard():

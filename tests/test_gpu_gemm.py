@@ -37,6 +37,11 @@ def _fq():
     return fq
 
 
+def _fq_lib():
+    from fp4_post_quantization_amd import _lib
+    return _lib.load()
+
+
 def _rand_mx(rng, rows, k, lo=120, hi=134):
     codes = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
     scales = rng.integers(lo, hi + 1, (rows, k // 32)).astype(np.uint8)
@@ -376,6 +381,63 @@ def test_gemm_nvfp4_of_quantized_operands_and_nan_scale():
     mask = np.ones(96, bool)
     mask[7] = False
     assert np.all(np.isfinite(c2[mask]))
+
+
+# at most 16 tokens with K a multiple of 256: the few-token kernel (codes decoded to float16 in
+# registers, float16 matrix cores, no workspace)
+@pytest.mark.parametrize("m,n,k", [(1, 16, 256), (3, 100, 4096), (16, 4096, 4096), (7, 1000, 14336),
+                                   (16, 33, 8192), (2, 8200, 1024), (16, 14336, 4096), (9, 512, 16384)])
+def test_gemm_nvfp4_few_tokens_exact(m, n, k):
+    rng = np.random.default_rng(5300 + m + n + k)
+    ac, _ = _rand_nv(rng, m, k)
+    bc, _ = _rand_nv(rng, n, k)
+    as_ = np.full((m, k // 16), 0x38, np.uint8)  # E4M3 1.0
+    bs = np.full((n, k // 16), 0x38, np.uint8)
+    assert _fq_lib().fp4q_gemm_nvfp4_workspace_bytes(m, n, k) == 0
+    c = _run_nv(ac, as_, 1.0, bc, bs, 1.0)
+    np.testing.assert_array_equal(c, GM.gemm_nvfp4(ac, as_, np.float32(1), bc, bs, np.float32(1)))
+
+
+def _rand_nv_any_scale(rng, rows, k):
+    """Codes and scale bytes over every non-NaN E4M3 pattern: zero, subnormal, normal, both signs."""
+    codes = rng.integers(0, 256, (rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(0, 256, (rows, k // 16)).astype(np.uint8)
+    scales[(scales & 0x7F) == 0x7F] = 0xB8  # -1.0 in place of NaN
+    return codes, scales
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (5, 300, 4096, torch.bfloat16),
+                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16)])
+def test_gemm_nvfp4_few_tokens_within_bound(m, n, k, out_dtype):
+    rng = np.random.default_rng(5400 + m + n + k)
+    ac, as_ = _rand_nv_any_scale(rng, m, k)
+    bc, bs = _rand_nv_any_scale(rng, n, k)
+    ag, bg = np.float32(0.0137), np.float32(-0.71)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    big = torch.full((m, n + 8), 7.0, device=DEV, dtype=out_dtype)
+    _fq().gemm_nvfp4((a, asd, float(ag)), (b, bsd, float(bg)), out=big[:, :n])
+    torch.cuda.synchronize()
+    got = big.float().cpu().numpy().astype(np.float64)
+    _check_nv(got[:, :n], ac, as_, ag, bc, bs, bg, k, bf16=out_dtype == torch.bfloat16)
+    assert (got[:, n:] == 7.0).all()  # the padding past n is untouched
+
+
+def test_gemm_nvfp4_few_tokens_nan_scales():
+    """An E4M3 NaN scale byte (0x7F or 0xFF) in A gives a NaN row, in B a NaN column."""
+    rng = np.random.default_rng(5500)
+    m, n, k = 6, 96, 1024
+    ac, as_ = _rand_nv(rng, m, k)
+    bc, bs = _rand_nv(rng, n, k)
+    as_[2, 5] = 0x7F
+    bs[40, 63] = 0xFF
+    c = _run_nv(ac, as_, 0.5, bc, bs, 2.0)
+    assert np.all(np.isnan(c[2])) and np.all(np.isnan(c[:, 40]))
+    keep = np.ones((m, n), bool)
+    keep[2] = False
+    keep[:, 40] = False
+    assert np.all(np.isfinite(c[keep]))
+    _check_nv(c[keep].reshape(m - 1, n - 1), ac[[0, 1, 3, 4, 5]], as_[[0, 1, 3, 4, 5]], 0.5,
+              np.delete(bc, 40, 0), np.delete(bs, 40, 0), 2.0, k)
 
 
 def test_gemm_nvfp4_full_size_sampled_rows():
