@@ -22,7 +22,8 @@ from . import _lib as L
 from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
-    "quantize_nvfp4", "quantize_mxfp4", "quantize_relaxed", "gptq_nvfp4", "gptq_mxfp4", "dequantize",
+    "quantize_nvfp4", "global_scale_nvfp4", "quantize_mxfp4", "quantize_relaxed",
+    "gptq_nvfp4", "gptq_mxfp4", "dequantize",
     "block_hadamard", "gemm_mxfp4", "gemm_nvfp4",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
 ]
@@ -164,6 +165,21 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
         _ptr(out.block_loss), _ptr(out.offsets), ws.data_ptr(), ws.numel(), _stream(dev)))
     if check:
         _check_data(ws)
+    return out
+
+
+def global_scale_nvfp4(x, hadamard_n=0, *, out=None, ws=None):
+    """The NVFP4 global scale S = max|x| / 1536 (after the optional rotation)
+    as a [1] float32 device tensor, enqueued on the current stream: the first
+    step of quantize_nvfp4, which takes it back through ``global_scale``."""
+    lib = L.load()
+    x, ld = _matrix(x)
+    rows, cols = x.shape
+    dev = x.device
+    out = torch.empty(1, dtype=torch.float32, device=dev) if out is None else out
+    ws = workspace(dev) if ws is None else ws
+    L.check(lib.fp4q_global_scale_nvfp4(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(hadamard_n),
+                                        out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
     return out
 
 

@@ -24,6 +24,7 @@ EXPORTS = (
     "fp4q_status_string",
     "fp4q_workspace_bytes",
     "fp4q_quantize_nvfp4",
+    "fp4q_global_scale_nvfp4",
     "fp4q_quantize_mxfp4",
     "fp4q_quantize_relaxed",
     "fp4q_gptq_nvfp4",
@@ -46,6 +47,7 @@ _SIGNATURES = {
     "fp4q_version": (_I, []),
     "fp4q_status_string": (ctypes.c_char_p, [_I]),
     "fp4q_workspace_bytes": (_SZ, []),
+    "fp4q_global_scale_nvfp4": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "fp4q_quantize_nvfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I, _U32,
                                  _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_quantize_mxfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I,

@@ -1260,6 +1260,27 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   return last_hip_status();
 }
 
+extern "C" fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                                 int64_t ld, int hadamard_n, float *global_scale, void *workspace,
+                                                 size_t workspace_bytes, void *stream) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!global_scale || (!empty && !x)) return FP4Q_ERR_NULL;
+  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, 16, hadamard_n);
+  if (st != FP4Q_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (empty) {
+    hipLaunchKernelGGL(zero_scale_kernel, dim3(1), dim3(1), 0, s, global_scale);
+    return last_hip_status();
+  }
+  // the max pass and the reduction of its partials, as at the start of fp4q_quantize_nvfp4
+  const int n_partials = launch_amax(x, dtype, rows, cols, ld, hadamard_n, amax_out(workspace, nullptr, 0), s);
+  hipLaunchKernelGGL(scale_from_partials_kernel, dim3(1), dim3(kThreads), 0, s,
+                     (const uint32_t *)((const char *)workspace + kWsPartials), n_partials, global_scale,
+                     (uint32_t *)((char *)workspace + kWsStatus));
+  return last_hip_status();
+}
+
 extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
                                              int64_t ld, const float *importance, int block,
                                              fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,

@@ -140,6 +140,29 @@ fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t row
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * The NVFP4 global scale alone: S = fp32(max|x| / 1536) over x, after the
+ * optional rotation ([SS] 2., Escala Global: the per-tensor FP32 scale puts
+ * the largest value at the top of the E2M1 x E4M3 range, 6 * 256).  This is
+ * the first step of fp4q_quantize_nvfp4, and fp4q_quantize_nvfp4 with
+ * FP4Q_GIVEN_SCALE and this S gives bit for bit what one call computing S
+ * gives.  Splitting the two serves callers that share one S across several
+ * calls: the row shards of one tensor (on one device or several) each
+ * compute their S, take the maximum (the rounding is monotone, so that
+ * maximum is the S of the whole tensor) and pass it with FP4Q_GIVEN_SCALE.
+ *
+ *   x, dtype, rows, cols, ld, hadamard_n  as for fp4q_quantize_nvfp4
+ *               (cols a multiple of 16 and of hadamard_n).
+ *   global_scale [1] float32 S (device, out); 0 for an empty matrix.
+ *   workspace   fp4q_workspace_bytes() bytes of device memory.
+ *
+ * Errors as for fp4q_quantize_nvfp4; a non-finite x sets
+ * FP4Q_DATA_NONFINITE_INPUT in the workspace's status word (asynchronous).
+ */
+fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                      int64_t ld, int hadamard_n, float *global_scale, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * MXFP4 quantization with an exponent-window search over E8M0 block scales
  * ([MR] 1., 2.: power-of-two scales, MSE-optimised grid; [TQ] S-step for the
  * base), optionally after a block Hadamard rotation.

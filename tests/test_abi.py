@@ -207,6 +207,25 @@ def test_gemm_validation():
     assert gm(n=0, b=None, bs=None, c=None) == L.OK
 
 
+def test_global_scale_nvfp4_validation():
+    L, lib = _lib()
+
+    def gs(**kw):
+        return lib.fp4q_global_scale_nvfp4(kw.get("x", X), kw.get("dt", L.BF16), kw.get("rows", 64),
+                                           kw.get("cols", 256), kw.get("ld", 256), kw.get("had", 0),
+                                           kw.get("g", OUT), kw.get("ws", WS), kw.get("wsb", 1 << 20), None)
+    assert gs(g=None) == L.ERR_NULL
+    assert gs(x=None) == L.ERR_NULL
+    assert gs(ws=None) == L.ERR_WORKSPACE
+    assert gs(wsb=16) == L.ERR_WORKSPACE
+    assert gs(dt=7) == L.ERR_ARG
+    assert gs(had=8) == L.ERR_ARG
+    assert gs(cols=40, ld=40) == L.ERR_SHAPE
+    assert gs(had=32, cols=48, ld=48) == L.ERR_SHAPE
+    assert gs(ld=100) == L.ERR_SHAPE
+    assert gs(x=X + 4) == L.ERR_ALIGN
+
+
 def test_gemm_nvfp4_validation():
     L, lib = _lib()
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(64, 32, 48) == (64 + 32) * 64 * 2

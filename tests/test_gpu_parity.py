@@ -224,6 +224,42 @@ def test_data_errors_set_status():
     fq.quantize_nvfp4(y, check=True)
 
 
+# ------------------------------------ the global scale alone, two streams ----
+@pytest.mark.parametrize("dtype,had,ld_extra", [(torch.bfloat16, 0, 0), (torch.float32, 0, 32),
+                                                (torch.bfloat16, 16, 0), (torch.float32, 128, 64)])
+def test_global_scale_alone_matches_oracle(dtype, had, ld_extra):
+    x = W.random_matrix(67, 1024 + ld_extra, seed=80 + had, dist="laplace", dtype=dtype)
+    fq = _fp4()
+    S = fq.global_scale_nvfp4(x.to(DEV)[:, :1024], had)
+    torch.cuda.synchronize()
+    ref = np.float32(_oracle_nvfp4(x[:, :1024].contiguous(), had=had).global_scale)
+    assert _np(S).view(np.uint32)[0] == np.array([ref]).view(np.uint32)[0], (float(_np(S)[0]), float(ref))
+
+
+def test_global_scale_of_empty_tensor_is_zero():
+    fq = _fp4()
+    S = torch.full((1,), 5.0, device=DEV)
+    fq.global_scale_nvfp4(torch.zeros((0, 64), device=DEV), out=S)
+    torch.cuda.synchronize()
+    assert float(S[0]) == 0.0
+
+
+def test_given_scale_from_the_scale_pass_is_one_call():
+    """The global scale alone, then the sweep with that scale given: every
+    output field identical to one quantize_nvfp4 call computing S."""
+    fq = _fp4()
+    specs = [(64, 1024, "t4", torch.bfloat16), (300, 512, "laplace", torch.float32), (1, 2048, "normal", torch.bfloat16)]
+    for i, (r, c, d, dt) in enumerate(specs):
+        x = W.random_matrix(r, c, seed=95 + i, dist=d, dtype=dt).to(DEV)
+        for had, imp in ((0, W.random_importance(c, seed=99 + i).to(DEV)), (16, None)):
+            S = fq.global_scale_nvfp4(x, had)
+            two = fq.quantize_nvfp4(x, imp, hadamard_n=had, global_scale=S)
+            one = fq.quantize_nvfp4(x, imp, hadamard_n=had)
+            torch.cuda.synchronize()
+            for f in ("codes", "scales", "global_scale", "block_loss", "offsets"):
+                assert torch.equal(getattr(two, f), getattr(one, f)), (i, had, f)
+
+
 def test_deterministic():
     fq = _fp4()
     x = W.random_matrix(512, 2048, seed=56, dtype=torch.bfloat16).to(DEV)
