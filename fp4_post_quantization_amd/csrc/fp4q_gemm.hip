@@ -1019,6 +1019,250 @@ __global__ __launch_bounds__(256) void nvfp4_to_bf16_kernel(const uint8_t *__res
   }
 }
 
+// NVFP4 operands through the direct-to-LDS ring, decoded in registers (K a multiple of 128).  A stage
+// is 128 K elements of every row: 64 code bytes (four 16-byte chunks, swizzled as in the MXFP4 ring)
+// and 8 E4M3 scale bytes.  Lane half h of a wave owns elements 64 h .. 64 h + 63 of the stage (chunks
+// 2 h and 2 h + 1, scale bytes 4 h .. 4 h + 3); k step ks (0 .. 7) feeds v_mfma_f32_32x32x16_f16
+// with elements 64 h + 8 ks .. + 7 of every lane, in both operands alike, decoded to q * E4M3(p) in
+// float16 (exact, as in the few-token kernel).  Steps run in ascending order within a stage, stages
+// in ascending order; the accumulator is scaled by fp32(S_a S_b) at the end.  Staging FP4 codes
+// instead of decoded bfloat16 cuts the LDS bytes per MFMA by four (the bfloat16 ring is bound by
+// them), at the price of about one VALU instruction per element read.
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN) void nv_gemm_ring_kernel(
+    const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
+    const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, int64_t sbytes, const float *__restrict__ ga,
+    const float *__restrict__ gb, OutT *__restrict__ C, int64_t ldc) {
+  constexpr int WAVES = WGM * WGN;
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  constexpr int ROWB = 64, SPR = 8;  // code and scale bytes per row per stage
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + BM * SPR;
+  constexpr int STAGE = SB_OFF + BN * SPR;
+  constexpr int RPL = 1024 / ROWB;  // rows per 1 KB code load
+  constexpr int A_INSTR = BM / RPL / WAVES, B_INSTR = BN / RPL / WAVES;
+  constexpr int SA_INSTR = BM * SPR / 256, SB_INSTR = BN * SPR / 256;  // 256 B scale loads (32 rows)
+  constexpr int SQ = (SA_INSTR + SB_INSTR + WAVES - 1) / WAVES;
+  static_assert(A_INSTR * WAVES * RPL == BM && B_INSTR * WAVES * RPL == BN, "code loads must divide evenly");
+  static_assert(SA_INSTR * 256 == BM * SPR && SB_INSTR * 256 == BN * SPR, "scale loads cover whole rows");
+  constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
+  constexpr int SPARE = NS * STAGE;               // target of the filler scale loads
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + 256];
+  __shared__ uint2 parts_tab[256];  // E4M3 byte -> (2^e, two float16 copies of m)
+  const float alpha = (*ga) * (*gb);
+
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l32 = lane & 31, h = lane >> 5;
+  for (int i = tid; i < 256; i += 64 * WAVES) parts_tab[i] = nv_scale_parts((uint32_t)i);
+
+  const uint8_t *srcA[A_INSTR];
+  const uint8_t *srcB[B_INSTR];
+#pragma unroll
+  for (int i = 0; i < A_INSTR; ++i) {
+    const int row = (wave * A_INSTR + i) * RPL + lane / 4;
+    srcA[i] = A + (int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane % 4) ^ swz<ROWB>(row));
+  }
+#pragma unroll
+  for (int i = 0; i < B_INSTR; ++i) {
+    const int row = (wave * B_INSTR + i) * RPL + lane / 4;
+    srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane % 4) ^ swz<ROWB>(row));
+  }
+  // scale load q: 32 rows, lane l loading dword l % 2 of row l / 2 (rows past M or N repeat the last)
+  const uint8_t *srcS[SQ];
+  int dstS[SQ];
+#pragma unroll
+  for (int j = 0; j < SQ; ++j) {
+    const int q = wave + WAVES * j;
+    const int rl = lane / 2, dw = lane % 2;
+    if (q < SA_INSTR) {
+      srcS[j] = As + (int64_t)min(m0 + 32 * q + rl, M - 1) * sbytes + 4 * dw;
+      dstS[j] = SA_OFF + 256 * q;
+    } else if (q < SA_INSTR + SB_INSTR) {
+      const int qb = q - SA_INSTR;
+      srcS[j] = Bs + (int64_t)min(n0 + 32 * qb + rl, N - 1) * sbytes + 4 * dw;
+      dstS[j] = SB_OFF + 256 * qb;
+    } else {
+      srcS[j] = As + (int64_t)min(m0 + rl, M - 1) * sbytes + 4 * dw;
+      dstS[j] = -1;
+    }
+  }
+  auto issue = [&](int st, int slot) {
+    uint8_t *base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_INSTR; ++i) load_lds16(srcA[i] + st * ROWB, base + (wave * A_INSTR + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i)
+      load_lds16(srcB[i] + st * ROWB, base + A_BYTES + (wave * B_INSTR + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < SQ; ++j) load_lds4(srcS[j] + st * SPR, dstS[j] >= 0 ? base + dstS[j] : smem + SPARE);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{0};
+
+  auto stage_barrier = [&]() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS; ++s) issue(min(s, nst - 1), s);
+  wait_vmcnt<(NS - 1) * LOADS>();
+  stage_barrier();  // also publishes parts_tab
+
+  int slot = 0;
+  for (int st = 0; st < nst; ++st) {
+    const uint8_t *base = smem + slot * STAGE;
+    // this wave's operands of the stage: two 16-byte chunks and one scale dword per row block
+    i32x4 ca[TM][2], cb[TN][2];
+    uint32_t sa[TM], sb[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * TM * 32 + i * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        ca[i][c] = *reinterpret_cast<const i32x4 *>(base + r * ROWB + 16 * ((2 * h + c) ^ swz<ROWB>(r)));
+      sa[i] = *reinterpret_cast<const uint32_t *>(base + SA_OFF + SPR * r + 4 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * TN * 32 + j * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        cb[j][c] = *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * ROWB + 16 * ((2 * h + c) ^ swz<ROWB>(r)));
+      sb[j] = *reinterpret_cast<const uint32_t *>(base + SB_OFF + SPR * r + 4 * h);
+    }
+    // software pipeline: step ks + 1 is decoded while step ks's MFMAs run, one MFMA between every
+    // six VALU instructions; steps 2 kp and 2 kp + 1 share a block, so a block's scale parts are
+    // looked up every other step
+    uint2 pa[TM], pb[TN];
+    f16x8 av[TM], bv[TN];
+    auto lookup = [&](int kp) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) pa[i] = parts_tab[(sa[i] >> (8 * kp)) & 0xFFu];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) pb[j] = parts_tab[(sb[j] >> (8 * kp)) & 0xFFu];
+    };
+    auto decode = [&](int ks, f16x8 *a_out, f16x8 *b_out) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a_out[i] = nv_decode8((uint32_t)ca[i][ks >> 2][ks & 3], pa[i]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b_out[j] = nv_decode8((uint32_t)cb[j][ks >> 2][ks & 3], pb[j]);
+    };
+    lookup(0);
+    decode(0, av, bv);
+    unroll(std::make_integer_sequence<int, 8>{}, [&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
+      f16x8 an[TM], bn[TN];
+      if constexpr (ks + 1 < 8) {
+        if constexpr ((ks + 1) % 2 == 0) lookup((ks + 1) / 2);
+        decode(ks + 1, an, bn);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      unroll(std::make_integer_sequence<int, TM * TN>{}, [&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      });
+      if constexpr (ks + 1 < 8) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) av[i] = an[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = bn[j];
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    const int next = slot == NS - 1 ? 0 : slot + 1;
+    wait_lgkmcnt0();                 // this wave's reads of stage st are complete
+    wait_vmcnt<(NS - 2) * LOADS>();  // stage st + 1 has landed
+    stage_barrier();                 // ... for every wave, and nobody reads stage st any more
+    issue(min(st + NS, nst - 1), slot);
+    slot = next;
+  }
+
+  // epilogue through LDS, as in the MXFP4 ring
+  __syncthreads();
+  constexpr int WCOLS = TN * 32;
+  constexpr int EPAD = 16 / (int)sizeof(OutT);
+  constexpr int EROW = WCOLS + EPAD;
+  constexpr int VEC = 16 / (int)sizeof(OutT);
+  constexpr int LPR = WCOLS / VEC;
+  constexpr int RPI = 64 / LPR;
+  static_assert(WAVES * 32 * EROW * (int)sizeof(OutT) <= NS * STAGE, "epilogue staging must fit in the ring");
+  OutT *stage_out = reinterpret_cast<OutT *>(smem) + wave * 32 * EROW;
+  const int col0 = n0 + wn * WCOLS;
+  const bool vec_ok = ((uintptr_t)C % 16 == 0) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+        OutT o;
+        if constexpr (sizeof(OutT) == 4) o = alpha * acc[i][j][v];
+        else o = f32_to_bf16_rne(alpha * acc[i][j][v]);
+        stage_out[r * EROW + j * 32 + l32] = o;
+      }
+    const int row0 = m0 + wm * TM * 32 + i * 32;
+#pragma unroll
+    for (int q = 0; q < 32 / RPI; ++q) {
+      const int r = q * RPI + lane / LPR, c = (lane % LPR) * VEC;
+      const int row = row0 + r, col = col0 + c;
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(stage_out + r * EROW + c);
+      if (row < M) {
+        OutT *dst = C + (int64_t)row * ldc + col;
+        if (vec_ok && col + VEC <= N) {
+          *reinterpret_cast<i32x4 *>(dst) = v;
+        } else {
+          const OutT *e = reinterpret_cast<const OutT *>(&v);
+#pragma unroll
+          for (int t = 0; t < VEC; ++t)
+            if (col + t < N) dst[t] = e[t];
+        }
+      }
+    }
+  }
+}
+
+template <int WGM, int WGN, int TM, int TN, int NS, typename OutT>
+hipError_t launch_nv_ring(const uint8_t *a, const uint8_t *as, const float *ga, const uint8_t *b, const uint8_t *bs,
+                          const float *gb, int m, int n, int k, OutT *c, int64_t ldc, hipStream_t s) {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  hipLaunchKernelGGL((nv_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT>), dim3((unsigned)tiles), dim3(64 * WGM * WGN),
+                     0, s, a, as, b, bs, m, n, k / 128, (int64_t)(k / 2), (int64_t)(k / 16), ga, gb, c, ldc);
+  return hipGetLastError();
+}
+
+// NVFP4 operands decoded in registers (K a multiple of 128), for products too small for 256 x 256
+// tiles on every CU: 128 x 128 or 64 x 64 tiles.  (With 256 x 256 tiles the decode, four waves'
+// worth per A row and two per B row, outweighs the saved LDS traffic: the decode pass and the
+// bfloat16 ring measured faster there.)
+bool nv_ring_applies(int64_t m, int64_t n, int64_t k) {
+  return k % 128 == 0 && ((m + 255) / 256) * ((n + 255) / 256) < 256;
+}
+
+template <typename OutT>
+hipError_t dispatch_nv_ring(const uint8_t *a, const uint8_t *as, const float *ga, const uint8_t *b, const uint8_t *bs,
+                            const float *gb, int m, int n, int k, OutT *c, int64_t ldc, hipStream_t s) {
+  const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
+  if (mid >= 128) return launch_nv_ring<2, 2, 2, 2, 4, OutT>(a, as, ga, b, bs, gb, m, n, k, c, ldc, s);
+  return launch_nv_ring<2, 2, 1, 1, 4, OutT>(a, as, ga, b, bs, gb, m, n, k, c, ldc, s);
+}
+
 template <typename OutT>
 hipError_t dispatch_nv(const uint16_t *a, const uint16_t *b, int m, int n, int kp, const float *ga, const float *gb,
                        OutT *c, int64_t ldc, hipStream_t s) {
@@ -1112,6 +1356,17 @@ extern "C" fp4q_status_t fp4q_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *
   if (!aligned(a_codes, 8) || !aligned(b_codes, 8) || !aligned(a_global, 4) || !aligned(b_global, 4) ||
       !aligned(workspace, 16) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
     return FP4Q_ERR_ALIGN;
+  if (nv_ring_applies(m, n, k) && aligned(a_codes, 16) && aligned(b_codes, 16) && aligned(a_scales, 4) &&
+      aligned(b_scales, 4)) {
+    // codes staged in LDS and decoded in registers (the workspace is not touched)
+    const hipError_t e =
+        out_dtype == FP4Q_F32
+            ? dispatch_nv_ring<float>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
+                                      (int)k, (float *)c, ldc, s)
+            : dispatch_nv_ring<uint16_t>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
+                                         (int)k, (uint16_t *)c, ldc, s);
+    return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
+  }
   uint16_t *wa = (uint16_t *)workspace;
   uint16_t *wb = wa + m * kp;
   const int64_t ta = m * (kp / 16), tb = n * (kp / 16);

@@ -128,10 +128,17 @@ size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * product is exact, summed in float32 one 16-element step of K at a time in
  * ascending K order.  The result is multiplied by fp32(S_a * S_b).
  *
+ * Products with K a multiple of 128 that are too small for 256 x 256 tiles
+ * on every CU (and have 16-byte aligned codes, 4-byte aligned scales) skip
+ * that pass as well: the codes are staged in LDS and decoded in registers
+ * to float16, which holds q * E4M3(p) exactly too, and summed on
+ * v_mfma_f32_32x32x16_f16.  K moves in stages of 128 elements, ascending;
+ * step s = 0 .. 7 of a stage holds its elements 8 s .. 8 s + 7 and
+ * 64 + 8 s .. 64 + 8 s + 7, steps ascending.  The workspace is not touched.
+ *
  * Products of at most 16 tokens with K a multiple of 256 and at most 16384
- * skip that pass: a few-token kernel decodes the codes in registers (float16
- * holds q * E4M3(p) exactly as well) and sums on the float16 matrix cores
- * (v_mfma_f32_16x16x32_f16).  K is cut into W contiguous ranges of S groups
+ * skip that pass too, in a few-token kernel that decodes in registers and
+ * sums on v_mfma_f32_16x16x32_f16.  K is cut into W contiguous ranges of S groups
  * of 128 elements (S = 2, 4 or 8, W = k / (128 S) <= 16); each range is
  * accumulated in float32 one 32-element step at a time, and the W range sums
  * are added in ascending K order before the multiplication by

@@ -440,6 +440,36 @@ def test_gemm_nvfp4_few_tokens_nan_scales():
               np.delete(bc, 40, 0), np.delete(bs, 40, 0), 2.0, k)
 
 
+# K a multiple of 128 (and 16-byte aligned codes), products below 256 x 256 tiles on every CU: codes
+# staged in LDS, decoded in registers, float16 matrix cores (128 x 128 and 64 x 64 tiles); one
+# product of the large-tile size checks the decode pass that takes those
+@pytest.mark.parametrize("m,n,k", [(4096, 4096, 256), (1536, 1408, 384), (200, 300, 640), (33, 65, 128)])
+def test_gemm_nvfp4_ring_exact(m, n, k):
+    rng = np.random.default_rng(5600 + m + n + k)
+    ac, _ = _rand_nv(rng, m, k)
+    bc, _ = _rand_nv(rng, n, k)
+    as_ = np.full((m, k // 16), 0x38, np.uint8)
+    bs = np.full((n, k // 16), 0x38, np.uint8)
+    c = _run_nv(ac, as_, 1.0, bc, bs, 1.0)
+    np.testing.assert_array_equal(c, GM.gemm_nvfp4(ac, as_, np.float32(1), bc, bs, np.float32(1)))
+
+
+@pytest.mark.parametrize("m,n,k,out_dtype", [(4096, 4096, 256, torch.bfloat16), (1536, 1408, 384, torch.float32),
+                                             (200, 300, 640, torch.bfloat16)])
+def test_gemm_nvfp4_ring_within_bound(m, n, k, out_dtype):
+    rng = np.random.default_rng(5700 + m + n + k)
+    ac, as_ = _rand_nv_any_scale(rng, m, k)
+    bc, bs = _rand_nv_any_scale(rng, n, k)
+    ag, bg = np.float32(0.0213), np.float32(-1.37)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    big = torch.full((m, n + 8), 7.0, device=DEV, dtype=out_dtype)
+    _fq().gemm_nvfp4((a, asd, float(ag)), (b, bsd, float(bg)), out=big[:, :n])
+    torch.cuda.synchronize()
+    got = big.float().cpu().numpy().astype(np.float64)
+    _check_nv(got[:, :n], ac, as_, ag, bc, bs, bg, k, bf16=out_dtype == torch.bfloat16)
+    assert (got[:, n:] == 7.0).all()  # the padding past n is untouched
+
+
 def test_gemm_nvfp4_full_size_sampled_rows():
     """8192 x 14336 x 4096 with bf16 output in the launch configuration of
     the large-tile path; 40 sampled rows against the oracle."""
