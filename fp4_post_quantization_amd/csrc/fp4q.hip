@@ -349,6 +349,21 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
     Vtab[tid] = kE4M3.v[tid];
     Rtab[tid] = kE4M3.r[tid];
   }
+  const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
+  const int band = tile % a.nbands, rg = tile / a.nbands;
+  const int c = band * 64 + lane;
+  const bool active = tile < a.ntiles && c < a.cpr;  // whole Hadamard groups are active or not together
+  const int r0 = rg * a.rows_per_tile;
+  const int r1 = min(a.rows, r0 + a.rows_per_tile);
+  const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
+  // the importance and the first row are loaded before S is known: their latency overlaps the
+  // reduction below
+  float w[16];
+  Raw<T> cur, nxt;
+  if (active) {
+    if constexpr (WMSE) load_importance(a.imp + (int64_t)c * 16, w);
+    load_raw(xc + (int64_t)r0 * a.ld, cur);
+  }
   // wave 0 finds S and S_inv (the maximum of the global-max partials, or the given scale) for the
   // workgroup
   __shared__ float sc[2];
@@ -376,29 +391,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   __syncthreads();
   const float S = sc[0], S_inv = sc[1];
   const float SS = S * S;
-
-  const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
-  if (tile >= a.ntiles) return;
-  const int band = tile % a.nbands, rg = tile / a.nbands;
-  const int c = band * 64 + lane;
-  const bool active = c < a.cpr;
-  const int r0 = rg * a.rows_per_tile;
-  const int r1 = min(a.rows, r0 + a.rows_per_tile);
-
-  float w[16];
+  if (!active) return;
   if constexpr (WMSE) {
-    if (active) {
-      load_importance(a.imp + (int64_t)c * 16, w);
-      if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
-    }
+    if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
   }
-  if (!active) return;  // whole Hadamard groups are active or not together
 
-  const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
   const int bpr = a.cpr;  // blocks per row
   const int lo = a.off_lo, hi = a.off_hi;
-  Raw<T> cur, nxt;
-  load_raw(xc + (int64_t)r0 * a.ld, cur);
   for (int r = r0; r < r1; ++r) {
     if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
     float z[16];
