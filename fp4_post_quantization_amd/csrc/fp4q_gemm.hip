@@ -563,31 +563,35 @@ hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, co
 // lane l takes byte l / 16 of the step's word by a shift.  Every load is issued before the first
 // MFMA (the whole product's bytes are in flight at once); the NT column tiles of a workgroup share
 // one read of A.  The waves' sums meet in LDS and are added in ascending K order.
-template <int S, int NT, typename OutT>
+template <int S, int NT, int RT, typename OutT>
 __global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__restrict__ A,
                                                               const uint8_t *__restrict__ As,
                                                               const uint8_t *__restrict__ B,
                                                               const uint8_t *__restrict__ Bs, int M, int N, int K,
                                                               float alpha, OutT *__restrict__ C, int64_t ldc) {
-  static_assert(S % 4 == 0 && S <= 8 && NT >= 1 && NT <= 2, "steps per wave, tiles per workgroup");
-  __shared__ float part[NT][16][64][4];  // [tile][wave][lane][register]
+  static_assert(S % 4 == 0 && S <= 8 && NT >= 1 && NT <= 2 && RT >= 1 && RT * S <= 16 && (NT == 1 || RT == 1),
+                "steps per wave, column tiles, row tiles");
+  __shared__ float part[RT * NT][16][64][4];  // [row tile, column tile][wave][lane][register]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
   const int n0 = blockIdx.x * 16 * NT;
   const int r16 = lane & 15, h = lane >> 4;
   const int kw0 = wave * S * 128;  // this wave's first K element
   const int64_t kb = K / 2, sb = K / 32;
-  const int arow = min(r16, M - 1);  // rows past M repeat row M - 1: computed, never stored
-  const uint8_t *ap = A + (int64_t)arow * kb + kw0 / 2 + 16 * h;
+  // rows past M repeat row M - 1: computed, never stored
+  int arow[RT], brow[NT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) arow[r] = min(16 * r + r16, M - 1);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) brow[t] = min(n0 + 16 * t + r16, N - 1);
   // every load is issued before the first MFMA, in the order of use: the scale words (16 bytes per
   // four steps), then step by step the codes of A and B, so that the first steps can start while
   // the later loads are in flight
-  i32x4 bc[NT][S], ac[S], bsw[NT][S / 4], asw[S / 4];
-  int brow[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) brow[t] = min(n0 + 16 * t + r16, N - 1);
+  i32x4 bc[NT][S], ac[RT][S], bsw[NT][S / 4], asw[RT][S / 4];
 #pragma unroll
   for (int q = 0; q < S / 4; ++q) {  // scale bytes of steps 4q .. 4q+3 (blocks 4 step + h)
-    asw[q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 32 + 16 * q);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      asw[r][q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow[r] * sb + kw0 / 32 + 16 * q);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       bsw[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow[t] * sb + kw0 / 32 + 16 * q);
@@ -595,37 +599,46 @@ __global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__r
   __builtin_amdgcn_sched_barrier(0);
   unroll(std::make_integer_sequence<int, S>{}, [&](auto st_c) {
     constexpr int st = decltype(st_c)::value;
-    ac[st] = *reinterpret_cast<const i32x4 *>(ap + 64 * st);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      ac[r][st] = *reinterpret_cast<const i32x4 *>(A + (int64_t)arow[r] * kb + kw0 / 2 + 16 * h + 64 * st);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       bc[t][st] = *reinterpret_cast<const i32x4 *>(B + (int64_t)brow[t] * kb + kw0 / 2 + 16 * h + 64 * st);
     __builtin_amdgcn_sched_barrier(0);
   });
   typedef float f32x4v __attribute__((ext_vector_type(4)));
-  f32x4v acc[NT];
+  f32x4v acc[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   unroll(std::make_integer_sequence<int, S>{}, [&](auto st_c) {
     constexpr int st = decltype(st_c)::value;
-    const i32x8 a = {ac[st][0], ac[st][1], ac[st][2], ac[st][3], 0, 0, 0, 0};
-    const int sa = (int)((uint32_t)asw[st / 4][st % 4] >> (8 * h));  // byte 0: block 4 st + h
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const i32x8 b = {bc[t][st][0], bc[t][st][1], bc[t][st][2], bc[t][st][3], 0, 0, 0, 0};
-      const int sbv = (int)((uint32_t)bsw[t][st / 4][st % 4] >> (8 * h));
-      acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[t], 4, 4, 0, sa, 0, sbv);
+    for (int r = 0; r < RT; ++r) {
+      const i32x8 a = {ac[r][st][0], ac[r][st][1], ac[r][st][2], ac[r][st][3], 0, 0, 0, 0};
+      const int sa = (int)((uint32_t)asw[r][st / 4][st % 4] >> (8 * h));  // byte 0: block 4 st + h
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const i32x8 b = {bc[t][st][0], bc[t][st][1], bc[t][st][2], bc[t][st][3], 0, 0, 0, 0};
+        const int sbv = (int)((uint32_t)bsw[t][st / 4][st % 4] >> (8 * h));
+        acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[r][t], 4, 4, 0, sa, 0, sbv);
+      }
     }
   });
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[t][wave][lane][v] = acc[t][v];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[r * NT + t][wave][lane][v] = acc[r][t][v];
   __syncthreads();
-  for (int i = threadIdx.x; i < 256 * NT; i += blockDim.x) {
-    const int t = i >> 8, m = (i >> 4) & 15, j = i & 15;
-    const int l = 16 * (m >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
-    float sum = part[t][0][l][v];
-    for (int w = 1; w < waves; ++w) sum = sum + part[t][w][l][v];
+  for (int i = threadIdx.x; i < 256 * RT * NT; i += blockDim.x) {
+    const int rt = i >> 8, t = rt % NT, m = 16 * (rt / NT) + ((i >> 4) & 15), j = i & 15;
+    const int l = 16 * ((m & 15) >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
+    float sum = part[rt][0][l][v];
+    for (int w = 1; w < waves; ++w) sum = sum + part[rt][w][l][v];
     const int col = n0 + 16 * t + j;
     if (m < M && col < N) store_out(C + (int64_t)m * ldc + col, alpha * sum);
   }
@@ -636,13 +649,14 @@ __global__ __launch_bounds__(1024) void mx_gemm_skinny_kernel(const uint8_t *__r
 // workgroups; past 16384 columns one tile measured faster up to eight tokens.
 int skinny_tiles(int64_t m, int64_t n) { return (m > 1 && n >= 8192 && (n <= 16384 || m > 8)) ? 2 : 1; }
 
-// Steps per wave of the few-token kernel for this shape, or 0 when it does not apply (M > 16, K not a
-// multiple of 512, or no S in {4, 8} with W = K / (128 S) <= 16 waves).
+// Steps per wave of the few-token kernel for this shape, or 0 when it does not apply: M above 64, K
+// not a multiple of 512, or no S in {4, 8} with W = K / (128 S) <= 16 waves.  Beyond one 16-row tile
+// (M > 16) only S = 4 (K <= 8192): two row tiles of eight steps measured slower than the split.
 int skinny_steps(int64_t m, int64_t k) {
-  if (m > 16 || m <= 0 || k % 512) return 0;
+  if (m > 64 || m <= 0 || k % 512) return 0;
   const int64_t nst = k / 128;
   for (int S : {4, 8})
-    if (nst % S == 0 && nst / S <= 16) return S;
+    if (nst % S == 0 && nst / S <= 16) return (m <= 16 || S == 4) ? S : 0;
   return 0;
 }
 
@@ -901,19 +915,23 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
   const int64_t big = (int64_t)((m + 255) / 256) * ((n + 255) / 256);
   const int64_t mid = (int64_t)((m + 127) / 128) * ((n + 127) / 128);
   // at most 16 tokens: the few-token kernel (whole K in flight, no workspace)
+  // up to 16 tokens, or up to 64 when the output has at most 4096 columns (one workgroup per CU or
+  // fewer; wider outputs ran faster on the tiled paths): the few-token kernel (whole K in flight, no
+  // workspace)
   const int S = skinny_steps(m, k);
-  if (S && aligned(as, 16) && aligned(bs, 16)) {
+  if (S && (m <= 16 || n <= 4096) && aligned(as, 16) && aligned(bs, 16)) {
     const int waves = k / (128 * S);
-    const int nt = skinny_tiles(m, n);
+    const int rt = (m + 15) / 16, nt = rt == 1 ? skinny_tiles(m, n) : 1;
     const dim3 grid((unsigned)((n + 16 * nt - 1) / (16 * nt))), block(64 * waves);
-    if (S == 4 && nt == 1)
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<4, 1, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
-    else if (S == 4)
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<4, 2, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
-    else if (nt == 1)
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<8, 1, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
-    else
-      hipLaunchKernelGGL((mx_gemm_skinny_kernel<8, 2, OutT>), grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a, as, b, bs, m, n, k, alpha, c, ldc); };
+    if (S == 4) {
+      if (rt == 1) nt == 1 ? go(mx_gemm_skinny_kernel<4, 1, 1, OutT>) : go(mx_gemm_skinny_kernel<4, 2, 1, OutT>);
+      else if (rt == 2) go(mx_gemm_skinny_kernel<4, 1, 2, OutT>);
+      else if (rt == 3) go(mx_gemm_skinny_kernel<4, 1, 3, OutT>);
+      else go(mx_gemm_skinny_kernel<4, 1, 4, OutT>);
+    } else {
+      nt == 1 ? go(mx_gemm_skinny_kernel<8, 1, 1, OutT>) : go(mx_gemm_skinny_kernel<8, 2, 1, OutT>);
+    }
     return hipGetLastError();
   }
   const int splits = gemm_mxfp4_splits(m, n, k);

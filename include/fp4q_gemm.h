@@ -66,8 +66,9 @@ extern "C" {
  * split, each range is summed that way and
  * the S partial sums are then added in ascending K order, which can round
  * differently from a single accumulation.  Products of at most 16 tokens
- * with K a multiple of 512 and at most 16384, and both scale arrays 16-byte
- * aligned, go to a few-token kernel (no workspace) that sums on
+ * with K a multiple of 512 and at most 16384 (and of at most 64 tokens with
+ * n <= 4096 and K at most 8192), with both scale arrays 16-byte aligned, go
+ * to a few-token kernel (no workspace) that sums on
  * v_mfma_scale_f32_16x16x128_f8f6f4: K is cut into W contiguous ranges of S
  * steps of 128 contiguous elements (S = 4 or 8, W = k / (128 S) <= 16),
  * each range is accumulated step by step in float32, and the W range sums

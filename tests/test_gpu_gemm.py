@@ -176,10 +176,12 @@ def test_gemm_scale_reorganisation_is_transparent(m, n, k):
     _check(c1[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), ac, as_, bc, bs, k, rows=rows)
 
 
-# at most 16 tokens: the few-token kernel (16 or 32 columns per workgroup, K split over its waves)
+# up to 64 tokens: the few-token kernel (16 or 32 columns per workgroup, K split over its waves, up to
+# four 16-row tiles)
 @pytest.mark.parametrize("m,n,k", [(1, 16, 512), (3, 100, 4096), (16, 4096, 4096), (7, 1000, 14336),
                                    (16, 33, 8192), (1, 4096, 1536), (5, 8200, 1024), (16, 14336, 4096),
-                                   (2, 8192, 14336)])
+                                   (2, 8192, 14336), (17, 1000, 4096), (33, 300, 4096), (64, 4096, 4096),
+                                   (48, 2000, 8192), (40, 4000, 512)])
 def test_gemm_few_tokens_exact(m, n, k):
     rng = np.random.default_rng(3400 + m + n + k)
     ac, _ = _rand_mx(rng, m, k)
@@ -190,7 +192,8 @@ def test_gemm_few_tokens_exact(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (5, 300, 4096, torch.bfloat16),
-                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16)])
+                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16),
+                                             (20, 4096, 14336, torch.float32), (33, 1024, 8192, torch.bfloat16)])
 def test_gemm_few_tokens_within_bound(m, n, k, out_dtype):
     fq = _fq()
     rng = np.random.default_rng(3500 + m + n + k)
@@ -211,9 +214,9 @@ def test_gemm_few_tokens_within_bound(m, n, k, out_dtype):
     assert (got[:, n:] == 7.0).all()  # the padding past n is untouched
 
 
-# few-token products beyond the few-token kernel (more than 16 tokens, or K not a multiple of 512): K
-# split over workgroups (the workspace holds the partial sums)
-@pytest.mark.parametrize("m,n,k", [(17, 1000, 4096), (32, 4096, 4096), (40, 700, 14336), (5, 1000, 4352)])
+# few-token products the few-token kernel does not take (K not a multiple of 512, or more row-tile
+# steps than it holds): K split over workgroups (the workspace holds the partial sums)
+@pytest.mark.parametrize("m,n,k", [(40, 700, 14336), (5, 1000, 4352), (64, 2048, 14336), (50, 4096, 12800)])
 def test_gemm_few_tokens_split_k_exact(m, n, k):
     rng = np.random.default_rng(3100 + m + n + k)
     ac, _ = _rand_mx(rng, m, k)
@@ -223,9 +226,8 @@ def test_gemm_few_tokens_split_k_exact(m, n, k):
     np.testing.assert_array_equal(_run(ac, as_, bc, bs), GM.gemm_mxfp4(ac, as_, bc, bs))
 
 
-@pytest.mark.parametrize("m,n,k,out_dtype", [(20, 4096, 14336, torch.float32), (24, 2000, 4096, torch.bfloat16),
-                                             (33, 1024, 8192, torch.float32), (64, 512, 14336, torch.float32),
-                                             (1, 4096, 14592, torch.float32)])
+@pytest.mark.parametrize("m,n,k,out_dtype", [(40, 2000, 14336, torch.bfloat16), (17, 1024, 5376, torch.float32),
+                                             (64, 512, 14336, torch.float32), (1, 4096, 14592, torch.float32)])
 def test_gemm_few_tokens_split_k_within_bound(m, n, k, out_dtype):
     fq = _fq()
     rng = np.random.default_rng(3200 + m + n + k)
