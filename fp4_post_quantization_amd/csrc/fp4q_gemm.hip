@@ -717,39 +717,46 @@ __device__ __forceinline__ uint32_t nv_scale_byte(const i32x4 *v, int h) {
 // register v of lane l holds row 4 (l / 16) + v, column l % 16; the waves' sums meet in LDS, are
 // added in ascending K order and scaled by fp32(S_a S_b).  The small variants are held to 64 VGPRs,
 // so that two 16-wave workgroups fit on a CU.
-template <int S, int NT, typename OutT>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(S * NT <= 4 ? 8 : 4))) void
+template <int S, int NT, int RT, bool SEG, typename OutT>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(S * NT * RT <= 4 ? 8 : 4))) void
 nv_gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
                       const uint8_t *__restrict__ Bs, int M, int N, int K, const float *__restrict__ ga,
-                      const float *__restrict__ gb, OutT *__restrict__ C, int64_t ldc) {
-  static_assert(S % 2 == 0 && S <= 8 && NT >= 1 && NT <= 2, "groups per wave, tiles per workgroup");
-  __shared__ float part[NT][16][64][4];  // [tile][wave][lane][register]
+                      const float *__restrict__ gb, OutT *__restrict__ C, int64_t ldc, float *__restrict__ P) {
+  static_assert(S % 2 == 0 && S <= 8 && NT >= 1 && NT <= 2 && RT >= 1 && RT * S <= 8 && (NT == 1 || RT == 1),
+                "groups per wave, column tiles, row tiles");
+  __shared__ float part[RT * NT][16][64][4];  // [row tile, column tile][wave][lane][register]
   __shared__ uint2 scale_parts[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
   const int n0 = blockIdx.x * 16 * NT;
   const int r16 = lane & 15, h = lane >> 4;
-  const int kw0 = wave * S * 128;  // this wave's first K element
+  // SEG: K in gridDim.y contiguous segments; workgroup y takes the y-th and writes its unscaled sums
+  // to P[y] (M x N), added in K order by the split sum kernel
+  const int kw0 = (SEG ? blockIdx.y * waves * S * 128 : 0) + wave * S * 128;  // this wave's first K element
   const int64_t kb = K / 2, sb = K / 16;
-  const int arow = min(r16, M - 1);
-  // every load first, in the order of use: scale bytes (16 bytes per two groups), then group by group
-  // the codes of A and B (one 16-byte load each), so the first groups' decode overlaps the rest
-  i32x4 bc[NT][S], ac[S], bsv[NT][S / 2], asv[S / 2];
-  int brow[NT];
+  // rows past M repeat row M - 1 (and columns past N column N - 1): computed, never stored
+  int arow[RT], brow[NT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) arow[r] = min(16 * r + r16, M - 1);
 #pragma unroll
   for (int t = 0; t < NT; ++t) brow[t] = min(n0 + 16 * t + r16, N - 1);
-  // rows past M repeat row M - 1 (and columns past N column N - 1): computed, never stored
+  // every load first, in the order of use: scale bytes (16 bytes per two groups), then group by group
+  // the codes of A and B (one 16-byte load each), so the first groups' decode overlaps the rest
+  i32x4 bc[NT][S], ac[RT][S], bsv[NT][S / 2], asv[RT][S / 2];
 #pragma unroll
   for (int q = 0; q < S / 2; ++q) {
-    asv[q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow * sb + kw0 / 16 + 16 * q);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      asv[r][q] = *reinterpret_cast<const i32x4 *>(As + (int64_t)arow[r] * sb + kw0 / 16 + 16 * q);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       bsv[t][q] = *reinterpret_cast<const i32x4 *>(Bs + (int64_t)brow[t] * sb + kw0 / 16 + 16 * q);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const uint8_t *ap = A + (int64_t)arow * kb + kw0 / 2 + 16 * h;
   unroll(std::make_integer_sequence<int, S>{}, [&](auto g_c) {
     constexpr int g = decltype(g_c)::value;
-    ac[g] = *reinterpret_cast<const i32x4 *>(ap + 64 * g);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+      ac[r][g] = *reinterpret_cast<const i32x4 *>(A + (int64_t)arow[r] * kb + kw0 / 2 + 16 * h + 64 * g);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       bc[t][g] = *reinterpret_cast<const i32x4 *>(B + (int64_t)brow[t] * kb + kw0 / 2 + 16 * h + 64 * g);
@@ -757,13 +764,19 @@ nv_gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
   });
   for (int i = threadIdx.x; i < 256; i += blockDim.x) scale_parts[i] = nv_scale_parts((uint32_t)i);
   __syncthreads();
-  f32x4 acc[NT];
+  f32x4 acc[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   unroll(std::make_integer_sequence<int, S>{}, [&](auto g_c) {
     constexpr int g = decltype(g_c)::value;
-    const uint2 sa0 = scale_parts[nv_scale_byte<g, 0>(asv, h)], sa1 = scale_parts[nv_scale_byte<g, 1>(asv, h)];
-    uint2 sbp[NT][2];
+    uint2 sap[RT][2], sbp[NT][2];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      sap[r][0] = scale_parts[nv_scale_byte<g, 0>(asv[r], h)];
+      sap[r][1] = scale_parts[nv_scale_byte<g, 1>(asv[r], h)];
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       sbp[t][0] = scale_parts[nv_scale_byte<g, 0>(bsv[t], h)];
@@ -771,54 +784,53 @@ nv_gemm_skinny_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const f16x8 a = nv_decode8((uint32_t)ac[g][st], st < 2 ? sa0 : sa1);
+      f16x8 b[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const f16x8 b = nv_decode8((uint32_t)bc[t][g][st], st < 2 ? sbp[t][0] : sbp[t][1]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[t], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) b[t] = nv_decode8((uint32_t)bc[t][g][st], st < 2 ? sbp[t][0] : sbp[t][1]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const f16x8 a = nv_decode8((uint32_t)ac[r][g][st], st < 2 ? sap[r][0] : sap[r][1]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[t], acc[r][t], 0, 0, 0);
       }
     }
   });
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) part[t][wave][lane][v] = acc[t][v];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[r * NT + t][wave][lane][v] = acc[r][t][v];
   __syncthreads();
-  const float alpha = (*ga) * (*gb);
-  for (int i = threadIdx.x; i < 256 * NT; i += blockDim.x) {
-    const int t = i >> 8, m = (i >> 4) & 15, j = i & 15;
-    const int l = 16 * (m >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
-    float sum = part[t][0][l][v];
-    for (int w = 1; w < waves; ++w) sum = sum + part[t][w][l][v];
+  const float alpha = SEG ? 1.0f : (*ga) * (*gb);
+  for (int i = threadIdx.x; i < 256 * RT * NT; i += blockDim.x) {
+    const int rt = i >> 8, t = rt % NT, m = 16 * (rt / NT) + ((i >> 4) & 15), j = i & 15;
+    const int l = 16 * ((m & 15) >> 2) + j, v = m & 3;  // the lane and register holding (m, j)
+    float sum = part[rt][0][l][v];
+    for (int w = 1; w < waves; ++w) sum = sum + part[rt][w][l][v];
     const int col = n0 + 16 * t + j;
-    if (m < M && col < N) store_out(C + (int64_t)m * ldc + col, alpha * sum);
+    if (m < M && col < N) {
+      if constexpr (SEG) P[((int64_t)blockIdx.y * M + m) * N + col] = sum;
+      else store_out(C + (int64_t)m * ldc + col, alpha * sum);
+    }
   }
 }
 
-// Groups per wave of the few-token NVFP4 kernel, or 0 when it does not apply (M > 16, K not a
-// multiple of 256, or no S in {2, 4, 8} with W = K / (128 S) <= 16 waves).
-int nv_skinny_groups(int64_t m, int64_t k) {
-  if (m > 16 || m <= 0 || k % 256) return 0;
-  const int64_t ng = k / 128;
-  for (int S : {2, 4, 8})
-    if (ng % S == 0 && ng / S <= 16) return S;
-  return 0;
-}
-
-template <typename OutT>
-hipError_t launch_nv_skinny(const uint8_t *a, const uint8_t *as, const float *ga, const uint8_t *b,
-                            const uint8_t *bs, const float *gb, int m, int n, int k, int S, OutT *c, int64_t ldc,
-                            hipStream_t s) {
-  const int nt = skinny_tiles(m, n) == 2 && S <= 4 ? 2 : 1;
-  const dim3 grid((unsigned)((n + 16 * nt - 1) / (16 * nt))), block(64 * (k / (128 * S)));
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a, as, b, bs, m, n, k, ga, gb, c, ldc); };
-  if (S == 2)
-    nt == 1 ? go(nv_gemm_skinny_kernel<2, 1, OutT>) : go(nv_gemm_skinny_kernel<2, 2, OutT>);
-  else if (S == 4)
-    nt == 1 ? go(nv_gemm_skinny_kernel<4, 1, OutT>) : go(nv_gemm_skinny_kernel<4, 2, OutT>);
-  else
-    go(nv_gemm_skinny_kernel<8, 1, OutT>);
-  return hipGetLastError();
+// Plan of the few-token NVFP4 kernel: S groups of 128 elements per wave and KS segments of K (one
+// workgroup each, partial sums in the workspace), or S = 0 when it does not apply: M above 32 (64
+// for outputs of at most 4096 columns; wider ones ran faster tiled from three row tiles on), K not a
+// multiple of 256, or no S in {2, 4, 8} with RT S <= 8 (RT = ceil(M / 16) row tiles) and at most 16
+// waves of S groups per segment, KS in {1, 2, 4}.
+struct NvSkinnyPlan {
+  int S, KS;
+};
+NvSkinnyPlan nv_skinny_plan(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || m > 64 || (m > 32 && n > 4096) || k % 256) return {0, 1};
+  const int64_t ng = k / 128, rt = (m + 15) / 16;
+  for (int KS : {1, 2, 4})
+    for (int S : {2, 4, 8})
+      if (rt * S <= 8 && ng % ((int64_t)S * KS) == 0 && ng / ((int64_t)S * KS) <= 16) return {S, KS};
+  return {0, 1};
 }
 
 // C = alpha * (P_0 + P_1 + ... + P_{splits-1}), the split partial sums added in ascending K order
@@ -827,9 +839,12 @@ hipError_t launch_nv_skinny(const uint8_t *a, const uint8_t *as, const float *ga
 constexpr int kMaxSplits = 16;
 template <typename OutT>
 __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ P, int splits, int m, int n,
-                                                         float alpha, OutT *__restrict__ C, int64_t ldc) {
+                                                         float alpha, const float *__restrict__ ga,
+                                                         const float *__restrict__ gb, OutT *__restrict__ C,
+                                                         int64_t ldc) {
   const int col = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y;
   if (col >= n) return;
+  if (ga) alpha = (*ga) * (*gb);  // NVFP4: fp32(S_a S_b)
   const int64_t plane = (int64_t)m * n, t = (int64_t)r * n + col;
   float v[kMaxSplits];
 #pragma unroll
@@ -839,6 +854,41 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
   for (int j = 1; j < kMaxSplits; ++j)
     if (j < splits) acc = acc + v[j];
   store_out(C + (int64_t)r * ldc + col, alpha * acc);
+}
+
+template <typename OutT>
+hipError_t launch_nv_skinny(const uint8_t *a, const uint8_t *as, const float *ga, const uint8_t *b,
+                            const uint8_t *bs, const float *gb, int m, int n, int k, NvSkinnyPlan plan, OutT *c,
+                            int64_t ldc, float *parts, hipStream_t s) {
+  const int S = plan.S, KS = plan.KS;
+  const int rt = (m + 15) / 16;
+  const int nt = rt == 1 && KS == 1 && skinny_tiles(m, n) == 2 && S <= 4 ? 2 : 1;
+  const dim3 grid((unsigned)((n + 16 * nt - 1) / (16 * nt)), (unsigned)KS), block(64 * (k / (128 * S * KS)));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, a, as, b, bs, m, n, k, ga, gb, c, ldc, parts);
+  };
+  auto pick = [&](auto seg_c) {
+    constexpr bool SEG = decltype(seg_c)::value;
+    if (S == 2) {
+      if (rt == 1)
+        nt == 1 ? go(nv_gemm_skinny_kernel<2, 1, 1, SEG, OutT>) : go(nv_gemm_skinny_kernel<2, 2, 1, SEG, OutT>);
+      else if (rt == 2) go(nv_gemm_skinny_kernel<2, 1, 2, SEG, OutT>);
+      else if (rt == 3) go(nv_gemm_skinny_kernel<2, 1, 3, SEG, OutT>);
+      else go(nv_gemm_skinny_kernel<2, 1, 4, SEG, OutT>);
+    } else if (S == 4) {
+      if (rt == 1)
+        nt == 1 ? go(nv_gemm_skinny_kernel<4, 1, 1, SEG, OutT>) : go(nv_gemm_skinny_kernel<4, 2, 1, SEG, OutT>);
+      else go(nv_gemm_skinny_kernel<4, 1, 2, SEG, OutT>);
+    } else {
+      go(nv_gemm_skinny_kernel<8, 1, 1, SEG, OutT>);
+    }
+  };
+  if (KS > 1) pick(std::true_type{});
+  else pick(std::false_type{});
+  if (KS > 1)
+    hipLaunchKernelGGL((splitk_sum_kernel<OutT>), dim3((unsigned)((n + 255) / 256), (unsigned)m), dim3(256), 0, s,
+                       (const float *)parts, KS, m, n, 1.0f, ga, gb, c, ldc);
+  return hipGetLastError();
 }
 
 // bf16 operands (rows of kp elements, kp a multiple of ROWB / 2) scaled by fp32(*ga * *gb)
@@ -941,7 +991,7 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
     hipError_t e = launch_ring<2, 2, 1, 1, 4, float, 128>(a, as, b, bs, m, n, k, 1.0f, parts, n, s, false, splits);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((splitk_sum_kernel<OutT>), dim3((unsigned)((n + 255) / 256), (unsigned)m), dim3(256), 0, s,
-                       parts, splits, m, n, alpha, c, ldc);
+                       parts, splits, m, n, alpha, (const float *)nullptr, (const float *)nullptr, c, ldc);
     return hipGetLastError();
   }
   const int64_t reo_blocks = ((m + kReoRows - 1) / kReoRows + (n + kReoRows - 1) / kReoRows) *
@@ -1338,7 +1388,9 @@ extern "C" fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *
 
 extern "C" size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m < 0 || n < 0 || k <= 0) return 0;
-  if (fp4q_gemm::nv_skinny_groups(m, k)) return 0;  // the few-token kernel decodes in registers
+  // the few-token kernel decodes in registers; it needs room only for its K segments' partial sums
+  const fp4q_gemm::NvSkinnyPlan plan = fp4q_gemm::nv_skinny_plan(m, n, k);
+  if (plan.S) return plan.KS > 1 ? (size_t)(plan.KS * m * n * 4) : 0;
   return (size_t)((m + n) * fp4q_gemm::padded_k(k) * 2);
 }
 
@@ -1356,18 +1408,23 @@ extern "C" fp4q_status_t fp4q_gemm_nvfp4(const uint8_t *a_codes, const uint8_t *
   if (((m + 127) / 128) * ((n + 127) / 128) >= ((int64_t)1 << 31) || (m + n) * (kp / 16) >= ((int64_t)1 << 40))
     return FP4Q_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
-  // at most 16 tokens: the few-token kernel decodes both operands in registers (no workspace)
-  const int S = nv_skinny_groups(m, k);
-  if (S) {
+  // few tokens: the few-token kernel decodes both operands in registers (a workspace only for the
+  // partial sums of its K segments)
+  const NvSkinnyPlan plan = nv_skinny_plan(m, n, k);
+  if (plan.S) {
+    if (plan.KS > 1 && (!workspace || workspace_bytes < fp4q_gemm_nvfp4_workspace_bytes(m, n, k)))
+      return FP4Q_ERR_WORKSPACE;
     if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 16) || !aligned(b_scales, 16) ||
-        !aligned(a_global, 4) || !aligned(b_global, 4) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2))
+        !aligned(a_global, 4) || !aligned(b_global, 4) || !aligned(c, out_dtype == FP4Q_F32 ? 4 : 2) ||
+        (plan.KS > 1 && !aligned(workspace, 16)))
       return FP4Q_ERR_ALIGN;
+    float *parts = plan.KS > 1 ? (float *)workspace : nullptr;
     const hipError_t e =
         out_dtype == FP4Q_F32
             ? launch_nv_skinny<float>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
-                                      (int)k, S, (float *)c, ldc, s)
+                                      (int)k, plan, (float *)c, ldc, parts, s)
             : launch_nv_skinny<uint16_t>(a_codes, a_scales, a_global, b_codes, b_scales, b_global, (int)m, (int)n,
-                                         (int)k, S, (uint16_t *)c, ldc, s);
+                                         (int)k, plan, (uint16_t *)c, ldc, parts, s);
     return e == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
   }
   if (!workspace || workspace_bytes < fp4q_gemm_nvfp4_workspace_bytes(m, n, k)) return FP4Q_ERR_WORKSPACE;

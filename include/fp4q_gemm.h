@@ -97,9 +97,9 @@ fp4q_status_t fp4q_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, c
 size_t fp4q_gemm_mxfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* Workspace the NVFP4 product needs: (m + n) * roundup(k, 32) * 2 bytes (the
- * operands decoded to bfloat16); 0 for the few-token products (m <= 16, k a
- * multiple of 256 up to 16384), which decode in registers, and for invalid
- * sizes. */
+ * operands decoded to bfloat16); for the few-token products (above), which
+ * decode in registers, 0 or KS * m * n * 4 bytes (their K segments' partial
+ * sums); 0 for invalid sizes. */
 size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* C = fp32(S_a * S_b) * (A_hat * B_hat^T) for NVFP4 operands, where A_hat and
@@ -117,8 +117,8 @@ size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   out_dtype, c, ldc  as for fp4q_gemm_mxfp4.
  *   workspace device memory of at least fp4q_gemm_nvfp4_workspace_bytes(m,
  *             n, k) bytes, 16-byte aligned; its contents are overwritten.
- *             None is needed (NULL is accepted) where that size is 0: the
- *             few-token products below.
+ *             None is needed (NULL is accepted) where that size is 0 (most
+ *             few-token products below).
  *
  * The scaled FP4 matrix core takes only power-of-two (E8M0) scales per 32
  * elements.  Folding an E4M3 block scale into the elements would need
@@ -137,13 +137,16 @@ size_t fp4q_gemm_nvfp4_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * step s = 0 .. 7 of a stage holds its elements 8 s .. 8 s + 7 and
  * 64 + 8 s .. 64 + 8 s + 7, steps ascending.  The workspace is not touched.
  *
- * Products of at most 16 tokens with K a multiple of 256 and at most 16384
- * skip that pass too, in a few-token kernel that decodes in registers and
- * sums on v_mfma_f32_16x16x32_f16.  K is cut into W contiguous ranges of S groups
- * of 128 elements (S = 2, 4 or 8, W = k / (128 S) <= 16); each range is
- * accumulated in float32 one 32-element step at a time, and the W range sums
- * are added in ascending K order before the multiplication by
- * fp32(S_a * S_b).
+ * Products of at most 32 tokens (64 on outputs of at most 4096 columns)
+ * with K a multiple of 256 skip that pass too, in a few-token kernel that
+ * decodes in registers and sums on v_mfma_f32_16x16x32_f16, when K fits its
+ * register budget: k / 128 groups over at most 16 waves of S groups each
+ * (S = 2, 4 or 8, S ceil(m / 16) <= 8), and over KS = 1, 2 or 4 workgroups
+ * per column tile (each writing its segment's float32 sums to the
+ * workspace; the workspace query sizes them).  K is thus cut into KS W
+ * contiguous ranges of S groups of 128 elements; each range is accumulated
+ * in float32 one 32-element step at a time, and the range sums are added in
+ * ascending K order before the multiplication by fp32(S_a * S_b).
  *
  * Alignment: a_codes and b_codes 8-byte aligned (16-byte, and the scale
  * arrays too, for the few-token products); the global-scale pointers 4-byte

@@ -233,9 +233,17 @@ def test_gemm_nvfp4_validation():
     # products of at most 16 tokens with K a multiple of 256 (up to 16384) decode in registers
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 4096, 4096) == 0
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(1, 4096, 16384) == 0
-    assert lib.fp4q_gemm_nvfp4_workspace_bytes(17, 4096, 4096) == (17 + 4096) * 4096 * 2
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(17, 4096, 4096) == 0  # up to 64 tokens on 4096 columns
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(17, 8192, 4096) == 0  # up to 32 tokens on any width
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(33, 8192, 4096) == (33 + 8192) * 4096 * 2
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(65, 1024, 4096) == (65 + 1024) * 4096 * 2
     assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 4096, 4224) == (16 + 4096) * 4224 * 2
-    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 64, 32768) == (16 + 64) * 32768 * 2
+    # K split over two workgroups per column tile: room for their partial sums
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 64, 32768) == 2 * 16 * 64 * 4
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(20, 4096, 14336) == 2 * 20 * 4096 * 4
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(60, 2048, 14336) == 4 * 60 * 2048 * 4
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 64, 65536) == 4 * 16 * 64 * 4
+    assert lib.fp4q_gemm_nvfp4_workspace_bytes(16, 64, 131072) == (16 + 64) * 131072 * 2
 
     def gn(**kw):
         m, n, k = kw.get("m", 64), kw.get("n", 64), kw.get("k", 128)

@@ -385,17 +385,21 @@ def test_gemm_nvfp4_of_quantized_operands_and_nan_scale():
     assert np.all(np.isfinite(c2[mask]))
 
 
-# at most 16 tokens with K a multiple of 256: the few-token kernel (codes decoded to float16 in
-# registers, float16 matrix cores, no workspace)
+# at most 32 tokens (64 on outputs of at most 4096 columns) with K a multiple of 256: the few-token
+# kernel (codes decoded to float16 in registers, float16 matrix cores, no workspace)
 @pytest.mark.parametrize("m,n,k", [(1, 16, 256), (3, 100, 4096), (16, 4096, 4096), (7, 1000, 14336),
-                                   (16, 33, 8192), (2, 8200, 1024), (16, 14336, 4096), (9, 512, 16384)])
+                                   (16, 33, 8192), (2, 8200, 1024), (16, 14336, 4096), (9, 512, 16384),
+                                   (17, 1000, 4096), (33, 300, 2048), (64, 4096, 4096), (20, 2000, 8192),
+                                   (32, 8200, 4096), (20, 4096, 14336), (60, 2048, 14336), (5, 512, 32768)])
 def test_gemm_nvfp4_few_tokens_exact(m, n, k):
+    """The last three split K over two or four workgroups per column tile (partial sums in the
+    workspace, added in K order)."""
     rng = np.random.default_rng(5300 + m + n + k)
     ac, _ = _rand_nv(rng, m, k)
     bc, _ = _rand_nv(rng, n, k)
     as_ = np.full((m, k // 16), 0x38, np.uint8)  # E4M3 1.0
     bs = np.full((n, k // 16), 0x38, np.uint8)
-    assert _fq_lib().fp4q_gemm_nvfp4_workspace_bytes(m, n, k) == 0
+    assert _fq_lib().fp4q_gemm_nvfp4_workspace_bytes(m, n, k) < (m + n) * k * 2
     c = _run_nv(ac, as_, 1.0, bc, bs, 1.0)
     np.testing.assert_array_equal(c, GM.gemm_nvfp4(ac, as_, np.float32(1), bc, bs, np.float32(1)))
 
@@ -409,7 +413,8 @@ def _rand_nv_any_scale(rng, rows, k):
 
 
 @pytest.mark.parametrize("m,n,k,out_dtype", [(1, 4096, 14336, torch.float32), (5, 300, 4096, torch.bfloat16),
-                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16)])
+                                             (16, 2048, 2048, torch.float32), (9, 8232, 2048, torch.bfloat16),
+                                             (48, 3000, 2048, torch.bfloat16), (24, 4096, 14336, torch.bfloat16)])
 def test_gemm_nvfp4_few_tokens_within_bound(m, n, k, out_dtype):
     rng = np.random.default_rng(5400 + m + n + k)
     ac, as_ = _rand_nv_any_scale(rng, m, k)
