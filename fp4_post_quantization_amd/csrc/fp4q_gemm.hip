@@ -1184,8 +1184,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void nv_gemm_ring_kernel(
 
 #pragma unroll
   for (int s = 0; s < NS; ++s) issue(min(s, nst - 1), s);
+  wait_lgkmcnt0();  // this wave's parts_tab stores are complete ...
   wait_vmcnt<(NS - 1) * LOADS>();
-  stage_barrier();  // also publishes parts_tab
+  stage_barrier();  // ... and visible to every wave after the barrier
 
   int slot = 0;
   for (int st = 0; st < nst; ++st) {
