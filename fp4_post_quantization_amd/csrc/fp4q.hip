@@ -885,7 +885,8 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       const float wi = row_bcast<tt>(w[k]);
       const float us_i = wi * S_inv;
       const float y_i = us_i * R;
-      const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0) & 0xFu;
+      // byte 0 holds y_i's code and that of +0 (nibble 0); the other bytes keep the 0 passed in
+      const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y_i, 0.0f, 1.0f, 0);
       const float q = fp4x2_to_f32<0>(code).x;  // signed E2M1 value
       const float what = MX ? q * V : (q * V) * S;  // q * V exact; NVFP4: one rounding by S
       const float err = (wi - what) * rd;
