@@ -171,6 +171,19 @@ def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     ms_step = _events_time(step, steps)
+    # per-step distribution (a second, separately timed pass: one event pair per step)
+    per_step = []
+    for i in range(steps):
+        s_ev = torch.cuda.Event(enable_timing=True)
+        e_ev = torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        step(i)
+        e_ev.record()
+        per_step.append((s_ev, e_ev))
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in per_step)
+    pct = lambda q: us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))]
+    bench_nvfp4_matrix.step_us = {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
     # out.global_scale now holds S; passing it back launches the sweep kernel only
     sweep = lambda i: fq.quantize_nvfp4(bufs[i % len(bufs)], imp, window=window, hadamard_n=had,
                                         global_scale=out.global_scale, out=out, ws=ws)
@@ -203,6 +216,7 @@ def run_c2(args, x_cpu, imp_cpu, cpu_line):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_us_percentiles": getattr(bench_nvfp4_matrix, "step_us", None),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
