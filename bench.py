@@ -293,6 +293,9 @@ def run_other(args):
         res["c2_wmse"] = study.nvfp4_scale_rules(x2.to("cuda:0"), imp2.to("cuda:0"))
         res["c4_q_mse"] = study.nvfp4_scale_rules(W.c4_matrix("q").to("cuda:0"))
         res["c1_mse"] = study.nvfp4_scale_rules(W.c1_weight().to("cuda:0"))
+        res["c5_gate_h16_wmse"] = study.nvfp4_scale_rules(W.c5_matrix(0, "gate", "cuda:0"),
+                                                          W.c5_importance("gate").to("cuda:0"), iters=5,
+                                                          hadamard_n=16)
         x3 = W.c3_activation().to("cuda:0")
         res["c3_mxfp4"] = [study.mxfp4_code_usage(x3, window=w, hadamard_n=h)
                            for h in (0, 32) for w in ((0, 0), (-1, 0))]

@@ -56,16 +56,16 @@ def _events_ms(fn, iters):
     return s.elapsed_time(e) / iters
 
 
-def nvfp4_scale_rules(x, importance=None, iters=20):
-    """AbsMax vs ScaleSweep vs exhaustive on one matrix."""
+def nvfp4_scale_rules(x, importance=None, iters=20, hadamard_n=0):
+    """AbsMax vs ScaleSweep vs exhaustive on one matrix (after the optional block rotation)."""
     sweep_window = (-8, 7) if importance is not None else (-3, 7)
     rules = {"absmax": (0, 0), "sweep": sweep_window, "exhaustive": (-126, 126)}
     res = {}
     out = {}
     for name, win in rules.items():
-        r = quantize_nvfp4(x, importance, window=win, check=True)
+        r = quantize_nvfp4(x, importance, window=win, hadamard_n=hadamard_n, check=True)
         out[name] = r
-        ms = _events_ms(lambda: quantize_nvfp4(x, importance, window=win, out=r), iters)
+        ms = _events_ms(lambda: quantize_nvfp4(x, importance, window=win, hadamard_n=hadamard_n, out=r), iters)
         res[name] = {"window": list(win), "ms": ms, "loss_sum": float(r.block_loss.double().sum())}
     a, s, e = (out[k].block_loss.double() for k in ("absmax", "sweep", "exhaustive"))
     nblk = a.numel()
