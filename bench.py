@@ -30,7 +30,8 @@ gptq (GPTQ with ScaleSweep group scales on the 4096 x 4096 weight),
 w4a4 (an 8B-shaped decoder layer at 8192 tokens in W4A4 MXFP4: on-the-fly
 activation quantization with a 32-point Hadamard, then the seven projections
 on the scaled FP4 matrix cores against weights quantized in the same basis),
-w4a4nv (the same layer with NVFP4 operands on the bf16 matrix cores).
+w4a4nv (the same layer with NVFP4 operands on the bf16 matrix cores),
+oracle (the CPU oracle alone, one process, on a 256-row sample of each workload).
 """
 
 import argparse
@@ -142,6 +143,48 @@ def cpu_baseline(x_cpu, imp, sample_rows, window=None):
             "single_core": {"value": xs.size / dt1 / 1e9, "cores": 1,
                             "sample": f"first {sample_rows} rows ({xs.size} elements), {dt1:.1f} s in one process"},
             "cpu_model": _cpu_model()}
+
+
+def oracle_table(sample_rows=256):
+    """The CPU oracle (numpy, unchanged) in one process on the first
+    ``sample_rows`` rows of each workload: elements per second per config,
+    for comparison with the GPU rates.  A sample's global scale is its own
+    max/1536.  The 70B-shaped matrix is drawn on cuda:0 when a GPU is present
+    (its defining generator), else on the CPU."""
+    import torch
+    import workloads as W
+    from oracle import quant as Q
+    dev = "cuda:0" if torch.cuda.is_available() else "cpu"
+    x2, imp2 = W.c2_weight_and_importance()
+    x3 = W.c3_activation()
+    gate = W.c5_matrix(0, "gate", dev)[:sample_rows].float().cpu().numpy()
+    f = lambda t, n=sample_rows: t[:n].float().numpy()
+    cases = [
+        ("c1 NVFP4 MSE fp32 256x1024 (whole)", lambda: Q.quantize_nvfp4(W.c1_weight().float().numpy()),
+         256 * 1024),
+        ("c2 NVFP4 WMSE [-8,7] bf16 4096x4096", lambda: Q.quantize_nvfp4(f(x2), imp2.numpy(), window=(-8, 7)),
+         sample_rows * 4096),
+        ("c3a MXFP4 AbsMax 8192x4096", lambda: Q.quantize_mxfp4(f(x3), window=(0, 0)), sample_rows * 4096),
+        ("c3b MXFP4 [-1,0] 8192x4096", lambda: Q.quantize_mxfp4(f(x3), window=(-1, 0)), sample_rows * 4096),
+        ("c3c MXFP4 [-1,0] after H32", lambda: Q.quantize_mxfp4(f(x3), window=(-1, 0), hadamard_n=32),
+         sample_rows * 4096),
+        ("c4 8B q projection, NVFP4 MSE [-3,7]", lambda: Q.quantize_nvfp4(f(W.c4_matrix("q"))), sample_rows * 4096),
+        ("c4 8B q projection, NVFP4 WMSE [-8,7]",
+         lambda: Q.quantize_nvfp4(f(W.c4_matrix("q")), W.c4_importance("q").numpy(), window=(-8, 7)),
+         sample_rows * 4096),
+        ("c5 70B gate layer 0, H16 + NVFP4 WMSE [-8,7]",
+         lambda: Q.quantize_nvfp4(gate, W.c5_importance("gate").numpy(), window=(-8, 7), hadamard_n=16),
+         sample_rows * 8192),
+    ]
+    out = []
+    for name, fn, n in cases:
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        out.append({"config": name, "sample_elements": n, "seconds": round(dt, 3),
+                    "G_elements_per_s": n / dt / 1e9})
+        print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+    return {"config": "oracle", "cores": 1, "sample_rows": sample_rows, "cpu_model": _cpu_model(), "rows": out}
 
 
 def prewarm(step, seconds=0.3):
@@ -514,6 +557,9 @@ def main():
         x_cpu, imp_cpu = W.c2_weight_and_importance()
         if not args.no_cpu_baseline:  # before the GPU is initialised: the CPU baseline forks
             cpu_line = cpu_baseline(x_cpu, imp_cpu, args.cpu_rows, window=(-8, 7))
+    if args.config == "oracle":  # the oracle's own host rates, no GPU work
+        print(json.dumps(oracle_table()), flush=True)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
