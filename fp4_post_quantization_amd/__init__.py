@@ -48,13 +48,17 @@ _WORKSPACES = {}
 
 
 def workspace(device=None):
-    """The per-device workspace used when none is passed (calls that overlap
-    on one device through this shared workspace race; pass your own)."""
+    """The workspace used when none is passed: one per device and stream,
+    taken for the device's current stream (calls on one stream run in
+    order, so they may share it; calls on different streams get different
+    ones).  The status word in it is sticky per workspace."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    ws = _WORKSPACES.get(device.index)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (index, torch.cuda.current_stream(index).cuda_stream)
+    ws = _WORKSPACES.get(key)
     if ws is None:
-        ws = torch.zeros(L.load().fp4q_workspace_bytes(), dtype=torch.uint8, device=device)
-        _WORKSPACES[device.index] = ws
+        ws = torch.zeros(L.load().fp4q_workspace_bytes(), dtype=torch.uint8, device=torch.device("cuda", index))
+        _WORKSPACES[key] = ws
     return ws
 
 

@@ -271,6 +271,34 @@ def test_deterministic():
         assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
+def test_default_workspace_is_per_stream():
+    """Calls that pass no workspace on two streams use two workspaces (the
+    global-max partials and status word of one cannot be overwritten by the
+    other), and both give the default stream's result."""
+    fq = _fp4()
+    x = W.random_matrix(300, 1024, seed=58, dtype=torch.bfloat16).to(DEV)
+    imp = W.random_importance(1024, seed=59).to(DEV)
+    main = fq.workspace(DEV)
+    assert fq.workspace(DEV) is main
+    ref = fq.quantize_nvfp4(x, imp, check=True)
+    side = [torch.cuda.Stream(DEV) for _ in range(2)]
+    torch.cuda.synchronize()
+    outs = []
+    for s in side:
+        with torch.cuda.stream(s):
+            assert fq.workspace(DEV) is not main
+            outs.append(fq.quantize_nvfp4(x, imp))
+    torch.cuda.synchronize()
+    assert fq.workspace(DEV) is main
+    with torch.cuda.stream(side[0]):
+        ws0 = fq.workspace(DEV)
+    with torch.cuda.stream(side[1]):
+        assert fq.workspace(DEV) is not ws0
+    for o in outs:
+        for f in ("codes", "scales", "offsets", "block_loss", "global_scale"):
+            assert torch.equal(getattr(o, f), getattr(ref, f)), f
+
+
 # ------------------------------------------------------------- MXFP4 ----
 @pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (257, 4128), (64, 1024)])
 @pytest.mark.parametrize("window", [(-1, 0), (0, 0), (-3, 2)])
