@@ -54,7 +54,7 @@ def workspace(device=None):
     ones).  The status word in it is sticky per workspace."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     index = device.index if device.index is not None else torch.cuda.current_device()
-    key = (index, torch.cuda.current_stream(index).cuda_stream)
+    key = (index, _stream(device))
     ws = _WORKSPACES.get(key)
     if ws is None:
         ws = torch.zeros(L.load().fp4q_workspace_bytes(), dtype=torch.uint8, device=torch.device("cuda", index))
@@ -110,8 +110,17 @@ def _matrix(x):
     return x, max(ld, x.size(1))
 
 
+# torch's raw query of the current stream handle (the one its own generated
+# code uses) costs far less host time per call than building a Stream object
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device):
-    return ctypes_ptr(torch.cuda.current_stream(device).cuda_stream)
+    """The device's current HIP stream handle, as an int."""
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    if _RAW_STREAM is not None:
+        return int(_RAW_STREAM(index))
+    return int(torch.cuda.current_stream(index).cuda_stream)
 
 
 def ctypes_ptr(v):

@@ -271,6 +271,16 @@ def test_deterministic():
         assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
+def test_binding_passes_the_current_stream():
+    fq = _fp4()
+    d = torch.device(DEV)
+    assert fq._stream(d) == int(torch.cuda.current_stream(d).cuda_stream)
+    side = torch.cuda.Stream(d)
+    with torch.cuda.stream(side):
+        assert fq._stream(d) == int(side.cuda_stream) == int(torch.cuda.current_stream(d).cuda_stream)
+    assert fq._stream(d) != int(side.cuda_stream)
+
+
 def test_default_workspace_is_per_stream():
     """Calls that pass no workspace on two streams use two workspaces (the
     global-max partials and status word of one cannot be overwritten by the
