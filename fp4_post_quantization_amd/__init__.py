@@ -359,11 +359,15 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
 
     ``a`` and ``b`` are MXFP4Result (or (codes, scales) pairs) as written by
     ``quantize_mxfp4``: A is M x K (activations), B is N x K (weights).
-    Returns C [M, N] in float32 or bfloat16.  With ``use_workspace`` (and K
-    a multiple of 256) the library gets a workspace (``workspace_buf`` or a
+    Returns C [M, N] in float32 or bfloat16.  Few-token products (M <= 16,
+    or M <= 64 on N <= 4096; K a multiple of 512, at most 16384, or 8192
+    above 16 tokens) run in one kernel without a workspace.  Otherwise, with ``use_workspace`` (and K a multiple of
+    256), the library gets the workspace that
+    ``fp4q_gemm_mxfp4_workspace_bytes`` asks for (``workspace_buf`` or a
     fresh one): large products copy the scales stage-major into it (same
-    result), few-token products (M <= 64) split K and keep their partial
-    sums there (added in K order: the result can differ in rounding)."""
+    result), other products of up to 64 tokens split K and keep their
+    partial sums there (added in K order: the result can differ in
+    rounding)."""
     lib = L.load()
     ac, as_ = (a.codes, a.scales) if isinstance(a, MXFP4Result) else a
     bc, bs = (b.codes, b.scales) if isinstance(b, MXFP4Result) else b
@@ -394,10 +398,12 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
 def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
     """C = fp32(S_a S_b) * A_hat @ B_hat^T for NVFP4 operands (NVFP4Result
     or (codes, scales, global_scale) triples as written by quantize_nvfp4):
-    A is M x K, B is N x K.  The operands are decoded to bfloat16 (exact) in
-    a workspace, allocated here unless ``workspace_buf`` is given; products of
-    at most 16 tokens (K a multiple of 256 up to 16384) decode in registers
-    and need none."""
+    A is M x K, B is N x K.  Large products decode the operands to bfloat16
+    (exact) in a workspace, allocated here unless ``workspace_buf`` is given;
+    smaller ones decode in registers.  Few-token products (M <= 32, or
+    M <= 64 on N <= 4096; K a multiple of 256) need a workspace only when
+    they split K, for the partial sums.  ``fp4q_gemm_nvfp4_workspace_bytes``
+    gives the size in every case."""
     lib = L.load()
     ac, as_, ag = (a.codes, a.scales, a.global_scale) if isinstance(a, NVFP4Result) else a
     bc, bs, bg = (b.codes, b.scales, b.global_scale) if isinstance(b, NVFP4Result) else b
