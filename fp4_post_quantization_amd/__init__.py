@@ -104,7 +104,9 @@ def _matrix(x):
         raise ValueError("x must be a 2-D row-major matrix")
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
-    if x.stride(1) != 1 and x.size(1) > 1:
+    # rows must not overlap (a broadcast view has row stride 0): copy unless
+    # the elements are unit-strided and rows sit at least one row apart
+    if (x.stride(1) != 1 and x.size(1) > 1) or (x.size(0) > 1 and x.stride(0) < x.size(1)):
         x = x.contiguous()
     ld = x.stride(0) if x.size(0) > 1 else x.size(1)
     return x, max(ld, x.size(1))
@@ -382,14 +384,15 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
         raise ValueError("scales must be rows x K/32")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
+    if (out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1
+            or (m > 1 and out.stride(0) < n)):
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     code = L.F32 if out.dtype == torch.float32 else L.BF16
     need = lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) if use_workspace else 0
     if need and (workspace_buf is None or workspace_buf.numel() < need):
         workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,
-                                float(alpha), code, out.data_ptr(), out.stride(0),
+                                float(alpha), code, out.data_ptr(), out.stride(0) if m > 1 else n,
                                 _ptr(workspace_buf) if need else None, workspace_buf.numel() if need else 0,
                                 _stream(dev)))
     return out
@@ -420,14 +423,15 @@ def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
         raise ValueError("scales must be rows x K/16")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1:
+    if (out.dtype not in (torch.float32, torch.bfloat16) or out.shape != (m, n) or out.stride(1) != 1
+            or (m > 1 and out.stride(0) < n)):
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     need = lib.fp4q_gemm_nvfp4_workspace_bytes(m, n, k)
     if need and (workspace_buf is None or workspace_buf.numel() < need):
         workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     code = L.F32 if out.dtype == torch.float32 else L.BF16
     L.check(lib.fp4q_gemm_nvfp4(ac.data_ptr(), as_.data_ptr(), ag.data_ptr(), bc.data_ptr(), bs.data_ptr(),
-                                bg.data_ptr(), m, n, k, code, out.data_ptr(), out.stride(0),
+                                bg.data_ptr(), m, n, k, code, out.data_ptr(), out.stride(0) if m > 1 else n,
                                 _ptr(workspace_buf) if need else None, workspace_buf.numel() if need else 0,
                                 _stream(dev)))
     return out

@@ -491,3 +491,29 @@ def test_gemm_nvfp4_full_size_sampled_rows():
     rows = np.sort(np.concatenate([[0, 255, 256, 8191], rng.choice(m, 36, replace=False)]))
     c = c_all[torch.from_numpy(rows).to(DEV)].float().cpu().numpy().astype(np.float64)
     _check_nv(c, ac, as_, ag, bc, bs, bg, k, bf16=True, rows=rows)
+
+
+def test_single_row_output_view_with_any_row_stride():
+    """A one-row output view whose row stride is below N (a transposed
+    column) is written like a dense row: its row stride is never used."""
+    rng = np.random.default_rng(77)
+    k, n = 1024, 96
+    ac, as_ = _rand_mx(rng, 1, k)
+    bc, bs = _rand_mx(rng, n, k)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    fq = _fq()
+    ref = fq.gemm_mxfp4((a, asd), (b, bsd))
+    out = torch.empty((n, 1), device=DEV).t()
+    assert out.shape == (1, n) and out.stride(0) < n
+    got = fq.gemm_mxfp4((a, asd), (b, bsd), out=out)
+    nac, nas = _rand_nv(rng, 1, k)
+    nbc, nbs = _rand_nv(rng, n, k)
+    na, nasd, nb, nbsd = _dev(nac, nas, nbc, nbs)
+    nref = fq.gemm_nvfp4((na, nasd, 1.0), (nb, nbsd, 1.0))
+    nout = torch.empty((n, 1), device=DEV).t()
+    ngot = fq.gemm_nvfp4((na, nasd, 1.0), (nb, nbsd, 1.0), out=nout)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == out.data_ptr() and torch.equal(got, ref)
+    assert ngot.data_ptr() == nout.data_ptr() and torch.equal(ngot, nref)
+    with pytest.raises(ValueError):
+        fq.gemm_mxfp4((a.expand(3, -1), asd.expand(3, -1)), (b, bsd), out=torch.empty(n, device=DEV).expand(3, n))

@@ -271,6 +271,26 @@ def test_deterministic():
         assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
+def test_broadcast_and_strided_views_are_read_as_their_values():
+    """A row-broadcast view (row stride 0) and a column-strided view reach
+    the library as dense copies, so it never reads past the storage."""
+    fq = _fp4()
+    row = W.random_matrix(1, 512, seed=60, dtype=torch.bfloat16).to(DEV)
+    view = row.expand(37, 512)
+    dense = view.contiguous()
+    a = fq.quantize_nvfp4(view, check=True)
+    b = fq.quantize_nvfp4(dense, check=True)
+    wide = W.random_matrix(20, 1024, seed=61).to(DEV)
+    c = fq.quantize_mxfp4(wide[:, ::2], check=True)
+    d = fq.quantize_mxfp4(wide[:, ::2].contiguous(), check=True)
+    torch.cuda.synchronize()
+    for f in ("codes", "scales", "offsets", "block_loss", "global_scale"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    for f in ("codes", "scales", "offsets", "block_loss"):
+        assert torch.equal(getattr(c, f), getattr(d, f)), f
+    _check_nvfp4(a, _oracle_nvfp4(dense.cpu()))
+
+
 def test_binding_passes_the_current_stream():
     fq = _fp4()
     d = torch.device(DEV)
