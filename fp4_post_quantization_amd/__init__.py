@@ -142,6 +142,44 @@ def _importance(importance, cols, device):
     return imp
 
 
+def _given(t, shape, dtype, device, name):
+    """A tensor the caller passes for the library to read or write in place:
+    checked against the shape, dtype and device it must have, and required
+    to be dense, so no access can fall outside it."""
+    if (not isinstance(t, torch.Tensor) or t.shape != shape or t.dtype != dtype or t.device != device
+            or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+    return t
+
+
+def _check_result(out, rows, cols, block, device):
+    """A caller-given NVFP4Result / MXFP4Result, checked like _given (one
+    pass of inexpensive tests; the per-field checks name a mismatch)."""
+    per_block = (rows, cols // block)
+    c, sc, g = out.codes, out.scales, getattr(out, "global_scale", None)
+    bl, of = out.block_loss, out.offsets
+    ok = (isinstance(c, torch.Tensor) and c.shape == (rows, cols // 2) and c.dtype == torch.uint8
+          and c.device == device and c.is_contiguous()
+          and isinstance(sc, torch.Tensor) and sc.shape == per_block and sc.dtype == torch.uint8
+          and sc.device == device and sc.is_contiguous()
+          and (g is None or (isinstance(g, torch.Tensor) and g.shape == (1,) and g.dtype == torch.float32
+                             and g.device == device))
+          and (bl is None or (isinstance(bl, torch.Tensor) and bl.shape == per_block and bl.dtype == torch.float32
+                              and bl.device == device and bl.is_contiguous()))
+          and (of is None or (isinstance(of, torch.Tensor) and of.shape == per_block and of.dtype == torch.int8
+                              and of.device == device and of.is_contiguous())))
+    if ok:
+        return
+    _given(c, (rows, cols // 2), torch.uint8, device, "out.codes")
+    _given(sc, per_block, torch.uint8, device, "out.scales")
+    if g is not None:
+        _given(g, (1,), torch.float32, device, "out.global_scale")
+    if bl is not None:
+        _given(bl, per_block, torch.float32, device, "out.block_loss")
+    if of is not None:
+        _given(of, per_block, torch.int8, device, "out.offsets")
+
+
 def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=None, *,
                    out=None, with_loss=True, with_offsets=True, ws=None, check=False):
     """NVFP4 ScaleSweep quantization of a 2-D float32/bfloat16 device tensor.
@@ -167,6 +205,8 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
             block_loss=torch.empty((rows, cols // 16), dtype=torch.float32, device=dev) if with_loss else None,
             offsets=torch.empty((rows, cols // 16), dtype=torch.int8, device=dev) if with_offsets else None,
         )
+    else:
+        _check_result(out, rows, cols, 16, dev)
     flags = 0
     if global_scale is not None:
         same = isinstance(global_scale, torch.Tensor) and global_scale.data_ptr() == out.global_scale.data_ptr()
@@ -191,7 +231,9 @@ def global_scale_nvfp4(x, hadamard_n=0, *, out=None, ws=None):
     x, ld = _matrix(x)
     rows, cols = x.shape
     dev = x.device
-    out = torch.empty(1, dtype=torch.float32, device=dev) if out is None else out
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=dev)
+    _given(out, (1,), torch.float32, dev, "out")
     ws = workspace(dev) if ws is None else ws
     L.check(lib.fp4q_global_scale_nvfp4(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(hadamard_n),
                                         out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
@@ -215,6 +257,8 @@ def quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, *, out=None
             block_loss=torch.empty((rows, cols // 32), dtype=torch.float32, device=dev) if with_loss else None,
             offsets=torch.empty((rows, cols // 32), dtype=torch.int8, device=dev) if with_offsets else None,
         )
+    else:
+        _check_result(out, rows, cols, 32, dev)
     ws = workspace(dev) if ws is None else ws
     L.check(lib.fp4q_quantize_mxfp4(
         x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 32, loss, int(window[0]), int(window[1]),
@@ -236,7 +280,8 @@ def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub
     rows, cols = x.shape
     dev = x.device
     fmt_code = {"nvfp4": L.NVFP4, "mxfp4": L.MXFP4}[fmt]
-    scales = scales.contiguous()
+    block = 16 if fmt_code == L.NVFP4 else 32
+    scales = _given(scales.contiguous(), (rows, cols // block), torch.uint8, dev, "scales")
     c = None
     if coeffs is not None:
         c = torch.as_tensor(coeffs, device=dev).to(torch.float16).contiguous()
@@ -245,10 +290,16 @@ def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub
     gs = None
     if fmt_code == L.NVFP4:
         gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1)
-    codes = out_codes if out_codes is not None else torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if out_codes is not None:
+        codes = _given(out_codes, (rows, cols // 2), torch.uint8, dev, "out_codes")
+    else:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
     dq = None
     if dequant:
-        dq = out_dequant if out_dequant is not None else torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        if out_dequant is not None:
+            dq = _given(out_dequant, (rows, cols), torch.float32, dev, "out_dequant")
+        else:
+            dq = torch.empty((rows, cols), dtype=torch.float32, device=dev)
     ws = workspace(dev) if ws is None else ws
     L.check(lib.fp4q_quantize_relaxed(
         fmt_code, x.data_ptr(), _dtype_code(x), rows, cols, ld, scales.data_ptr(), _ptr(gs), _ptr(c), int(sub),
@@ -332,10 +383,11 @@ def dequantize(fmt, codes, scales, global_scale=None, out=None):
     rows, half = codes.shape
     cols = half * 2
     dev = codes.device
-    codes = codes.contiguous()
-    scales = scales.contiguous()
+    codes = _given(codes.contiguous(), (rows, half), torch.uint8, dev, "codes")
+    scales = _given(scales.contiguous(), (rows, cols // block), torch.uint8, dev, "scales")
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    _given(out, (rows, cols), torch.float32, dev, "out")
     gs = None
     if fmt_code == L.NVFP4:
         gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1)
@@ -351,6 +403,7 @@ def block_hadamard(x, n, out=None):
     rows, cols = x.shape
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    _given(out, (rows, cols), torch.float32, x.device, "out")
     L.check(lib.fp4q_block_hadamard(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(n), out.data_ptr(),
                                     _stream(x.device)))
     return out

@@ -291,6 +291,31 @@ def test_broadcast_and_strided_views_are_read_as_their_values():
     _check_nvfp4(a, _oracle_nvfp4(dense.cpu()))
 
 
+def test_caller_buffers_are_checked_before_the_library_writes():
+    fq = _fp4()
+    x = W.random_matrix(32, 256, seed=62).to(DEV)
+    good = fq.quantize_nvfp4(x)
+    bad = [good._replace(codes=good.codes[:, :64]),
+           good._replace(scales=good.scales.to(torch.int8)),
+           good._replace(block_loss=torch.empty((32, 32), device=DEV)[:, ::2]),
+           good._replace(offsets=good.offsets.cpu())]
+    for out in bad:
+        with pytest.raises(ValueError):
+            fq.quantize_nvfp4(x, out=out)
+    mx = fq.quantize_mxfp4(x)
+    with pytest.raises(ValueError):
+        fq.quantize_mxfp4(x, out=mx._replace(scales=good.scales))
+    with pytest.raises(ValueError):
+        fq.dequantize("nvfp4", good.codes, good.scales[:, :8], good.global_scale)
+    with pytest.raises(ValueError):
+        fq.block_hadamard(x, 16, out=torch.empty((32, 128), device=DEV))
+    with pytest.raises(ValueError):
+        fq.global_scale_nvfp4(x, out=torch.empty(1, dtype=torch.float64, device=DEV))
+    with pytest.raises(ValueError):
+        fq.quantize_relaxed(x, good.scales, global_scale=good.global_scale, out_codes=good.codes[:16])
+    torch.cuda.synchronize()
+
+
 def test_binding_passes_the_current_stream():
     fq = _fp4()
     d = torch.device(DEV)
