@@ -152,6 +152,25 @@ def _given(t, shape, dtype, device, name):
     return t
 
 
+def _ws(ws, device):
+    """The caller's workspace (a dense uint8 tensor on the call's device) or
+    the default one for the device's current stream."""
+    if ws is None:
+        return workspace(device)
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous uint8 tensor on {device}")
+    return ws
+
+
+def _same_device(device, **tensors):
+    """Every operand of a product on the device of its first operand (a GPU)."""
+    if device.type != "cuda":
+        raise ValueError("the operands must be device tensors")
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+
+
 def _check_result(out, rows, cols, block, device):
     """A caller-given NVFP4Result / MXFP4Result, checked like _given (one
     pass of inexpensive tests; the per-field checks name a mismatch)."""
@@ -213,7 +232,7 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
         if not same:
             out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
         flags |= L.GIVEN_SCALE
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_quantize_nvfp4(
         x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 16, loss, int(window[0]), int(window[1]),
         int(hadamard_n), flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(),
@@ -234,7 +253,7 @@ def global_scale_nvfp4(x, hadamard_n=0, *, out=None, ws=None):
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=dev)
     _given(out, (1,), torch.float32, dev, "out")
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_global_scale_nvfp4(x.data_ptr(), _dtype_code(x), rows, cols, ld, int(hadamard_n),
                                         out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
     return out
@@ -259,7 +278,7 @@ def quantize_mxfp4(x, importance=None, window=(-1, 0), hadamard_n=0, *, out=None
         )
     else:
         _check_result(out, rows, cols, 32, dev)
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_quantize_mxfp4(
         x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 32, loss, int(window[0]), int(window[1]),
         int(hadamard_n), out.codes.data_ptr(), out.scales.data_ptr(), _ptr(out.block_loss),
@@ -300,7 +319,7 @@ def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub
             dq = _given(out_dequant, (rows, cols), torch.float32, dev, "out_dequant")
         else:
             dq = torch.empty((rows, cols), dtype=torch.float32, device=dev)
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_quantize_relaxed(
         fmt_code, x.data_ptr(), _dtype_code(x), rows, cols, ld, scales.data_ptr(), _ptr(gs), _ptr(c), int(sub),
         codes.data_ptr(), _ptr(dq), ws.data_ptr(), ws.numel(), _stream(dev)))
@@ -336,7 +355,7 @@ def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *,
     if global_scale is not None:
         out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
         flags |= L.GIVEN_SCALE
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_gptq_nvfp4(
         work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
         flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(),
@@ -366,7 +385,7 @@ def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=
         codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
         scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
         block_loss=None, offsets=None)
-    ws = workspace(dev) if ws is None else ws
+    ws = _ws(ws, dev)
     L.check(lib.fp4q_gptq_mxfp4(
         work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
         out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
@@ -433,6 +452,7 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
     k = 2 * kh
     dev = ac.device
     ac, as_, bc, bs = (t.contiguous() for t in (ac, as_, bc, bs))
+    _same_device(dev, a_scales=as_, b_codes=bc, b_scales=bs, out=out, workspace_buf=workspace_buf)
     if as_.shape != (m, k // 32) or bs.shape != (n, k // 32):
         raise ValueError("scales must be rows x K/32")
     if out is None:
@@ -442,6 +462,8 @@ def gemm_mxfp4(a, b, *, alpha=1.0, out_dtype=torch.float32, out=None, workspace_
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     code = L.F32 if out.dtype == torch.float32 else L.BF16
     need = lib.fp4q_gemm_mxfp4_workspace_bytes(m, n, k) if use_workspace else 0
+    if workspace_buf is not None and not workspace_buf.is_contiguous():
+        raise ValueError("workspace_buf must be contiguous")
     if need and (workspace_buf is None or workspace_buf.numel() < need):
         workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     L.check(lib.fp4q_gemm_mxfp4(ac.data_ptr(), as_.data_ptr(), bc.data_ptr(), bs.data_ptr(), m, n, k,
@@ -470,6 +492,7 @@ def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
     k = 2 * kh
     dev = ac.device
     ac, as_, bc, bs = (t.contiguous() for t in (ac, as_, bc, bs))
+    _same_device(dev, a_scales=as_, b_codes=bc, b_scales=bs, out=out, workspace_buf=workspace_buf)
     ag = torch.as_tensor(ag, dtype=torch.float32, device=dev).reshape(1)
     bg = torch.as_tensor(bg, dtype=torch.float32, device=dev).reshape(1)
     if as_.shape != (m, k // 16) or bs.shape != (n, k // 16):
@@ -480,6 +503,8 @@ def gemm_nvfp4(a, b, *, out_dtype=torch.float32, out=None, workspace_buf=None):
             or (m > 1 and out.stride(0) < n)):
         raise ValueError("out must be a row-major float32 or bfloat16 [M, N] tensor")
     need = lib.fp4q_gemm_nvfp4_workspace_bytes(m, n, k)
+    if workspace_buf is not None and not workspace_buf.is_contiguous():
+        raise ValueError("workspace_buf must be contiguous")
     if need and (workspace_buf is None or workspace_buf.numel() < need):
         workspace_buf = torch.empty(need, dtype=torch.uint8, device=dev)
     code = L.F32 if out.dtype == torch.float32 else L.BF16

@@ -517,3 +517,26 @@ def test_single_row_output_view_with_any_row_stride():
     assert ngot.data_ptr() == nout.data_ptr() and torch.equal(ngot, nref)
     with pytest.raises(ValueError):
         fq.gemm_mxfp4((a.expand(3, -1), asd.expand(3, -1)), (b, bsd), out=torch.empty(n, device=DEV).expand(3, n))
+
+
+def test_operands_on_another_device_are_refused():
+    rng = np.random.default_rng(78)
+    ac, as_ = _rand_mx(rng, 4, 512)
+    bc, bs = _rand_mx(rng, 64, 512)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    fq = _fq()
+    with pytest.raises(ValueError):
+        fq.gemm_mxfp4((a, asd), (b.cpu(), bsd))
+    with pytest.raises(ValueError):
+        fq.gemm_mxfp4((a, asd), (b, bsd), out=torch.empty((4, 64)))
+    with pytest.raises(ValueError):
+        fq.gemm_mxfp4((a.cpu(), asd.cpu()), (b.cpu(), bsd.cpu()))
+    nac, nas = _rand_nv(rng, 4, 512)
+    nbc, nbs = _rand_nv(rng, 64, 512)
+    na, nasd, nb, nbsd = _dev(nac, nas, nbc, nbs)
+    with pytest.raises(ValueError):
+        fq.gemm_nvfp4((na, nasd, 1.0), (nb, nbsd.cpu(), 1.0))
+    x = torch.randn(8, 64, device=DEV)
+    with pytest.raises(ValueError):
+        fq.quantize_nvfp4(x, ws=torch.zeros(fq._lib.load().fp4q_workspace_bytes(), dtype=torch.uint8))
+    torch.cuda.synchronize()
