@@ -173,6 +173,9 @@ def test_edge_exact_ties():
     _check_mxfp4(r, Q.quantize_mxfp4(xm.numpy(), window=(0, 0)))
 
 
+# rows near the float32 maximum overflow S*S and the losses in the oracle on purpose (both sides
+# must then agree on inf / NaN), so numpy's overflow warnings are expected here
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
 def test_edge_subnormal_bases_and_bf16_extremes():
     rng = np.random.default_rng(51)
     x = (rng.standard_normal((16, 256)) * 1e-7).astype(np.float32)
