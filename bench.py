@@ -47,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# fp32 vector peak without packed-FP32 instructions (disabled in this build):
+# fp32 vector peak without packed-FP32 instructions (the library is compiled without them):
 # 256 CU x 64 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s
 VALU_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
 METRIC = "G elements/s quantized (NVFP4 WMSE sweep) + % of MI355X HBM roofline"
