@@ -39,9 +39,9 @@ grid; "Resumo Técnico: TORQ", B. Rotação de Alinhamento Micro, S-step)
   to [-127, 127] (a_b = 0 gives -127): the block maximum maps onto the largest
   code without clipping.  Candidates E in [E_base + lo, E_base + hi] clipped to
   [-127, 127] (default lo, hi = -1, 0); per E: y = fp32(u * 2**-E);
-  q = RNE_E2M1(y); d = q * 2**E (exact); e as above; L = fp32(L_a + L_b)
-  where L_a, L_b are the fused in-order sums above over the block's two
-  16-element halves.
+  q = RNE_E2M1(y); d = q * 2**E (exact); e as above; L = the fused in-order
+  sum above over all 32 elements of the block (one rounding per term, the
+  same rule as the NVFP4 block's 16).
   E* = smallest E with the minimum loss.  Scale byte E* + 127, offset
   E* - E_base, loss L_{E*} (no global scale).
 """
@@ -276,8 +276,8 @@ def sweep_blocks_mx(ub, w, lo, hi):
     """The MXFP4 exponent sweep on blocks of magnitudes ub [..., 32] with
     per-element weights w (broadcastable, or None for MSE): the base
     exponent, then for E = base + lo .. base + hi in ascending order the
-    loss of the block's two 16-element halves, each a fused in-order sum,
-    added in float32; returns (E*, its loss, the base exponent)."""
+    block's loss, the fused in-order sum over its 32 elements; returns
+    (E*, its loss, the base exponent)."""
     E_base = mx_base_exponent(ub.max(axis=-1))
     offsets = np.arange(lo, hi + 1)
     losses = np.empty(E_base.shape + (offsets.size,), dtype=np.float32)
@@ -288,14 +288,12 @@ def sweep_blocks_mx(ub, w, lo, hi):
         Ec = np.clip(E, -127, 127)
         down = F.pow2_f32(-Ec)[..., None]
         up = F.pow2_f32(Ec)[..., None]
-        y = (ub * down).astype(np.float32)
+        with np.errstate(over="ignore"):      # far below the base y overflows to inf: code 6
+            y = (ub * down).astype(np.float32)
         q = F.e2m1_value(F.e2m1_rne_index(y))
         d = (q * up).astype(np.float32)
         e = (ub - d).astype(np.float32)
-        halves = e.reshape(e.shape[:-1] + (2, 16))
-        wh = np.broadcast_to(w, e.shape).reshape(halves.shape) if w is not None else None
-        part = fused_sum_sq(halves, wh)
-        losses[..., k] = (part[..., 0] + part[..., 1]).astype(np.float32)
+        losses[..., k] = fused_sum_sq(e, None if w is None else np.broadcast_to(w, e.shape))
         valid[..., k] = ok
     k_best = _first_argmin(losses, valid)
     E_best = E_base + offsets[k_best]

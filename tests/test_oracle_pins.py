@@ -123,12 +123,13 @@ def test_mx_base_exponent_frexp_rule():
 def test_fused_loss_golden():
     for row in _read_golden("fused_loss.txt"):
         parts = [p.strip() for p in row.split("|")]
-        e = np.zeros(16, dtype=np.float32)
         vals = [float.fromhex(v) for v in parts[0].split()]
+        n = 16 if len(vals) <= 16 else 32      # an NVFP4 or an MXFP4 block
+        e = np.zeros(n, dtype=np.float32)
         e[:len(vals)] = vals
         w = None
         if parts[1].startswith("w:"):
-            w = np.ones(16, dtype=np.float32)
+            w = np.ones(n, dtype=np.float32)
             wv = [float.fromhex(v) for v in parts[1][2:].split()]
             w[:len(wv)] = wv
         expect = np.float32(float.fromhex(parts[-1]))
@@ -420,6 +421,126 @@ def test_mxfp4_absmax_never_clips():
     xh = Q.dequantize_mxfp4(m.codes, m.scales)
     ref = np.abs(x.astype(np.float64) - xh) ** 2
     np.testing.assert_allclose(ref.reshape(64, 8, 32).sum(-1), m.block_loss, rtol=2e-5)
+
+
+def test_mxfp4_block_loss_is_one_in_order_chain():
+    """Hand-evaluated MXFP4 block at E = 0: x = [6, 5, 0 x 14, 2^-12, 2^-12,
+    0 x 14].  6 is exact, 5 is the tie between 4 and 6 and rounds to 4
+    (error 1), 2^-12 rounds to 0.  Summed in element order over all 32
+    terms the two 2^-24 terms each meet acc = 1 at a tie and vanish: loss 1.
+    A sum of two separate 16-element halves would give 1 + 2^-23."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0], x[0, 1] = 6.0, 5.0
+    x[0, 16] = x[0, 17] = np.float32(2.0 ** -12)
+    for window in ((0, 0), (-1, 0)):
+        r = Q.quantize_mxfp4(x, window=window)
+        assert int(r.scales[0, 0]) == 127 and int(r.e_base[0, 0]) == 0
+        assert r.block_loss[0, 0].view(np.uint32) == np.float32(1.0).view(np.uint32)
+
+
+def _mx_blocks(kind, rows, rng):
+    """rows x 256 magnitudes with a per-row scale spread over many binades."""
+    if kind == "normal":
+        x = rng.standard_normal((rows, 256))
+    elif kind == "t4":
+        x = rng.standard_t(4, (rows, 256))
+    elif kind == "laplace":
+        x = rng.laplace(0, 1, (rows, 256))
+    else:  # outlier: one element of every 32-block scaled x20
+        x = rng.standard_normal((rows, 256))
+        x[:, 5::32] *= 20
+    return (x * np.exp(rng.uniform(-6, 6, (rows, 1)))).astype(np.float32)
+
+
+def _e8m0_independent(scales):
+    b = torch.from_numpy(np.ascontiguousarray(scales)).view(torch.float8_e8m0fnu)
+    return b.double().numpy()
+
+
+@pytest.mark.parametrize("window", [(-1, 0), (-3, 2), (-2, 2), (-16, 16)])
+@pytest.mark.parametrize("wmse", [False, True])
+def test_mxfp4_choice_is_float64_argmin_up_to_rounding(window, wmse):
+    """The MXFP4 exponent chosen by the sweep lies in the window around the
+    base exponent and its float64 loss (E2M1 decision taken on the float64
+    quotient, scale decoded by torch's E8M0 type) is within float32 rounding
+    of the float64 minimum over that window ("Bridging the Gap ... Microscaling
+    FP4", 2. Metodologia: the scale grid is chosen to minimise the error)."""
+    rng = np.random.default_rng(21)
+    x = _mx_blocks("t4", 48, rng)
+    imp = np.exp(2 * rng.standard_normal(256)).astype(np.float32) if wmse else None
+    r = Q.quantize_mxfp4(x, importance=imp, window=window)
+    lo, hi = window
+    off = r.offsets.astype(np.int64)
+    assert off.min() >= lo and off.max() <= hi
+    assert off.min() < 0          # the window below the base is really searched
+    ub = np.abs(x.astype(np.float64)).reshape(48, 8, 32)
+    w = None if imp is None else np.broadcast_to(imp.astype(np.float64).reshape(8, 32), ub.shape)
+    Lchosen = study.block_loss64(ub, _e8m0_independent(r.scales)[..., None], w)[..., 0]
+    Lmin = np.full(Lchosen.shape, np.inf)
+    for o in range(lo, hi + 1):
+        E = np.clip(r.e_base + o, -127, 127)
+        Lmin = np.minimum(Lmin, study.block_loss64(ub, np.ldexp(1.0, E)[..., None], w)[..., 0])
+    assert np.all(Lchosen <= Lmin * (1 + 1e-5) + 1e-300)
+
+
+@pytest.mark.parametrize("wmse", [False, True])
+def test_mxfp4_loss_matches_float64_reconstruction(wmse):
+    """The reported MXFP4 block loss equals sum_i w_i (x_i - x_hat_i)**2
+    recomputed in float64 from the packed codes and the E8M0 bytes (decoded
+    by torch), per block within the float32 summation error; catches sign,
+    nibble, exponent-bias and importance-column mix-ups."""
+    rng = np.random.default_rng(22)
+    x = _mx_blocks("laplace", 40, rng)
+    imp = np.exp(rng.standard_normal(256)).astype(np.float32) if wmse else None
+    r = Q.quantize_mxfp4(x, importance=imp, window=(-2, 1))
+    c = Q.unpack_nibbles(r.codes)
+    sign = np.where(c >> 3, -1.0, 1.0)
+    mag = F.E2M1_VALUES.astype(np.float64)[c & 7]
+    xh = sign * mag * np.repeat(_e8m0_independent(r.scales), 32, axis=-1)
+    err = (x.astype(np.float64) - xh) ** 2
+    if wmse:
+        err = err * imp.astype(np.float64)[None, :]
+    ref = err.reshape(40, 8, 32).sum(-1)
+    np.testing.assert_allclose(r.block_loss, ref, rtol=1e-5, atol=0)
+    np.testing.assert_array_equal(Q.dequantize_mxfp4(r.codes, r.scales), xh.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["normal", "t4", "laplace", "outlier"])
+def test_mxfp4_exhaustive_exponent_optimum(kind):
+    """Exhaustive float64 search over every E8M0 exponent in [-127, 127]: the
+    MSE optimum is the base exponent (least E with 6 * 2^E >= block max, the
+    S-step of "Resumo Técnico: TORQ", B. Rotação de Alinhamento Micro) or the
+    one below it, so the window [-1, 0] holds the MSE-optimal power-of-two
+    scale ("Bridging the Gap ... Microscaling FP4", 2. Metodologia).  With
+    any non-negative weights the optimum is never above the base (doubling
+    a scale that already covers the block max cannot lower any element's
+    error); how often it falls below E_base - 1 is only reported."""
+    rng = np.random.default_rng(23)
+    u = np.abs(_mx_blocks(kind, 64, rng).astype(np.float64)).reshape(-1, 32)
+    Eb = Q.mx_base_exponent(u.max(-1).astype(np.float32))
+    Es = np.arange(-127, 128)
+    L = study.block_loss64(u, np.broadcast_to(np.ldexp(1.0, Es), (u.shape[0], Es.size)))
+    best = Es[np.argmin(L, axis=-1)]
+    off = best - Eb
+    assert off.min() >= -1 and off.max() <= 0
+    assert np.mean(off == -1) > 0.05    # both window members are used
+    w = np.exp(2 * rng.standard_normal(u.shape))
+    Lw = study.block_loss64(u, np.broadcast_to(np.ldexp(1.0, Es), (u.shape[0], Es.size)), w)
+    off_w = Es[np.argmin(Lw, axis=-1)] - Eb
+    assert off_w.max() <= 0
+    assert np.mean(off_w < -1) < 0.2    # reported: below the window only with skewed weights
+
+
+def test_mxfp4_exhaustive_canonical_fp32_matches_window():
+    """The oracle's own float32 sweep over every exponent picks the same
+    exponent (and codes) as the window [-1, 0] for MSE."""
+    rng = np.random.default_rng(24)
+    x = _mx_blocks("t4", 32, rng)
+    full = Q.quantize_mxfp4(x, window=(-254, 254))
+    win = Q.quantize_mxfp4(x, window=(-1, 0))
+    np.testing.assert_array_equal(full.scales, win.scales)
+    np.testing.assert_array_equal(full.codes, win.codes)
+    np.testing.assert_array_equal(full.block_loss.view(np.uint32), win.block_loss.view(np.uint32))
 
 
 # ----------------------------------------------------------- Hadamard ----
