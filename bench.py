@@ -10,7 +10,8 @@ than the 256 MB Infinity Cache) are rotated so every step reads HBM.
 
 The ``roofline`` object is for the dominant kernel (the sweep), timed alone
 with HIP events on the stream it runs on (a call with a given global scale
-launches exactly that kernel).  Its ``traffic`` is the calibrated
+that adds to the status word, FP4Q_ACCUMULATE_STATUS, launches exactly that
+kernel).  Its ``traffic`` is the calibrated
 FETCH_SIZE + WRITE_SIZE bytes per launch recorded under profiles/ by
 ``python -m fp4_post_quantization_amd.evidence`` for the current kernel
 sources, or null when the kernels changed since.  ``cpu_baseline`` times the CPU oracle on a
@@ -207,7 +208,6 @@ def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
     bufs = _rotating_copies(x)
     out = fq.quantize_nvfp4(bufs[0], imp, window=window, hadamard_n=had)
     ws = fq.workspace(x.device)
-    fq.clear_status(ws)
     step = lambda i: fq.quantize_nvfp4(bufs[i % len(bufs)], imp, window=window, hadamard_n=had, out=out, ws=ws)
     prewarm(step)
     for i in range(warmup):
@@ -227,9 +227,10 @@ def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
     us = sorted(a.elapsed_time(b) * 1e3 for a, b in per_step)
     pct = lambda q: us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))]
     bench_nvfp4_matrix.step_us = {"p10": round(pct(0.1), 2), "p50": round(pct(0.5), 2), "p90": round(pct(0.9), 2)}
-    # out.global_scale now holds S; passing it back launches the sweep kernel only
+    # out.global_scale now holds S; passing it back and adding to the status word (no clearing
+    # kernel) launches the sweep kernel only
     sweep = lambda i: fq.quantize_nvfp4(bufs[i % len(bufs)], imp, window=window, hadamard_n=had,
-                                        global_scale=out.global_scale, out=out, ws=ws)
+                                        global_scale=out.global_scale, out=out, ws=ws, accumulate_status=True)
     for i in range(warmup):
         sweep(i)
     ms_sweep = _events_time(sweep, steps)

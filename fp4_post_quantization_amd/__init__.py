@@ -51,7 +51,8 @@ def workspace(device=None):
     """The workspace used when none is passed: one per device and stream,
     taken for the device's current stream (calls on one stream run in
     order, so they may share it; calls on different streams get different
-    ones).  The status word in it is sticky per workspace."""
+    ones).  Its status word holds the data errors of the last call on it
+    (every call writes it on its stream)."""
     device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     index = device.index if device.index is not None else torch.cuda.current_device()
     key = (index, _stream(device))
@@ -63,8 +64,8 @@ def workspace(device=None):
 
 
 def read_status(ws):
-    """Device status word (FP4Q_DATA_* bits, sticky until cleared) after the
-    stream has finished."""
+    """Device status word (FP4Q_DATA_* bits of the last call on this
+    workspace) after the stream has finished."""
     return int(ws[:4].view(torch.int32).item())
 
 
@@ -76,7 +77,6 @@ def _check_data(ws):
     torch.cuda.current_stream(ws.device).synchronize()
     st = read_status(ws)
     if st:
-        clear_status(ws)
         names = []
         if st & L.DATA_NONFINITE_INPUT:
             names.append("non-finite input")
@@ -200,13 +200,15 @@ def _check_result(out, rows, cols, block, device):
 
 
 def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=None, *,
-                   out=None, with_loss=True, with_offsets=True, ws=None, check=False):
+                   out=None, with_loss=True, with_offsets=True, ws=None, check=False, accumulate_status=False):
     """NVFP4 ScaleSweep quantization of a 2-D float32/bfloat16 device tensor.
 
     importance: per-column weights -> WMSE (default window (-8, 7)); None ->
     MSE (default window (-3, 7)).  global_scale: a given S (float or [1]
     tensor; passing ``out.global_scale`` itself copies nothing) instead of
     max|x|/1536.  out: a preallocated NVFP4Result to write into.  check: synchronize and raise on data errors.
+    accumulate_status: add this call's data errors to the workspace's status
+    word instead of replacing it (FP4Q_ACCUMULATE_STATUS; no clearing kernel).
     """
     lib = L.load()
     x, ld = _matrix(x)
@@ -232,6 +234,8 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
         if not same:
             out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
         flags |= L.GIVEN_SCALE
+    if accumulate_status:
+        flags |= L.ACCUMULATE_STATUS
     ws = _ws(ws, dev)
     L.check(lib.fp4q_quantize_nvfp4(
         x.data_ptr(), _dtype_code(x), rows, cols, ld, _ptr(imp), 16, loss, int(window[0]), int(window[1]),

@@ -13,6 +13,7 @@ F32, BF16 = 0, 1
 MSE, WMSE = 0, 1
 NVFP4, MXFP4 = 0, 1
 GIVEN_SCALE = 0x1
+ACCUMULATE_STATUS = 0x2
 DATA_NONFINITE_INPUT = 0x1
 DATA_BAD_IMPORTANCE = 0x2
 DATA_BAD_GLOBAL_SCALE = 0x4

@@ -1,15 +1,15 @@
 // fp4q: FP4 microscaling block quantization with block-scale search for
 // gfx950 (MI355X).  Kernels and the C ABI declared in include/fp4q.h.
 //
-// Work decomposition (all kernels): a lane owns 16 contiguous elements of a
-// row ("chunk"); an NVFP4 block is one lane, an MXFP4 block two adjacent
-// lanes, an n-point Hadamard group n/16 adjacent lanes.  Block losses are
-// accumulated inside the lane (plus one DPP exchange for MXFP4), so the
-// candidate sweep needs no LDS traffic for data and no barriers.
+// Work decomposition: a lane owns 16 contiguous elements of a row ("chunk"),
+// an n-point Hadamard group n/16 adjacent lanes; an NVFP4 block is one lane.
+// The MXFP4 sweep gives a lane a whole 32-element block instead.  Block
+// losses are accumulated inside the lane, so the candidate sweep needs no
+// LDS traffic for data and no barriers.
 //
-// The quantize kernels map a wave to a tile of 64 consecutive chunks of a
-// column band times a few rows; the per-column importance of WMSE is loaded
-// into registers once per tile and reused for every row.
+// The quantize kernels map a wave to a tile of 64 consecutive lane units of
+// a column band times a few rows; the per-column importance of WMSE is
+// loaded into registers once per tile and reused for every row.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -57,8 +57,30 @@ __constant__ E4M3Tables kE4M3 = make_e4m3_tables();
 
 // ============================================================ kernels ====
 
-// Global scale of an empty NVFP4 tensor (max over nothing = 0).
-__global__ void zero_scale_kernel(float *global_scale) { *global_scale = 0.0f; }
+// First kernel of a call that runs no global-max pass: writes the call's
+// status word (so no bit of an earlier call survives) with the result of
+// validating what the call reads once: a given NVFP4 global scale (S < 0,
+// Inf or NaN is an error) and the importance vector (< 0, Inf or NaN).
+// Optionally writes the global scale of an empty NVFP4 tensor (0).  One
+// workgroup; the kernels that follow in the call only add bits.
+__global__ __launch_bounds__(kThreads) void status_init_kernel(uint32_t *__restrict__ status,
+                                                                const float *__restrict__ given_scale,
+                                                                const float *__restrict__ imp, int imp_n,
+                                                                float *__restrict__ zero_scale_out) {
+  bool ok = true;
+  if (imp)
+    for (int i = threadIdx.x; i < imp_n; i += kThreads) ok &= (imp[i] >= 0.0f) & (imp[i] <= 3.402823466e38f);
+  const int bad_imp = __syncthreads_or(!ok);
+  if (threadIdx.x == 0) {
+    uint32_t bits = bad_imp ? FP4Q_DATA_BAD_IMPORTANCE : 0u;
+    if (given_scale) {
+      const float S = *given_scale;
+      if (!(S >= 0.0f) || isinf(S)) bits |= FP4Q_DATA_BAD_GLOBAL_SCALE;
+    }
+    if (zero_scale_out) *zero_scale_out = 0.0f;
+    if (status) *status = bits;
+  }
+}
 
 // Where the global-max pass puts its results.
 struct AmaxOut {
@@ -66,30 +88,53 @@ struct AmaxOut {
   uint32_t *status;
   const float *imp;    // importance [imp_n] to validate, or null
   int imp_n;
+  bool clear_status;   // the call's status word starts here (else the call adds to it)
 };
 
-// End of a global-max pass: m is this thread's maximum |bits|; the
-// workgroup's maximum goes to partials[blockIdx.x].  The workgroups also
-// validate the importance vector between them (a strided slice each), so
-// the quantizer that follows need not.
+// Bit 31 of a max-pass partial (the maxima are |x| bit patterns, below
+// 2^31): its workgroup found a bad importance entry.
+constexpr uint32_t kPartialBadImp = 0x80000000u;
+
+// End of a global-max pass, the first kernel of its call: m is this
+// thread's maximum |bits|; the workgroup's maximum goes to
+// partials[blockIdx.x].  The workgroups also validate the importance vector
+// between them (a strided slice each), so the quantizer that follows need
+// not, and report it in bit 31 of their partial.  No workgroup touches the
+// status word except workgroup 0, which clears it for the call (unless the
+// call adds to it); the kernel that reduces the partials sets its bits.
 __device__ void finish_amax(uint32_t m, const AmaxOut &o) {
   __shared__ uint32_t red[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  bool ok = true;
   if (o.imp) {
-    bool ok = true;
     for (int i = blockIdx.x * kThreads + threadIdx.x; i < o.imp_n; i += gridDim.x * kThreads)
       ok &= (o.imp[i] >= 0.0f) & (o.imp[i] <= 3.402823466e38f);
-    if (!ok) atomicOr(o.status, FP4Q_DATA_BAD_IMPORTANCE);
   }
   m = wave_max_u32(m);
   if (lane == 0) red[wave] = m;
-  __syncthreads();
+  const int bad_imp = __syncthreads_or(!ok);
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
-    o.partials[blockIdx.x] = r;
+    o.partials[blockIdx.x] = r | (bad_imp ? kPartialBadImp : 0u);
+    if (blockIdx.x == 0 && o.clear_status) *o.status = 0u;
   }
+}
+
+// Reduction of the max-pass partials by one wave: the maximum |x| bit
+// pattern and the status bits the partials carry.
+__device__ __forceinline__ uint32_t reduce_partials(const uint32_t *partials, int n, int lane, uint32_t &bits) {
+  uint32_t m = 0, f = 0;
+  for (int i = lane; i < n; i += 64) {
+    const uint32_t v = partials[i];
+    m = max(m, v & ~kPartialBadImp);
+    f |= v;
+  }
+  m = wave_max_u32(m);
+  f = wave_max_u32(f & kPartialBadImp);
+  bits = (m >= 0x7F800000u ? FP4Q_DATA_NONFINITE_INPUT : 0u) | (f ? FP4Q_DATA_BAD_IMPORTANCE : 0u);
+  return m;
 }
 
 // Per-workgroup maximum of |x| (after the optional rotation) as a float32
@@ -100,9 +145,9 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const T *__restrict__ x,
                                                          int total, AmaxOut o) {
   const int lane = threadIdx.x & 63;
   uint32_t m = 0;
-  const int stride = gridDim.x * kThreads;
-  for (int g = blockIdx.x * kThreads + threadIdx.x; g < total; g += stride) {
-    const int r = g / cpr, c = g - r * cpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += stride) {
+    const int64_t r = g / cpr, c = g - r * cpr;
     float z[16];
     load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
     if constexpr (HAD != 0) fwht<HAD>(z, lane);
@@ -193,14 +238,14 @@ __global__ __launch_bounds__(kThreads) void amax_chunks_kernel(const T *__restri
 struct SweepArgs {
   const void *x;
   int64_t ld;
-  int rows, cols, cpr;          // cpr = chunks (16 columns) per row
+  int rows, cols, cpr;          // cpr = lane units per row: 16-column chunks (NVFP4), 32-column blocks (MXFP4)
   const float *imp;             // [cols] or null
   int off_lo, off_hi;
   int rows_per_tile, nbands, ntiles;
   const uint32_t *partials;     // amax partials (NVFP4, computed scale)
   int n_partials;
-  bool check_imp;               // validate the importance (no global-max pass did)
   const float *given_scale;     // NVFP4 with FP4Q_GIVEN_SCALE, else null
+  bool check_given;             // validate the given scale and the importance here (no kernel before did)
   uint8_t *codes, *scales;
   float *gscale_out;            // NVFP4 global scale output (computed scale)
   float *loss;
@@ -240,19 +285,21 @@ __device__ __forceinline__ uint32_t cvt8(const float y[8], uint32_t old) {
   return old;
 }
 
-// Loss of one candidate over this lane's 16 elements from their codes:
-// e_i = fp32(us_i - q_i*V), summed in element order with one rounding per
-// term, acc <- fma(t_i, e_i, acc), t_i = e_i (MSE) or fp32(w_i * e_i) (WMSE).
-// us and q carry the sign of x (the conversions are sign-symmetric), so e_i
-// is the error up to its sign and t_i * e_i is unchanged; q*V is exact, so
-// fmaf(-q, V, us) is exactly fp32(us - q*V).
+// Loss of one candidate over 16 elements from their codes: e_i =
+// fp32(us_i - q_i*V), summed in element order with one rounding per term,
+// acc <- fma(t_i, e_i, acc), t_i = e_i (MSE) or fp32(w_i * e_i) (WMSE),
+// starting from acc0 (0 for a block's first 16 elements; a 32-element block
+// continues its first half's sum).  us and q carry the sign of x (the
+// conversions are sign-symmetric), so e_i is the error up to its sign and
+// t_i * e_i is unchanged; q*V is exact, so fmaf(-q, V, us) is exactly
+// fp32(us - q*V).
 template <bool WMSE>
 __device__ __forceinline__ float loss_of_codes(const float us[16], const float w[16], uint32_t pk0,
-                                               uint32_t pk1, float V) {
+                                               uint32_t pk1, float V, float acc0 = 0.0f) {
   float q[16];
   fp4x8_to_f32(pk0, q);
   fp4x8_to_f32(pk1, q + 8);
-  float acc = 0.0f;
+  float acc = acc0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float e = fmaf(-q[i], V, us[i]);
@@ -370,17 +417,16 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   if (wave == 0) {
     float S;
     if (a.given_scale) {
-      S = *a.given_scale;
-      if (blockIdx.x == 0 && lane == 0 && (!(S >= 0.0f) || isinf(S)))
+      S = *a.given_scale;  // validated by the call's first kernel, or just below
+      if (a.check_given && blockIdx.x == 0 && lane == 0 && (!(S >= 0.0f) || isinf(S)))
         atomicOr(a.status, FP4Q_DATA_BAD_GLOBAL_SCALE);
     } else {
-      uint32_t m = 0;
-      for (int i = lane; i < a.n_partials; i += 64) m = max(m, a.partials[i]);
-      m = wave_max_u32(m);
+      uint32_t bits;
+      const uint32_t m = reduce_partials(a.partials, a.n_partials, lane, bits);
       S = as_f(m) / 1536.0f;  // max|x| / (256 * 6), correctly rounded
       if (blockIdx.x == 0 && lane == 0) {
         *a.gscale_out = S;
-        if (m >= 0x7F800000u) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+        if (bits) atomicOr(a.status, bits);
       }
     }
     if (lane == 0) {
@@ -393,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   const float SS = S * S;
   if (!active) return;
   if constexpr (WMSE) {
-    if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+    if (a.check_given && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
   }
 
   const int bpr = a.cpr;  // blocks per row
@@ -446,104 +492,203 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   }
 }
 
-// MXFP4 exponent sweep for one block (this lane's 16 elements and its
-// partner lane's): exponents E and E + 1 pair up, E + 1 converted from the
-// products of E with the halving scale.  Returns E*; Lbest gets its loss
-// and, KEEP, b0 / b1 its codes.
+// Loss of one candidate over a lane's 32-element MXFP4 block from its four
+// code words: one in-order chain over all 32 elements.
+template <bool WMSE>
+__device__ __forceinline__ float loss_of_codes32(const float z[32], const float w[32], const uint32_t k[4], float V) {
+  return loss_of_codes<WMSE>(z + 16, w + 16, k[2], k[3], V, loss_of_codes<WMSE>(z, w, k[0], k[1], V));
+}
+
+// MXFP4 exponent sweep for one block (this lane's 32 elements): exponents E
+// and E + 1 pair up, E + 1 converted from the products of E with the halving
+// scale (8 products at a time, each converted for both members).  Returns
+// E*; Lbest gets its loss and, KEEP, kb its codes.
 template <bool WMSE, bool KEEP>
-__device__ __forceinline__ int mx_sweep(const float z[16], const float w[16], int eb, int lo, int hi, float &Lbest,
-                                        uint32_t &b0, uint32_t &b1) {
+__device__ __forceinline__ int mx_sweep(const float z[32], const float w[32], int eb, int lo, int hi, float &Lbest,
+                                        uint32_t kb[4]) {
   Lbest = __builtin_inff();
   int ebest = max(-127, eb + lo);
-  uint32_t k0 = 0, k1 = 0, h0 = 0, h1 = 0;
+  uint32_t k[4] = {0u, 0u, 0u, 0u}, h[4] = {0u, 0u, 0u, 0u};
   for (int o = lo; o <= hi; o += 2) {
     const int E = eb + o;
     const bool ok = (E >= -127) & (E <= 127);
     const int Ec = min(max(E, -127), 127);
     const float down = pow2f(-Ec);
-    float y[16];
+    const bool pair = o + 1 <= hi;
+    const bool exact_half = E >= -127;  // else the lower member is clamped: convert E + 1 directly
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = z[i] * down;
-    k0 = cvt8<false>(y, k0);
-    k1 = cvt8<false>(y + 8, k1);
-    if (o + 1 <= hi) {
+    for (int j = 0; j < 4; ++j) {
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = z[8 * j + i] * down;
+      k[j] = cvt8<false>(y, k[j]);
+      if (pair & exact_half) h[j] = cvt8<true>(y, h[j]);
+    }
+    if (pair) {
       const int E1 = E + 1;
       const bool ok1 = (E1 >= -127) & (E1 <= 127);
       const int E1c = min(max(E1, -127), 127);
-      if (E >= -127) {
-        h0 = cvt8<true>(y, h0);
-        h1 = cvt8<true>(y + 8, h1);
-      } else {  // lower member clamped: convert the upper one directly
+      if (!exact_half) {
         const float d1 = pow2f(-E1c);
-        float y2[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y2[i] = z[i] * d1;
-        h0 = cvt8<false>(y2, h0);
-        h1 = cvt8<false>(y2 + 8, h1);
+        for (int j = 0; j < 4; ++j) {
+          float y[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = z[8 * j + i] * d1;
+          h[j] = cvt8<false>(y, h[j]);
+        }
       }
-      const float half1 = loss_of_codes<WMSE>(z, w, h0, h1, pow2f(E1c));
-      const bool t1 = consider(half1 + xor_lane<1>(half1), E1, ok1, Lbest, ebest);
+      const bool t1 = consider(loss_of_codes32<WMSE>(z, w, h, pow2f(E1c)), E1, ok1, Lbest, ebest);
       if constexpr (KEEP) {
-        b0 = t1 ? h0 : b0;
-        b1 = t1 ? h1 : b1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kb[j] = t1 ? h[j] : kb[j];
       }
     }
-    const float half0 = loss_of_codes<WMSE>(z, w, k0, k1, pow2f(Ec));
-    const bool t0 = consider(half0 + xor_lane<1>(half0), E, ok, Lbest, ebest);
+    const bool t0 = consider(loss_of_codes32<WMSE>(z, w, k, pow2f(Ec)), E, ok, Lbest, ebest);
     if constexpr (KEEP) {
-      b0 = t0 ? k0 : b0;
-      b1 = t0 ? k1 : b1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kb[j] = t0 ? k[j] : kb[j];
     }
   }
   return ebest;
 }
 
-// MXFP4 exponent sweep: two adjacent lanes per 32-element block.  Exponents
-// E and E + 1 form pairs: fp32(x * 2^-(E+1)) = fp32(x * 2^-E) / 2.
+// Sylvester block Hadamard for lanes that own 32 elements: stages h = 1 ..
+// min(N, 32)/2 inside the lane (two independent 16-groups when N = 16), then
+// h = 32 and 64 with the partner lanes l ^ 1 and l ^ 2 (N = 64, 128), in the
+// oracle's stage order, then the scaling by fp32(1/sqrt(N)).
+template <int N>
+__device__ __forceinline__ void fwht32(float z[32], int lane) {
+  constexpr int HM = N < 32 ? N : 32;
+#pragma unroll
+  for (int h = 1; h < HM; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        float a = z[i], b = z[i + h];
+        z[i] = a + b;
+        z[i + h] = a - b;
+      }
+    }
+  }
+  if constexpr (N >= 64) {
+    const bool hi = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float o = xor_lane<1>(z[i]);
+      z[i] = hi ? (o - z[i]) : (z[i] + o);
+    }
+  }
+  if constexpr (N >= 128) {
+    const bool hi = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float o = xor_lane<2>(z[i]);
+      z[i] = hi ? (o - z[i]) : (z[i] + o);
+    }
+  }
+  const float c = hadamard_scale<N>();
+#pragma unroll
+  for (int i = 0; i < 32; ++i) z[i] = z[i] * c;
+}
+
+// A wave's row segment for the MXFP4 sweep (64 blocks of 32 elements, NP
+// 16-byte pieces per block) is read with fully coalesced loads (lane l takes
+// piece 64k + l in load k), stored in LDS block by block with one piece of
+// padding (so both the stores and the lanes' reads of their own blocks
+// spread over the banks), and read back as each lane's own block.
+template <typename T>
+struct MxStage {
+  static constexpr int NP = 2 * (int)sizeof(T);  // 4 (bf16) or 8 (float32)
+  u32x4 q[64 * (NP + 1)];
+};
+
+// The 32 elements of a block from its NP pieces, widened to float32.
+__device__ __forceinline__ void widen_block(const u32x4 (&p)[4], float z[32]) {  // bf16
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t w = p[k >> 2][k & 3];
+    z[2 * k] = as_f(w << 16);
+    z[2 * k + 1] = as_f(w & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void widen_block(const u32x4 (&p)[8], float z[32]) {  // float32
+#pragma unroll
+  for (int k = 0; k < 32; ++k) z[k] = as_f(p[k >> 2][k & 3]);
+}
+
+// MXFP4 exponent sweep: one lane per 32-element block (a.cpr counts blocks
+// here), so a block's loss is one in-lane chain and its maximum needs no
+// exchange.  Exponents E and E + 1 form pairs: fp32(x * 2^-(E+1)) =
+// fp32(x * 2^-E) / 2.
 template <typename T, bool WMSE, int HAD>
 __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
+  constexpr int NP = MxStage<T>::NP;
+  __shared__ MxStage<T> stage[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wave);
   if (tile >= a.ntiles) return;
   const int band = tile % a.nbands, rg = tile / a.nbands;
-  const int c = band * 64 + lane;
-  const bool active = c < a.cpr;  // cpr is even: both lanes of a block agree
+  const int b = band * 64 + lane;
+  // every lane takes part in the loads and the staging; only lanes on a block store results (a
+  // Hadamard group's lanes agree, since cols is a multiple of HAD)
+  const bool active = b < a.cpr;
+  const int npieces = min(64, a.cpr - band * 64) * NP;  // pieces of this band's segment
   const int r0 = rg * a.rows_per_tile;
   const int r1 = min(a.rows, r0 + a.rows_per_tile);
+  u32x4 *st = stage[wave].q;
 
-  float w[16];
+  float w[32];
   if constexpr (WMSE) {
     if (active) {
-      load_importance(a.imp + (int64_t)c * 16, w);
-      if (a.check_imp && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+      load_importance(a.imp + (int64_t)b * 32, w);
+      load_importance(a.imp + (int64_t)b * 32 + 16, w + 16);
     }
   }
-  if (!active) return;
 
-  const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
-  const int bpr = a.cpr / 2;
-  const bool even = (lane & 1) == 0;
+  const char *seg = static_cast<const char *>(a.x) + (int64_t)band * 64 * 32 * (int64_t)sizeof(T);
+  const int64_t row_bytes = a.ld * (int64_t)sizeof(T);
+  auto load_row = [&](int r, u32x4 (&d)[NP]) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(seg + (int64_t)r * row_bytes);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int g = 64 * k + lane;
+      d[k] = g < npieces ? __builtin_nontemporal_load(src + g) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   const int lo = a.off_lo, hi = a.off_hi;
-  // short windows keep the winner's codes (two selects per candidate) instead of converting again
+  // short windows keep the winner's codes (selects per candidate) instead of converting again
   const bool keep = hi - lo < 8;
-  Raw<T> cur, nxt;
-  load_raw(xc + (int64_t)r0 * a.ld, cur);
+  u32x4 cur[NP], nxt[NP];
+  load_row(r0, cur);
   for (int r = r0; r < r1; ++r) {
-    if (r + 1 < r1) load_raw(xc + (int64_t)(r + 1) * a.ld, nxt);
-    float z[16];
-    widen(cur, z);
-    if constexpr (HAD != 0) fwht<HAD>(z, lane);
+    if (r + 1 < r1) load_row(r + 1, nxt);
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int g = 64 * k + lane;
+      st[(g / NP) * (NP + 1) + g % NP] = cur[k];
+    }
+    // lanes read what other lanes of the same wave wrote: LDS operations of a wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    u32x4 mine[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) mine[j] = st[lane * (NP + 1) + j];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float z[32];
+    widen_block(mine, z);
+    if constexpr (HAD != 0) fwht32<HAD>(z, lane);
 
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(z[i]));
-    amax = fmaxf(amax, xor_lane<1>(amax));
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[i]));
     const int eb = mx_base_exponent(amax);
 
     float Lbest;
-    uint32_t b0 = 0, b1 = 0;  // codes of the best candidate (short windows)
-    const int ebest = keep ? mx_sweep<WMSE, true>(z, w, eb, lo, hi, Lbest, b0, b1)
-                           : mx_sweep<WMSE, false>(z, w, eb, lo, hi, Lbest, b0, b1);
+    uint32_t kb[4] = {0u, 0u, 0u, 0u};  // codes of the best candidate (short windows)
+    const int ebest = keep ? mx_sweep<WMSE, true>(z, w, eb, lo, hi, Lbest, kb)
+                           : mx_sweep<WMSE, false>(z, w, eb, lo, hi, Lbest, kb);
 
     // A non-finite element makes its e, and so every candidate's loss, NaN or infinite (the terms
     // t * e are never negative), so a finite best loss proves the block finite; the elementwise
@@ -552,26 +697,30 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
     if (!lfin) {
       bool finite = true;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
-      if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+      for (int i = 0; i < 32; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
+      if (!finite && active) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
     }
-    uint32_t k0 = b0, k1 = b1;  // a finite best loss was taken, and its codes with it
-    if (!(keep & lfin)) {
+    if (!(keep & lfin)) {  // else the winner's codes were kept
       const float db = pow2f(-ebest);
-      float y[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = z[i] * db;
-      k0 = cvt8<false>(y, 0u);
-      k1 = cvt8<false>(y + 8, 0u);
+      for (int j = 0; j < 4; ++j) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = z[8 * j + i] * db;
+        kb[j] = cvt8<false>(y, 0u);
+      }
     }
-    *reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
-    if (even) {
-      const int64_t bi = (int64_t)r * bpr + (c >> 1);
+    if (active) {
+      uint2 *cp = reinterpret_cast<uint2 *>(a.codes + (int64_t)r * (a.cols / 2) + (int64_t)b * 16);
+      cp[0] = make_uint2(kb[0], kb[1]);
+      cp[1] = make_uint2(kb[2], kb[3]);
+      const int64_t bi = (int64_t)r * a.cpr + b;
       a.scales[bi] = (uint8_t)(ebest + 127);
       if (a.loss) a.loss[bi] = Lbest;
       if (a.offs) a.offs[bi] = (int8_t)(ebest - eb);
     }
-    cur = nxt;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) cur[k] = nxt[k];
   }
 }
 
@@ -605,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
                                                                   float *__restrict__ dq,
                                                                   uint32_t *__restrict__ status) {
   const int lane = threadIdx.x & 63;
-  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  const int64_t g0 = (int64_t)blockIdx.x * kThreads + 64 * wave_index();
   int r, c;
   if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
   float z[16];
@@ -682,18 +831,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __global__ __launch_bounds__(kThreads) void scale_from_partials_kernel(const uint32_t *__restrict__ partials,
                                                                         int n, float *__restrict__ gscale,
                                                                         uint32_t *__restrict__ status) {
-  __shared__ uint32_t red[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) m = max(m, partials[i]);
-  m = wave_max_u32(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < kWaves; ++i) m = max(m, red[i]);
-    m = max(m, red[0]);
-    *gscale = as_f(m) / 1536.0f;
-    if (m >= 0x7F800000u) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+  if (threadIdx.x < 64) {
+    uint32_t bits;
+    const uint32_t m = reduce_partials(partials, n, threadIdx.x, bits);
+    if (threadIdx.x == 0) {
+      *gscale = as_f(m) / 1536.0f;
+      if (bits) atomicOr(status, bits);
+    }
   }
 }
 
@@ -783,7 +927,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     w[k] = live ? wa[k] : 0.0f;
     w[4 + k] = live ? wb[k] : 0.0f;
   }
-  if constexpr (MX) {  // no global-max pass checked the weights
+  {  // MXFP4 and NVFP4 with a given scale run no global-max pass over the weights
     bool finite = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) finite &= fabsf(w[k]) <= 3.402823466e38f;
@@ -823,10 +967,11 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       float y[32];
 #pragma unroll
       for (int e = 0; e < 32; ++e) y[e] = z[e] * down;
-      // the block's loss: its two 16-element halves, each summed in order, then added
-      const float L0 = loss_of_codes<WMSE>(z, wg, cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), up);
-      const float L1 = loss_of_codes<WMSE>(z + 16, wg + 16, cvt8<false>(y + 16, 0u), cvt8<false>(y + 24, 0u), up);
-      float Lm = ok ? L0 + L1 : __builtin_inff();
+      // the block's loss: one in-order chain over its 32 elements
+      const uint32_t kc[4] = {cvt8<false>(y, 0u), cvt8<false>(y + 8, 0u), cvt8<false>(y + 16, 0u),
+                              cvt8<false>(y + 24, 0u)};
+      const float L = loss_of_codes32<WMSE>(z, wg, kc, up);
+      float Lm = ok ? L : __builtin_inff();
       int em = ok ? E : 0x7FFFFFFF;
       row_argmin16(Lm, em);
       const int es = em == 0x7FFFFFFF ? max(-127, eb + lo) : em;
@@ -1005,7 +1150,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__rest
                                                             const float *__restrict__ gscale, int cpr,
                                                             int cols, int total, float *__restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  const int64_t g0 = (int64_t)blockIdx.x * kThreads + 64 * wave_index();
   int r, c;
   if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
   const uint2 pk = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)c * 8);
@@ -1032,7 +1177,7 @@ template <typename T, int HAD>
 __global__ __launch_bounds__(kThreads) void hadamard_kernel(const T *__restrict__ x, int64_t ld, int cpr,
                                                              int cols, int total, float *__restrict__ out) {
   const int lane = threadIdx.x & 63;
-  const int64_t g0 = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kThreads + (threadIdx.x & ~63u)));
+  const int64_t g0 = (int64_t)blockIdx.x * kThreads + 64 * wave_index();
   int r, c;
   // whole groups end together: total is a multiple of HAD/16
   if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
@@ -1105,9 +1250,9 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
   }
 }
 
-static AmaxOut amax_out(void *workspace, const float *imp, int imp_n) {
+static AmaxOut amax_out(void *workspace, const float *imp, int imp_n, bool clear_status = true) {
   char *b = (char *)workspace;
-  return AmaxOut{(uint32_t *)(b + kWsPartials), (uint32_t *)(b + kWsStatus), imp, imp_n};
+  return AmaxOut{(uint32_t *)(b + kWsPartials), (uint32_t *)(b + kWsStatus), imp, imp_n, clear_status};
 }
 
 // Global-max pass over x (after the optional rotation): per-workgroup
@@ -1202,7 +1347,7 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
   if (block != 16) return FP4Q_ERR_SHAPE;
   if (off_lo > 0 || off_hi < 0 || off_lo < -126 || off_hi > 126) return FP4Q_ERR_ARG;
-  if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
+  if (flags & ~(FP4Q_GIVEN_SCALE | FP4Q_ACCUMULATE_STATUS)) return FP4Q_ERR_ARG;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, hadamard_n);
   if (st != FP4Q_OK) return st;
   const bool wmse = loss == FP4Q_WMSE;
@@ -1212,17 +1357,26 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   const bool given = flags & FP4Q_GIVEN_SCALE;
+  const bool accumulate = flags & FP4Q_ACCUMULATE_STATUS;
 
-  if (rows == 0 || cols == 0) {
-    if (!given) hipLaunchKernelGGL(zero_scale_kernel, dim3(1), dim3(1), 0, s, global_scale);
+  // the call's first kernel clears the status word: the global-max pass, or with a given scale (and
+  // for an empty tensor) the kernel that validates the scale and the importance.  A call that adds
+  // to the word launches no such kernel: its sweep validates a given scale and the importance itself.
+  if ((given || empty) && !accumulate)
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, given ? global_scale : nullptr,
+                       (wmse && !empty) ? importance : nullptr, (wmse && !empty) ? (int)cols : 0,
+                       given ? nullptr : global_scale);
+  if (empty) {
+    if (accumulate && !given) hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, nullptr, nullptr,
+                                                 nullptr, 0, global_scale);
     return last_hip_status();
   }
 
   const int cpr = (int)(cols / 16);
-  const int total = (int)(rows * cpr);
   const int n_partials =
-      given ? 0 : launch_amax(x, dtype, rows, cols, ld, hadamard_n, amax_out(workspace, wmse ? importance : nullptr,
-                                                                                      (int)cols), s);
+      given ? 0
+            : launch_amax(x, dtype, rows, cols, ld, hadamard_n,
+                          amax_out(workspace, wmse ? importance : nullptr, (int)cols, !accumulate), s);
 
   SweepArgs a;
   a.x = x;
@@ -1238,8 +1392,8 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
   a.partials = (const uint32_t *)((const char *)workspace + kWsPartials);
   a.n_partials = n_partials;
-  a.check_imp = given;  // else the global-max pass validates the importance
   a.given_scale = given ? global_scale : nullptr;
+  a.check_given = given && accumulate;
   a.codes = codes;
   a.scales = scales;
   a.gscale_out = global_scale;
@@ -1270,7 +1424,8 @@ extern "C" fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dty
   if (st != FP4Q_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (empty) {
-    hipLaunchKernelGGL(zero_scale_kernel, dim3(1), dim3(1), 0, s, global_scale);
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, (uint32_t *)((char *)workspace + kWsStatus),
+                       nullptr, nullptr, 0, global_scale);
     return last_hip_status();
   }
   // the max pass and the reduction of its partials, as at the start of fp4q_quantize_nvfp4
@@ -1302,25 +1457,28 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  if (rows == 0 || cols == 0) return FP4Q_OK;
+  // first kernel of the call: clears the status word, validates the importance
+  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, nullptr,
+                     (wmse && !empty) ? importance : nullptr, (wmse && !empty) ? (int)cols : 0, nullptr);
+  if (empty) return last_hip_status();
 
-  const int cpr = (int)(cols / 16);
+  const int bpr = (int)(cols / 32);  // one lane per 32-element block
   SweepArgs a;
   a.x = x;
   a.ld = ld;
   a.rows = (int)rows;
   a.cols = (int)cols;
-  a.cpr = cpr;
+  a.cpr = bpr;
   a.imp = wmse ? importance : nullptr;
   a.off_lo = off_lo;
   a.off_hi = off_hi;
-  a.nbands = ceil_div(cpr, 64);
+  a.nbands = ceil_div(bpr, 64);
   a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands, kMxTileTarget);
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
   a.partials = nullptr;
   a.n_partials = 0;
-  a.check_imp = true;
   a.given_scale = nullptr;
+  a.check_given = false;
   a.codes = codes;
   a.scales = scales;
   a.gscale_out = nullptr;
@@ -1356,13 +1514,17 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
     return FP4Q_ERR_ARG;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, 0);
   if (st != FP4Q_OK) return st;
-  if (empty) return FP4Q_OK;
-  if (!aligned(codes, 8) || (dequant_out && !aligned(dequant_out, 16)) || (coeffs && !aligned(coeffs, 2)))
+  if (!empty &&
+      (!aligned(codes, 8) || (dequant_out && !aligned(dequant_out, 16)) || (coeffs && !aligned(coeffs, 2))))
     return FP4Q_ERR_ALIGN;
-  const int cpr = (int)(cols / 16);
-  const int total = (int)(rows * cpr);
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  // first kernel of the call: clears the status word, validates an NVFP4 global scale
+  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status,
+                     (format == FP4Q_NVFP4 && !empty) ? global_scale : nullptr, nullptr, 0, nullptr);
+  if (empty) return last_hip_status();
+  const int cpr = (int)(cols / 16);
+  const int total = (int)(rows * cpr);
   const int grid = ceil_div(total, kThreads);
   with_dtype(dtype, [&](auto tp) {
     using T = std::remove_const_t<std::remove_pointer_t<decltype(tp)>>;
@@ -1402,13 +1564,18 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
   if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
-  if (empty) return FP4Q_OK;
-  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
-      (importance && !aligned(importance, 4)))
+  if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
+                 (importance && !aligned(importance, 4))))
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   const bool given = flags & FP4Q_GIVEN_SCALE;
+  // the call's first kernel clears the status word: the global-max pass, or with a given scale (and
+  // for an empty matrix) the kernel that validates the scale
+  if (given || empty)
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, given ? global_scale : nullptr,
+                       nullptr, 0, given ? nullptr : global_scale);
+  if (empty) return last_hip_status();
   if (!given) {
     uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
     const int n_partials = launch_amax(w, FP4Q_F32, rows, cols, ld, 0, amax_out(workspace, nullptr, 0), s);
@@ -1431,12 +1598,14 @@ extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, i
   if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
-  if (empty) return FP4Q_OK;
-  if (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
-      (importance && !aligned(importance, 4)))
+  if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
+                 (importance && !aligned(importance, 4))))
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  // first kernel of the call: clears the status word
+  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, nullptr, nullptr, 0, nullptr);
+  if (empty) return last_hip_status();
   gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, hinv_chol, importance, nullptr, off_lo, off_hi, codes, scales,
                            status, s);
   return last_hip_status();

@@ -42,11 +42,12 @@
  *     enqueued.  Errors in the data (non-finite x, negative or non-finite
  *     importance, an invalid given global scale) are found on the device:
  *     they set bits of the status word at byte 0 of the workspace
- *     (FP4Q_DATA_* below) and leave that call's outputs unspecified.  The
- *     word is sticky: kernels only ever set bits, never clear them, so the
- *     caller zero-fills the workspace once before first use, reads the word
- *     after the stream has finished, and writes 0 to it to clear an error.
- *     Calls that overlap on one workspace race on its scratch part.
+ *     (FP4Q_DATA_* below) and leave that call's outputs unspecified.  Every
+ *     call that takes a workspace writes that word on its stream before any
+ *     of its kernels can set a bit, so after the stream has finished the
+ *     word holds exactly the data errors of the last call on that workspace
+ *     (0: none).  A fresh, uninitialised workspace is fine.  Calls that
+ *     overlap on one workspace (different streams) race on it.
  */
 #ifndef FP4Q_H
 #define FP4Q_H
@@ -74,6 +75,11 @@ typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
 
 /* flags of fp4q_quantize_nvfp4 */
 #define FP4Q_GIVEN_SCALE 0x1u /* read S from *global_scale instead of computing it */
+/* Add this call's data errors to the status word instead of replacing it:
+ * no clearing kernel runs first (a call with a given scale then launches its
+ * sweep kernel alone).  For chains of calls on one stream that check the
+ * word once at the end; the caller zeroes the word before the chain. */
+#define FP4Q_ACCUMULATE_STATUS 0x2u
 
 /* bits of the device status word (uint32 at byte 0 of the workspace) */
 #define FP4Q_DATA_NONFINITE_INPUT 0x1u  /* x (after rotation) holds Inf or NaN */
@@ -89,8 +95,8 @@ int fp4q_version(void);
 const char *fp4q_status_string(fp4q_status_t status);
 
 /* Bytes of device workspace every quantize call needs (a constant).  Bytes
- * 0..3 hold the sticky status word (zero it before first use); the rest is
- * scratch the library overwrites. */
+ * 0..3 hold the status word of the last call (written by every call on its
+ * stream); the rest is scratch the library overwrites. */
 size_t fp4q_workspace_bytes(void);
 
 /*
@@ -109,7 +115,7 @@ size_t fp4q_workspace_bytes(void);
  *               MSE; -8, 7 for WMSE; 0, 0 is plain AbsMax round-to-nearest).
  *   hadamard_n  0 (none) or 16, 32, 64, 128: rotate each row's n-column
  *               groups by the orthonormal Sylvester Hadamard matrix first.
- *   flags       0 or FP4Q_GIVEN_SCALE.
+ *   flags       0, FP4Q_GIVEN_SCALE and/or FP4Q_ACCUMULATE_STATUS.
  *   codes       [rows * cols / 2] packed E2M1 codes (out).
  *   scales      [rows * cols / 16] E4M3 block-scale bit patterns (out).
  *   global_scale [1] float32 S (out; in with FP4Q_GIVEN_SCALE).
@@ -179,9 +185,9 @@ fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t
  * Computation: u = |x|; per block E_base = least E with 6 * 2^E >= max u,
  * clamped to [-127, 127]; for E = max(-127, E_base+off_lo) ..
  * min(127, E_base+off_hi): q = E2M1 nearest to fp32(u * 2^-E),
- * e = fp32(u - q*2^E); the loss is fp32(L_a + L_b), L_a and L_b the fused
- * in-order sums above over the block's two 16-element halves; the smallest
- * E with the least loss is chosen.
+ * e = fp32(u - q*2^E); the loss is the fused in-order sum above over all
+ * 32 elements of the block (one rounding per term); the smallest E with the
+ * least loss is chosen.
  */
 fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
                                   int64_t ld, const float *importance, int block, fp4q_loss_t loss,
@@ -269,8 +275,8 @@ fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
  * optimised per format, MXFP4 as well as NVFP4).  The same procedure as
  * fp4q_gptq_nvfp4 with 32-column groups: when column c opens a group, each
  * row's E8M0 exponent is the exponent sweep's choice (fp4q_quantize_mxfp4's
- * search: base exponent, window of exponent offsets, the block loss as two
- * 16-element halves) on the group's current values; column c is rounded at
+ * search: base exponent, window of exponent offsets, the block loss as one
+ * in-order sum over its 32 elements) on the group's current values; column c is rounded at
  * 2^E, x_hat = q * 2^E exactly, and the scaled errors and updates are those
  * of fp4q_gptq_nvfp4.  There is no global scale.
  *

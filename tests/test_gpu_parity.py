@@ -446,7 +446,21 @@ def test_nvfp4_rotated(n):
     _check_nvfp4(res, ref)
 
 
-@pytest.mark.parametrize("n", [32, 128])
+@pytest.mark.parametrize("rows,cols", [(5, 2080), (130, 64)])
+@pytest.mark.parametrize("window", [(-8, 8), (-16, 16)])
+def test_mxfp4_fp32_wide_windows(rows, cols, window):
+    """float32 input and windows of 17 and 33 exponents (the winner's codes
+    are converted again rather than kept), MSE and WMSE."""
+    fq = _fp4()
+    x = W.random_matrix(rows, cols, seed=rows * cols, dist="t4", scale=0.3, dtype=torch.float32)
+    r = fq.quantize_mxfp4(x.to(DEV), window=window, check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(x.numpy(), window=window))
+    imp = W.random_importance(cols, seed=cols + 3)
+    r = fq.quantize_mxfp4(x.to(DEV), imp.to(DEV), window=window, check=True)
+    _check_mxfp4(r, Q.quantize_mxfp4(x.numpy(), imp.numpy(), window=window))
+
+
+@pytest.mark.parametrize("n", [16, 32, 64, 128])
 def test_mxfp4_rotated(n):
     fq = _fp4()
     x = W.random_matrix(65, 4096, seed=80 + n, dist="laplace", scale=1.0, dtype=torch.bfloat16)
@@ -773,6 +787,80 @@ def test_gptq_data_errors_set_status():
         fq.gptq_mxfp4(w.to(DEV), U, bad_imp.to(DEV), check=True)
     with pytest.raises(fq.FP4QError, match="importance"):
         fq.gptq_nvfp4(w.to(DEV), U, bad_imp.to(DEV), check=True)
+
+
+def test_gptq_given_scale_data_errors_set_status():
+    """With a given global scale no max pass reads the weights: the batch
+    kernel flags non-finite weights, the call's first kernel an invalid S."""
+    fq = _fp4()
+    w, H, U, imp = _gptq_inputs(8, 128, seed=131)
+    S = float(np.abs(w.numpy()).max()) / 1536
+    bad_w = w.clone()
+    bad_w[5, 100] = float("inf")
+    with pytest.raises(fq.FP4QError, match="non-finite"):
+        fq.gptq_nvfp4(bad_w.to(DEV), U, global_scale=S, check=True)
+    for bad_s in (float("nan"), -1.0, float("inf")):
+        with pytest.raises(fq.FP4QError, match="global scale"):
+            fq.gptq_nvfp4(w.to(DEV), U, global_scale=bad_s, check=True)
+    ok = fq.gptq_nvfp4(w.to(DEV), U, global_scale=S, check=True)
+    ref = fq.gptq_nvfp4(w.to(DEV), U, check=True)
+    if np.float32(S) == np.float32(_np(ref.global_scale)[0]):
+        assert torch.equal(ok.codes, ref.codes) and torch.equal(ok.scales, ref.scales)
+
+
+def test_status_word_belongs_to_the_last_call():
+    """Every call writes the workspace's status word on its stream before
+    any kernel can set a bit: a workspace full of garbage reports no error
+    for clean data, and an error does not outlive its call."""
+    fq = _fp4()
+    x = W.random_matrix(16, 256, seed=57).to(DEV)
+    imp = W.random_importance(256, seed=58).to(DEV)
+    bad = x.clone()
+    bad[2, 5] = float("nan")
+    U = torch.eye(128)
+    calls = [
+        lambda ws, t: fq.quantize_nvfp4(t, imp, ws=ws),
+        lambda ws, t: fq.quantize_nvfp4(t, imp, global_scale=0.01, ws=ws),
+        lambda ws, t: fq.quantize_mxfp4(t, imp, ws=ws),
+        lambda ws, t: fq.gptq_nvfp4(t[:, :128], U, ws=ws),
+        lambda ws, t: fq.gptq_mxfp4(t[:, :128], U, ws=ws),
+        lambda ws, t: fq.global_scale_nvfp4(t, ws=ws),
+    ]
+    for k, call in enumerate(calls):
+        ws = torch.full((fq.workspace(DEV).numel(),), 0xFF, dtype=torch.uint8, device=DEV)
+        call(ws, x)
+        torch.cuda.synchronize()
+        assert fq.read_status(ws) == 0, k
+        call(ws, bad)
+        torch.cuda.synchronize()
+        assert fq.read_status(ws) & 0x1, k
+        call(ws, x)
+        torch.cuda.synchronize()
+        assert fq.read_status(ws) == 0, k
+    # FP4Q_ACCUMULATE_STATUS: errors add up over a chain of calls, and a given scale or the
+    # importance are still validated (by the sweep itself)
+    ws = torch.zeros(fq.workspace(DEV).numel(), dtype=torch.uint8, device=DEV)
+    S = fq.quantize_nvfp4(x, imp, ws=ws).global_scale
+    fq.quantize_nvfp4(bad, imp, ws=ws, accumulate_status=True)
+    fq.quantize_nvfp4(x, imp, global_scale=S, ws=ws, accumulate_status=True)
+    torch.cuda.synchronize()
+    assert fq.read_status(ws) == 0x1
+    bad_imp = imp.clone()
+    bad_imp[7] = -2.0
+    fq.quantize_nvfp4(x, bad_imp, global_scale=S, ws=ws, accumulate_status=True)
+    fq.quantize_nvfp4(x, imp, global_scale=float("nan"), ws=ws, accumulate_status=True)
+    torch.cuda.synchronize()
+    assert fq.read_status(ws) == 0x7
+    a = fq.quantize_nvfp4(x, imp, global_scale=S, ws=ws, accumulate_status=True)
+    b = fq.quantize_nvfp4(x, imp, global_scale=S)
+    for f in ("codes", "scales", "block_loss", "offsets"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # empty tensors clear it too
+    ws = torch.full((fq.workspace(DEV).numel(),), 0xFF, dtype=torch.uint8, device=DEV)
+    fq.quantize_nvfp4(x[:0], ws=ws)
+    fq.quantize_mxfp4(x[:0], ws=ws)
+    torch.cuda.synchronize()
+    assert fq.read_status(ws) == 0
 
 
 def test_gptq_bad_hessian_sets_status():
