@@ -22,7 +22,7 @@ from . import _lib as L
 from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
-    "quantize_nvfp4", "global_scale_nvfp4", "quantize_mxfp4", "quantize_relaxed",
+    "quantize_nvfp4", "quantize_nvfp4_noalloc", "global_scale_nvfp4", "quantize_mxfp4", "quantize_relaxed",
     "gptq_nvfp4", "gptq_mxfp4", "dequantize",
     "block_hadamard", "gemm_mxfp4", "gemm_nvfp4",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
@@ -243,6 +243,36 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
         _ptr(out.block_loss), _ptr(out.offsets), ws.data_ptr(), ws.numel(), _stream(dev)))
     if check:
         _check_data(ws)
+    return out
+
+
+def quantize_nvfp4_noalloc(x, importance=None, window=None, hadamard_n=0, *, out, status,
+                           given_scale=False, accumulate_status=False):
+    """quantize_nvfp4 through fp4q_quantize_nvfp4_noalloc: no workspace and
+    no device allocation in the call.  Every tensor is the caller's and is
+    used in place: x a dense row-major float32/bfloat16 matrix, importance a
+    dense float32 [cols] vector (WMSE) or None, out a preallocated
+    NVFP4Result, status a [1] int32 device tensor for the data-error bits.
+    given_scale: out.global_scale already holds S (FP4Q_GIVEN_SCALE)."""
+    lib = L.load()
+    if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D device tensor")
+    rows, cols = x.shape
+    dev = x.device
+    if importance is not None:
+        _given(importance, (cols,), torch.float32, dev, "importance")
+    loss = L.WMSE if importance is not None else L.MSE
+    if window is None:
+        window = (-8, 7) if importance is not None else (-3, 7)
+    _check_result(out, rows, cols, 16, dev)
+    if out.global_scale is None:
+        raise ValueError("out.global_scale is required")
+    _given(status, (1,), torch.int32, dev, "status")
+    flags = (L.GIVEN_SCALE if given_scale else 0) | (L.ACCUMULATE_STATUS if accumulate_status else 0)
+    L.check(lib.fp4q_quantize_nvfp4_noalloc(
+        x.data_ptr(), _dtype_code(x), rows, cols, cols, _ptr(importance), 16, loss, int(window[0]),
+        int(window[1]), int(hadamard_n), flags, out.codes.data_ptr(), out.scales.data_ptr(),
+        out.global_scale.data_ptr(), _ptr(out.block_loss), _ptr(out.offsets), status.data_ptr(), _stream(dev)))
     return out
 
 

@@ -25,6 +25,8 @@ EXPORTS = (
     "fp4q_status_string",
     "fp4q_workspace_bytes",
     "fp4q_quantize_nvfp4",
+    "fp4q_quantize_nvfp4_noalloc",
+    "fp4q_noalloc_scratch_bytes",
     "fp4q_global_scale_nvfp4",
     "fp4q_quantize_mxfp4",
     "fp4q_quantize_relaxed",
@@ -51,6 +53,9 @@ _SIGNATURES = {
     "fp4q_global_scale_nvfp4": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "fp4q_quantize_nvfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I, _U32,
                                  _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fp4q_quantize_nvfp4_noalloc": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I, _U32,
+                                         _P, _P, _P, _P, _P, _P, _P]),
+    "fp4q_noalloc_scratch_bytes": (_SZ, []),
     "fp4q_quantize_mxfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I,
                                  _P, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_quantize_relaxed": (_I, [_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),

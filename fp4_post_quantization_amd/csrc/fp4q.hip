@@ -17,6 +17,8 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1334,17 +1336,19 @@ static fp4q_status_t last_hip_status() {
   return hipGetLastError() == hipSuccess ? FP4Q_OK : FP4Q_ERR_HIP;
 }
 
-extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
-                                             int64_t ld, const float *importance, int block,
-                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
-                                             uint32_t flags, uint8_t *codes, uint8_t *scales,
-                                             float *global_scale, float *block_loss, int8_t *offsets,
-                                             void *workspace, size_t workspace_bytes, void *stream) {
+// fp4q_quantize_nvfp4 on explicit scratch: the call's status word and
+// kAmaxGroups words for the max-pass partials (ws_ok: the caller's scratch
+// passed its check, reported in the argument-check order of the C ABI).
+static fp4q_status_t quantize_nvfp4_on(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                       const float *importance, int block, fp4q_loss_t loss, int off_lo, int off_hi,
+                                       int hadamard_n, uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                       float *global_scale, float *block_loss, int8_t *offsets, bool ws_ok,
+                                       uint32_t *status, uint32_t *partials, hipStream_t s) {
   const bool empty = rows == 0 || cols == 0;
   if (!global_scale || (!empty && (!x || !codes || !scales))) return FP4Q_ERR_NULL;
   if (loss != FP4Q_MSE && loss != FP4Q_WMSE) return FP4Q_ERR_ARG;
   if (loss == FP4Q_WMSE && !importance && !empty) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!ws_ok) return FP4Q_ERR_WORKSPACE;
   if (block != 16) return FP4Q_ERR_SHAPE;
   if (off_lo > 0 || off_hi < 0 || off_lo < -126 || off_hi > 126) return FP4Q_ERR_ARG;
   if (flags & ~(FP4Q_GIVEN_SCALE | FP4Q_ACCUMULATE_STATUS)) return FP4Q_ERR_ARG;
@@ -1354,8 +1358,6 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   if (!empty && wmse && !aligned(importance, 16)) return FP4Q_ERR_ALIGN;
   if (!empty && (!aligned(codes, 8) || (block_loss && !aligned(block_loss, 4)))) return FP4Q_ERR_ALIGN;
 
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   const bool given = flags & FP4Q_GIVEN_SCALE;
   const bool accumulate = flags & FP4Q_ACCUMULATE_STATUS;
 
@@ -1376,7 +1378,7 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   const int n_partials =
       given ? 0
             : launch_amax(x, dtype, rows, cols, ld, hadamard_n,
-                          amax_out(workspace, wmse ? importance : nullptr, (int)cols, !accumulate), s);
+                          AmaxOut{partials, status, wmse ? importance : nullptr, (int)cols, !accumulate}, s);
 
   SweepArgs a;
   a.x = x;
@@ -1390,7 +1392,7 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   a.nbands = ceil_div(cpr, 64);
   a.rows_per_tile = pick_rows_per_tile((int)rows, a.nbands, kNvTileTarget);
   a.ntiles = a.nbands * ceil_div(rows, a.rows_per_tile);
-  a.partials = (const uint32_t *)((const char *)workspace + kWsPartials);
+  a.partials = partials;
   a.n_partials = n_partials;
   a.given_scale = given ? global_scale : nullptr;
   a.check_given = given && accumulate;
@@ -1412,6 +1414,72 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
     });
   });
   return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                             int64_t ld, const float *importance, int block,
+                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
+                                             uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                             float *global_scale, float *block_loss, int8_t *offsets,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+  char *ws = (char *)workspace;
+  return quantize_nvfp4_on(x, dtype, rows, cols, ld, importance, block, loss, off_lo, off_hi, hadamard_n, flags,
+                           codes, scales, global_scale, block_loss, offsets,
+                           workspace && workspace_bytes >= kWorkspaceBytes, (uint32_t *)(ws + kWsStatus),
+                           (uint32_t *)(ws + kWsPartials), (hipStream_t)stream);
+}
+
+// ------------------------------------------------ no-allocation variant ----
+// Scratch of fp4q_quantize_nvfp4_noalloc: the global-max pass's
+// per-workgroup partials (at most kAmaxGroups, whatever the tensor's size),
+// in a device array of this library rather than a caller workspace.  Each
+// GPU holds its own copy until the process ends; host code reaches a
+// device's copy only through the address hipGetSymbolAddress gives on that
+// device (the array's name is a host-side stand-in).
+static __device__ __align__(256) uint32_t scratch[kAmaxGroups];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<uint32_t *> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// This device's address of `scratch`, looked up once per device (with that
+// device current, on its first call).
+static fp4q_status_t scratch_of_current_device(uint32_t **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4Q_ERR_HIP;
+  uint32_t *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void *addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return FP4Q_ERR_HIP;
+      p = (uint32_t *)addr;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP4Q_OK;
+}
+
+extern "C" size_t fp4q_noalloc_scratch_bytes(void) { return sizeof(scratch); }
+
+extern "C" fp4q_status_t fp4q_quantize_nvfp4_noalloc(const void *x, fp4q_dtype_t dtype, int64_t rows,
+                                                     int64_t cols, int64_t ld, const float *importance, int block,
+                                                     fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
+                                                     uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                                     float *global_scale, float *block_loss, int8_t *offsets,
+                                                     uint32_t *status, void *stream) {
+  if (!status) return FP4Q_ERR_NULL;
+  uint32_t *partials = nullptr;
+  const fp4q_status_t st = scratch_of_current_device(&partials);
+  if (st != FP4Q_OK) return st;
+  // the max pass writes at most kAmaxGroups partials, the size of the array, for any input: no input
+  // size exceeds the scratch
+  static_assert(sizeof(scratch) >= kAmaxGroups * sizeof(uint32_t), "scratch holds every max-pass partial");
+  return quantize_nvfp4_on(x, dtype, rows, cols, ld, importance, block, loss, off_lo, off_hi, hadamard_n, flags,
+                           codes, scales, global_scale, block_loss, offsets, true, status, partials,
+                           (hipStream_t)stream);
 }
 
 extern "C" fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,

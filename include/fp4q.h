@@ -146,6 +146,37 @@ fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t row
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * fp4q_quantize_nvfp4 without a workspace, for callers that cannot allocate
+ * device memory for one: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  It allocates nothing and
+ * calls no allocating routine.
+ *
+ * Same arguments, computation, errors and results as fp4q_quantize_nvfp4,
+ * except that the workspace is replaced by:
+ *   status  [1] uint32 device word (out): the call's data errors
+ *           (FP4Q_DATA_* bits), written on the stream like the workspace's
+ *           status word (with FP4Q_ACCUMULATE_STATUS the call adds to it).
+ * The global-max pass keeps its per-workgroup partials in a static device
+ * array of the library instead, fp4q_noalloc_scratch_bytes() = 1 KiB per
+ * GPU, held until the process ends.  That is the most the pass ever writes
+ * (at most 256 partials whatever the tensor's size), so no input is too
+ * large for it.  The array's address on the current device is looked up
+ * once per device, on its first call (FP4Q_ERR_HIP if that fails); the
+ * current device must be the stream's.  All calls on one GPU share the
+ * array: calls that overlap on a GPU (different streams, or threads) race
+ * on it and must be serialized by the caller.  Calls in order on one
+ * stream are fine: each call writes every partial it reads.
+ */
+fp4q_status_t fp4q_quantize_nvfp4_noalloc(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                          int64_t ld, const float *importance, int block, fp4q_loss_t loss,
+                                          int off_lo, int off_hi, int hadamard_n, uint32_t flags,
+                                          uint8_t *codes, uint8_t *scales, float *global_scale,
+                                          float *block_loss, int8_t *offsets, uint32_t *status, void *stream);
+
+/* Bytes of the static device scratch of fp4q_quantize_nvfp4_noalloc (per GPU). */
+size_t fp4q_noalloc_scratch_bytes(void);
+
+/*
  * The NVFP4 global scale alone: S = fp32(max|x| / 1536) over x, after the
  * optional rotation ([SS] 2., Escala Global: the per-tensor FP32 scale puts
  * the largest value at the top of the E2M1 x E4M3 range, 6 * 256).  This is
