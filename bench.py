@@ -23,7 +23,9 @@ untimed steps run for 0.3 s so the GPU has left its idle clocks.
 Other workloads (for the design notes, not the headline line) are selected
 with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
-c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N),
+c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N; outputs
+reduced to per-matrix checksums on the device, --state FILE records them per
+layer and --start-layer K resumes from that file),
 c5gate (one 70B-shaped gate projection, 16-point Hadamard + WMSE, repeated),
 focus (FOCUS forward quantizer on the c2 weight, sub-blocks of 8),
 study (AbsMax / ScaleSweep / exhaustive windows and MXFP4 code usage),
@@ -36,6 +38,7 @@ oracle (the CPU oracle alone, one process, on a 256-row sample of each workload)
 """
 
 import argparse
+import hashlib
 import json
 
 import numpy as np
@@ -94,14 +97,63 @@ def _rotating_copies(x, min_bytes=300 * 2**20, min_count=10):
 
 _POOL = {}
 
+# Worker processes of the CPU baseline: every core the process may run on, up
+# to the 16 that a one-GPU machine shares with its GPU (its CPU share; more
+# processes would only queue behind each other there).
+POOL_CAP = 16
 
-def _oracle_rows(bounds):
+
+def _pool_cores():
+    avail = len(os.sched_getaffinity(0))
+    return min(POOL_CAP, avail), avail
+
+
+def _oracle_shard(job):
     """One worker of the all-cores CPU baseline: the oracle on rows [r0, r1)
-    of the shared matrix with the whole matrix's global scale."""
+    of the shared matrix ``name`` with the whole matrix's global scale."""
     from oracle import quant as Q
-    r0, r1 = bounds
-    Q.quantize_nvfp4(_POOL["x"][r0:r1], _POOL["imp"], window=_POOL["window"], global_scale=_POOL["S"])
+    name, r0, r1 = job
+    m = _POOL[name]
+    x = m["x"][r0:r1].astype(np.float32)
+    if m["fmt"] == "nvfp4":
+        Q.quantize_nvfp4(x, m["imp"], window=m["window"], global_scale=m["S"], hadamard_n=m["had"])
+    else:
+        Q.quantize_mxfp4(x, m["imp"], window=m["window"], hadamard_n=m["had"])
     return r1 - r0
+
+
+def _oracle_pool(mats, cores):
+    """Time the oracle on whole matrices with ``cores`` forked worker
+    processes over row shards.  mats: name -> dict(x=float32 or bf16-as-float
+    numpy matrix, fmt, imp, window, had).  NVFP4 global scales are computed
+    first, once per matrix (in the timed region).  Returns seconds."""
+    import multiprocessing as mp
+    from oracle import hadamard as OH
+    from oracle import quant as Q
+    t0 = time.perf_counter()
+    for name, m in mats.items():
+        if m["fmt"] == "nvfp4":
+            x = m["x"]
+            if m["had"]:
+                amax = np.float32(0)
+                for r0 in range(0, x.shape[0], 1024):
+                    amax = max(amax, np.abs(OH.block_hadamard(x[r0:r0 + 1024].astype(np.float32), m["had"])).max())
+                m["S"] = np.float32(np.float32(amax) / np.float32(1536))
+            else:
+                m["S"] = Q.global_scale_nvfp4(x)
+        _POOL[name] = m
+    jobs = []
+    for name, m in mats.items():
+        rows = m["x"].shape[0]
+        n = max(1, min(rows, 4 * cores))
+        jobs += [(name, rows * i // n, rows * (i + 1) // n) for i in range(n)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        done = sum(pool.map(_oracle_shard, jobs, chunksize=1))
+    dt = time.perf_counter() - t0
+    assert done == sum(m["x"].shape[0] for m in mats.values())
+    for name in mats:
+        _POOL.pop(name, None)
+    return dt
 
 
 def _cpu_model():
@@ -120,7 +172,6 @@ def cpu_baseline(x_cpu, imp, sample_rows, window=None):
     forked worker processes over row shards of the whole matrix (the
     workload's global scale computed once).  Runs before the GPU is touched
     (the pool forks)."""
-    import multiprocessing as mp
     from oracle import quant as Q
     x = x_cpu.float().numpy()
     imp_np = None if imp is None else imp.numpy()
@@ -128,64 +179,97 @@ def cpu_baseline(x_cpu, imp, sample_rows, window=None):
     t0 = time.perf_counter()
     Q.quantize_nvfp4(xs, imp_np, window=window)
     dt1 = time.perf_counter() - t0
-    cores = min(16, len(os.sched_getaffinity(0)))
-    _POOL.update(x=x, imp=imp_np, window=window)
-    t0 = time.perf_counter()
-    _POOL["S"] = Q.global_scale_nvfp4(x)
+    cores, avail = _pool_cores()
+    dtp = _oracle_pool({"c2": dict(x=x, fmt="nvfp4", imp=imp_np, window=window, had=0)}, cores)
     rows = x.shape[0]
-    bounds = [(rows * i // cores, rows * (i + 1) // cores) for i in range(cores)]
-    with mp.get_context("fork").Pool(cores) as pool:
-        done = sum(pool.map(_oracle_rows, bounds))
-    dtp = time.perf_counter() - t0
-    assert done == rows
     return {"value": x.size / dtp / 1e9, "unit": "G elements/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole {rows} x {x.shape[1]} workload in {cores} forked numpy processes (row shards, "
                       f"global scale computed once): {dtp:.1f} s",
+            "available_cores": avail,
             "single_core": {"value": xs.size / dt1 / 1e9, "cores": 1,
                             "sample": f"first {sample_rows} rows ({xs.size} elements), {dt1:.1f} s in one process"},
             "cpu_model": _cpu_model()}
 
 
+_C5_DUMP = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import workloads as W
+for name in W.LAYER_70B:
+    dev = "cuda:0" if torch.cuda.is_available() else "cpu"
+    w = W.c5_matrix(0, name, dev).cpu().view(torch.int16).numpy()
+    np.save(f"{sys.argv[2]}/c5_l0_{name}.npy", w)
+"""
+
+
+def _c5_layer0_host(tmp):
+    """Layer 0 of the 70B-shaped stream, drawn by its defining device
+    generator in a child process (so this process never opens the GPU and
+    may fork its worker pool), as float32 numpy matrices (memory-mapped)."""
+    import subprocess
+    subprocess.run([sys.executable, "-c", _C5_DUMP, ROOT, tmp], check=True)
+    import workloads as W
+    out = {}
+    for name in W.LAYER_70B:
+        raw = np.load(f"{tmp}/c5_l0_{name}.npy", mmap_mode="r")
+        out[name] = (raw.astype(np.int32) << 16).view(np.float32)   # bf16 bits -> float32, exact
+    return out
+
+
 def oracle_table(sample_rows=256):
-    """The CPU oracle (numpy, unchanged) in one process on the first
-    ``sample_rows`` rows of each workload: elements per second per config,
-    for comparison with the GPU rates.  A sample's global scale is its own
-    max/1536.  The 70B-shaped matrix is drawn on cuda:0 when a GPU is present
-    (its defining generator), else on the CPU."""
-    import torch
+    """The CPU oracle (numpy, unchanged) on this host, beside the GPU rates:
+    per workload, one process on its first ``sample_rows`` rows (one core)
+    and the worker pool over the whole workload -- c1, c2, c3 (three
+    variants), the whole 8B-shaped layer (c4, MSE and WMSE) and layer 0 of
+    the 70B-shaped stream (c5, seven matrices, 16-point Hadamard + WMSE).
+    Never opens the GPU itself (the worker pool forks); the 70B-shaped
+    matrices come from a child process."""
+    import tempfile
     import workloads as W
     from oracle import quant as Q
-    dev = "cuda:0" if torch.cuda.is_available() else "cpu"
+    cores, avail = _pool_cores()
+    f32 = lambda t: t.float().numpy()
     x2, imp2 = W.c2_weight_and_importance()
-    x3 = W.c3_activation()
-    gate = W.c5_matrix(0, "gate", dev)[:sample_rows].float().cpu().numpy()
-    f = lambda t, n=sample_rows: t[:n].float().numpy()
-    cases = [
-        ("c1 NVFP4 MSE fp32 256x1024 (whole)", lambda: Q.quantize_nvfp4(W.c1_weight().float().numpy()),
-         256 * 1024),
-        ("c2 NVFP4 WMSE [-8,7] bf16 4096x4096", lambda: Q.quantize_nvfp4(f(x2), imp2.numpy(), window=(-8, 7)),
-         sample_rows * 4096),
-        ("c3a MXFP4 AbsMax 8192x4096", lambda: Q.quantize_mxfp4(f(x3), window=(0, 0)), sample_rows * 4096),
-        ("c3b MXFP4 [-1,0] 8192x4096", lambda: Q.quantize_mxfp4(f(x3), window=(-1, 0)), sample_rows * 4096),
-        ("c3c MXFP4 [-1,0] after H32", lambda: Q.quantize_mxfp4(f(x3), window=(-1, 0), hadamard_n=32),
-         sample_rows * 4096),
-        ("c4 8B q projection, NVFP4 MSE [-3,7]", lambda: Q.quantize_nvfp4(f(W.c4_matrix("q"))), sample_rows * 4096),
-        ("c4 8B q projection, NVFP4 WMSE [-8,7]",
-         lambda: Q.quantize_nvfp4(f(W.c4_matrix("q")), W.c4_importance("q").numpy(), window=(-8, 7)),
-         sample_rows * 4096),
-        ("c5 70B gate layer 0, H16 + NVFP4 WMSE [-8,7]",
-         lambda: Q.quantize_nvfp4(gate, W.c5_importance("gate").numpy(), window=(-8, 7), hadamard_n=16),
-         sample_rows * 8192),
+    x3 = f32(W.c3_activation())
+    workloads = [
+        ("c1 NVFP4 MSE [-3,7] fp32 256x1024", {"c1": dict(x=f32(W.c1_weight()), fmt="nvfp4", imp=None,
+                                                          window=(-3, 7), had=0)}),
+        ("c2 NVFP4 WMSE [-8,7] bf16 4096x4096", {"c2": dict(x=f32(x2), fmt="nvfp4", imp=imp2.numpy(),
+                                                            window=(-8, 7), had=0)}),
+        ("c3a MXFP4 AbsMax bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(0, 0), had=0)}),
+        ("c3b MXFP4 [-1,0] bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(-1, 0), had=0)}),
+        ("c3c MXFP4 [-1,0] after H32", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(-1, 0), had=32)}),
     ]
-    out = []
-    for name, fn, n in cases:
-        t0 = time.perf_counter()
-        fn()
-        dt = time.perf_counter() - t0
-        out.append({"config": name, "sample_elements": n, "seconds": round(dt, 3),
-                    "G_elements_per_s": n / dt / 1e9})
-        print(json.dumps(out[-1]), file=sys.stderr, flush=True)
-    return {"config": "oracle", "cores": 1, "sample_rows": sample_rows, "cpu_model": _cpu_model(), "rows": out}
+    c4 = {n: f32(W.c4_matrix(n)) for n in W.LAYER_8B}
+    c4imp = {n: W.c4_importance(n).numpy() for n in W.LAYER_8B}
+    workloads.append(("c4 8B layer (7 matrices), NVFP4 MSE [-3,7]",
+                      {n: dict(x=c4[n], fmt="nvfp4", imp=None, window=(-3, 7), had=0) for n in c4}))
+    workloads.append(("c4 8B layer (7 matrices), NVFP4 WMSE [-8,7]",
+                      {n: dict(x=c4[n], fmt="nvfp4", imp=c4imp[n], window=(-8, 7), had=0) for n in c4}))
+    with tempfile.TemporaryDirectory(dir="/dev/shm" if os.path.isdir("/dev/shm") else None) as tmp:
+        c5 = _c5_layer0_host(tmp)
+        workloads.append(("c5 70B layer 0 (7 matrices), H16 + NVFP4 WMSE [-8,7]",
+                          {n: dict(x=c5[n], fmt="nvfp4", imp=W.c5_importance(n).numpy(), window=(-8, 7), had=16)
+                           for n in c5}))
+        out = []
+        for name, mats in workloads:
+            elements = sum(m["x"].size for m in mats.values())
+            # one core: the first sample_rows rows of the first matrix, with their own scale
+            m0 = next(iter(mats.values()))
+            xs = np.ascontiguousarray(m0["x"][:sample_rows], dtype=np.float32)
+            t0 = time.perf_counter()
+            if m0["fmt"] == "nvfp4":
+                Q.quantize_nvfp4(xs, m0["imp"], window=m0["window"], hadamard_n=m0["had"])
+            else:
+                Q.quantize_mxfp4(xs, m0["imp"], window=m0["window"], hadamard_n=m0["had"])
+            dt1 = time.perf_counter() - t0
+            dtp = _oracle_pool(mats, cores)
+            out.append({"config": name, "elements": elements, "pool_seconds": round(dtp, 2),
+                        "pool_G_elements_per_s": elements / dtp / 1e9, "cores": cores,
+                        "one_core_sample_elements": xs.size, "one_core_G_elements_per_s": xs.size / dt1 / 1e9})
+            print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+    return {"config": "oracle", "cores": cores, "available_cores": avail, "one_core_sample_rows": sample_rows,
+            "cpu_model": _cpu_model(), "rows": out}
 
 
 def prewarm(step, seconds=0.3):
@@ -343,6 +427,27 @@ def run_other(args):
         x3 = W.c3_activation().to("cuda:0")
         res["c3_mxfp4"] = [study.mxfp4_code_usage(x3, window=w, hadamard_n=h)
                            for h in (0, 32) for w in ((0, 0), (-1, 0))]
+        # per-block gap quantiles on every workload: AbsMax - window and window - exhaustive
+        gaps = {"c1 NVFP4 MSE": study.gap_report(study.nvfp4_block_losses(W.c1_weight().to("cuda:0"))),
+                "c2 NVFP4 WMSE": study.gap_report(study.nvfp4_block_losses(x2.to("cuda:0"), imp2.to("cuda:0"))),
+                "c3a/b MXFP4 [-1,0]": study.gap_report(study.mxfp4_block_losses(x3)),
+                "c3c MXFP4 [-1,0] after H32": study.gap_report(study.mxfp4_block_losses(x3, hadamard_n=32))}
+        del x3
+        for loss in ("MSE", "WMSE"):
+            pooled = {"absmax": [], "sweep": [], "exhaustive": []}
+            for name in W.LAYER_8B:
+                imp = W.c4_importance(name).to("cuda:0") if loss == "WMSE" else None
+                for k, v in study.nvfp4_block_losses(W.c4_matrix(name).to("cuda:0"), imp).items():
+                    pooled[k].append(v)
+            gaps[f"c4 8B layer (7 matrices) NVFP4 {loss}"] = study.gap_report(pooled)
+        pooled = {"absmax": [], "sweep": [], "exhaustive": []}
+        for name in W.LAYER_70B:
+            ls = study.nvfp4_block_losses(W.c5_matrix(0, name, "cuda:0"), W.c5_importance(name).to("cuda:0"),
+                                          hadamard_n=16)
+            for k, v in ls.items():
+                pooled[k].append(v)
+        gaps["c5 70B layer 0 (7 matrices) H16 + NVFP4 WMSE"] = study.gap_report(pooled)
+        res["gap_quantiles"] = gaps
     elif args.config == "gptq":
         # GPTQ with ScaleSweep group scales on the 4096 x 4096 c2 weight,
         # Hessian from 2048 correlated synthetic calibration tokens
@@ -418,23 +523,7 @@ def run_other(args):
         warm = W.c5_matrix(0, "k", "cuda:0")
         prewarm(lambda i: fq.quantize_nvfp4(warm, imps["k"], hadamard_n=16))
         del warm
-        out_ms = 0.0
-        n = 0
-        for layer in range(args.layers):
-            for name in W.LAYER_70B:
-                x = W.c5_matrix(layer, name, "cuda:0")
-                torch.cuda.synchronize()
-                s = torch.cuda.Event(enable_timing=True)
-                e = torch.cuda.Event(enable_timing=True)
-                s.record()
-                fq.quantize_nvfp4(x, imps[name], hadamard_n=16)
-                e.record()
-                e.synchronize()
-                out_ms += s.elapsed_time(e)
-                n += x.numel()
-                del x
-            print(f"layer {layer} done, {n / out_ms / 1e6:.1f} G el/s so far", file=sys.stderr, flush=True)
-        res.update(layers=args.layers, elements=n, ms_total=out_ms, gel_s=n / out_ms / 1e6)
+        res.update(c5_stream(args.layers, imps, start_layer=args.start_layer, state_path=args.state))
     elif args.config == "w4a4":
         res.update(run_w4a4(args))
     elif args.config == "w4a4nv":
@@ -442,6 +531,67 @@ def run_other(args):
     else:
         raise SystemExit(f"unknown config {args.config}")
     return res
+
+
+def _digest(t):
+    """Order-sensitive 64-bit checksum of a uint8 device tensor, computed on
+    the device: sum of (index + 1) * word over its int32 words, mod 2^63."""
+    import torch
+    w = t.reshape(-1).view(torch.int32).to(torch.int64)
+    k = torch.arange(1, w.numel() + 1, device=w.device, dtype=torch.int64)
+    return int(((w & 0xFFFFFFFF) * k).sum().item()) & (2**63 - 1)
+
+
+def c5_stream(layers, imps, start_layer=0, state_path=None, shapes=None, device="cuda:0"):
+    """The 70B-shaped weight stream, layer by layer: each matrix is drawn on
+    the device, rotated (16-point block Hadamard) and quantized (NVFP4 WMSE),
+    its outputs reduced to a checksum on the device and discarded.  Only the
+    quantize calls are timed.  With ``state_path`` a record per finished
+    layer (per-matrix checksums of codes and scales, the global scale) is
+    written there after every layer (write to a temporary file, then
+    rename); ``start_layer`` > 0 resumes a stream from that file, whose
+    records of the earlier layers must all be present."""
+    import torch
+    import fp4_post_quantization_amd as fq
+    import workloads as W
+    shapes = shapes or W.LAYER_70B
+    records = {}
+    if start_layer:
+        if not state_path or not os.path.exists(state_path):
+            raise SystemExit(f"--start-layer {start_layer} needs the state file of the earlier layers")
+        records = {int(k): v for k, v in json.load(open(state_path))["layers"].items()}
+        missing = [k for k in range(start_layer) if k not in records]
+        if missing:
+            raise SystemExit(f"state file {state_path} lacks layers {missing}")
+        records = {k: v for k, v in records.items() if k < start_layer}
+    out_ms, n = 0.0, 0
+    for layer in range(start_layer, layers):
+        rec = {}
+        for name, shape in shapes.items():
+            x = W.c5_matrix(layer, name, device, shape=shape)
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            r = fq.quantize_nvfp4(x, imps[name], hadamard_n=16, with_loss=False, with_offsets=False)
+            e.record()
+            e.synchronize()
+            out_ms += s.elapsed_time(e)
+            n += x.numel()
+            rec[name] = {"codes": _digest(r.codes), "scales": _digest(r.scales),
+                         "global_scale_bits": int(r.global_scale.view(torch.int32).item()) & 0xFFFFFFFF}
+            del x, r
+        records[layer] = rec
+        if state_path:
+            tmp = state_path + ".tmp"
+            with open(tmp, "w") as f:
+                json.dump({"layers": {str(k): v for k, v in sorted(records.items())}}, f)
+            os.replace(tmp, state_path)
+        print(f"layer {layer} done, {n / out_ms / 1e6:.1f} G el/s so far", file=sys.stderr, flush=True)
+    whole = ",".join(f"{k}:{v[m]['codes']}:{v[m]['scales']}" for k, v in sorted(records.items()) for m in v)
+    return {"layers": layers, "start_layer": start_layer, "elements": n, "ms_total": out_ms,
+            "gel_s": n / out_ms / 1e6 if out_ms else None,
+            "stream_digest": hashlib.sha256(whole.encode()).hexdigest()[:16], "records": len(records)}
 
 
 def run_w4a4(args, fmt="mxfp4"):
@@ -541,6 +691,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--layers", type=int, default=2)
+    ap.add_argument("--start-layer", type=int, default=0,
+                    help="c5: resume the stream at this layer from the --state file")
+    ap.add_argument("--state", default=None, help="c5: per-layer checksum records, written after every layer")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",

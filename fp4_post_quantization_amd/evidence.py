@@ -105,7 +105,8 @@ WORKLOADS = {
              "alg_flops": {_W4A4_BIG: _gemm_mean(_W4A4_NK_BIG, "flops"),
                            _W4A4_SMALL: _gemm_mean(_W4A4_NK_SMALL, "flops")},
              "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
-             "peak_tflops": 10100.0, "sources": GEMM_SOURCES},
+             "peak_tflops": 10100.0, "peak_label": "the published dense FP4 (MXFP4 scaled MFMA) figure",
+             "sources": GEMM_SOURCES},
     "w4a4nv": {"stem": "nvfp4_w4a4_gemm_8b_layer_8192tok", "kernel": _W4A4NV_BIG,
                "title": "W4A4 NVFP4 layer (8B shapes, 8192 tokens): bf16-decoded operands on the bf16 matrix cores",
                "alg_bytes": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "bytes"),
@@ -115,7 +116,9 @@ WORKLOADS = {
                "alg_flops": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "flops"),
                              _W4A4NV_SMALL: _bf16_gemm_mean(_W4A4_NK_SMALL, "flops")},
                "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
-               "peak_tflops": 2500.0, "sources": GEMM_SOURCES},
+               "peak_tflops": 2500.0, "peak_label": "the published dense bf16/fp16 figure (the operands run on "
+                                                    "the bf16 and fp16 matrix cores)",
+               "sources": GEMM_SOURCES},
     # FOCUS forward quantizer on the c2 weight: x (bf16), FP16 coefficients per 8, E4M3 scales in;
     # codes and the float32 dequantized output out
     "focus": {"stem": "focus_relaxed_bf16_4096x4096", "kernel": "relaxed_quant_kernel",
@@ -214,6 +217,8 @@ def summarize(config, in_dir, profiles):
     clk_mhz = float(agent.get("Max_Engine_Clk_Fcompute", 2400))
     xcc = int(agent.get("Num_Xcc", 8))
     cus = int(agent.get("Cu_Count", 256))
+    # shader engines: SQ_BUSY_CYCLES is summed over them (4 per XCD on gfx950)
+    ses = int(agent.get("Num_Shader_Engines", 0) or agent.get("Shader_Engines", 0) or 4 * xcc)
     valu = _counter_means(os.path.join(in_dir, "valu", f"{config}_counter_collection.csv"))
     fetch = _counter_means(os.path.join(in_dir, "fetch", f"{config}_counter_collection.csv"))
     write = _counter_means(os.path.join(in_dir, "write", f"{config}_counter_collection.csv"))
@@ -268,9 +273,12 @@ def summarize(config, in_dir, profiles):
         lines.append(f"| `{_short(name)}` | {r['Calls']} | {avg:.2f} | {float(r['MinNs'])/1000:.2f} "
                      f"| {float(r['MaxNs'])/1000:.2f} |")
     lines += ["", "## Counters per dispatch (averages)", "",
-              "VALU issue = SQ_INSTS_VALU x 4 cycles / (SIMDs x trace duration x clock); VALUBusy = "
-              "100 x SQ_ACTIVE_INST_VALU / CUs / (GRBM_GUI_ACTIVE / XCDs), the counter runs being "
-              "slower than the trace.", "",
+              "VALU issue = SQ_INSTS_VALU x 4 cycles (one wave64 VALU instruction per SIMD per 4 cycles) "
+              "/ (SIMDs x trace duration x clock).  VALUBusy = the same instruction cycles / (SIMDs x "
+              "SQ_BUSY_CYCLES / shader engines), i.e. within the cycles the shader engines held waves, "
+              "both from the counter run; neither can exceed 100%.  (SQ_ACTIVE_INST_VALU is not used: it "
+              "counts every wave with a VALU instruction in flight, so its ratio to SIMD cycles can pass "
+              "100%.)", "",
               "| kernel | waves | VALU insts | VALU issue | VALUBusy | FETCH KiB | WRITE KiB | HBM bytes "
               "(calibrated) | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
     record = None
@@ -280,12 +288,11 @@ def summarize(config, in_dir, profiles):
         key = _short(name) if _short(name) in w["alg_bytes"] else _short(name).split("<")[0]
         insts = pick(valu, name, "SQ_INSTS_VALU")
         waves = pick(valu, name, "SQ_WAVES")
-        active = pick(valu, name, "SQ_ACTIVE_INST_VALU")
-        grbm = pick(valu, name, "GRBM_GUI_ACTIVE")
+        sq_busy = pick(valu, name, "SQ_BUSY_CYCLES")
         fk = pick(fetch, name, "FETCH_SIZE")
         wk = pick(write, name, "WRITE_SIZE")
         issue = insts[0] * 4 / (simds * avg_us * 1e-6 * clk_mhz * 1e6) if insts else None
-        busy = 100 * active[0] / cus / (grbm[0] / xcc) if active and grbm else None
+        busy = 100 * insts[0] * 4 / (simds * sq_busy[0] / ses) if (insts and sq_busy and sq_busy[0]) else None
         hbm = (fk[0] * 1024 * f_factor + wk[0] * 1024 * w_factor) if (fk and wk and f_factor) else None
         alg = w["alg_bytes"].get(key)
         lines.append(
@@ -301,8 +308,9 @@ def summarize(config, in_dir, profiles):
                       "source_sha256": source_hash(config)}
     if w.get("alg_flops"):
         lines += ["", "## Matrix cores", "",
-                  f"Achieved = mean algorithmic flops per dispatch / average duration; peak = the published dense "
-                  f"FP4 figure ({w['peak_tflops']:.0f} TFLOP/s at 2.4 GHz).  MFMA busy share = "
+                  f"Achieved = mean algorithmic flops per dispatch / average duration; peak = "
+                  f"{w.get('peak_label', 'the published dense figure')} ({w['peak_tflops']:.0f} TFLOP/s at "
+                  f"2.4 GHz).  MFMA busy share = "
                   "SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCDs); cycles per MFMA = "
                   "SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA.", "",
                   "| kernel | flops per dispatch | achieved TFLOP/s | of peak | MFMA insts | cycles per MFMA | "

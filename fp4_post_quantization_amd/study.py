@@ -56,6 +56,60 @@ def _events_ms(fn, iters):
     return s.elapsed_time(e) / iters
 
 
+QUANTILES = (0.5, 0.9, 0.99)
+
+
+def quantiles(v):
+    """p50 / p90 / p99 / max of a 1-D tensor (sorted on the device; no size
+    limit), as floats."""
+    v = v.reshape(-1).double().sort().values
+    n = v.numel()
+    out = {f"p{int(round(q * 100))}": float(v[min(n - 1, int(q * (n - 1) + 0.5))]) for q in QUANTILES}
+    out["max"] = float(v[-1])
+    return out
+
+
+def gap_quantiles(l_from, l_to):
+    """Per-block gap l_from - l_to (never negative here: the narrower rule's
+    candidates are a subset) and the same gap relative to l_from, as
+    quantiles over the blocks (blocks with l_from = 0 have relative gap 0)."""
+    g = (l_from - l_to).reshape(-1)
+    rel = torch.where(l_from.reshape(-1) > 0, g / l_from.reshape(-1), torch.zeros_like(g))
+    return {"absolute": quantiles(g), "relative": quantiles(rel), "negative_blocks": int((g < 0).sum())}
+
+
+def nvfp4_block_losses(x, importance=None, hadamard_n=0):
+    """Per-block losses (float64) of AbsMax, the ScaleSweep window and the
+    exhaustive window on one matrix, no timing."""
+    sweep_window = (-8, 7) if importance is not None else (-3, 7)
+    rules = {"absmax": (0, 0), "sweep": sweep_window, "exhaustive": (-126, 126)}
+    return {k: quantize_nvfp4(x, importance, window=w, hadamard_n=hadamard_n, check=True).block_loss.double()
+            for k, w in rules.items()}
+
+
+def gap_report(losses):
+    """Gap quantiles AbsMax - sweep and sweep - exhaustive over the blocks of
+    one or several matrices (lists of per-block loss tensors are pooled)."""
+    cat = {k: torch.cat([v.reshape(-1) for v in (vs if isinstance(vs, list) else [vs])])
+           for k, vs in losses.items()}
+    a, s, e = cat["absmax"], cat["sweep"], cat["exhaustive"]
+    return {"blocks": a.numel(),
+            "absmax_minus_sweep": gap_quantiles(a, s),
+            "sweep_minus_exhaustive": gap_quantiles(s, e),
+            "loss_reduction_sweep_vs_absmax": 1 - float(s.sum() / a.sum()),
+            "loss_reduction_exhaustive_vs_sweep": 1 - float(e.sum() / s.sum()) if float(s.sum()) else 0.0,
+            "blocks_where_exhaustive_beats_sweep": float((e < s).double().mean())}
+
+
+def mxfp4_block_losses(x, importance=None, hadamard_n=0, window=(-1, 0)):
+    """Per-block MXFP4 losses for AbsMax (0, 0), the exponent window, and the
+    widest window the call takes (-16, +16: a block whose best exponent lies
+    16 binades below its maximum's would zero every element)."""
+    rules = {"absmax": (0, 0), "sweep": window, "exhaustive": (-16, 16)}
+    return {k: quantize_mxfp4(x, importance, window=w, hadamard_n=hadamard_n, check=True).block_loss.double()
+            for k, w in rules.items()}
+
+
 def nvfp4_scale_rules(x, importance=None, iters=20, hadamard_n=0):
     """AbsMax vs ScaleSweep vs exhaustive on one matrix (after the optional block rotation)."""
     sweep_window = (-8, 7) if importance is not None else (-3, 7)
@@ -68,6 +122,7 @@ def nvfp4_scale_rules(x, importance=None, iters=20, hadamard_n=0):
         ms = _events_ms(lambda: quantize_nvfp4(x, importance, window=win, hadamard_n=hadamard_n, out=r), iters)
         res[name] = {"window": list(win), "ms": ms, "loss_sum": float(r.block_loss.double().sum())}
     a, s, e = (out[k].block_loss.double() for k in ("absmax", "sweep", "exhaustive"))
+    res["gaps"] = gap_report({"absmax": a, "sweep": s, "exhaustive": e})
     nblk = a.numel()
     res["blocks"] = nblk
     res["sweep_vs_absmax"] = {

@@ -10,6 +10,8 @@ is additionally checked to reproduce the oracle's float32 fast transform bit
 for bit, in which case everything downstream is bit-exact too.
 """
 
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -870,3 +872,26 @@ def test_gptq_bad_hessian_sets_status():
     U[5, 5] = 0.0
     with pytest.raises(fq.FP4QError, match="inverse-Hessian"):
         fq.gptq_nvfp4(w, U, check=True)
+
+
+# ------------------------------------------- the layer stream's records ----
+def test_c5_stream_checksums_and_resume(tmp_path):
+    """The 70B-shaped stream on small shapes: three layers in one run give
+    the same per-layer checksums and stream digest as two layers followed by
+    a run resumed at layer 2 from the state file; resuming without the
+    earlier layers' records is refused; the device checksum equals a host
+    recomputation."""
+    import bench
+    shapes = {"q": (64, 256), "k": (32, 256), "down": (256, 512)}
+    imps = {n: W.random_importance(c, seed=600 + c).to(DEV) for n, (r, c) in shapes.items()}
+    full = bench.c5_stream(3, imps, state_path=str(tmp_path / "a.json"), shapes=shapes)
+    bench.c5_stream(2, imps, state_path=str(tmp_path / "b.json"), shapes=shapes)
+    resumed = bench.c5_stream(3, imps, start_layer=2, state_path=str(tmp_path / "b.json"), shapes=shapes)
+    assert resumed["stream_digest"] == full["stream_digest"] and resumed["records"] == 3
+    assert json.load(open(tmp_path / "a.json")) == json.load(open(tmp_path / "b.json"))
+    with pytest.raises(SystemExit):
+        bench.c5_stream(3, imps, start_layer=2, state_path=str(tmp_path / "missing.json"), shapes=shapes)
+    codes = torch.randint(0, 256, (64, 128), dtype=torch.uint8)
+    words = codes.numpy().reshape(-1).view(np.uint32).astype(object)
+    host = sum((i + 1) * int(w) for i, w in enumerate(words)) % 2**63
+    assert bench._digest(codes.to(DEV)) == host

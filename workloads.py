@@ -129,13 +129,14 @@ def c5_importance(name):
     return torch.from_numpy(rotated_gram_diag_importance(2048, cols, C5_HADAMARD, _IMP_SEEDS_70B[group]))
 
 
-def c5_matrix(layer, name, device):
+def c5_matrix(layer, name, device, shape=None):
     """One 70B-shaped matrix of layer ``layer``, drawn on ``device``:
-    N(0, 0.02) with a Bernoulli(5e-4) mask of entries times 30, bf16."""
+    N(0, 0.02) with a Bernoulli(5e-4) mask of entries times 30, bf16.
+    ``shape`` overrides the 70B shape (small streams in tests)."""
     order = list(LAYER_70B)
     g = torch.Generator(device=device)
     g.manual_seed(500000 + 1000 * layer + order.index(name))
-    rows, cols = LAYER_70B[name]
+    rows, cols = shape if shape is not None else LAYER_70B[name]
     w = torch.randn((rows, cols), generator=g, device=device, dtype=torch.float32) * 0.02
     mask = torch.rand((rows, cols), generator=g, device=device) < 5e-4
     w = torch.where(mask, w * 30.0, w)
