@@ -134,8 +134,8 @@ __device__ __forceinline__ uint32_t reduce_partials(const uint32_t *partials, in
     f |= v;
   }
   m = wave_max_u32(m);
-  f = wave_max_u32(f & kPartialBadImp);
-  bits = (m >= 0x7F800000u ? FP4Q_DATA_NONFINITE_INPUT : 0u) | (f ? FP4Q_DATA_BAD_IMPORTANCE : 0u);
+  const bool bad_imp = __ballot((f & kPartialBadImp) != 0) != 0;  // one wave-wide test, no shuffles
+  bits = (m >= 0x7F800000u ? FP4Q_DATA_NONFINITE_INPUT : 0u) | (bad_imp ? FP4Q_DATA_BAD_IMPORTANCE : 0u);
   return m;
 }
 

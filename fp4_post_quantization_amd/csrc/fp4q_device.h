@@ -180,13 +180,24 @@ __device__ __forceinline__ float xor_lane(float v) {
 // value: tile arithmetic and row loops derived from it run on the scalar unit.
 __device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Maximum of v over the 64 lanes of the wave, in every lane, by DPP (no LDS
+// round trips): row shifts by 1, 2, 4 and 8 leave each 16-lane row's maximum
+// in its lane 15 (lanes shifted in from outside a row read 0, the identity),
+// row_bcast:15 and row_bcast:31 carry rows 0-1 and 0-2 upwards, so lane 63
+// ends with the wave's maximum, which is read back as a scalar.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+  return v > o ? v : o;
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint32_t o = __shfl_xor(v, m, 64);
-    v = v > o ? v : o;
-  }
-  return v;
+  v = dpp_max_step<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // ------------------------------------------------- block Hadamard ----
