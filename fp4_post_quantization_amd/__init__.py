@@ -208,7 +208,7 @@ def quantize_nvfp4(x, importance=None, window=None, hadamard_n=0, global_scale=N
     tensor; passing ``out.global_scale`` itself copies nothing) instead of
     max|x|/1536.  out: a preallocated NVFP4Result to write into.  check: synchronize and raise on data errors.
     accumulate_status: add this call's data errors to the workspace's status
-    word instead of replacing it (FP4Q_ACCUMULATE_STATUS; no clearing kernel).
+    word instead of replacing it (FP4Q_ACCUMULATE_STATUS).
     """
     lib = L.load()
     x, ld = _matrix(x)
@@ -252,7 +252,8 @@ def quantize_nvfp4_noalloc(x, importance=None, window=None, hadamard_n=0, *, out
     no device allocation in the call.  Every tensor is the caller's and is
     used in place: x a dense row-major float32/bfloat16 matrix, importance a
     dense float32 [cols] vector (WMSE) or None, out a preallocated
-    NVFP4Result, status a [1] int32 device tensor for the data-error bits.
+    NVFP4Result, status a [2] int32 device tensor (element 0 receives the
+    data-error bits, element 1 the call's tag).
     given_scale: out.global_scale already holds S (FP4Q_GIVEN_SCALE)."""
     lib = L.load()
     if x.dim() != 2 or not x.is_cuda or not x.is_contiguous():
@@ -267,7 +268,7 @@ def quantize_nvfp4_noalloc(x, importance=None, window=None, hadamard_n=0, *, out
     _check_result(out, rows, cols, 16, dev)
     if out.global_scale is None:
         raise ValueError("out.global_scale is required")
-    _given(status, (1,), torch.int32, dev, "status")
+    _given(status, (2,), torch.int32, dev, "status")
     flags = (L.GIVEN_SCALE if given_scale else 0) | (L.ACCUMULATE_STATUS if accumulate_status else 0)
     L.check(lib.fp4q_quantize_nvfp4_noalloc(
         x.data_ptr(), _dtype_code(x), rows, cols, cols, _ptr(importance), 16, loss, int(window[0]),

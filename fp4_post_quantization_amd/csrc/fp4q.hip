@@ -59,28 +59,72 @@ __constant__ E4M3Tables kE4M3 = make_e4m3_tables();
 
 // ============================================================ kernels ====
 
-// First kernel of a call that runs no global-max pass: writes the call's
-// status word (so no bit of an earlier call survives) with the result of
-// validating what the call reads once: a given NVFP4 global scale (S < 0,
-// Inf or NaN is an error) and the importance vector (< 0, Inf or NaN).
-// Optionally writes the global scale of an empty NVFP4 tensor (0).  One
-// workgroup; the kernels that follow in the call only add bits.
-__global__ __launch_bounds__(kThreads) void status_init_kernel(uint32_t *__restrict__ status,
-                                                                const float *__restrict__ given_scale,
-                                                                const float *__restrict__ imp, int imp_n,
-                                                                float *__restrict__ zero_scale_out) {
-  bool ok = true;
-  if (imp)
-    for (int i = threadIdx.x; i < imp_n; i += kThreads) ok &= (imp[i] >= 0.0f) & (imp[i] <= 3.402823466e38f);
-  const int bad_imp = __syncthreads_or(!ok);
+// The dispatch ID of the running kernel: the index of its packet in the
+// hardware queue, the same in every workgroup of a launch and different for
+// every launch on the queue.
+extern "C" __device__ unsigned long long fp4q_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// The status word of a call is a 64-bit slot at the start of the workspace:
+// its low half (byte 0) holds the FP4Q_DATA_* bits, its high half the low
+// 32 bits of the dispatch ID of the call's first kernel.  That kernel's
+// workgroups merge into the slot by compare-and-swap.  A slot with another
+// tag belongs to an earlier call, or is garbage, and is replaced; a slot
+// with this call's tag gets the bits ORed in.  So in whichever order the
+// workgroups arrive, the slot ends with this call's tag and exactly the
+// bits its kernels reported.  Workgroup 0 of the first kernel always merges
+// (with no bits if it has none), so a call without errors still replaces
+// the slot; nothing waits on anything.  The call's later kernels run after
+// the first on the stream and OR their bits into the low half.
+struct Status {
+  uint32_t *slot;
+  bool first;  // this kernel is the call's first: merge under its dispatch tag
+
+  __device__ void merge(uint32_t bits) const {
+    unsigned long long *p = reinterpret_cast<unsigned long long *>(slot);
+    const unsigned long long tag = (unsigned long long)(uint32_t)fp4q_dispatch_id() << 32;
+    unsigned long long old = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+      const unsigned long long keep = (old & 0xFFFFFFFF00000000ull) == tag ? (old & 0xFFFFFFFFull) : 0ull;
+      const unsigned long long want = tag | keep | bits;
+      if (want == old) return;
+      const unsigned long long seen = atomicCAS(p, old, want);
+      if (seen == old) return;
+      old = seen;
+    }
+  }
+  // an error found by any workgroup
+  __device__ void report(uint32_t bits) const {
+    if (first) merge(bits);
+    else atomicOr(slot, bits);
+  }
+  // at the start of a kernel: workgroup 0 of the call's first kernel takes the slot
+  __device__ void begin() const {
+    if (first && blockIdx.x == 0 && threadIdx.x == 0) merge(0u);
+  }
+  // at the end of a kernel whose lanes gathered their error bits in err: one report site for all
+  // of them (thread 0 of workgroup 0 reports even without errors, taking the slot for a first kernel)
+  __device__ void finish(uint32_t err) const {
+    if (__builtin_expect(err != 0u, 0) || (first && blockIdx.x == 0 && threadIdx.x == 0)) report(err);
+  }
+};
+
+// The only kernel of an empty call: takes the status slot for the call, or
+// adds to it (first = false), with no bits or those of validating a given
+// NVFP4 global scale, and optionally writes the global scale of an empty
+// NVFP4 tensor (0).
+__global__ __launch_bounds__(64) void status_init_kernel(uint32_t *__restrict__ status, bool first,
+                                                          const float *__restrict__ given_scale,
+                                                          float *__restrict__ zero_scale_out) {
   if (threadIdx.x == 0) {
-    uint32_t bits = bad_imp ? FP4Q_DATA_BAD_IMPORTANCE : 0u;
+    uint32_t bits = 0u;
     if (given_scale) {
       const float S = *given_scale;
       if (!(S >= 0.0f) || isinf(S)) bits |= FP4Q_DATA_BAD_GLOBAL_SCALE;
     }
     if (zero_scale_out) *zero_scale_out = 0.0f;
-    if (status) *status = bits;
+    const Status st{status, first};
+    if (first) st.merge(bits);
+    else if (bits) st.report(bits);
   }
 }
 
@@ -90,7 +134,7 @@ struct AmaxOut {
   uint32_t *status;
   const float *imp;    // importance [imp_n] to validate, or null
   int imp_n;
-  bool clear_status;   // the call's status word starts here (else the call adds to it)
+  bool first;          // the call's first kernel: takes the status slot (else the call adds to it)
 };
 
 // Bit 31 of a max-pass partial (the maxima are |x| bit patterns, below
@@ -102,7 +146,7 @@ constexpr uint32_t kPartialBadImp = 0x80000000u;
 // partials[blockIdx.x].  The workgroups also validate the importance vector
 // between them (a strided slice each), so the quantizer that follows need
 // not, and report it in bit 31 of their partial.  No workgroup touches the
-// status word except workgroup 0, which clears it for the call (unless the
+// status slot except workgroup 0, which takes it for the call (unless the
 // call adds to it); the kernel that reduces the partials sets its bits.
 __device__ void finish_amax(uint32_t m, const AmaxOut &o) {
   __shared__ uint32_t red[kWaves];
@@ -120,7 +164,7 @@ __device__ void finish_amax(uint32_t m, const AmaxOut &o) {
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) r = red[k] > r ? red[k] : r;
     o.partials[blockIdx.x] = r | (bad_imp ? kPartialBadImp : 0u);
-    if (blockIdx.x == 0 && o.clear_status) *o.status = 0u;
+    if (blockIdx.x == 0 && o.first) Status{o.status, true}.merge(0u);
   }
 }
 
@@ -247,7 +291,8 @@ struct SweepArgs {
   const uint32_t *partials;     // amax partials (NVFP4, computed scale)
   int n_partials;
   const float *given_scale;     // NVFP4 with FP4Q_GIVEN_SCALE, else null
-  bool check_given;             // validate the given scale and the importance here (no kernel before did)
+  bool check_inputs;            // validate the importance and a given scale here (no max pass did)
+  bool status_first;            // this sweep is the call's first kernel (takes the status slot)
   uint8_t *codes, *scales;
   float *gscale_out;            // NVFP4 global scale output (computed scale)
   float *loss;
@@ -402,6 +447,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   const int band = tile % a.nbands, rg = tile / a.nbands;
   const int c = band * 64 + lane;
   const bool active = tile < a.ntiles && c < a.cpr;  // whole Hadamard groups are active or not together
+  const Status st{a.status, a.status_first};
+  uint32_t err = 0u;  // this lane's data errors, reported once at the end
   const int r0 = rg * a.rows_per_tile;
   const int r1 = min(a.rows, r0 + a.rows_per_tile);
   const T *xc = static_cast<const T *>(a.x) + (int64_t)c * 16;
@@ -419,16 +466,16 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   if (wave == 0) {
     float S;
     if (a.given_scale) {
-      S = *a.given_scale;  // validated by the call's first kernel, or just below
-      if (a.check_given && blockIdx.x == 0 && lane == 0 && (!(S >= 0.0f) || isinf(S)))
-        atomicOr(a.status, FP4Q_DATA_BAD_GLOBAL_SCALE);
+      S = *a.given_scale;
+      if (a.check_inputs && blockIdx.x == 0 && lane == 0 && (!(S >= 0.0f) || isinf(S)))
+        err |= FP4Q_DATA_BAD_GLOBAL_SCALE;
     } else {
       uint32_t bits;
       const uint32_t m = reduce_partials(a.partials, a.n_partials, lane, bits);
       S = as_f(m) / 1536.0f;  // max|x| / (256 * 6), correctly rounded
       if (blockIdx.x == 0 && lane == 0) {
         *a.gscale_out = S;
-        if (bits) atomicOr(a.status, bits);
+        err |= bits;
       }
     }
     if (lane == 0) {
@@ -439,9 +486,9 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
   __syncthreads();
   const float S = sc[0], S_inv = sc[1];
   const float SS = S * S;
-  if (!active) return;
+  if (!active) return;  // thread 0 of workgroup 0 (tile 0, chunk 0) is always active
   if constexpr (WMSE) {
-    if (a.check_given && !importance_ok(w)) atomicOr(a.status, FP4Q_DATA_BAD_IMPORTANCE);
+    if (a.check_inputs && !importance_ok(w)) err |= FP4Q_DATA_BAD_IMPORTANCE;
   }
 
   const int bpr = a.cpr;  // blocks per row
@@ -465,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
       bool finite = true;
 #pragma unroll
       for (int i = 0; i < 16; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
-      if (!finite) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+      if (!finite) err |= FP4Q_DATA_NONFINITE_INPUT;
     }
     const float t = amax / 6.0f;  // correctly rounded
     int base = e4m3_rne_sat(t);
@@ -492,6 +539,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep_kernel(SweepArgs a) {
     if (a.offs) a.offs[bi] = (int8_t)(pbest - base);
     cur = nxt;
   }
+  st.finish(err);
 }
 
 // Loss of one candidate over a lane's 32-element MXFP4 block from its four
@@ -639,12 +687,15 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
   const int r0 = rg * a.rows_per_tile;
   const int r1 = min(a.rows, r0 + a.rows_per_tile);
   u32x4 *st = stage[wave].q;
+  const Status status{a.status, a.status_first};
+  uint32_t err = 0u;  // this lane's data errors, reported once at the end
 
   float w[32];
   if constexpr (WMSE) {
     if (active) {
       load_importance(a.imp + (int64_t)b * 32, w);
       load_importance(a.imp + (int64_t)b * 32 + 16, w + 16);
+      if (a.check_inputs && !(importance_ok(w) & importance_ok(w + 16))) err |= FP4Q_DATA_BAD_IMPORTANCE;
     }
   }
 
@@ -700,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
       bool finite = true;
 #pragma unroll
       for (int i = 0; i < 32; ++i) finite &= fabsf(z[i]) <= 3.402823466e38f;
-      if (!finite && active) atomicOr(a.status, FP4Q_DATA_NONFINITE_INPUT);
+      if (!finite && active) err |= FP4Q_DATA_NONFINITE_INPUT;
     }
     if (!(keep & lfin)) {  // else the winner's codes were kept
       const float db = pow2f(-ebest);
@@ -724,6 +775,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep_kernel(SweepArgs a) {
 #pragma unroll
     for (int k = 0; k < NP; ++k) cur[k] = nxt[k];
   }
+  status.finish(err);  // thread 0 of workgroup 0 (tile 0) gets here
 }
 
 // 16 floats of chunk c of an output row (row stride 16 cpr floats).  When
@@ -753,12 +805,18 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
                                                                   const float *__restrict__ gscale,
                                                                   const uint16_t *__restrict__ coeffs,
                                                                   uint8_t *__restrict__ codes,
-                                                                  float *__restrict__ dq,
-                                                                  uint32_t *__restrict__ status) {
+                                                                  float *__restrict__ dq, Status status) {
   const int lane = threadIdx.x & 63;
+  uint32_t err = 0u;  // this lane's data errors, reported once at the end
+  if constexpr (FMT == FP4Q_NVFP4) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const float Sg = *gscale;
+      if (!(Sg >= 0.0f) || isinf(Sg)) err |= FP4Q_DATA_BAD_GLOBAL_SCALE;
+    }
+  }
   const int64_t g0 = (int64_t)blockIdx.x * kThreads + 64 * wave_index();
   int r, c;
-  if (!lane_chunk(g0, lane, cpr, total, r, c)) return;
+  if (!lane_chunk(g0, lane, cpr, total, r, c)) return;  // thread 0 of workgroup 0 never returns here
   float z[16];
   load16(x + (int64_t)r * ld + (int64_t)c * 16, z);
 
@@ -798,8 +856,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
 #pragma unroll
     for (int i = 0; i < E; ++i) y[j * E + i] = us[j * E + i] * R;
   }
-  if (bad) atomicOr(status, FP4Q_DATA_BAD_SCALE);
-  if (!finite) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+  err |= (bad ? FP4Q_DATA_BAD_SCALE : 0u) | (finite ? 0u : FP4Q_DATA_NONFINITE_INPUT);
   const uint32_t k0 = cvt8<false>(y, 0u), k1 = cvt8<false>(y + 8, 0u);
   *reinterpret_cast<uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)c * 8) = make_uint2(k0, k1);
   if (dq) {
@@ -814,6 +871,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_kernel(const T *__rest
     }
     store_chunk_f32(dq + (int64_t)r * cols, c, cpr, lane, v);
   }
+  status.finish(err);
 }
 
 // ================================================================ GPTQ ====
@@ -876,7 +934,7 @@ template <bool WMSE, int FMT>
 __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     float *__restrict__ W, int64_t ld, int rows, int cols, int i1, const float *__restrict__ U,
     const float *__restrict__ imp, const float *__restrict__ gscale, int lo, int hi, uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ scales, uint32_t *__restrict__ status) {
+    uint8_t *__restrict__ scales, Status status) {
   __shared__ __attribute__((aligned(1024))) float Ub[kGptqBatch][kGptqBatch];
   __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch], impb[kGptqBatch];
   const int tid = threadIdx.x;
@@ -899,6 +957,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     dg = U[(int64_t)(i1 + tid) * cols + i1 + tid];
     if (WMSE) im = imp[i1 + tid];
   }
+  status.begin();
+  // a given NVFP4 scale is checked once, by the call's first kernel
+  if (!MX && status.first && blockIdx.x == 0 && tid == 0 && (!(S >= 0.0f) || isinf(S)))
+    status.report(FP4Q_DATA_BAD_GLOBAL_SCALE);
   float *wr = W + (int64_t)(live ? r : 0) * ld + i1 + 8 * t;
   const f32x4 wa = *reinterpret_cast<const f32x4 *>(wr);
   const f32x4 wb = *reinterpret_cast<const f32x4 *>(wr + 4);
@@ -917,10 +979,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
   if (tid < 128) {
     Vtab[tid] = tv;
     Rtab[tid] = trc;
-    if (!((dg > 0.0f) & (dg <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_HESSIAN);
+    if (!((dg > 0.0f) & (dg <= 3.402823466e38f))) status.report(FP4Q_DATA_BAD_HESSIAN);
     rdiag[tid] = 1.0f / dg;  // correctly rounded
     impb[tid] = im;
-    if (WMSE && !((im >= 0.0f) & (im <= 3.402823466e38f))) atomicOr(status, FP4Q_DATA_BAD_IMPORTANCE);
+    if (WMSE && !((im >= 0.0f) & (im <= 3.402823466e38f))) status.report(FP4Q_DATA_BAD_IMPORTANCE);
   }
   stash_u(std::integral_constant<int, 0>{});
   float w[8];
@@ -933,7 +995,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     bool finite = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) finite &= fabsf(w[k]) <= 3.402823466e38f;
-    if (!finite) atomicOr(status, FP4Q_DATA_NONFINITE_INPUT);
+    if (!finite) status.report(FP4Q_DATA_NONFINITE_INPUT);
   }
   __syncthreads();  // the tables and rows 0 .. 7 of the U block
   uint32_t code8 = 0;
@@ -1231,9 +1293,11 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
 template <int FMT>
 static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
                          const float *importance, const float *global_scale, int off_lo, int off_hi, uint8_t *codes,
-                         uint8_t *scales, uint32_t *status, hipStream_t s) {
+                         uint8_t *scales, uint32_t *status_slot, bool first_kernel, hipStream_t s) {
   const int gb = ceil_div(rows, kGptqRowsPerWg);
   for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
+    // the first batch kernel is the call's first kernel unless a max pass ran before it
+    const Status status{status_slot, first_kernel && i1 == 0};
     if (importance)
       hipLaunchKernelGGL((gptq_batch_kernel<true, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
                          (int)cols, i1, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
@@ -1252,9 +1316,9 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
   }
 }
 
-static AmaxOut amax_out(void *workspace, const float *imp, int imp_n, bool clear_status = true) {
+static AmaxOut amax_out(void *workspace, const float *imp, int imp_n, bool first = true) {
   char *b = (char *)workspace;
-  return AmaxOut{(uint32_t *)(b + kWsPartials), (uint32_t *)(b + kWsStatus), imp, imp_n, clear_status};
+  return AmaxOut{(uint32_t *)(b + kWsPartials), (uint32_t *)(b + kWsStatus), imp, imp_n, first};
 }
 
 // Global-max pass over x (after the optional rotation): per-workgroup
@@ -1361,16 +1425,12 @@ static fp4q_status_t quantize_nvfp4_on(const void *x, fp4q_dtype_t dtype, int64_
   const bool given = flags & FP4Q_GIVEN_SCALE;
   const bool accumulate = flags & FP4Q_ACCUMULATE_STATUS;
 
-  // the call's first kernel clears the status word: the global-max pass, or with a given scale (and
-  // for an empty tensor) the kernel that validates the scale and the importance.  A call that adds
-  // to the word launches no such kernel: its sweep validates a given scale and the importance itself.
-  if ((given || empty) && !accumulate)
-    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, given ? global_scale : nullptr,
-                       (wmse && !empty) ? importance : nullptr, (wmse && !empty) ? (int)cols : 0,
-                       given ? nullptr : global_scale);
+  // The call's first kernel takes the status slot: the global-max pass, or with a given scale the sweep
+  // (which then validates the scale and the importance itself).  A call that adds to the word does
+  // not take it.  An empty tensor gets one small kernel for the slot and the scale.
   if (empty) {
-    if (accumulate && !given) hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, nullptr, nullptr,
-                                                 nullptr, 0, global_scale);
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, !accumulate,
+                       given ? global_scale : nullptr, given ? nullptr : global_scale);
     return last_hip_status();
   }
 
@@ -1395,7 +1455,8 @@ static fp4q_status_t quantize_nvfp4_on(const void *x, fp4q_dtype_t dtype, int64_
   a.partials = partials;
   a.n_partials = n_partials;
   a.given_scale = given ? global_scale : nullptr;
-  a.check_given = given && accumulate;
+  a.check_inputs = given;
+  a.status_first = given && !accumulate;
   a.codes = codes;
   a.scales = scales;
   a.gscale_out = global_scale;
@@ -1425,7 +1486,8 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
   char *ws = (char *)workspace;
   return quantize_nvfp4_on(x, dtype, rows, cols, ld, importance, block, loss, off_lo, off_hi, hadamard_n, flags,
                            codes, scales, global_scale, block_loss, offsets,
-                           workspace && workspace_bytes >= kWorkspaceBytes, (uint32_t *)(ws + kWsStatus),
+                           workspace && workspace_bytes >= kWorkspaceBytes && aligned(workspace, 8),
+                           (uint32_t *)(ws + kWsStatus),
                            (uint32_t *)(ws + kWsPartials), (hipStream_t)stream);
 }
 
@@ -1471,6 +1533,7 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4_noalloc(const void *x, fp4q_dtype_t
                                                      float *global_scale, float *block_loss, int8_t *offsets,
                                                      uint32_t *status, void *stream) {
   if (!status) return FP4Q_ERR_NULL;
+  if (!aligned(status, 8)) return FP4Q_ERR_ALIGN;  // the status slot is one 64-bit word
   uint32_t *partials = nullptr;
   const fp4q_status_t st = scratch_of_current_device(&partials);
   if (st != FP4Q_OK) return st;
@@ -1487,13 +1550,13 @@ extern "C" fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dty
                                                  size_t workspace_bytes, void *stream) {
   const bool empty = rows == 0 || cols == 0;
   if (!global_scale || (!empty && !x)) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, 16, hadamard_n);
   if (st != FP4Q_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (empty) {
-    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, (uint32_t *)((char *)workspace + kWsStatus),
-                       nullptr, nullptr, 0, global_scale);
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, (uint32_t *)((char *)workspace + kWsStatus),
+                       true, nullptr, global_scale);
     return last_hip_status();
   }
   // the max pass and the reduction of its partials, as at the start of fp4q_quantize_nvfp4
@@ -1514,7 +1577,7 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   if (!empty && (!x || !codes || !scales)) return FP4Q_ERR_NULL;
   if (loss != FP4Q_MSE && loss != FP4Q_WMSE) return FP4Q_ERR_ARG;
   if (loss == FP4Q_WMSE && !importance && !empty) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (block != 32) return FP4Q_ERR_SHAPE;
   if (off_lo > 0 || off_hi < 0 || off_lo < -16 || off_hi > 16) return FP4Q_ERR_ARG;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, hadamard_n);
@@ -1525,10 +1588,11 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
 
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  // first kernel of the call: clears the status word, validates the importance
-  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, nullptr,
-                     (wmse && !empty) ? importance : nullptr, (wmse && !empty) ? (int)cols : 0, nullptr);
-  if (empty) return last_hip_status();
+  // the sweep is the call's only kernel and takes the status slot; an empty call gets a small kernel for it
+  if (empty) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
+    return last_hip_status();
+  }
 
   const int bpr = (int)(cols / 32);  // one lane per 32-element block
   SweepArgs a;
@@ -1546,7 +1610,8 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   a.partials = nullptr;
   a.n_partials = 0;
   a.given_scale = nullptr;
-  a.check_given = false;
+  a.check_inputs = true;  // no max pass read the importance
+  a.status_first = true;
   a.codes = codes;
   a.scales = scales;
   a.gscale_out = nullptr;
@@ -1577,7 +1642,7 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!x || !scales || !codes)) return FP4Q_ERR_NULL;
   if (!empty && format == FP4Q_NVFP4 && !global_scale) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (sub_block != 4 && sub_block != 8 && sub_block != 16 && !(sub_block == 32 && block == 32))
     return FP4Q_ERR_ARG;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, 0);
@@ -1587,10 +1652,11 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  // first kernel of the call: clears the status word, validates an NVFP4 global scale
-  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status,
-                     (format == FP4Q_NVFP4 && !empty) ? global_scale : nullptr, nullptr, 0, nullptr);
-  if (empty) return last_hip_status();
+  // the quantizer is the call's only kernel and takes the status slot; an empty call gets a small one
+  if (empty) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
+    return last_hip_status();
+  }
   const int cpr = (int)(cols / 16);
   const int total = (int)(rows * cpr);
   const int grid = ceil_div(total, kThreads);
@@ -1599,7 +1665,8 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
     auto go = [&](auto fmt_c, auto sub_c) {
       constexpr int FM = decltype(fmt_c)::value, SB = decltype(sub_c)::value;
       hipLaunchKernelGGL((relaxed_quant_kernel<T, FM, SB>), dim3(grid), dim3(kThreads), 0, s, (const T *)x, ld,
-                         cpr, (int)cols, total, scales, global_scale, coeffs, codes, dequant_out, status);
+                         cpr, (int)cols, total, scales, global_scale, coeffs, codes, dequant_out,
+                         Status{status, true});
     };
     auto with_sub = [&](auto fmt_c) {
       switch (sub_block) {
@@ -1626,7 +1693,7 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
                                          void *stream) {
   const bool empty = rows == 0 || cols == 0;
   if (!global_scale || (!empty && (!w || !hinv_chol || !codes || !scales))) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
   if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
   if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
@@ -1638,12 +1705,13 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   const bool given = flags & FP4Q_GIVEN_SCALE;
-  // the call's first kernel clears the status word: the global-max pass, or with a given scale (and
-  // for an empty matrix) the kernel that validates the scale
-  if (given || empty)
-    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, given ? global_scale : nullptr,
-                       nullptr, 0, given ? nullptr : global_scale);
-  if (empty) return last_hip_status();
+  // the call's first kernel takes the status slot: the global-max pass, or with a given scale the first
+  // batch kernel (which also validates the scale); an empty matrix gets a small kernel for it
+  if (empty) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, given ? global_scale : nullptr,
+                       given ? nullptr : global_scale);
+    return last_hip_status();
+  }
   if (!given) {
     uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
     const int n_partials = launch_amax(w, FP4Q_F32, rows, cols, ld, 0, amax_out(workspace, nullptr, 0), s);
@@ -1651,7 +1719,7 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
                        global_scale, status);
   }
   gptq_batches<FP4Q_NVFP4>(w, rows, cols, ld, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales,
-                           status, s);
+                           status, given, s);
   return last_hip_status();
 }
 
@@ -1661,7 +1729,7 @@ extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, i
                                          size_t workspace_bytes, void *stream) {
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!w || !hinv_chol || !codes || !scales)) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes) return FP4Q_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
   if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
@@ -1671,11 +1739,13 @@ extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, i
     return FP4Q_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
-  // first kernel of the call: clears the status word
-  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(kThreads), 0, s, status, nullptr, nullptr, 0, nullptr);
-  if (empty) return last_hip_status();
+  // the first batch kernel takes the status slot; an empty matrix gets a small kernel for it
+  if (empty) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
+    return last_hip_status();
+  }
   gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, hinv_chol, importance, nullptr, off_lo, off_hi, codes, scales,
-                           status, s);
+                           status, true, s);
   return last_hip_status();
 }
 

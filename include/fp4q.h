@@ -41,13 +41,16 @@
  *   - Errors in the arguments are returned synchronously, before anything is
  *     enqueued.  Errors in the data (non-finite x, negative or non-finite
  *     importance, an invalid given global scale) are found on the device:
- *     they set bits of the status word at byte 0 of the workspace
- *     (FP4Q_DATA_* below) and leave that call's outputs unspecified.  Every
- *     call that takes a workspace writes that word on its stream before any
- *     of its kernels can set a bit, so after the stream has finished the
- *     word holds exactly the data errors of the last call on that workspace
- *     (0: none).  A fresh, uninitialised workspace is fine.  Calls that
- *     overlap on one workspace (different streams) race on it.
+ *     they set bits of the status word, the uint32 at byte 0 of the
+ *     workspace (FP4Q_DATA_* below), and leave that call's outputs
+ *     unspecified.  After the stream has finished, the word holds exactly
+ *     the data errors of the last call on that workspace (0: none); a
+ *     fresh, uninitialised workspace is fine.  Bytes 4..7 hold a tag of
+ *     the call: the call's first kernel merges its bits into the 64-bit
+ *     slot under its dispatch ID (the packet's index in the hardware
+ *     queue), replacing a slot left by any earlier call, and later kernels
+ *     of the call add bits.  The workspace must be 8-byte aligned.  Calls
+ *     that overlap on one workspace (different streams) race on it.
  */
 #ifndef FP4Q_H
 #define FP4Q_H
@@ -75,10 +78,9 @@ typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
 
 /* flags of fp4q_quantize_nvfp4 */
 #define FP4Q_GIVEN_SCALE 0x1u /* read S from *global_scale instead of computing it */
-/* Add this call's data errors to the status word instead of replacing it:
- * no clearing kernel runs first (a call with a given scale then launches its
- * sweep kernel alone).  For chains of calls on one stream that check the
- * word once at the end; the caller zeroes the word before the chain. */
+/* Add this call's data errors to the status word instead of replacing it,
+ * for chains of calls on one stream that check the word once at the end
+ * (the caller zeroes the word before the chain). */
 #define FP4Q_ACCUMULATE_STATUS 0x2u
 
 /* bits of the device status word (uint32 at byte 0 of the workspace) */
@@ -95,8 +97,8 @@ int fp4q_version(void);
 const char *fp4q_status_string(fp4q_status_t status);
 
 /* Bytes of device workspace every quantize call needs (a constant).  Bytes
- * 0..3 hold the status word of the last call (written by every call on its
- * stream); the rest is scratch the library overwrites. */
+ * 0..3 hold the status word of the last call, 4..7 that call's tag; the
+ * rest is scratch the library overwrites. */
 size_t fp4q_workspace_bytes(void);
 
 /*
@@ -153,9 +155,10 @@ fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, int64_t row
  *
  * Same arguments, computation, errors and results as fp4q_quantize_nvfp4,
  * except that the workspace is replaced by:
- *   status  [1] uint32 device word (out): the call's data errors
- *           (FP4Q_DATA_* bits), written on the stream like the workspace's
- *           status word (with FP4Q_ACCUMULATE_STATUS the call adds to it).
+ *   status  [2] uint32 device words, 8-byte aligned (out): word 0 receives
+ *           the call's data errors (FP4Q_DATA_* bits) and word 1 its tag,
+ *           exactly like bytes 0..7 of the workspace (with
+ *           FP4Q_ACCUMULATE_STATUS the call adds to word 0).
  * The global-max pass keeps its per-workgroup partials in a static device
  * array of the library instead, fp4q_noalloc_scratch_bytes() = 1 KiB per
  * GPU, held until the process ends.  That is the most the pass ever writes

@@ -857,6 +857,14 @@ def test_status_word_belongs_to_the_last_call():
     b = fq.quantize_nvfp4(x, imp, global_scale=S)
     for f in ("codes", "scales", "block_loss", "offsets"):
         assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # the slot's tag (bytes 4..7) is the dispatch ID of each call's first kernel: it changes per call
+    ws = torch.zeros(fq.workspace(DEV).numel(), dtype=torch.uint8, device=DEV)
+    tags = []
+    for _ in range(3):
+        fq.quantize_mxfp4(x, ws=ws)
+        torch.cuda.synchronize()
+        tags.append(int(ws[4:8].view(torch.int32).item()))
+    assert len(set(tags)) == 3 and fq.read_status(ws) == 0
     # empty tensors clear it too
     ws = torch.full((fq.workspace(DEV).numel(),), 0xFF, dtype=torch.uint8, device=DEV)
     fq.quantize_nvfp4(x[:0], ws=ws)

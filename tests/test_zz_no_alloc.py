@@ -39,7 +39,7 @@ def _assert_same(a, b):
                                             (torch.bfloat16, 16, True), (torch.float32, 128, False)])
 def test_noalloc_matches_workspace_call_twice(dtype, had, wmse):
     fq = _fq()
-    status = torch.full((1,), -1, dtype=torch.int32, device=DEV)   # garbage: the call writes it
+    status = torch.full((2,), -1, dtype=torch.int32, device=DEV)   # garbage: the call writes it
     for rows, cols, seed in ((300, 4096, 1), (37, 1024, 2)):       # the second call is smaller
         x = W.random_matrix(rows, cols, seed=seed, dist="t4", dtype=dtype).to(DEV)
         imp = W.random_importance(cols, seed=seed + 10).to(DEV) if wmse else None
@@ -50,31 +50,31 @@ def test_noalloc_matches_workspace_call_twice(dtype, had, wmse):
         assert torch.cuda.memory_allocated() == before
         torch.cuda.synchronize()
         _assert_same(out, ref)
-        assert int(status.item()) == 0
+        assert int(status[0].item()) == 0
         # with the scale given
         out2 = _empty_result(fq, rows, cols)
         out2.global_scale.copy_(ref.global_scale)
         fq.quantize_nvfp4_noalloc(x, imp, hadamard_n=had, out=out2, status=status, given_scale=True)
         torch.cuda.synchronize()
         _assert_same(out2, ref)
-        assert int(status.item()) == 0
+        assert int(status[0].item()) == 0
 
 
 def test_noalloc_status_and_scratch_size():
     fq = _fq()
     lib = fq._lib.load()
     assert lib.fp4q_noalloc_scratch_bytes() == 1024
-    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    status = torch.zeros(2, dtype=torch.int32, device=DEV)
     x = W.random_matrix(64, 512, seed=5).to(DEV)
     bad = x.clone()
     bad[3, 100] = float("inf")
     out = _empty_result(fq, 64, 512)
     fq.quantize_nvfp4_noalloc(bad, out=out, status=status)
     torch.cuda.synchronize()
-    assert int(status.item()) & 0x1
+    assert int(status[0].item()) & 0x1
     fq.quantize_nvfp4_noalloc(x, out=out, status=status)
     torch.cuda.synchronize()
-    assert int(status.item()) == 0
+    assert int(status[0].item()) == 0
     # a NULL status is refused before anything is enqueued
     assert lib.fp4q_quantize_nvfp4_noalloc(
         x.data_ptr(), fq._lib.F32, 64, 512, 512, None, 16, fq._lib.MSE, -3, 7, 0, 0, out.codes.data_ptr(),
@@ -90,7 +90,7 @@ def test_noalloc_in_a_captured_graph():
     x = W.random_matrix(rows, cols, seed=7, dist="t4", dtype=torch.bfloat16).to(DEV)
     imp = W.random_importance(cols, seed=8).to(DEV)
     out = _empty_result(fq, rows, cols)
-    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    status = torch.zeros(2, dtype=torch.int32, device=DEV)
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         fq.quantize_nvfp4_noalloc(x, imp, out=out, status=status)   # scratch address looked up eagerly
@@ -105,4 +105,4 @@ def test_noalloc_in_a_captured_graph():
         g.replay()
         torch.cuda.synchronize()
         _assert_same(out, ref)
-        assert int(status.item()) == 0
+        assert int(status[0].item()) == 0
