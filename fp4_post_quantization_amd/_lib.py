@@ -4,7 +4,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfp4q.so")
+# the in-tree build; FP4Q_LIBRARY names another build of the same sources (e.g. the host-sanitized
+# checking build of build.py --host-sanitize)
+LIB_PATH = os.environ.get("FP4Q_LIBRARY") or os.path.join(_PKG, "libfp4q.so")
 
 # status codes
 OK, ERR_NULL, ERR_SHAPE, ERR_ARG, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP = range(7)

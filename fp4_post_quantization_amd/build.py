@@ -28,17 +28,35 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", LIB + ".tmp"]
+# Host-code sanitizers (AddressSanitizer, UndefinedBehaviorSanitizer) for a
+# checking build: each flag applies to the host pass only, the device code is
+# compiled as usual.  The result needs the sanitizer runtime preloaded, e.g.
+#   LD_PRELOAD=$(/opt/rocm/bin/hipcc -print-file-name=libclang_rt.asan-x86_64.so)
+HOST_SANITIZE = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan"]
+
+
+def build(verbose=False, out=None, host_sanitize=False):
+    """Compile libfp4q.so in place (or to ``out``); host_sanitize builds the
+    checking variant described above, which must not replace the library."""
+    target = out or LIB
+    if host_sanitize and os.path.abspath(target) == LIB:
+        raise ValueError("the host-sanitized build goes to a path of its own")
+    flags = FLAGS + (HOST_SANITIZE if host_sanitize else [])
+    cmd = [HIPCC, *flags, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", target + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libfp4q.so")
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+        raise RuntimeError("hipcc failed building " + target)
+    os.replace(target + ".tmp", target)
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--host-sanitize", metavar="OUT", help="build the host-sanitized checking library at OUT")
+    a = ap.parse_args()
+    print(build(verbose=True, out=a.host_sanitize, host_sanitize=bool(a.host_sanitize)))

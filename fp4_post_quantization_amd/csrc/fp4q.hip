@@ -1483,12 +1483,12 @@ extern "C" fp4q_status_t fp4q_quantize_nvfp4(const void *x, fp4q_dtype_t dtype, 
                                              uint32_t flags, uint8_t *codes, uint8_t *scales,
                                              float *global_scale, float *block_loss, int8_t *offsets,
                                              void *workspace, size_t workspace_bytes, void *stream) {
-  char *ws = (char *)workspace;
+  const bool ws_ok = workspace && workspace_bytes >= kWorkspaceBytes && aligned(workspace, 8);
+  char *ws = (char *)workspace;  // offsets into it only once it is known to be there
   return quantize_nvfp4_on(x, dtype, rows, cols, ld, importance, block, loss, off_lo, off_hi, hadamard_n, flags,
-                           codes, scales, global_scale, block_loss, offsets,
-                           workspace && workspace_bytes >= kWorkspaceBytes && aligned(workspace, 8),
-                           (uint32_t *)(ws + kWsStatus),
-                           (uint32_t *)(ws + kWsPartials), (hipStream_t)stream);
+                           codes, scales, global_scale, block_loss, offsets, ws_ok,
+                           ws_ok ? (uint32_t *)(ws + kWsStatus) : nullptr,
+                           ws_ok ? (uint32_t *)(ws + kWsPartials) : nullptr, (hipStream_t)stream);
 }
 
 // ------------------------------------------------ no-allocation variant ----

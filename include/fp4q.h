@@ -72,9 +72,27 @@ typedef enum fp4q_status {
   FP4Q_ERR_HIP = 6        /* a kernel launch failed (hipGetLastError) */
 } fp4q_status_t;
 
-typedef enum fp4q_dtype { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype_t;
-typedef enum fp4q_loss { FP4Q_MSE = 0, FP4Q_WMSE = 1 } fp4q_loss_t;
-typedef enum fp4q_format { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1 } fp4q_format_t;
+/* The *_INT_MIN_ / *_INT_MAX_ enumerators are not values to pass: they make
+ * every int a valid value of the enum, so an out-of-range value a caller
+ * passes reaches the library's argument checks (FP4Q_ERR_ARG). */
+typedef enum fp4q_dtype {
+  FP4Q_F32 = 0,
+  FP4Q_BF16 = 1,
+  FP4Q_DTYPE_INT_MIN_ = -2147483647 - 1,
+  FP4Q_DTYPE_INT_MAX_ = 2147483647
+} fp4q_dtype_t;
+typedef enum fp4q_loss {
+  FP4Q_MSE = 0,
+  FP4Q_WMSE = 1,
+  FP4Q_LOSS_INT_MIN_ = -2147483647 - 1,
+  FP4Q_LOSS_INT_MAX_ = 2147483647
+} fp4q_loss_t;
+typedef enum fp4q_format {
+  FP4Q_NVFP4 = 0,
+  FP4Q_MXFP4 = 1,
+  FP4Q_FORMAT_INT_MIN_ = -2147483647 - 1,
+  FP4Q_FORMAT_INT_MAX_ = 2147483647
+} fp4q_format_t;
 
 /* flags of fp4q_quantize_nvfp4 */
 #define FP4Q_GIVEN_SCALE 0x1u /* read S from *global_scale instead of computing it */
