@@ -1119,8 +1119,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 
 // Trailing update W[:, c] -= E * U[i1:i1+kn, c] for the columns c from cbeg
 // on (blockIdx.y selects 64 of them), with E = W[:, i1:i1+kn] the scaled
-// errors of kn already quantized columns (one batch of 128, or a block of
-// 1024): a dense contraction on fp32 MFMA (32x32x2).  A workgroup computes a 64 x 64 tile, each wave a
+// errors of kn already quantized columns: the near update (one batch of 128
+// columns onto the rest of its block) as a dense contraction on fp32 MFMA
+// (32x32x2).  With K = 128 it is short and latency-bound, where small tiles
+// keep enough workgroups in flight.  A workgroup computes a 64 x 64 tile, each wave a
 // 32 x 32 sub-tile whose 16 accumulator rows per lane are read from W at the
 // start (their HBM latency then hides behind the contraction instead of
 // stalling the epilogue).  E and U are staged through LDS in K chunks of 32:
@@ -1194,6 +1196,146 @@ __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict
     const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
     if (row < rows) W[(int64_t)row * ld + c0 + wc * 32 + lr] = cur[v] - acc[v];
   }
+}
+
+// The far update (a block's 1024 error columns against all later columns) on the bf16 matrix cores
+// at fp32-class accuracy.  Every fp32 operand x is split exactly into three bf16 parts by round to
+// nearest even, x = h + m + l: x - h and (x - h) - m are exact in fp32, |m| <= 2^-8 |x|,
+// |l| <= 2^-16 |x|, and l fits bf16's 8-bit significand.  Of the nine part products the kernel keeps
+// the six down to order 2^-16 (hh, hm, mh, hl, mm, lh); the three it drops (ml, lm, ll) add up to at
+// most about 2^-23 |a b| per product, the size of an fp32 product's own rounding.  bf16 products are
+// exact in the MFMA's fp32 accumulation, so the result matches an fp32 contraction to within fp32
+// summation error, at six bf16 MFMAs (32x32x16) where fp32 needs eight (32x32x2) at a sixteenth of
+// the rate.  A 128 x 128 workgroup tile; K in stages of 16 (one bf16 MFMA step).  Each stage's E
+// and U values are split once as they go from registers into LDS: E row-major, U column-major, each
+// part its own [128][24] bf16 array, so an operand is one 16-byte read and the 48-byte rows put 16
+// consecutive lanes on distinct banks.  Finite operands below 2^127 (h must not round to infinity).
+constexpr int kSplitKc = 16;   // K elements per stage
+constexpr int kSplitRow = 24;  // bf16 per staged row (16 + 8 padding)
+constexpr int kSplitWaves = 8;  // measured faster than 4 waves (2 x 2 blocks each) at every far-update size
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+// Two floats to their three bf16 parts, each pair packed low element first.
+__device__ __forceinline__ void split_bf16x3(float x0, float x1, uint32_t &h, uint32_t &m, uint32_t &l) {
+  h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x0, x1}), bf16x2v));
+  const float r0 = x0 - as_f(h << 16), r1 = x1 - as_f(h & 0xFFFF0000u);
+  m = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{r0, r1}), bf16x2v));
+  const float s0 = r0 - as_f(m << 16), s1 = r1 - as_f(m & 0xFFFF0000u);
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{s0, s1}), bf16x2v));
+}
+
+// NW waves per workgroup: 4 (each wave a 2 x 2 grid of 32 x 32 blocks) or 8 (each wave 1 x 2).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__restrict__ W, int64_t ld, int rows,
+                                                                    int cols, int i1, int kn, int cbeg,
+                                                                    const float *__restrict__ U) {
+  constexpr int BM = 128, BN = 128, NT = 64 * NW;
+  constexpr int WR = NW / 2, TI = 4 / WR, TJ = 2;  // wave grid WR x 2; blocks per wave TI x TJ
+  constexpr int EPT = BM * kSplitKc / NT;           // values per thread per operand per stage (8 or 4)
+  constexpr int NPC = EPT;                          // split pieces per stage (pairs of E, then of U)
+  constexpr int NMF = 6 * TI * TJ;                  // MFMAs per wave per stage
+  static_assert(NMF == 3 * NPC, "a piece after every third MFMA");
+  // [stage buffer][0: E rows, 1: U columns][part h, m, l][row or column][k]
+  __shared__ __attribute__((aligned(16))) uint16_t S[2][2][3][BM][kSplitRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.x * BM, c0 = cbeg + blockIdx.y * BN;
+  const int wr = wave % WR, wc = wave / WR;
+  const int lr = lane & 31, lk = lane >> 5;
+  // a stage: thread t takes EPT consecutive k of one E row and of U column t % 128
+  const int ar = tid / (kSplitKc / EPT), ak = EPT * (tid % (kSplitKc / EPT));
+  const int bc = tid % BN, bk = EPT * (tid / BN);
+  // rows past the end read row 0: a row of E only reaches the same row of the output, which is not
+  // stored
+  const float *asrc = W + (int64_t)(r0 + ar < rows ? r0 + ar : 0) * ld + i1 + ak;
+  const float *bsrc = U + (int64_t)(i1 + bk) * cols + c0 + bc;
+  // stage kc's raw values into a / b (kc is clamped by the caller, so every load is in bounds)
+  auto fetch = [&](int kc, float (&a)[EPT], float (&b)[EPT]) {
+#pragma unroll
+    for (int h = 0; h < EPT / 4; ++h) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(asrc + kc + 4 * h);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[4 * h + k] = v[k];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) b[k] = bsrc[(int64_t)(kc + k) * cols];
+  };
+  // split piece q of a stage (q < EPT / 2: E pair q, else U pair q - EPT / 2) into ph / pm / pl;
+  // after the last pair of each operand its parts are stored to LDS buffer buf
+  constexpr int NW2 = EPT / 2;
+  uint32_t ph[NW2], pm[NW2], pl[NW2];
+  auto store = [&](uint16_t *dst, const uint32_t (&v)[NW2]) {
+    if constexpr (NW2 == 4)
+      *reinterpret_cast<u32x4 *>(dst) = u32x4{v[0], v[1], v[2], v[3]};
+    else
+      *reinterpret_cast<uint2 *>(dst) = uint2{v[0], v[1]};
+  };
+  auto piece = [&](int q, int buf, const float (&a)[EPT], const float (&b)[EPT]) {
+    const float *x = q < NW2 ? a : b;
+    const int qq = q % NW2;
+    split_bf16x3(x[2 * qq], x[2 * qq + 1], ph[qq], pm[qq], pl[qq]);
+    if (qq == NW2 - 1) {
+      const int o = q < NW2 ? 0 : 1, rr = o ? bc : ar, kk = o ? bk : ak;
+      store(&S[buf][o][0][rr][kk], ph);
+      store(&S[buf][o][1][rr][kk], pm);
+      store(&S[buf][o][2][rr][kk], pl);
+    }
+  };
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{0};
+  // Software pipeline over stages of 16: while stage kc's MFMAs run from LDS buffer buf, stage
+  // kc + 16 (loaded one stage earlier into as / bs) is split into the other buffer, one piece after
+  // every third MFMA, and stage kc + 32 loads into an / bn.  Past the end the loads repeat the last
+  // stage and the split fills a buffer nobody reads.  Terms go small products first, each term
+  // across the wave's blocks in turn, so consecutive MFMAs never share an accumulator.
+  const int klast = kn - kSplitKc;
+  auto stage = [&](int kc, int buf, const float (&as)[EPT], const float (&bs)[EPT], float (&an)[EPT],
+                   float (&bn)[EPT]) {
+    fetch(min(kc + 2 * kSplitKc, klast), an, bn);
+    bf16x8v av[TI][3], bv[TJ][3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        av[i][2 - p] = *reinterpret_cast<const bf16x8v *>(&S[buf][0][2 - p][wr * 32 * TI + 32 * i + lr][8 * lk]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bv[j][p] = *reinterpret_cast<const bf16x8v *>(&S[buf][1][p][wc * 64 + 32 * j + lr][8 * lk]);
+    }
+    constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+    for (int g = 0; g < NMF; ++g) {
+      const int t = g / (TI * TJ), i = (g / TJ) % TI, j = g % TJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i][PA[t]], bv[j][PB[t]], acc[i][j], 0, 0, 0);
+      if (g % 3 == 2) piece(g / 3, buf ^ 1, as, bs);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+  float a0[EPT], b0[EPT], a1[EPT], b1[EPT];
+  fetch(0, a0, b0);
+#pragma unroll
+  for (int q = 0; q < NPC; ++q) piece(q, 0, a0, b0);
+  fetch(min(kSplitKc, klast), a0, b0);
+  __syncthreads();
+  for (int kc = 0; kc < kn; kc += 2 * kSplitKc) {  // kn is a multiple of 32
+    stage(kc, 0, a0, b0, a1, b1);
+    stage(kc + kSplitKc, 1, a1, b1, a0, b0);
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // accumulator v of block (i, j) in lane l: row 32 i + 8*(v/4) + 4*(l/32) + v%4, column 32 j + l%32
+        const int row = r0 + wr * 32 * TI + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
+        float *o = W + (int64_t)row * ld + c0 + wc * 64 + 32 * j + lr;
+        if (row < rows) *o = *o - acc[i][j][v];
+      }
 }
 
 // Decode of an arbitrary E4M3 byte (sign, 0x7F / 0xFF = NaN).
@@ -1308,11 +1450,11 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
     const int i2 = i1 + kGptqBatch;
     const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
     if (i2 < b1)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w, ld,
-                         (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
-    else if (b1 < cols)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), ((int)cols - b1) / 64), dim3(kThreads), 0, s,
-                         w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w,
+                         ld, (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
+    else if (b1 < cols)  // the far update (cols - b1 is a multiple of the 128-column tile)
+      hipLaunchKernelGGL(gptq_update_split_kernel<kSplitWaves>, dim3(ceil_div(rows, 128), ((int)cols - b1) / 128),
+                         dim3(64 * kSplitWaves), 0, s, w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
   }
 }
 

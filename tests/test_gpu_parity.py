@@ -706,15 +706,19 @@ def test_gptq_multi_batch_against_oracle(wmse):
     assert lg < lr and lo < lr
 
 
-def test_gptq_block_updates_against_oracle():
-    """2304 columns: two full 1024-column blocks, whose errors reach the later
-    columns as one contraction each, and a 256-column tail.  Same bar as the
-    multi-batch case."""
+@pytest.mark.parametrize("rows,cols,wmse", [(64, 2304, False), (200, 2176, True)])
+def test_gptq_block_updates_against_oracle(rows, cols, wmse):
+    """Past 1024 columns: each full 1024-column block's errors reach the later
+    columns as one contraction (on the bf16 matrix cores with operands split
+    in three), then the tail.  2304 columns: two blocks and a 256-column
+    tail; 2176: two blocks and a 128-column tail, on 200 rows (one full and
+    one ragged 128-row tile).  Same bar as the multi-batch case."""
     fq = _fp4()
-    w, H, U, imp = _gptq_inputs(64, 2304, seed=116)
-    res = fq.gptq_nvfp4(w.to(DEV), U, None, check=True)
+    w, H, U, imp = _gptq_inputs(rows, cols, seed=116 + rows)
+    im = imp if wmse else None
+    res = fq.gptq_nvfp4(w.to(DEV), U, None if im is None else im.to(DEV), check=True)
     torch.cuda.synchronize()
-    codes, scales, S = GQ.gptq_nvfp4(w.numpy(), U, None)
+    codes, scales, S = GQ.gptq_nvfp4(w.numpy(), U, None if im is None else im.numpy())
     gc, gs = _np(res.codes), _np(res.scales)
     assert np.float32(_np(res.global_scale)[0]) == S
     code_mis = np.mean(Q.unpack_nibbles(gc) != Q.unpack_nibbles(codes))
@@ -753,7 +757,8 @@ def test_gptq_mxfp4_without_feedback_equals_sweep():
         _assert_equal("scales", _np(g.scales), _np(s_.scales))
 
 
-@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (192, 512, True), (64, 2304, False)])
+@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (192, 512, True), (64, 2304, False),
+                                             (200, 2176, True)])
 def test_gptq_mxfp4_multi_batch_against_oracle(rows, cols, wmse):
     """MXFP4 GPTQ across batches (and, at 2304 columns, across 1024-column
     blocks): the same bar as NVFP4 GPTQ."""
