@@ -374,7 +374,8 @@ def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *,
         raise ValueError("w must be a 2-D device tensor")
     rows, cols = w.shape
     dev = w.device
-    work = w.to(torch.float32).contiguous().clone()
+    work = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    work.copy_(w)  # one pass: the float32 working copy, whatever w's dtype and strides
     U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
     if U.shape != (cols, cols):
         raise ValueError("hinv_chol must be [cols, cols]")
@@ -411,7 +412,8 @@ def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=
         raise ValueError("w must be a 2-D device tensor")
     rows, cols = w.shape
     dev = w.device
-    work = w.to(torch.float32).contiguous().clone()
+    work = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    work.copy_(w)  # one pass: the float32 working copy, whatever w's dtype and strides
     U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
     if U.shape != (cols, cols):
         raise ValueError("hinv_chol must be [cols, cols]")

@@ -1208,10 +1208,19 @@ __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict
 // summation error, at six bf16 MFMAs (32x32x16) where fp32 needs eight (32x32x2) at a sixteenth of
 // the rate.  A 128 x 128 workgroup tile; K in stages of 16 (one bf16 MFMA step).  Each stage's E
 // and U values are split once as they go from registers into LDS: E row-major, U column-major, each
-// part its own [128][24] bf16 array, so an operand is one 16-byte read and the 48-byte rows put 16
-// consecutive lanes on distinct banks.  Finite operands below 2^127 (h must not round to infinity).
-constexpr int kSplitKc = 16;   // K elements per stage
-constexpr int kSplitRow = 24;  // bf16 per staged row (16 + 8 padding)
+// part its own [128][KC] bf16 array, so an operand is one 16-byte read.  A row's 16-byte chunks are
+// permuted by an XOR with bits of the row index, which puts 16 consecutive rows' reads of one chunk,
+// and the stores, on distinct banks.  Finite operands below 2^127 (h must not round to infinity).
+// K elements per stage: one bf16 MFMA step.  Stages of 32 (two steps per barrier) need 96 KB of LDS,
+// one workgroup per CU, and measured slower.
+constexpr int kSplitKc = 16;
+// offset in bf16 of element k (0..KC-1) of row r in a staged part array of KC-element rows
+template <int KC>
+__device__ __forceinline__ int split_idx(int r, int k) {
+  constexpr int NC = KC / 8, SH = NC == 2 ? 3 : 2;  // 16-byte chunks per row; row bits that permute them
+  static_assert(NC == 2 || NC == 4, "16- or 32-element rows");
+  return KC * r + 8 * ((k >> 3) ^ ((r >> SH) & (NC - 1))) + (k & 7);
+}
 constexpr int kSplitWaves = 8;  // measured faster than 4 waves (2 x 2 blocks each) at every far-update size
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -1225,26 +1234,28 @@ __device__ __forceinline__ void split_bf16x3(float x0, float x1, uint32_t &h, ui
   l = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{s0, s1}), bf16x2v));
 }
 
-// NW waves per workgroup: 4 (each wave a 2 x 2 grid of 32 x 32 blocks) or 8 (each wave 1 x 2).
-template <int NW>
+// NW waves per workgroup: 4 (each wave a 2 x 2 grid of 32 x 32 blocks) or 8 (each wave 1 x 2); KC K
+// elements per stage (16 or 32).
+template <int NW, int KC>
 __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__restrict__ W, int64_t ld, int rows,
                                                                     int cols, int i1, int kn, int cbeg,
                                                                     const float *__restrict__ U) {
-  constexpr int BM = 128, BN = 128, NT = 64 * NW;
+  constexpr int BM = 128, BN = 128, NT = 64 * NW, KS = KC / 16;
   constexpr int WR = NW / 2, TI = 4 / WR, TJ = 2;  // wave grid WR x 2; blocks per wave TI x TJ
-  constexpr int EPT = BM * kSplitKc / NT;           // values per thread per operand per stage (8 or 4)
+  constexpr int EPT = BM * KC / NT;                 // values per thread per operand per stage
   constexpr int NPC = EPT;                          // split pieces per stage (pairs of E, then of U)
-  constexpr int NMF = 6 * TI * TJ;                  // MFMAs per wave per stage
+  constexpr int NMF = 6 * TI * TJ * KS;             // MFMAs per wave per stage
   static_assert(NMF == 3 * NPC, "a piece after every third MFMA");
-  // [stage buffer][0: E rows, 1: U columns][part h, m, l][row or column][k]
-  __shared__ __attribute__((aligned(16))) uint16_t S[2][2][3][BM][kSplitRow];
+  static_assert(EPT == 4 || EPT % 8 == 0, "a thread's parts are stored as 8-byte or 16-byte chunks");
+  // [stage buffer][0: E rows, 1: U columns][part h, m, l][row or column, k] (split_idx)
+  __shared__ __attribute__((aligned(16))) uint16_t S[2][2][3][BM * KC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.x * BM, c0 = cbeg + blockIdx.y * BN;
   const int wr = wave % WR, wc = wave / WR;
   const int lr = lane & 31, lk = lane >> 5;
-  // a stage: thread t takes EPT consecutive k of one E row and of U column t % 128
-  const int ar = tid / (kSplitKc / EPT), ak = EPT * (tid % (kSplitKc / EPT));
-  const int bc = tid % BN, bk = EPT * (tid / BN);
+  // a stage: thread t takes EPT consecutive k of E row t / (KC / EPT) and of U column t / (KC / EPT)
+  const int ar = tid / (KC / EPT), ak = EPT * (tid % (KC / EPT));
+  const int bc = ar, bk = ak;
   // rows past the end read row 0: a row of E only reaches the same row of the output, which is not
   // stored
   const float *asrc = W + (int64_t)(r0 + ar < rows ? r0 + ar : 0) * ld + i1 + ak;
@@ -1264,11 +1275,15 @@ __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__res
   // after the last pair of each operand its parts are stored to LDS buffer buf
   constexpr int NW2 = EPT / 2;
   uint32_t ph[NW2], pm[NW2], pl[NW2];
-  auto store = [&](uint16_t *dst, const uint32_t (&v)[NW2]) {
-    if constexpr (NW2 == 4)
-      *reinterpret_cast<u32x4 *>(dst) = u32x4{v[0], v[1], v[2], v[3]};
-    else
-      *reinterpret_cast<uint2 *>(dst) = uint2{v[0], v[1]};
+  auto store = [&](uint16_t *part, int rr, int kk, const uint32_t (&v)[NW2]) {
+    if constexpr (NW2 == 2) {
+      *reinterpret_cast<uint2 *>(part + split_idx<KC>(rr, kk)) = uint2{v[0], v[1]};
+    } else {
+#pragma unroll
+      for (int h = 0; h < NW2 / 4; ++h)
+        *reinterpret_cast<u32x4 *>(part + split_idx<KC>(rr, kk + 8 * h)) =
+            u32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+    }
   };
   auto piece = [&](int q, int buf, const float (&a)[EPT], const float (&b)[EPT]) {
     const float *x = q < NW2 ? a : b;
@@ -1276,9 +1291,9 @@ __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__res
     split_bf16x3(x[2 * qq], x[2 * qq + 1], ph[qq], pm[qq], pl[qq]);
     if (qq == NW2 - 1) {
       const int o = q < NW2 ? 0 : 1, rr = o ? bc : ar, kk = o ? bk : ak;
-      store(&S[buf][o][0][rr][kk], ph);
-      store(&S[buf][o][1][rr][kk], pm);
-      store(&S[buf][o][2][rr][kk], pl);
+      store(S[buf][o][0], rr, kk, ph);
+      store(S[buf][o][1], rr, kk, pm);
+      store(S[buf][o][2], rr, kk, pl);
     }
   };
   f32x16 acc[TI][TJ];
@@ -1286,30 +1301,35 @@ __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__res
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16{0};
-  // Software pipeline over stages of 16: while stage kc's MFMAs run from LDS buffer buf, stage
-  // kc + 16 (loaded one stage earlier into as / bs) is split into the other buffer, one piece after
-  // every third MFMA, and stage kc + 32 loads into an / bn.  Past the end the loads repeat the last
+  // Software pipeline over stages of KC: while stage kc's MFMAs run from LDS buffer buf, stage
+  // kc + KC (loaded one stage earlier into as / bs) is split into the other buffer, one piece after
+  // every third MFMA, and stage kc + 2 KC loads into an / bn.  Past the end the loads repeat the last
   // stage and the split fills a buffer nobody reads.  Terms go small products first, each term
   // across the wave's blocks in turn, so consecutive MFMAs never share an accumulator.
-  const int klast = kn - kSplitKc;
+  const int klast = kn - KC;
   auto stage = [&](int kc, int buf, const float (&as)[EPT], const float (&bs)[EPT], float (&an)[EPT],
                    float (&bn)[EPT]) {
-    fetch(min(kc + 2 * kSplitKc, klast), an, bn);
-    bf16x8v av[TI][3], bv[TJ][3];
+    fetch(min(kc + 2 * KC, klast), an, bn);
+    bf16x8v av[KS][TI][3], bv[KS][TJ][3];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        av[i][2 - p] = *reinterpret_cast<const bf16x8v *>(&S[buf][0][2 - p][wr * 32 * TI + 32 * i + lr][8 * lk]);
+      for (int p = 0; p < 3; ++p) {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        bv[j][p] = *reinterpret_cast<const bf16x8v *>(&S[buf][1][p][wc * 64 + 32 * j + lr][8 * lk]);
-    }
+        for (int i = 0; i < TI; ++i)
+          av[ks][i][2 - p] = *reinterpret_cast<const bf16x8v *>(
+              &S[buf][0][2 - p][split_idx<KC>(wr * 32 * TI + 32 * i + lr, 16 * ks + 8 * lk)]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          bv[ks][j][p] = *reinterpret_cast<const bf16x8v *>(
+              &S[buf][1][p][split_idx<KC>(wc * 64 + 32 * j + lr, 16 * ks + 8 * lk)]);
+      }
     constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
     for (int g = 0; g < NMF; ++g) {
-      const int t = g / (TI * TJ), i = (g / TJ) % TI, j = g % TJ;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i][PA[t]], bv[j][PB[t]], acc[i][j], 0, 0, 0);
+      const int ks = g / (6 * TI * TJ), t = (g / (TI * TJ)) % 6, i = (g / TJ) % TI, j = g % TJ;
+      acc[i][j] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][i][PA[t]], bv[ks][j][PB[t]], acc[i][j], 0, 0, 0);
       if (g % 3 == 2) piece(g / 3, buf ^ 1, as, bs);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1319,11 +1339,11 @@ __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__res
   fetch(0, a0, b0);
 #pragma unroll
   for (int q = 0; q < NPC; ++q) piece(q, 0, a0, b0);
-  fetch(min(kSplitKc, klast), a0, b0);
+  fetch(min(KC, klast), a0, b0);
   __syncthreads();
-  for (int kc = 0; kc < kn; kc += 2 * kSplitKc) {  // kn is a multiple of 32
+  for (int kc = 0; kc < kn; kc += 2 * KC) {  // kn is a multiple of 2 KC
     stage(kc, 0, a0, b0, a1, b1);
-    stage(kc + kSplitKc, 1, a1, b1, a0, b0);
+    stage(kc + KC, 1, a1, b1, a0, b0);
   }
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -1453,8 +1473,9 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
       hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w,
                          ld, (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
     else if (b1 < cols)  // the far update (cols - b1 is a multiple of the 128-column tile)
-      hipLaunchKernelGGL(gptq_update_split_kernel<kSplitWaves>, dim3(ceil_div(rows, 128), ((int)cols - b1) / 128),
-                         dim3(64 * kSplitWaves), 0, s, w, ld, (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
+      hipLaunchKernelGGL((gptq_update_split_kernel<kSplitWaves, kSplitKc>),
+                         dim3(ceil_div(rows, 128), ((int)cols - b1) / 128), dim3(64 * kSplitWaves), 0, s, w, ld,
+                         (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
   }
 }
 
