@@ -81,18 +81,26 @@ WORKLOADS = {
     "c3b": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
-    # GPTQ: per-dispatch bytes averaged over the 31 updates of a call (1024-column blocks of eight
-    # 128-column batches): 28 in-block updates (the rest of the block, r = 896 ... 128 columns: read
-    # and write W[:, rest], read the batch's errors and U[batch, rest]) and 3 block updates (all later
-    # columns, L = 3072, 2048, 1024, with the block's 1024 error columns and U[block, later]); and the
-    # 32 batch kernels (read and write 128 columns, write codes and scales, read U's 128 x 128 block)
-    "gptq": {"stem": "gptq_nvfp4_f32_4096x4096", "kernel": "gptq_update_kernel",
+    # GPTQ on 4096 x 4096 (1024-column blocks of eight 128-column batches).  Per dispatch, averaged
+    # over a call: the 28 near updates (the rest of the block, r = 896 ... 128 columns: read and write
+    # W[:, rest], read the batch's errors and U[batch, rest]; fp32 MFMA), the 3 far updates (all later
+    # columns, L = 3072, 2048, 1024, with the block's 1024 error columns and U[block, later]; bf16 MFMA
+    # on operands split in three, six bf16 products per fp32 product) and the 32 batch kernels (read
+    # and write 128 columns, write codes and scales, read U's 128 x 128 block)
+    "gptq": {"stem": "gptq_nvfp4_f32_4096x4096", "kernel": "gptq_update_split_kernel",
              "title": "GPTQ with ScaleSweep group scales, fp32 4096x4096, MSE and WMSE",
-             "alg_bytes": {"gptq_update_kernel": (sum(4 * (4096 * r * 8 + 4096 * 128 * 4 + 128 * r * 4)
-                                                      for r in range(128, 1024, 128))
-                                                  + sum(4096 * L * 8 + 4096 * 1024 * 4 + 1024 * L * 4
-                                                        for L in (1024, 2048, 3072))) / 31,
-                           "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4}},
+             "alg_bytes": {"gptq_update_kernel": sum(4 * (4096 * r * 8 + 4096 * 128 * 4 + 128 * r * 4)
+                                                     for r in range(128, 1024, 128)) / 28,
+                           "gptq_update_split_kernel": sum(4096 * L * 8 + 4096 * 1024 * 4 + 1024 * L * 4
+                                                           for L in (1024, 2048, 3072)) / 3,
+                           "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4},
+             "alg_flops": {"gptq_update_kernel": sum(4 * 2 * 4096 * 128 * r for r in range(128, 1024, 128)) / 28,
+                           "gptq_update_split_kernel": sum(6 * 2 * 4096 * 1024 * L for L in (1024, 2048, 3072)) / 3},
+             "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
+             "peak_tflops": {"gptq_update_kernel": 157.3, "gptq_update_split_kernel": 2500.0},
+             "peak_label": "the published dense figure of the kernel's MFMA type: fp32 157.3 TFLOP/s for the "
+                           "near update, bf16 2500 TFLOP/s for the far update, whose flops count its six bf16 "
+                           "products per fp32 product"},
     # W4A4 8B layer at 8192 tokens.  Per GEMM dispatch: A (codes + scales) + B (codes + scales)
     # + C (bf16), flops 2 M N K, averaged over the projections each kernel instantiation serves
     # (256 x 256 tiles: q, o, gate, up, down; 128 x 128 tiles: k, v).  The activation quantizer
@@ -307,25 +315,28 @@ def summarize(config, in_dir, profiles):
                       "traffic_bytes": hbm, "alg_bytes": alg, "valu_issue": issue, "valu_busy_pct": busy,
                       "source_sha256": source_hash(config)}
     if w.get("alg_flops"):
+        one_peak = not isinstance(w["peak_tflops"], dict)
+        peak_note = f" ({w['peak_tflops']:.0f} TFLOP/s at 2.4 GHz)" if one_peak else ""
         lines += ["", "## Matrix cores", "",
                   f"Achieved = mean algorithmic flops per dispatch / average duration; peak = "
-                  f"{w.get('peak_label', 'the published dense figure')} ({w['peak_tflops']:.0f} TFLOP/s at "
-                  f"2.4 GHz).  MFMA busy share = "
+                  f"{w.get('peak_label', 'the published dense figure')}{peak_note}.  MFMA busy share = "
                   "SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCDs); cycles per MFMA = "
                   "SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA.", "",
                   "| kernel | flops per dispatch | achieved TFLOP/s | of peak | MFMA insts | cycles per MFMA | "
                   "MFMA busy share | GPU clock (GRBM) |", "|---|---|---|---|---|---|---|---|"]
         for name, avg_us in durations.items():
-            fl = w["alg_flops"].get(_short(name))
+            base = _short(name).split("<")[0]
+            fl = w["alg_flops"].get(_short(name), w["alg_flops"].get(base))
             if fl is None:
                 continue
+            peak = w["peak_tflops"].get(base) if isinstance(w["peak_tflops"], dict) else w["peak_tflops"]
             mi = pick(valu, name, "SQ_INSTS_MFMA")
             mb = pick(valu, name, "SQ_VALU_MFMA_BUSY_CYCLES")
             grbm = pick(valu, name, "GRBM_GUI_ACTIVE")
             tf = fl / (avg_us * 1e-6) / 1e12
             share = mb[0] / (simds * grbm[0] / xcc) if (mb and grbm) else None
             cpm = mb[0] / mi[0] if (mb and mi and mi[0]) else None
-            lines.append(f"| `{_short(name)}` | {fl:.4g} | {tf:.0f} | {100 * tf / w['peak_tflops']:.1f}% | "
+            lines.append(f"| `{_short(name)}` | {fl:.4g} | {tf:.0f} | {100 * tf / peak:.1f}% | "
                          f"{'' if mi is None else f'{mi[0]:.4g}'} | {'' if cpm is None else f'{cpm:.1f}'} | "
                          f"{'' if share is None else f'{100 * share:.1f}%'} | counter-run cycles "
                          f"{'' if grbm is None else f'{grbm[0] / xcc:.4g}'} per XCD |")
