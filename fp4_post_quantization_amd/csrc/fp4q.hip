@@ -1449,9 +1449,13 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
 }
 
 // The GPTQ batches of either format: per 128-column batch the batch kernel,
-// then the two-level lazy update (the rest of this block of kGptqBlock
-// columns with the batch's 128 error columns; after the block's last batch,
-// all later columns with the block's error columns as one contraction).
+// then the lazy updates.  Within a block of kGptqBlock columns they follow a
+// binary tree: after batch t of the block, with m the lowest set bit of t + 1,
+// the last m batches' errors go to the next m batches' columns (m = 1, 2, 1,
+// 4, 1, 2, 1: every column still gets every earlier batch's errors before its
+// own batch, with the same flops as updating the whole rest of the block
+// after every batch, in fewer wide launches).  After the block's last batch,
+// all later columns get the block's error columns as one contraction.
 template <int FMT>
 static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
                          const float *importance, const float *global_scale, int off_lo, int off_hi, uint8_t *codes,
@@ -1469,9 +1473,13 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
                          status);
     const int i2 = i1 + kGptqBatch;
     const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
+    // batch t of the block (m = the lowest set bit of t + 1): the last m batches' errors onto the
+    // next m batches' columns
+    const int tb = (i1 - b0) / kGptqBatch, m = (tb + 1) & -(tb + 1);
+    const int e2 = std::min(b1, i2 + m * kGptqBatch);
     if (i2 < b1)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (b1 - i2) / 64), dim3(kThreads), 0, s, w,
-                         ld, (int)rows, (int)cols, i1, kGptqBatch, i2, hinv_chol);
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (e2 - i2) / 64), dim3(kThreads), 0, s, w,
+                         ld, (int)rows, (int)cols, i2 - m * kGptqBatch, m * kGptqBatch, i2, hinv_chol);
     else if (b1 < cols)  // the far update (cols - b1 is a multiple of the 128-column tile)
       hipLaunchKernelGGL((gptq_update_split_kernel<kSplitWaves, kSplitKc>),
                          dim3(ceil_div(rows, 128), ((int)cols - b1) / 128), dim3(64 * kSplitWaves), 0, s, w, ld,

@@ -683,13 +683,16 @@ def test_gptq_without_feedback_equals_sweep():
 
 
 @pytest.mark.parametrize("wmse", [False, True])
-def test_gptq_multi_batch_against_oracle(wmse):
+@pytest.mark.parametrize("rows,cols", [(192, 512), (96, 768)])
+def test_gptq_multi_batch_against_oracle(wmse, rows, cols):
     """Across batches the trailing update is an MFMA contraction whose
     summation order differs from the oracle's float64 product, so values
     agree to float32 rounding: code and scale mismatch rates <= 1e-3, GPTQ
-    proxy losses within 1e-3 relative, and both below round-to-nearest."""
+    proxy losses within 1e-3 relative, and both below round-to-nearest.
+    768 columns: a block of six batches, where the update after the fourth
+    (four batches' errors onto the next four) is cut to the two left."""
     fq = _fp4()
-    w, H, U, imp = _gptq_inputs(192, 512, seed=114)
+    w, H, U, imp = _gptq_inputs(rows, cols, seed=114 + cols - 512)
     im = imp if wmse else None
     res = fq.gptq_nvfp4(w.to(DEV), U, None if im is None else im.to(DEV), check=True)
     torch.cuda.synchronize()
