@@ -363,19 +363,33 @@ def quantize_relaxed(x, scales, coeffs=None, fmt="nvfp4", global_scale=None, sub
     return codes, dq
 
 
-def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *, ws=None, check=False):
-    """GPTQ with ScaleSweep group scales (NVFP4).  w: [R, C] weight (any
-    float dtype; a float32 working copy is made, C a multiple of 128);
-    hinv_chol: [C, C] upper Cholesky factor U of the damped inverse Hessian
-    (H^-1 = U^T U); importance: per-column WMSE weights or None (MSE).
-    Returns an NVFP4Result without losses and offsets."""
-    lib = L.load()
+def _gptq_operands(w):
+    """The weight as the library reads it, and float32 working storage.  A
+    float32 weight with unit column stride, a row stride that is a multiple
+    of 4 and 16-byte alignment is read in place (the library reads each
+    column from it until an update first writes the working copy); any other
+    is copied into the working storage first."""
     if w.dim() != 2 or not w.is_cuda:
         raise ValueError("w must be a 2-D device tensor")
     rows, cols = w.shape
+    work = torch.empty((rows, cols), dtype=torch.float32, device=w.device)
+    if (w.dtype == torch.float32 and w.stride(1) == 1 and w.stride(0) % 4 == 0 and w.stride(0) >= cols
+            and w.data_ptr() % 16 == 0):
+        return w, w.stride(0), work
+    work.copy_(w)
+    return None, 0, work
+
+
+def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *, ws=None, check=False):
+    """GPTQ with ScaleSweep group scales (NVFP4).  w: [R, C] weight (any
+    float dtype, C a multiple of 128; left unchanged); hinv_chol: [C, C]
+    upper Cholesky factor U of the damped inverse Hessian (H^-1 = U^T U);
+    importance: per-column WMSE weights or None (MSE).  Returns an
+    NVFP4Result without losses and offsets."""
+    lib = L.load()
+    src, ld_src, work = _gptq_operands(w)
+    rows, cols = w.shape
     dev = w.device
-    work = torch.empty((rows, cols), dtype=torch.float32, device=dev)
-    work.copy_(w)  # one pass: the float32 working copy, whatever w's dtype and strides
     U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
     if U.shape != (cols, cols):
         raise ValueError("hinv_chol must be [cols, cols]")
@@ -393,27 +407,24 @@ def gptq_nvfp4(w, hinv_chol, importance=None, window=None, global_scale=None, *,
         flags |= L.GIVEN_SCALE
     ws = _ws(ws, dev)
     L.check(lib.fp4q_gptq_nvfp4(
-        work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
-        flags, out.codes.data_ptr(), out.scales.data_ptr(), out.global_scale.data_ptr(), ws.data_ptr(),
-        ws.numel(), _stream(dev)))
+        work.data_ptr(), rows, cols, work.stride(0), _ptr(src), ld_src, U.data_ptr(), _ptr(imp),
+        int(window[0]), int(window[1]), flags, out.codes.data_ptr(), out.scales.data_ptr(),
+        out.global_scale.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
     if check:
         _check_data(ws)
     return out
 
 
 def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=False):
-    """GPTQ with MXFP4 group scales.  w: [R, C] weight (a float32 working
-    copy is made, C a multiple of 128); hinv_chol: [C, C] upper Cholesky
-    factor U of the damped inverse Hessian; importance: per-column WMSE
-    weights or None (MSE); window: E8M0 exponent offsets around each group's
-    base exponent.  Returns an MXFP4Result without losses and offsets."""
+    """GPTQ with MXFP4 group scales.  w: [R, C] weight (C a multiple of
+    128; left unchanged); hinv_chol: [C, C] upper Cholesky factor U of the
+    damped inverse Hessian; importance: per-column WMSE weights or None
+    (MSE); window: E8M0 exponent offsets around each group's base exponent.
+    Returns an MXFP4Result without losses and offsets."""
     lib = L.load()
-    if w.dim() != 2 or not w.is_cuda:
-        raise ValueError("w must be a 2-D device tensor")
+    src, ld_src, work = _gptq_operands(w)
     rows, cols = w.shape
     dev = w.device
-    work = torch.empty((rows, cols), dtype=torch.float32, device=dev)
-    work.copy_(w)  # one pass: the float32 working copy, whatever w's dtype and strides
     U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
     if U.shape != (cols, cols):
         raise ValueError("hinv_chol must be [cols, cols]")
@@ -424,8 +435,9 @@ def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=
         block_loss=None, offsets=None)
     ws = _ws(ws, dev)
     L.check(lib.fp4q_gptq_mxfp4(
-        work.data_ptr(), rows, cols, work.stride(0), U.data_ptr(), _ptr(imp), int(window[0]), int(window[1]),
-        out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+        work.data_ptr(), rows, cols, work.stride(0), _ptr(src), ld_src, U.data_ptr(), _ptr(imp),
+        int(window[0]), int(window[1]), out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream(dev)))
     if check:
         _check_data(ws)
     return out

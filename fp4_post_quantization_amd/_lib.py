@@ -61,8 +61,8 @@ _SIGNATURES = {
     "fp4q_quantize_mxfp4": (_I, [_P, _I, _I64, _I64, _I64, _P, _I, _I, _I, _I, _I,
                                  _P, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_quantize_relaxed": (_I, [_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
-    "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
-    "fp4q_gptq_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
+    "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
+    "fp4q_gptq_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "fp4q_dequantize": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "fp4q_block_hadamard": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P]),
     "fp4q_gemm_mxfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _I, _P, _I64, _P, _SZ, _P]),

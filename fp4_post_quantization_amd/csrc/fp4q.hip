@@ -930,20 +930,38 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
   (f(std::integral_constant<int, I>{}), ...);
 }
 
+// partials (NVFP4, the call's first batch when a max pass ran): every workgroup takes S from the max
+// pass's per-workgroup maxima itself, and workgroup 0 writes it to gscale for the later batches.
+// Win / ldin: where the batch's columns are read (W, or the caller's weight when no update has
+// touched them yet); W is where its errors go.  pk >= 0: first apply the errors of the 128 columns
+// at pk (the previous batch, in W) to this batch's columns, for the workgroup's own rows: a
+// 16 x 128 x 128 contraction on fp32 MFMA (16x16x4) in place of a launch of the near update.
 template <bool WMSE, int FMT>
 __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
-    float *__restrict__ W, int64_t ld, int rows, int cols, int i1, const float *__restrict__ U,
-    const float *__restrict__ imp, const float *__restrict__ gscale, int lo, int hi, uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ scales, Status status) {
+    float *W, int64_t ld, const float *Win, int64_t ldin, int pk, int rows, int cols, int i1,
+    const float *__restrict__ U,
+    const float *__restrict__ imp, float *__restrict__ gscale, const uint32_t *__restrict__ partials,
+    int n_partials, int lo, int hi, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, Status status) {
   __shared__ __attribute__((aligned(1024))) float Ub[kGptqBatch][kGptqBatch];
   __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch], impb[kGptqBatch];
+  __shared__ float Pe[kGptqRowsPerWg][kGptqBatch + 4];  // pk >= 0: the rows' errors, then the update
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = lane & 15;
   const int r = blockIdx.x * kGptqRowsPerWg + (tid >> 4);
   const bool live = r < rows;  // dead rows still take part in the broadcasts
   constexpr bool MX = FMT == FP4Q_MXFP4;
-  const float S = MX ? 1.0f : *gscale;
+  float S = 1.0f;
+  if (!MX && partials) {
+    uint32_t bits;
+    S = as_f(reduce_partials(partials, n_partials, lane, bits)) / 1536.0f;
+    if (blockIdx.x == 0 && tid == 0) {
+      *gscale = S;
+      if (bits) status.report(bits);
+    }
+  } else if (!MX) {
+    S = *gscale;
+  }
   const float S_inv = (S == 0.0f) ? 0.0f : 1.0f / S;
   // Every global load is issued before any of them is waited for: the tables, the diagonal and the
   // importance (threads < 128), the row's weights (dead rows read row 0), and the U block into
@@ -962,8 +980,9 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
   if (!MX && status.first && blockIdx.x == 0 && tid == 0 && (!(S >= 0.0f) || isinf(S)))
     status.report(FP4Q_DATA_BAD_GLOBAL_SCALE);
   float *wr = W + (int64_t)(live ? r : 0) * ld + i1 + 8 * t;
-  const f32x4 wa = *reinterpret_cast<const f32x4 *>(wr);
-  const f32x4 wb = *reinterpret_cast<const f32x4 *>(wr + 4);
+  const float *wsrc = Win + (int64_t)(live ? r : 0) * ldin + i1 + 8 * t;
+  const f32x4 wa = *reinterpret_cast<const f32x4 *>(wsrc);
+  const f32x4 wb = *reinterpret_cast<const f32x4 *>(wsrc + 4);
   f32x4 up[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -984,13 +1003,46 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     impb[tid] = im;
     if (WMSE && !((im >= 0.0f) & (im <= 3.402823466e38f))) status.report(FP4Q_DATA_BAD_IMPORTANCE);
   }
-  stash_u(std::integral_constant<int, 0>{});
   float w[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     w[k] = live ? wa[k] : 0.0f;
     w[4 + k] = live ? wb[k] : 0.0f;
   }
+  if (pk >= 0) {
+    // the rows' errors at pk into Pe, U[pk .. pk + 128][i1 .. i1 + 128] into Ub (free until part 0
+    // of this batch's own U block is stored below)
+    const float *er = W + (int64_t)(live ? r : 0) * ld + pk + 8 * t;
+    *reinterpret_cast<f32x4 *>(&Pe[tid >> 4][8 * t]) = *reinterpret_cast<const f32x4 *>(er);
+    *reinterpret_cast<f32x4 *>(&Pe[tid >> 4][8 * t + 4]) = *reinterpret_cast<const f32x4 *>(er + 4);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int e = tid + kGptqBatchThreads * j;
+      *reinterpret_cast<f32x4 *>(&Ub[e >> 5][(e & 31) * 4]) =
+          *reinterpret_cast<const f32x4 *>(U + (int64_t)(pk + (e >> 5)) * cols + i1 + (e & 31) * 4);
+    }
+    __syncthreads();
+    // wave v: columns 32 v .. 32 v + 31 as two 16 x 16 blocks; lane l supplies A[l % 16][k = l / 16]
+    // and B[k = l / 16][l % 16] of each k step of 4, and holds D[4 (l / 16) + i][l % 16] in register i
+    const int wv = tid >> 6, li = lane & 15, lq = lane >> 4;
+    f32x4 d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int k = 0; k < kGptqBatch; k += 4) {
+      const float a = Pe[li][k + lq];
+      d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[k + lq][32 * wv + li], d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ub[k + lq][32 * wv + 16 + li], d1, 0, 0, 0);
+    }
+    __syncthreads();  // every wave is done with Pe and Ub
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      Pe[4 * lq + i][32 * wv + li] = d0[i];
+      Pe[4 * lq + i][32 * wv + 16 + li] = d1[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = w[k] - Pe[tid >> 4][8 * t + k];
+  }
+  stash_u(std::integral_constant<int, 0>{});
   {  // MXFP4 and NVFP4 with a given scale run no global-max pass over the weights
     bool finite = true;
 #pragma unroll
@@ -1131,8 +1183,10 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 // ascending order, so every output element accumulates in the same order.
 constexpr int kUpdKc = 32;
 
-__global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict__ W, int64_t ld, int rows,
-                                                               int cols, int i1, int kn, int cbeg,
+// C / ldc: where the output tile's current values are read (W, or the caller's weight for
+// columns no update has touched yet); the result goes to W.
+__global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *W, int64_t ld, const float *C, int64_t ldc,
+                                                               int rows, int cols, int i1, int kn, int cbeg,
                                                                const float *__restrict__ U) {
   __shared__ float As[2][64][kUpdKc + 1];
   __shared__ float Bs[2][kUpdKc][64];
@@ -1145,7 +1199,7 @@ __global__ __launch_bounds__(kThreads) void gptq_update_kernel(float *__restrict
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int row = r0 + wr * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-    cur[v] = row < rows ? W[(int64_t)row * ld + c0 + wc * 32 + lr] : 0.0f;
+    cur[v] = row < rows ? C[(int64_t)row * ldc + c0 + wc * 32 + lr] : 0.0f;
   }
   // chunk kc of the operands: E rows r0.. (64 x 32, 8 float4 per row), U rows i1 + kc.. (32 x 64)
   f32x4 a[2], b[2];
@@ -1237,9 +1291,9 @@ __device__ __forceinline__ void split_bf16x3(float x0, float x1, uint32_t &h, ui
 // NW waves per workgroup: 4 (each wave a 2 x 2 grid of 32 x 32 blocks) or 8 (each wave 1 x 2); KC K
 // elements per stage (16 or 32).
 template <int NW, int KC>
-__global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__restrict__ W, int64_t ld, int rows,
-                                                                    int cols, int i1, int kn, int cbeg,
-                                                                    const float *__restrict__ U) {
+__global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *W, int64_t ld, const float *C,
+                                                                    int64_t ldc, int rows, int cols, int i1, int kn,
+                                                                    int cbeg, const float *__restrict__ U) {
   constexpr int BM = 128, BN = 128, NT = 64 * NW, KS = KC / 16;
   constexpr int WR = NW / 2, TI = 4 / WR, TJ = 2;  // wave grid WR x 2; blocks per wave TI x TJ
   constexpr int EPT = BM * KC / NT;                 // values per thread per operand per stage
@@ -1353,8 +1407,8 @@ __global__ __launch_bounds__(64 * NW) void gptq_update_split_kernel(float *__res
       for (int v = 0; v < 16; ++v) {
         // accumulator v of block (i, j) in lane l: row 32 i + 8*(v/4) + 4*(l/32) + v%4, column 32 j + l%32
         const int row = r0 + wr * 32 * TI + 32 * i + 8 * (v >> 2) + 4 * lk + (v & 3);
-        float *o = W + (int64_t)row * ld + c0 + wc * 64 + 32 * j + lr;
-        if (row < rows) *o = *o - acc[i][j][v];
+        const int64_t col = c0 + wc * 64 + 32 * j + lr;
+        if (row < rows) W[(int64_t)row * ld + col] = C[(int64_t)row * ldc + col] - acc[i][j][v];
       }
 }
 
@@ -1457,33 +1511,65 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
 // after every batch, in fewer wide launches).  After the block's last batch,
 // all later columns get the block's error columns as one contraction.
 template <int FMT>
-static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
-                         const float *importance, const float *global_scale, int off_lo, int off_hi, uint8_t *codes,
+static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in, int64_t ld_in,
+                         const float *hinv_chol, const float *importance, float *global_scale,
+                         const uint32_t *partials, int n_partials, int off_lo, int off_hi, uint8_t *codes,
                          uint8_t *scales, uint32_t *status_slot, bool first_kernel, hipStream_t s) {
   const int gb = ceil_div(rows, kGptqRowsPerWg);
+  // w holds columns [0, held); a launch reads the current values of later columns from w_in (the
+  // caller's weight, untouched so far), so w needs no copy of it (w_in == w: in place)
+  int held = 0;
+  int pk = -1;  // start of the batch whose errors the next batch kernel applies to its own columns
+  auto near = [&](int k0, int kn, int c0, int c1) {  // errors of columns [k0, k0 + kn) onto [c0, c1)
+    for (int lo = c0; lo < c1;) {
+      const bool old = lo < held;
+      const int hi = old ? std::min(c1, held) : c1;
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (hi - lo) / 64), dim3(kThreads), 0, s, w, ld,
+                         old ? w : w_in, old ? ld : ld_in, (int)rows, (int)cols, k0, kn, lo, hinv_chol);
+      lo = hi;
+    }
+    held = std::max(held, c1);
+  };
+  auto far = [&](int k0, int kn, int c0, int c1) {
+    for (int lo = c0; lo < c1;) {
+      const bool old = lo < held;
+      const int hi = old ? std::min(c1, held) : c1;
+      hipLaunchKernelGGL((gptq_update_split_kernel<kSplitWaves, kSplitKc>), dim3(ceil_div(rows, 128), (hi - lo) / 128),
+                         dim3(64 * kSplitWaves), 0, s, w, ld, old ? w : w_in, old ? ld : ld_in, (int)rows,
+                         (int)cols, k0, kn, lo, hinv_chol);
+      lo = hi;
+    }
+    held = std::max(held, c1);
+  };
   for (int i1 = 0; i1 < cols; i1 += kGptqBatch) {
-    // the first batch kernel is the call's first kernel unless a max pass ran before it
+    // the first batch kernel is the call's first kernel unless a max pass ran before it, whose
+    // partials it then reduces to S
     const Status status{status_slot, first_kernel && i1 == 0};
+    const uint32_t *part = i1 == 0 ? partials : nullptr;
+    const bool old = i1 < held;
+    const float *src = old ? w : w_in;
+    const int64_t lds = old ? ld : ld_in;
     if (importance)
-      hipLaunchKernelGGL((gptq_batch_kernel<true, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, (int)rows,
-                         (int)cols, i1, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales, status);
+      hipLaunchKernelGGL((gptq_batch_kernel<true, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, src, lds,
+                         pk, (int)rows, (int)cols, i1, hinv_chol, importance, global_scale, part, n_partials,
+                         off_lo, off_hi, codes, scales, status);
     else
-      hipLaunchKernelGGL((gptq_batch_kernel<false, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld,
-                         (int)rows, (int)cols, i1, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales,
-                         status);
+      hipLaunchKernelGGL((gptq_batch_kernel<false, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, src, lds,
+                         pk, (int)rows, (int)cols, i1, hinv_chol, importance, global_scale, part, n_partials,
+                         off_lo, off_hi, codes, scales, status);
+    held = std::max(held, i1 + kGptqBatch);
+    pk = -1;
     const int i2 = i1 + kGptqBatch;
     const int b0 = i1 / kGptqBlock * kGptqBlock, b1 = std::min((int)cols, b0 + kGptqBlock);
     // batch t of the block (m = the lowest set bit of t + 1): the last m batches' errors onto the
-    // next m batches' columns
+    // next m batches' columns; for m = 1 the next batch kernel applies them itself
     const int tb = (i1 - b0) / kGptqBatch, m = (tb + 1) & -(tb + 1);
-    const int e2 = std::min(b1, i2 + m * kGptqBatch);
-    if (i2 < b1)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(ceil_div(rows, 64), (e2 - i2) / 64), dim3(kThreads), 0, s, w,
-                         ld, (int)rows, (int)cols, i2 - m * kGptqBatch, m * kGptqBatch, i2, hinv_chol);
+    if (i2 < b1 && m == 1)
+      pk = i1;
+    else if (i2 < b1)
+      near(i2 - m * kGptqBatch, m * kGptqBatch, i2, std::min(b1, i2 + m * kGptqBatch));
     else if (b1 < cols)  // the far update (cols - b1 is a multiple of the 128-column tile)
-      hipLaunchKernelGGL((gptq_update_split_kernel<kSplitWaves, kSplitKc>),
-                         dim3(ceil_div(rows, 128), ((int)cols - b1) / 128), dim3(64 * kSplitWaves), 0, s, w, ld,
-                         (int)rows, (int)cols, b0, b1 - b0, b1, hinv_chol);
+      far(b0, b1 - b0, b1, (int)cols);
   }
 }
 
@@ -1857,22 +1943,29 @@ extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void 
   return last_hip_status();
 }
 
-extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
-                                         const float *hinv_chol, const float *importance, int off_lo,
-                                         int off_hi, uint32_t flags, uint8_t *codes, uint8_t *scales,
-                                         float *global_scale, void *workspace, size_t workspace_bytes,
-                                         void *stream) {
+// The weight is read from w_in (ld_in), or from w when w_in is NULL; w is the working storage.
+static bool gptq_source_ok(const float *w_in, int64_t ld_in, int64_t cols) {
+  return !w_in || (ld_in >= cols);
+}
+
+extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                         int64_t ld_in, const float *hinv_chol, const float *importance,
+                                         int off_lo, int off_hi, uint32_t flags, uint8_t *codes,
+                                         uint8_t *scales, float *global_scale, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
   const bool empty = rows == 0 || cols == 0;
   if (!global_scale || (!empty && (!w || !hinv_chol || !codes || !scales))) return FP4Q_ERR_NULL;
   if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
   if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
-  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch || !gptq_source_ok(w_in, ld_in, cols))
+    return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
   if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
-                 (importance && !aligned(importance, 4))))
+                 (importance && !aligned(importance, 4)) || (w_in && (!aligned(w_in, 16) || ld_in % 4))))
     return FP4Q_ERR_ALIGN;
+  if (!w_in) w_in = w, ld_in = ld;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   const bool given = flags & FP4Q_GIVEN_SCALE;
@@ -1883,31 +1976,31 @@ extern "C" fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, i
                        given ? nullptr : global_scale);
     return last_hip_status();
   }
-  if (!given) {
-    uint32_t *partials = (uint32_t *)((char *)workspace + kWsPartials);
-    const int n_partials = launch_amax(w, FP4Q_F32, rows, cols, ld, 0, amax_out(workspace, nullptr, 0), s);
-    hipLaunchKernelGGL(scale_from_partials_kernel, dim3(1), dim3(kThreads), 0, s, partials, n_partials,
-                       global_scale, status);
-  }
-  gptq_batches<FP4Q_NVFP4>(w, rows, cols, ld, hinv_chol, importance, global_scale, off_lo, off_hi, codes, scales,
-                           status, given, s);
+  // without a given scale, the max pass runs first and the first batch kernel reduces its partials
+  const uint32_t *partials = given ? nullptr : (const uint32_t *)((char *)workspace + kWsPartials);
+  const int n_partials =
+      given ? 0 : launch_amax(w_in, FP4Q_F32, rows, cols, ld_in, 0, amax_out(workspace, nullptr, 0), s);
+  gptq_batches<FP4Q_NVFP4>(w, rows, cols, ld, w_in, ld_in, hinv_chol, importance, global_scale, partials,
+                           n_partials, off_lo, off_hi, codes, scales, status, given, s);
   return last_hip_status();
 }
 
-extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
-                                         const float *hinv_chol, const float *importance, int off_lo,
-                                         int off_hi, uint8_t *codes, uint8_t *scales, void *workspace,
-                                         size_t workspace_bytes, void *stream) {
+extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                         int64_t ld_in, const float *hinv_chol, const float *importance,
+                                         int off_lo, int off_hi, uint8_t *codes, uint8_t *scales,
+                                         void *workspace, size_t workspace_bytes, void *stream) {
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!w || !hinv_chol || !codes || !scales)) return FP4Q_ERR_NULL;
   if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
   if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
-  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch) return FP4Q_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch || !gptq_source_ok(w_in, ld_in, cols))
+    return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
   if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(hinv_chol, 16) || !aligned(codes, 4) ||
-                 (importance && !aligned(importance, 4))))
+                 (importance && !aligned(importance, 4)) || (w_in && (!aligned(w_in, 16) || ld_in % 4))))
     return FP4Q_ERR_ALIGN;
+  if (!w_in) w_in = w, ld_in = ld;
   hipStream_t s = (hipStream_t)stream;
   uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   // the first batch kernel takes the status slot; an empty matrix gets a small kernel for it
@@ -1915,8 +2008,8 @@ extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, i
     hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
     return last_hip_status();
   }
-  gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, hinv_chol, importance, nullptr, off_lo, off_hi, codes, scales,
-                           status, true, s);
+  gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, w_in, ld_in, hinv_chol, importance, nullptr, nullptr, 0, off_lo,
+                           off_hi, codes, scales, status, true, s);
   return last_hip_status();
 }
 

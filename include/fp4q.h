@@ -288,9 +288,15 @@ fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dt
  * format).  GPTQ (only named on the pages) is the published column-by-column
  * quantization with error feedback through the inverse Hessian.
  *
- *   w          [rows x cols] float32, leading dimension ld (multiple of 4),
- *              the weight; OVERWRITTEN (working storage: on return it holds
- *              the scaled quantization errors).
+ *   w          [rows x cols] float32, leading dimension ld (multiple of 4):
+ *              working storage, OVERWRITTEN (on return it holds the scaled
+ *              quantization errors).
+ *   w_in       [rows x cols] float32, leading dimension ld_in (>= cols,
+ *              multiple of 4): the weight, read only; or NULL when w holds
+ *              the weight (quantized in place).  With a separate w_in, no
+ *              copy of the weight is needed: each column is read from w_in
+ *              until an update first writes it into w.  w_in must not
+ *              overlap w unless it is w itself.
  *   cols       a multiple of 128 (the lazy-batch width).
  *   hinv_chol  [cols x cols] float32 row-major U, the upper Cholesky factor
  *              of H^-1 (H = X^T X of calibration activations, damped by the
@@ -310,17 +316,24 @@ fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dt
  * column c is rounded to nearest at that scale, its scaled error
  * err = fp32(fp32(w_c - x_hat_c) * fp32(1 / U[c][c])) is kept, and every
  * later column j of the same 128-column batch becomes fma(-err, U[c][j],
- * w_j).  Later columns receive the batch's errors as fp32 MFMA contractions
- * w -= Err * U[batch, cols]: after each batch the rest of its block of 1024
- * columns, and after each block all later columns, with the whole block's
- * errors in one contraction (two-level lazy batches; the float32 grouping of
- * the updates is therefore not that of 128-column batches alone).  A
+ * w_j).  Later columns receive earlier errors as contractions
+ * w -= Err * U[rows of Err, cols] (lazy batches): within each block of 1024
+ * columns, after batch t of the block (m the lowest set bit of t + 1) the
+ * last m batches' errors reach the next m batches' columns, on fp32 matrix
+ * cores; after each block all later columns get the whole block's errors in
+ * one contraction on the bf16 matrix cores, each fp32 operand split exactly
+ * into three bf16 parts and the six part products down to order 2^-16 kept
+ * (the dropped ones at most ~2^-23 of a product).  The float32 grouping of
+ * the updates is therefore not that of 128-column batches alone.  A
  * non-positive or non-finite diagonal entry of U sets FP4Q_DATA_BAD_HESSIAN.
+ * Argument errors: FP4Q_ERR_SHAPE for ld or ld_in below cols, FP4Q_ERR_ALIGN
+ * for w, w_in or hinv_chol not 16-byte aligned or ld, ld_in not multiples
+ * of 4.
  */
-fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
-                              const float *importance, int off_lo, int off_hi, uint32_t flags,
-                              uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
-                              size_t workspace_bytes, void *stream);
+fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                              int64_t ld_in, const float *hinv_chol, const float *importance, int off_lo,
+                              int off_hi, uint32_t flags, uint8_t *codes, uint8_t *scales,
+                              float *global_scale, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * GPTQ with MXFP4 group scales ([MR] 2., MR-GPTQ component 1: the grid is
@@ -332,7 +345,8 @@ fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
  * 2^E, x_hat = q * 2^E exactly, and the scaled errors and updates are those
  * of fp4q_gptq_nvfp4.  There is no global scale.
  *
- *   w, rows, cols, ld, hinv_chol, importance  as for fp4q_gptq_nvfp4.
+ *   w, rows, cols, ld, w_in, ld_in, hinv_chol, importance  as for
+ *              fp4q_gptq_nvfp4.
  *   off_lo, off_hi  exponent window (at most 16 candidates), e.g. -1, 0.
  *   codes      [rows x cols/2] packed E2M1 codes (4-byte aligned).
  *   scales     [rows x cols/32] E8M0 bytes (E + 127).
@@ -341,9 +355,10 @@ fp4q_status_t fp4q_gptq_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
  * non-finite importance FP4Q_DATA_BAD_IMPORTANCE, a bad diagonal of U
  * FP4Q_DATA_BAD_HESSIAN.  Argument errors as for fp4q_gptq_nvfp4.
  */
-fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *hinv_chol,
-                              const float *importance, int off_lo, int off_hi, uint8_t *codes,
-                              uint8_t *scales, void *workspace, size_t workspace_bytes, void *stream);
+fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                              int64_t ld_in, const float *hinv_chol, const float *importance, int off_lo,
+                              int off_hi, uint8_t *codes, uint8_t *scales, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * Dequantization (the consumer side: only codes and dequantization scales

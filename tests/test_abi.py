@@ -152,8 +152,9 @@ def test_gptq_validation():
     L, lib = _lib()
     wsb = lib.fp4q_workspace_bytes()
     gq = lambda **kw: lib.fp4q_gptq_nvfp4(
-        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("u", OUT), None, kw.get("lo", -3),
-        kw.get("hi", 7), kw.get("flags", 0), OUT, OUT, kw.get("gs", OUT), kw.get("ws", WS), wsb, None)
+        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("src", None), kw.get("lds", 0),
+        kw.get("u", OUT), None, kw.get("lo", -3), kw.get("hi", 7), kw.get("flags", 0), OUT, OUT,
+        kw.get("gs", OUT), kw.get("ws", WS), wsb, None)
     assert gq(w=None) == L.ERR_NULL
     assert gq(u=None) == L.ERR_NULL
     assert gq(gs=None) == L.ERR_NULL
@@ -164,9 +165,14 @@ def test_gptq_validation():
     assert gq(ld=100) == L.ERR_SHAPE
     assert gq(ld=130) == L.ERR_ALIGN
     assert gq(u=OUT + 4) == L.ERR_ALIGN
+    # a separate read-only weight: its row stride at least cols, a multiple of 4, 16-byte aligned
+    assert gq(src=X, lds=100) == L.ERR_SHAPE
+    assert gq(src=X, lds=130) == L.ERR_ALIGN
+    assert gq(src=X + 4, lds=128) == L.ERR_ALIGN
     gm = lambda **kw: lib.fp4q_gptq_mxfp4(
-        kw.get("w", X), kw.get("rows", 4), kw.get("cols", 128), kw.get("ld", 128), kw.get("u", OUT), None,
-        kw.get("lo", -1), kw.get("hi", 0), OUT, OUT, kw.get("ws", WS), wsb, None)
+        kw.get("w", X), kw.get("rows", 4), kw.get("cols", 128), kw.get("ld", 128), kw.get("src", None),
+        kw.get("lds", 0), kw.get("u", OUT), None, kw.get("lo", -1), kw.get("hi", 0), OUT, OUT, kw.get("ws", WS),
+        wsb, None)
     assert gm(w=None) == L.ERR_NULL
     assert gm(u=None) == L.ERR_NULL
     assert gm(ws=None) == L.ERR_WORKSPACE
@@ -175,6 +181,8 @@ def test_gptq_validation():
     assert gm(cols=160, ld=160) == L.ERR_SHAPE
     assert gm(ld=100) == L.ERR_SHAPE
     assert gm(ld=130) == L.ERR_ALIGN
+    assert gm(src=X, lds=64) == L.ERR_SHAPE
+    assert gm(src=X + 8, lds=128) == L.ERR_ALIGN
     # empty: the arguments pass; the call still enqueues the kernel that writes the status word,
     # whose launch needs a GPU
     assert gm(rows=0) in (L.OK, L.ERR_HIP)

@@ -733,6 +733,44 @@ def test_gptq_block_updates_against_oracle(rows, cols, wmse):
     assert abs(lg - lo) <= 1e-3 * lo
 
 
+def test_gptq_reads_the_weight_in_place_of_a_copy():
+    """A float32 weight is read where it lies (each column until an update
+    first writes the working storage) and left unchanged; the results are
+    bit-identical to a call on a working copy holding the weight (w_in NULL),
+    for both formats, over 2304 columns (first touches by the first batch,
+    the block's updates and the far update) on a ragged 200 rows."""
+    fq = _fp4()
+    from fp4_post_quantization_amd import _lib as L
+    lib = L.load()
+    w, H, U, imp = _gptq_inputs(200, 2304, seed=131)
+    wd, Ud, imd = w.to(DEV), torch.from_numpy(U).to(DEV), imp.to(DEV)
+    before = wd.clone()
+    rows, cols = wd.shape
+    ws = torch.zeros(lib.fp4q_workspace_bytes(), dtype=torch.uint8, device=DEV)
+    stream = torch.cuda.current_stream().cuda_stream
+    nv = fq.gptq_nvfp4(wd, Ud, imd, check=True)
+    work = wd.clone()
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=DEV)
+    gs = torch.empty(1, dtype=torch.float32, device=DEV)
+    L.check(lib.fp4q_gptq_nvfp4(work.data_ptr(), rows, cols, cols, None, 0, Ud.data_ptr(), imd.data_ptr(), -8, 7,
+                                0, codes.data_ptr(), scales.data_ptr(), gs.data_ptr(), ws.data_ptr(), ws.numel(),
+                                stream))
+    mx = fq.gptq_mxfp4(wd, Ud, imd, check=True)
+    work2 = wd.clone()
+    mcodes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=DEV)
+    mscales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    L.check(lib.fp4q_gptq_mxfp4(work2.data_ptr(), rows, cols, cols, None, 0, Ud.data_ptr(), imd.data_ptr(), -1, 0,
+                                mcodes.data_ptr(), mscales.data_ptr(), ws.data_ptr(), ws.numel(), stream))
+    torch.cuda.synchronize()
+    assert torch.equal(wd, before), "the weight was written"
+    _assert_equal("nvfp4 codes", _np(nv.codes), _np(codes))
+    _assert_equal("nvfp4 scales", _np(nv.scales), _np(scales))
+    _assert_equal("nvfp4 S", _np(nv.global_scale), _np(gs))
+    _assert_equal("mxfp4 codes", _np(mx.codes), _np(mcodes))
+    _assert_equal("mxfp4 scales", _np(mx.scales), _np(mscales))
+
+
 @pytest.mark.parametrize("wmse", [False, True])
 def test_gptq_mxfp4_single_batch_bitexact(wmse):
     """MXFP4 GPTQ, one batch (no contraction): bit-exact codes and exponents."""
@@ -760,8 +798,8 @@ def test_gptq_mxfp4_without_feedback_equals_sweep():
         _assert_equal("scales", _np(g.scales), _np(s_.scales))
 
 
-@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (192, 512, True), (64, 2304, False),
-                                             (200, 2176, True)])
+@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (192, 512, True), (96, 768, True),
+                                             (64, 2304, False), (200, 2176, True)])
 def test_gptq_mxfp4_multi_batch_against_oracle(rows, cols, wmse):
     """MXFP4 GPTQ across batches (and, at 2304 columns, across 1024-column
     blocks): the same bar as NVFP4 GPTQ."""
