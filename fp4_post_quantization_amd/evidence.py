@@ -82,19 +82,23 @@ WORKLOADS = {
             "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
     # GPTQ on 4096 x 4096 (1024-column blocks of eight 128-column batches).  Per dispatch, averaged
-    # over a call: the 28 near updates (the rest of the block, r = 896 ... 128 columns: read and write
-    # W[:, rest], read the batch's errors and U[batch, rest]; fp32 MFMA), the 3 far updates (all later
-    # columns, L = 3072, 2048, 1024, with the block's 1024 error columns and U[block, later]; bf16 MFMA
-    # on operands split in three, six bf16 products per fp32 product) and the 32 batch kernels (read
-    # and write 128 columns, write codes and scales, read U's 128 x 128 block)
+    # over a call: the 12 near updates of the block-internal binary tree (per block two of the next
+    # 256 columns with the last two batches' errors, one of the next 512 with the last four's: read
+    # and write W[:, N], read the K error columns and U[K rows, N]; fp32 MFMA), the 3 far updates
+    # (all later columns, L = 3072, 2048, 1024, with the block's 1024 error columns and
+    # U[block, later]; bf16 MFMA on operands split in three, six bf16 products per fp32 product) and
+    # the 32 batch kernels (read and write 128 columns, write codes and scales, read U's 128 x 128
+    # block; the odd batches of a block first apply the previous batch's errors to their columns,
+    # reading those 128 error columns and another 128 x 128 block of U)
     "gptq": {"stem": "gptq_nvfp4_f32_4096x4096", "kernel": "gptq_update_split_kernel",
              "title": "GPTQ with ScaleSweep group scales, fp32 4096x4096, MSE and WMSE",
-             "alg_bytes": {"gptq_update_kernel": sum(4 * (4096 * r * 8 + 4096 * 128 * 4 + 128 * r * 4)
-                                                     for r in range(128, 1024, 128)) / 28,
+             "alg_bytes": {"gptq_update_kernel": sum(c * (4096 * n * 8 + 4096 * n * 4 + n * n * 4)
+                                                     for c, n in ((8, 256), (4, 512))) / 12,
                            "gptq_update_split_kernel": sum(4096 * L * 8 + 4096 * 1024 * 4 + 1024 * L * 4
                                                            for L in (1024, 2048, 3072)) / 3,
-                           "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4},
-             "alg_flops": {"gptq_update_kernel": sum(4 * 2 * 4096 * 128 * r for r in range(128, 1024, 128)) / 28,
+                           "gptq_batch_kernel": 4096 * 128 * 8 + 4096 * 64 + 4096 * 8 + 128 * 128 * 4
+                                                + (4096 * 128 * 4 + 128 * 128 * 4) / 2},
+             "alg_flops": {"gptq_update_kernel": sum(c * 2 * 4096 * n * n for c, n in ((8, 256), (4, 512))) / 12,
                            "gptq_update_split_kernel": sum(6 * 2 * 4096 * 1024 * L for L in (1024, 2048, 3072)) / 3},
              "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
              "peak_tflops": {"gptq_update_kernel": 157.3, "gptq_update_split_kernel": 2500.0},
