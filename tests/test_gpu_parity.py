@@ -762,8 +762,15 @@ def test_gptq_reads_the_weight_in_place_of_a_copy():
     mscales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
     L.check(lib.fp4q_gptq_mxfp4(work2.data_ptr(), rows, cols, cols, None, 0, Ud.data_ptr(), imd.data_ptr(), -1, 0,
                                 mcodes.data_ptr(), mscales.data_ptr(), ws.data_ptr(), ws.numel(), stream))
+    # a weight with a wider row stride (a column slice) is read in place as well
+    wide = torch.zeros((rows, cols + 64), dtype=torch.float32, device=DEV)
+    wide[:, :cols] = wd
+    nvs = fq.gptq_nvfp4(wide[:, :cols], Ud, imd, check=True)
     torch.cuda.synchronize()
     assert torch.equal(wd, before), "the weight was written"
+    assert torch.equal(wide[:, :cols], before), "the strided weight was written"
+    _assert_equal("nvfp4 codes, strided weight", _np(nvs.codes), _np(nv.codes))
+    _assert_equal("nvfp4 scales, strided weight", _np(nvs.scales), _np(nv.scales))
     _assert_equal("nvfp4 codes", _np(nv.codes), _np(codes))
     _assert_equal("nvfp4 scales", _np(nv.scales), _np(scales))
     _assert_equal("nvfp4 S", _np(nv.global_scale), _np(gs))
