@@ -72,6 +72,37 @@ def _gemm_mean(nks, what, m=8192):
             for n, k in nks]
     return sum(vals) / len(vals)
 
+
+def panel_fetch(m, n, row_bytes, bm, bn, resident=32, xcds=8, group_rows=8):
+    """Bytes one ring-GEMM dispatch fetches into the XCDs' L2 caches if each L2 holds the operand
+    panels (BM or BN rows x all of K) of the tiles its XCD runs at once, and nothing from one such
+    round to the next (a round's panels exceed the 4 MB L2).  Workgroup i runs on XCD i % xcds;
+    the kernel numbers an XCD's tiles contiguously, in groups of group_rows tile rows walked column
+    by column (as the GEMM source's tile order does), and the XCD's `resident` workgroups (one per
+    CU) hold consecutive numbers.  Each round then fetches its distinct A and B panels once."""
+    tiles_m, tiles_n = -(-m // bm), -(-n // bn)
+    per, rem = divmod(tiles_m * tiles_n, xcds)
+    total = 0
+    for x in range(xcds):
+        start = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
+        count = per + (1 if x < rem else 0)
+        for r0 in range(0, count, resident):
+            rows, cols = set(), set()
+            for lin in range(start + r0, start + min(count, r0 + resident)):
+                group = lin // (group_rows * tiles_n)
+                first = group * group_rows
+                gsize = min(tiles_m - first, group_rows)
+                r = lin - group * group_rows * tiles_n
+                rows.add(first + r % gsize)
+                cols.add(r // gsize)
+            total += (sum(min(bm, m - t * bm) for t in rows) + sum(min(bn, n - t * bn) for t in cols)) * row_bytes
+    return total
+
+
+def _panel_mean(nks, bytes_per_k, tile, m=8192):
+    vals = [panel_fetch(m, n, k * bytes_per_k, tile, tile) for n, k in nks]
+    return sum(vals) / len(vals)
+
 # dominant kernel and algorithmic bytes per dispatch of each workload
 WORKLOADS = {
     "c2": {"stem": "nvfp4_wmse_bf16_4096x4096", "kernel": "nvfp4_sweep_kernel",
@@ -118,6 +149,7 @@ WORKLOADS = {
                            _W4A4_SMALL: _gemm_mean(_W4A4_NK_SMALL, "flops")},
              "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
              "peak_tflops": 10100.0, "peak_label": "the published dense FP4 (MXFP4 scaled MFMA) figure",
+             "panel_fetch": {_W4A4_BIG: _panel_mean(_W4A4_NK_BIG, 0.5 + 1 / 32, 256)},
              "sources": GEMM_SOURCES},
     "w4a4nv": {"stem": "nvfp4_w4a4_gemm_8b_layer_8192tok", "kernel": _W4A4NV_BIG,
                "title": "W4A4 NVFP4 layer (8B shapes, 8192 tokens): bf16-decoded operands on the bf16 matrix cores",
@@ -130,6 +162,7 @@ WORKLOADS = {
                "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
                "peak_tflops": 2500.0, "peak_label": "the published dense bf16/fp16 figure (the operands run on "
                                                     "the bf16 and fp16 matrix cores)",
+               "panel_fetch": {_W4A4NV_BIG: _panel_mean(_W4A4_NK_BIG, 2, 256)},
                "sources": GEMM_SOURCES},
     # FOCUS forward quantizer on the c2 weight: x (bf16), FP16 coefficients per 8, E4M3 scales in;
     # codes and the float32 dequantized output out
@@ -294,6 +327,7 @@ def summarize(config, in_dir, profiles):
               "| kernel | waves | VALU insts | VALU issue | VALUBusy | FETCH KiB | WRITE KiB | HBM bytes "
               "(calibrated) | algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|---|---|"]
     record = None
+    fetched = {}  # calibrated FETCH_SIZE bytes per dispatch, by kernel
     for name, avg_us in durations.items():
         if not _ours(name):
             continue
@@ -306,6 +340,8 @@ def summarize(config, in_dir, profiles):
         issue = insts[0] * 4 / (simds * avg_us * 1e-6 * clk_mhz * 1e6) if insts else None
         busy = 100 * insts[0] * 4 / (simds * sq_busy[0] / ses) if (insts and sq_busy and sq_busy[0]) else None
         hbm = (fk[0] * 1024 * f_factor + wk[0] * 1024 * w_factor) if (fk and wk and f_factor) else None
+        if fk and f_factor:
+            fetched[name] = fk[0] * 1024 * f_factor
         alg = w["alg_bytes"].get(key)
         lines.append(
             f"| `{_short(name)}` | {waves[0]:.0f} | {insts[0]:.4g} | "
@@ -318,6 +354,25 @@ def summarize(config, in_dir, profiles):
                       "write_kib": wk[0], "fetch_factor": f_factor, "write_factor": w_factor,
                       "traffic_bytes": hbm, "alg_bytes": alg, "valu_issue": issue, "valu_busy_pct": busy,
                       "source_sha256": source_hash(config)}
+    if w.get("panel_fetch"):
+        lines += ["", "## L2 panel model", "",
+                  "Predicted = the bytes the XCDs' L2 caches fetch if each holds the A and B panels (tile rows "
+                  "x all of K) of the 32 tiles its CUs run at once and nothing from one such round to the "
+                  "next, with the kernel's XCD-contiguous tile order (`panel_fetch` in this module); "
+                  "measured = calibrated FETCH_SIZE.  Agreement says the fetch above the algorithmic bytes "
+                  "is the panels each round re-reads, which a 4 MB L2 per XCD cannot keep across rounds "
+                  "(and which the 256 MB Infinity Cache may serve without HBM).", "",
+                  "| kernel | predicted fetch | measured fetch | measured / predicted |", "|---|---|---|---|"]
+        for name in durations:
+            pf = w["panel_fetch"].get(_short(name))
+            if pf is None:
+                continue
+            got = fetched.get(name)
+            lines.append(f"| `{_short(name)}` | {pf / 1e6:.2f} MB | "
+                         f"{'' if got is None else f'{got / 1e6:.2f} MB'} | "
+                         f"{'' if got is None else f'{got / pf:.3f}'} |")
+            if record is not None and w["kernel"] in name:
+                record.update(panel_fetch_bytes=pf)
     if w.get("alg_flops"):
         one_peak = not isinstance(w["peak_tflops"], dict)
         peak_note = f" ({w['peak_tflops']:.0f} TFLOP/s at 2.4 GHz)" if one_peak else ""
