@@ -59,11 +59,15 @@ __device__ __forceinline__ void unroll(std::integer_sequence<int, I...>, F &&f) 
   (f(std::integral_constant<int, I>{}), ...);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);  // quiet NaN
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+// float32 -> bfloat16, round to nearest even, two values per instruction (v_cvt_pk_bf16_f32: lo in
+// the low half).  On every float32 pattern, in both halves, it gives what the integer rounding
+// (b + 0x7FFF + lsb) >> 16 gives, and a NaN gives (b >> 16) | 0x40 (checked on the device over all
+// 2^32 patterns).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((fp4q::f32x2{lo, hi}), bf16x2v));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.0f); }
 
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t *p, float v) { *p = f32_to_bf16_rne(v); }
@@ -490,12 +494,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {
+        // registers v and v + 1 hold rows r and r + 1 of the same column
         const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-        OutT o;
-        if constexpr (sizeof(OutT) == 4) o = alpha * acc[i][j][v];
-        else o = f32_to_bf16_rne(alpha * acc[i][j][v]);
-        stage_out[r * EROW + j * 32 + l32] = o;
+        OutT *o = stage_out + r * EROW + j * 32 + l32;
+        if constexpr (sizeof(OutT) == 4) {
+          o[0] = alpha * acc[i][j][v];
+          o[EROW] = alpha * acc[i][j][v + 1];
+        } else {
+          const uint32_t p = f32x2_to_bf16x2(alpha * acc[i][j][v], alpha * acc[i][j][v + 1]);
+          o[0] = (uint16_t)p;
+          o[EROW] = (uint16_t)(p >> 16);
+        }
       }
     const int row0 = m0 + wm * TM * 32 + i * 32;
 #pragma unroll
@@ -1278,12 +1288,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void nv_gemm_ring_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
+      for (int v = 0; v < 16; v += 2) {
+        // registers v and v + 1 hold rows r and r + 1 of the same column
         const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-        OutT o;
-        if constexpr (sizeof(OutT) == 4) o = alpha * acc[i][j][v];
-        else o = f32_to_bf16_rne(alpha * acc[i][j][v]);
-        stage_out[r * EROW + j * 32 + l32] = o;
+        OutT *o = stage_out + r * EROW + j * 32 + l32;
+        if constexpr (sizeof(OutT) == 4) {
+          o[0] = alpha * acc[i][j][v];
+          o[EROW] = alpha * acc[i][j][v + 1];
+        } else {
+          const uint32_t p = f32x2_to_bf16x2(alpha * acc[i][j][v], alpha * acc[i][j][v + 1]);
+          o[0] = (uint16_t)p;
+          o[EROW] = (uint16_t)(p >> 16);
+        }
       }
     const int row0 = m0 + wm * TM * 32 + i * 32;
 #pragma unroll
