@@ -234,6 +234,14 @@ __device__ __forceinline__ int swz(int r) {
   else return (r >> 1) & 7;                       // 128-byte rows: 8 chunks, rows pair up per bank half
 }
 
+// This lane's index in its wave, opaque to the optimiser (values derived from it are computed
+// where they are used rather than hoisted out of loops).
+__device__ __forceinline__ int opaque_lane() {
+  int l = (int)(threadIdx.x & 63);
+  __asm__ volatile("" : "+v"(l));
+  return l;
+}
+
 // s_waitcnt with only the vector-memory counter (expcnt, lgkmcnt at their maxima)
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -253,6 +261,39 @@ __device__ __forceinline__ void load_lds4(const void *g, void *l) {
                                    (__attribute__((address_space(3))) void *)l, 4, 0, 0);
 }
 
+// Whether one ring stage can hold the epilogue's staging area (the persistent form stages the
+// output in the slot of a tile's last stage while the other slot holds the next tile's first).
+template <int WGM, int WGN, int TM, int TN, typename OutT, bool MX, int ROWB>
+constexpr bool ring_stage_holds_epilogue() {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, SPR = ROWB / 16;
+  constexpr int stage = MX ? (BM + BN) * (ROWB + SPR) : (BM + BN) * ROWB;
+  constexpr int staging = WGM * WGN * 32 * (TN * 32 + 16 / (int)sizeof(OutT)) * (int)sizeof(OutT);
+  return staging <= stage;
+}
+
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Grid of the persistent ring: one workgroup per CU, a multiple of the XCD count so that the
+// workgroup -> XCD assignment matches the tile order; 0 (use the one-tile form) when a product has
+// no more tiles than that, or when an operand's rows (rows x row_bytes, row_bytes >= its scale
+// bytes per row) reach 4 GiB, past the kernel's 32-bit load offsets.
+int persistent_grid(int64_t tiles, int64_t rows, int64_t row_bytes) {
+  if (rows * row_bytes + 4096 > (int64_t)UINT32_MAX) return 0;
+  const int cus = device_cus();
+  const int g = cus - cus % kXcds;
+  return (g > 0 && tiles > g) ? g : 0;
+}
+
 // Where the E8M0 bytes of row r for stage st are: S + r * row + st * stage.  Row-major scales (the
 // quantizer's layout): row = K / 32, stage = scale bytes per stage.  Stage-major scales
 // ([K / (2 ROWB)][rows][ROWB / 16], written by the scale reorganisation pass): row = ROWB / 16,
@@ -269,7 +310,7 @@ struct ScaleLayout {
 // per row; v_mfma_f32_32x32x16_bf16, lane l holding row l % 32 and K elements 8 (l / 32) .. +8, checked
 // on the device), scaled at the end by fp32(*ga * *gb).  Rows are kb bytes apart; nst stages.
 template <int WGM, int WGN, int TM, int TN, int NS, typename OutT, bool MX = true, int ROWB = 64,
-          bool SCALE16 = false>
+          bool SCALE16 = false, bool PERSIST = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     const uint8_t *__restrict__ A, const uint8_t *__restrict__ As, const uint8_t *__restrict__ B,
     const uint8_t *__restrict__ Bs, int M, int N, int nst, int64_t kb, ScaleLayout sl, const float *__restrict__ ga,
@@ -297,21 +338,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
   static_assert(!MX || (SA_INSTR * SBYTES == BM * SPR && SB_INSTR * SBYTES == BN * SPR),
                 "scale loads cover whole rows");
   static_assert(!SCALE16 || SPR == 8, "16-byte scale loads take two rows of 8 scale bytes");
+  // PERSIST: the waits below are all vmcnt(0) only with two slots, which keeps them exact once
+  // epilogue stores share the counter with the loads
+  static_assert(!PERSIST || NS == 2, "the persistent form runs a two-slot ring");
   constexpr int LOADS = A_INSTR + B_INSTR + SQ;  // per wave per stage
   constexpr int SPARE = NS * STAGE;               // target of the filler scale loads
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + SBYTES];
   if constexpr (!MX) alpha = (*ga) * (*gb);
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Tiles of this workgroup.  One launch tile per workgroup, or (PERSIST, gridDim.x a multiple of
+  // the XCD count) tiles blockIdx.x + j gridDim.x for j = 0, 1, ...: the tiles the one-per-workgroup
+  // launch would give those workgroup ids, so each stays on the same XCD in the same round.
+  const int total = PERSIST ? tiles_m * tiles_n : (int)gridDim.x;
+  const int ntiles = PERSIST ? (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 1;
+  // the wave index is the same in every lane of a wave: readfirstlane lets the compiler keep it and
+  // what derives from it in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WGM, wn = wave / WGM;
   const int l32 = lane & 31, h = lane >> 5;
-  // split K (blockIdx.y): this workgroup sums stages [sp nst, (sp + 1) nst) into its own M x ldc
-  // partial (row-major scales only)
-  if (gridDim.y > 1) {
+  // split K (blockIdx.y, one tile per workgroup): this workgroup sums stages [sp nst, (sp + 1) nst)
+  // into its own M x ldc partial (row-major scales only)
+  if (!PERSIST && gridDim.y > 1) {
     const int64_t sp = blockIdx.y;
     A += sp * nst * ROWB;
     B += sp * nst * ROWB;
@@ -320,60 +368,87 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     C += sp * M * ldc;
   }
 
-  // per-lane source addresses of the loads (advanced by ROWB code bytes / SPR scale bytes per stage)
-  const uint8_t *srcA[A_INSTR];
-  const uint8_t *srcB[B_INSTR];
-#pragma unroll
-  for (int i = 0; i < A_INSTR; ++i) {
-    const int row = (wave * A_INSTR + i) * RPL + lane / CPR;
-    srcA[i] = A + (int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row));
-  }
-#pragma unroll
-  for (int i = 0; i < B_INSTR; ++i) {
-    const int row = (wave * B_INSTR + i) * RPL + lane / CPR;
-    srcB[i] = B + (int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row));
-  }
+  // per-lane source addresses of the loads for the tile whose stages are being issued (advanced by
+  // ROWB code bytes / SPR scale bytes per stage)
+  // Sources of the loads, as byte offsets from the operand (A, B, As or Bs) of each load: 32-bit
+  // per-lane offsets for PERSIST (every operand under 4 GiB: checked by the launch), which keeps
+  // the register file free for the tile loop; 64-bit otherwise.
+  using Off = std::conditional_t<PERSIST, uint32_t, int64_t>;
+  Off offA[A_INSTR], offB[B_INSTR];
   // scale load q covers 256 bytes: 256 / SPR rows, lane l loading dword l % (SPR / 4) of row l / (SPR / 4)
   constexpr int DPR = SPR / 4;  // scale dwords per row per stage
-  const uint8_t *srcS[SQ > 0 ? SQ : 1];
+  Off offS[SQ > 0 ? SQ : 1];
+  const uint8_t *baseS[SQ > 0 ? SQ : 1];
   int64_t stepS[SQ > 0 ? SQ : 1];
   int dstS[SQ > 0 ? SQ : 1];
+  auto set_sources = [&](int j) {
+    const int lane = ::fp4q_gemm::opaque_lane();
+    int tm, tn;
+    tile_of((int)blockIdx.x + j * (int)gridDim.x, total, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
-  for (int j = 0; j < SQ; ++j) {
-    const int q = wave + WAVES * j;
-    // SCALE16: lane l loads rows 2l, 2l + 1 (16 contiguous bytes of stage-major scales); the row is
-    // clamped to the last one, and a pair starting there reads 8 bytes past the rows' end (the
-    // reorganised copy is padded for it)
-    const int rl = SCALE16 ? 2 * lane : lane / DPR, dw = SCALE16 ? 0 : lane % DPR;
-    constexpr int RPS = SBYTES / SPR;  // rows per scale load
-    if (q < SA_INSTR) {
-      srcS[j] = As + (int64_t)min(m0 + RPS * q + rl, M - 1) * sl.a_row + 4 * dw;
-      stepS[j] = sl.a_stage;
-      dstS[j] = SA_OFF + SBYTES * q;
-    } else if (q < SA_INSTR + SB_INSTR) {
-      const int qb = q - SA_INSTR;
-      srcS[j] = Bs + (int64_t)min(n0 + RPS * qb + rl, N - 1) * sl.b_row + 4 * dw;
-      stepS[j] = sl.b_stage;
-      dstS[j] = SB_OFF + SBYTES * qb;
-    } else {
-      srcS[j] = As + (int64_t)min(m0 + rl, M - 1) * sl.a_row + 4 * dw;
-      stepS[j] = sl.a_stage;
-      dstS[j] = -1;
+    for (int i = 0; i < A_INSTR; ++i) {
+      const int row = (wave * A_INSTR + i) * RPL + lane / CPR;
+      offA[i] = (Off)((int64_t)min(m0 + row, M - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row)));
     }
-  }
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+      const int row = (wave * B_INSTR + i) * RPL + lane / CPR;
+      offB[i] = (Off)((int64_t)min(n0 + row, N - 1) * kb + 16 * ((lane % CPR) ^ swz<ROWB>(row)));
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < SQ; ++j2) {
+      const int q = wave + WAVES * j2;
+      // SCALE16: lane l loads rows 2l, 2l + 1 (16 contiguous bytes of stage-major scales); the row is
+      // clamped to the last one, and a pair starting there reads 8 bytes past the rows' end (the
+      // reorganised copy is padded for it)
+      const int rl = SCALE16 ? 2 * lane : lane / DPR, dw = SCALE16 ? 0 : lane % DPR;
+      constexpr int RPS = SBYTES / SPR;  // rows per scale load
+      if (q < SA_INSTR) {
+        baseS[j2] = As;
+        offS[j2] = (Off)((int64_t)min(m0 + RPS * q + rl, M - 1) * sl.a_row + 4 * dw);
+        stepS[j2] = sl.a_stage;
+        dstS[j2] = SA_OFF + SBYTES * q;
+      } else if (q < SA_INSTR + SB_INSTR) {
+        const int qb = q - SA_INSTR;
+        baseS[j2] = Bs;
+        offS[j2] = (Off)((int64_t)min(n0 + RPS * qb + rl, N - 1) * sl.b_row + 4 * dw);
+        stepS[j2] = sl.b_stage;
+        dstS[j2] = SB_OFF + SBYTES * qb;
+      } else {
+        baseS[j2] = As;
+        offS[j2] = (Off)((int64_t)min(m0 + rl, M - 1) * sl.a_row + 4 * dw);
+        stepS[j2] = sl.a_stage;
+        dstS[j2] = -1;
+      }
+    }
+  };
 
   auto issue = [&](int st, int slot) {
     uint8_t *base = smem + slot * STAGE;
+    const uint8_t *a_st = A + (int64_t)st * ROWB, *b_st = B + (int64_t)st * ROWB;
 #pragma unroll
-    for (int i = 0; i < A_INSTR; ++i) load_lds16(srcA[i] + st * ROWB, base + (wave * A_INSTR + i) * 1024);
+    for (int i = 0; i < A_INSTR; ++i) load_lds16(a_st + offA[i], base + (wave * A_INSTR + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_INSTR; ++i)
-      load_lds16(srcB[i] + st * ROWB, base + A_BYTES + (wave * B_INSTR + i) * 1024);
+    for (int i = 0; i < B_INSTR; ++i) load_lds16(b_st + offB[i], base + A_BYTES + (wave * B_INSTR + i) * 1024);
 #pragma unroll
     for (int j = 0; j < SQ; ++j) {
       uint8_t *d = dstS[j] >= 0 ? base + dstS[j] : smem + SPARE;
-      if constexpr (SCALE16) load_lds16(srcS[j] + st * stepS[j], d);
-      else load_lds4(srcS[j] + st * stepS[j], d);
+      const uint8_t *src = baseS[j] + st * stepS[j] + offS[j];
+      if constexpr (SCALE16) load_lds16(src, d);
+      else load_lds4(src, d);
+    }
+  };
+  // The issue stream runs over the stages of all this workgroup's tiles in order, NS stages ahead
+  // of the MFMAs; past the last stage it reloads the last stage (never read again).  Every call
+  // issues exactly one stage of loads, so each wait below is one constant.
+  int iss_j = 0, iss_st = 0;
+  set_sources(0);
+  auto issue_next = [&](int slot) {
+    issue(iss_j < ntiles ? iss_st : nst - 1, slot);
+    if (iss_j < ntiles && ++iss_st == nst) {
+      iss_st = 0;
+      if (++iss_j < ntiles) set_sources(iss_j);
     }
   };
 
@@ -395,23 +470,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     if constexpr (SPR == 8) return (int)*reinterpret_cast<const uint32_t *>(p + 4 * h);
     else return (int)*reinterpret_cast<const uint16_t *>(p + 2 * h);
   };
+  // The rows a lane reads are l32 plus multiples of 32, and swz looks only at bits 1-3 (or 2-3) of
+  // the row, so every row this lane reads has its lane's swizzle: one per-lane offset per k step,
+  // with the block offsets as immediates.
+  const int lane_sw = swz<ROWB>(l32);
   auto read_ops = [&](int slot_, auto ks_c, Ops &o, const Ops &prev) {
     constexpr int ks = decltype(ks_c)::value;
-    const uint8_t *base = smem + slot_ * STAGE;
+    const uint8_t *base = smem + slot_ * STAGE + l32 * ROWB + 16 * (chunk(ks) ^ lane_sw);
+    const uint8_t *base_a = base + wm * TM * 32 * ROWB, *base_b = base + A_BYTES + wn * TN * 32 * ROWB;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r = wm * TM * 32 + i * 32 + l32;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(base + r * ROWB + 16 * (chunk(ks) ^ swz<ROWB>(r)));
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base_a + i * 32 * ROWB);
       o.a[i] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sa[i] = ks == 0 ? scale_word(base + SA_OFF + SPR * r) : prev.sa[i];
+      if constexpr (MX)
+        o.sa[i] = ks == 0 ? scale_word(smem + slot_ * STAGE + SA_OFF + SPR * (wm * TM * 32 + i * 32 + l32))
+                          : prev.sa[i];
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int r = wn * TN * 32 + j * 32 + l32;
-      const i32x4 v =
-          *reinterpret_cast<const i32x4 *>(base + A_BYTES + r * ROWB + 16 * (chunk(ks) ^ swz<ROWB>(r)));
+      const i32x4 v = *reinterpret_cast<const i32x4 *>(base_b + j * 32 * ROWB);
       o.b[j] = i32x8{v.x, v.y, v.z, v.w, 0, 0, 0, 0};
-      if constexpr (MX) o.sb[j] = ks == 0 ? scale_word(base + SB_OFF + SPR * r) : prev.sb[j];
+      if constexpr (MX)
+        o.sb[j] = ks == 0 ? scale_word(smem + slot_ * STAGE + SB_OFF + SPR * (wn * TN * 32 + j * 32 + l32))
+                          : prev.sb[j];
     }
   };
   auto mfmas = [&](const Ops &o, auto ks_c) {
@@ -439,21 +520,86 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
-  // Stage st sits in slot st % NS.  Stages 0 .. NS-1 are issued up front; in iteration st, once
-  // every wave has read all of stage st, stage st + NS is issued into its slot.  Every iteration
-  // issues exactly one stage of loads (past the last stage it reloads the last stage into the slot
-  // just freed, which is never read again), so the loop body has no branches and each wait is one
-  // constant: after stage st + 1, NS - 2 stages of this wave's loads may still be in flight.
+  // Epilogue staging: each wave writes one 32-row block of its tile at a time into its own LDS area
+  // (row-major, padded), then stores it with 16-byte writes along the rows of C.  PERSIST stages in
+  // the slot of the tile's last stage (the other slot holds the next tile's first stage).
+  constexpr int WCOLS = TN * 32;                    // columns of a wave's tile
+  constexpr int EPAD = 16 / (int)sizeof(OutT);      // 16 bytes of padding per row
+  constexpr int EROW = WCOLS + EPAD;                // elements per staged row
+  constexpr int VEC = 16 / (int)sizeof(OutT);       // elements per 16-byte store
+  constexpr int LPR = WCOLS / VEC;                  // lanes per row
+  constexpr int RPI = 64 / LPR;                     // rows per store instruction
+  constexpr int EBYTES = WAVES * 32 * EROW * (int)sizeof(OutT);
+  static_assert(EBYTES <= (PERSIST ? STAGE : NS * STAGE), "epilogue staging must fit in the ring");
+  static_assert(!PERSIST || ring_stage_holds_epilogue<WGM, WGN, TM, TN, OutT, MX, ROWB>(), "staging size");
+  const bool vec_ok = ((uintptr_t)C % 16 == 0) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+  auto epilogue = [&](int m0, int n0, uint8_t *area) {
+    // lane-dependent addresses come from an opaque copy of the lane index, so that the compiler
+    // computes them here instead of holding them in registers across the whole tile loop
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+    const int l32 = ln & 31, h = ln >> 5;
+    OutT *stage_out = reinterpret_cast<OutT *>(area) + wave * 32 * EROW;
+    const int col0 = n0 + wn * WCOLS;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) issue(min(s, nst - 1), s);
-  wait_vmcnt<(NS - 1) * LOADS>();
-  stage_barrier();
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          // registers v and v + 1 hold rows r and r + 1 of the same column
+          const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+          OutT *o = stage_out + r * EROW + j * 32 + l32;
+          if constexpr (sizeof(OutT) == 4) {
+            o[0] = alpha * acc[i][j][v];
+            o[EROW] = alpha * acc[i][j][v + 1];
+          } else {
+            const uint32_t p = f32x2_to_bf16x2(alpha * acc[i][j][v], alpha * acc[i][j][v + 1]);
+            o[0] = (uint16_t)p;
+            o[EROW] = (uint16_t)(p >> 16);
+          }
+        }
+      const int row0 = m0 + wm * TM * 32 + i * 32;
+#pragma unroll
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int r = q * RPI + ln / LPR, c = (ln % LPR) * VEC;
+        const int row = row0 + r, col = col0 + c;
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(stage_out + r * EROW + c);
+        if (row < M) {
+          OutT *dst = C + (int64_t)row * ldc + col;
+          if (vec_ok && col + VEC <= N) {
+            *reinterpret_cast<i32x4 *>(dst) = v;
+          } else {
+            const OutT *e = reinterpret_cast<const OutT *>(&v);
+#pragma unroll
+            for (int t = 0; t < VEC; ++t)
+              if (col + t < N) dst[t] = e[t];
+          }
+        }
+      }
+    }
+  };
 
+  // Stage g of the stream sits in slot g % NS.  Stages 0 .. NS-1 are issued up front; in the
+  // iteration of stage g, once every wave has read all of it, stage g + NS is issued into its slot.
+  // After stage g + 1 has landed, NS - 2 stages of this wave's loads may still be in flight.
   Ops o0, o1;
-  read_ops(0, std::integral_constant<int, 0>{}, o0, o1);
   int slot = 0;
-  for (int st = 0; st < nst; ++st) {
-    // k steps 0 .. KS-2: read step ks + 1 while step ks's MFMAs run (KS is even: o0 holds the even steps)
+  // k steps 0 .. KS-2 of the stage in `slot`: read step ks + 1 while step ks's MFMAs run (KS is even:
+  // o0 holds the even steps), then wait until stage g + 1 has landed and every wave is past stage g
+  // PERSIST: the MFMAs issued so far are placed here.  The compiler treats them as pure and would
+  // otherwise sink them below later branches (the tile-boundary branch of the issue stream, the
+  // epilogue's row blocks), past the barrier and with every k step's operands live at once.  The
+  // empty asm emits nothing.
+  auto pin_acc = [&]() {
+    if constexpr (PERSIST) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) __asm__ volatile("" : "+v"(acc[i][j]));
+    }
+  };
+  auto stage_body = [&]() {
     unroll(std::make_integer_sequence<int, KS - 1>{}, [&](auto ks_c) {
       constexpr int ks = decltype(ks_c)::value;
       if constexpr (ks % 2 == 0) {
@@ -464,66 +610,73 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mx_gemm_ring_kernel(
         mfmas(o1, ks_c);
       }
     });
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);  // keep these MFMAs ahead of the barrier below
-    const int next = slot == NS - 1 ? 0 : slot + 1;
-    wait_lgkmcnt0();                    // this wave's reads of stage st are complete
-    wait_vmcnt<(NS - 2) * LOADS>();     // stage st + 1 has landed
-    stage_barrier();                    // ... for every wave, and nobody reads stage st any more
-    issue(min(st + NS, nst - 1), slot);
-    read_ops(next, std::integral_constant<int, 0>{}, o0, o1);  // the next stage's first k step
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(o1, std::integral_constant<int, KS - 1>{});
-    slot = next;
-  }
-
-  // Epilogue through LDS: each wave writes one 32-row block of its tile at a time into its own
-  // LDS area (row-major, padded), then stores it with 16-byte writes along the rows of C.
-  __syncthreads();  // every wave is done reading the ring
-  constexpr int WCOLS = TN * 32;                    // columns of a wave's tile
-  constexpr int EPAD = 16 / (int)sizeof(OutT);      // 16 bytes of padding per row
-  constexpr int EROW = WCOLS + EPAD;                // elements per staged row
-  constexpr int VEC = 16 / (int)sizeof(OutT);       // elements per 16-byte store
-  constexpr int LPR = WCOLS / VEC;                  // lanes per row
-  constexpr int RPI = 64 / LPR;                     // rows per store instruction
-  static_assert(WAVES * 32 * EROW * (int)sizeof(OutT) <= NS * STAGE, "epilogue staging must fit in the ring");
-  OutT *stage_out = reinterpret_cast<OutT *>(smem) + wave * 32 * EROW;
-  const int col0 = n0 + wn * WCOLS;
-  const bool vec_ok = ((uintptr_t)C % 16 == 0) && ((ldc * (int64_t)sizeof(OutT)) % 16 == 0);
+    wait_lgkmcnt0();                    // this wave's reads of stage g are complete
+    wait_vmcnt<(NS - 2) * LOADS>();     // stage g + 1 has landed
+    stage_barrier();                    // ... for every wave, and nobody reads stage g any more
+  };
+  if constexpr (!PERSIST) {
+    // one tile: past the last stage every iteration reloads the last stage into the slot just freed
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int s = 0; s < NS; ++s) issue(min(s, nst - 1), s);
+    wait_vmcnt<(NS - 1) * LOADS>();
+    stage_barrier();
+    read_ops(0, std::integral_constant<int, 0>{}, o0, o1);
+    for (int st = 0; st < nst; ++st) {
+      stage_body();
+      const int next = slot == NS - 1 ? 0 : slot + 1;
+      issue(min(st + NS, nst - 1), slot);
+      read_ops(next, std::integral_constant<int, 0>{}, o0, o1);  // the next stage's first k step
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(o1, std::integral_constant<int, KS - 1>{});
+      slot = next;
+    }
+    int tm, tn;
+    tile_of(blockIdx.x, total, tiles_m, tiles_n, tm, tn);
+    __syncthreads();  // every wave is done reading the ring
+    epilogue(tm * BM, tn * BN, smem);
+  } else {
+    // The issue stream continues from one tile into the next.  A tile's last stage is peeled: its
+    // issue waits until the epilogue has staged the output through that stage's slot (the other
+    // slot already holds the next tile's first stage), and a tile with no successor issues nothing
+    // more.  Every wait is vmcnt(0) (two slots), so the epilogue's stores in the counter are waited
+    // for with the loads.
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        // registers v and v + 1 hold rows r and r + 1 of the same column
-        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-        OutT *o = stage_out + r * EROW + j * 32 + l32;
-        if constexpr (sizeof(OutT) == 4) {
-          o[0] = alpha * acc[i][j][v];
-          o[EROW] = alpha * acc[i][j][v + 1];
-        } else {
-          const uint32_t p = f32x2_to_bf16x2(alpha * acc[i][j][v], alpha * acc[i][j][v + 1]);
-          o[0] = (uint16_t)p;
-          o[EROW] = (uint16_t)(p >> 16);
-        }
+    for (int s = 0; s < NS; ++s) issue_next(s);
+    wait_vmcnt<(NS - 1) * LOADS>();
+    stage_barrier();
+    read_ops(0, std::integral_constant<int, 0>{}, o0, o1);
+#pragma nounroll
+    for (int j = 0; j < ntiles; ++j) {
+#pragma nounroll
+      for (int st = 0; st + 1 < nst; ++st) {
+        stage_body();
+        const int next = slot == NS - 1 ? 0 : slot + 1;
+        issue_next(slot);
+        read_ops(next, std::integral_constant<int, 0>{}, o0, o1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(o1, std::integral_constant<int, KS - 1>{});
+        slot = next;
       }
-    const int row0 = m0 + wm * TM * 32 + i * 32;
+      stage_body();
+      mfmas(o1, std::integral_constant<int, KS - 1>{});
+      pin_acc();
+      int tm, tn;
+      tile_of((int)blockIdx.x + j * (int)gridDim.x, total, tiles_m, tiles_n, tm, tn);
+      epilogue(tm * BM, tn * BN, smem + slot * STAGE);
+      const int next = slot == NS - 1 ? 0 : slot + 1;
+      if (j + 1 < ntiles) {
+        wait_lgkmcnt0();  // this wave's staging reads are complete
+        stage_barrier();  // ... for every wave: the slot may be refilled
+        issue_next(slot);
 #pragma unroll
-    for (int q = 0; q < 32 / RPI; ++q) {
-      const int r = q * RPI + lane / LPR, c = (lane % LPR) * VEC;
-      const int row = row0 + r, col = col0 + c;
-      const i32x4 v = *reinterpret_cast<const i32x4 *>(stage_out + r * EROW + c);
-      if (row < M) {
-        OutT *dst = C + (int64_t)row * ldc + col;
-        if (vec_ok && col + VEC <= N) {
-          *reinterpret_cast<i32x4 *>(dst) = v;
-        } else {
-          const OutT *e = reinterpret_cast<const OutT *>(&v);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int t = 0; t < VEC; ++t)
-            if (col + t < N) dst[t] = e[t];
-        }
+          for (int j2 = 0; j2 < TN; ++j2) acc[i][j2] = f32x16{0};
+        read_ops(next, std::integral_constant<int, 0>{}, o0, o1);
       }
+      slot = next;
     }
   }
 }
@@ -557,6 +710,17 @@ hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, co
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   const ScaleLayout sl = staged ? ScaleLayout{SPR, (int64_t)m * SPR, SPR, (int64_t)n * SPR}
                                 : ScaleLayout{k / 32, SPR, k / 32, SPR};
+  if constexpr (NS == 2 && ring_stage_holds_epilogue<WGM, WGN, TM, TN, OutT, true, ROWB>()) {
+    // more tiles than CUs: one persistent workgroup per CU walks its tiles, fetching the next
+    // tile's first stage while it finishes the current one
+    const int grid = splits == 1 ? persistent_grid(tiles, std::max(m, n), k / 2) : 0;
+    if (grid > 0) {
+      hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16, true>), dim3(grid),
+                         dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), sl,
+                         (const float *)nullptr, (const float *)nullptr, alpha, c, ldc);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16>),
                      dim3((unsigned)tiles, (unsigned)splits), dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n,
                      k / (2 * ROWB) / splits, (int64_t)(k / 2), sl, (const float *)nullptr, (const float *)nullptr,
@@ -907,6 +1071,16 @@ hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, 
                             const float *gb, OutT *c, int64_t ldc, hipStream_t s) {
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if constexpr (NS == 2 && ring_stage_holds_epilogue<WGM, WGN, TM, TN, OutT, false, ROWB>()) {
+    const int grid = persistent_grid(tiles, std::max(m, n), (int64_t)kp * 2);
+    if (grid > 0) {
+      hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false, ROWB, false, true>), dim3(grid),
+                         dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr,
+                         (const uint8_t *)b, (const uint8_t *)nullptr, m, n, kp * 2 / ROWB, (int64_t)kp * 2,
+                         ScaleLayout{0, 0, 0, 0}, ga, gb, 1.0f, c, ldc);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false, ROWB>), dim3((unsigned)tiles),
                      dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr, (const uint8_t *)b,
                      (const uint8_t *)nullptr, m, n, kp * 2 / ROWB, (int64_t)kp * 2, ScaleLayout{0, 0, 0, 0}, ga, gb,

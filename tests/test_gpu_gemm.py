@@ -307,6 +307,31 @@ def test_gemm_full_size_sampled_rows(out_dtype):
     _check(c, ac, as_, bc, bs, k, bf16=out_dtype == torch.bfloat16, rows=rows)
 
 
+# More 256 x 256 tiles than CUs: each workgroup walks several tiles, fetching the next tile's first
+# stage while it finishes the current one and staging the output through a ring slot.  Ragged edges
+# in both dimensions, one stage per tile (K = 256) and several, stage-major and row-major scales.
+@pytest.mark.parametrize("m,n,k,use_ws", [(4100, 4200, 256, True), (4100, 4200, 256, False),
+                                          (4352, 4160, 768, True), (4352, 4160, 768, False)])
+def test_gemm_persistent_tiles_exact(m, n, k, use_ws):
+    rng = np.random.default_rng(3100 + m + k + use_ws)
+    ac, _ = _rand_mx(rng, m, k)
+    bc, _ = _rand_mx(rng, n, k)
+    as_ = np.full((m, k // 32), 127, np.uint8)
+    bs = np.full((n, k // 32), 127, np.uint8)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    fq = _fq()
+    c32 = fq.gemm_mxfp4((a, asd), (b, bsd), use_workspace=use_ws)
+    c16 = fq.gemm_mxfp4((a, asd), (b, bsd), use_workspace=use_ws, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.unique(np.concatenate([[0, 255, 256, 4095, 4096, m - 1], rng.choice(m, 40, replace=False)])))
+    ref = GM.gemm(GM.decode_mxfp4_64(ac, as_)[rows], GM.decode_mxfp4_64(bc, bs))
+    r = torch.from_numpy(rows).to(DEV)
+    np.testing.assert_array_equal(c32[r].cpu().numpy().astype(np.float64), ref)
+    # exact float32 sums, so the bfloat16 output is their round-to-nearest-even
+    ref16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(c16[r].cpu(), ref16)
+
+
 # ----------------------------------------------------------- NVFP4 operands ----
 # Bar: the operands are decoded exactly (q * E4M3 in bfloat16) and each product is exact in the
 # float32 accumulator, so |C - C_exact| <= (2 ceil(K/16) + 3) * 2^-24 * sum_k |a_ik b_jk|, with
@@ -475,6 +500,25 @@ def test_gemm_nvfp4_ring_within_bound(m, n, k, out_dtype):
     got = big.float().cpu().numpy().astype(np.float64)
     _check_nv(got[:, :n], ac, as_, ag, bc, bs, bg, k, bf16=out_dtype == torch.bfloat16)
     assert (got[:, n:] == 7.0).all()  # the padding past n is untouched
+
+
+def test_gemm_nvfp4_persistent_tiles_exact():
+    """bfloat16 output over more 256 x 256 tiles than CUs (the decode pass and the bf16 ring walking
+    several tiles per workgroup), ragged in both dimensions, unit scales: every sum is exact, so the
+    output is its round-to-nearest-even."""
+    rng = np.random.default_rng(5650)
+    m, n, k = 4100, 4200, 512
+    ac, _ = _rand_nv(rng, m, k)
+    bc, _ = _rand_nv(rng, n, k)
+    as_ = np.full((m, k // 16), 0x38, np.uint8)
+    bs = np.full((n, k // 16), 0x38, np.uint8)
+    a, asd, b, bsd = _dev(ac, as_, bc, bs)
+    c16 = _fq().gemm_nvfp4((a, asd, 1.0), (b, bsd, 1.0), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.unique(np.concatenate([[0, 255, 256, 4095, 4096, m - 1], rng.choice(m, 40, replace=False)])))
+    ref = GM.gemm(GM.decode_nvfp4_64(ac, as_, np.float32(1))[rows], GM.decode_nvfp4_64(bc, bs, np.float32(1)))
+    ref16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(c16[torch.from_numpy(rows).to(DEV)].cpu(), ref16)
 
 
 def test_gemm_nvfp4_full_size_sampled_rows():
