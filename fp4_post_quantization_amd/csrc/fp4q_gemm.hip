@@ -283,14 +283,25 @@ int device_cus() {
   return cache[dev];
 }
 
-// Grid of the persistent ring: one workgroup per CU, a multiple of the XCD count so that the
-// workgroup -> XCD assignment matches the tile order; 0 (use the one-tile form) when a product has
-// no more tiles than that, or when an operand's rows (rows x row_bytes, row_bytes >= its scale
-// bytes per row) reach 4 GiB, past the kernel's 32-bit load offsets.
-int persistent_grid(int64_t tiles, int64_t rows, int64_t row_bytes) {
+// LDS bytes of a ring kernel instantiation, and the workgroups of it one CU holds (160 KB of LDS
+// per CU on gfx950; the ring kernels are LDS-bound in occupancy).
+template <int WGM, int WGN, int TM, int TN, int NS, bool MX, int ROWB, bool SCALE16>
+constexpr int ring_lds_bytes() {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32, SPR = ROWB / 16;
+  constexpr int stage = MX ? (BM + BN) * (ROWB + SPR) : (BM + BN) * ROWB;
+  return NS * stage + (SCALE16 ? 1024 : 256);
+}
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Grid of the persistent ring: as many workgroups as the CUs hold at once (per_cu each), a
+// multiple of the XCD count so that the workgroup -> XCD assignment matches the tile order; 0 (use
+// the one-tile form) when a product has no more tiles than that, or when an operand's rows (rows x
+// row_bytes, row_bytes >= its scale bytes per row) reach 4 GiB, past the kernel's 32-bit load
+// offsets.
+int persistent_grid(int64_t tiles, int64_t rows, int64_t row_bytes, int per_cu) {
   if (rows * row_bytes + 4096 > (int64_t)UINT32_MAX) return 0;
-  const int cus = device_cus();
-  const int g = cus - cus % kXcds;
+  const int slots = device_cus() * per_cu;
+  const int g = slots - slots % kXcds;
   return (g > 0 && tiles > g) ? g : 0;
 }
 
@@ -713,7 +724,8 @@ hipError_t launch_ring(const uint8_t *a, const uint8_t *as, const uint8_t *b, co
   if constexpr (NS == 2 && ring_stage_holds_epilogue<WGM, WGN, TM, TN, OutT, true, ROWB>()) {
     // more tiles than CUs: one persistent workgroup per CU walks its tiles, fetching the next
     // tile's first stage while it finishes the current one
-    const int grid = splits == 1 ? persistent_grid(tiles, std::max(m, n), k / 2) : 0;
+    constexpr int per_cu = kLdsPerCu / ring_lds_bytes<WGM, WGN, TM, TN, NS, true, ROWB, SCALE16>();
+    const int grid = splits == 1 ? persistent_grid(tiles, std::max(m, n), k / 2, per_cu) : 0;
     if (grid > 0) {
       hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, true, ROWB, SCALE16, true>), dim3(grid),
                          dim3(64 * WGM * WGN), 0, s, a, as, b, bs, m, n, k / (2 * ROWB), (int64_t)(k / 2), sl,
@@ -1072,7 +1084,8 @@ hipError_t launch_ring_bf16(const uint16_t *a, const uint16_t *b, int m, int n, 
   constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   if constexpr (NS == 2 && ring_stage_holds_epilogue<WGM, WGN, TM, TN, OutT, false, ROWB>()) {
-    const int grid = persistent_grid(tiles, std::max(m, n), (int64_t)kp * 2);
+    constexpr int per_cu = kLdsPerCu / ring_lds_bytes<WGM, WGN, TM, TN, NS, false, ROWB, false>();
+    const int grid = persistent_grid(tiles, std::max(m, n), (int64_t)kp * 2, per_cu);
     if (grid > 0) {
       hipLaunchKernelGGL((mx_gemm_ring_kernel<WGM, WGN, TM, TN, NS, OutT, false, ROWB, false, true>), dim3(grid),
                          dim3(64 * WGM * WGN), 0, s, (const uint8_t *)a, (const uint8_t *)nullptr,
@@ -1191,11 +1204,12 @@ hipError_t dispatch(const uint8_t *a, const uint8_t *as, const uint8_t *b, const
     return launch_ring<2, 4, 4, 2, 2, OutT, 128, true>(a, was, b, wbs, m, n, k, alpha, c, ldc, s, true);
   }
   // direct-to-LDS ring: 256 x 256 tiles when they give every CU a workgroup, 128 x 128 down to half
-  // the CUs, 64 x 64 for few-token products; stages of 128 code bytes per row (full 128-byte lines per
-  // load) when K allows, else 64
+  // the CUs (two slots, so that two workgroups share a CU: measured 11-16% faster than three slots
+  // and one), 64 x 64 for few-token products; stages of 128 code bytes per row (full 128-byte lines
+  // per load) when K allows, else 64
   if (k % 256 == 0 && aligned(as, 4) && aligned(bs, 4)) {
     if (big >= 256) return launch_ring<2, 4, 4, 2, 2, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
-    if (mid >= 128) return launch_ring<2, 2, 2, 2, 3, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
+    if (mid >= 128) return launch_ring<2, 2, 2, 2, 2, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
     return launch_ring<2, 2, 1, 1, 4, OutT, 128>(a, as, b, bs, m, n, k, alpha, c, ldc, s);
   }
   if (k % 128 == 0 && aligned(as, 4) && aligned(bs, 4)) {

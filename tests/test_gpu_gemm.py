@@ -307,11 +307,14 @@ def test_gemm_full_size_sampled_rows(out_dtype):
     _check(c, ac, as_, bc, bs, k, bf16=out_dtype == torch.bfloat16, rows=rows)
 
 
-# More 256 x 256 tiles than CUs: each workgroup walks several tiles, fetching the next tile's first
-# stage while it finishes the current one and staging the output through a ring slot.  Ragged edges
-# in both dimensions, one stage per tile (K = 256) and several, stage-major and row-major scales.
+# More tiles than the CUs hold at once: each workgroup walks several tiles, fetching the next
+# tile's first stage while it finishes the current one and staging the output through a ring slot.
+# Ragged edges in both dimensions, one stage per tile (K = 256) and several, stage-major and
+# row-major scales; 256 x 256 tiles (289 and 306 of them, one workgroup per CU) and 128 x 128 tiles
+# (528, two workgroups per CU).
 @pytest.mark.parametrize("m,n,k,use_ws", [(4100, 4200, 256, True), (4100, 4200, 256, False),
-                                          (4352, 4160, 768, True), (4352, 4160, 768, False)])
+                                          (4352, 4160, 768, True), (4352, 4160, 768, False),
+                                          (4100, 2000, 256, False), (4100, 2000, 768, True)])
 def test_gemm_persistent_tiles_exact(m, n, k, use_ws):
     rng = np.random.default_rng(3100 + m + k + use_ws)
     ac, _ = _rand_mx(rng, m, k)
