@@ -47,23 +47,30 @@ COPY_BYTES = 256 * 2**20  # bench.py --copy-calib: one read and one write of 256
 
 # (N, K) of the projections of an 8B-shaped layer by GEMM kernel instantiation, and the widths of
 # its four activation inputs
-_W4A4_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, true, 128, true>"
-_W4A4_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 3, unsigned short, true, 128, false>"
+_W4A4_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, true, 128, true, true>"
+_W4A4_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 2, unsigned short, true, 128, false, false>"
 _W4A4_NK_BIG = [(4096, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
 _W4A4_NK_SMALL = [(1024, 4096), (1024, 4096)]
 _W4A4_IN = [4096, 4096, 4096, 14336]
 
 
-# NVFP4 W4A4 layer: bf16 ring instantiations (256 x 256 tiles: q, o, gate, up, down; 128 x 128: k, v)
-_W4A4NV_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, false, 128, false>"
-_W4A4NV_SMALL = "mx_gemm_ring_kernel<2, 2, 2, 2, 4, unsigned short, false, 64, false>"
-# decode passes: per product one of A (8192 x K) and one of B (N x K): codes + scales in, bf16 out
-_W4A4NV_DECODE = [8192 * k for n, k in _W4A4_NK_BIG + _W4A4_NK_SMALL] + [n * k for n, k in
-                                                                         _W4A4_NK_BIG + _W4A4_NK_SMALL]
+# NVFP4 W4A4 layer: q, o, gate, up, down through the decode pass and the bf16 ring (256 x 256 tiles)
+_W4A4NV_BIG = "mx_gemm_ring_kernel<2, 4, 4, 2, 2, unsigned short, false, 128, false, true>"
+# k, v: NVFP4 codes staged in LDS and decoded in registers (128 x 128 tiles)
+_W4A4NV_SMALL = "nv_gemm_ring_kernel<2, 2, 2, 2, 4, unsigned short>"
+# decode passes: per large product one of A (8192 x K) and one of B (N x K): codes + scales in,
+# bf16 out
+_W4A4NV_DECODE = [8192 * k for n, k in _W4A4_NK_BIG] + [n * k for n, k in _W4A4_NK_BIG]
 
 
 def _bf16_gemm_mean(nks, what, m=8192):
     vals = [2 * m * n * k if what == "flops" else (m + n) * k * 2 + m * n * 2 for n, k in nks]
+    return sum(vals) / len(vals)
+
+
+def _nv_codes_gemm_mean(nks, what, m=8192):
+    # NVFP4 operands read as codes + E4M3 scales (one byte per 16 elements), bf16 output
+    vals = [2 * m * n * k if what == "flops" else (m + n) * k * (0.5 + 1 / 16) + m * n * 2 for n, k in nks]
     return sum(vals) / len(vals)
 
 
@@ -154,11 +161,11 @@ WORKLOADS = {
     "w4a4nv": {"stem": "nvfp4_w4a4_gemm_8b_layer_8192tok", "kernel": _W4A4NV_BIG,
                "title": "W4A4 NVFP4 layer (8B shapes, 8192 tokens): bf16-decoded operands on the bf16 matrix cores",
                "alg_bytes": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "bytes"),
-                             _W4A4NV_SMALL: _bf16_gemm_mean(_W4A4_NK_SMALL, "bytes"),
+                             _W4A4NV_SMALL: _nv_codes_gemm_mean(_W4A4_NK_SMALL, "bytes"),
                              "nvfp4_to_bf16_kernel": sum(e * (0.5 + 1 / 16 + 2) for e in _W4A4NV_DECODE)
                              / len(_W4A4NV_DECODE)},
                "alg_flops": {_W4A4NV_BIG: _bf16_gemm_mean(_W4A4_NK_BIG, "flops"),
-                             _W4A4NV_SMALL: _bf16_gemm_mean(_W4A4_NK_SMALL, "flops")},
+                             _W4A4NV_SMALL: _nv_codes_gemm_mean(_W4A4_NK_SMALL, "flops")},
                "extra_counters": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES"],
                "peak_tflops": 2500.0, "peak_label": "the published dense bf16/fp16 figure (the operands run on "
                                                     "the bf16 and fp16 matrix cores)",
