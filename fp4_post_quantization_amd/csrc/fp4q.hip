@@ -153,7 +153,7 @@ __device__ void finish_amax(uint32_t m, const AmaxOut &o) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   bool ok = true;
   if (o.imp) {
-    for (int i = blockIdx.x * kThreads + threadIdx.x; i < o.imp_n; i += gridDim.x * kThreads)
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < o.imp_n; i += (int64_t)gridDim.x * kThreads)
       ok &= (o.imp[i] >= 0.0f) & (o.imp[i] <= 3.402823466e38f);
   }
   m = wave_max_u32(m);
