@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -271,16 +272,21 @@ constexpr bool ring_stage_holds_epilogue() {
   return staging <= stage;
 }
 
-// Compute units of the current device (cached per device; 0 if the query fails).
+// Compute units of the current device (cached per device, safe to call from several host threads;
+// 0 if the query fails).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cache[dev] = n;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int q = 0;
+    if (hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && q > 0) {
+      cache[dev].store(q, std::memory_order_relaxed);
+      n = q;
+    }
   }
-  return cache[dev];
+  return n;
 }
 
 // LDS bytes of a ring kernel instantiation, and the workgroups of it one CU holds (160 KB of LDS
