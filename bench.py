@@ -21,7 +21,7 @@ initialised.  Before the warmup steps,
 untimed steps run for 0.3 s so the GPU has left its idle clocks.
 
 Other workloads (for the design notes, not the headline line) are selected
-with --config: c1, c2, c3a (MXFP4 AbsMax), c3b (MXFP4 window [-1,0]),
+with --config: c1, c2, c3a (MXFP4 window [-1,0]), c3b (MXFP4 AbsMax),
 c3c (MXFP4 after 32-point Hadamard), c4 (8B layer, MSE then WMSE),
 c5 (70B-shaped layer stream, 16-point Hadamard + WMSE; --layers N; outputs
 reduced to per-matrix checksums on the device, --state FILE records them per
@@ -236,8 +236,8 @@ def oracle_table(sample_rows=256):
                                                           window=(-3, 7), had=0)}),
         ("c2 NVFP4 WMSE [-8,7] bf16 4096x4096", {"c2": dict(x=f32(x2), fmt="nvfp4", imp=imp2.numpy(),
                                                             window=(-8, 7), had=0)}),
-        ("c3a MXFP4 AbsMax bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(0, 0), had=0)}),
-        ("c3b MXFP4 [-1,0] bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(-1, 0), had=0)}),
+        ("c3a MXFP4 [-1,0] bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(-1, 0), had=0)}),
+        ("c3b MXFP4 AbsMax bf16 8192x4096", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(0, 0), had=0)}),
         ("c3c MXFP4 [-1,0] after H32", {"c3": dict(x=x3, fmt="mxfp4", imp=None, window=(-1, 0), had=32)}),
     ]
     c4 = {n: f32(W.c4_matrix(n)) for n in W.LAYER_8B}
@@ -384,7 +384,7 @@ def run_other(args):
         res.update(elements=x.numel(), ms_step=ms, ms_sweep=msw, gel_s=x.numel() / ms / 1e6)
     elif args.config.startswith("c3"):
         x = W.c3_activation().to("cuda:0")
-        window = (0, 0) if args.config == "c3a" else (-1, 0)
+        window = (0, 0) if args.config == "c3b" else (-1, 0)
         had = 32 if args.config == "c3c" else 0
         bufs = _rotating_copies(x)
         out = fq.quantize_mxfp4(bufs[0], window=window, hadamard_n=had)
@@ -430,7 +430,7 @@ def run_other(args):
         # per-block gap quantiles on every workload: AbsMax - window and window - exhaustive
         gaps = {"c1 NVFP4 MSE": study.gap_report(study.nvfp4_block_losses(W.c1_weight().to("cuda:0"))),
                 "c2 NVFP4 WMSE": study.gap_report(study.nvfp4_block_losses(x2.to("cuda:0"), imp2.to("cuda:0"))),
-                "c3a/b MXFP4 [-1,0]": study.gap_report(study.mxfp4_block_losses(x3)),
+                "c3a MXFP4 [-1,0] (AbsMax = c3b)": study.gap_report(study.mxfp4_block_losses(x3)),
                 "c3c MXFP4 [-1,0] after H32": study.gap_report(study.mxfp4_block_losses(x3, hadamard_n=32))}
         del x3
         for loss in ("MSE", "WMSE"):

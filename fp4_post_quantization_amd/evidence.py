@@ -116,7 +116,7 @@ WORKLOADS = {
            "title": "NVFP4 WMSE ScaleSweep, bf16 4096x4096, offsets [-8,+7]",
            "alg_bytes": {"nvfp4_sweep_kernel": 4096 * 4096 * (2 + 0.5 + 6 / 16),
                          "amax_flat_kernel": 4096 * 4096 * 2}},
-    "c3b": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
+    "c3a": {"stem": "mxfp4_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 exponent window [-1,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
     # GPTQ on 4096 x 4096 (1024-column blocks of eight 128-column batches).  Per dispatch, averaged
@@ -181,7 +181,7 @@ WORKLOADS = {
                "title": "NVFP4 WMSE ScaleSweep after a 16-point block Hadamard, bf16 28672x8192 (70B gate)",
                "alg_bytes": {"nvfp4_sweep_kernel": 28672 * 8192 * (2 + 0.5 + 6 / 16),
                              "amax_chunks_kernel": 28672 * 8192 * 2}},
-    "c3a": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
+    "c3b": {"stem": "mxfp4_absmax_bf16_8192x4096", "kernel": "mxfp4_sweep_kernel",
             "title": "MXFP4 AbsMax window [0,0], bf16 8192x4096 activations",
             "alg_bytes": {"mxfp4_sweep_kernel": 8192 * 4096 * (2 + 0.5 + 6 / 32)}},
 }
