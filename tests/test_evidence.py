@@ -17,8 +17,8 @@ def test_rounds_split_over_xcds_by_hand():
 
 
 def test_resident_rounds_do_not_share_panels():
-    # one XCD, 2 resident tiles, a 2 x 2 grid: round 1 = tile rows 0, 1 of column 0 (2 A + 1 B),
-    # round 2 = the same rows of column 1 (2 A again + 1 B)
+    # one XCD, 2 resident tiles, a 2 x 2 grid: the first pair = tile rows 0, 1 of column 0 (2 A + 1 B),
+    # the second pair = the same rows of column 1 (2 A again + 1 B)
     assert panel_fetch(512, 512, 1, 256, 256, resident=2, xcds=1) == (2 + 1 + 2 + 1) * 256
 
 
