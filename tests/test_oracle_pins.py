@@ -895,3 +895,114 @@ def test_gemm_e8m0_nan_and_quantized_product():
     ref = X.astype(np.float64) @ W.astype(np.float64).T
     rel = np.linalg.norm(Cq - ref) / np.linalg.norm(ref)
     assert 0.01 < rel < 0.25, rel
+
+
+# -------------------------------------------------- GPTQ, static reordering ----
+def test_static_gptq_without_feedback_is_the_sweep():
+    """With a diagonal factor no error moves between columns, so static-order
+    GPTQ is round-to-nearest at the scales the quantizer picks on the weight
+    as given, whatever the processing order: codes and scales in the stored
+    order equal the plain quantizers' (NVFP4 MSE and WMSE, MXFP4 windows).
+    A column rounded at the scale of its processing slot's group instead of
+    its stored group's, or codes left in processing order, fail here."""
+    rng = np.random.default_rng(61)
+    W = (rng.standard_t(4, (12, 256)) * 0.02).astype(np.float32)
+    U = np.diag(np.exp(rng.normal(0.0, 0.3, 256))).astype(np.float32)
+    imp = np.exp(rng.standard_normal(256)).astype(np.float32)
+    perm = rng.permutation(256)
+    for im in (None, imp):
+        codes, scales, S = GQ.gptq_nvfp4_static(W, U, perm, im)
+        ref = Q.quantize_nvfp4(W, im)
+        np.testing.assert_array_equal(codes, ref.codes)
+        np.testing.assert_array_equal(scales, ref.scales)
+        assert S == ref.global_scale
+        for win in ((-1, 0), (-2, 1)):
+            codes, scales = GQ.gptq_mxfp4_static(W, U, perm, im, window=win)
+            ref = Q.quantize_mxfp4(W, im, window=win)
+            np.testing.assert_array_equal(codes, ref.codes)
+            np.testing.assert_array_equal(scales, ref.scales)
+
+
+def _gptq_static_explicit_inverse64(W, Hd, perm, xhat_col):
+    """Textbook GPTQ in float64 on the columns in the order perm, with the
+    explicit inverse of the Hessian in that order (rank-one elimination, no
+    Cholesky factor, no lazy batches); xhat_col(c, w32) rounds stored column
+    c at its fixed group scale and returns (code, x_hat)."""
+    W = np.array(W, dtype=np.float64)
+    rows, cols = W.shape
+    perm = np.asarray(perm)
+    Hinv = np.linalg.inv(np.asarray(Hd, dtype=np.float64)[perm][:, perm])
+    Wp = W[:, perm]
+    codes = np.zeros((rows, cols), np.uint8)
+    for j in range(cols):
+        c = int(perm[j])
+        codes[:, c], xhat = xhat_col(c, Wp[:, j].astype(np.float32))
+        d = (Wp[:, j] - xhat) / Hinv[j, j]
+        Wp[:, j + 1:] -= d[:, None] * Hinv[j, j + 1:][None, :]
+        Hinv = Hinv - np.outer(Hinv[:, j], Hinv[j, :]) / Hinv[j, j]
+    return Q.pack_nibbles(codes)
+
+
+def test_static_gptq_matches_explicit_inverse_formulation():
+    """Static-order GPTQ (Cholesky factor of the permuted inverse Hessian,
+    lazy batches, float32) against the float64 explicit-inverse elimination
+    in the same order with the plain quantizers' scales: agreement up to
+    rounding over two batches, for NVFP4 and MXFP4, far from round-to-nearest
+    and from the natural order.  A factor of the unpermuted Hessian, or a
+    processing order other than perm, fails here."""
+    import workloads as W_
+    rng = np.random.default_rng(62)
+    W = (rng.standard_t(4, (16, 256)) * 0.02).astype(np.float32)
+    X = W_.calibration_activations(512, 256, seed=63)
+    H, perm, U = W_.act_order_and_factor(X, damp=0.01)
+    assert np.all(np.diff(np.diag(H)[perm]) <= 0)
+    Hd = H + 0.01 * np.mean(np.diag(H)) * np.eye(256)
+
+    codes, scales, S = GQ.gptq_nvfp4_static(W, U, perm)
+    ref = Q.quantize_nvfp4(W)
+    np.testing.assert_array_equal(scales, ref.scales)
+    sdq = F.E4M3_VALUES[ref.scales].astype(np.float64) * float(S)
+    S_inv = np.float32(1.0) / S
+    recip = F.e4m3_reciprocal_table()
+
+    def nv_col(c, w):
+        p = ref.scales[:, c // 16]
+        idx = F.e2m1_rne_index(((np.abs(w) * S_inv).astype(np.float32) * recip[p]).astype(np.float32))
+        code = (np.signbit(w).astype(np.uint8) << 3) | idx
+        return code, np.where(np.signbit(w), -1.0, 1.0) * F.e2m1_value(idx).astype(np.float64) * sdq[:, c // 16]
+
+    c64 = _gptq_static_explicit_inverse64(W, Hd, perm, nv_col)
+    agree = np.mean(Q.unpack_nibbles(codes) == Q.unpack_nibbles(c64))
+    assert agree >= 0.995, agree
+    g = GQ.proxy_loss(W, codes, scales, S, H)
+    t = GQ.proxy_loss(W, c64, scales, S, H)
+    assert abs(g - t) <= 0.02 * t, (g, t)
+    assert np.mean(Q.unpack_nibbles(ref.codes) == Q.unpack_nibbles(c64)) < 0.9
+    nat = _gptq_static_explicit_inverse64(W, Hd, np.arange(256), nv_col)
+    assert np.mean(Q.unpack_nibbles(nat) == Q.unpack_nibbles(c64)) < 0.95
+
+    mcodes, mscales = GQ.gptq_mxfp4_static(W, U, perm)
+    mref = Q.quantize_mxfp4(W)
+    np.testing.assert_array_equal(mscales, mref.scales)
+    e = mref.scales.astype(np.int64) - 127
+
+    def mx_col(c, w):
+        idx = F.e2m1_rne_index((np.abs(w) * F.pow2_f32(-e[:, c // 32])).astype(np.float32))
+        code = (np.signbit(w).astype(np.uint8) << 3) | idx
+        return code, np.where(np.signbit(w), -1.0, 1.0) * F.e2m1_value(idx).astype(np.float64) * np.ldexp(1.0, e[:, c // 32])
+
+    m64 = _gptq_static_explicit_inverse64(W, Hd, perm, mx_col)
+    agree = np.mean(Q.unpack_nibbles(mcodes) == Q.unpack_nibbles(m64))
+    assert agree >= 0.995, agree
+    assert np.mean(Q.unpack_nibbles(mref.codes) == Q.unpack_nibbles(m64)) < 0.9
+
+
+def test_static_gptq_rejects_a_non_permutation():
+    W = np.zeros((2, 128), np.float32)
+    U = np.eye(128, dtype=np.float32)
+    bad = np.arange(128)
+    bad[5] = 6
+    with pytest.raises(ValueError):
+        GQ.gptq_nvfp4_static(W, U, bad)
+    with pytest.raises(ValueError):
+        GQ.gptq_mxfp4_static(W, U, np.arange(127))

@@ -205,6 +205,24 @@ def calibration_activations(n_tokens, n_channels, seed, corr=0.5):
     return z * lam
 
 
+def act_order_and_factor(x, damp=0.01):
+    """GPTQ's processing order for static reordering and the factor that goes
+    with it: perm lists the columns by descending diagonal of H = X^T X (ties
+    by index), and U is the upper Cholesky factor of (Hp + damp * mean(diag
+    H) * I)^-1 for Hp = H[perm][:, perm], as float32.  Returns (H, perm as
+    int32, U).  numpy's sort and dense linear algebra (input preparation,
+    not the path)."""
+    x = np.asarray(x, dtype=np.float64)
+    H = x.T @ x
+    perm = np.argsort(-np.diag(H), kind="stable").astype(np.int32)
+    Hp = H[perm][:, perm]
+    Hd = Hp + damp * np.mean(np.diag(H)) * np.eye(H.shape[0])
+    L = np.linalg.cholesky(Hd)
+    Linv = np.linalg.inv(L)
+    U = np.linalg.cholesky(Linv.T @ Linv).T
+    return H, perm, np.ascontiguousarray(U, dtype=np.float32)
+
+
 def hessian_and_factor(x, damp=0.01):
     """H = X^T X (float64) and U, the upper Cholesky factor of (H + damp *
     mean(diag H) * I)^-1, as float32: the inputs GPTQ consumes.  Computed
