@@ -23,7 +23,7 @@ from ._lib import FP4QError  # noqa: F401
 
 __all__ = [
     "quantize_nvfp4", "quantize_nvfp4_noalloc", "global_scale_nvfp4", "quantize_mxfp4", "quantize_relaxed",
-    "gptq_nvfp4", "gptq_mxfp4", "dequantize",
+    "gptq_nvfp4", "gptq_mxfp4", "gptq_static_nvfp4", "gptq_static_mxfp4", "dequantize",
     "block_hadamard", "gemm_mxfp4", "gemm_nvfp4",
     "NVFP4Result", "MXFP4Result", "workspace", "read_status", "clear_status", "FP4QError",
 ]
@@ -88,6 +88,8 @@ def _check_data(ws):
             names.append("invalid scale or coefficient")
         if st & L.DATA_BAD_HESSIAN:
             names.append("invalid inverse-Hessian factor")
+        if st & L.DATA_BAD_PERM:
+            names.append("processing order is not a permutation")
         raise FP4QError("data error: " + ", ".join(names))
 
 
@@ -438,6 +440,88 @@ def gptq_mxfp4(w, hinv_chol, importance=None, window=(-1, 0), *, ws=None, check=
         work.data_ptr(), rows, cols, work.stride(0), _ptr(src), ld_src, U.data_ptr(), _ptr(imp),
         int(window[0]), int(window[1]), out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(), ws.numel(),
         _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
+
+
+def _gptq_static_operands(w, perm, hinv_chol, importance):
+    """Static-order GPTQ operands: the weight as a float32 source the
+    library can read (copied when it is not one), float32 working storage,
+    the order as a dense int32 device vector, U and the importance (16-byte
+    aligned) and a workspace of the size the call needs."""
+    if w.dim() != 2 or not w.is_cuda:
+        raise ValueError("w must be a 2-D device tensor")
+    rows, cols = w.shape
+    dev = w.device
+    src = w
+    if not (w.dtype == torch.float32 and w.stride(1) == 1 and w.stride(0) % 4 == 0 and w.stride(0) >= cols
+            and w.data_ptr() % 16 == 0):
+        src = w.to(torch.float32).contiguous()
+    work = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    p = torch.as_tensor(perm, device=dev).to(torch.int32).contiguous()
+    if p.shape != (cols,):
+        raise ValueError("perm must have one entry per column")
+    U = torch.as_tensor(hinv_chol, dtype=torch.float32, device=dev).contiguous()
+    if U.shape != (cols, cols):
+        raise ValueError("hinv_chol must be [cols, cols]")
+    imp = _importance(importance, cols, dev)
+    if imp is not None and imp.data_ptr() % 16:
+        imp = imp.clone()
+    lib = L.load()
+    ws = torch.empty(lib.fp4q_gptq_static_workspace_bytes(rows, cols) + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    return src, work, p, U, imp, ws[off:off + lib.fp4q_gptq_static_workspace_bytes(rows, cols)]
+
+
+def gptq_static_nvfp4(w, perm, hinv_chol, importance=None, window=None, global_scale=None, *, check=False):
+    """GPTQ with static activation reordering, NVFP4 group scales.  w: [R, C]
+    weight in the stored order (C a multiple of 128; left unchanged); perm:
+    [C] processing order (slot j takes stored column perm[j]); hinv_chol:
+    [C, C] upper Cholesky factor of the damped inverse Hessian permuted to
+    that order; importance: stored-order WMSE weights or None.  Every
+    group's scale is the sweep's on w as given.  Returns an NVFP4Result (codes
+    and scales in the stored order) without losses and offsets."""
+    lib = L.load()
+    src, work, p, U, imp, ws = _gptq_static_operands(w, perm, hinv_chol, importance)
+    rows, cols = w.shape
+    dev = w.device
+    if window is None:
+        window = (-8, 7) if imp is not None else (-3, 7)
+    out = NVFP4Result(
+        codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+        global_scale=torch.empty(1, dtype=torch.float32, device=dev),
+        block_loss=None, offsets=None)
+    flags = 0
+    if global_scale is not None:
+        out.global_scale.copy_(torch.as_tensor(global_scale, dtype=torch.float32).reshape(1))
+        flags |= L.GIVEN_SCALE
+    L.check(lib.fp4q_gptq_static_nvfp4(
+        work.data_ptr(), rows, cols, work.stride(0), src.data_ptr(), src.stride(0), p.data_ptr(), U.data_ptr(),
+        _ptr(imp), int(window[0]), int(window[1]), flags, out.codes.data_ptr(), out.scales.data_ptr(),
+        out.global_scale.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev)))
+    if check:
+        _check_data(ws)
+    return out
+
+
+def gptq_static_mxfp4(w, perm, hinv_chol, importance=None, window=(-1, 0), *, check=False):
+    """gptq_static_nvfp4 with MXFP4 group exponents (the exponent sweep's on
+    w as given, window of exponent offsets).  Returns an MXFP4Result (codes
+    and E8M0 bytes in the stored order) without losses and offsets."""
+    lib = L.load()
+    src, work, p, U, imp, ws = _gptq_static_operands(w, perm, hinv_chol, importance)
+    rows, cols = w.shape
+    dev = w.device
+    out = MXFP4Result(
+        codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+        block_loss=None, offsets=None)
+    L.check(lib.fp4q_gptq_static_mxfp4(
+        work.data_ptr(), rows, cols, work.stride(0), src.data_ptr(), src.stride(0), p.data_ptr(), U.data_ptr(),
+        _ptr(imp), int(window[0]), int(window[1]), out.codes.data_ptr(), out.scales.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream(dev)))
     if check:
         _check_data(ws)
     return out

@@ -21,6 +21,7 @@ DATA_BAD_IMPORTANCE = 0x2
 DATA_BAD_GLOBAL_SCALE = 0x4
 DATA_BAD_SCALE = 0x8
 DATA_BAD_HESSIAN = 0x10
+DATA_BAD_PERM = 0x20
 
 EXPORTS = (
     "fp4q_version",
@@ -34,6 +35,9 @@ EXPORTS = (
     "fp4q_quantize_relaxed",
     "fp4q_gptq_nvfp4",
     "fp4q_gptq_mxfp4",
+    "fp4q_gptq_static_workspace_bytes",
+    "fp4q_gptq_static_nvfp4",
+    "fp4q_gptq_static_mxfp4",
     "fp4q_dequantize",
     "fp4q_block_hadamard",
     "fp4q_gemm_mxfp4",
@@ -63,6 +67,10 @@ _SIGNATURES = {
     "fp4q_quantize_relaxed": (_I, [_I, _P, _I, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P, _P, _SZ, _P]),
     "fp4q_gptq_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ, _P]),
     "fp4q_gptq_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
+    "fp4q_gptq_static_workspace_bytes": (_SZ, [_I64, _I64]),
+    "fp4q_gptq_static_nvfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I, _I, _U32, _P, _P, _P, _P, _SZ,
+                                    _P]),
+    "fp4q_gptq_static_mxfp4": (_I, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "fp4q_dequantize": (_I, [_I, _P, _P, _P, _I64, _I64, _I, _P, _P]),
     "fp4q_block_hadamard": (_I, [_P, _I, _I64, _I64, _I64, _I, _P, _P]),
     "fp4q_gemm_mxfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_float, _I, _P, _I64, _P, _SZ, _P]),

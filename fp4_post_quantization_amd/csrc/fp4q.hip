@@ -936,15 +936,24 @@ __device__ __forceinline__ void static_for(std::integer_sequence<int, I...>, F &
 // touched them yet); W is where its errors go.  pk >= 0: first apply the errors of the 128 columns
 // at pk (the previous batch, in W) to this batch's columns, for the workgroup's own rows: a
 // 16 x 128 x 128 contraction on fp32 MFMA (16x16x4) in place of a launch of the near update.
-template <bool WMSE, int FMT>
+//
+// GIVEN (static reordering): the batch's columns are processing slots i1 .. i1 + 127 of the order perm,
+// and every group's scale is fixed already: slot j of row r is rounded at the scale byte of its stored
+// group, scales[r][perm[j] / block] (row-major, cols / block bytes per row), read here and not
+// written.  The sweep at group starts is skipped; codes go to slot j's position in `codes`.
+template <bool WMSE, int FMT, bool GIVEN = false>
 __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     float *W, int64_t ld, const float *Win, int64_t ldin, int pk, int rows, int cols, int i1,
     const float *__restrict__ U,
     const float *__restrict__ imp, float *__restrict__ gscale, const uint32_t *__restrict__ partials,
-    int n_partials, int lo, int hi, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, Status status) {
+    int n_partials, int lo, int hi, uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, Status status,
+    const int32_t *__restrict__ perm = nullptr) {
   __shared__ __attribute__((aligned(1024))) float Ub[kGptqBatch][kGptqBatch];
   __shared__ float Vtab[128], Rtab[128], rdiag[kGptqBatch], impb[kGptqBatch];
   __shared__ float Pe[kGptqRowsPerWg][kGptqBatch + 4];  // pk >= 0: the rows' errors, then the update
+  // GIVEN: each row's value and reciprocal of its fixed scale for every column of the batch
+  __shared__ float Vg[GIVEN ? kGptqRowsPerWg : 1][GIVEN ? kGptqBatch : 1];
+  __shared__ float Rg[GIVEN ? kGptqRowsPerWg : 1][GIVEN ? kGptqBatch : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = lane & 15;
@@ -1043,6 +1052,28 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
     for (int k = 0; k < 8; ++k) w[k] = w[k] - Pe[tid >> 4][8 * t + k];
   }
   static_for(std::make_integer_sequence<int, 16>{}, [&](auto j_c) { stash_u(j_c); });
+  if constexpr (GIVEN) {
+    // lane t of a row: the scales of the batch's columns 8t .. 8t+7 (perm entries were range-checked by
+    // the call's first kernel; clamped here all the same)
+    constexpr int kBlk = FMT == FP4Q_MXFP4 ? 32 : 16;
+    const uint8_t *srow = scales + (int64_t)(live ? r : 0) * (cols / kBlk);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = min(max(perm[i1 + 8 * t + k], 0), cols - 1);
+      const int b = srow[c / kBlk];
+      float v, rc;
+      if constexpr (FMT == FP4Q_MXFP4) {
+        v = pow2f(b - 127);
+        rc = pow2f(127 - b);
+      } else {
+        const int pc = min(max(b, 1), 126);
+        v = kE4M3.v[pc];
+        rc = kE4M3.r[pc];
+      }
+      Vg[tid >> 4][8 * t + k] = v;
+      Rg[tid >> 4][8 * t + k] = rc;
+    }
+  }
   {  // MXFP4 and NVFP4 with a given scale run no global-max pass over the weights
     bool finite = true;
 #pragma unroll
@@ -1055,12 +1086,13 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) err8[k] = 0.0f;
   float V = 1.0f, R = 1.0f;
+  float vgn = GIVEN ? Vg[GIVEN ? tid >> 4 : 0][0] : 1.0f, rgn = GIVEN ? Rg[GIVEN ? tid >> 4 : 0][0] : 1.0f;
   f32x4 un0 = *reinterpret_cast<const f32x4 *>(&Ub[0][8 * t]);
   f32x4 un1 = *reinterpret_cast<const f32x4 *>(&Ub[0][8 * t + 4]);
   float rdn = rdiag[0];
   static_for(std::make_integer_sequence<int, 16>{}, [&](auto tt_c) {
     constexpr int tt = decltype(tt_c)::value;
-    if constexpr (MX && (tt & 3) == 0) {
+    if constexpr (!GIVEN && MX && (tt & 3) == 0) {
       // group [8 tt, 8 tt + 32): its values sit in lanes tt .. tt + 3 of the row
       float z[32], wg[32];
 #pragma unroll
@@ -1095,7 +1127,7 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
       R = pow2f(-es);
       if (live && t == 0) scales[(int64_t)r * (cols / 32) + ((i1 + 8 * tt) >> 5)] = (uint8_t)(es + 127);
     }
-    if constexpr (!MX && (tt & 1) == 0) {
+    if constexpr (!GIVEN && !MX && (tt & 1) == 0) {
       // group [8 tt, 8 tt + 16): its values sit in lanes tt and tt + 1 of the row
       float us[16], wg[16];
 #pragma unroll
@@ -1137,6 +1169,14 @@ __global__ __launch_bounds__(kGptqBatchThreads) void gptq_batch_kernel(
         un0 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t]);
         un1 = *reinterpret_cast<const f32x4 *>(&Ub[i + 1][8 * t + 4]);
         rdn = rdiag[i + 1];
+      }
+      if constexpr (GIVEN) {  // this column's fixed scale, read one column ahead like its U row
+        V = vgn;
+        R = rgn;
+        if (i + 1 < kGptqBatch) {
+          vgn = Vg[tid >> 4][i + 1];
+          rgn = Rg[tid >> 4][i + 1];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       const float wi = row_bcast<tt>(w[k]);
@@ -1498,6 +1538,73 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
   return rpt < 1 ? 1 : (rpt > 64 ? 64 : rpt);
 }
 
+// ------------------------------------------------ GPTQ, static reordering ----
+// "Bridging the Gap Between Promise and Performance for Microscaling FP4 Quantization", 2. Metodologia,
+// MR-GPTQ component 2: GPTQ's column order is applied once, while quantizing, so inference shuffles
+// nothing.  The columns are processed in the caller's order perm (slot j holds stored column perm[j]);
+// the groups, their scales and the codes stay in the stored order.
+
+// inv[perm[j]] = j for every slot j (entries of perm outside [0, cols) are reported and clamped).  The
+// call's first kernel: it takes the status slot.
+__global__ __launch_bounds__(kThreads) void perm_inverse_kernel(const int32_t *__restrict__ perm, int cols,
+                                                                 int32_t *__restrict__ inv, Status status) {
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  uint32_t err = 0u;
+  if (j < cols) {
+    const int p = perm[j];
+    if (p < 0 || p >= cols) err = FP4Q_DATA_BAD_PERM;
+    inv[min(max(p, 0), cols - 1)] = j;
+  }
+  status.finish(err);
+}
+
+// The weight in processing order, w[r][j] = w_in[r][perm[j]], four slots per thread (cols is a
+// multiple of 128).  Row 0 also checks that perm is a permutation: a repeated entry leaves a slot whose
+// entry of inv names another slot.
+__global__ __launch_bounds__(kThreads) void perm_gather_kernel(const float *__restrict__ w_in, int64_t ld_in,
+                                                                const int32_t *__restrict__ perm,
+                                                                const int32_t *__restrict__ inv, int rows, int cols,
+                                                                float *__restrict__ w, int64_t ld,
+                                                                uint32_t *__restrict__ status) {
+  const int q = cols / 4;
+  const int64_t total = (int64_t)rows * q;
+  uint32_t err = 0u;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (int64_t)gridDim.x * kThreads) {
+    const int r = (int)(g / q), j0 = (int)(g % q) * 4;
+    const float *src = w_in + (int64_t)r * ld_in;
+    f32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pc = min(max(perm[j0 + k], 0), cols - 1);
+      v[k] = src[pc];
+      if (r == 0 && inv[pc] != j0 + k) err = FP4Q_DATA_BAD_PERM;
+    }
+    *reinterpret_cast<f32x4 *>(w + (int64_t)r * ld + j0) = v;
+  }
+  if (err) atomicOr(status, err);
+}
+
+// Codes back in the stored order: the code of stored column c sits at slot inv[c] of the
+// processing-order codes cp (both [rows][cols / 2], low nibble first).  Sixteen columns per thread.
+__global__ __launch_bounds__(kThreads) void codes_unpermute_kernel(const uint8_t *__restrict__ cp,
+                                                                    const int32_t *__restrict__ inv, int rows,
+                                                                    int cols, uint8_t *__restrict__ codes) {
+  const int q = cols / 16;
+  const int64_t total = (int64_t)rows * q;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (int64_t)gridDim.x * kThreads) {
+    const int r = (int)(g / q), c0 = (int)(g % q) * 16;
+    const uint8_t *row = cp + (int64_t)r * (cols / 2);
+    uint32_t word[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int sl = min(max(inv[c0 + k], 0), cols - 1);
+      const uint32_t nib = (row[sl >> 1] >> (4 * (sl & 1))) & 0xFu;
+      word[k >> 3] |= nib << (4 * (k & 7));
+    }
+    *reinterpret_cast<uint2 *>(codes + (int64_t)r * (cols / 2) + c0 / 2) = make_uint2(word[0], word[1]);
+  }
+}
+
 // The GPTQ batches of either format: per 128-column batch the batch kernel,
 // then the lazy updates.  Within a block of kGptqBlock columns they follow a
 // binary tree: after batch t of the block, with m the lowest set bit of t + 1,
@@ -1506,11 +1613,15 @@ static int pick_rows_per_tile(int rows, int nbands, int64_t default_target) {
 // own batch, with the same flops as updating the whole rest of the block
 // after every batch, in fewer wide launches).  After the block's last batch,
 // all later columns get the block's error columns as one contraction.
-template <int FMT>
+//
+// GIVEN: static reordering (gptq_batch_kernel's GIVEN mode): the columns are processing slots of the
+// order perm, every group's scale is already in `scales`, and codes go to the slots' positions.
+template <int FMT, bool GIVEN = false>
 static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in, int64_t ld_in,
                          const float *hinv_chol, const float *importance, float *global_scale,
                          const uint32_t *partials, int n_partials, int off_lo, int off_hi, uint8_t *codes,
-                         uint8_t *scales, uint32_t *status_slot, bool first_kernel, hipStream_t s) {
+                         uint8_t *scales, uint32_t *status_slot, bool first_kernel, hipStream_t s,
+                         const int32_t *perm = nullptr) {
   const int gb = ceil_div(rows, kGptqRowsPerWg);
   // w holds columns [0, held); a launch reads the current values of later columns from w_in (the
   // caller's weight, untouched so far), so w needs no copy of it (w_in == w: in place)
@@ -1545,7 +1656,11 @@ static void gptq_batches(float *w, int64_t rows, int64_t cols, int64_t ld, const
     const bool old = i1 < held;
     const float *src = old ? w : w_in;
     const int64_t lds = old ? ld : ld_in;
-    if (importance)
+    if constexpr (GIVEN)
+      hipLaunchKernelGGL((gptq_batch_kernel<false, FMT, true>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, src,
+                         lds, pk, (int)rows, (int)cols, i1, hinv_chol, nullptr, global_scale, part, n_partials,
+                         off_lo, off_hi, codes, scales, status, perm);
+    else if (importance)
       hipLaunchKernelGGL((gptq_batch_kernel<true, FMT>), dim3(gb), dim3(kGptqBatchThreads), 0, s, w, ld, src, lds,
                          pk, (int)rows, (int)cols, i1, hinv_chol, importance, global_scale, part, n_partials,
                          off_lo, off_hi, codes, scales, status);
@@ -1820,17 +1935,18 @@ extern "C" fp4q_status_t fp4q_global_scale_nvfp4(const void *x, fp4q_dtype_t dty
   return last_hip_status();
 }
 
-extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
-                                             int64_t ld, const float *importance, int block,
-                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
-                                             uint8_t *codes, uint8_t *scales, float *block_loss,
-                                             int8_t *offsets, void *workspace, size_t workspace_bytes,
-                                             void *stream) {
+// fp4q_quantize_mxfp4 on a checked workspace's status word; status_first: the sweep is the call's
+// first kernel and takes the status slot (else it adds to the word).
+static fp4q_status_t quantize_mxfp4_on(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                                       const float *importance, int block, fp4q_loss_t loss, int off_lo,
+                                       int off_hi, int hadamard_n, uint8_t *codes, uint8_t *scales,
+                                       float *block_loss, int8_t *offsets, bool ws_ok, uint32_t *status,
+                                       bool status_first, hipStream_t s) {
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!x || !codes || !scales)) return FP4Q_ERR_NULL;
   if (loss != FP4Q_MSE && loss != FP4Q_WMSE) return FP4Q_ERR_ARG;
   if (loss == FP4Q_WMSE && !importance && !empty) return FP4Q_ERR_NULL;
-  if (!workspace || workspace_bytes < kWorkspaceBytes || !aligned(workspace, 8)) return FP4Q_ERR_WORKSPACE;
+  if (!ws_ok) return FP4Q_ERR_WORKSPACE;
   if (block != 32) return FP4Q_ERR_SHAPE;
   if (off_lo > 0 || off_hi < 0 || off_lo < -16 || off_hi > 16) return FP4Q_ERR_ARG;
   fp4q_status_t st = check_matrix(x, dtype, rows, cols, ld, block, hadamard_n);
@@ -1839,11 +1955,9 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   if (!empty && wmse && !aligned(importance, 16)) return FP4Q_ERR_ALIGN;
   if (!empty && (!aligned(codes, 8) || (block_loss && !aligned(block_loss, 4)))) return FP4Q_ERR_ALIGN;
 
-  hipStream_t s = (hipStream_t)stream;
-  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
   // the sweep is the call's only kernel and takes the status slot; an empty call gets a small kernel for it
   if (empty) {
-    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, status_first, nullptr, nullptr);
     return last_hip_status();
   }
 
@@ -1864,7 +1978,7 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
   a.n_partials = 0;
   a.given_scale = nullptr;
   a.check_inputs = true;  // no max pass read the importance
-  a.status_first = true;
+  a.status_first = status_first;
   a.codes = codes;
   a.scales = scales;
   a.gscale_out = nullptr;
@@ -1883,6 +1997,19 @@ extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, 
     });
   });
   return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_quantize_mxfp4(const void *x, fp4q_dtype_t dtype, int64_t rows, int64_t cols,
+                                             int64_t ld, const float *importance, int block,
+                                             fp4q_loss_t loss, int off_lo, int off_hi, int hadamard_n,
+                                             uint8_t *codes, uint8_t *scales, float *block_loss,
+                                             int8_t *offsets, void *workspace, size_t workspace_bytes,
+                                             void *stream) {
+  const bool ws_ok = workspace && workspace_bytes >= kWorkspaceBytes && aligned(workspace, 8);
+  return quantize_mxfp4_on(x, dtype, rows, cols, ld, importance, block, loss, off_lo, off_hi, hadamard_n, codes,
+                           scales, block_loss, offsets, ws_ok,
+                           ws_ok ? (uint32_t *)((char *)workspace + kWsStatus) : nullptr, true,
+                           (hipStream_t)stream);
 }
 
 extern "C" fp4q_status_t fp4q_quantize_relaxed(fp4q_format_t format, const void *x, fp4q_dtype_t dtype,
@@ -2007,6 +2134,119 @@ extern "C" fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, i
   gptq_batches<FP4Q_MXFP4>(w, rows, cols, ld, w_in, ld_in, hinv_chol, importance, nullptr, nullptr, 0, off_lo,
                            off_hi, codes, scales, status, true, s);
   return last_hip_status();
+}
+
+// --------------------------------------------------- static reordering ----
+// Workspace of the static-order GPTQ calls: the quantize workspace (status word, max-pass partials), then
+// the inverse order (int32 per column), then the codes in processing order.
+static int64_t round_up256(int64_t n) { return (n + 255) / 256 * 256; }
+static int64_t static_ws_inv(void) { return (int64_t)kWorkspaceBytes; }
+static int64_t static_ws_codes(int64_t cols) { return static_ws_inv() + round_up256(4 * cols); }
+
+extern "C" size_t fp4q_gptq_static_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return (size_t)(static_ws_codes(cols) + round_up256(rows * (cols / 2)));
+}
+
+// Argument checks of both static-order calls (the format's own window and alignment rules aside).
+static fp4q_status_t check_gptq_static(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                       int64_t ld_in, const int32_t *perm, const float *hinv_chol,
+                                       const float *importance, int off_lo, int off_hi, uint8_t *codes,
+                                       uint8_t *scales, void *workspace, size_t workspace_bytes) {
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (!w || !w_in || !perm || !hinv_chol || !codes || !scales)) return FP4Q_ERR_NULL;
+  if (!workspace || !aligned(workspace, 256) || rows < 0 || cols < 0 ||
+      workspace_bytes < fp4q_gptq_static_workspace_bytes(rows, cols))
+    return FP4Q_ERR_WORKSPACE;
+  if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
+  if (ld < cols || cols % kGptqBatch || ld_in < cols) return FP4Q_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
+    return FP4Q_ERR_SHAPE;
+  if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(w_in, 16) || ld_in % 4 || !aligned(hinv_chol, 16) ||
+                 !aligned(codes, 8) || !aligned(perm, 4) || (importance && !aligned(importance, 16))))
+    return FP4Q_ERR_ALIGN;
+  return FP4Q_OK;
+}
+
+// The steps shared by both formats around the scale pass `scales_pass` (which must only add to the status
+// word): the inverse order (the call's first kernel), the weight in processing order, the scales, the
+// GPTQ batches with fixed scales, and the codes back to the stored order.
+template <int FMT, typename ScalePass>
+static fp4q_status_t gptq_static_run(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                     int64_t ld_in, const int32_t *perm, const float *hinv_chol, int off_lo,
+                                     int off_hi, uint8_t *codes, uint8_t *scales, float *global_scale,
+                                     void *workspace, hipStream_t s, ScalePass scales_pass) {
+  char *ws = (char *)workspace;
+  uint32_t *status = (uint32_t *)(ws + kWsStatus);
+  int32_t *inv = (int32_t *)(ws + static_ws_inv());
+  uint8_t *codes_p = (uint8_t *)(ws + static_ws_codes(cols));
+  hipLaunchKernelGGL(perm_inverse_kernel, dim3(ceil_div(cols, kThreads)), dim3(kThreads), 0, s, perm, (int)cols,
+                     inv, Status{status, true});
+  const int64_t quads = rows * (cols / 4);
+  hipLaunchKernelGGL(perm_gather_kernel, dim3((int)std::min<int64_t>(ceil_div(quads, (int64_t)kThreads), 8192)),
+                     dim3(kThreads), 0, s, w_in, ld_in, perm, inv, (int)rows, (int)cols, w, ld, status);
+  const fp4q_status_t st = scales_pass();
+  if (st != FP4Q_OK) return st;
+  gptq_batches<FMT, true>(w, rows, cols, ld, w, ld, hinv_chol, nullptr, global_scale, nullptr, 0, off_lo, off_hi,
+                          codes_p, scales, status, false, s, perm);
+  const int64_t sixteens = rows * (cols / 16);
+  hipLaunchKernelGGL(codes_unpermute_kernel,
+                     dim3((int)std::min<int64_t>(ceil_div(sixteens, (int64_t)kThreads), 8192)), dim3(kThreads), 0,
+                     s, codes_p, inv, (int)rows, (int)cols, codes);
+  return last_hip_status();
+}
+
+extern "C" fp4q_status_t fp4q_gptq_static_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
+                                                const float *w_in, int64_t ld_in, const int32_t *perm,
+                                                const float *hinv_chol, const float *importance, int off_lo,
+                                                int off_hi, uint32_t flags, uint8_t *codes, uint8_t *scales,
+                                                float *global_scale, void *workspace, size_t workspace_bytes,
+                                                void *stream) {
+  if (!global_scale) return FP4Q_ERR_NULL;
+  fp4q_status_t st = check_gptq_static(w, rows, cols, ld, w_in, ld_in, perm, hinv_chol, importance, off_lo, off_hi,
+                                       codes, scales, workspace, workspace_bytes);
+  if (st != FP4Q_OK) return st;
+  if (flags & ~FP4Q_GIVEN_SCALE) return FP4Q_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  const bool given = flags & FP4Q_GIVEN_SCALE;
+  if (rows == 0 || cols == 0) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, given ? global_scale : nullptr,
+                       given ? nullptr : global_scale);
+    return last_hip_status();
+  }
+  return gptq_static_run<FP4Q_NVFP4>(
+      w, rows, cols, ld, w_in, ld_in, perm, hinv_chol, off_lo, off_hi, codes, scales, global_scale, workspace, s,
+      [&]() {
+        // S and every group's scale: the sweep on the stored weight (codes are overwritten later)
+        return quantize_nvfp4_on(w_in, FP4Q_F32, rows, cols, ld_in, importance, 16,
+                                 importance ? FP4Q_WMSE : FP4Q_MSE, off_lo, off_hi, 0,
+                                 flags | FP4Q_ACCUMULATE_STATUS, codes, scales, global_scale, nullptr, nullptr, true,
+                                 status, (uint32_t *)((char *)workspace + kWsPartials), s);
+      });
+}
+
+extern "C" fp4q_status_t fp4q_gptq_static_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld,
+                                                const float *w_in, int64_t ld_in, const int32_t *perm,
+                                                const float *hinv_chol, const float *importance, int off_lo,
+                                                int off_hi, uint8_t *codes, uint8_t *scales, void *workspace,
+                                                size_t workspace_bytes, void *stream) {
+  fp4q_status_t st = check_gptq_static(w, rows, cols, ld, w_in, ld_in, perm, hinv_chol, importance, off_lo, off_hi,
+                                       codes, scales, workspace, workspace_bytes);
+  if (st != FP4Q_OK) return st;
+  if (off_lo < -16 || off_hi > 16) return FP4Q_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t *status = (uint32_t *)((char *)workspace + kWsStatus);
+  if (rows == 0 || cols == 0) {
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(64), 0, s, status, true, nullptr, nullptr);
+    return last_hip_status();
+  }
+  return gptq_static_run<FP4Q_MXFP4>(
+      w, rows, cols, ld, w_in, ld_in, perm, hinv_chol, off_lo, off_hi, codes, scales, nullptr, workspace, s, [&]() {
+        return quantize_mxfp4_on(w_in, FP4Q_F32, rows, cols, ld_in, importance, 32,
+                                 importance ? FP4Q_WMSE : FP4Q_MSE, off_lo, off_hi, 0, codes, scales, nullptr,
+                                 nullptr, true, status, false, s);
+      });
 }
 
 extern "C" fp4q_status_t fp4q_dequantize(fp4q_format_t format, const uint8_t *codes, const uint8_t *scales,

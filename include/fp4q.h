@@ -107,6 +107,7 @@ typedef enum fp4q_format {
 #define FP4Q_DATA_BAD_GLOBAL_SCALE 0x4u /* given S is < 0, Inf or NaN */
 #define FP4Q_DATA_BAD_SCALE 0x8u        /* fp4q_quantize_relaxed: invalid scale byte or coefficient */
 #define FP4Q_DATA_BAD_HESSIAN 0x10u     /* fp4q_gptq_nvfp4: a diagonal entry of U is not finite and > 0 */
+#define FP4Q_DATA_BAD_PERM 0x20u        /* fp4q_gptq_static_*: perm is not a permutation of 0 .. cols-1 */
 
 /* Library version as 10000 * major + 100 * minor + patch. */
 int fp4q_version(void);
@@ -359,6 +360,69 @@ fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
                               int64_t ld_in, const float *hinv_chol, const float *importance, int off_lo,
                               int off_hi, uint8_t *codes, uint8_t *scales, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * GPTQ with static activation reordering ([MR] 2., MR-GPTQ component 2:
+ * GPTQ's column-reordering heuristic is applied once, when quantizing, so
+ * that inference shuffles nothing).  The columns are processed in the
+ * caller's order perm (GPTQ's heuristic puts the columns with the largest
+ * diagonal entries of H first); the groups stay the contiguous blocks of the
+ * stored order, and each group's scale is fixed before any update.
+ *
+ *   w          [rows x cols] float32, leading dimension ld (multiple of 4):
+ *              working storage, OVERWRITTEN (on return it holds the scaled
+ *              errors in processing order).
+ *   w_in       [rows x cols] float32, leading dimension ld_in (>= cols,
+ *              multiple of 4): the weight in the stored order, read only;
+ *              required, and must not overlap w.
+ *   perm       [cols] int32 device array: slot j of the processing order
+ *              takes stored column perm[j].
+ *   hinv_chol  [cols x cols] float32 row-major U, the upper Cholesky factor
+ *              of the inverse of the (damped) Hessian permuted to the
+ *              processing order, Hp = H[perm][:, perm], so Hp^-1 = U^T U.
+ *   importance [cols] float32 WMSE weights in the stored order (16-byte
+ *              aligned), or NULL for MSE.
+ *   off_lo, off_hi, flags, global_scale  as for fp4q_gptq_nvfp4.
+ *   codes      [rows x cols/2] packed E2M1 codes in the stored order (out;
+ *              8-byte aligned).
+ *   scales     [rows x cols/16] E4M3 patterns in the stored order (out).
+ *   workspace  fp4q_gptq_static_workspace_bytes(rows, cols) bytes (the
+ *              status word, the inverse order and the codes in processing
+ *              order), 256-byte aligned.
+ * Computation: S and every group's scale are those of fp4q_quantize_nvfp4
+ * on w_in with the same importance, window and flags (the sweep on the
+ * weight before any update).  Slot j is then processed as column j of
+ * fp4q_gptq_nvfp4 would be, on the permuted weight with U, except that it
+ * is rounded at the scale of its stored group (perm[j] / 16) and no sweep
+ * runs at group starts; codes are written back to the stored positions.
+ * Data errors: those of fp4q_quantize_nvfp4 and fp4q_gptq_nvfp4, and
+ * FP4Q_DATA_BAD_PERM when perm is not a permutation (out-of-range entries
+ * are clamped, so nothing is read out of bounds; the results are then
+ * meaningless).  Argument errors as for fp4q_gptq_nvfp4, FP4Q_ERR_NULL for
+ * a NULL w_in or perm, FP4Q_ERR_WORKSPACE for a short or misaligned
+ * workspace.
+ */
+size_t fp4q_gptq_static_workspace_bytes(int64_t rows, int64_t cols);
+
+fp4q_status_t fp4q_gptq_static_nvfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                     int64_t ld_in, const int32_t *perm, const float *hinv_chol,
+                                     const float *importance, int off_lo, int off_hi, uint32_t flags,
+                                     uint8_t *codes, uint8_t *scales, float *global_scale, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * fp4q_gptq_static_nvfp4 with MXFP4 groups ([MR] 2., components 1 and 2):
+ * every group's E8M0 exponent is that of fp4q_quantize_mxfp4 on w_in with
+ * the same importance and exponent window (-16 <= off_lo <= 0 <= off_hi <=
+ * 16, at most 16 candidates); slot j is rounded at 2^E of its stored group
+ * (perm[j] / 32), with no global scale.  Arguments as for
+ * fp4q_gptq_static_nvfp4 without flags and global_scale; scales
+ * [rows x cols/32] E8M0 bytes.
+ */
+fp4q_status_t fp4q_gptq_static_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, const float *w_in,
+                                     int64_t ld_in, const int32_t *perm, const float *hinv_chol,
+                                     const float *importance, int off_lo, int off_hi, uint8_t *codes,
+                                     uint8_t *scales, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Dequantization (the consumer side: only codes and dequantization scales

@@ -188,6 +188,42 @@ def test_gptq_validation():
     assert gm(rows=0) in (L.OK, L.ERR_HIP)
 
 
+def test_gptq_static_validation():
+    """Static-order GPTQ: argument errors are returned before anything is
+    enqueued (no GPU needed), and the workspace query covers the inverse
+    order and the processing-order codes."""
+    L, lib = _lib()
+    assert lib.fp4q_gptq_static_workspace_bytes(4, 128) >= lib.fp4q_workspace_bytes() + 4 * 128 + 4 * 64
+    assert lib.fp4q_gptq_static_workspace_bytes(-1, 128) == 0
+    wsb = lib.fp4q_gptq_static_workspace_bytes(4, 128)
+    big = 1 << 40
+    gs = lambda **kw: lib.fp4q_gptq_static_nvfp4(
+        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("src", X), kw.get("lds", 128),
+        kw.get("perm", X), kw.get("u", OUT), kw.get("imp", None), kw.get("lo", -3), kw.get("hi", 7),
+        kw.get("flags", 0), kw.get("codes", OUT), OUT, kw.get("gs", OUT), kw.get("ws", WS), kw.get("wsb", big), None)
+    assert gs(src=None) == L.ERR_NULL
+    assert gs(perm=None) == L.ERR_NULL
+    assert gs(gs=None) == L.ERR_NULL
+    assert gs(ws=None) == L.ERR_WORKSPACE
+    assert gs(wsb=wsb - 1) == L.ERR_WORKSPACE
+    assert gs(ws=WS + 16) == L.ERR_WORKSPACE
+    assert gs(lo=-9, hi=7) == L.ERR_ARG
+    assert gs(flags=2) == L.ERR_ARG
+    assert gs(cols=144, ld=144, lds=144) == L.ERR_SHAPE
+    assert gs(lds=100) == L.ERR_SHAPE
+    assert gs(src=X + 4) == L.ERR_ALIGN
+    assert gs(perm=X + 2) == L.ERR_ALIGN
+    assert gs(codes=OUT + 4) == L.ERR_ALIGN
+    assert gs(imp=OUT + 4) == L.ERR_ALIGN
+    gm = lambda **kw: lib.fp4q_gptq_static_mxfp4(
+        X, kw.get("rows", 4), 128, 128, X, 128, kw.get("perm", X), OUT, None, kw.get("lo", -1), kw.get("hi", 0),
+        OUT, OUT, WS, big, None)
+    assert gm(perm=None) == L.ERR_NULL
+    assert gm(lo=-17, hi=-2) == L.ERR_ARG
+    assert gm(lo=0, hi=17) == L.ERR_ARG
+    assert gm(rows=0) in (L.OK, L.ERR_HIP)
+
+
 def test_gemm_validation():
     L, lib = _lib()
 

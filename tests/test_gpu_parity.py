@@ -956,3 +956,134 @@ def test_c5_stream_checksums_and_resume(tmp_path):
     words = codes.numpy().reshape(-1).view(np.uint32).astype(object)
     host = sum((i + 1) * int(w) for i, w in enumerate(words)) % 2**63
     assert bench._digest(codes.to(DEV)) == host
+
+
+# ------------------------------------------------ GPTQ, static reordering ----
+def _gptq_static_inputs(rows, cols, seed):
+    w = W.random_matrix(rows, cols, seed=seed, dist="t4")
+    X = W.calibration_activations(4 * cols, cols, seed=seed + 1)
+    H, perm, U = W.act_order_and_factor(X)
+    imp = torch.from_numpy(np.diag(H).astype(np.float32))
+    return w, H, perm, U, imp
+
+
+def _static_call(fmt, w, perm, U, im, **kw):
+    fq = _fp4()
+    f = fq.gptq_static_nvfp4 if fmt == "nvfp4" else fq.gptq_static_mxfp4
+    return f(w.to(DEV), torch.from_numpy(perm).to(DEV), U, None if im is None else im.to(DEV), check=True, **kw)
+
+
+def _static_oracle(fmt, w, perm, U, im, **kw):
+    f = GQ.gptq_nvfp4_static if fmt == "nvfp4" else GQ.gptq_mxfp4_static
+    return f(w.numpy(), U, perm, None if im is None else im.numpy(), **kw)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("wmse", [False, True])
+def test_gptq_static_single_batch_bitexact(fmt, wmse):
+    """Static reordering, one 128-column batch (no contraction): the scales
+    come from the sweep on the weight as given and each processing slot is
+    rounded at its stored group's scale, in the oracle's float32 steps:
+    codes (back in the stored order), scales and S are bit-exact."""
+    w, H, perm, U, imp = _gptq_static_inputs(37, 128, seed=140)
+    im = imp if wmse else None
+    res = _static_call(fmt, w, perm, U, im)
+    torch.cuda.synchronize()
+    ref = _static_oracle(fmt, w, perm, U, im)
+    if fmt == "nvfp4":
+        _assert_equal("static S", np.float32(_np(res.global_scale)[0]), ref[2])
+    _assert_equal("static scales", _np(res.scales), ref[1])
+    _assert_equal("static codes", _np(res.codes), ref[0])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_gptq_static_without_feedback_equals_sweep(fmt):
+    """A diagonal factor moves no error: whatever the order, the result is
+    the plain quantizer's, bit for bit (MSE and WMSE)."""
+    fq = _fp4()
+    w = W.random_matrix(64, 512, seed=141, dist="t4")
+    U = np.diag(np.exp(np.random.default_rng(142).normal(0, 0.3, 512))).astype(np.float32)
+    perm = np.random.default_rng(143).permutation(512).astype(np.int32)
+    imp = W.random_importance(512, seed=144)
+    for im in (None, imp):
+        g = _static_call(fmt, w, perm, U, im)
+        q = (fq.quantize_nvfp4 if fmt == "nvfp4" else fq.quantize_mxfp4)(
+            w.to(DEV), None if im is None else im.to(DEV), check=True)
+        torch.cuda.synchronize()
+        _assert_equal("codes", _np(g.codes), _np(q.codes))
+        _assert_equal("scales", _np(g.scales), _np(q.scales))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("rows,cols,wmse", [(192, 512, False), (96, 768, True), (200, 2176, True)])
+def test_gptq_static_multi_batch_against_oracle(fmt, rows, cols, wmse):
+    """Static reordering across batches and (2176 columns) 1024-column
+    blocks: the scales are fixed before any update, so they are bit-exact;
+    codes differ from the oracle's float64 trailing product by float32
+    rounding only (mismatch <= 1e-3), proxy losses agree within 1e-3 and lie
+    below round-to-nearest."""
+    w, H, perm, U, imp = _gptq_static_inputs(rows, cols, seed=145 + cols)
+    im = imp if wmse else None
+    res = _static_call(fmt, w, perm, U, im)
+    torch.cuda.synchronize()
+    ref = _static_oracle(fmt, w, perm, U, im)
+    gc, gs = _np(res.codes), _np(res.scales)
+    _assert_equal("static scales", gs, ref[1])
+    mis = np.mean(Q.unpack_nibbles(gc) != Q.unpack_nibbles(ref[0]))
+    if fmt == "nvfp4":
+        S = ref[2]
+        assert np.float32(_np(res.global_scale)[0]) == S
+        lg, lo = GQ.proxy_loss(w.numpy(), gc, gs, S, H), GQ.proxy_loss(w.numpy(), ref[0], ref[1], S, H)
+        rtn = Q.quantize_nvfp4(w.numpy(), None if im is None else im.numpy())
+        lr = GQ.proxy_loss(w.numpy(), rtn.codes, rtn.scales, rtn.global_scale, H)
+    else:
+        lg, lo = GQ.proxy_loss_mx(w.numpy(), gc, gs, H), GQ.proxy_loss_mx(w.numpy(), ref[0], ref[1], H)
+        rtn = Q.quantize_mxfp4(w.numpy(), None if im is None else im.numpy())
+        lr = GQ.proxy_loss_mx(w.numpy(), rtn.codes, rtn.scales, H)
+    print(f"code mismatch {mis:.2e}, loss rel {abs(lg - lo) / lo:.2e}, vs round-to-nearest {lg / lr:.3f}")
+    assert mis <= 1e-3
+    assert abs(lg - lo) <= 1e-3 * lo
+    assert lg < lr
+
+
+def test_gptq_static_full_size_sampled_rows():
+    """4096 x 4096 (the GPTQ bench's shape), NVFP4 MSE with act-order: rows
+    are independent under GPTQ, so the oracle runs on 24 sampled rows with
+    the same factor and S; scales bit-exact, codes within the multi-batch
+    bar."""
+    rows = cols = 4096
+    w = W.random_matrix(rows, cols, seed=150, dist="t4")
+    X = W.calibration_activations(2048, cols, seed=151)
+    H, perm, U = W.act_order_and_factor(X)
+    res = _static_call("nvfp4", w, perm, U, None)
+    torch.cuda.synchronize()
+    S = np.float32(_np(res.global_scale)[0])
+    assert S == Q.global_scale_nvfp4(w.numpy())
+    pick = np.sort(np.random.default_rng(152).choice(rows, 24, replace=False))
+    codes, scales, _ = GQ.gptq_nvfp4_static(w.numpy()[pick], U, perm, global_scale=S)
+    _assert_equal("static scales (sampled rows)", _np(res.scales)[pick], scales)
+    mis = np.mean(Q.unpack_nibbles(_np(res.codes)[pick]) != Q.unpack_nibbles(codes))
+    print(f"code mismatch on sampled rows {mis:.2e}")
+    assert mis <= 1e-3
+
+
+def test_gptq_static_bad_order_sets_status():
+    """A repeated or out-of-range entry in the order is reported (entries
+    are clamped, so nothing is read out of bounds); a valid call afterwards
+    on the same data is exact again."""
+    fq = _fp4()
+    w, H, perm, U, imp = _gptq_static_inputs(8, 128, seed=153)
+    dup = perm.copy()
+    dup[7] = dup[3]
+    oob = perm.copy()
+    oob[11] = 128
+    neg = perm.copy()
+    neg[0] = -5
+    for bad in (dup, oob, neg):
+        for fmt in ("nvfp4", "mxfp4"):
+            with pytest.raises(fq.FP4QError, match="permutation"):
+                _static_call(fmt, w, bad, U, None)
+    res = _static_call("nvfp4", w, perm, U, None)
+    torch.cuda.synchronize()
+    ref = _static_oracle("nvfp4", w, perm, U, None)
+    _assert_equal("static codes after bad calls", _np(res.codes), ref[0])
