@@ -493,6 +493,22 @@ def run_other(args):
                          "proxy_gptq": proxy_mx(r.codes, r.scales),
                          "proxy_rtn_sweep": proxy_mx(rtn.codes, rtn.scales),
                          "proxy_rtn_absmax": proxy_mx(ab.codes, ab.scales)}
+
+        # static activation reordering (MR-GPTQ component 2): GPTQ's order (largest Hessian diagonal
+        # first) with each group's scale fixed beforehand, codes and scales in the stored order
+        _, perm, Us = W.act_order_and_factor(X)
+        permd = torch.from_numpy(perm).to("cuda:0")
+        Usd = torch.from_numpy(Us).to("cuda:0")
+        for name, fn, im, loss in (("static_mse", fq.gptq_static_nvfp4, None, proxy),
+                                   ("static_wmse", fq.gptq_static_nvfp4, impd, proxy),
+                                   ("static_mxfp4_mse", fq.gptq_static_mxfp4, None, proxy_mx),
+                                   ("static_mxfp4_wmse", fq.gptq_static_mxfp4, impd, proxy_mx)):
+            r = fn(xd, permd, Usd, im, check=True)
+            step = lambda i: fn(xd, permd, Usd, im)
+            prewarm(step, seconds=0.5)
+            ms = _events_time(step, max(3, args.steps // 10))
+            args_ = (r.codes, r.scales, r.global_scale) if loss is proxy else (r.codes, r.scales)
+            res[name] = {"ms": ms, "gel_s": xd.numel() / ms / 1e6, "proxy_gptq": loss(*args_)}
     elif args.config == "c4":
         total_ms = {"mse": 0.0, "wmse": 0.0}
         n = 0
