@@ -1558,28 +1558,47 @@ __global__ __launch_bounds__(kThreads) void perm_inverse_kernel(const int32_t *_
   status.finish(err);
 }
 
-// The weight in processing order, w[r][j] = w_in[r][perm[j]], four slots per thread (cols is a
-// multiple of 128).  Row 0 also checks that perm is a permutation: a repeated entry leaves a slot whose
-// entry of inv names another slot.
+// The weight in processing order, w[r][j] = w_in[r][perm[j]]: one workgroup per row (a row's random
+// reads then fill one XCD's L2 once; spread over the workgroups of several XCDs, each fetched the whole
+// row), four slots per thread and step (cols is a multiple of 128).  Row 0 also checks that perm is a
+// permutation: a repeated entry leaves a slot whose entry of inv names another slot.
 __global__ __launch_bounds__(kThreads) void perm_gather_kernel(const float *__restrict__ w_in, int64_t ld_in,
                                                                 const int32_t *__restrict__ perm,
                                                                 const int32_t *__restrict__ inv, int rows, int cols,
                                                                 float *__restrict__ w, int64_t ld,
                                                                 uint32_t *__restrict__ status) {
-  const int q = cols / 4;
-  const int64_t total = (int64_t)rows * q;
+  // four steps of four slots per pass, every load of a pass issued before its first store; steps past
+  // the row's end read slot 0 and store nothing
+  constexpr int kSteps = 4;
   uint32_t err = 0u;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total; g += (int64_t)gridDim.x * kThreads) {
-    const int r = (int)(g / q), j0 = (int)(g % q) * 4;
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
     const float *src = w_in + (int64_t)r * ld_in;
-    f32x4 v;
+    for (int jb = 4 * (int)threadIdx.x; jb < cols; jb += 4 * kThreads * kSteps) {
+      int pc[kSteps][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int pc = min(max(perm[j0 + k], 0), cols - 1);
-      v[k] = src[pc];
-      if (r == 0 && inv[pc] != j0 + k) err = FP4Q_DATA_BAD_PERM;
+      for (int u = 0; u < kSteps; ++u) {
+        const int j0 = jb + 4 * kThreads * u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pc[u][k] = j0 < cols ? min(max(perm[j0 + k], 0), cols - 1) : 0;
+      }
+      f32x4 v[kSteps];
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[u][k] = src[pc[u][k]];
+#pragma unroll
+      for (int u = 0; u < kSteps; ++u) {
+        const int j0 = jb + 4 * kThreads * u;
+        if (j0 < cols) {
+          *reinterpret_cast<f32x4 *>(w + (int64_t)r * ld + j0) = v[u];
+          if (r == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (inv[pc[u][k]] != j0 + k) err = FP4Q_DATA_BAD_PERM;
+          }
+        }
+      }
     }
-    *reinterpret_cast<f32x4 *>(w + (int64_t)r * ld + j0) = v;
   }
   if (err) atomicOr(status, err);
 }
@@ -2182,9 +2201,8 @@ static fp4q_status_t gptq_static_run(float *w, int64_t rows, int64_t cols, int64
   uint8_t *codes_p = (uint8_t *)(ws + static_ws_codes(cols));
   hipLaunchKernelGGL(perm_inverse_kernel, dim3(ceil_div(cols, kThreads)), dim3(kThreads), 0, s, perm, (int)cols,
                      inv, Status{status, true});
-  const int64_t quads = rows * (cols / 4);
-  hipLaunchKernelGGL(perm_gather_kernel, dim3((int)std::min<int64_t>(ceil_div(quads, (int64_t)kThreads), 8192)),
-                     dim3(kThreads), 0, s, w_in, ld_in, perm, inv, (int)rows, (int)cols, w, ld, status);
+  hipLaunchKernelGGL(perm_gather_kernel, dim3((int)std::min<int64_t>(rows, 16384)), dim3(kThreads), 0, s, w_in,
+                     ld_in, perm, inv, (int)rows, (int)cols, w, ld, status);
   const fp4q_status_t st = scales_pass();
   if (st != FP4Q_OK) return st;
   gptq_batches<FMT, true>(w, rows, cols, ld, w, ld, hinv_chol, nullptr, global_scale, nullptr, 0, off_lo, off_hi,
