@@ -7,6 +7,11 @@ with per-column importance, i.e. everything fp4q_quantize_nvfp4 does.
 Prints ONE JSON line.  ``value`` is quantized elements per second (G/s) with
 the inputs already resident in HBM; ten distinct input buffers (320 MiB, more
 than the 256 MB Infinity Cache) are rotated so every step reads HBM.
+Consecutive steps are spread round-robin over ``--streams`` HIP streams
+(default 2, default priority; each stream has its own output and workspace),
+so that one matrix's max pass and the previous matrix's sweep overlap, as a
+stream of weight matrices would be quantized; ``pipeline`` also reports the
+time per step with every call on one stream.
 
 The ``roofline`` object is for the dominant kernel (the sweep), timed alone
 with HIP events on the stream it runs on (a call with a given global scale
@@ -285,8 +290,55 @@ def prewarm(step, seconds=0.3):
         torch.cuda.synchronize()
 
 
-def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
-    """Time the full call (max pass + sweep) and the sweep kernel alone."""
+def _pipelined_time(jobs, window, had, steps, warmup, nstreams):
+    """Milliseconds per step with consecutive steps issued round-robin on
+    nstreams HIP streams (default priority), step i quantizing jobs[i %
+    len(jobs)] = (x, importance) into an output of its own stream, each
+    stream with its own workspace, so one matrix's max pass and sweep overlap
+    the previous matrix's on another stream.  Every step is still one whole
+    call.  Returns (ms per step, data-error status words)."""
+    import torch
+    import fp4_post_quantization_amd as fq
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+    outs, wss = {}, []
+    for k, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            wss.append(torch.zeros_like(fq.workspace(jobs[0][0].device)))
+            for j, (x, imp) in enumerate(jobs):
+                outs[k, j] = fq.quantize_nvfp4(x, imp, window=window, hadamard_n=had)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k, j = i % nstreams, i % len(jobs)
+        with torch.cuda.stream(streams[k]):
+            x, imp = jobs[j]
+            fq.quantize_nvfp4(x, imp, window=window, hadamard_n=had, out=outs[k, j], ws=wss[k])
+
+    prewarm(step)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for st in streams[1:]:
+        st.wait_event(e0)
+    for i in range(steps):
+        step(i)
+    for st in streams[1:]:
+        done = torch.cuda.Event()
+        done.record(st)
+        main.wait_event(done)
+    e1.record(main)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, [fq.read_status(w) for w in wss]
+
+
+def bench_nvfp4_matrix(x, imp, window, had, steps, warmup, streams=1):
+    """Time the full call (max pass + sweep) per step on one stream, and the
+    sweep kernel alone; with streams > 1 also the steps pipelined over that
+    many streams (bench_nvfp4_matrix.pipelined_ms)."""
     import torch
     import fp4_post_quantization_amd as fq
     bufs = _rotating_copies(x)
@@ -298,6 +350,12 @@ def bench_nvfp4_matrix(x, imp, window, had, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     ms_step = _events_time(step, steps)
+    bench_nvfp4_matrix.pipelined_ms = None
+    if streams > 1:
+        ms_pipe, st = _pipelined_time([(b, imp) for b in bufs], window, had, steps, warmup, streams)
+        if any(st):
+            raise RuntimeError(f"device reported data errors {st}")
+        bench_nvfp4_matrix.pipelined_ms = ms_pipe
     # per-step distribution (a second, separately timed pass: one event pair per step)
     per_step = []
     for i in range(steps):
@@ -331,7 +389,8 @@ def run_c2(args, x_cpu, imp_cpu, cpu_line):
     rows, cols = x.shape
     n = rows * cols
     window = (-8, 7)
-    ms_step, ms_sweep = bench_nvfp4_matrix(x, imp, window, 0, args.steps, args.warmup)
+    ms_one, ms_sweep = bench_nvfp4_matrix(x, imp, window, 0, args.steps, args.warmup, streams=args.streams)
+    ms_step = bench_nvfp4_matrix.pipelined_ms or ms_one
     value = n / (ms_step * 1e-3) / 1e9
     ops = _alg_ops_per_element(16, True)
     byts = _alg_bytes_per_element(2, 16)
@@ -344,6 +403,10 @@ def run_c2(args, x_cpu, imp_cpu, cpu_line):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "pipeline": {"streams": args.streams, "ms_per_step_one_stream": round(ms_one, 5),
+                     "note": "consecutive steps alternate over the HIP streams (default priority), each "
+                             "with its own output and workspace; every step is one whole call (max pass "
+                             "+ sweep) on its own input buffer"},
         "step_us_percentiles": getattr(bench_nvfp4_matrix, "step_us", None),
         "higher_is_better": True,
         "scaling": "weak",
@@ -522,6 +585,18 @@ def run_other(args):
             del x
             torch.cuda.empty_cache()
         res.update(elements=n, ms_layer=total_ms, gel_s={k: n / v / 1e6 for k, v in total_ms.items()})
+        if args.streams > 1:
+            # the layer's seven matrices one after another, spread over the streams (all resident)
+            mats = [(W.c4_matrix(name).to("cuda:0"), W.c4_importance(name).to("cuda:0")) for name in W.LAYER_8B]
+            pipe = {}
+            for loss, win in (("mse", (-3, 7)), ("wmse", (-8, 7))):
+                jobs = [(m, im if loss == "wmse" else None) for m, im in mats]
+                ms, st = _pipelined_time(jobs, win, 0, 7 * max(3, args.steps // 5), 7, args.streams)
+                if any(st):
+                    raise RuntimeError(f"device reported data errors {st}")
+                pipe[loss] = 7 * ms
+            res.update(streams=args.streams, ms_layer_pipelined=pipe,
+                       gel_s_pipelined={k: n / v / 1e6 for k, v in pipe.items()})
     elif args.config == "c5gate":
         # one 70B-shaped gate projection (28672 x 8192, 470 MB bf16) with H16 + WMSE, repeated: the c5
         # kernel on a single shape (the c5 stream mixes seven)
@@ -706,6 +781,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="c2 and c4: HIP streams the steps are spread over (1 = one call after another)")
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--start-layer", type=int, default=0,
                     help="c5: resume the stream at this layer from the --state file")

@@ -2174,11 +2174,11 @@ static fp4q_status_t check_gptq_static(float *w, int64_t rows, int64_t cols, int
                                        uint8_t *scales, void *workspace, size_t workspace_bytes) {
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (!w || !w_in || !perm || !hinv_chol || !codes || !scales)) return FP4Q_ERR_NULL;
-  if (!workspace || !aligned(workspace, 256) || rows < 0 || cols < 0 ||
-      workspace_bytes < fp4q_gptq_static_workspace_bytes(rows, cols))
+  if (!workspace || !aligned(workspace, 256) ||
+      (rows >= 0 && cols >= 0 && workspace_bytes < fp4q_gptq_static_workspace_bytes(rows, cols)))
     return FP4Q_ERR_WORKSPACE;
   if (off_lo > 0 || off_hi < 0 || off_hi - off_lo > 15) return FP4Q_ERR_ARG;
-  if (ld < cols || cols % kGptqBatch || ld_in < cols) return FP4Q_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld < cols || cols % kGptqBatch || ld_in < cols) return FP4Q_ERR_SHAPE;
   if (rows > 0 && cols > 0 && (rows * (cols / 16) >= ((int64_t)1 << 31) || rows >= ((int64_t)1 << 31)))
     return FP4Q_ERR_SHAPE;
   if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(w_in, 16) || ld_in % 4 || !aligned(hinv_chol, 16) ||

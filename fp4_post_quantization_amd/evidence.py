@@ -206,8 +206,10 @@ def source_hash(config=None):
 
 
 def bench_cmd(config, steps):
+    # every call on one stream, so each kernel's traced duration is its own (the bench line's pipelined
+    # steps overlap kernels of consecutive steps)
     return [sys.executable, os.path.join(ROOT, "bench.py"), "--config", config, "--steps", str(steps),
-            "--warmup", "1", "--no-cpu-baseline", "--copy-calib"]
+            "--warmup", "1", "--no-cpu-baseline", "--copy-calib", "--streams", "1"]
 
 
 def passes(config):

@@ -210,6 +210,7 @@ def test_gptq_static_validation():
     assert gs(lo=-9, hi=7) == L.ERR_ARG
     assert gs(flags=2) == L.ERR_ARG
     assert gs(cols=144, ld=144, lds=144) == L.ERR_SHAPE
+    assert gs(cols=-128) == L.ERR_SHAPE
     assert gs(lds=100) == L.ERR_SHAPE
     assert gs(src=X + 4) == L.ERR_ALIGN
     assert gs(perm=X + 2) == L.ERR_ALIGN
