@@ -438,6 +438,35 @@ def committed_traffic(config):
     return rec if rec.get("source_sha256") == source_hash(config) else None
 
 
+def overlap(trace_csv, gap_us=200.0):
+    """Concurrency of this library's kernels in a rocprofv3 kernel trace
+    (kernel_trace.csv): the dispatches are cut into bursts at idle gaps
+    longer than gap_us, and for the three largest bursts the summed kernel
+    durations are compared with the burst's wall time (above 1: kernels of
+    different queues ran at the same time).  Returns one dict per burst."""
+    rows = list(csv.DictReader(open(trace_csv)))
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"], r["Queue_Id"])
+                for r in rows if _ours(r["Kernel_Name"]))
+    bursts, cur, end = [], [], None
+    for k in ks:
+        if cur and k[0] - end > gap_us * 1e3:
+            bursts.append(cur)
+            cur = []
+        cur.append(k)
+        end = k[1] if end is None or not cur[:-1] else max(end, k[1])
+    if cur:
+        bursts.append(cur)
+    out = []
+    for b in sorted(bursts, key=len)[-3:]:
+        wall = (max(e for _, e, _, _ in b) - min(s_ for s_, _, _, _ in b)) / 1e3
+        busy = sum(e - s_ for s_, e, _, _ in b) / 1e3
+        sweeps = sum(1 for k in b if "sweep_kernel" in k[2])
+        out.append({"kernels": len(b), "sweeps": sweeps, "queues": sorted({k[3] for k in b}),
+                    "wall_us": round(wall, 1), "kernel_us": round(busy, 1),
+                    "concurrency": round(busy / wall, 3), "wall_us_per_sweep": round(wall / max(sweeps, 1), 2)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -449,9 +478,14 @@ def main():
     s.add_argument("--config", default="c2")
     s.add_argument("--in", dest="in_dir", required=True)
     s.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
+    o = sub.add_parser("overlap")
+    o.add_argument("--trace", required=True, help="a rocprofv3 kernel_trace.csv")
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.config, a.out, a.steps)
+    elif a.cmd == "overlap":
+        for b in overlap(a.trace):
+            print(json.dumps(b))
     else:
         summarize(a.config, a.in_dir, a.profiles)
 
