@@ -335,6 +335,37 @@ def _pipelined_time(jobs, window, had, steps, warmup, nstreams):
     return e0.elapsed_time(e1) / steps, [fq.read_status(w) for w in wss]
 
 
+def _pipelined_calls(fn, items, nstreams, steps, warmup=4):
+    """Milliseconds per call of fn(item) with the calls issued round-robin
+    over nstreams HIP streams (default priority), as independent jobs (the
+    weight matrices of a layer) would be; the items are cycled."""
+    import torch
+    main = torch.cuda.current_stream()
+    streams = [main] + [torch.cuda.Stream() for _ in range(nstreams - 1)]
+
+    def step(i):
+        with torch.cuda.stream(streams[i % nstreams]):
+            fn(items[i % len(items)])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(main)
+    for st in streams[1:]:
+        st.wait_event(e0)
+    for i in range(steps):
+        step(i)
+    for st in streams[1:]:
+        done = torch.cuda.Event()
+        done.record(st)
+        main.wait_event(done)
+    e1.record(main)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def bench_nvfp4_matrix(x, imp, window, had, steps, warmup, streams=1):
     """Time the full call (max pass + sweep) per step on one stream, and the
     sweep kernel alone; with streams > 1 also the steps pipelined over that
@@ -572,6 +603,18 @@ def run_other(args):
             ms = _events_time(step, max(3, args.steps // 10))
             args_ = (r.codes, r.scales, r.global_scale) if loss is proxy else (r.codes, r.scales)
             res[name] = {"ms": ms, "gel_s": xd.numel() / ms / 1e6, "proxy_gptq": loss(*args_)}
+
+        # the GPTQ calls of four weight matrices (the c2 weight and three t4 matrices of its shape) as
+        # independent jobs: one after another on one stream, and spread over the streams
+        mats = [xd] + [W.random_matrix(4096, 4096, seed=205 + j, dist="t4").to("cuda:0") for j in range(3)]
+        calls = {"mse": lambda m: fq.gptq_nvfp4(m, Ud), "static_mse": lambda m: fq.gptq_static_nvfp4(m, permd, Usd),
+                 "mxfp4_mse": lambda m: fq.gptq_mxfp4(m, Ud)}
+        pipe = {}
+        for name, fn in calls.items():
+            pipe[name] = {"one_stream_ms": _pipelined_calls(fn, mats, 1, 12)}
+            if args.streams > 1:
+                pipe[name]["ms"] = _pipelined_calls(fn, mats, args.streams, 12)
+        res["matrices_as_jobs"] = {"streams": args.streams, "matrices": len(mats), "ms_per_call": pipe}
     elif args.config == "c4":
         total_ms = {"mse": 0.0, "wmse": 0.0}
         n = 0
@@ -782,7 +825,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--streams", type=int, default=2,
-                    help="c2 and c4: HIP streams the steps are spread over (1 = one call after another)")
+                    help="c2, c4 and gptq: HIP streams independent calls are spread over (1 = one after another)")
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--start-layer", type=int, default=0,
                     help="c5: resume the stream at this layer from the --state file")
