@@ -1087,3 +1087,44 @@ def test_gptq_static_bad_order_sets_status():
     torch.cuda.synchronize()
     ref = _static_oracle("nvfp4", w, perm, U, None)
     _assert_equal("static codes after bad calls", _np(res.codes), ref[0])
+
+
+# ------------------------------------------------------- calls on streams ----
+def test_calls_on_two_streams_match_one_stream():
+    """The library keeps no state between calls: quantize calls of several
+    matrices issued alternately on two HIP streams (each stream its own
+    workspace and outputs, the bench's pipelined steps), and GPTQ calls
+    likewise, give bit for bit what the same calls give one after another,
+    and every status word stays clear."""
+    fq = _fp4()
+    xs = [W.random_matrix(512, 1024, seed=160 + j, dist="t4").to(DEV).to(torch.bfloat16) for j in range(4)]
+    imp = W.random_importance(1024, seed=165).to(DEV)
+    ref = [fq.quantize_nvfp4(x, imp, check=True) for x in xs]
+    mref = [fq.quantize_mxfp4(x, window=(-1, 0), hadamard_n=32, check=True) for x in xs]
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    wss = [torch.zeros_like(fq.workspace(DEV)) for _ in streams]
+    got, mgot = [], []
+    for rep in range(3):
+        for j, x in enumerate(xs):
+            k = (rep * len(xs) + j) % 2
+            with torch.cuda.stream(streams[k]):
+                got.append((j, fq.quantize_nvfp4(x, imp, ws=wss[k])))
+                mgot.append((j, fq.quantize_mxfp4(x, window=(-1, 0), hadamard_n=32, ws=wss[k])))
+    torch.cuda.synchronize()
+    for j, r in got:
+        for f in ("codes", "scales", "global_scale", "block_loss", "offsets"):
+            assert torch.equal(getattr(r, f), getattr(ref[j], f)), (j, f)
+    for j, r in mgot:
+        assert torch.equal(r.codes, mref[j].codes) and torch.equal(r.scales, mref[j].scales), j
+    assert [fq.read_status(w) for w in wss] == [0, 0]
+
+    w, H, U, imp_g = _gptq_inputs(96, 512, seed=166)
+    ws_ = [w.to(DEV), (w * 0.5).to(DEV), (-w).to(DEV)]
+    gref = [fq.gptq_nvfp4(m, U) for m in ws_]
+    gout = []
+    for i in range(6):
+        with torch.cuda.stream(streams[i % 2]):
+            gout.append((i % 3, fq.gptq_nvfp4(ws_[i % 3], U)))
+    torch.cuda.synchronize()
+    for j, r in gout:
+        assert torch.equal(r.codes, gref[j].codes) and torch.equal(r.scales, gref[j].scales), j
