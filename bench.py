@@ -490,6 +490,22 @@ def run_other(args):
         byts = _alg_bytes_per_element(2, 32)
         res.update(elements=x.numel(), ms_step=ms, gel_s=x.numel() / ms / 1e6,
                    hbm_GBs=byts * x.numel() / ms / 1e6, hbm_frac=byts * x.numel() / ms / 1e6 / HBM_PEAK_GBS)
+        if args.streams > 1:
+            # the same steps spread over the streams, each stream with its own outputs and workspace
+            # (outputs keyed by stream: consecutive steps on one stream run in order)
+            outs = {}
+
+            def call(b):
+                k = torch.cuda.current_stream().cuda_stream
+                if k not in outs:
+                    outs[k] = (fq.quantize_mxfp4(b, window=window, hadamard_n=had),
+                               torch.zeros_like(fq.workspace(x.device)))
+                o, w_ = outs[k]
+                fq.quantize_mxfp4(b, window=window, hadamard_n=had, out=o, ws=w_)
+
+            msp = _pipelined_calls(call, bufs, args.streams, args.steps, warmup=max(4, args.warmup))
+            res.update(streams=args.streams, ms_step_pipelined=msp, gel_s_pipelined=x.numel() / msp / 1e6,
+                       hbm_frac_pipelined=byts * x.numel() / msp / 1e6 / HBM_PEAK_GBS)
     elif args.config == "focus":
         # FOCUS forward quantizer on the c2 weight: stored scales from the
         # sweep, FP16 coefficients per 8-element sub-block, dequantized output
@@ -825,7 +841,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--streams", type=int, default=2,
-                    help="c2, c4 and gptq: HIP streams independent calls are spread over (1 = one after another)")
+                    help="c2, c3*, c4 and gptq: HIP streams independent calls are spread over (1 = one after another)")
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--start-layer", type=int, default=0,
                     help="c5: resume the stream at this layer from the --state file")
