@@ -766,8 +766,12 @@ def run_w4a4(args, fmt="mxfp4"):
 
     lib = fq._lib.load()
     ws_bytes = lib.fp4q_gemm_mxfp4_workspace_bytes if mx else lib.fp4q_gemm_nvfp4_workspace_bytes
-    ws = torch.empty(max(max(ws_bytes(W.W4A4_TOKENS, n, k) for n, k in W.LAYER_8B.values()), 16),
-                     dtype=torch.uint8, device=dev)
+    # projections that read the same input, also run as one product each with their rows of B
+    # concatenated (the products are row-independent): q|k|v and gate|up
+    fused = {"qkv": ["q", "k", "v"], "o": ["o"], "gate_up": ["gate", "up"], "down": ["down"]}
+    shapes = list(W.LAYER_8B.values()) + [(sum(W.LAYER_8B[n][0] for n in ns), W.LAYER_8B[ns[0]][1])
+                                          for ns in fused.values()]
+    ws = torch.empty(max(max(ws_bytes(W.W4A4_TOKENS, n, k) for n, k in shapes), 16), dtype=torch.uint8, device=dev)
 
     def gemm(a, b, out=None, out_dtype=torch.bfloat16):
         if mx:
@@ -816,9 +820,39 @@ def run_w4a4(args, fmt="mxfp4"):
         per[n] = {"shape_mnk": [W.W4A4_TOKENS, *W.LAYER_8B[n]], "ms": ms_n,
                   "tflops": flops[n] / ms_n / 1e9, "rel_err_vs_unquantized": err[n]}
     total_flops = sum(flops.values())
-    return {"format": fmt, "tokens": W.W4A4_TOKENS, "ms_layer": ms_layer, "ms_activation_quant": ms_quant, "ms_gemms": ms_gemm,
-            "gemm_tflops": total_flops / ms_gemm / 1e9, "layer_tflops": total_flops / ms_layer / 1e9,
-            "matrix_core_dense_peak_tflops": 10100.0 if mx else 2500.0, "per_matrix": per}
+    res = {"format": fmt, "tokens": W.W4A4_TOKENS, "ms_layer": ms_layer, "ms_activation_quant": ms_quant,
+           "ms_gemms": ms_gemm, "gemm_tflops": total_flops / ms_gemm / 1e9, "layer_tflops": total_flops / ms_layer / 1e9,
+           "matrix_core_dense_peak_tflops": 10100.0 if mx else 2500.0, "per_matrix": per}
+    if not args.fused:
+        return res
+
+    wf = {}
+    for g, names in fused.items():
+        if len(names) == 1:
+            wf[g] = wq[names[0]]
+            continue
+        w = torch.cat([W.c4_matrix(n) for n in names]).to(dev)
+        if mx:
+            wf[g] = fq.quantize_mxfp4(w, window=(-1, 0), hadamard_n=32, with_loss=False, check=True)
+        else:  # one global scale for the concatenated weight
+            wf[g] = fq.quantize_nvfp4(w, window=(-3, 7), with_loss=False, check=True)
+        del w
+    outs_f = {g: torch.empty((W.W4A4_TOKENS, wf[g].codes.shape[0]), dtype=torch.bfloat16, device=dev) for g in fused}
+
+    def gemm_step_fused():
+        for g, names in fused.items():
+            gemm(aq[W.W4A4_READS[names[0]]], wf[g], out=outs_f[g])
+
+    def layer_fused(i):
+        quant_step()
+        gemm_step_fused()
+
+    prewarm(layer_fused, seconds=0.5)
+    ms_layer_f = _events_time(layer_fused, args.steps)
+    ms_gemm_f = _events_time(lambda i: gemm_step_fused(), args.steps)
+    res["fused_inputs"] = {"products": {g: "|".join(ns) for g, ns in fused.items()}, "ms_layer": ms_layer_f,
+                           "ms_gemms": ms_gemm_f, "gemm_tflops": total_flops / ms_gemm_f / 1e9}
+    return res
 
 
 def copy_calibration(nbytes=256 * 2**20, reps=3):
@@ -840,6 +874,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c2")
+    ap.add_argument("--fused", action="store_true",
+                    help="w4a4, w4a4nv: also run the layer with q|k|v and gate|up as one product each")
     ap.add_argument("--streams", type=int, default=2,
                     help="c2, c3*, c4 and gptq: HIP streams independent calls are spread over (1 = one after another)")
     ap.add_argument("--layers", type=int, default=2)
