@@ -683,7 +683,8 @@ def run_other(args):
         warm = W.c5_matrix(0, "k", "cuda:0")
         prewarm(lambda i: fq.quantize_nvfp4(warm, imps["k"], hadamard_n=16))
         del warm
-        res.update(c5_stream(args.layers, imps, start_layer=args.start_layer, state_path=args.state))
+        res.update(c5_stream(args.layers, imps, start_layer=args.start_layer, state_path=args.state,
+                             streams=args.streams))
     elif args.config == "w4a4":
         res.update(run_w4a4(args))
     elif args.config == "w4a4nv":
@@ -702,14 +703,16 @@ def _digest(t):
     return int(((w & 0xFFFFFFFF) * k).sum().item()) & (2**63 - 1)
 
 
-def c5_stream(layers, imps, start_layer=0, state_path=None, shapes=None, device="cuda:0"):
-    """The 70B-shaped weight stream, layer by layer: each matrix is drawn on
-    the device, rotated (16-point block Hadamard) and quantized (NVFP4 WMSE),
-    its outputs reduced to a checksum on the device and discarded.  Only the
-    quantize calls are timed.  With ``state_path`` a record per finished
-    layer (per-matrix checksums of codes and scales, the global scale) is
-    written there after every layer (write to a temporary file, then
-    rename); ``start_layer`` > 0 resumes a stream from that file, whose
+def c5_stream(layers, imps, start_layer=0, state_path=None, shapes=None, device="cuda:0", streams=1):
+    """The 70B-shaped weight stream, layer by layer: each layer's matrices
+    are drawn on the device, then rotated (16-point block Hadamard) and
+    quantized (NVFP4 WMSE), the calls spread round-robin over ``streams``
+    HIP streams, their outputs reduced to checksums on the device and
+    discarded.  Only the quantize calls are timed (events around each
+    layer's calls, all streams joined).  With ``state_path`` a record per
+    finished layer (per-matrix checksums of codes and scales, the global
+    scale) is written there after every layer (write to a temporary file,
+    then rename); ``start_layer`` > 0 resumes a stream from that file, whose
     records of the earlier layers must all be present."""
     import torch
     import fp4_post_quantization_amd as fq
@@ -724,24 +727,42 @@ def c5_stream(layers, imps, start_layer=0, state_path=None, shapes=None, device=
         if missing:
             raise SystemExit(f"state file {state_path} lacks layers {missing}")
         records = {k: v for k, v in records.items() if k < start_layer}
+    main = torch.cuda.current_stream()
+    sts = [main] + [torch.cuda.Stream() for _ in range(streams - 1)]
+    wss = []
+    for st in sts:
+        with torch.cuda.stream(st):
+            wss.append(torch.zeros_like(fq.workspace(torch.device(device))))
     out_ms, n = 0.0, 0
     for layer in range(start_layer, layers):
-        rec = {}
-        for name, shape in shapes.items():
-            x = W.c5_matrix(layer, name, device, shape=shape)
-            torch.cuda.synchronize()
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            r = fq.quantize_nvfp4(x, imps[name], hadamard_n=16, with_loss=False, with_offsets=False)
-            e.record()
-            e.synchronize()
-            out_ms += s.elapsed_time(e)
-            n += x.numel()
-            rec[name] = {"codes": _digest(r.codes), "scales": _digest(r.scales),
-                         "global_scale_bits": int(r.global_scale.view(torch.int32).item()) & 0xFFFFFFFF}
-            del x, r
-        records[layer] = rec
+        xs = {name: W.c5_matrix(layer, name, device, shape=shape) for name, shape in shapes.items()}
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(main)
+        for st in sts[1:]:
+            st.wait_event(s)
+        rs = {}
+        for j, name in enumerate(xs):
+            k = j % streams
+            with torch.cuda.stream(sts[k]):
+                rs[name] = fq.quantize_nvfp4(xs[name], imps[name], hadamard_n=16, with_loss=False,
+                                             with_offsets=False, ws=wss[k])
+        for st in sts[1:]:
+            done = torch.cuda.Event()
+            done.record(st)
+            main.wait_event(done)
+        e.record(main)
+        e.synchronize()
+        out_ms += s.elapsed_time(e)
+        n += sum(x.numel() for x in xs.values())
+        status = [fq.read_status(w) for w in wss]
+        if any(status):
+            raise RuntimeError(f"layer {layer}: device reported data errors {status}")
+        records[layer] = {name: {"codes": _digest(r.codes), "scales": _digest(r.scales),
+                                 "global_scale_bits": int(r.global_scale.view(torch.int32).item()) & 0xFFFFFFFF}
+                          for name, r in rs.items()}
+        del xs, rs
         if state_path:
             tmp = state_path + ".tmp"
             with open(tmp, "w") as f:
@@ -749,7 +770,7 @@ def c5_stream(layers, imps, start_layer=0, state_path=None, shapes=None, device=
             os.replace(tmp, state_path)
         print(f"layer {layer} done, {n / out_ms / 1e6:.1f} G el/s so far", file=sys.stderr, flush=True)
     whole = ",".join(f"{k}:{v[m]['codes']}:{v[m]['scales']}" for k, v in sorted(records.items()) for m in v)
-    return {"layers": layers, "start_layer": start_layer, "elements": n, "ms_total": out_ms,
+    return {"layers": layers, "start_layer": start_layer, "streams": streams, "elements": n, "ms_total": out_ms,
             "gel_s": n / out_ms / 1e6 if out_ms else None,
             "stream_digest": hashlib.sha256(whole.encode()).hexdigest()[:16], "records": len(records)}
 
@@ -887,7 +908,7 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="w4a4, w4a4nv: also run the layer with q|k|v and gate|up as one product each")
     ap.add_argument("--streams", type=int, default=2,
-                    help="c2, c3*, c4 and gptq: HIP streams independent calls are spread over (1 = one after another)")
+                    help="c2, c3*, c4, c5 and gptq: HIP streams independent calls are spread over (1 = one after another)")
     ap.add_argument("--layers", type=int, default=2)
     ap.add_argument("--start-layer", type=int, default=0,
                     help="c5: resume the stream at this layer from the --state file")

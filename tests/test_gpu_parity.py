@@ -939,7 +939,8 @@ def test_gptq_bad_hessian_sets_status():
 def test_c5_stream_checksums_and_resume(tmp_path):
     """The 70B-shaped stream on small shapes: three layers in one run give
     the same per-layer checksums and stream digest as two layers followed by
-    a run resumed at layer 2 from the state file; resuming without the
+    a run resumed at layer 2 from the state file, and as a run with each
+    layer's calls on two streams; resuming without the
     earlier layers' records is refused; the device checksum equals a host
     recomputation."""
     import bench
@@ -949,6 +950,9 @@ def test_c5_stream_checksums_and_resume(tmp_path):
     bench.c5_stream(2, imps, state_path=str(tmp_path / "b.json"), shapes=shapes)
     resumed = bench.c5_stream(3, imps, start_layer=2, state_path=str(tmp_path / "b.json"), shapes=shapes)
     assert resumed["stream_digest"] == full["stream_digest"] and resumed["records"] == 3
+    # the calls of each layer spread over two streams: the same records
+    two = bench.c5_stream(3, imps, shapes=shapes, streams=2)
+    assert two["stream_digest"] == full["stream_digest"] and two["records"] == 3
     assert json.load(open(tmp_path / "a.json")) == json.load(open(tmp_path / "b.json"))
     with pytest.raises(SystemExit):
         bench.c5_stream(3, imps, start_layer=2, state_path=str(tmp_path / "missing.json"), shapes=shapes)
