@@ -1132,3 +1132,22 @@ def test_calls_on_two_streams_match_one_stream():
     torch.cuda.synchronize()
     for j, r in gout:
         assert torch.equal(r.codes, gref[j].codes) and torch.equal(r.scales, gref[j].scales), j
+
+
+def test_gptq_static_given_scale_and_empty():
+    """Static reordering with the global scale given: passing back the scale
+    the call computed gives the same codes and scales, a NaN scale is
+    reported, and an empty matrix returns empty results without errors."""
+    fq = _fp4()
+    w, H, perm, U, imp = _gptq_static_inputs(24, 256, seed=170)
+    a = _static_call("nvfp4", w, perm, U, imp)
+    b = _static_call("nvfp4", w, perm, U, imp, global_scale=float(_np(a.global_scale)[0]))
+    torch.cuda.synchronize()
+    for f in ("codes", "scales", "global_scale"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    with pytest.raises(fq.FP4QError, match="global scale"):
+        _static_call("nvfp4", w, perm, U, imp, global_scale=float("nan"))
+    e = fq.gptq_static_nvfp4(torch.zeros((0, 256), device=DEV), torch.from_numpy(perm).to(DEV), U, check=True)
+    m = fq.gptq_static_mxfp4(torch.zeros((0, 256), device=DEV), torch.from_numpy(perm).to(DEV), U, check=True)
+    torch.cuda.synchronize()
+    assert e.codes.shape == (0, 128) and e.scales.shape == (0, 16) and m.scales.shape == (0, 8)
