@@ -2184,6 +2184,11 @@ static fp4q_status_t check_gptq_static(float *w, int64_t rows, int64_t cols, int
   if (!empty && (!aligned(w, 16) || ld % 4 || !aligned(w_in, 16) || ld_in % 4 || !aligned(hinv_chol, 16) ||
                  !aligned(codes, 8) || !aligned(perm, 4) || (importance && !aligned(importance, 16))))
     return FP4Q_ERR_ALIGN;
+  if (!empty) {  // the weight is gathered into w, so the two must not share memory
+    const uintptr_t a0 = (uintptr_t)w, a1 = a0 + (uintptr_t)(((rows - 1) * ld + cols) * 4);
+    const uintptr_t b0 = (uintptr_t)w_in, b1 = b0 + (uintptr_t)(((rows - 1) * ld_in + cols) * 4);
+    if (a0 < b1 && b0 < a1) return FP4Q_ERR_ARG;
+  }
   return FP4Q_OK;
 }
 

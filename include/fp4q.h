@@ -399,8 +399,8 @@ fp4q_status_t fp4q_gptq_mxfp4(float *w, int64_t rows, int64_t cols, int64_t ld, 
  * FP4Q_DATA_BAD_PERM when perm is not a permutation (out-of-range entries
  * are clamped, so nothing is read out of bounds; the results are then
  * meaningless).  Argument errors as for fp4q_gptq_nvfp4, FP4Q_ERR_NULL for
- * a NULL w_in or perm, FP4Q_ERR_WORKSPACE for a short or misaligned
- * workspace.
+ * a NULL w_in or perm, FP4Q_ERR_ARG when w_in and w overlap,
+ * FP4Q_ERR_WORKSPACE for a short or misaligned workspace.
  */
 size_t fp4q_gptq_static_workspace_bytes(int64_t rows, int64_t cols);
 

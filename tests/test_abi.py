@@ -198,7 +198,7 @@ def test_gptq_static_validation():
     wsb = lib.fp4q_gptq_static_workspace_bytes(4, 128)
     big = 1 << 40
     gs = lambda **kw: lib.fp4q_gptq_static_nvfp4(
-        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("src", X), kw.get("lds", 128),
+        kw.get("w", X), 4, kw.get("cols", 128), kw.get("ld", 128), kw.get("src", 0x80000), kw.get("lds", 128),
         kw.get("perm", X), kw.get("u", OUT), kw.get("imp", None), kw.get("lo", -3), kw.get("hi", 7),
         kw.get("flags", 0), kw.get("codes", OUT), OUT, kw.get("gs", OUT), kw.get("ws", WS), kw.get("wsb", big), None)
     assert gs(src=None) == L.ERR_NULL
@@ -212,12 +212,15 @@ def test_gptq_static_validation():
     assert gs(cols=144, ld=144, lds=144) == L.ERR_SHAPE
     assert gs(cols=-128) == L.ERR_SHAPE
     assert gs(lds=100) == L.ERR_SHAPE
-    assert gs(src=X + 4) == L.ERR_ALIGN
+    assert gs(src=0x80004) == L.ERR_ALIGN
     assert gs(perm=X + 2) == L.ERR_ALIGN
     assert gs(codes=OUT + 4) == L.ERR_ALIGN
     assert gs(imp=OUT + 4) == L.ERR_ALIGN
+    # the weight and the working storage must not share memory
+    assert gs(src=X + 16 * 64) == L.ERR_ARG
+    assert gs(src=X) == L.ERR_ARG
     gm = lambda **kw: lib.fp4q_gptq_static_mxfp4(
-        X, kw.get("rows", 4), 128, 128, X, 128, kw.get("perm", X), OUT, None, kw.get("lo", -1), kw.get("hi", 0),
+        X, kw.get("rows", 4), 128, 128, 0x80000, 128, kw.get("perm", X), OUT, None, kw.get("lo", -1), kw.get("hi", 0),
         OUT, OUT, WS, big, None)
     assert gm(perm=None) == L.ERR_NULL
     assert gm(lo=-17, hi=-2) == L.ERR_ARG
