@@ -438,6 +438,95 @@ def committed_traffic(config):
     return rec if rec.get("source_sha256") == source_hash(config) else None
 
 
+# issue-rate passes over the headline workload (each within the 8-SQ-counter limit of one pass)
+ISSUE_PASSES = {
+    "p1": ["SQ_INSTS_VALU", "SQ_INSTS_VALU_CVT", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_LDS",
+           "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"],
+    "p2": ["SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SALU",
+           "SQ_ACTIVE_INST_MISC", "SQ_INSTS_VALU_TRANS_F32", "SQ_IFETCH"],
+}
+ISSUE_KERNEL = "nvfp4_sweep_kernel<unsigned short, true, 0>"
+
+
+def issue_cmd(name, out_dir):
+    return ["rocprofv3", "--pmc", *ISSUE_PASSES[name], "-d", os.path.join(out_dir, name), "-o", name,
+            "--output-format", "csv", "--", sys.executable, os.path.join(ROOT, "bench.py"), "--config", "c2",
+            "--steps", "5", "--warmup", "1", "--no-cpu-baseline", "--streams", "1"]
+
+
+def issue_run(out_dir):
+    os.makedirs(out_dir, exist_ok=True)
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    for name in ISSUE_PASSES:
+        cmd = issue_cmd(name, out_dir)
+        print("==", " ".join(cmd), flush=True)
+        subprocess.run(["timeout", "-s", "KILL", "240", *cmd], check=True, env=env)
+
+
+def issue_summarize(in_dir, profiles):
+    """Issue-rate summary of the headline sweep kernel from the two passes:
+    per-dispatch counter means, the shader engines' busy window, the VALU
+    issue rate inside it and the instructions per block-candidate."""
+    vals, counts = {}, {}
+    agent = {}
+    for name in ISSUE_PASSES:
+        path = os.path.join(in_dir, name, f"{name}_counter_collection.csv")
+        for (k, grid, c), (v, n) in _counter_means(path).items():
+            if ISSUE_KERNEL.split("<")[0] in k and "unsigned short, true, 0>" in k:
+                tot, cnt = vals.get(c, (0.0, 0))
+                vals[c] = (tot + v * n, cnt + n)
+                counts[name] = counts.get(name, 0) + n
+        agent = agent or _agent(os.path.join(in_dir, name, f"{name}_agent_info.csv"))
+    m = {c: t / n for c, (t, n) in vals.items()}
+    simds = int(agent.get("Simd_Count", 1024))
+    xcc = int(agent.get("Num_Xcc", 8))
+    ses = int(agent.get("Num_Shader_Engines", 0) or agent.get("Shader_Engines", 0) or 4 * xcc)
+    clk = float(agent.get("Max_Engine_Clk_Fcompute", 2400)) * 1e6
+    busy = m["SQ_BUSY_CYCLES"] / ses
+    issue = (m["SQ_INSTS_VALU"] / simds) / (busy / 4)
+    waves = 16384
+    lines = [f"# Issue-rate counters: `{ISSUE_KERNEL}`, NVFP4 WMSE, bf16 4096x4096", "",
+             f"Device: {agent.get('Name', 'gfx950')}, {simds} SIMDs, {ses} shader engines ({xcc} XCDs), "
+             f"max engine clock {clk / 1e6:.0f} MHz.", "",
+             "Two counter passes over the headline workload with every call on one stream (each pass its own "
+             f"run; averages over every dispatch of the kernel in the run: {counts.get('p1', 0)} and "
+             f"{counts.get('p2', 0)} dispatches):", ""]
+    for name in ISSUE_PASSES:
+        cmd = issue_cmd(name, in_dir)
+        lines.append("    " + " ".join("python" if c == sys.executable else ("bench.py" if c.endswith("bench.py") else c)
+                                       for c in cmd))
+    lines += ["", "run by", "", f"    python -m fp4_post_quantization_amd.evidence issue --out {in_dir}", "",
+              "and summarized by", "",
+              f"    python -m fp4_post_quantization_amd.evidence issue-summary --in {in_dir} --profiles profiles", "",
+              "| counter (per dispatch) | value |", "|---|---|"]
+    unit = {"SQ_WAIT_INST_LDS": " quad-cycles", "SQ_WAVE_CYCLES": " quad-cycles", "SQ_ACTIVE_INST_VALU": " quad-cycles",
+            "SQ_ACTIVE_INST_VALU2": " quad-cycles", "SQ_ACTIVE_INST_SCA": " quad-cycles",
+            "SQ_WAIT_INST_ANY": " quad-cycles", "SQ_BUSY_CYCLES": f" (sum over {ses} SEs)"}
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+              "SQ_WAIT_INST_LDS", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VALU2",
+              "SQ_ACTIVE_INST_SCA", "SQ_WAIT_INST_ANY"):
+        if c in m:
+            extra = f" ({100 * m[c] / m['SQ_INSTS_VALU']:.1f}% of VALU)" if c == "SQ_INSTS_VALU_CVT" else ""
+            lines.append(f"| {c} | {m[c]:.4g}{unit.get(c, '')}{extra} |")
+    lines += ["", "Derived:",
+              f"- Busy window per SE: {m['SQ_BUSY_CYCLES']:.4g} / {ses} = {busy / 1e3:.1f} k cycles = "
+              f"{busy / clk * 1e6:.1f} us at {clk / 1e9:.1f} GHz (the rest of the kernel's traced duration is "
+              "launch ramp and drain).",
+              f"- VALU issue inside the busy window: ({m['SQ_INSTS_VALU']:.4g} / {simds} SIMDs) / "
+              f"({busy / 1e3:.1f} k / 4 quad-cycles) = **{100 * issue:.1f}%** of a SIMD's VALU issue slots "
+              "(one wave64 VALU instruction per quad-cycle).",
+              f"- Per lane and candidate (a lane owns one 16-element block; {waves} waves x 16 candidates): "
+              f"{m['SQ_INSTS_VALU_CVT'] / (waves * 16):.1f} converts of "
+              f"{m['SQ_INSTS_VALU'] / (waves * 16):.1f} VALU instructions (the candidate loop's 16 converts and "
+              "60 other VALU, plus prologue and emit).",
+              f"- LDS waits: {m['SQ_WAIT_INST_LDS']:.3g} quad-cycles, "
+              f"{100 * m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:.2f}% of wave-cycles."]
+    md = "\n".join(lines) + "\n"
+    with open(os.path.join(profiles, "nvfp4_wmse_bf16_4096x4096_issue.md"), "w") as f:
+        f.write(md)
+    print(md)
+
+
 def overlap(trace_csv, gap_us=200.0):
     """Concurrency of this library's kernels in a rocprofv3 kernel trace
     (kernel_trace.csv): the dispatches are cut into bursts at idle gaps
@@ -480,9 +569,18 @@ def main():
     s.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     o = sub.add_parser("overlap")
     o.add_argument("--trace", required=True, help="a rocprofv3 kernel_trace.csv")
+    i = sub.add_parser("issue")
+    i.add_argument("--out", required=True)
+    i2 = sub.add_parser("issue-summary")
+    i2.add_argument("--in", dest="in_dir", required=True)
+    i2.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
     if a.cmd == "run":
         run(a.config, a.out, a.steps)
+    elif a.cmd == "issue":
+        issue_run(a.out)
+    elif a.cmd == "issue-summary":
+        issue_summarize(a.in_dir, a.profiles)
     elif a.cmd == "overlap":
         for b in overlap(a.trace):
             print(json.dumps(b))
